@@ -1,0 +1,82 @@
+"""ctypes loader for the plain-C Bareiss oracle (oracle/bareiss.c).
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__``).  ``build()`` compiles the C
+source with gcc into ``oracle/liboracle_bareiss.so``; ``solve`` runs it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(_HERE, "bareiss.c")
+LIB = os.path.join(_HERE, "liboracle_bareiss.so")
+_lib = None
+
+
+def build() -> str:
+    """Compile the C oracle (gcc, -O2, POSIX threads) in place."""
+    tmp = LIB + ".tmp"
+    subprocess.check_call(["gcc", "-O2", "-std=gnu11", "-shared", "-fPIC", "-pthread",
+                           "-Wall", "-Wno-unused-function", SRC, "-o", tmp])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            build()
+        lib = ctypes.CDLL(LIB)
+        lib.oracle_solve.argtypes = [ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64),
+                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     ctypes.POINTER(ctypes.c_char_p)]
+        lib.oracle_solve.restype = ctypes.c_int
+        lib.oracle_free.argtypes = [ctypes.c_char_p]
+        lib.oracle_free.restype = None
+        _lib = lib
+    return _lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:
+        return max(1, os.cpu_count() or 1)
+
+
+def run(A, b, threads: int | None = None, max_steps: int = -1):
+    """Raw call: returns (status, text or None).  status 0 ok, 1 singular, 2 stopped."""
+    lib = _load()
+    A = np.ascontiguousarray(A, dtype=np.int64)
+    b = np.ascontiguousarray(b, dtype=np.int64)
+    n = A.shape[0]
+    c = b.shape[1]
+    assert A.shape == (n, n) and b.shape == (n, c)
+    out = ctypes.c_char_p()
+    st = lib.oracle_solve(A.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                          b.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                          n, c, int(threads or default_threads()), int(max_steps), ctypes.byref(out))
+    if st < 0:
+        raise ValueError("oracle_solve rejected its arguments")
+    text = None
+    if out.value is not None:
+        text = out.value.decode()
+        lib.oracle_free(out)
+    return st, text
+
+
+def solve(A, b, threads: int | None = None):
+    """x = A^-1 b as [n][c] (num, den) pairs in lowest terms, or None if singular."""
+    st, text = run(A, b, threads)
+    if st == 1:
+        return None
+    assert st == 0
+    n, c = np.asarray(A).shape[0], np.asarray(b).shape[1]
+    vals = [tuple(int(tok, 16) for tok in line.split()) for line in text.splitlines()]
+    assert len(vals) == n * c
+    return [vals[r * c:(r + 1) * c] for r in range(n)]

@@ -1,0 +1,432 @@
+"""Pins for the CPU oracle: each check ties it to something other than itself.
+
+The exact-solve card prints no matrices or solutions, so the pins are closed
+forms (Pascal and Hilbert inverses), brute force on tiny inputs (Cramer's rule
+with Leibniz determinants), textbook and library routines (a Fraction
+Gauss-Jordan written here, sympy's rational LU solve, sympy's prime list), the
+card's invariants (A x == b, None on singular input, integral Pascal
+solution, planted integer solutions) and the defining identities of the
+intermediate quantities (B A = I mod q, P r_{i+1} = r_i - A x_i, X = N/d mod P^m).
+"""
+import itertools
+import math
+import random
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import sympy
+
+from dixon_adic_lifting_amd import workloads as W
+from oracle import cbareiss, dixon, exact, modular
+
+
+# ---------------------------------------------------------------- references
+
+def leibniz_det(A):
+    n = len(A)
+    total = 0
+    for perm in itertools.permutations(range(n)):
+        inv = sum(1 for i in range(n) for j in range(i + 1, n) if perm[i] > perm[j])
+        p = 1
+        for i in range(n):
+            p *= int(A[i][perm[i]])
+        total += -p if inv % 2 else p
+    return total
+
+
+def cramer(A, b):
+    n = len(A)
+    d = leibniz_det(A)
+    if d == 0:
+        return None
+    c = len(b[0])
+    out = [[None] * c for _ in range(n)]
+    for t in range(c):
+        for i in range(n):
+            Ai = [[int(b[r][t]) if j == i else int(A[r][j]) for j in range(n)] for r in range(n)]
+            f = Fraction(leibniz_det(Ai), d)
+            out[i][t] = (f.numerator, f.denominator)
+    return out
+
+
+def fraction_gauss_jordan(A, b):
+    """Textbook Gauss-Jordan over Fraction with partial pivoting by nonzero."""
+    n = len(A)
+    c = len(b[0])
+    M = [[Fraction(int(v)) for v in A[i]] + [Fraction(int(v)) for v in b[i]] for i in range(n)]
+    for k in range(n):
+        p = next((i for i in range(k, n) if M[i][k] != 0), None)
+        if p is None:
+            return None
+        M[k], M[p] = M[p], M[k]
+        pv = M[k][k]
+        M[k] = [v / pv for v in M[k]]
+        for i in range(n):
+            if i != k and M[i][k] != 0:
+                f = M[i][k]
+                M[i] = [a - f * bb for a, bb in zip(M[i], M[k])]
+    return [[(M[i][n + t].numerator, M[i][n + t].denominator) for t in range(c)] for i in range(n)]
+
+
+def sympy_solve(A, b):
+    MA = sympy.Matrix([[sympy.Integer(int(v)) for v in row] for row in A])
+    if MA.det() == 0:
+        return None
+    Mb = sympy.Matrix([[sympy.Integer(int(v)) for v in row] for row in b])
+    X = MA.LUsolve(Mb)
+    return [[(int(sympy.fraction(X[i, t])[0]), int(sympy.fraction(X[i, t])[1]))
+             for t in range(Mb.shape[1])] for i in range(MA.shape[0])]
+
+
+def rand_system(n, c, lo, hi, seed):
+    rng = random.Random(seed)
+    A = [[rng.randrange(lo, hi) for _ in range(n)] for _ in range(n)]
+    b = [[rng.randrange(lo, hi) for _ in range(c)] for _ in range(n)]
+    return A, b
+
+
+# ---------------------------------------------------------------- primes
+
+def test_primes_match_sympy(primes):
+    assert primes == list(sympy.primerange(3, 256))
+    assert len(primes) == 53 and all(q % 2 for q in primes)
+    P = math.prod(primes)
+    assert P.bit_length() == 334
+
+
+# ---------------------------------------------------------------- determinant
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 6])
+def test_det_vs_leibniz(n):
+    for seed in range(6):
+        A, _ = rand_system(n, 1, -50, 50, 100 * n + seed)
+        assert exact.bareiss_det(A) == leibniz_det(A)
+
+
+def test_det_special():
+    assert exact.bareiss_det(W.pascal_matrix(30)) == 1
+    D = np.diag(modular.odd_primes_below(256)).astype(np.int64)
+    assert exact.bareiss_det(D) == math.prod(modular.odd_primes_below(256))
+    A, _ = W.duplicate_row_system(9, 3)
+    assert exact.bareiss_det(A) == 0
+
+
+# ---------------------------------------------------------------- solve
+
+@pytest.mark.parametrize("n,c", [(1, 1), (2, 1), (3, 2), (4, 1), (5, 3), (6, 2)])
+def test_solve_vs_cramer(n, c):
+    for seed in range(4):
+        A, b = rand_system(n, c, -30, 30, 7 * n + seed)
+        assert exact.solve(A, b) == cramer(A, b)
+
+
+@pytest.mark.parametrize("n,c,bits", [(8, 2, 8), (12, 1, 24), (20, 3, 16), (40, 1, 8)])
+def test_solve_vs_fraction_gauss_jordan(n, c, bits):
+    A, b = W.uniform_system(n, c, bits, 11 * n + c)
+    assert exact.solve(A, b) == fraction_gauss_jordan(A, b)
+
+
+@pytest.mark.parametrize("n,c", [(5, 1), (10, 2), (14, 1)])
+def test_solve_vs_sympy(n, c):
+    A, b = W.uniform_system(n, c, 20, 3 * n + c)
+    assert exact.solve(A, b) == sympy_solve(A, b)
+
+
+def pascal_inverse(n):
+    return [[(-1) ** (i + j) * sum(math.comb(k, i) * math.comb(k, j) for k in range(max(i, j), n))
+             for j in range(n)] for i in range(n)]
+
+
+def test_pascal_closed_form():
+    A, b = W.generate("c2_pascal30")
+    Sinv = pascal_inverse(30)
+    expect = [[(sum(Sinv[i][j] * int(b[j][0]) for j in range(30)), 1)] for i in range(30)]
+    X = exact.solve(A, b)
+    assert X == expect
+    assert all(den == 1 for row in X for (_, den) in row)   # unimodular -> integral
+
+
+def hilbert_inverse(n):
+    """(H^-1)_ij for H_ij = 1/(i+j-1), 1-indexed closed form."""
+    out = []
+    for i in range(1, n + 1):
+        row = []
+        for j in range(1, n + 1):
+            row.append((-1) ** (i + j) * (i + j - 1) * math.comb(n + i - 1, n - j)
+                       * math.comb(n + j - 1, n - i) * math.comb(i + j - 2, i - 1) ** 2)
+        out.append(row)
+    return out
+
+
+@pytest.mark.parametrize("n", [3, 6, 9, 12])
+def test_scaled_hilbert_closed_form(n):
+    A, L = W.scaled_hilbert(n)
+    rng = np.random.default_rng(n)
+    b = rng.integers(-1000, 1000, size=(n, 2), dtype=np.int64)
+    Hinv = hilbert_inverse(n)
+    expect = [[None, None] for _ in range(n)]
+    for t in range(2):
+        for i in range(n):
+            f = Fraction(sum(Hinv[i][j] * int(b[j][t]) for j in range(n)), L)
+            expect[i][t] = (f.numerator, f.denominator)
+    X = exact.solve(A, b)
+    assert X == expect
+    assert any(den > 1 for row in X for (_, den) in row)      # dense denominators
+
+
+def test_planted_integer_solution():
+    A, b, X = W.planted_system(24, 2, 16, 20, 5)
+    assert exact.solve(A, b) == [[(int(v), 1) for v in row] for row in X]
+
+
+@pytest.mark.parametrize("maker", [
+    lambda: W.duplicate_row_system(12, 1),
+    lambda: W.zero_column_system(12, 2),
+    lambda: W.low_rank_system(12, 7, 3),
+])
+def test_singular_families(maker):
+    A, b = maker()
+    assert exact.solve(A, b) is None
+    assert cbareiss.solve(A, b, 2) is None
+
+
+def test_special_cases():
+    A, _ = W.uniform_system(10, 1, 16, 9)
+    zero = np.zeros((10, 3), dtype=np.int64)
+    assert exact.solve(A, zero) == [[(0, 1)] * 3 for _ in range(10)]
+    I = np.eye(7, dtype=np.int64)
+    b = np.arange(-7, 7, dtype=np.int64).reshape(7, 2)
+    assert exact.solve(I, b) == [[(int(v), 1) for v in row] for row in b]
+    qs = modular.odd_primes_below(256)
+    D = np.diag(qs).astype(np.int64)
+    bb = np.arange(1, 54, dtype=np.int64).reshape(53, 1) * 7
+    X = exact.solve(D, bb)
+    for i, q in enumerate(qs):
+        f = Fraction(int(bb[i, 0]), q)
+        assert X[i][0] == (f.numerator, f.denominator)
+
+
+def test_int64_extremes():
+    # b holds INT64_MIN and INT64_MAX; A = I and a 2x2 with n*max|A| just under 2^63
+    b = np.array([[-(1 << 63)], [(1 << 63) - 1]], dtype=np.int64)
+    assert exact.solve(np.eye(2, dtype=np.int64), b) == [[(-(1 << 63), 1)], [((1 << 63) - 1, 1)]]
+    big = (1 << 62) - 1
+    A = np.array([[big, 1], [3, big]], dtype=np.int64)
+    assert exact.solve(A, b) == cramer(A.tolist(), b.tolist())
+
+
+def test_solution_identity_every_output():
+    for seed in range(5):
+        A, b = W.uniform_system(16, 2, 24, 200 + seed)
+        X = exact.solve(A, b)
+        assert exact.check_solution(A, b, X)
+        # and the check is not vacuous: a perturbed answer fails
+        bad = [list(r) for r in X]
+        bad[3][1] = (bad[3][1][0] + 1, bad[3][1][1])
+        assert not exact.check_solution(A, b, bad)
+
+
+# ---------------------------------------------------------------- C oracle
+
+@pytest.mark.parametrize("n,c,bits,seed", [(1, 1, 8, 0), (3, 4, 8, 1), (17, 2, 24, 2),
+                                           (33, 1, 24, 3), (64, 3, 24, 4), (50, 1, 63, 5)])
+def test_c_oracle_matches_python(n, c, bits, seed):
+    if bits == 63:   # full-width entries within the range limit n * max|A| < 2^63
+        rng = np.random.default_rng(seed)
+        lim = ((1 << 63) - 1) // n
+        A = rng.integers(-lim, lim, size=(n, n), dtype=np.int64)
+        b = rng.integers(np.iinfo(np.int64).min, np.iinfo(np.int64).max, size=(n, c), dtype=np.int64)
+    else:
+        A, b = W.uniform_system(n, c, bits, seed)
+    assert cbareiss.solve(A, b, 3) == exact.solve(A, b)
+
+
+@pytest.mark.parametrize("name", ["c1_n32_int8", "c2_pascal30"])
+def test_c_oracle_configs(name):
+    A, b = W.generate(name)
+    X = exact.solve(A, b)
+    assert X is not None                       # C1's canonical draw is nonsingular
+    assert cbareiss.solve(A, b, 4) == X
+
+
+def test_c_oracle_thread_count_invariant():
+    A, b = W.uniform_system(48, 2, 24, 77)
+    ref = cbareiss.solve(A, b, 1)
+    for T in (2, 5, 8):
+        assert cbareiss.solve(A, b, T) == ref
+
+
+# ---------------------------------------------------------------- modular inverse
+
+@pytest.mark.parametrize("n", [1, 4, 9, 20])
+def test_inverse_mod_definition(n, primes):
+    A, _ = W.uniform_system(n, 1, 24, 40 + n)
+    det = exact.bareiss_det(A)
+    for q in primes:
+        B = modular.inverse_mod(A, q)
+        if det % q == 0:
+            assert B is None
+            continue
+        Am = np.asarray(A, dtype=np.int64) % q
+        assert np.array_equal((B @ Am) % q, np.eye(n, dtype=np.int64))
+        assert np.array_equal((Am @ B) % q, np.eye(n, dtype=np.int64))
+        assert B.min() >= 0 and B.max() < q
+
+
+def test_inverse_mod_vs_adjugate(primes):
+    A, _ = W.uniform_system(6, 1, 12, 8)
+    MA = sympy.Matrix(A.tolist())
+    adj = MA.adjugate()
+    det = int(MA.det())
+    for q in primes:
+        B = modular.inverse_mod(A, q)
+        if det % q == 0:
+            assert B is None
+            continue
+        dinv = pow(det % q, -1, q)
+        expect = np.array([[int(adj[i, j]) * dinv % q for j in range(6)] for i in range(6)])
+        assert np.array_equal(B, expect)
+
+
+def test_det_mod_matches_bareiss(primes):
+    for seed in range(4):
+        A, _ = W.uniform_system(12, 1, 10, 60 + seed)
+        det = exact.bareiss_det(A)
+        for q in primes:
+            assert modular.det_mod(A, q) == det % q
+
+
+def test_dropped_prime_case(primes):
+    # det divisible by 3: A = diag(3, 1, 1, ...) * random unimodular-ish perturbation
+    A, _ = W.uniform_system(8, 1, 8, 5)
+    A = A.copy()
+    A[0] *= 3
+    det = exact.bareiss_det(A)
+    assert det % 3 == 0 and det != 0
+    assert modular.inverse_mod(A, 3) is None
+    live, _ = dixon.surviving_primes(A, primes)
+    assert 3 not in live
+
+
+# ---------------------------------------------------------------- Dixon model
+
+def test_hadamard_bounds_hold():
+    for seed in range(6):
+        n, c = 7, 2
+        A, b = W.uniform_system(n, c, 12, 300 + seed)
+        N, D = dixon.hadamard_bounds(A, b)
+        det = exact.bareiss_det(A)
+        assert abs(det) <= D
+        for t in range(c):
+            for i in range(n):
+                Ai = [[int(b[r][t]) if j == i else int(A[r][j]) for j in range(n)] for r in range(n)]
+                assert abs(exact.bareiss_det(Ai)) <= N
+
+
+def test_step_count_minimal(primes):
+    P = math.prod(primes)
+    for (N, D) in [(1, 1), (10 ** 50, 10 ** 60), (2 ** 700, 2 ** 690)]:
+        m = dixon.step_count(P, N, D)
+        assert P ** m > 2 * N * D
+        assert m == 0 or P ** (m - 1) <= 2 * N * D
+
+
+@pytest.mark.parametrize("n,c,bits", [(6, 1, 24), (12, 2, 16), (32, 1, 8)])
+def test_padic_digits_identities(n, c, bits, primes):
+    A, b = W.uniform_system(n, c, bits, 5 * n + c)
+    live, invs = dixon.surviving_primes(A, primes)
+    P = math.prod(live)
+    m = 4
+    digits, res = dixon.padic_digits(A, b, live, m)
+    for i in range(m):
+        for r in range(n):
+            for t in range(c):
+                x = digits[i][r][t]
+                assert -(P - 1) // 2 <= x <= (P - 1) // 2
+                s = res[i][r][t] - sum(int(A[r][j]) * digits[i][j][t] for j in range(n))
+                assert P * res[i + 1][r][t] == s
+    # X = N / d mod P^m with N/d from Bareiss (independent of the digits)
+    X = dixon.assemble(digits, P)
+    M = P ** m
+    N, d = exact.bareiss_solve_numerators(A, b)
+    dinv = pow(d % M, -1, M)
+    for r in range(n):
+        for t in range(c):
+            assert (X[r][t] - N[r][t] * dinv) % M == 0
+
+
+def test_rational_reconstruct_brute_force():
+    M = 1009 * 7
+    Nb, Db = 8, 30                  # 2 N D = 480 < M
+    for a in range(0, M, 7):
+        found = [(p, q) for q in range(1, Db + 1) for p in range(-Nb, Nb + 1)
+                 if math.gcd(p, q) == 1 and math.gcd(q, M) == 1 and (p - a * q) % M == 0]
+        assert len(found) <= 1
+        got = dixon.rational_reconstruct(a, M, Nb, Db)
+        assert got == (found[0] if found else None)
+
+
+def test_rational_reconstruct_large():
+    rng = random.Random(7)
+    M = math.prod(modular.odd_primes_below(256)) ** 3
+    for _ in range(50):
+        den = rng.randrange(1, 1 << 400)
+        num = rng.randrange(-(1 << 400), 1 << 400)
+        g = math.gcd(num, den)
+        num, den = num // g, den // g
+        if math.gcd(den, M) != 1:
+            continue
+        a = num * pow(den, -1, M) % M
+        assert dixon.rational_reconstruct(a, M, 1 << 400, 1 << 400) == (num, den)
+
+
+@pytest.mark.parametrize("name_or_shape", ["c1_n32_int8", "c2_pascal30", (24, 3, 24, 9), (1, 1, 24, 1)])
+def test_dixon_solve_matches_bareiss(name_or_shape, primes):
+    if isinstance(name_or_shape, str):
+        A, b = W.generate(name_or_shape)
+    else:
+        A, b = W.uniform_system(*name_or_shape)
+    sol, info = dixon.dixon_solve(A, b, primes)
+    assert sol == exact.solve(A, b)
+    P = info["P"]
+    assert P ** info["m"] > 2 * info["N"] * info["D"]
+
+
+def test_dixon_with_dense_denominators(primes):
+    A, L = W.scaled_hilbert(8)
+    b = np.arange(16, dtype=np.int64).reshape(8, 2) - 5
+    sol, _ = dixon.dixon_solve(A, b, primes)
+    assert sol == exact.solve(A, b)
+
+
+# ---------------------------------------------------------------- planted mistakes
+
+def test_pins_catch_a_dropped_term(monkeypatch):
+    """A Bareiss update that drops the second product must fail the Cramer pin."""
+    def broken(A, b):
+        A = [[int(v) for v in r] for r in A]
+        n = len(A)
+        M = [A[i] + [int(v) for v in b[i]] for i in range(n)]
+        prev = 1
+        for k in range(n):
+            for i in range(k + 1, n):
+                for j in range(k + 1, len(M[0])):
+                    M[i][j] = (M[k][k] * M[i][j]) // prev       # dropped - M[i][k] M[k][j]
+                M[i][k] = 0
+            prev = M[k][k]
+        return M, M[n - 1][n - 1]
+    monkeypatch.setattr(exact, "bareiss_eliminate", broken)
+    A, b = rand_system(4, 1, -9, 9, 1)
+    with pytest.raises(AssertionError):
+        assert exact.solve(A, b) == cramer(A, b)
+
+
+def test_pins_catch_a_sign_error_in_digits(primes, monkeypatch):
+    """A digit recurrence with r + A x in place of r - A x must fail the identity."""
+    A, b = W.uniform_system(5, 1, 16, 3)
+    live, _ = dixon.surviving_primes(A, primes)
+    orig = dixon.balanced_mod
+    monkeypatch.setattr(dixon, "balanced_mod", lambda v, P: -orig(v, P))
+    with pytest.raises(AssertionError):
+        dixon.padic_digits(A, b, live, 2)
