@@ -1,0 +1,351 @@
+// C ABI of the exact solver (include/es_solve.h): argument checks, the order
+// of the stages on one HIP stream, and the solution object.
+//
+// Stages (exact-solve card, phanerozoic/exact-solve, section "Method"):
+//   checks + bounds -> residues of A -> batched Gauss-Jordan inverse (one
+//   launch per elimination step, all 53 primes) -> prime-set selection and
+//   step count -> m lift steps (contraction, Garner, residual) -> one
+//   device-to-host copy of the digits per chunk of steps -> host rational
+//   reconstruction.
+#include <hip/hip_runtime.h>
+
+#include <chrono>
+#include <climits>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "../../include/es_solve.h"
+#include "es_internal.h"
+#include "host.h"
+
+using namespace es;
+
+struct es_solution {
+    SolutionData data;
+};
+
+namespace {
+
+thread_local double g_timings[5] = {0, 0, 0, 0, 0};
+
+typedef std::chrono::steady_clock clk;
+double ms_since(clk::time_point t0) {
+    return std::chrono::duration<double, std::milli>(clk::now() - t0).count();
+}
+
+#define HIP_CHECK(expr)                          \
+    do {                                         \
+        if ((expr) != hipSuccess) return ES_EHIP; \
+    } while (0)
+
+// Two 62-bit primes for the rank test that separates "singular" from "det A
+// is a nonzero multiple of every odd prime below 256".
+const uint64_t kRankPrimes[2] = {4611686018427387847ULL, 4611686018427387817ULL};  // 2^62-57, 2^62-87
+
+bool valid_shape(int32_t n, int32_t c) { return n >= 1 && n <= ES_MAX_N && c >= 1 && (int64_t)n * c <= (1LL << 31); }
+
+struct Prep {
+    Layout L;
+    uint64_t maxabs = 0;
+    int nbits = 0, dbits = 0;
+    bool a32 = false;
+};
+
+// Initialise the workspace, compute the norms, check the range.
+int prepare(const int64_t* dA, const int64_t* db, int32_t n, int32_t c, uint8_t* ws, hipStream_t st,
+            Prep* pr) {
+    Layout& L = pr->L;
+    HIP_CHECK(launch_fill_u32((uint32_t*)(ws + L.off_piv), (size_t)kNumPrimes * (n + 1), (uint32_t)INT_MAX, st));
+    HIP_CHECK(launch_fill_u32((uint32_t*)(ws + L.off_rowpos), (size_t)kNumPrimes * n, 0xffffffffu, st));
+    HIP_CHECK(launch_fill_u32((uint32_t*)(ws + L.off_flags), kNumPrimes, 0u, st));
+    HIP_CHECK(launch_fill_u32((uint32_t*)(ws + L.off_rho), (size_t)kNumPrimes * c * L.pitch / 4, 0u, st));
+    HIP_CHECK(launch_stats(dA, db, L, ws, st));
+    std::vector<uint64_t> rowmax(n);
+    std::vector<double> rn(n), cn(n), bn(c);
+    HIP_CHECK(hipMemcpyAsync(rowmax.data(), ws + L.off_rowmax, n * sizeof(uint64_t), hipMemcpyDeviceToHost, st));
+    HIP_CHECK(hipMemcpyAsync(rn.data(), ws + L.off_rownorm, n * sizeof(double), hipMemcpyDeviceToHost, st));
+    HIP_CHECK(hipMemcpyAsync(cn.data(), ws + L.off_colnorm, n * sizeof(double), hipMemcpyDeviceToHost, st));
+    HIP_CHECK(hipMemcpyAsync(bn.data(), ws + L.off_bnorm, c * sizeof(double), hipMemcpyDeviceToHost, st));
+    HIP_CHECK(hipStreamSynchronize(st));
+    uint64_t mx = 0;
+    for (int i = 0; i < n; i++) mx = rowmax[i] > mx ? rowmax[i] : mx;
+    pr->maxabs = mx;
+    if ((unsigned __int128)mx * (unsigned)n >= ((unsigned __int128)1 << 63)) return ES_ERANGE;
+    for (int i = 0; i < n; i++)
+        if (rn[i] == 0.0 || cn[i] == 0.0) return ES_SINGULAR;  // a zero row or column
+    hadamard_bits(rn.data(), cn.data(), bn.data(), n, c, &pr->nbits, &pr->dbits);
+    pr->a32 = mx < (1ULL << 31);
+    return ES_OK;
+}
+
+// Residues and the n Gauss-Jordan launches; flags to the host.
+int run_inverse(const int64_t* dA, uint8_t* ws, hipStream_t st, Prep* pr, int* flags) {
+    const Layout& L = pr->L;
+    HIP_CHECK(launch_residues(dA, L, ws, pr->a32, st));
+    for (int k = 0; k < L.n; k++) HIP_CHECK(launch_gj_step(L, ws, k, st));
+    HIP_CHECK(hipMemcpyAsync(flags, ws + L.off_flags, kNumPrimes * sizeof(int), hipMemcpyDeviceToHost, st));
+    HIP_CHECK(hipStreamSynchronize(st));
+    return ES_OK;
+}
+
+// No prime survived: every q_j divides det A.  Decide singular vs ENOPRIME.
+int no_prime_decision(const int64_t* dA, int32_t n, const Prep& pr, hipStream_t st) {
+    // |det A| <= 2^dbits; if that is below the product of all 53 primes, the
+    // only multiple of it within the bound is 0.
+    BigInt all = BigInt::from_u64(1);
+    for (int j = 0; j < kNumPrimes; j++) all = mul_small(all, kPrimeTable.q[j]);
+    if ((size_t)pr.dbits + 1 < all.bit_length()) return ES_SINGULAR;
+    std::vector<int64_t> A((size_t)n * n);
+    HIP_CHECK(hipMemcpyAsync(A.data(), dA, A.size() * sizeof(int64_t), hipMemcpyDeviceToHost, st));
+    HIP_CHECK(hipStreamSynchronize(st));
+    for (uint64_t p : kRankPrimes)
+        if (full_rank_mod(A.data(), n, p)) return ES_ENOPRIME;  // det != 0 for certain
+    return ES_SINGULAR;  // singular modulo two 62-bit primes as well
+}
+
+// Lift m steps; digits land in host [n*c][m][6].
+int run_lift(const int64_t* dA, const int64_t* db, uint8_t* ws, hipStream_t st, const Prep& pr,
+             const LiveSet& ls, int m, int64_t* digits_host) {
+    const Layout& L = pr.L;
+    LiftParams prm;
+    fill_lift_params(ls, &prm);
+    HIP_CHECK(hipMemcpyAsync(ws + L.off_params, &prm, sizeof prm, hipMemcpyHostToDevice, st));
+    HIP_CHECK(launch_split_b(db, L, ws, ls.E, st));
+    const size_t NC = (size_t)L.n * L.c;
+    for (int i0 = 0; i0 < m; i0 += L.kchunk) {
+        const int cnt = std::min(L.kchunk, m - i0);
+        for (int s = 0; s < cnt; s++) HIP_CHECK(launch_lift_step(L, ws, ls.E, pr.a32, dA, s, st));
+        HIP_CHECK(hipMemcpy2DAsync(digits_host + (size_t)i0 * kDigitLimbs, (size_t)m * kDigitLimbs * 8,
+                                   ws + L.off_digits, (size_t)L.kchunk * kDigitLimbs * 8,
+                                   (size_t)cnt * kDigitLimbs * 8, NC, hipMemcpyDeviceToHost, st));
+    }
+    HIP_CHECK(hipStreamSynchronize(st));
+    return ES_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* es_strerror(int status) {
+    switch (status) {
+        case ES_OK: return "ok";
+        case ES_SINGULAR: return "A is singular over the rationals";
+        case ES_EINVAL: return "invalid argument (size, null pointer or workspace too small)";
+        case ES_ERANGE: return "n * max|A_ij| >= 2^63";
+        case ES_ENOPRIME: return "det A is a nonzero multiple of every odd prime below 256";
+        case ES_EHIP: return "HIP runtime error";
+        case ES_ENOMEM: return "out of memory";
+        case ES_EINTERNAL: return "internal consistency check failed";
+        default: return "unknown status";
+    }
+}
+
+int es_primes(int32_t* q, int32_t cap) {
+    for (int j = 0; j < kNumPrimes && j < cap; j++) q[j] = (int32_t)kPrimeTable.q[j];
+    return kNumPrimes;
+}
+
+size_t es_workspace_bytes(int32_t n, int32_t c) {
+    if (!valid_shape(n, c)) return 0;
+    return make_layout(n, c).total;
+}
+
+int es_last_timings(double* ms5) {
+    if (!ms5) return ES_EINVAL;
+    for (int i = 0; i < 5; i++) ms5[i] = g_timings[i];
+    return ES_OK;
+}
+
+int es_solve_device(const int64_t* dA, const int64_t* db, int32_t n, int32_t c, void* d_ws, size_t ws_bytes,
+                    void* stream, es_solution** out) {
+    if (out) *out = nullptr;
+    if (!out || !dA || !db || !d_ws || !valid_shape(n, c)) return ES_EINVAL;
+    Prep pr;
+    pr.L = make_layout(n, c);
+    if (ws_bytes < pr.L.total) return ES_EINVAL;
+    for (double& t : g_timings) t = 0;
+    hipStream_t st = (hipStream_t)stream;
+    uint8_t* ws = (uint8_t*)d_ws;
+    try {
+        auto t0 = clk::now();
+        int rc = prepare(dA, db, n, c, ws, st, &pr);
+        g_timings[0] = ms_since(t0);
+        if (rc != ES_OK) return rc;
+        t0 = clk::now();
+        int flags[kNumPrimes];
+        rc = run_inverse(dA, ws, st, &pr, flags);
+        g_timings[1] = ms_since(t0);
+        if (rc != ES_OK) return rc;
+        LiveSet ls = make_live_set(flags);
+        if (ls.E == 0) return no_prime_decision(dA, n, pr, st);
+        BigInt M;
+        const int m = choose_m(ls.P, pr.nbits, pr.dbits, &M);
+        std::vector<int64_t> digits((size_t)n * c * m * kDigitLimbs);
+        t0 = clk::now();
+        rc = run_lift(dA, db, ws, st, pr, ls, m, digits.data());
+        g_timings[2] = ms_since(t0);
+        if (rc != ES_OK) return rc;
+        t0 = clk::now();
+        es_solution* sol = new es_solution;
+        rc = reconstruct(digits.data(), (size_t)m, n, c, m, ls.P, M, pr.nbits, pr.dbits, default_threads(),
+                         &sol->data);
+        g_timings[4] = ms_since(t0);
+        if (rc != ES_OK) {
+            delete sol;
+            return rc;
+        }
+        sol->data.live = ls.E;
+        sol->data.m = m;
+        sol->data.nbits = pr.nbits;
+        sol->data.dbits = pr.dbits;
+        *out = sol;
+        return ES_OK;
+    } catch (const std::bad_alloc&) {
+        return ES_ENOMEM;
+    } catch (...) {
+        return ES_EINTERNAL;
+    }
+}
+
+int es_solve(const int64_t* A, const int64_t* b, int32_t n, int32_t c, es_solution** out) {
+    if (out) *out = nullptr;
+    if (!out || !A || !b || !valid_shape(n, c)) return ES_EINVAL;
+    const size_t wsb = es_workspace_bytes(n, c);
+    void *dA = nullptr, *db = nullptr, *ws = nullptr;
+    int rc = ES_OK;
+    if (hipMalloc(&dA, (size_t)n * n * 8) != hipSuccess || hipMalloc(&db, (size_t)n * c * 8) != hipSuccess ||
+        hipMalloc(&ws, wsb) != hipSuccess) {
+        rc = ES_ENOMEM;
+    } else if (hipMemcpy(dA, A, (size_t)n * n * 8, hipMemcpyHostToDevice) != hipSuccess ||
+               hipMemcpy(db, b, (size_t)n * c * 8, hipMemcpyHostToDevice) != hipSuccess) {
+        rc = ES_EHIP;
+    } else {
+        rc = es_solve_device((const int64_t*)dA, (const int64_t*)db, n, c, ws, wsb, nullptr, out);
+    }
+    if (dA) (void)hipFree(dA);
+    if (db) (void)hipFree(db);
+    if (ws) (void)hipFree(ws);
+    return rc;
+}
+
+int32_t es_solution_rows(const es_solution* s) { return s ? s->data.n : 0; }
+int32_t es_solution_cols(const es_solution* s) { return s ? s->data.c : 0; }
+
+int es_solution_get(const es_solution* s, int32_t i, int32_t k, int* num_sign, const uint64_t** num,
+                    int32_t* num_len, const uint64_t** den, int32_t* den_len) {
+    if (!s || !num_sign || !num || !num_len || !den || !den_len) return ES_EINVAL;
+    if (i < 0 || i >= s->data.n || k < 0 || k >= s->data.c) return ES_EINVAL;
+    const size_t idx = (size_t)i * s->data.c + k;
+    const BigInt& nu = s->data.num[idx];
+    const BigInt& de = s->data.den[idx];
+    *num_sign = nu.is_zero() ? 0 : (nu.neg ? -1 : 1);
+    *num = nu.d.data();
+    *num_len = (int32_t)nu.size();
+    *den = de.d.data();
+    *den_len = (int32_t)de.size();
+    return ES_OK;
+}
+
+int es_solution_info(const es_solution* s, int32_t* live_primes, int32_t* m, int32_t* num_bound_bits,
+                     int32_t* den_bound_bits) {
+    if (!s) return ES_EINVAL;
+    if (live_primes) *live_primes = s->data.live;
+    if (m) *m = s->data.m;
+    if (num_bound_bits) *num_bound_bits = s->data.nbits;
+    if (den_bound_bits) *den_bound_bits = s->data.dbits;
+    return ES_OK;
+}
+
+void es_solution_free(es_solution* s) { delete s; }
+
+int es_batched_inverse(const int64_t* dA, int32_t n, void* d_ws, size_t ws_bytes, void* stream, int8_t* dB_out,
+                       int32_t* flags_host) {
+    if (!dA || !d_ws || !dB_out || !flags_host || !valid_shape(n, 1)) return ES_EINVAL;
+    Prep pr;
+    pr.L = make_layout(n, 1);
+    if (ws_bytes < pr.L.total) return ES_EINVAL;
+    hipStream_t st = (hipStream_t)stream;
+    uint8_t* ws = (uint8_t*)d_ws;
+    try {
+        // the norms of b are not needed here; A stands in for it
+        int rc = prepare(dA, dA, n, 1, ws, st, &pr);
+        if (rc == ES_SINGULAR) rc = ES_OK;  // a zero row/column just makes every prime singular
+        if (rc != ES_OK) return rc;
+        int flags[kNumPrimes];
+        rc = run_inverse(dA, ws, st, &pr, flags);
+        if (rc != ES_OK) return rc;
+        HIP_CHECK(launch_export_inverse(pr.L, ws, dB_out, st));
+        HIP_CHECK(hipStreamSynchronize(st));
+        for (int j = 0; j < kNumPrimes; j++) flags_host[j] = flags[j] ? 1 : 0;
+        return ES_OK;
+    } catch (...) {
+        return ES_EINTERNAL;
+    }
+}
+
+int es_lift_digits(const int64_t* dA, const int64_t* db, int32_t n, int32_t c, void* d_ws, size_t ws_bytes,
+                   void* stream, int32_t m_req, int64_t* digits_host, size_t digits_cap,
+                   uint64_t* live_mask_host, int32_t* m_out) {
+    if (!dA || !db || !d_ws || !live_mask_host || !m_out || !valid_shape(n, c)) return ES_EINVAL;
+    Prep pr;
+    pr.L = make_layout(n, c);
+    if (ws_bytes < pr.L.total) return ES_EINVAL;
+    hipStream_t st = (hipStream_t)stream;
+    uint8_t* ws = (uint8_t*)d_ws;
+    try {
+        int rc = prepare(dA, db, n, c, ws, st, &pr);
+        if (rc != ES_OK) return rc;
+        int flags[kNumPrimes];
+        rc = run_inverse(dA, ws, st, &pr, flags);
+        if (rc != ES_OK) return rc;
+        LiveSet ls = make_live_set(flags);
+        if (ls.E == 0) return no_prime_decision(dA, n, pr, st);
+        int m = m_req;
+        if (m <= 0) {
+            BigInt M;
+            m = choose_m(ls.P, pr.nbits, pr.dbits, &M);
+        }
+        uint64_t mask = 0;
+        for (int l = 0; l < ls.E; l++) mask |= 1ULL << ls.idx[l];
+        *live_mask_host = mask;
+        *m_out = m;
+        if (!digits_host) return ES_OK;  // query: m and the live set only
+        if ((size_t)n * c * m * kDigitLimbs > digits_cap) return ES_EINVAL;
+        return run_lift(dA, db, ws, st, pr, ls, m, digits_host);
+    } catch (...) {
+        return ES_EINTERNAL;
+    }
+}
+
+int es_reconstruct(const int64_t* digits, int32_t n, int32_t c, int32_t m, uint64_t live_mask, int32_t num_bits,
+                   int32_t den_bits, int32_t nthreads, es_solution** out) {
+    if (out) *out = nullptr;
+    if (!digits || !out || !valid_shape(n, c) || m < 1 || num_bits < 0 || den_bits < 0) return ES_EINVAL;
+    if (live_mask == 0 || (live_mask >> kNumPrimes) != 0) return ES_EINVAL;
+    try {
+        LiveSet ls = live_set_from_mask(live_mask);
+        BigInt M = pow_u(ls.P, (unsigned)m);
+        if (M.bit_length() < (size_t)num_bits + den_bits + 2) return ES_EINVAL;
+        es_solution* sol = new es_solution;
+        int rc = reconstruct(digits, (size_t)m, n, c, m, ls.P, M, num_bits, den_bits,
+                             nthreads > 0 ? nthreads : default_threads(), &sol->data);
+        if (rc != ES_OK) {
+            delete sol;
+            return rc;
+        }
+        sol->data.live = ls.E;
+        sol->data.m = m;
+        sol->data.nbits = num_bits;
+        sol->data.dbits = den_bits;
+        *out = sol;
+        return ES_OK;
+    } catch (const std::bad_alloc&) {
+        return ES_ENOMEM;
+    } catch (...) {
+        return ES_EINTERNAL;
+    }
+}
+
+}  // extern "C"

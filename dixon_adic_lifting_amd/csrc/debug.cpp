@@ -1,0 +1,64 @@
+// Test hooks into the host bignum code (include/es_debug.h).
+#include "../../include/es_debug.h"
+
+#include "bignum.h"
+
+using es::BigInt;
+
+namespace {
+
+BigInt make(const uint64_t* p, int32_t len, int neg) {
+    BigInt r;
+    if (len > 0) r.d.assign(p, p + len);
+    r.neg = neg != 0;
+    r.trim();
+    return r;
+}
+
+bool put(const BigInt& v, uint64_t* out, int32_t* len, int* neg, int32_t cap) {
+    if ((int32_t)v.size() > cap) return false;
+    for (size_t i = 0; i < v.size(); i++) out[i] = v.d[i];
+    *len = (int32_t)v.size();
+    if (neg) *neg = v.neg ? 1 : 0;
+    return true;
+}
+
+}  // namespace
+
+extern "C" int es_dbg_bignum(int op, const uint64_t* a, int32_t la, int a_neg, const uint64_t* b, int32_t lb,
+                             int b_neg, uint64_t* r1, int32_t* l1, int* n1, uint64_t* r2, int32_t* l2, int* n2,
+                             int32_t cap) {
+    try {
+        BigInt A = make(a, la, a_neg), B = make(b, lb, b_neg), x, y;
+        switch (op) {
+            case ES_DBG_MUL: x = es::mul(A, B); break;
+            case ES_DBG_DIVMOD:
+                if (B.is_zero()) return -1;
+                es::divmod_trunc(A, B, &x, &y);
+                break;
+            case ES_DBG_GCD: x = es::gcd(A, B); break;
+            case ES_DBG_ADD: x = es::add(A, B); break;
+            case ES_DBG_SUB: x = es::sub(A, B); break;
+            default: return -1;
+        }
+        if (!put(x, r1, l1, n1, cap)) return -1;
+        if (op == ES_DBG_DIVMOD && !put(y, r2, l2, n2, cap)) return -1;
+        return 0;
+    } catch (...) {
+        return -6;
+    }
+}
+
+extern "C" int es_dbg_ratrec(const uint64_t* a, int32_t la, const uint64_t* M, int32_t lM, const uint64_t* N,
+                             int32_t lN, const uint64_t* D, int32_t lD, uint64_t* num, int32_t* lnum, int* nneg,
+                             uint64_t* den, int32_t* lden, int32_t cap) {
+    try {
+        BigInt nu, de;
+        if (!es::rational_reconstruct(make(a, la, 0), make(M, lM, 0), make(N, lN, 0), make(D, lD, 0), &nu, &de))
+            return 1;
+        if (!put(nu, num, lnum, nneg, cap) || !put(de, den, lden, nullptr, cap)) return -1;
+        return 0;
+    } catch (...) {
+        return -6;
+    }
+}

@@ -1,0 +1,106 @@
+// Internal declarations shared by the host runtime (api.cpp, host.cpp) and
+// the HIP kernels (kernels.hip).  Not part of the public C ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace es {
+
+constexpr int kNumPrimes = 53;   // odd primes below 256
+constexpr int kDigitLimbs = 6;   // one base-P digit, 384-bit two's complement
+constexpr int kDigitWords = 12;  // the same in 32-bit words
+
+// Odd primes below 256 (Eratosthenes) with their Barrett constants:
+// mu16 = floor(2^16 / q) reduces x < 2^16; mu32 = floor(2^32 / q) reduces
+// x < 2^32; r32 = 2^32 mod q folds the high word of a 64-bit value.
+struct PrimeTable {
+    uint32_t q[kNumPrimes];
+    uint32_t mu16[kNumPrimes];
+    uint32_t mu32[kNumPrimes];
+    uint32_t r32[kNumPrimes];
+};
+
+constexpr PrimeTable make_prime_table() {
+    PrimeTable t{};
+    bool composite[256] = {};
+    for (unsigned i = 2; i < 256; i++)
+        if (!composite[i])
+            for (unsigned j = i * i; j < 256; j += i) composite[j] = true;
+    int cnt = 0;
+    for (unsigned v = 3; v < 256; v++) {
+        if (composite[v]) continue;
+        t.q[cnt] = v;
+        t.mu16[cnt] = 65536u / v;
+        t.mu32[cnt] = (uint32_t)(4294967296ull / v);
+        t.r32[cnt] = (uint32_t)(4294967296ull % v);
+        cnt++;
+    }
+    return t;
+}
+
+constexpr PrimeTable kPrimeTable = make_prime_table();
+static_assert(kPrimeTable.q[0] == 3 && kPrimeTable.q[kNumPrimes - 1] == 251, "prime table");
+
+// Per-solve constants of the lift, for the live primes in ascending order.
+// Lives in the device workspace; kernels read it with uniform (scalar) loads.
+struct LiftParams {
+    int32_t E;                    // number of live primes
+    int32_t pad0;
+    uint64_t Pinv;                // P^-1 mod 2^64 (P odd)
+    uint32_t qidx[kNumPrimes];    // index into the 53-prime table
+    uint32_t q[kNumPrimes];
+    uint32_t mu16[kNumPrimes];
+    uint32_t mu32[kNumPrimes];
+    uint32_t r32[kNumPrimes];
+    uint32_t pad1[3];
+    uint64_t corr[kDigitWords];   // 128 * sum_l Qw[l][w], see garner kernels
+    uint32_t Qw[kNumPrimes][kDigitWords];  // words of Q_l = prod_{l' < l} q_l'
+    uint8_t ginv[kNumPrimes][64];          // ginv[l][k] = q_l^-1 mod q_k (l < k)
+};
+
+// Device workspace layout for an n x n system with c right-hand sides.
+struct Layout {
+    int n, c;
+    int pitch;            // row pitch of the residue matrices, bytes
+    int lpr;              // lanes per row in the row kernels (4 .. 64)
+    int kchunk;           // lift steps whose digits the device buffer holds
+    size_t off_S;         // u8/int8 [53][n][pitch]   GJ matrix, then B_j
+    size_t off_piv;       // int32 [53][n + 1]         pivot row per step
+    size_t off_rowpos;    // int32 [53][n]             step at which a row pivoted
+    size_t off_pend;      // u8 [2][53][pitch]         scaled pivot rows
+    size_t off_flags;     // int32 [53]                singular mod q_j
+    size_t off_rowmax;    // uint64 [n]                max |A_ij| per row
+    size_t off_rownorm;   // double [n]                row norms^2 of A
+    size_t off_colpart;   // double [ceil(n/64)][n]    column partial sums
+    size_t off_colnorm;   // double [n]                column norms^2 of A
+    size_t off_bpart;     // double [ceil(n/64)][c]
+    size_t off_bnorm;     // double [c]                column norms^2 of b
+    size_t off_A32;       // int32 [n][n]              A when |A| < 2^31
+    size_t off_R;         // int64 [n][c]              residual r_i
+    size_t off_rho;       // int8 [53][c][pitch]       r_i mods q_j, permuted
+    size_t off_U;         // u8 [53][n*c]              (B_j r_i) mod q_j
+    size_t off_xlow;      // uint64 [n][c]             x_i mod 2^64
+    size_t off_digits;    // uint64 [n*c][kchunk][6]   digits of a chunk of steps
+    size_t off_params;    // LiftParams
+    size_t total;
+};
+
+Layout make_layout(int n, int c);
+
+// ---------------------------------------------------------------- launchers
+// Each enqueues on `st` and returns the launch status.
+
+hipError_t launch_fill_u32(uint32_t* p, size_t count, uint32_t value, hipStream_t st);
+hipError_t launch_stats(const int64_t* A, const int64_t* b, const Layout& L, uint8_t* ws,
+                        hipStream_t st);
+hipError_t launch_residues(const int64_t* A, const Layout& L, uint8_t* ws, bool make_a32,
+                           hipStream_t st);
+hipError_t launch_gj_step(const Layout& L, uint8_t* ws, int k, hipStream_t st);
+hipError_t launch_export_inverse(const Layout& L, const uint8_t* ws, int8_t* B, hipStream_t st);
+hipError_t launch_split_b(const int64_t* b, const Layout& L, uint8_t* ws, int E, hipStream_t st);
+hipError_t launch_lift_step(const Layout& L, uint8_t* ws, int E, bool a32, const int64_t* A64,
+                            int slot, hipStream_t st);
+
+}  // namespace es

@@ -1,0 +1,320 @@
+// Host-side stages of the solver (see host.h).
+//
+// Prime set and step count follow the exact-solve card (phanerozoic/
+// exact-solve), section "Method": P is a squarefree product of odd primes
+// below 256 (odd so that P^-1 mod 2^64 exists), and the lift runs until P^m
+// exceeds twice the product of the Hadamard bounds on numerator and
+// denominator.  Reconstruction follows the same section: a common
+// denominator from a small sample of components, then one modular multiply
+// per numerator.
+#include "host.h"
+
+#include <sched.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <thread>
+
+#include "../../include/es_solve.h"
+
+namespace es {
+
+typedef unsigned __int128 u128;
+
+static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+Layout make_layout(int n, int c) {
+    Layout L{};
+    L.n = n;
+    L.c = c;
+    if (n <= 1024) {
+        int p = 64;
+        while (p < n) p <<= 1;
+        L.pitch = p;
+    } else {
+        L.pitch = (int)align_up((size_t)n, 64);
+    }
+    L.lpr = std::min(64, L.pitch / 16);
+    const size_t NC = (size_t)n * c;
+    const size_t per_step = NC * kDigitLimbs * sizeof(uint64_t);
+    size_t kc = ((size_t)64 << 20) / per_step;
+    L.kchunk = (int)std::max<size_t>(1, std::min<size_t>(kc, 4096));
+    const size_t E = kNumPrimes, nrb = ((size_t)n + 63) / 64;
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = o;
+        o = align_up(o + bytes, 256);
+        return at;
+    };
+    L.off_S = take(E * n * (size_t)L.pitch);
+    L.off_piv = take(E * (n + 1) * sizeof(int32_t));
+    L.off_rowpos = take(E * n * sizeof(int32_t));
+    L.off_pend = take(2 * E * (size_t)L.pitch);
+    L.off_flags = take(E * sizeof(int32_t));
+    L.off_rowmax = take((size_t)n * sizeof(uint64_t));
+    L.off_rownorm = take((size_t)n * sizeof(double));
+    L.off_colpart = take(nrb * n * sizeof(double));
+    L.off_colnorm = take((size_t)n * sizeof(double));
+    L.off_bpart = take(nrb * c * sizeof(double));
+    L.off_bnorm = take((size_t)c * sizeof(double));
+    L.off_A32 = take((size_t)n * n * sizeof(int32_t));
+    L.off_R = take(NC * sizeof(int64_t));
+    L.off_rho = take(E * c * (size_t)L.pitch);
+    L.off_U = take(E * NC);
+    L.off_xlow = take(NC * sizeof(uint64_t));
+    L.off_digits = take(NC * (size_t)L.kchunk * kDigitLimbs * sizeof(uint64_t));
+    L.off_params = take(sizeof(LiftParams));
+    L.total = o;
+    return L;
+}
+
+// ---------------------------------------------------------------- primes
+
+LiveSet make_live_set(const int* flags) {
+    LiveSet ls;
+    ls.P = BigInt::from_u64(1);
+    for (int j = 0; j < kNumPrimes; j++) {
+        if (flags[j]) continue;
+        ls.idx[ls.E++] = j;
+        ls.P = mul_small(ls.P, kPrimeTable.q[j]);
+    }
+    // P^-1 mod 2^64 by Newton's iteration x <- x (2 - P x); P x = 1 mod 8 at x = P
+    uint64_t p0 = ls.P.is_zero() ? 1 : ls.P.d[0];
+    uint64_t x = p0;
+    for (int it = 0; it < 6; it++) x *= 2 - p0 * x;
+    ls.Pinv = x;
+    return ls;
+}
+
+LiveSet live_set_from_mask(uint64_t mask) {
+    int flags[kNumPrimes];
+    for (int j = 0; j < kNumPrimes; j++) flags[j] = ((mask >> j) & 1) ? 0 : 1;
+    return make_live_set(flags);
+}
+
+static uint32_t inv_mod_small(uint32_t a, uint32_t q) {
+    // extended Euclid on small integers
+    int64_t t0 = 0, t1 = 1, r0 = q, r1 = a % q;
+    while (r1) {
+        int64_t qt = r0 / r1, tmp;
+        tmp = r0 - qt * r1; r0 = r1; r1 = tmp;
+        tmp = t0 - qt * t1; t0 = t1; t1 = tmp;
+    }
+    return (uint32_t)((t0 % (int64_t)q + q) % q);
+}
+
+void fill_lift_params(const LiveSet& ls, LiftParams* prm) {
+    std::memset(prm, 0, sizeof *prm);
+    prm->E = ls.E;
+    prm->Pinv = ls.Pinv;
+    for (int l = 0; l < ls.E; l++) {
+        const int j = ls.idx[l];
+        prm->qidx[l] = (uint32_t)j;
+        prm->q[l] = kPrimeTable.q[j];
+        prm->mu16[l] = kPrimeTable.mu16[j];
+        prm->mu32[l] = kPrimeTable.mu32[j];
+        prm->r32[l] = kPrimeTable.r32[j];
+    }
+    for (int l = 0; l < ls.E; l++)
+        for (int k = l + 1; k < ls.E; k++) prm->ginv[l][k] = (uint8_t)inv_mod_small(prm->q[l], prm->q[k]);
+    // Q_l = q_0 ... q_{l-1} as 32-bit words
+    BigInt Q = BigInt::from_u64(1);
+    for (int l = 0; l < ls.E; l++) {
+        for (int w = 0; w < kDigitWords; w++) {
+            size_t limb = (size_t)w / 2;
+            uint64_t v = limb < Q.size() ? Q.d[limb] : 0;
+            prm->Qw[l][w] = (uint32_t)(w % 2 ? v >> 32 : v);
+        }
+        Q = mul_small(Q, prm->q[l]);
+    }
+    for (int w = 0; w < kDigitWords; w++) {
+        uint64_t s = 0;
+        for (int l = 0; l < ls.E; l++) s += prm->Qw[l][w];
+        prm->corr[w] = 128 * s;
+    }
+}
+
+// ---------------------------------------------------------------- bounds
+
+void hadamard_bits(const double* rownorm, const double* colnorm, const double* bnorm, int n, int c,
+                   int* nbits, int* dbits) {
+    double lr = 0, lc = 0, lcmin = INFINITY, lb = -INFINITY;
+    for (int i = 0; i < n; i++) lr += 0.5 * std::log2(rownorm[i]);
+    for (int j = 0; j < n; j++) {
+        double v = 0.5 * std::log2(colnorm[j]);
+        lc += v;
+        lcmin = std::min(lcmin, v);
+    }
+    for (int t = 0; t < c; t++)
+        if (bnorm[t] > 0) lb = std::max(lb, 0.5 * std::log2(bnorm[t]));
+    // |det A| <= min(prod row norms, prod column norms); each numerator is a
+    // determinant with one column replaced by a column of b (Cramer), so
+    // |num| <= ||b_t|| prod_j ||A_j|| / min_j ||A_j||.  Two bits of margin
+    // absorb the rounding of the fp64 sums and logarithms.
+    const double ld = std::min(lr, lc);
+    *dbits = std::max(1, (int)std::ceil(ld + 2.0));
+    if (lb == -INFINITY) {
+        *nbits = 1;  // b = 0: every numerator is 0
+    } else {
+        const double ln = lb + lc - lcmin;
+        *nbits = std::max(1, (int)std::ceil(ln + 2.0));
+    }
+}
+
+int choose_m(const BigInt& P, int nbits, int dbits, BigInt* M) {
+    // P^m > 2^B with B = nbits + dbits + 1 holds exactly when the odd number
+    // P^m has bit length >= B + 1.  Start from a float estimate just below
+    // and confirm with exact powers.
+    const size_t need = (size_t)nbits + dbits + 2;
+    const size_t bl = P.bit_length();
+    const BigInt top = shr_abs(P, bl > 64 ? bl - 64 : 0);
+    const double l2p = std::log2((double)top.d[0]) + (double)(bl > 64 ? bl - 64 : 0);
+    int m = std::max(1, (int)std::floor((double)need / l2p) - 1);
+    BigInt Pm = pow_u(P, (unsigned)m);
+    while (Pm.bit_length() < need) {
+        Pm = mul(Pm, P);
+        m++;
+    }
+    *M = std::move(Pm);
+    return m;
+}
+
+// ---------------------------------------------------------------- singular decision
+
+static uint64_t mulmod62(uint64_t a, uint64_t b, uint64_t p) { return (uint64_t)((u128)a * b % p); }
+
+static uint64_t powmod62(uint64_t a, uint64_t e, uint64_t p) {
+    uint64_t r = 1;
+    while (e) {
+        if (e & 1) r = mulmod62(r, a, p);
+        a = mulmod62(a, a, p);
+        e >>= 1;
+    }
+    return r;
+}
+
+bool full_rank_mod(const int64_t* A, int n, uint64_t p) {
+    std::vector<uint64_t> M((size_t)n * n);
+    for (size_t i = 0; i < (size_t)n * n; i++) {
+        int64_t v = A[i];
+        uint64_t u = v < 0 ? (uint64_t)0 - (uint64_t)v : (uint64_t)v;
+        u %= p;
+        M[i] = (v < 0 && u) ? p - u : u;
+    }
+    for (int k = 0; k < n; k++) {
+        int piv = -1;
+        for (int i = k; i < n; i++)
+            if (M[(size_t)i * n + k]) { piv = i; break; }
+        if (piv < 0) return false;
+        if (piv != k)
+            for (int j = 0; j < n; j++) std::swap(M[(size_t)k * n + j], M[(size_t)piv * n + j]);
+        const uint64_t inv = powmod62(M[(size_t)k * n + k], p - 2, p);
+        for (int i = k + 1; i < n; i++) {
+            const uint64_t f = mulmod62(M[(size_t)i * n + k], inv, p);
+            if (!f) continue;
+            for (int j = k; j < n; j++) {
+                uint64_t t = mulmod62(f, M[(size_t)k * n + j], p);
+                uint64_t& x = M[(size_t)i * n + j];
+                x = x >= t ? x - t : x + p - t;
+            }
+        }
+    }
+    return true;
+}
+
+// ---------------------------------------------------------------- reconstruction
+
+int default_threads() {
+    if (const char* e = std::getenv("ES_THREADS")) {
+        int v = std::atoi(e);
+        if (v > 0) return v;
+    }
+    cpu_set_t set;
+    if (sched_getaffinity(0, sizeof set, &set) == 0) {
+        int cnt = CPU_COUNT(&set);
+        if (cnt > 0) return cnt;
+    }
+    unsigned h = std::thread::hardware_concurrency();
+    return h ? (int)h : 1;
+}
+
+template <class F>
+static void parallel_for(size_t count, int nthreads, F&& fn) {
+    if (count == 0) return;
+    nthreads = (int)std::max<size_t>(1, std::min<size_t>((size_t)nthreads, count));
+    std::atomic<size_t> next{0};
+    auto body = [&]() {
+        for (;;) {
+            size_t i = next.fetch_add(1);
+            if (i >= count) break;
+            fn(i);
+        }
+    };
+    std::vector<std::thread> th;
+    for (int t = 1; t < nthreads; t++) th.emplace_back(body);
+    body();
+    for (auto& t : th) t.join();
+}
+
+// X = sum_{i<m} x_i P^i from balanced 384-bit two's-complement digits (Horner).
+static BigInt assemble(const int64_t* dig, int m, const BigInt& P) {
+    BigInt X;
+    for (int i = m - 1; i >= 0; i--)
+        X = add(mul(X, P), BigInt::from_twos((const uint64_t*)(dig + (size_t)i * kDigitLimbs), kDigitLimbs));
+    return X;
+}
+
+int reconstruct(const int64_t* digits, size_t stride_m, int n, int c, int m, const BigInt& P,
+                const BigInt& M, int nbits, int dbits, int nthreads, SolutionData* out) {
+    const size_t NC = (size_t)n * c;
+    std::vector<BigInt> X(NC);
+    parallel_for(NC, nthreads, [&](size_t j) { X[j] = assemble(digits + j * stride_m * kDigitLimbs, m, P); });
+    const BigInt Nb = shl(BigInt::from_u64(1), (size_t)nbits);
+    const BigInt Db = shl(BigInt::from_u64(1), (size_t)dbits);
+    BigInt Mhalf = shr_abs(M, 1);
+
+    // common denominator from the sample: component 0, then every ceil(NC/4)-th
+    const size_t step = std::max<size_t>(1, (NC + 3) / 4);
+    std::vector<size_t> sample;
+    for (size_t j = 0; j < NC; j += step) sample.push_back(j);
+    std::vector<BigInt> sden(sample.size());
+    std::atomic<int> bad{0};
+    parallel_for(sample.size(), nthreads, [&](size_t s) {
+        BigInt a = mod_floor(X[sample[s]], M), nu, de;
+        if (!rational_reconstruct(a, M, Nb, Db, &nu, &de)) bad = 1;
+        else sden[s] = de;
+    });
+    if (bad) return ES_EINTERNAL;
+    BigInt d = BigInt::from_u64(1);
+    for (auto& v : sden) d = lcm(d, v);
+
+    out->n = n;
+    out->c = c;
+    out->num.assign(NC, BigInt());
+    out->den.assign(NC, BigInt());
+    std::vector<char> failed(NC, 0);
+    parallel_for(NC, nthreads, [&](size_t j) {
+        BigInt y = mod_floor(mul(d, X[j]), M);
+        if (cmp_abs(y, Mhalf) > 0) y = sub(y, M);  // balanced representative
+        if (cmp_abs(y, Nb) > 0) {
+            failed[j] = 1;
+            return;
+        }
+        BigInt g = gcd(y, d);
+        out->num[j] = divexact(y, g);
+        out->den[j] = divexact(d, g);
+    });
+    for (size_t j = 0; j < NC; j++) {
+        if (!failed[j]) continue;
+        BigInt a = mod_floor(X[j], M), nu, de;
+        if (!rational_reconstruct(a, M, Nb, Db, &nu, &de)) return ES_EINTERNAL;
+        out->num[j] = nu;
+        out->den[j] = de;
+    }
+    return ES_OK;
+}
+
+}  // namespace es

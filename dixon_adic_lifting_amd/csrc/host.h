@@ -1,0 +1,49 @@
+// Host-side stages of the solver: workspace layout, prime-set selection and
+// lift constants, bounds and step count, the singularity decision, and the
+// rational reconstruction.
+#pragma once
+#include <cstdint>
+#include <vector>
+
+#include "bignum.h"
+#include "es_internal.h"
+
+namespace es {
+
+struct SolutionData {
+    int n = 0, c = 0;
+    std::vector<BigInt> num, den;  // [n*c], lowest terms, den > 0
+    int live = 0, m = 0, nbits = 0, dbits = 0;
+};
+
+// Live prime set: indices into the 53-prime table, ascending.
+struct LiveSet {
+    int E = 0;
+    int idx[kNumPrimes];
+    BigInt P;
+    uint64_t Pinv = 0;  // P^-1 mod 2^64
+};
+
+LiveSet make_live_set(const int* flags);       // flags[j] != 0 drops prime j
+LiveSet live_set_from_mask(uint64_t mask);
+void fill_lift_params(const LiveSet& ls, LiftParams* prm);
+
+// Bit sizes of the Hadamard bounds from the squared row/column norms of A and
+// the squared column norms of b (fp64 sums, rounded up with a margin).
+void hadamard_bits(const double* rownorm, const double* colnorm, const double* bnorm, int n, int c,
+                   int* nbits, int* dbits);
+
+// Least m with P^m > 2^(nbits + dbits + 1); also returns M = P^m.
+int choose_m(const BigInt& P, int nbits, int dbits, BigInt* M);
+
+// Exact rank test of A modulo a 62-bit prime (host Gaussian elimination).
+bool full_rank_mod(const int64_t* A, int n, uint64_t p);
+
+// digits: int64 [n*c][stride_m][6] (first m used), balanced base-P digits.
+// Returns ES_OK or ES_EINTERNAL.
+int reconstruct(const int64_t* digits, size_t stride_m, int n, int c, int m, const BigInt& P,
+                const BigInt& M, int nbits, int dbits, int nthreads, SolutionData* out);
+
+int default_threads();
+
+}  // namespace es

@@ -1,0 +1,696 @@
+// HIP kernels for CDNA4 (gfx950): the hot path of multi-prime Dixon lifting.
+//
+// Method: exact-solve card (phanerozoic/exact-solve), section "Method":
+//   * batched modular inverse: Gauss-Jordan on [A | I] mod every odd prime
+//     q_j < 256 at once, one launch per elimination step across all primes,
+//     Barrett reduction instead of a hardware modulo;
+//   * lift step: per-prime balanced-residue int8 contraction with int32
+//     accumulation, balanced Garner CRT into the wide base-P digit, and the
+//     one-limb residual update (r_i - A x_i) P^-1 mod 2^64 (P odd);
+//   * range limits (card, "Method"/"Requirements"): n * max|A_ij| < 2^63 so
+//     the residual is one signed 64-bit limb; n <= 2^17 so int8 x int8
+//     products accumulate in int32 without overflow.
+//
+// Layout (see es_internal.h, Layout): the residue matrices are u8/int8
+// [53][n][pitch] with a power-of-two (n <= 1024) or 64-aligned row pitch so
+// that one lane always moves 16 aligned bytes.  The Gauss-Jordan inverse runs
+// in place without physical row swaps: the row chosen as pivot of column k
+// (piv[j][k]) keeps its place, and slot k of every row then holds column
+// piv[j][k] of the inverse.  rowpos[j][i] records the step at which row i
+// became the pivot.  Hence A^-1 mod q_j = S_j with rows gathered by piv and
+// columns scattered by rowpos, and the lift uses S_j as is: its input vector
+// is stored permuted by rowpos and its outputs are scattered by rowpos.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+
+#include "es_internal.h"
+
+namespace es {
+
+__constant__ PrimeTable c_pt = kPrimeTable;
+
+// ---------------------------------------------------------------- arithmetic
+
+// x mod q for x < 2^16 (Barrett with mu16 = floor(2^16/q)): the estimate
+// floor(x mu16 / 2^16) is floor(x/q) or one less, so one conditional
+// subtraction finishes; min(r, r - q) is that subtraction in unsigned form.
+__device__ __forceinline__ uint32_t red16(uint32_t x, uint32_t q, uint32_t mu16) {
+    uint32_t t = __umul24(x, mu16) >> 16;
+    uint32_t r = x - __umul24(t, q);
+    return min(r, r - q);
+}
+
+// x mod q for x < 2^32 (Barrett with mu32 = floor(2^32/q)).
+__device__ __forceinline__ uint32_t red32(uint32_t x, uint32_t q, uint32_t mu32) {
+    uint32_t t = __umulhi(x, mu32);
+    uint32_t r = x - t * q;
+    return min(r, r - q);
+}
+
+// u mod q for u < 2^64: fold the high word with r32 = 2^32 mod q.
+__device__ __forceinline__ uint32_t red64(uint64_t u, uint32_t q, uint32_t mu16, uint32_t mu32,
+                                          uint32_t r32) {
+    uint32_t h = red32((uint32_t)(u >> 32), q, mu32);
+    uint32_t l = red32((uint32_t)u, q, mu32);
+    return red16(h * r32 + l, q, mu16);  // <= (q-1)^2 + (q-1) < 2^16
+}
+
+// signed 64-bit value mod q in [0, q)
+__device__ __forceinline__ uint32_t mod_i64(int64_t a, uint32_t q, uint32_t mu16, uint32_t mu32,
+                                            uint32_t r32) {
+    uint64_t u = a < 0 ? (uint64_t)0 - (uint64_t)a : (uint64_t)a;
+    uint32_t r = red64(u, q, mu16, mu32, r32);
+    return (a < 0 && r) ? q - r : r;
+}
+
+// signed 32-bit value mod q in [0, q)
+__device__ __forceinline__ uint32_t mod_i32(int32_t a, uint32_t q, uint32_t mu32) {
+    uint32_t u = a < 0 ? (uint32_t)0 - (uint32_t)a : (uint32_t)a;
+    uint32_t r = red32(u, q, mu32);
+    return (a < 0 && r) ? q - r : r;
+}
+
+// balanced representative in [-(q-1)/2, (q-1)/2] of r in [0, q), q odd
+__device__ __forceinline__ int balanced(uint32_t r, uint32_t q) {
+    return r > (q >> 1) ? (int)r - (int)q : (int)r;
+}
+
+// a^-1 mod q by Fermat (a != 0 mod q, q prime)
+__device__ __forceinline__ uint32_t inv_mod(uint32_t a, uint32_t q, uint32_t mu16) {
+    uint32_t r = 1, b = a, e = q - 2;
+    while (e) {
+        if (e & 1) r = red16(r * b, q, mu16);
+        b = red16(b * b, q, mu16);
+        e >>= 1;
+    }
+    return r;
+}
+
+__device__ __forceinline__ void unpack16(const uint4 w, uint32_t (&x)[16]) {
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+#pragma unroll
+        for (int b = 0; b < 4; b++) x[4 * i + b] = (ws[i] >> (8 * b)) & 0xffu;
+    }
+}
+
+__device__ __forceinline__ uint4 pack16(const uint32_t (&x)[16]) {
+    uint32_t ws[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+        ws[i] = (x[4 * i] & 0xffu) | ((x[4 * i + 1] & 0xffu) << 8) | ((x[4 * i + 2] & 0xffu) << 16) |
+                ((x[4 * i + 3] & 0xffu) << 24);
+    return make_uint4(ws[0], ws[1], ws[2], ws[3]);
+}
+
+// ---------------------------------------------------------------- utility
+
+__global__ void fill_u32_kernel(uint32_t* __restrict__ p, size_t count, uint32_t value) {
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (; i < count; i += stride) p[i] = value;
+}
+
+hipError_t launch_fill_u32(uint32_t* p, size_t count, uint32_t value, hipStream_t st) {
+    if (count == 0) return hipSuccess;
+    size_t blocks = (count + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p, count, value);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- range check and norms
+// Feeds the range check n * max|A| < 2^63 (card, "Method") and the Hadamard
+// bounds that fix the step count.  Reductions run in a fixed order, so the
+// fp64 sums (and hence the step count) are reproducible.
+
+__global__ __launch_bounds__(256) void row_stats_kernel(const int64_t* __restrict__ A, int n,
+                                                        uint64_t* __restrict__ rowmax,
+                                                        double* __restrict__ rownorm) {
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= n) return;
+    uint64_t mx = 0;
+    double s = 0.0;
+    const int64_t* a = A + (size_t)row * n;
+    for (int j = lane; j < n; j += 64) {
+        int64_t v = a[j];
+        uint64_t u = v < 0 ? (uint64_t)0 - (uint64_t)v : (uint64_t)v;
+        mx = u > mx ? u : mx;
+        double f = (double)v;
+        s += f * f;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        uint64_t o = __shfl_xor(mx, off);
+        mx = o > mx ? o : mx;
+        s += __shfl_xor(s, off);
+    }
+    if (lane == 0) {
+        rowmax[row] = mx;
+        rownorm[row] = s;
+    }
+}
+
+// partial column sums of squares over a 64-row block
+__global__ __launch_bounds__(256) void col_part_kernel(const int64_t* __restrict__ M, int rows,
+                                                       int cols, double* __restrict__ part) {
+    const int col = blockIdx.x * 256 + threadIdx.x;
+    const int rb = blockIdx.y;
+    if (col >= cols) return;
+    const int r0 = rb * 64, r1 = min(rows, r0 + 64);
+    double s = 0.0;
+    for (int r = r0; r < r1; r++) {
+        double f = (double)M[(size_t)r * cols + col];
+        s += f * f;
+    }
+    part[(size_t)rb * cols + col] = s;
+}
+
+__global__ __launch_bounds__(256) void col_final_kernel(const double* __restrict__ part, int nrb,
+                                                        int cols, double* __restrict__ out) {
+    const int col = blockIdx.x * 256 + threadIdx.x;
+    if (col >= cols) return;
+    double s = 0.0;
+    for (int rb = 0; rb < nrb; rb++) s += part[(size_t)rb * cols + col];
+    out[col] = s;
+}
+
+hipError_t launch_stats(const int64_t* A, const int64_t* b, const Layout& L, uint8_t* ws,
+                        hipStream_t st) {
+    const int n = L.n, c = L.c, nrb = (n + 63) / 64;
+    hipLaunchKernelGGL(row_stats_kernel, dim3((n + 3) / 4), dim3(256), 0, st, A, n,
+                       (uint64_t*)(ws + L.off_rowmax), (double*)(ws + L.off_rownorm));
+    hipLaunchKernelGGL(col_part_kernel, dim3((n + 255) / 256, nrb), dim3(256), 0, st, A, n, n,
+                       (double*)(ws + L.off_colpart));
+    hipLaunchKernelGGL(col_final_kernel, dim3((n + 255) / 256), dim3(256), 0, st,
+                       (const double*)(ws + L.off_colpart), nrb, n, (double*)(ws + L.off_colnorm));
+    hipLaunchKernelGGL(col_part_kernel, dim3((c + 255) / 256, nrb), dim3(256), 0, st, b, n, c,
+                       (double*)(ws + L.off_bpart));
+    hipLaunchKernelGGL(col_final_kernel, dim3((c + 255) / 256), dim3(256), 0, st,
+                       (const double*)(ws + L.off_bpart), nrb, c, (double*)(ws + L.off_bnorm));
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- residues of A
+// S[j][i][col] = A[i][col] mod q_j for all 53 primes (zero in the pitch
+// padding); optionally an int32 copy of A for the residual update.
+template <bool SMALL>  // SMALL: every |A_ij| < 2^32
+__global__ __launch_bounds__(256) void residue_kernel(const int64_t* __restrict__ A, int n, int pitch,
+                                                      uint8_t* __restrict__ S,
+                                                      int32_t* __restrict__ A32, int make_a32) {
+    const int i = blockIdx.x;
+    const int col = (blockIdx.y * 256 + threadIdx.x) * 4;
+    if (col >= pitch) return;
+    uint64_t mag[4];
+    bool neg[4];
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+        int64_t a = (col + u < n) ? A[(size_t)i * n + col + u] : 0;
+        if (make_a32 && col + u < n) A32[(size_t)i * n + col + u] = (int32_t)a;
+        neg[u] = a < 0;
+        mag[u] = a < 0 ? (uint64_t)0 - (uint64_t)a : (uint64_t)a;
+    }
+    for (int j = 0; j < kNumPrimes; j++) {
+        const uint32_t q = c_pt.q[j], mu16 = c_pt.mu16[j], mu32 = c_pt.mu32[j], r32 = c_pt.r32[j];
+        uint32_t w = 0;
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            uint32_t r = SMALL ? red32((uint32_t)mag[u], q, mu32) : red64(mag[u], q, mu16, mu32, r32);
+            if (neg[u] && r) r = q - r;
+            w |= r << (8 * u);
+        }
+        *(uint32_t*)(S + ((size_t)j * n + i) * pitch + col) = w;
+    }
+}
+
+// first pivot (step 0) per prime: the lowest row with a nonzero residue in column 0
+__global__ __launch_bounds__(256) void pivot0_kernel(const uint8_t* __restrict__ S, int n, int pitch,
+                                                     int* __restrict__ piv) {
+    const int j = blockIdx.x;
+    __shared__ int smin;
+    if (threadIdx.x == 0) smin = INT_MAX;
+    __syncthreads();
+    int cand = INT_MAX;
+    for (int i = threadIdx.x; i < n; i += 256)
+        if (S[((size_t)j * n + i) * pitch] != 0) {
+            cand = i;
+            break;
+        }
+    if (cand != INT_MAX) atomicMin(&smin, cand);
+    __syncthreads();
+    if (threadIdx.x == 0) piv[(size_t)j * (n + 1)] = smin;
+}
+
+hipError_t launch_residues(const int64_t* A, const Layout& L, uint8_t* ws, bool make_a32,
+                           hipStream_t st) {
+    // caller guarantees small (< 2^32) entries whenever make_a32 is set
+    dim3 grid(L.n, (L.pitch / 4 + 255) / 256);
+    if (make_a32)
+        hipLaunchKernelGGL(residue_kernel<true>, grid, dim3(256), 0, st, A, L.n, L.pitch,
+                           ws + L.off_S, (int32_t*)(ws + L.off_A32), 1);
+    else
+        hipLaunchKernelGGL(residue_kernel<false>, grid, dim3(256), 0, st, A, L.n, L.pitch,
+                           ws + L.off_S, (int32_t*)(ws + L.off_A32), 0);
+    hipLaunchKernelGGL(pivot0_kernel, dim3(kNumPrimes), dim3(256), 0, st,
+                       (const uint8_t*)(ws + L.off_S), L.n, L.pitch, (int*)(ws + L.off_piv));
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- Gauss-Jordan step
+// One launch per elimination step k, grid (row tiles, 53 primes).  With the
+// pivot row p = piv[j][k] (chosen by the previous launch) scaled to
+// v = S[p] * inv(S[p][k]) and v[k] = inv(S[p][k]), every other row becomes
+// S[i] <- S[i] with slot k cleared, plus (q - S[i][k]) * v, mod q.  The
+// pivot row itself is not written back here (other blocks are still reading
+// it): its scaled form goes to a side buffer, and its owner folds it back
+// into S as an ordinary row in the next launch.  While updating, each block
+// records the lowest not-yet-pivoted row with a nonzero entry in column
+// k + 1, which becomes the next pivot (atomicMin), so no separate pivot
+// search is launched.  A prime with no pivot is singular mod q_j: its flag
+// is set and all of its later launches exit at once.  The last step writes
+// balanced int8 residues, the operand format of the lift.
+template <int LPR, int RI>
+__global__ __launch_bounds__(256) void gj_step_kernel(uint8_t* __restrict__ S, int n, int pitch,
+                                                      int k, int* __restrict__ piv,
+                                                      int* __restrict__ rowpos,
+                                                      uint8_t* __restrict__ pend,
+                                                      int* __restrict__ flags) {
+    constexpr int RPW = 64 / LPR;           // rows per wave and pass
+    constexpr int ROWS = 4 * RPW * RI;      // rows per block
+    const int j = blockIdx.y;
+    int* pj = piv + (size_t)j * (n + 1);
+    const int p = pj[k];
+    if (p == INT_MAX) {
+        if (blockIdx.x == 0 && threadIdx.x == 0) flags[j] = 1;
+        return;
+    }
+    const bool last = (k == n - 1);
+    const uint32_t q = c_pt.q[j], mu = c_pt.mu16[j];
+    uint8_t* Sj = S + (size_t)j * n * pitch;
+    int* rpj = rowpos + (size_t)j * n;
+    const int pprev = k > 0 ? pj[k - 1] : -1;
+    const uint8_t* pend_prev = pend + ((size_t)((k + 1) & 1) * kNumPrimes + j) * pitch;
+    uint8_t* pend_cur = pend + ((size_t)(k & 1) * kNumPrimes + j) * pitch;
+    const uint32_t pinv = inv_mod(Sj[(size_t)p * pitch + k], q, mu);
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane / LPR, cl = lane % LPR;
+    const int npass = (LPR == 64) ? (pitch + 1023) >> 10 : 1;
+    const int row0 = blockIdx.x * ROWS;
+    int cand = INT_MAX;
+
+    // Column k of every row this thread updates, read once before any pass
+    // writes (with two or more column passes, an earlier pass overwrites it).
+    uint32_t fneg[RI];
+    const uint8_t* srcs[RI];
+#pragma unroll
+    for (int r = 0; r < RI; r++) {
+        const int i = row0 + wave * RPW + g + r * 4 * RPW;
+        fneg[r] = 0;
+        srcs[r] = nullptr;
+        if (i < n && i != p) {
+            srcs[r] = (i == pprev) ? pend_prev : Sj + (size_t)i * pitch;
+            const uint32_t f = srcs[r][k];
+            fneg[r] = f ? q - f : 0;
+        }
+    }
+
+    for (int pass = 0; pass < npass; ++pass) {
+        const int col0 = pass * 1024 + cl * 16;
+        const bool active = col0 < pitch;
+        uint32_t v[16];
+        {
+            uint4 raw = active ? *(const uint4*)(Sj + (size_t)p * pitch + col0) : make_uint4(0, 0, 0, 0);
+            unpack16(raw, v);
+#pragma unroll
+            for (int b = 0; b < 16; b++) v[b] = (col0 + b == k) ? pinv : red16(v[b] * pinv, q, mu);
+        }
+        // load all of this thread's rows first, then update them
+        uint4 s[RI];
+#pragma unroll
+        for (int r = 0; r < RI; r++)
+            s[r] = (srcs[r] && active) ? *(const uint4*)(srcs[r] + col0) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < RI; r++) {
+            const int i = row0 + wave * RPW + g + r * 4 * RPW;
+            if (i >= n || !active) continue;
+            uint32_t x[16];
+            if (i == p) {
+#pragma unroll
+                for (int b = 0; b < 16; b++) x[b] = last ? (uint32_t)balanced(v[b], q) : v[b];
+                *(uint4*)(pend_cur + col0) = pack16(x);
+                continue;
+            }
+            unpack16(s[r], x);
+            bool nz_next = false;
+#pragma unroll
+            for (int b = 0; b < 16; b++) {
+                const uint32_t sb = (col0 + b == k) ? 0u : x[b];
+                uint32_t y = red16(sb + __umul24(fneg[r], v[b]), q, mu);
+                if (col0 + b == k + 1) nz_next = y != 0;
+                x[b] = last ? (uint32_t)balanced(y, q) : y;
+            }
+            if (!last && nz_next && rpj[i] < 0) cand = min(cand, i);
+            *(uint4*)(Sj + (size_t)i * pitch + col0) = pack16(x);
+        }
+    }
+    if (threadIdx.x == 0 && p >= row0 && p < row0 + ROWS) rpj[p] = k;
+    if (!last) {
+        __shared__ int smin;
+        if (threadIdx.x == 0) smin = INT_MAX;
+        __syncthreads();
+        if (cand != INT_MAX) atomicMin(&smin, cand);
+        __syncthreads();
+        if (threadIdx.x == 0 && smin != INT_MAX) atomicMin(&pj[k + 1], smin);
+    }
+}
+
+// After the last step: fold each prime's final pivot row back into S.
+__global__ __launch_bounds__(256) void gj_finalize_kernel(uint8_t* __restrict__ S, int n, int pitch,
+                                                          const int* __restrict__ piv,
+                                                          const uint8_t* __restrict__ pend) {
+    const int j = blockIdx.x;
+    const int p = piv[(size_t)j * (n + 1) + n - 1];
+    if (p == INT_MAX) return;
+    const uint8_t* src = pend + ((size_t)((n - 1) & 1) * kNumPrimes + j) * pitch;
+    uint8_t* dst = S + ((size_t)j * n + p) * pitch;
+    for (int col = threadIdx.x * 4; col < pitch; col += 1024)
+        *(uint32_t*)(dst + col) = *(const uint32_t*)(src + col);
+}
+
+template <int LPR, int RI>
+static void launch_gj_t(const Layout& L, uint8_t* ws, int k, hipStream_t st) {
+    constexpr int ROWS = 4 * (64 / LPR) * RI;
+    dim3 grid((L.n + ROWS - 1) / ROWS, kNumPrimes);
+    hipLaunchKernelGGL((gj_step_kernel<LPR, RI>), grid, dim3(256), 0, st, ws + L.off_S, L.n, L.pitch,
+                       k, (int*)(ws + L.off_piv), (int*)(ws + L.off_rowpos), ws + L.off_pend,
+                       (int*)(ws + L.off_flags));
+}
+
+hipError_t launch_gj_step(const Layout& L, uint8_t* ws, int k, hipStream_t st) {
+    switch (L.lpr) {
+        case 4: launch_gj_t<4, 1>(L, ws, k, st); break;
+        case 8: launch_gj_t<8, 1>(L, ws, k, st); break;
+        case 16: launch_gj_t<16, 2>(L, ws, k, st); break;
+        case 32: launch_gj_t<32, 4>(L, ws, k, st); break;
+        default: launch_gj_t<64, 4>(L, ws, k, st); break;
+    }
+    if (k == L.n - 1)
+        hipLaunchKernelGGL(gj_finalize_kernel, dim3(kNumPrimes), dim3(256), 0, st, ws + L.off_S, L.n,
+                           L.pitch, (const int*)(ws + L.off_piv), (const uint8_t*)(ws + L.off_pend));
+    return hipGetLastError();
+}
+
+// B[j][k][col] = A^-1 mod q_j (balanced int8): row piv[j][k] of S, slot rowpos[j][col]
+__global__ __launch_bounds__(256) void export_inverse_kernel(const int8_t* __restrict__ S, int n, int pitch,
+                                                             const int* __restrict__ piv,
+                                                             const int* __restrict__ rowpos,
+                                                             const int* __restrict__ flags,
+                                                             int8_t* __restrict__ B) {
+    const int k = blockIdx.x, j = blockIdx.y;
+    if (flags[j]) return;
+    const int p = piv[(size_t)j * (n + 1) + k];
+    const int8_t* src = S + ((size_t)j * n + p) * pitch;
+    const int* rp = rowpos + (size_t)j * n;
+    int8_t* dst = B + ((size_t)j * n + k) * n;
+    for (int col = threadIdx.x; col < n; col += 256) dst[col] = src[rp[col]];
+}
+
+hipError_t launch_export_inverse(const Layout& L, const uint8_t* ws, int8_t* B, hipStream_t st) {
+    hipLaunchKernelGGL(export_inverse_kernel, dim3(L.n, kNumPrimes), dim3(256), 0, st,
+                       (const int8_t*)(ws + L.off_S), L.n, L.pitch, (const int*)(ws + L.off_piv),
+                       (const int*)(ws + L.off_rowpos), (const int*)(ws + L.off_flags), B);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- lift: contraction
+// y_j = B_j rho_j for every live prime, int8 x int8 -> int32 with the 4-way
+// dot product (v_dot4_i32_i8); u_j = y_j mod q_j is scattered to component
+// order through rowpos.  Grid (row tiles, live primes); a lane covers 16
+// columns of a row and CT right-hand sides at once.
+template <int LPR, int RI, int CT>
+__global__ __launch_bounds__(256) void lift_gemv_kernel(const int8_t* __restrict__ S, int n, int pitch,
+                                                        int c, const int8_t* __restrict__ rho,
+                                                        const LiftParams* __restrict__ prm,
+                                                        const int* __restrict__ rowpos,
+                                                        uint8_t* __restrict__ U) {
+    constexpr int RPW = 64 / LPR;
+    constexpr int ROWS = 4 * RPW * RI;
+    const int jl = blockIdx.y;
+    const int J = prm->qidx[jl];
+    const uint32_t q = prm->q[jl], mu32 = prm->mu32[jl];
+    const int8_t* Sj = S + (size_t)J * n * pitch;
+    const int8_t* rj = rho + (size_t)jl * c * pitch;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane / LPR, cl = lane % LPR;
+    const int npass = (LPR == 64) ? (pitch + 1023) >> 10 : 1;
+    const int row0 = blockIdx.x * ROWS;
+    const size_t NC = (size_t)n * c;
+
+    for (int t0 = 0; t0 < c; t0 += CT) {
+        int acc[RI][CT];
+#pragma unroll
+        for (int r = 0; r < RI; r++)
+#pragma unroll
+            for (int t = 0; t < CT; t++) acc[r][t] = 0;
+        for (int pass = 0; pass < npass; ++pass) {
+            const int col0 = pass * 1024 + cl * 16;
+            const bool active = col0 < pitch;
+            uint4 rv[CT];
+#pragma unroll
+            for (int t = 0; t < CT; t++)
+                rv[t] = (active && t0 + t < c) ? *(const uint4*)(rj + (size_t)(t0 + t) * pitch + col0)
+                                               : make_uint4(0, 0, 0, 0);
+            uint4 s[RI];
+#pragma unroll
+            for (int r = 0; r < RI; r++) {
+                const int i = row0 + wave * RPW + g + r * 4 * RPW;
+                s[r] = (active && i < n) ? *(const uint4*)(Sj + (size_t)i * pitch + col0)
+                                         : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int r = 0; r < RI; r++)
+#pragma unroll
+                for (int t = 0; t < CT; t++) {
+                    int a = acc[r][t];
+                    a = __builtin_amdgcn_sdot4((int)s[r].x, (int)rv[t].x, a, false);
+                    a = __builtin_amdgcn_sdot4((int)s[r].y, (int)rv[t].y, a, false);
+                    a = __builtin_amdgcn_sdot4((int)s[r].z, (int)rv[t].z, a, false);
+                    a = __builtin_amdgcn_sdot4((int)s[r].w, (int)rv[t].w, a, false);
+                    acc[r][t] = a;
+                }
+        }
+#pragma unroll
+        for (int r = 0; r < RI; r++)
+#pragma unroll
+            for (int t = 0; t < CT; t++)
+#pragma unroll
+                for (int off = LPR / 2; off > 0; off >>= 1) acc[r][t] += __shfl_xor(acc[r][t], off);
+        if (cl == 0) {
+#pragma unroll
+            for (int r = 0; r < RI; r++) {
+                const int i = row0 + wave * RPW + g + r * 4 * RPW;
+                if (i >= n) continue;
+                const size_t kdst = (size_t)rowpos[(size_t)J * n + i] * c;
+#pragma unroll
+                for (int t = 0; t < CT; t++)
+                    if (t0 + t < c) U[(size_t)jl * NC + kdst + t0 + t] = (uint8_t)mod_i32(acc[r][t], q, mu32);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- lift: balanced Garner
+// One wave per component, lane l holds the residue for live prime l.
+// Mixed-radix digits v_l (balanced, so x = sum v_l Q_l lies in
+// [-(P-1)/2, (P-1)/2], Q_l = q_0 ... q_{l-1}) come out one per iteration: v_l
+// is read from lane l, then every lane k > l replaces its value t_k by
+// (t_k - v_l) q_l^-1 mod q_k.  Lanes 0..11 accumulate word w of
+// sum (v_l + 128) Q_l (nonnegative factors for the unsigned multiply-add)
+// and subtract 128 sum Q_l at the end; a carry pass turns the 12 words into
+// the 384-bit two's-complement digit.  x mod 2^64 is kept for the residual.
+__global__ __launch_bounds__(256) void garner_wave_kernel(const LiftParams* __restrict__ prm,
+                                                          const uint8_t* __restrict__ U, int NC,
+                                                          uint64_t* __restrict__ digits, int kchunk,
+                                                          int slot, uint64_t* __restrict__ xlow) {
+    const int lane = threadIdx.x & 63;
+    const int comp = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (comp >= NC) return;
+    const int E = prm->E;
+    const bool live = lane < E;
+    const uint32_t qk = live ? prm->q[lane] : 1u;
+    const uint32_t muk = live ? prm->mu16[lane] : 0u;
+    uint32_t t = live ? U[(size_t)lane * NC + comp] : 0u;
+    uint64_t acc = 0;
+#pragma unroll
+    for (int l = 0; l < kNumPrimes; ++l) {
+        if (l < E) {
+            const uint32_t ql = prm->q[l];
+            int vl = __builtin_amdgcn_readlane((int)t, l);
+            vl = vl > (int)(ql >> 1) ? vl - (int)ql : vl;
+            if (lane > l && live) {
+                int d = (int)t - vl;  // in (-q_k/2, 3q_k/2) since |v_l| < q_l/2 < q_k/2
+                d = d < 0 ? d + (int)qk : d;
+                d = d >= (int)qk ? d - (int)qk : d;
+                t = red16(__umul24((uint32_t)d, (uint32_t)prm->ginv[l][lane]), qk, muk);
+            }
+            if (lane < kDigitWords) acc += (uint64_t)(uint32_t)(vl + 128) * (uint64_t)prm->Qw[l][lane];
+        }
+    }
+    if (lane < kDigitWords) acc -= prm->corr[lane];
+    const uint32_t alo = (uint32_t)acc, ahi = (uint32_t)(acc >> 32);
+    int64_t carry = 0;
+    uint32_t word = 0, word1 = 0;
+#pragma unroll
+    for (int w = 0; w < kDigitWords; ++w) {
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)alo, w);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)ahi, w);
+        const int64_t s = (int64_t)(((uint64_t)hi << 32) | lo) + carry;
+        if (lane == w) word = (uint32_t)s;
+        if (w == 1) word1 = (uint32_t)s;
+        carry = s >> 32;
+    }
+    uint32_t* dst = (uint32_t*)(digits + ((size_t)comp * kchunk + slot) * kDigitLimbs);
+    if (lane < kDigitWords) dst[lane] = word;
+    if (lane == 0) xlow[comp] = ((uint64_t)word1 << 32) | word;
+}
+
+// ---------------------------------------------------------------- lift: residual
+// r <- (r - A x_low) P^-1 mod 2^64, one wave per row.  The true quotient lies
+// in (-2^63, 2^63) (card, "Method": the residual stays one signed 64-bit limb
+// when n max|A| < 2^63), so the wrapped product read as int64 is exact.
+// The new residual is split at once into the next step's balanced residues,
+// stored permuted by rowpos.  With first != 0 only the split of r = b runs.
+template <typename AT, int CT>
+__global__ __launch_bounds__(256) void residual_kernel(const AT* __restrict__ A, int n, int c,
+                                                       int64_t* __restrict__ R,
+                                                       const uint64_t* __restrict__ xlow,
+                                                       const LiftParams* __restrict__ prm,
+                                                       const int* __restrict__ rowpos,
+                                                       int8_t* __restrict__ rho, int pitch, int first) {
+    const int lane = threadIdx.x & 63;
+    const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= n) return;
+    const int E = prm->E;
+    const uint64_t Pinv = prm->Pinv;
+    uint32_t q = 1, mu16 = 0, mu32 = 0, r32 = 0;
+    int pos = 0;
+    if (lane < E) {
+        q = prm->q[lane];
+        mu16 = prm->mu16[lane];
+        mu32 = prm->mu32[lane];
+        r32 = prm->r32[lane];
+        pos = rowpos[(size_t)prm->qidx[lane] * n + r];
+    }
+    for (int t0 = 0; t0 < c; t0 += CT) {
+        uint64_t acc[CT];
+#pragma unroll
+        for (int t = 0; t < CT; t++) acc[t] = 0;
+        if (!first) {
+            const AT* a = A + (size_t)r * n;
+            for (int jc = lane; jc < n; jc += 64) {
+                const uint64_t av = (uint64_t)(int64_t)a[jc];
+                const uint64_t* xr = xlow + (size_t)jc * c + t0;
+#pragma unroll
+                for (int t = 0; t < CT; t++)
+                    if (t0 + t < c) acc[t] += av * xr[t];
+            }
+#pragma unroll
+            for (int t = 0; t < CT; t++)
+#pragma unroll
+                for (int off = 32; off > 0; off >>= 1) acc[t] += __shfl_xor(acc[t], off);
+        }
+#pragma unroll
+        for (int t = 0; t < CT; t++) {
+            if (t0 + t >= c) continue;
+            int64_t* rp = R + (size_t)r * c + t0 + t;
+            const uint64_t old = (uint64_t)*rp;
+            const uint64_t val = first ? old : (old - acc[t]) * Pinv;
+            if (!first && lane == 0) *rp = (int64_t)val;
+            if (lane < E) {
+                const uint32_t res = mod_i64((int64_t)val, q, mu16, mu32, r32);
+                rho[((size_t)lane * c + t0 + t) * pitch + pos] = (int8_t)balanced(res, q);
+            }
+        }
+    }
+}
+
+hipError_t launch_split_b(const int64_t* b, const Layout& L, uint8_t* ws, int E, hipStream_t st) {
+    (void)E;
+    hipError_t e = hipMemcpyAsync(ws + L.off_R, b, (size_t)L.n * L.c * sizeof(int64_t),
+                                  hipMemcpyDeviceToDevice, st);
+    if (e != hipSuccess) return e;
+    const dim3 grid((L.n + 3) / 4);
+    if (L.c == 1)
+        hipLaunchKernelGGL((residual_kernel<int64_t, 1>), grid, dim3(256), 0, st, (const int64_t*)nullptr,
+                           L.n, L.c, (int64_t*)(ws + L.off_R), (const uint64_t*)(ws + L.off_xlow),
+                           (const LiftParams*)(ws + L.off_params), (const int*)(ws + L.off_rowpos),
+                           (int8_t*)(ws + L.off_rho), L.pitch, 1);
+    else
+        hipLaunchKernelGGL((residual_kernel<int64_t, 16>), grid, dim3(256), 0, st, (const int64_t*)nullptr,
+                           L.n, L.c, (int64_t*)(ws + L.off_R), (const uint64_t*)(ws + L.off_xlow),
+                           (const LiftParams*)(ws + L.off_params), (const int*)(ws + L.off_rowpos),
+                           (int8_t*)(ws + L.off_rho), L.pitch, 1);
+    return hipGetLastError();
+}
+
+template <int LPR, int RI, int CT>
+static void launch_gemv_t(const Layout& L, uint8_t* ws, int E, hipStream_t st) {
+    constexpr int ROWS = 4 * (64 / LPR) * RI;
+    dim3 grid((L.n + ROWS - 1) / ROWS, E);
+    hipLaunchKernelGGL((lift_gemv_kernel<LPR, RI, CT>), grid, dim3(256), 0, st,
+                       (const int8_t*)(ws + L.off_S), L.n, L.pitch, L.c, (const int8_t*)(ws + L.off_rho),
+                       (const LiftParams*)(ws + L.off_params), (const int*)(ws + L.off_rowpos),
+                       ws + L.off_U);
+}
+
+template <int CT>
+static void launch_gemv_c(const Layout& L, uint8_t* ws, int E, hipStream_t st) {
+    switch (L.lpr) {
+        case 4: launch_gemv_t<4, 1, CT>(L, ws, E, st); break;
+        case 8: launch_gemv_t<8, 1, CT>(L, ws, E, st); break;
+        case 16: launch_gemv_t<16, 2, CT>(L, ws, E, st); break;
+        case 32: launch_gemv_t<32, 4, CT>(L, ws, E, st); break;
+        default: launch_gemv_t<64, (CT == 1 ? 8 : 4), CT>(L, ws, E, st); break;
+    }
+}
+
+hipError_t launch_lift_step(const Layout& L, uint8_t* ws, int E, bool a32, const int64_t* A64, int slot,
+                            hipStream_t st) {
+    if (L.c == 1)
+        launch_gemv_c<1>(L, ws, E, st);
+    else
+        launch_gemv_c<16>(L, ws, E, st);
+    const int NC = L.n * L.c;
+    hipLaunchKernelGGL(garner_wave_kernel, dim3((NC + 3) / 4), dim3(256), 0, st,
+                       (const LiftParams*)(ws + L.off_params), (const uint8_t*)(ws + L.off_U), NC,
+                       (uint64_t*)(ws + L.off_digits), L.kchunk, slot, (uint64_t*)(ws + L.off_xlow));
+    const dim3 grid((L.n + 3) / 4);
+    const LiftParams* prm = (const LiftParams*)(ws + L.off_params);
+    int64_t* R = (int64_t*)(ws + L.off_R);
+    const uint64_t* xl = (const uint64_t*)(ws + L.off_xlow);
+    const int* rp = (const int*)(ws + L.off_rowpos);
+    int8_t* rho = (int8_t*)(ws + L.off_rho);
+    if (a32) {
+        const int32_t* A = (const int32_t*)(ws + L.off_A32);
+        if (L.c == 1)
+            hipLaunchKernelGGL((residual_kernel<int32_t, 1>), grid, dim3(256), 0, st, A, L.n, L.c, R, xl, prm,
+                               rp, rho, L.pitch, 0);
+        else
+            hipLaunchKernelGGL((residual_kernel<int32_t, 16>), grid, dim3(256), 0, st, A, L.n, L.c, R, xl,
+                               prm, rp, rho, L.pitch, 0);
+    } else {
+        if (L.c == 1)
+            hipLaunchKernelGGL((residual_kernel<int64_t, 1>), grid, dim3(256), 0, st, A64, L.n, L.c, R, xl,
+                               prm, rp, rho, L.pitch, 0);
+        else
+            hipLaunchKernelGGL((residual_kernel<int64_t, 16>), grid, dim3(256), 0, st, A64, L.n, L.c, R, xl,
+                               prm, rp, rho, L.pitch, 0);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace es

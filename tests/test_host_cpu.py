@@ -1,0 +1,251 @@
+"""CPU tests of the HIP library's host side (no GPU needed).
+
+* every function declared in include/*.h is exported by libexact_solve.so;
+* the host big-integer routines agree with Python integers;
+* Wang reconstruction agrees with the oracle's;
+* the host reconstruction stage (es_reconstruct), fed with the oracle's own
+  Dixon digits, returns exactly the oracle's Bareiss solution.
+"""
+import ctypes
+import glob
+import math
+import os
+import random
+import re
+
+import numpy as np
+import pytest
+
+from dixon_adic_lifting_amd import _lib
+from dixon_adic_lifting_amd import workloads as W
+import dixon_adic_lifting_amd as es
+from oracle import dixon, exact, modular
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def lib():
+    return _lib.load()
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"\b(es_\w+)\s*\(", text):
+            names.add(m.group(1))
+    return sorted(names)
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert "es_solve_device" in names and "es_batched_inverse" in names
+    L = ctypes.CDLL(_lib.LIB_PATH)
+    for name in names:
+        assert hasattr(L, name), name
+    assert set(_lib.EXPORTS) <= set(names)
+
+
+def test_workspace_bytes_limits():
+    assert es.workspace_bytes(0, 1) == 0
+    assert es.workspace_bytes(1, 0) == 0
+    assert es.workspace_bytes((1 << 17) + 1, 1) == 0
+    assert es.workspace_bytes(1, 1) > 0
+    assert es.workspace_bytes(1024, 1) < es.workspace_bytes(2048, 16)
+
+
+def test_primes_and_strerror():
+    assert es.primes() == modular.odd_primes_below(256)
+    for st in (0, 1, -1, -2, -3, -4, -5, -6):
+        assert _lib.strerror(st)
+
+
+# ------------------------------------------------------------------ bignum
+
+def to_limbs(v):
+    v = abs(v)
+    out = []
+    while v:
+        out.append(v & ((1 << 64) - 1))
+        v >>= 64
+    return out
+
+
+def arr(limbs):
+    a = (ctypes.c_uint64 * max(1, len(limbs)))(*limbs)
+    return a, len(limbs)
+
+
+def from_limbs(buf, n, neg=0):
+    v = 0
+    for i in range(n - 1, -1, -1):
+        v = (v << 64) | buf[i]
+    return -v if neg else v
+
+
+def dbg(op, a, b, cap=8192):
+    L = ctypes.CDLL(_lib.LIB_PATH)
+    f = L.es_dbg_bignum
+    pa, la = arr(to_limbs(a))
+    pb, lb = arr(to_limbs(b))
+    r1 = (ctypes.c_uint64 * cap)()
+    r2 = (ctypes.c_uint64 * cap)()
+    l1, l2, n1, n2 = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int(), ctypes.c_int()
+    st = f(op, pa, la, int(a < 0), pb, lb, int(b < 0), r1, ctypes.byref(l1), ctypes.byref(n1),
+           r2, ctypes.byref(l2), ctypes.byref(n2), cap)
+    assert st == 0
+    return from_limbs(r1, l1.value, n1.value), from_limbs(r2, l2.value, n2.value)
+
+
+def rand_int(rng, limbs, signed=True):
+    v = rng.getrandbits(64 * limbs) if limbs else 0
+    # sprinkle in all-ones limbs to stress carries
+    if limbs and rng.random() < 0.3:
+        v |= ((1 << 64) - 1) << (64 * rng.randrange(limbs))
+    return -v if signed and rng.random() < 0.5 else v
+
+
+SIZES = [0, 1, 2, 3, 7, 39, 40, 41, 64, 100, 257, 700]
+
+
+@pytest.mark.parametrize("la", SIZES)
+def test_bignum_mul(la):
+    rng = random.Random(la)
+    for lb in [0, 1, 5, 40, 41, 80, 300, 700]:
+        a, b = rand_int(rng, la), rand_int(rng, lb)
+        assert dbg(0, a, b)[0] == a * b
+
+
+@pytest.mark.parametrize("la", [1, 2, 5, 40, 90, 400, 1000])
+def test_bignum_divmod(la):
+    rng = random.Random(100 + la)
+    for lb in [1, 2, 3, 17, 64, 200, 500]:
+        a, b = rand_int(rng, la), rand_int(rng, lb)
+        if b == 0:
+            continue
+        q, r = dbg(1, a, b)
+        tq = abs(a) // abs(b) * (1 if (a < 0) == (b < 0) else -1)
+        assert q == tq and r == a - tq * b
+    # quotient digit edge cases: divisor with top limb all ones, dividend = k*b - 1
+    b = ((1 << 64) - 1) << 128 | 12345
+    for k in [1, 2, (1 << 64) - 1, 1 << 70]:
+        a = k * b - 1
+        q, r = dbg(1, a, b)
+        assert (q, r) == (a // b, a % b)
+
+
+def test_bignum_gcd():
+    rng = random.Random(5)
+    for la, lb in [(1, 1), (2, 1), (5, 5), (50, 48), (400, 400), (437, 300)]:
+        g = rand_int(rng, rng.randrange(1, 4), signed=False) | 1
+        a, b = rand_int(rng, la) * g, rand_int(rng, lb) * g
+        assert dbg(2, a, b)[0] == math.gcd(a, b)
+    assert dbg(2, 0, 0)[0] == 0
+    assert dbg(2, 12, 0)[0] == 12
+    fib = [1, 1]
+    while len(fib) < 3000:
+        fib.append(fib[-1] + fib[-2])
+    assert dbg(2, fib[-1], fib[-2])[0] == 1   # worst case for Euclid
+
+
+def test_bignum_add_sub():
+    rng = random.Random(9)
+    for _ in range(200):
+        a, b = rand_int(rng, rng.randrange(0, 9)), rand_int(rng, rng.randrange(0, 9))
+        assert dbg(3, a, b)[0] == a + b
+        assert dbg(4, a, b)[0] == a - b
+
+
+def ratrec(a, M, N, D, cap=4096):
+    L = ctypes.CDLL(_lib.LIB_PATH)
+    args = []
+    keep = []
+    for v in (a, M, N, D):
+        p, ln = arr(to_limbs(v))
+        keep.append(p)
+        args += [p, ln]
+    num = (ctypes.c_uint64 * cap)()
+    den = (ctypes.c_uint64 * cap)()
+    ln_, ld_, nn = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int()
+    st = L.es_dbg_ratrec(*args, num, ctypes.byref(ln_), ctypes.byref(nn), den, ctypes.byref(ld_), cap)
+    assert st in (0, 1)
+    if st == 1:
+        return None
+    return from_limbs(num, ln_.value, nn.value), from_limbs(den, ld_.value)
+
+
+def test_ratrec_matches_oracle():
+    rng = random.Random(3)
+    P = math.prod(modular.odd_primes_below(256))
+    for k in [1, 2, 8, 40]:
+        M = P ** k
+        half = (M.bit_length() - 2) // 2
+        for _ in range(12):
+            den = rng.randrange(1, 1 << half)
+            num = rng.randrange(-(1 << half), 1 << half)
+            if math.gcd(den, M) != 1:
+                continue
+            a = num * pow(den, -1, M) % M
+            expect = dixon.rational_reconstruct(a, M, 1 << half, 1 << half)
+            assert ratrec(a, M, 1 << half, 1 << half) == expect
+        # a random residue usually has no small fraction
+        a = rng.randrange(M)
+        assert ratrec(a, M, 1 << half, 1 << half) == dixon.rational_reconstruct(a, M, 1 << half, 1 << half)
+
+
+# ------------------------------------------------------------------ reconstruction stage
+
+def digits_to_words(digits):
+    """oracle digits [m][n][c] (Python ints) -> int64 [n*c][m][6] two's complement."""
+    m, n, c = len(digits), len(digits[0]), len(digits[0][0])
+    out = np.zeros((n * c, m, 6), dtype=np.uint64)
+    for i in range(m):
+        for r in range(n):
+            for t in range(c):
+                v = digits[i][r][t] % (1 << 384)
+                for w in range(6):
+                    out[r * c + t, i, w] = (v >> (64 * w)) & ((1 << 64) - 1)
+    return out.view(np.int64)
+
+
+def oracle_case(A, b, primes):
+    live, invs = dixon.surviving_primes(A, primes)
+    P = math.prod(live)
+    N, D = dixon.hadamard_bounds(A, b)
+    nbits, dbits = max(1, N.bit_length()), max(1, D.bit_length())
+    m = dixon.step_count(P, 1 << nbits, 1 << dbits)
+    digits, _ = dixon.padic_digits(A, b, live, m, B=dixon.crt_matrix(invs, live))
+    mask = sum(1 << primes.index(q) for q in live)
+    return digits_to_words(digits), mask, nbits, dbits
+
+
+@pytest.mark.parametrize("case", ["c1_n32_int8", "c2_pascal30", "uniform", "hilbert", "planted", "zero_b",
+                                  "int64_extremes"])
+def test_reconstruct_matches_oracle(case, primes):
+    if case.startswith("c"):
+        A, b = W.generate(case)
+    elif case == "uniform":
+        A, b = W.uniform_system(24, 3, 24, 17)
+    elif case == "hilbert":
+        A, _ = W.scaled_hilbert(8)
+        b = np.arange(16, dtype=np.int64).reshape(8, 2) - 7
+    elif case == "planted":
+        A, b, _ = W.planted_system(20, 2, 12, 16, 4)
+    elif case == "zero_b":
+        A, _ = W.uniform_system(9, 1, 16, 2)
+        b = np.zeros((9, 2), dtype=np.int64)
+    else:
+        A = np.array([[3, (1 << 61)], [-(1 << 61), 5]], dtype=np.int64)
+        b = np.array([[-(1 << 63)], [(1 << 63) - 1]], dtype=np.int64)
+    n, c = A.shape[0], b.shape[1]
+    words, mask, nbits, dbits = oracle_case(A, b, primes)
+    got = es.reconstruct(words, n, c, mask, nbits, dbits, threads=3)
+    assert got == exact.solve(A, b)
+
+
+def test_reconstruct_rejects_short_precision(primes):
+    A, b = W.uniform_system(6, 1, 16, 1)
+    words, mask, nbits, dbits = oracle_case(A, b, primes)
+    with pytest.raises(ValueError):
+        es.reconstruct(words[:, :1], 6, 1, mask, nbits + 400, dbits + 400)
