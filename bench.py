@@ -1,0 +1,341 @@
+"""Benchmark: full exact solve of the n = 1024, c = 1, 24-bit system on one MI355X.
+
+A step is one full solve through the C ABI (es_solve_device): inputs already
+resident in HBM, output as host limbs (numerators and denominators in lowest
+terms) -- the checks, residues, batched Gauss-Jordan inverse, the lift, the
+digit copy and the host reconstruction.  W warm-up steps, then K timed steps
+bracketed by device synchronisation.  One JSON line goes to stdout.
+
+Extra passes (outside the timed region): one profiled solve with HIP events
+around every hot-kernel launch gives each kernel's average launch duration,
+from which the roofline fractions are computed; the benched output is checked
+against the oracle's stored digest; and the CPU oracle (plain-C Bareiss) is
+timed on a bounded sample of the same workload (its first elimination steps)
+and projected to a full solve.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, TOP/s
+PAGES_MS_C4 = {"rtx_pro_6000": 2411.0, "h200": 2235.0}   # card, "Measured" table, n=1024 c=1
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="c4_n1024_int24")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=12.0,
+                    help="approximate CPU seconds for the bounded oracle sample")
+    ap.add_argument("--copy-calib-mb", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--sweep", action="store_true", help="time every workload and print a table")
+    return ap.parse_args()
+
+
+def digest(pairs):
+    def h(v):
+        return ("-" + format(-v, "x")) if v < 0 else format(v, "x")
+    return hashlib.sha256("".join(f"{h(p)} {h(q)}\n" for row in pairs for (p, q) in row).encode()).hexdigest()
+
+
+class Solver:
+    """Raw C-ABI solve on torch-allocated device memory and the current stream."""
+
+    def __init__(self, A, b):
+        import torch
+        import dixon_adic_lifting_amd as es
+        from dixon_adic_lifting_amd import _lib
+        self.torch, self.es, self._lib = torch, es, _lib
+        self.lib = _lib.load()
+        self.dev = torch.device("cuda", 0)
+        self.A = torch.as_tensor(A, device=self.dev).contiguous()
+        self.b = torch.as_tensor(b, device=self.dev).contiguous()
+        self.n, self.c = self.A.shape[0], self.b.shape[1]
+        self.ws = torch.empty(es.workspace_bytes(self.n, self.c), dtype=torch.uint8, device=self.dev)
+        self.stream = ctypes.c_void_p(torch.cuda.current_stream(self.dev).cuda_stream)
+
+    def solve(self, keep=False):
+        sol = ctypes.c_void_p()
+        st = self.lib.es_solve_device(ctypes.c_void_p(self.A.data_ptr()), ctypes.c_void_p(self.b.data_ptr()),
+                                      self.n, self.c, ctypes.c_void_p(self.ws.data_ptr()), self.ws.numel(),
+                                      self.stream, ctypes.byref(sol))
+        if st != 0:
+            raise RuntimeError(f"solve failed: {self._lib.strerror(st)}")
+        if keep:
+            return sol
+        self.lib.es_solution_free(sol)
+        return None
+
+    def sync(self):
+        self.torch.cuda.synchronize(self.dev)
+
+
+def time_solves(S, steps, warmup):
+    for _ in range(warmup):
+        S.solve()
+    S.sync()
+    per = []
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        t1 = time.perf_counter()
+        S.solve()
+        per.append(time.perf_counter() - t1)
+    S.sync()
+    total = time.perf_counter() - t0
+    return total, per
+
+
+def profiled_pass(S):
+    _lib = S._lib
+    _lib.set_profiling(True)
+    sol = S.solve(keep=True)
+    S.sync()
+    _lib.set_profiling(False)
+    prof = _lib.kernel_profile()
+    info = _lib.solution_info(sol)
+    stages = _lib.last_timings()
+    pairs = _lib.read_solution(sol)
+    S.lib.es_solution_free(sol)
+    return prof, info, stages, pairs
+
+
+MOD_PRIMES = [1048573, 1048571, 1048559]   # primes below 2^20: int64 products stay exact
+
+
+def verify_mod_primes(A, b, pairs):
+    """A x == b modulo a few 20-bit primes for every component (a property
+    that holds only for the true solution, up to a 2^-60 chance), plus lowest
+    terms and positive denominators on a sample."""
+    import numpy as np
+    for p in MOD_PRIMES:
+        try:
+            xm = np.array([[(num % p) * pow(den % p, -1, p) % p for (num, den) in row] for row in pairs],
+                          dtype=np.int64)
+        except ValueError:
+            return False
+        if not np.array_equal((np.mod(A, p).astype(np.int64) @ xm) % p, np.mod(b, p)):
+            return False
+    for row in pairs[:: max(1, len(pairs) // 16)]:
+        for (num, den) in row:
+            if den <= 0 or math.gcd(num, den) != 1:
+                return False
+    return True
+
+
+def rooflines(prof, info, n, c):
+    pitch = 64
+    while pitch < n and n <= 1024:
+        pitch <<= 1
+    if n > 1024:
+        pitch = -(-n // 64) * 64
+    E = info["live_primes"]
+    out = {}
+    ms, cnt = prof["gj_step"]
+    if cnt:
+        # each launch reads and writes every live prime's n x pitch u8 working matrix
+        bytes_per = 2.0 * E * n * pitch
+        avg_s = ms / cnt / 1e3
+        gbs = bytes_per / avg_s / 1e9
+        out["gj_step"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                          "avg_launch_us": round(avg_s * 1e6, 2), "launches": cnt,
+                          "algorithmic_bytes_per_launch": int(bytes_per)}
+    ms, cnt = prof["lift_contract"]
+    if cnt:
+        # B_j (int8, n x pitch) once per step, plus the residue vector in and the residues out
+        bytes_per = E * n * pitch + E * c * pitch + E * n * c
+        ops_per = 2.0 * E * n * n * c
+        avg_s = ms / cnt / 1e3
+        gbs = bytes_per / avg_s / 1e9
+        out["lift_contract"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                                "avg_launch_us": round(avg_s * 1e6, 2), "launches": cnt,
+                                "algorithmic_bytes_per_launch": int(bytes_per),
+                                "int8_tops": round(ops_per / avg_s / 1e12, 3),
+                                "int8_frac_of_peak": round(ops_per / avg_s / 1e12 / INT8_PEAK_TOPS, 5)}
+    for k in ("garner", "residual", "residues"):
+        ms, cnt = prof[k]
+        if cnt:
+            out[k] = {"avg_launch_us": round(ms / cnt * 1e3, 2), "launches": cnt, "total_ms": round(ms, 3)}
+    return out
+
+
+def cpu_baseline(A, b, budget_s):
+    """Time the plain-C Bareiss oracle on the first K elimination steps of this
+    very system (K sized to the CPU budget) and project a full solve.
+
+    The oracle reports each step's wall time; a least-squares fit of
+    t_k = a e_k + b e_k L_k^2 (e_k entries updated at step k, each about L_k
+    64-bit limbs: entries after step k are (k+1)-minors) is summed over all
+    n steps.  Back substitution (O(n^4) limb operations against O(n^5) for the
+    elimination) is left out, so the projection is a lower bound.
+    """
+    import numpy as np
+    from oracle import cbareiss
+    n, c = A.shape[0], b.shape[1]
+    threads = cbareiss.default_threads()
+    amax = max(2, int(np.abs(A).max()))
+    bits_entry = math.log2(amax)
+
+    def model(k):
+        e = (n - k - 1) * (n + c - k - 1)
+        limbs = (k + 1) * (bits_entry + 0.5 * math.log2(k + 1) + 1.0) / 64.0 + 1.0
+        return e, e * limbs * limbs
+
+    def run(K):
+        st = np.zeros(n, dtype=np.float64)
+        t0 = time.perf_counter()
+        cbareiss.run(A, b, threads=threads, max_steps=K, step_seconds=st)
+        return time.perf_counter() - t0, st[:K]
+
+    def fit(ts, lo):
+        X = np.array([model(k) for k in range(lo, len(ts))], dtype=np.float64)
+        y = ts[lo:]
+        coef, *_ = np.linalg.lstsq(X, y, rcond=None)
+        return max(coef[0], 0.0), max(coef[1], 0.0)
+
+    K = min(n, 48)
+    dt, ts = run(K)
+    spent = dt
+    a_, b_ = fit(ts, 4)
+    # choose K so that the sampled steps take about the remaining budget
+    if K < n:
+        acc, K2 = 0.0, 0
+        while K2 < n and acc < max(budget_s - spent, 1.0):
+            e, w = model(K2)
+            acc += a_ * e + b_ * w
+            K2 += 1
+        K2 = max(K2, K + 16)
+        K = min(n, K2)
+        dt, ts = run(K)
+        spent += dt
+        a_, b_ = fit(ts, 4)
+    full = sum(a_ * model(k)[0] + b_ * model(k)[1] for k in range(n))
+    return {"value": round(full * 1e3, 1), "unit": "ms per full solve (projected from the sample)",
+            "cores": threads, "kind": "oracle",
+            "sample": (f"plain-C Bareiss oracle (oracle/bareiss.c) on this {n}x{n}, c={c} system, {threads} "
+                       f"threads: first {K} of {n} elimination steps in {dt:.2f} s; per-step times fitted "
+                       f"with t_k = a e_k + b e_k L_k^2 and summed over all n steps (back substitution "
+                       f"not included)"),
+            "sample_steps": K, "sample_seconds": round(dt, 3), "cpu_seconds_spent": round(spent, 2),
+            "fit": {"a_s_per_entry": a_, "b_s_per_entry_limb2": b_}}
+
+
+def copy_calibration(mb):
+    import torch
+    x = torch.empty(mb << 20, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    x.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    return {"copy_bytes_each_way": mb << 20, "copies": 3}
+
+
+def sweep(args):
+    from dixon_adic_lifting_amd import workloads as W
+    from dixon_adic_lifting_amd import _lib
+    rows = []
+    for name in list(W.WORKLOADS):
+        A, b = W.generate(name)
+        S = Solver(A, b)
+        steps = 3 if A.shape[0] >= 2048 else 5
+        total, per = time_solves(S, steps, 1)
+        prof, info, stages, pairs = profiled_pass(S)
+        rf = rooflines(prof, info, S.n, S.c)
+        rows.append({"workload": name, "ms_median": round(1e3 * sorted(per)[len(per) // 2], 2),
+                     "ms_min": round(1e3 * min(per), 2), "stages_ms": {k: round(v, 2) for k, v in stages.items()},
+                     "m": info["m"], "live": info["live_primes"], "roofline": rf})
+        print(json.dumps(rows[-1]), flush=True)
+    for (n, c) in W.CARD_SHAPES:
+        A, b = W.uniform_system(n, c, 24, 1000 + n + c)
+        S = Solver(A, b)
+        total, per = time_solves(S, 5, 1)
+        print(json.dumps({"workload": f"card_n{n}_c{c}_int24", "ms_median": round(1e3 * sorted(per)[len(per) // 2], 2),
+                          "ms_min": round(1e3 * min(per), 2), "stages_ms": {k: round(v, 2) for k, v in _lib.last_timings().items()}}),
+              flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this solver has no multi-GPU path; "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.sweep:
+        sweep(args)
+        return
+    from dixon_adic_lifting_amd import workloads as W
+    A, b = W.generate(args.workload)
+    S = Solver(A, b)
+    total, per = time_solves(S, args.steps, args.warmup)
+    ms_per = total / args.steps * 1e3
+    prof, info, stages, pairs = profiled_pass(S)
+    rf = rooflines(prof, info, S.n, S.c)
+    # parity of the benched output: the oracle's stored digest
+    gold = None
+    gpath = os.path.join(ROOT, "tests", "golden", "oracle_digests.json")
+    if os.path.exists(gpath):
+        with open(gpath) as f:
+            gold = json.load(f).get(args.workload)
+    parity = None if gold is None else (digest(pairs) == gold["sha256"])
+    identity_ok = verify_mod_primes(A, b, pairs)
+    max_bits = max(max(abs(p).bit_length(), q.bit_length()) for row in pairs for (p, q) in row)
+    if args.copy_calib_mb:
+        copy_calibration(args.copy_calib_mb)
+    dominant = max(("gj_step", "lift_contract"), key=lambda k: prof[k][0])
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(A, b, args.cpu_budget_s)
+    wl = W.WORKLOADS[args.workload]
+    line = {
+        "metric": "full exact-solve ms at n=1024 c=1 int24",
+        "value": round(ms_per, 3),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per, 3),
+        "solves_per_s": round(1e3 / ms_per, 3),
+        "ms_min": round(1e3 * min(per), 3),
+        "ms_median": round(1e3 * sorted(per)[len(per) // 2], 3),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": round(ms_per / PAGES_MS_C4["h200"], 5),
+        "dtype": "int8/int32/int64 (exact)",
+        "data": "synthetic (seeded, i.i.d. uniform 24-bit entries)",
+        "config": {"workload": wl.name, "n": wl.n, "c": wl.c, "entries": "uniform [-2^23, 2^23)",
+                   "seed": wl.seed, "m": info["m"], "live_primes": info["live_primes"]},
+        "parity_vs_oracle_digest": parity,
+        "output_check_Ax_eq_b_mod_primes": identity_ok,
+        "output_max_bits": max_bits,
+        "stages_ms": {k: round(v, 3) for k, v in stages.items()},
+        "roofline": {**{k: rf[dominant][k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")},
+                     "kernel": dominant},
+        "kernels": rf,
+        "pages_context_ms": PAGES_MS_C4,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -20,8 +20,8 @@ DIGIT_LIMBS = 6
 
 EXPORTS = ["es_strerror", "es_primes", "es_workspace_bytes", "es_solve_device", "es_solve",
            "es_solution_rows", "es_solution_cols", "es_solution_get", "es_solution_info",
-           "es_solution_free", "es_last_timings", "es_batched_inverse", "es_lift_digits",
-           "es_reconstruct"]
+           "es_solution_free", "es_last_timings", "es_set_profiling", "es_kernel_profile",
+           "es_batched_inverse", "es_lift_digits", "es_reconstruct"]
 
 _lib = None
 
@@ -68,6 +68,10 @@ def load():
     lib.es_solution_free.restype = None
     lib.es_last_timings.argtypes = [ctypes.POINTER(ctypes.c_double)]
     lib.es_last_timings.restype = ctypes.c_int
+    lib.es_set_profiling.argtypes = [ctypes.c_int]
+    lib.es_set_profiling.restype = ctypes.c_int
+    lib.es_kernel_profile.argtypes = [ctypes.POINTER(ctypes.c_double), c_i32p, ctypes.c_int32]
+    lib.es_kernel_profile.restype = ctypes.c_int
     lib.es_batched_inverse.argtypes = [c_vp, ctypes.c_int32, c_vp, ctypes.c_size_t, c_vp, c_vp, c_i32p]
     lib.es_batched_inverse.restype = ctypes.c_int
     lib.es_lift_digits.argtypes = [c_vp, c_vp, ctypes.c_int32, ctypes.c_int32, c_vp, ctypes.c_size_t, c_vp,
@@ -125,3 +129,18 @@ def last_timings():
     load().es_last_timings(buf)
     return {"checks_ms": buf[0], "inverse_ms": buf[1], "lift_ms": buf[2], "d2h_ms": buf[3],
             "reconstruct_ms": buf[4]}
+
+
+KERNEL_CLASSES = ["gj_step", "lift_contract", "garner", "residual", "residues"]
+
+
+def set_profiling(on: bool):
+    load().es_set_profiling(1 if on else 0)
+
+
+def kernel_profile():
+    """{class: (total_ms, launches)} for the last solve on this thread (profiling on)."""
+    ms = (ctypes.c_double * 8)()
+    cnt = (ctypes.c_int32 * 8)()
+    k = load().es_kernel_profile(ms, cnt, 8)
+    return {KERNEL_CLASSES[i]: (ms[i], cnt[i]) for i in range(min(k, len(KERNEL_CLASSES)))}

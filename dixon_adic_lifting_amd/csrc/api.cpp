@@ -39,6 +39,65 @@ double ms_since(clk::time_point t0) {
         if ((expr) != hipSuccess) return ES_EHIP; \
     } while (0)
 
+// Opt-in per-launch timing: a pair of HIP events on the solve's stream around
+// every launch of the hot kernels; totals are read after the final sync.
+enum KernelClass { KC_GJ = 0, KC_CONTRACT = 1, KC_GARNER = 2, KC_RESIDUAL = 3, KC_RESIDUES = 4, KC_COUNT = 5 };
+
+thread_local bool g_profiling = false;
+thread_local double g_kernel_ms[KC_COUNT] = {0, 0, 0, 0, 0};
+thread_local int32_t g_kernel_cnt[KC_COUNT] = {0, 0, 0, 0, 0};
+
+struct Profiler {
+    bool on = false;
+    hipStream_t st = nullptr;
+    std::vector<hipEvent_t> pool;
+    size_t used = 0;
+    std::vector<std::pair<int, size_t>> marks;  // (class, index of the start event)
+
+    explicit Profiler(hipStream_t s) : on(g_profiling), st(s) {}
+    ~Profiler() {
+        for (hipEvent_t e : pool) (void)hipEventDestroy(e);
+    }
+    hipEvent_t next() {
+        if (used == pool.size()) {
+            hipEvent_t e = nullptr;
+            if (hipEventCreate(&e) != hipSuccess) return nullptr;
+            pool.push_back(e);
+        }
+        return pool[used++];
+    }
+    // returns the index of the start event (or -1 when off)
+    long start(int cls) {
+        if (!on) return -1;
+        hipEvent_t e = next();
+        if (!e) return -1;
+        (void)hipEventRecord(e, st);
+        marks.push_back({cls, used - 1});
+        return (long)(used - 1);
+    }
+    void stop(long idx) {
+        if (idx < 0) return;
+        hipEvent_t e = next();
+        if (e) (void)hipEventRecord(e, st);
+    }
+    // after the stream has been synchronised
+    void collect() {
+        if (!on) return;
+        for (int k = 0; k < KC_COUNT; k++) {
+            g_kernel_ms[k] = 0;
+            g_kernel_cnt[k] = 0;
+        }
+        for (auto& mk : marks) {
+            if (mk.second + 1 >= used) continue;
+            float ms = 0;
+            if (hipEventElapsedTime(&ms, pool[mk.second], pool[mk.second + 1]) == hipSuccess) {
+                g_kernel_ms[mk.first] += ms;
+                g_kernel_cnt[mk.first] += 1;
+            }
+        }
+    }
+};
+
 // Two 62-bit primes for the rank test that separates "singular" from "det A
 // is a nonzero multiple of every odd prime below 256".
 const uint64_t kRankPrimes[2] = {4611686018427387847ULL, 4611686018427387817ULL};  // 2^62-57, 2^62-87
@@ -80,10 +139,16 @@ int prepare(const int64_t* dA, const int64_t* db, int32_t n, int32_t c, uint8_t*
 }
 
 // Residues and the n Gauss-Jordan launches; flags to the host.
-int run_inverse(const int64_t* dA, uint8_t* ws, hipStream_t st, Prep* pr, int* flags) {
+int run_inverse(const int64_t* dA, uint8_t* ws, hipStream_t st, Prep* pr, int* flags, Profiler* prof) {
     const Layout& L = pr->L;
+    long ev = prof->start(KC_RESIDUES);
     HIP_CHECK(launch_residues(dA, L, ws, pr->a32, st));
-    for (int k = 0; k < L.n; k++) HIP_CHECK(launch_gj_step(L, ws, k, st));
+    prof->stop(ev);
+    for (int k = 0; k < L.n; k++) {
+        ev = prof->start(KC_GJ);
+        HIP_CHECK(launch_gj_step(L, ws, k, st));
+        prof->stop(ev);
+    }
     HIP_CHECK(hipMemcpyAsync(flags, ws + L.off_flags, kNumPrimes * sizeof(int), hipMemcpyDeviceToHost, st));
     HIP_CHECK(hipStreamSynchronize(st));
     return ES_OK;
@@ -104,10 +169,35 @@ int no_prime_decision(const int64_t* dA, int32_t n, const Prep& pr, hipStream_t 
     return ES_SINGULAR;  // singular modulo two 62-bit primes as well
 }
 
+// Pinned host memory for the digits, kept per thread and grown on demand
+// (device-to-host copies into pageable memory go through an extra staging
+// copy, and pinned memory is allocated with hipHostMalloc, never registered).
+struct PinnedBuffer {
+    void* p = nullptr;
+    size_t bytes = 0;
+    ~PinnedBuffer() {
+        if (p) (void)hipHostFree(p);
+    }
+    void* get(size_t need) {
+        if (need <= bytes) return p;
+        if (p) (void)hipHostFree(p);
+        p = nullptr;
+        bytes = 0;
+        if (hipHostMalloc(&p, need, hipHostMallocDefault) != hipSuccess) {
+            p = nullptr;
+            return nullptr;
+        }
+        bytes = need;
+        return p;
+    }
+};
+thread_local PinnedBuffer g_pinned;
+
 // Lift m steps; digits land in host [n*c][m][6].
 int run_lift(const int64_t* dA, const int64_t* db, uint8_t* ws, hipStream_t st, const Prep& pr,
-             const LiveSet& ls, int m, int64_t* digits_host) {
-    const Layout& L = pr.L;
+             const LiveSet& ls, int m, int64_t* digits_host, Profiler* prof) {
+    Layout L = pr.L;
+    if (m <= L.kchunk) L.kchunk = m;  // one chunk: the device digits are laid out exactly as the host's
     LiftParams prm;
     fill_lift_params(ls, &prm);
     HIP_CHECK(hipMemcpyAsync(ws + L.off_params, &prm, sizeof prm, hipMemcpyHostToDevice, st));
@@ -115,10 +205,25 @@ int run_lift(const int64_t* dA, const int64_t* db, uint8_t* ws, hipStream_t st, 
     const size_t NC = (size_t)L.n * L.c;
     for (int i0 = 0; i0 < m; i0 += L.kchunk) {
         const int cnt = std::min(L.kchunk, m - i0);
-        for (int s = 0; s < cnt; s++) HIP_CHECK(launch_lift_step(L, ws, ls.E, pr.a32, dA, s, st));
-        HIP_CHECK(hipMemcpy2DAsync(digits_host + (size_t)i0 * kDigitLimbs, (size_t)m * kDigitLimbs * 8,
-                                   ws + L.off_digits, (size_t)L.kchunk * kDigitLimbs * 8,
-                                   (size_t)cnt * kDigitLimbs * 8, NC, hipMemcpyDeviceToHost, st));
+        for (int s = 0; s < cnt; s++) {
+            long ev = prof->start(KC_CONTRACT);
+            HIP_CHECK(launch_lift_contract(L, ws, ls.E, st));
+            prof->stop(ev);
+            ev = prof->start(KC_GARNER);
+            HIP_CHECK(launch_lift_garner(L, ws, s, st));
+            prof->stop(ev);
+            ev = prof->start(KC_RESIDUAL);
+            HIP_CHECK(launch_lift_residual(L, ws, pr.a32, dA, st));
+            prof->stop(ev);
+        }
+        if (cnt == m) {
+            HIP_CHECK(hipMemcpyAsync(digits_host, ws + L.off_digits, NC * (size_t)m * kDigitLimbs * 8,
+                                     hipMemcpyDeviceToHost, st));
+        } else {
+            HIP_CHECK(hipMemcpy2DAsync(digits_host + (size_t)i0 * kDigitLimbs, (size_t)m * kDigitLimbs * 8,
+                                       ws + L.off_digits, (size_t)L.kchunk * kDigitLimbs * 8,
+                                       (size_t)cnt * kDigitLimbs * 8, NC, hipMemcpyDeviceToHost, st));
+        }
     }
     HIP_CHECK(hipStreamSynchronize(st));
     return ES_OK;
@@ -152,6 +257,20 @@ size_t es_workspace_bytes(int32_t n, int32_t c) {
     return make_layout(n, c).total;
 }
 
+int es_set_profiling(int on) {
+    g_profiling = on != 0;
+    return ES_OK;
+}
+
+int es_kernel_profile(double* total_ms, int32_t* counts, int32_t cap) {
+    if (!total_ms || !counts) return ES_EINVAL;
+    for (int k = 0; k < KC_COUNT && k < cap; k++) {
+        total_ms[k] = g_kernel_ms[k];
+        counts[k] = g_kernel_cnt[k];
+    }
+    return KC_COUNT;
+}
+
 int es_last_timings(double* ms5) {
     if (!ms5) return ES_EINVAL;
     for (int i = 0; i < 5; i++) ms5[i] = g_timings[i];
@@ -168,6 +287,7 @@ int es_solve_device(const int64_t* dA, const int64_t* db, int32_t n, int32_t c, 
     for (double& t : g_timings) t = 0;
     hipStream_t st = (hipStream_t)stream;
     uint8_t* ws = (uint8_t*)d_ws;
+    Profiler prof(st);
     try {
         auto t0 = clk::now();
         int rc = prepare(dA, db, n, c, ws, st, &pr);
@@ -175,21 +295,23 @@ int es_solve_device(const int64_t* dA, const int64_t* db, int32_t n, int32_t c, 
         if (rc != ES_OK) return rc;
         t0 = clk::now();
         int flags[kNumPrimes];
-        rc = run_inverse(dA, ws, st, &pr, flags);
+        rc = run_inverse(dA, ws, st, &pr, flags, &prof);
         g_timings[1] = ms_since(t0);
         if (rc != ES_OK) return rc;
         LiveSet ls = make_live_set(flags);
         if (ls.E == 0) return no_prime_decision(dA, n, pr, st);
         BigInt M;
         const int m = choose_m(ls.P, pr.nbits, pr.dbits, &M);
-        std::vector<int64_t> digits((size_t)n * c * m * kDigitLimbs);
+        int64_t* digits = (int64_t*)g_pinned.get((size_t)n * c * m * kDigitLimbs * sizeof(int64_t));
+        if (!digits) return ES_ENOMEM;
         t0 = clk::now();
-        rc = run_lift(dA, db, ws, st, pr, ls, m, digits.data());
+        rc = run_lift(dA, db, ws, st, pr, ls, m, digits, &prof);
         g_timings[2] = ms_since(t0);
         if (rc != ES_OK) return rc;
+        prof.collect();
         t0 = clk::now();
         es_solution* sol = new es_solution;
-        rc = reconstruct(digits.data(), (size_t)m, n, c, m, ls.P, M, pr.nbits, pr.dbits, default_threads(),
+        rc = reconstruct(digits, (size_t)m, n, c, m, ls.P, M, pr.nbits, pr.dbits, default_threads(),
                          &sol->data);
         g_timings[4] = ms_since(t0);
         if (rc != ES_OK) {
@@ -274,7 +396,8 @@ int es_batched_inverse(const int64_t* dA, int32_t n, void* d_ws, size_t ws_bytes
         if (rc == ES_SINGULAR) rc = ES_OK;  // a zero row/column just makes every prime singular
         if (rc != ES_OK) return rc;
         int flags[kNumPrimes];
-        rc = run_inverse(dA, ws, st, &pr, flags);
+        Profiler prof(st);
+        rc = run_inverse(dA, ws, st, &pr, flags, &prof);
         if (rc != ES_OK) return rc;
         HIP_CHECK(launch_export_inverse(pr.L, ws, dB_out, st));
         HIP_CHECK(hipStreamSynchronize(st));
@@ -298,7 +421,8 @@ int es_lift_digits(const int64_t* dA, const int64_t* db, int32_t n, int32_t c, v
         int rc = prepare(dA, db, n, c, ws, st, &pr);
         if (rc != ES_OK) return rc;
         int flags[kNumPrimes];
-        rc = run_inverse(dA, ws, st, &pr, flags);
+        Profiler prof(st);
+        rc = run_inverse(dA, ws, st, &pr, flags, &prof);
         if (rc != ES_OK) return rc;
         LiveSet ls = make_live_set(flags);
         if (ls.E == 0) return no_prime_decision(dA, n, pr, st);
@@ -313,7 +437,9 @@ int es_lift_digits(const int64_t* dA, const int64_t* db, int32_t n, int32_t c, v
         *m_out = m;
         if (!digits_host) return ES_OK;  // query: m and the live set only
         if ((size_t)n * c * m * kDigitLimbs > digits_cap) return ES_EINVAL;
-        return run_lift(dA, db, ws, st, pr, ls, m, digits_host);
+        rc = run_lift(dA, db, ws, st, pr, ls, m, digits_host, &prof);
+        prof.collect();
+        return rc;
     } catch (...) {
         return ES_EINTERNAL;
     }

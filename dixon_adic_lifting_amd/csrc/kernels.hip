@@ -658,16 +658,23 @@ static void launch_gemv_c(const Layout& L, uint8_t* ws, int E, hipStream_t st) {
     }
 }
 
-hipError_t launch_lift_step(const Layout& L, uint8_t* ws, int E, bool a32, const int64_t* A64, int slot,
-                            hipStream_t st) {
+hipError_t launch_lift_contract(const Layout& L, uint8_t* ws, int E, hipStream_t st) {
     if (L.c == 1)
         launch_gemv_c<1>(L, ws, E, st);
     else
         launch_gemv_c<16>(L, ws, E, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_lift_garner(const Layout& L, uint8_t* ws, int slot, hipStream_t st) {
     const int NC = L.n * L.c;
     hipLaunchKernelGGL(garner_wave_kernel, dim3((NC + 3) / 4), dim3(256), 0, st,
                        (const LiftParams*)(ws + L.off_params), (const uint8_t*)(ws + L.off_U), NC,
                        (uint64_t*)(ws + L.off_digits), L.kchunk, slot, (uint64_t*)(ws + L.off_xlow));
+    return hipGetLastError();
+}
+
+hipError_t launch_lift_residual(const Layout& L, uint8_t* ws, bool a32, const int64_t* A64, hipStream_t st) {
     const dim3 grid((L.n + 3) / 4);
     const LiftParams* prm = (const LiftParams*)(ws + L.off_params);
     int64_t* R = (int64_t*)(ws + L.off_R);

@@ -103,10 +103,24 @@ int es_solution_info(const es_solution *s, int32_t *live_primes, int32_t *m,
 /* Frees everything the library allocated for a solution; NULL is a no-op. */
 void es_solution_free(es_solution *s);
 
-/* Stage timings of the last es_solve_device call on this thread, in ms:
- * [0] checks and bounds, [1] residues + batched inverse, [2] lift,
- * [3] device-to-host copy, [4] host reconstruction. */
+/* Host wall-clock stage timings of the last es_solve_device call on this
+ * thread, in ms: [0] checks and bounds, [1] residues + batched inverse,
+ * [2] lift including its device-to-host digit copies, [3] unused (0),
+ * [4] host reconstruction. */
 int es_last_timings(double *ms5);
+
+/*
+ * Opt-in kernel timing for measurement.  With es_set_profiling(1) on a
+ * thread, later solves on that thread bracket every launch of the hot
+ * kernels with a pair of HIP events on the solve's stream (small added gaps
+ * between launches; results are unchanged).  es_kernel_profile then gives,
+ * for the last solve, the summed event time in ms and the launch count per
+ * kernel class: [0] Gauss-Jordan step, [1] lift contraction (GEMV / GEMM),
+ * [2] Garner, [3] residual update, [4] residues of A.  Writes min(cap, 5)
+ * entries and returns 5.
+ */
+int es_set_profiling(int on);
+int es_kernel_profile(double *total_ms, int32_t *counts, int32_t cap);
 
 /* ------------------------------------------------------------------------
  * Stage entry points: the hot path's steps, exposed for tests and

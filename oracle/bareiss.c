@@ -291,8 +291,16 @@ typedef struct {
     bz *num, *den;   /* reduced output [n][c] */
     int singular, stopped;
     int cur_i, cur_t;
+    double *step_seconds; /* optional: wall time of each elimination step */
     pthread_barrier_t bar;
 } job;
+
+#include <time.h>
+static double now_s(void) {
+    struct timespec ts;
+    clock_gettime(CLOCK_MONOTONIC, &ts);
+    return ts.tv_sec + 1e-9 * ts.tv_nsec;
+}
 
 typedef struct { job *J; int tid; } warg;
 
@@ -305,8 +313,14 @@ static void *worker(void *arg) {
     bz a = {0}, b = {0};
 
     /* forward elimination */
+    double t_step = now_s();
     for (int k = 0; k < n; k++) {
         if (tid == 0) {
+            if (J->step_seconds && k > 0) {
+                double t = now_s();
+                J->step_seconds[k - 1] = t - t_step;
+                t_step = t;
+            }
             if (J->max_steps >= 0 && k >= J->max_steps) {
                 J->stopped = 1;
             } else {
@@ -394,15 +408,18 @@ static size_t put_hex(char *o, const bz *x) {
  * nthreads >= 1.  max_steps < 0 runs to completion; otherwise elimination
  * stops after that many steps (used to time a bounded sample of the work).
  * Returns 0 and *out = malloc'd text "num den\n" per component (hex, row-major)
- * on success, 1 if A is singular, 2 if stopped by max_steps.
+ * on success, 1 if A is singular, 2 if stopped by max_steps.  If step_seconds
+ * is not NULL it receives the wall time of each elimination step that ran
+ * (n doubles; only timing, the arithmetic is the same).
  */
-int oracle_solve(const int64_t *A, const int64_t *b, int n, int c, int nthreads,
-                 int max_steps, char **out) {
+int oracle_solve_timed(const int64_t *A, const int64_t *b, int n, int c, int nthreads,
+                       int max_steps, char **out, double *step_seconds) {
     *out = NULL;
     if (n < 1 || c < 1 || nthreads < 1) return -1;
     job J;
     memset(&J, 0, sizeof J);
     J.n = n; J.c = c; J.T = nthreads; J.max_steps = max_steps;
+    J.step_seconds = step_seconds;
     int W = n + c;
     J.M = (bz **)calloc((size_t)n, sizeof(bz *));
     for (int i = 0; i < n; i++) {
@@ -452,6 +469,12 @@ int oracle_solve(const int64_t *A, const int64_t *b, int n, int c, int nthreads,
     bz_clear(&J.d);
     free(th); free(wa);
     return status;
+}
+
+/* Same as oracle_solve_timed without the per-step timing. */
+int oracle_solve(const int64_t *A, const int64_t *b, int n, int c, int nthreads,
+                 int max_steps, char **out) {
+    return oracle_solve_timed(A, b, n, c, nthreads, max_steps, out, NULL);
 }
 
 void oracle_free(char *p) { free(p); }

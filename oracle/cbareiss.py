@@ -36,6 +36,8 @@ def _load():
                                      ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                      ctypes.POINTER(ctypes.c_char_p)]
         lib.oracle_solve.restype = ctypes.c_int
+        lib.oracle_solve_timed.argtypes = lib.oracle_solve.argtypes + [ctypes.POINTER(ctypes.c_double)]
+        lib.oracle_solve_timed.restype = ctypes.c_int
         lib.oracle_free.argtypes = [ctypes.c_char_p]
         lib.oracle_free.restype = None
         _lib = lib
@@ -49,8 +51,12 @@ def default_threads() -> int:
         return max(1, os.cpu_count() or 1)
 
 
-def run(A, b, threads: int | None = None, max_steps: int = -1):
-    """Raw call: returns (status, text or None).  status 0 ok, 1 singular, 2 stopped."""
+def run(A, b, threads: int | None = None, max_steps: int = -1, step_seconds=None):
+    """Raw call: returns (status, text or None).  status 0 ok, 1 singular, 2 stopped.
+
+    step_seconds: optional float64 numpy array of length n that receives the
+    wall time of each elimination step.
+    """
     lib = _load()
     A = np.ascontiguousarray(A, dtype=np.int64)
     b = np.ascontiguousarray(b, dtype=np.int64)
@@ -58,9 +64,13 @@ def run(A, b, threads: int | None = None, max_steps: int = -1):
     c = b.shape[1]
     assert A.shape == (n, n) and b.shape == (n, c)
     out = ctypes.c_char_p()
-    st = lib.oracle_solve(A.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
-                          b.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
-                          n, c, int(threads or default_threads()), int(max_steps), ctypes.byref(out))
+    args = (A.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), b.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+            n, c, int(threads or default_threads()), int(max_steps), ctypes.byref(out))
+    if step_seconds is not None:
+        assert step_seconds.dtype == np.float64 and step_seconds.size >= n
+        st = lib.oracle_solve_timed(*args, step_seconds.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
+    else:
+        st = lib.oracle_solve(*args)
     if st < 0:
         raise ValueError("oracle_solve rejected its arguments")
     text = None
