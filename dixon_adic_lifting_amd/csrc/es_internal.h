@@ -41,6 +41,26 @@ constexpr PrimeTable make_prime_table() {
 }
 
 constexpr PrimeTable kPrimeTable = make_prime_table();
+
+// Inverses modulo each prime: inv[j][a] = a^-1 mod q_j (inv[j][0] = 0), from
+// the recurrence a^-1 = -(q div a) (q mod a)^-1 mod q.
+struct InverseTable {
+    uint8_t inv[kNumPrimes][256];
+};
+
+constexpr InverseTable make_inverse_table() {
+    InverseTable t{};
+    for (int j = 0; j < kNumPrimes; j++) {
+        const uint32_t q = kPrimeTable.q[j];
+        t.inv[j][1] = 1;
+        for (uint32_t a = 2; a < q; a++)
+            t.inv[j][a] = (uint8_t)((q - (q / a) * t.inv[j][q % a] % q) % q);
+    }
+    return t;
+}
+
+constexpr InverseTable kInverseTable = make_inverse_table();
+static_assert(kInverseTable.inv[52][250] == 250 && kInverseTable.inv[0][2] == 2, "inverse table");
 static_assert(kPrimeTable.q[0] == 3 && kPrimeTable.q[kNumPrimes - 1] == 251, "prime table");
 
 // Per-solve constants of the lift, for the live primes in ascending order.

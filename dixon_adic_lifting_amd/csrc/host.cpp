@@ -13,7 +13,9 @@
 
 #include <algorithm>
 #include <atomic>
+#include <chrono>
 #include <cmath>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <thread>
@@ -267,11 +269,29 @@ static BigInt assemble(const int64_t* dig, int m, const BigInt& P) {
     return X;
 }
 
+static bool verbose() {
+    static const bool v = [] {
+        const char* e = std::getenv("ES_VERBOSE");
+        return e && *e && *e != '0';
+    }();
+    return v;
+}
+
 int reconstruct(const int64_t* digits, size_t stride_m, int n, int c, int m, const BigInt& P,
                 const BigInt& M, int nbits, int dbits, int nthreads, SolutionData* out) {
     const size_t NC = (size_t)n * c;
+    typedef std::chrono::steady_clock clk;
+    auto t0 = clk::now();
+    auto lap = [&](const char* what) {
+        if (!verbose()) return;
+        auto t1 = clk::now();
+        fprintf(stderr, "[es] reconstruct %-10s %8.3f ms\n", what,
+                std::chrono::duration<double, std::milli>(t1 - t0).count());
+        t0 = t1;
+    };
     std::vector<BigInt> X(NC);
     parallel_for(NC, nthreads, [&](size_t j) { X[j] = assemble(digits + j * stride_m * kDigitLimbs, m, P); });
+    lap("assemble");
     const BigInt Nb = shl(BigInt::from_u64(1), (size_t)nbits);
     const BigInt Db = shl(BigInt::from_u64(1), (size_t)dbits);
     BigInt Mhalf = shr_abs(M, 1);
@@ -290,6 +310,7 @@ int reconstruct(const int64_t* digits, size_t stride_m, int n, int c, int m, con
     if (bad) return ES_EINTERNAL;
     BigInt d = BigInt::from_u64(1);
     for (auto& v : sden) d = lcm(d, v);
+    lap("sample");
 
     out->n = n;
     out->c = c;
@@ -307,6 +328,7 @@ int reconstruct(const int64_t* digits, size_t stride_m, int n, int c, int m, con
         out->num[j] = divexact(y, g);
         out->den[j] = divexact(d, g);
     });
+    lap("numerators");
     for (size_t j = 0; j < NC; j++) {
         if (!failed[j]) continue;
         BigInt a = mod_floor(X[j], M), nu, de;

@@ -23,12 +23,14 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
+#include <cstdlib>
 
 #include "es_internal.h"
 
 namespace es {
 
 __constant__ PrimeTable c_pt = kPrimeTable;
+__constant__ InverseTable c_inv = kInverseTable;
 
 // ---------------------------------------------------------------- arithmetic
 
@@ -272,7 +274,30 @@ hipError_t launch_residues(const int64_t* A, const Layout& L, uint8_t* ws, bool 
 // search is launched.  A prime with no pivot is singular mod q_j: its flag
 // is set and all of its later launches exit at once.  The last step writes
 // balanced int8 residues, the operand format of the lift.
-template <int LPR, int RI>
+//
+// Arithmetic runs "one byte up": each residue s sits in bits 8..15 of a
+// 32-bit lane value, x' = 256 (s + f v) < 2^24, and the Barrett quotient
+// floor(x mu16 / 2^16) is the high word of the 24 x 24-bit product
+// x' (mu16 * 256) (v_mul_hi_u32_u24), so extraction, reduction and
+// repacking take about seven VALU operations per element.
+
+// byte b of w placed in bits 8..15 (other bits zero)
+__device__ __forceinline__ uint32_t byte_up(uint32_t w, int b) {
+    return b == 0 ? (w << 8) & 0xff00u : b == 1 ? w & 0xff00u : b == 2 ? (w >> 8) & 0xff00u : (w >> 16) & 0xff00u;
+}
+
+__device__ __forceinline__ uint32_t mulhi_u24(uint32_t a, uint32_t b) {
+    return (uint32_t)(((uint64_t)(a & 0xffffffu) * (uint64_t)(b & 0xffffffu)) >> 32);
+}
+
+// (xs / 256) mod q, returned as 256 * residue; xs = 256 x with x < 2^16
+__device__ __forceinline__ uint32_t red16_up(uint32_t xs, uint32_t q8, uint32_t mu8) {
+    const uint32_t t = mulhi_u24(xs, mu8);
+    const uint32_t r = xs - __umul24(t, q8);
+    return min(r, r - q8);
+}
+
+template <int LPR, int RI, bool LAST>
 __global__ __launch_bounds__(256) void gj_step_kernel(uint8_t* __restrict__ S, int n, int pitch,
                                                       int k, int* __restrict__ piv,
                                                       int* __restrict__ rowpos,
@@ -282,83 +307,128 @@ __global__ __launch_bounds__(256) void gj_step_kernel(uint8_t* __restrict__ S, i
     constexpr int ROWS = 4 * RPW * RI;      // rows per block
     const int j = blockIdx.y;
     int* pj = piv + (size_t)j * (n + 1);
-    const int p = pj[k];
-    if (p == INT_MAX) {
-        if (blockIdx.x == 0 && threadIdx.x == 0) flags[j] = 1;
-        return;
-    }
-    const bool last = (k == n - 1);
-    const uint32_t q = c_pt.q[j], mu = c_pt.mu16[j];
     uint8_t* Sj = S + (size_t)j * n * pitch;
-    int* rpj = rowpos + (size_t)j * n;
-    const int pprev = k > 0 ? pj[k - 1] : -1;
-    const uint8_t* pend_prev = pend + ((size_t)((k + 1) & 1) * kNumPrimes + j) * pitch;
-    uint8_t* pend_cur = pend + ((size_t)(k & 1) * kNumPrimes + j) * pitch;
-    const uint32_t pinv = inv_mod(Sj[(size_t)p * pitch + k], q, mu);
-
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane / LPR, cl = lane % LPR;
     const int npass = (LPR == 64) ? (pitch + 1023) >> 10 : 1;
     const int row0 = blockIdx.x * ROWS;
-    int cand = INT_MAX;
 
-    // Column k of every row this thread updates, read once before any pass
-    // writes (with two or more column passes, an earlier pass overwrites it).
-    uint32_t fneg[RI];
-    const uint8_t* srcs[RI];
+    // Issue this thread's first-pass row loads and column-k bytes before the
+    // pivot index arrives: they depend only on the row index (the previous
+    // step's pivot row is re-read from the side buffer below).
+    uint4 s[RI];
+    uint32_t f[RI];
 #pragma unroll
     for (int r = 0; r < RI; r++) {
         const int i = row0 + wave * RPW + g + r * 4 * RPW;
+        const bool ok = i < n && cl * 16 < pitch;
+        s[r] = ok ? *(const uint4*)(Sj + (size_t)i * pitch + cl * 16) : make_uint4(0, 0, 0, 0);
+        f[r] = i < n ? Sj[(size_t)i * pitch + k] : 0u;
+    }
+    const int p = pj[k];
+    const int pprev = k > 0 ? pj[k - 1] : -1;
+    if (p == INT_MAX) {
+        if (blockIdx.x == 0 && threadIdx.x == 0) flags[j] = 1;
+        return;
+    }
+    const uint32_t q = c_pt.q[j], mu = c_pt.mu16[j];
+    const uint32_t q8 = q << 8, mu8 = mu << 8, half8 = (q >> 1) << 8;
+    int* rpj = rowpos + (size_t)j * n;
+    const uint8_t* pend_prev = pend + ((size_t)((k + 1) & 1) * kNumPrimes + j) * pitch;
+    uint8_t* pend_cur = pend + ((size_t)(k & 1) * kNumPrimes + j) * pitch;
+    const uint32_t pinv = c_inv.inv[j][Sj[(size_t)p * pitch + k]];
+    int cand = INT_MAX;
+
+    // live[r]: row r is updated here (it exists and is not the pivot row);
+    // the previous pivot row's current content is in the side buffer
+    bool live[RI];
+    uint32_t fneg[RI];
+#pragma unroll
+    for (int r = 0; r < RI; r++) {
+        const int i = row0 + wave * RPW + g + r * 4 * RPW;
+        live[r] = i < n && i != p;
         fneg[r] = 0;
-        srcs[r] = nullptr;
-        if (i < n && i != p) {
-            srcs[r] = (i == pprev) ? pend_prev : Sj + (size_t)i * pitch;
-            const uint32_t f = srcs[r][k];
-            fneg[r] = f ? q - f : 0;
+        if (live[r]) {
+            if (i == pprev) {
+                f[r] = pend_prev[k];
+                if (cl * 16 < pitch) s[r] = *(const uint4*)(pend_prev + cl * 16);
+            }
+            fneg[r] = f[r] ? q - f[r] : 0;
         }
     }
+    const bool own_p = (p >= row0 && p < row0 + ROWS) && ((p - row0) % (4 * RPW)) == wave * RPW + g;
 
     for (int pass = 0; pass < npass; ++pass) {
         const int col0 = pass * 1024 + cl * 16;
-        const bool active = col0 < pitch;
-        uint32_t v[16];
-        {
-            uint4 raw = active ? *(const uint4*)(Sj + (size_t)p * pitch + col0) : make_uint4(0, 0, 0, 0);
-            unpack16(raw, v);
+        if (col0 >= pitch) continue;
+        if (pass > 0) {
 #pragma unroll
-            for (int b = 0; b < 16; b++) v[b] = (col0 + b == k) ? pinv : red16(v[b] * pinv, q, mu);
-        }
-        // load all of this thread's rows first, then update them
-        uint4 s[RI];
-#pragma unroll
-        for (int r = 0; r < RI; r++)
-            s[r] = (srcs[r] && active) ? *(const uint4*)(srcs[r] + col0) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-        for (int r = 0; r < RI; r++) {
-            const int i = row0 + wave * RPW + g + r * 4 * RPW;
-            if (i >= n || !active) continue;
-            uint32_t x[16];
-            if (i == p) {
-#pragma unroll
-                for (int b = 0; b < 16; b++) x[b] = last ? (uint32_t)balanced(v[b], q) : v[b];
-                *(uint4*)(pend_cur + col0) = pack16(x);
-                continue;
+            for (int r = 0; r < RI; r++) {
+                const int i = row0 + wave * RPW + g + r * 4 * RPW;
+                const uint8_t* src = (i == pprev) ? pend_prev : Sj + (size_t)i * pitch;
+                s[r] = live[r] ? *(const uint4*)(src + col0) : make_uint4(0, 0, 0, 0);
             }
-            unpack16(s[r], x);
-            bool nz_next = false;
+        }
+        // scaled pivot row, one byte up; slot k holds pinv
+        uint32_t vs[16];
+        {
+            const uint4 raw = *(const uint4*)(Sj + (size_t)p * pitch + col0);
+            const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
             for (int b = 0; b < 16; b++) {
-                const uint32_t sb = (col0 + b == k) ? 0u : x[b];
-                uint32_t y = red16(sb + __umul24(fneg[r], v[b]), q, mu);
-                if (col0 + b == k + 1) nz_next = y != 0;
-                x[b] = last ? (uint32_t)balanced(y, q) : y;
+                const uint32_t x = (w[b >> 2] >> (8 * (b & 3))) & 0xffu;
+                vs[b] = (col0 + b == k) ? (pinv << 8) : (red16(__umul24(x, pinv), q, mu) << 8);
             }
-            if (!last && nz_next && rpj[i] < 0) cand = min(cand, i);
-            *(uint4*)(Sj + (size_t)i * pitch + col0) = pack16(x);
+        }
+        if (own_p) {  // the pivot row's new content goes to the side buffer
+            uint32_t o[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                uint32_t e[4];
+#pragma unroll
+                for (int b = 0; b < 4; b++) {
+                    uint32_t y = vs[4 * i + b];
+                    if (LAST) y = (y > half8 ? y - q8 : y) & 0xff00u;  // balanced, two's complement byte
+                    e[b] = y;
+                }
+                o[i] = (e[0] >> 8) | e[1] | (e[2] << 8) | (e[3] << 16);
+            }
+            *(uint4*)(pend_cur + col0) = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+        // slot k of every other row is cleared before the update: a per-lane word mask
+        const int kk = k - col0, kk1 = k + 1 - col0;
+        uint32_t kmask[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            kmask[i] = (kk >= 0 && kk < 16 && (kk >> 2) == i) ? ~(0xffu << (8 * (kk & 3))) : 0xffffffffu;
+#pragma unroll
+        for (int r = 0; r < RI; r++) {
+            if (!live[r]) continue;
+            const uint32_t w[4] = {s[r].x & kmask[0], s[r].y & kmask[1], s[r].z & kmask[2], s[r].w & kmask[3]};
+            const uint32_t fr = fneg[r];
+            uint32_t o[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                uint32_t e[4];
+#pragma unroll
+                for (int b = 0; b < 4; b++) {
+                    const uint32_t xs = byte_up(w[i], b) + __umul24(fr, vs[4 * i + b]);
+                    uint32_t y = red16_up(xs, q8, mu8);
+                    if (LAST) y = (y > half8 ? y - q8 : y) & 0xff00u;
+                    e[b] = y;
+                }
+                o[i] = (e[0] >> 8) | e[1] | (e[2] << 8) | (e[3] << 16);
+            }
+            const int i = row0 + wave * RPW + g + r * 4 * RPW;
+            if (!LAST && kk1 >= 0 && kk1 < 16) {
+                const uint32_t word = (kk1 >> 2) == 0 ? o[0] : (kk1 >> 2) == 1 ? o[1] : (kk1 >> 2) == 2 ? o[2] : o[3];
+                if (((word >> (8 * (kk1 & 3))) & 0xffu) != 0 && rpj[i] < 0) cand = min(cand, i);
+            }
+            *(uint4*)(Sj + (size_t)i * pitch + col0) = make_uint4(o[0], o[1], o[2], o[3]);
         }
     }
     if (threadIdx.x == 0 && p >= row0 && p < row0 + ROWS) rpj[p] = k;
-    if (!last) {
+    if (!LAST) {
         __shared__ int smin;
         if (threadIdx.x == 0) smin = INT_MAX;
         __syncthreads();
@@ -381,13 +451,28 @@ __global__ __launch_bounds__(256) void gj_finalize_kernel(uint8_t* __restrict__ 
         *(uint32_t*)(dst + col) = *(const uint32_t*)(src + col);
 }
 
+// Rows per thread for the wide-row Gauss-Jordan kernel (8 unless ES_GJ_RI=4):
+// a tuning knob, both variants compute the same result.
+static int gj_rows_per_thread() {
+    static const int v = [] {
+        const char* e = getenv("ES_GJ_RI");
+        return (e && e[0] == '4') ? 4 : 8;
+    }();
+    return v;
+}
+
 template <int LPR, int RI>
 static void launch_gj_t(const Layout& L, uint8_t* ws, int k, hipStream_t st) {
     constexpr int ROWS = 4 * (64 / LPR) * RI;
     dim3 grid((L.n + ROWS - 1) / ROWS, kNumPrimes);
-    hipLaunchKernelGGL((gj_step_kernel<LPR, RI>), grid, dim3(256), 0, st, ws + L.off_S, L.n, L.pitch,
-                       k, (int*)(ws + L.off_piv), (int*)(ws + L.off_rowpos), ws + L.off_pend,
-                       (int*)(ws + L.off_flags));
+    if (k == L.n - 1)
+        hipLaunchKernelGGL((gj_step_kernel<LPR, RI, true>), grid, dim3(256), 0, st, ws + L.off_S, L.n, L.pitch,
+                           k, (int*)(ws + L.off_piv), (int*)(ws + L.off_rowpos), ws + L.off_pend,
+                           (int*)(ws + L.off_flags));
+    else
+        hipLaunchKernelGGL((gj_step_kernel<LPR, RI, false>), grid, dim3(256), 0, st, ws + L.off_S, L.n,
+                           L.pitch, k, (int*)(ws + L.off_piv), (int*)(ws + L.off_rowpos), ws + L.off_pend,
+                           (int*)(ws + L.off_flags));
 }
 
 hipError_t launch_gj_step(const Layout& L, uint8_t* ws, int k, hipStream_t st) {
@@ -396,7 +481,10 @@ hipError_t launch_gj_step(const Layout& L, uint8_t* ws, int k, hipStream_t st) {
         case 8: launch_gj_t<8, 1>(L, ws, k, st); break;
         case 16: launch_gj_t<16, 2>(L, ws, k, st); break;
         case 32: launch_gj_t<32, 4>(L, ws, k, st); break;
-        default: launch_gj_t<64, 4>(L, ws, k, st); break;
+        default:
+            if (gj_rows_per_thread() == 4) launch_gj_t<64, 4>(L, ws, k, st);
+            else launch_gj_t<64, 8>(L, ws, k, st);
+            break;
     }
     if (k == L.n - 1)
         hipLaunchKernelGGL(gj_finalize_kernel, dim3(kNumPrimes), dim3(256), 0, st, ws + L.off_S, L.n,
