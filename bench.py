@@ -85,16 +85,23 @@ class Solver:
         self.torch.cuda.synchronize(self.dev)
 
 
+def progress(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def time_solves(S, steps, warmup):
-    for _ in range(warmup):
+    for w in range(warmup):
+        t1 = time.perf_counter()
         S.solve()
+        progress(f"warmup {w + 1}/{warmup}: {1e3 * (time.perf_counter() - t1):.1f} ms")
     S.sync()
     per = []
     t0 = time.perf_counter()
-    for _ in range(steps):
+    for k in range(steps):
         t1 = time.perf_counter()
         S.solve()
         per.append(time.perf_counter() - t1)
+        progress(f"step {k + 1}/{steps}: {1e3 * per[-1]:.1f} ms")
     S.sync()
     total = time.perf_counter() - t0
     return total, per
@@ -312,6 +319,7 @@ def main():
     total, per = time_solves(S, args.steps, args.warmup)
     ms_per = total / args.steps * 1e3
     prof, info, stages, pairs = profiled_pass(S)
+    progress(f"profiled pass done: stages {stages}")
     rf = rooflines(prof, info, S.n, S.c, counter_traffic(args.workload))
     # parity of the benched output: the oracle's stored digest
     gold = None
@@ -321,6 +329,7 @@ def main():
             gold = json.load(f).get(args.workload)
     parity = None if gold is None else (digest(pairs) == gold["sha256"])
     identity_ok = verify_mod_primes(A, b, pairs)
+    progress(f"output checks done: digest match {parity}, A x = b mod primes {identity_ok}")
     max_bits = max(max(abs(p).bit_length(), q.bit_length()) for row in pairs for (p, q) in row)
     if args.copy_calib_mb:
         copy_calibration(args.copy_calib_mb)

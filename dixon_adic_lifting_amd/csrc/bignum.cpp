@@ -455,26 +455,41 @@ static bool lehmer_matrix(int64_t xh, int64_t yh, int64_t* A, int64_t* B, int64_
     return b != 0;
 }
 
-// (x, y) <- (A x + B y, C x + D y) for nonnegative x, y whose images are
-// nonnegative (guaranteed by Algorithm L).
+// (x, y) <- (A x + B y, C x + D y) in place, for nonnegative x, y whose
+// images are nonnegative (guaranteed by Algorithm L).  The cofactors come in
+// sign pattern (+, -, -, +) or (-, +, +, -), so each new limb is a difference
+// of two unsigned 64 x 64 -> 128-bit products.
 static void apply_matrix(BigInt& x, BigInt& y, int64_t A, int64_t B, int64_t C, int64_t D) {
-    size_t n = std::max(x.size(), y.size());
-    std::vector<limb_t> nx(n), ny(n);
-    i128 cx = 0, cy = 0;
+    const size_t n = std::max(x.size(), y.size());
+    x.d.resize(n, 0);
+    y.d.resize(n, 0);
+    // new_x = p1 * u1 - p2 * u2, new_y = p3 * u3 - p4 * u4 with u in {x, y}
+    const bool even = A >= 0 && B <= 0 && C <= 0 && D >= 0;
+    const uint64_t a = (uint64_t)(A < 0 ? -A : A), b = (uint64_t)(B < 0 ? -B : B);
+    const uint64_t c = (uint64_t)(C < 0 ? -C : C), d = (uint64_t)(D < 0 ? -D : D);
+    limb_t* xp = x.d.data();
+    limb_t* yp = y.d.data();
+    u128 px = 0, mx = 0, py = 0, my = 0;  // running positive / negative partial sums (carries)
     for (size_t i = 0; i < n; i++) {
-        i128 xi = i < x.size() ? (i128)x.d[i] : 0;
-        i128 yi = i < y.size() ? (i128)y.d[i] : 0;
-        i128 sx = (i128)A * xi + (i128)B * yi + cx;
-        i128 sy = (i128)C * xi + (i128)D * yi + cy;
-        nx[i] = (limb_t)sx;
-        ny[i] = (limb_t)sy;
-        cx = sx >> 64;  // arithmetic shift keeps the sign of the carry
-        cy = sy >> 64;
+        const u128 xi = xp[i], yi = yp[i];
+        // new_x: even -> a x - b y ; odd -> b y - a x.  new_y: even -> d y - c x ; odd -> c x - d y
+        px += even ? a * xi : b * yi;
+        mx += even ? b * yi : a * xi;
+        py += even ? d * yi : c * xi;
+        my += even ? c * xi : d * yi;
+        // limb i of (px - mx): borrow handled by keeping both sums and carrying their high parts
+        const limb_t lx = (limb_t)px - (limb_t)mx;
+        const limb_t bx = (limb_t)px < (limb_t)mx;
+        const limb_t ly = (limb_t)py - (limb_t)my;
+        const limb_t by = (limb_t)py < (limb_t)my;
+        xp[i] = lx;
+        yp[i] = ly;
+        px = (px >> 64);
+        mx = (mx >> 64) + bx;
+        py = (py >> 64);
+        my = (my >> 64) + by;
     }
-    if (cx != 0 || cy != 0) throw std::logic_error("Lehmer step left a carry");
-    x.d.swap(nx);
-    y.d.swap(ny);
-    x.neg = y.neg = false;
+    if (px != mx || py != my) throw std::logic_error("Lehmer step left a carry");
     x.trim();
     y.trim();
 }

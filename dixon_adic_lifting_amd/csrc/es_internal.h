@@ -15,11 +15,15 @@ constexpr int kDigitWords = 12;  // the same in 32-bit words
 // Odd primes below 256 (Eratosthenes) with their Barrett constants:
 // mu16 = floor(2^16 / q) reduces x < 2^16; mu32 = floor(2^32 / q) reduces
 // x < 2^32; r32 = 2^32 mod q folds the high word of a 64-bit value.
+// mq24 = ceil(2^24 / q) gives the exact quotient floor(x / q) =
+// floor(x mq24 / 2^24) for every x < 2^16 (round-up reciprocal with
+// 16 + 8 bits of precision, q <= 2^8), so no correction step follows.
 struct PrimeTable {
     uint32_t q[kNumPrimes];
     uint32_t mu16[kNumPrimes];
     uint32_t mu32[kNumPrimes];
     uint32_t r32[kNumPrimes];
+    uint32_t mq24[kNumPrimes];
 };
 
 constexpr PrimeTable make_prime_table() {
@@ -35,6 +39,7 @@ constexpr PrimeTable make_prime_table() {
         t.mu16[cnt] = 65536u / v;
         t.mu32[cnt] = (uint32_t)(4294967296ull / v);
         t.r32[cnt] = (uint32_t)(4294967296ull % v);
+        t.mq24[cnt] = (uint32_t)((16777216ull + v - 1) / v);
         cnt++;
     }
     return t;

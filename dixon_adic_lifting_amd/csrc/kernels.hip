@@ -276,25 +276,41 @@ hipError_t launch_residues(const int64_t* A, const Layout& L, uint8_t* ws, bool 
 // balanced int8 residues, the operand format of the lift.
 //
 // Arithmetic runs "one byte up": each residue s sits in bits 8..15 of a
-// 32-bit lane value, x' = 256 (s + f v) < 2^24, and the Barrett quotient
-// floor(x mu16 / 2^16) is the high word of the 24 x 24-bit product
-// x' (mu16 * 256) (v_mul_hi_u32_u24), so extraction, reduction and
-// repacking take about seven VALU operations per element.
+// 32-bit lane value and x' = 256 (s + f v) < 2^24.  With mq24 = ceil(2^24/q)
+// the high word of the 24 x 24-bit product x' mq24 (v_mul_hi_u32_u24) is the
+// exact quotient floor(x / q), and x' - 256 q floor(x/q) (one signed 24-bit
+// multiply-add) is 256 (x mod q) with no correction step.  Bytes move in and
+// out of that position with byte permutes, so an element costs about five
+// VALU operations.
 
 // byte b of w placed in bits 8..15 (other bits zero)
 __device__ __forceinline__ uint32_t byte_up(uint32_t w, int b) {
-    return b == 0 ? (w << 8) & 0xff00u : b == 1 ? w & 0xff00u : b == 2 ? (w >> 8) & 0xff00u : (w >> 16) & 0xff00u;
+    return __builtin_amdgcn_perm(0u, w, 0x0c0c000cu | ((uint32_t)b << 8));
 }
 
 __device__ __forceinline__ uint32_t mulhi_u24(uint32_t a, uint32_t b) {
     return (uint32_t)(((uint64_t)(a & 0xffffffu) * (uint64_t)(b & 0xffffffu)) >> 32);
 }
 
-// (xs / 256) mod q, returned as 256 * residue; xs = 256 x with x < 2^16
-__device__ __forceinline__ uint32_t red16_up(uint32_t xs, uint32_t q8, uint32_t mu8) {
-    const uint32_t t = mulhi_u24(xs, mu8);
-    const uint32_t r = xs - __umul24(t, q8);
-    return min(r, r - q8);
+// a * b + c on signed 24-bit operands, b uniform across the wave.  Written as
+// an instruction because the compiler otherwise widens t * q to the
+// quarter-rate 32-bit multiply.
+__device__ __forceinline__ uint32_t mad_i24(uint32_t a, int32_t b, uint32_t c) {
+    uint32_t r;
+    asm("v_mad_i32_i24 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(b), "v"(c));
+    return r;
+}
+
+// 256 (x mod q) from xs = 256 x, x < 2^16 (exact quotient, no correction)
+__device__ __forceinline__ uint32_t red_up(uint32_t xs, uint32_t mq24, int32_t nq8) {
+    return mad_i24(mulhi_u24(xs, mq24), nq8, xs);
+}
+
+// four values held in bits 8..15 -> one packed word (byte b from e[b])
+__device__ __forceinline__ uint32_t pack_up(uint32_t e0, uint32_t e1, uint32_t e2, uint32_t e3) {
+    const uint32_t lo = __builtin_amdgcn_perm(e1, e0, 0x0c0c0501u);
+    const uint32_t hi = __builtin_amdgcn_perm(e3, e2, 0x0c0c0501u);
+    return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
 }
 
 template <int LPR, int RI, bool LAST>
@@ -331,8 +347,9 @@ __global__ __launch_bounds__(256) void gj_step_kernel(uint8_t* __restrict__ S, i
         if (blockIdx.x == 0 && threadIdx.x == 0) flags[j] = 1;
         return;
     }
-    const uint32_t q = c_pt.q[j], mu = c_pt.mu16[j];
-    const uint32_t q8 = q << 8, mu8 = mu << 8, half8 = (q >> 1) << 8;
+    const uint32_t q = c_pt.q[j], mq = c_pt.mq24[j];
+    const uint32_t q8 = q << 8, half8 = (q >> 1) << 8;
+    const int32_t nq8 = -(int32_t)q8;
     int* rpj = rowpos + (size_t)j * n;
     const uint8_t* pend_prev = pend + ((size_t)((k + 1) & 1) * kNumPrimes + j) * pitch;
     uint8_t* pend_cur = pend + ((size_t)(k & 1) * kNumPrimes + j) * pitch;
@@ -376,8 +393,8 @@ __global__ __launch_bounds__(256) void gj_step_kernel(uint8_t* __restrict__ S, i
             const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
             for (int b = 0; b < 16; b++) {
-                const uint32_t x = (w[b >> 2] >> (8 * (b & 3))) & 0xffu;
-                vs[b] = (col0 + b == k) ? (pinv << 8) : (red16(__umul24(x, pinv), q, mu) << 8);
+                const uint32_t xs = __umul24(byte_up(w[b >> 2], b & 3), pinv);  // 256 x pinv < 2^24
+                vs[b] = (col0 + b == k) ? (pinv << 8) : red_up(xs, mq, nq8);
             }
         }
         if (own_p) {  // the pivot row's new content goes to the side buffer
@@ -391,7 +408,7 @@ __global__ __launch_bounds__(256) void gj_step_kernel(uint8_t* __restrict__ S, i
                     if (LAST) y = (y > half8 ? y - q8 : y) & 0xff00u;  // balanced, two's complement byte
                     e[b] = y;
                 }
-                o[i] = (e[0] >> 8) | e[1] | (e[2] << 8) | (e[3] << 16);
+                o[i] = pack_up(e[0], e[1], e[2], e[3]);
             }
             *(uint4*)(pend_cur + col0) = make_uint4(o[0], o[1], o[2], o[3]);
         }
@@ -412,12 +429,12 @@ __global__ __launch_bounds__(256) void gj_step_kernel(uint8_t* __restrict__ S, i
                 uint32_t e[4];
 #pragma unroll
                 for (int b = 0; b < 4; b++) {
-                    const uint32_t xs = byte_up(w[i], b) + __umul24(fr, vs[4 * i + b]);
-                    uint32_t y = red16_up(xs, q8, mu8);
+                    const uint32_t xs = byte_up(w[i], b) + __umul24(fr, vs[4 * i + b]);  // 256 (s + f v)
+                    uint32_t y = red_up(xs, mq, nq8);
                     if (LAST) y = (y > half8 ? y - q8 : y) & 0xff00u;
                     e[b] = y;
                 }
-                o[i] = (e[0] >> 8) | e[1] | (e[2] << 8) | (e[3] << 16);
+                o[i] = pack_up(e[0], e[1], e[2], e[3]);
             }
             const int i = row0 + wave * RPW + g + r * 4 * RPW;
             if (!LAST && kk1 >= 0 && kk1 < 16) {
@@ -451,12 +468,12 @@ __global__ __launch_bounds__(256) void gj_finalize_kernel(uint8_t* __restrict__ 
         *(uint32_t*)(dst + col) = *(const uint32_t*)(src + col);
 }
 
-// Rows per thread for the wide-row Gauss-Jordan kernel (8 unless ES_GJ_RI=4):
+// Rows per thread for the wide-row Gauss-Jordan kernel (4 unless ES_GJ_RI=8):
 // a tuning knob, both variants compute the same result.
 static int gj_rows_per_thread() {
     static const int v = [] {
         const char* e = getenv("ES_GJ_RI");
-        return (e && e[0] == '4') ? 4 : 8;
+        return (e && e[0] == '8') ? 8 : 4;
     }();
     return v;
 }
@@ -482,8 +499,8 @@ hipError_t launch_gj_step(const Layout& L, uint8_t* ws, int k, hipStream_t st) {
         case 16: launch_gj_t<16, 2>(L, ws, k, st); break;
         case 32: launch_gj_t<32, 4>(L, ws, k, st); break;
         default:
-            if (gj_rows_per_thread() == 4) launch_gj_t<64, 4>(L, ws, k, st);
-            else launch_gj_t<64, 8>(L, ws, k, st);
+            if (gj_rows_per_thread() == 8) launch_gj_t<64, 8>(L, ws, k, st);
+            else launch_gj_t<64, 4>(L, ws, k, st);
             break;
     }
     if (k == L.n - 1)
@@ -571,23 +588,199 @@ __global__ __launch_bounds__(256) void lift_gemv_kernel(const int8_t* __restrict
                     acc[r][t] = a;
                 }
         }
+        {
 #pragma unroll
-        for (int r = 0; r < RI; r++)
-#pragma unroll
-            for (int t = 0; t < CT; t++)
-#pragma unroll
-                for (int off = LPR / 2; off > 0; off >>= 1) acc[r][t] += __shfl_xor(acc[r][t], off);
-        if (cl == 0) {
-#pragma unroll
-            for (int r = 0; r < RI; r++) {
-                const int i = row0 + wave * RPW + g + r * 4 * RPW;
-                if (i >= n) continue;
-                const size_t kdst = (size_t)rowpos[(size_t)J * n + i] * c;
+            for (int r = 0; r < RI; r++)
 #pragma unroll
                 for (int t = 0; t < CT; t++)
-                    if (t0 + t < c) U[(size_t)jl * NC + kdst + t0 + t] = (uint8_t)mod_i32(acc[r][t], q, mu32);
+#pragma unroll
+                    for (int off = LPR / 2; off > 0; off >>= 1) acc[r][t] += __shfl_xor(acc[r][t], off);
+            if (cl == 0) {
+#pragma unroll
+                for (int r = 0; r < RI; r++) {
+                    const int i = row0 + wave * RPW + g + r * 4 * RPW;
+                    if (i >= n) continue;
+                    const size_t kdst = (size_t)rowpos[(size_t)J * n + i] * c;
+#pragma unroll
+                    for (int t = 0; t < CT; t++)
+                        if (t0 + t < c)
+                            U[(size_t)jl * NC + kdst + t0 + t] = (uint8_t)mod_i32(acc[r][t], q, mu32);
+                }
             }
         }
+    }
+}
+
+// Exchange with a partner lane whose bit BIT differs (a fixed permutation of
+// the wave): data-parallel-primitive moves within a row of 16 lanes, LDS
+// permutes across rows.  Any such pairing serves a butterfly sum.
+template <int BIT>
+__device__ __forceinline__ int xchg_bit(int v, int lane) {
+    if constexpr (BIT >= 16) return __builtin_amdgcn_ds_bpermute((lane ^ BIT) << 2, v);
+    else if constexpr (BIT == 8) return __builtin_amdgcn_update_dpp(0, v, 0x140, 0xf, 0xf, false);  // row_mirror
+    else if constexpr (BIT == 4) return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xf, 0xf, false);  // row_half_mirror
+    else if constexpr (BIT == 2) return __builtin_amdgcn_update_dpp(0, v, 0x4e, 0xf, 0xf, false);   // quad [2,3,0,1]
+    else return __builtin_amdgcn_update_dpp(0, v, 0xb1, 0xf, 0xf, false);                            // quad [1,0,3,2]
+}
+
+// One butterfly level at lane bit BIT over the first 2 * HALF entries of v:
+// keep the half picked by this lane's bit, add the partner's matching half.
+template <int BIT, int HALF, int N>
+__device__ __forceinline__ void split_level(int (&v)[N], int lane) {
+    const bool hi = (lane & BIT) != 0;
+#pragma unroll
+    for (int u = 0; u < HALF; u++) {
+        const int send = hi ? v[u] : v[u + HALF];
+        const int keep = hi ? v[u + HALF] : v[u];
+        v[u] = keep + xchg_bit<BIT>(send, lane);
+    }
+}
+
+// Transposed butterfly sum of RI per-lane row sums (RI in {8, 16}) over the
+// 64 lanes: the first log2(RI) levels split the rows between partner lanes,
+// the rest are plain sums.  Afterwards v[0] of every lane holds the total of
+// row (lane >> (6 - log2 RI)) & (RI - 1); 6 + RI - 1 - log2(RI) exchanges
+// replace 6 RI.
+template <int RI>
+__device__ __forceinline__ void wave_sum_rows(int (&v)[RI], int lane) {
+    static_assert(RI == 8 || RI == 16, "row count");
+    split_level<32, RI / 2>(v, lane);
+    split_level<16, RI / 4>(v, lane);
+    split_level<8, RI / 8>(v, lane);
+    if constexpr (RI == 16) split_level<4, 1>(v, lane);
+    else v[0] += xchg_bit<4>(v[0], lane);
+    v[0] += xchg_bit<2>(v[0], lane);
+    v[0] += xchg_bit<1>(v[0], lane);
+}
+
+// y_j = B_j rho_j for one right-hand side when rows span at least 1 KB
+// (pitch >= 1024): each load instruction of a wave covers 1 KB of one row,
+// a wave owns RI consecutive rows, and the sums meet in a transposed
+// butterfly.  Loads are unconditional: rows past n re-read row n - 1 and
+// lanes past the pitch re-read the pass's first column, and both results
+// are discarded, so the loop has no branches.
+template <int RI>
+__global__ __launch_bounds__(256) void lift_gemv1_kernel(const int8_t* __restrict__ S, int n, int pitch,
+                                                         const int8_t* __restrict__ rho,
+                                                         const LiftParams* __restrict__ prm,
+                                                         const int* __restrict__ rowpos,
+                                                         uint8_t* __restrict__ U) {
+    const int jl = blockIdx.y;
+    const int J = prm->qidx[jl];
+    const uint32_t q = prm->q[jl], mu32 = prm->mu32[jl];
+    const int8_t* Sj = S + (size_t)J * n * pitch;
+    const int8_t* rj = rho + (size_t)jl * pitch;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int rbase = (blockIdx.x * 4 + wave) * RI;
+    const int8_t* rowp[RI];
+#pragma unroll
+    for (int r = 0; r < RI; r++) rowp[r] = Sj + (size_t)min(rbase + r, n - 1) * pitch;
+    int acc[RI];
+#pragma unroll
+    for (int r = 0; r < RI; r++) acc[r] = 0;
+    for (int col0 = 0; col0 < pitch; col0 += 1024) {
+        const int col = col0 + lane * 16;
+        const bool cin = col < pitch;
+        const int colc = cin ? col : col0;
+        uint4 rv = *(const uint4*)(rj + colc);
+        if (!cin) rv = make_uint4(0, 0, 0, 0);
+        uint4 s[RI];
+#pragma unroll
+        for (int r = 0; r < RI; r++) s[r] = *(const uint4*)(rowp[r] + colc);
+#pragma unroll
+        for (int r = 0; r < RI; r++) {
+            int a = acc[r];
+            a = __builtin_amdgcn_sdot4((int)s[r].x, (int)rv.x, a, false);
+            a = __builtin_amdgcn_sdot4((int)s[r].y, (int)rv.y, a, false);
+            a = __builtin_amdgcn_sdot4((int)s[r].z, (int)rv.z, a, false);
+            a = __builtin_amdgcn_sdot4((int)s[r].w, (int)rv.w, a, false);
+            acc[r] = a;
+        }
+    }
+    wave_sum_rows<RI>(acc, lane);
+    constexpr int LOG_RI = RI == 16 ? 4 : 3;
+    if ((lane & ((64 / RI) - 1)) == 0) {
+        const int i = rbase + ((lane >> (6 - LOG_RI)) & (RI - 1));
+        if (i < n) U[(size_t)jl * n + (size_t)rowpos[(size_t)J * n + i]] = (uint8_t)mod_i32(acc[0], q, mu32);
+    }
+}
+
+// ---------------------------------------------------------------- lift: MFMA contraction (c > 1)
+// For several right-hand sides the per-prime product Y_j = B_j R_j is a real
+// int8 GEMM (n x n by n x c), run on v_mfma_i32_16x16x64_i8.  A wave owns 32
+// storage rows (two 16-row tiles) and 16 right-hand sides; B_j streams from
+// HBM once, the block's 16 residue columns (R_j transposed, [t][k]) sit in
+// LDS for the whole K range.  Operand lanes: lane l feeds row (or column)
+// l % 16 with 16 bytes of k; lane group g = l / 16 and register quad u cover
+// k in [kc + 64 u + 16 g, +16), the same for both operands, so every k of a
+// 256-byte block is summed exactly once.  Output lane l holds column l % 16,
+// rows 4 (l / 16) + 0..3 of each 16 x 16 tile.
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+constexpr int kMfmaRowsPerWave = 32;
+constexpr int kMfmaKSeg = 2048;          // k bytes staged in LDS at a time
+constexpr int kMfmaLdsStride = kMfmaKSeg + 16;
+
+__global__ __launch_bounds__(256) void lift_mfma_kernel(const int8_t* __restrict__ S, int n, int pitch, int c,
+                                                        const int8_t* __restrict__ rho,
+                                                        const LiftParams* __restrict__ prm,
+                                                        const int* __restrict__ rowpos,
+                                                        uint8_t* __restrict__ U) {
+    __shared__ __attribute__((aligned(16))) int8_t Bs[16 * kMfmaLdsStride];
+    const int jl = blockIdx.y;
+    const int t0 = blockIdx.z * 16;
+    const int J = prm->qidx[jl];
+    const uint32_t q = prm->q[jl], mu32 = prm->mu32[jl];
+    const int8_t* Sj = S + (size_t)J * n * pitch;
+    const int8_t* rj = rho + (size_t)jl * c * pitch;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int wrow0 = blockIdx.x * (4 * kMfmaRowsPerWave) + wave * kMfmaRowsPerWave;
+    const int ra = wrow0 + lr, rb = wrow0 + 16 + lr;     // this lane's A rows
+    const bool okA = ra < n, okB = rb < n;
+    v4i acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+
+    for (int seg = 0; seg < pitch; seg += kMfmaKSeg) {
+        const int seglen = min(kMfmaKSeg, pitch - seg);
+        __syncthreads();  // previous segment's readers are done
+        // stage R^T[t0 .. t0+15][seg .. seg+seglen) (zero beyond c)
+        for (int idx = threadIdx.x; idx < 16 * (seglen / 16); idx += 256) {
+            const int t = idx / (seglen / 16), off = (idx % (seglen / 16)) * 16;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (t0 + t < c) v = *(const uint4*)(rj + (size_t)(t0 + t) * pitch + seg + off);
+            *(uint4*)(Bs + t * kMfmaLdsStride + off) = v;
+        }
+        __syncthreads();
+        for (int kc = 0; kc < seglen; kc += 256) {
+            v4i a0[4], a1[4], b[4];
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                const int ko = kc + 64 * u + 16 * lg;
+                const bool in = ko < seglen;
+                a0[u] = (okA && in) ? *(const v4i*)(Sj + (size_t)ra * pitch + seg + ko) : v4i{0, 0, 0, 0};
+                a1[u] = (okB && in) ? *(const v4i*)(Sj + (size_t)rb * pitch + seg + ko) : v4i{0, 0, 0, 0};
+                b[u] = in ? *(const v4i*)(Bs + lr * kMfmaLdsStride + ko) : v4i{0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                if (kc + 64 * u < seglen) {
+                    acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0[u], b[u], acc0, 0, 0, 0);
+                    acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1[u], b[u], acc1, 0, 0, 0);
+                }
+            }
+        }
+    }
+    // epilogue: lane holds column t0 + lr, rows 4 lg + 0..3 of each tile
+    const int t = t0 + lr;
+    if (t >= c) return;
+    const size_t NC = (size_t)n * c;
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+        const int i0 = wrow0 + 4 * lg + r, i1 = wrow0 + 16 + 4 * lg + r;
+        if (i0 < n)
+            U[(size_t)jl * NC + (size_t)rowpos[(size_t)J * n + i0] * c + t] = (uint8_t)mod_i32(acc0[r], q, mu32);
+        if (i1 < n)
+            U[(size_t)jl * NC + (size_t)rowpos[(size_t)J * n + i1] * c + t] = (uint8_t)mod_i32(acc1[r], q, mu32);
     }
 }
 
@@ -609,6 +802,15 @@ __global__ __launch_bounds__(256) void garner_wave_kernel(const LiftParams* __re
     if (comp >= NC) return;
     const int E = prm->E;
     const bool live = lane < E;
+    const bool wlane = lane < kDigitWords;
+    // Every per-lane constant of the serial loop is loaded up front, so the
+    // loop's E dependent iterations wait on no memory access.
+    uint32_t gi[kNumPrimes], qw[kNumPrimes];
+#pragma unroll
+    for (int l = 0; l < kNumPrimes; ++l) {
+        gi[l] = live ? prm->ginv[l][lane] : 0u;
+        qw[l] = wlane ? prm->Qw[l][lane] : 0u;
+    }
     const uint32_t qk = live ? prm->q[lane] : 1u;
     const uint32_t muk = live ? prm->mu16[lane] : 0u;
     uint32_t t = live ? U[(size_t)lane * NC + comp] : 0u;
@@ -623,9 +825,9 @@ __global__ __launch_bounds__(256) void garner_wave_kernel(const LiftParams* __re
                 int d = (int)t - vl;  // in (-q_k/2, 3q_k/2) since |v_l| < q_l/2 < q_k/2
                 d = d < 0 ? d + (int)qk : d;
                 d = d >= (int)qk ? d - (int)qk : d;
-                t = red16(__umul24((uint32_t)d, (uint32_t)prm->ginv[l][lane]), qk, muk);
+                t = red16(__umul24((uint32_t)d, gi[l]), qk, muk);
             }
-            if (lane < kDigitWords) acc += (uint64_t)(uint32_t)(vl + 128) * (uint64_t)prm->Qw[l][lane];
+            acc += (uint64_t)(uint32_t)(vl + 128) * (uint64_t)qw[l];
         }
     }
     if (lane < kDigitWords) acc -= prm->corr[lane];
@@ -706,6 +908,48 @@ __global__ __launch_bounds__(256) void residual_kernel(const AT* __restrict__ A,
     }
 }
 
+// The same update for one right-hand side, one block per row: 256 threads
+// cover 1024 columns per pass with 16-byte loads of A (int32) and x_low, the
+// 64-bit sums meet in a wave butterfly and then in LDS, and the first wave
+// writes r_{i+1} and its balanced residues.
+__global__ __launch_bounds__(256) void residual1_kernel(const int32_t* __restrict__ A, int n,
+                                                        int64_t* __restrict__ R,
+                                                        const uint64_t* __restrict__ xlow,
+                                                        const LiftParams* __restrict__ prm,
+                                                        const int* __restrict__ rowpos,
+                                                        int8_t* __restrict__ rho, int pitch) {
+    const int r = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int32_t* a = A + (size_t)r * n;
+    uint64_t acc = 0;
+    if ((n & 3) == 0) {  // rows start 16-byte aligned
+        for (int j0 = tid * 4; j0 < n; j0 += 1024) {
+            const int4 av = *(const int4*)(a + j0);
+            const ulonglong2 x01 = *(const ulonglong2*)(xlow + j0);
+            const ulonglong2 x23 = *(const ulonglong2*)(xlow + j0 + 2);
+            acc += (uint64_t)(int64_t)av.x * x01.x + (uint64_t)(int64_t)av.y * x01.y +
+                   (uint64_t)(int64_t)av.z * x23.x + (uint64_t)(int64_t)av.w * x23.y;
+        }
+    } else {
+        for (int jc = tid; jc < n; jc += 256) acc += (uint64_t)(int64_t)a[jc] * xlow[jc];
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    __shared__ uint64_t part[4];
+    if (lane == 0) part[wave] = acc;
+    __syncthreads();
+    if (wave != 0) return;
+    acc = part[0] + part[1] + part[2] + part[3];
+    const int E = prm->E;
+    const uint64_t val = ((uint64_t)R[r] - acc) * prm->Pinv;
+    if (lane == 0) R[r] = (int64_t)val;
+    if (lane < E) {
+        const uint32_t q = prm->q[lane];
+        const uint32_t res = mod_i64((int64_t)val, q, prm->mu16[lane], prm->mu32[lane], prm->r32[lane]);
+        rho[(size_t)lane * pitch + rowpos[(size_t)prm->qidx[lane] * n + r]] = (int8_t)balanced(res, q);
+    }
+}
+
 hipError_t launch_split_b(const int64_t* b, const Layout& L, uint8_t* ws, int E, hipStream_t st) {
     (void)E;
     hipError_t e = hipMemcpyAsync(ws + L.off_R, b, (size_t)L.n * L.c * sizeof(int64_t),
@@ -746,11 +990,48 @@ static void launch_gemv_c(const Layout& L, uint8_t* ws, int E, hipStream_t st) {
     }
 }
 
+// Contraction path: the v_dot4 GEMV for one right-hand side, MFMA for more
+// (ES_LIFT_VALU=1 keeps the VALU kernel for c > 1, for comparison).
+static bool lift_use_valu() {
+    static const bool v = [] {
+        const char* e = getenv("ES_LIFT_VALU");
+        return e && e[0] == '1';
+    }();
+    return v;
+}
+
+// Rows per wave of the wide-row c = 1 contraction (8 unless ES_GEMV_RI=16):
+// a tuning knob, both compute the same result.
+static int gemv_rows_per_wave() {
+    static const int v = [] {
+        const char* e = getenv("ES_GEMV_RI");
+        return (e && e[0] == '1') ? 16 : 8;
+    }();
+    return v;
+}
+
+template <int RI>
+static void launch_gemv1_t(const Layout& L, uint8_t* ws, int E, hipStream_t st) {
+    dim3 grid((L.n + 4 * RI - 1) / (4 * RI), E);
+    hipLaunchKernelGGL(lift_gemv1_kernel<RI>, grid, dim3(256), 0, st, (const int8_t*)(ws + L.off_S), L.n, L.pitch,
+                       (const int8_t*)(ws + L.off_rho), (const LiftParams*)(ws + L.off_params),
+                       (const int*)(ws + L.off_rowpos), ws + L.off_U);
+}
+
 hipError_t launch_lift_contract(const Layout& L, uint8_t* ws, int E, hipStream_t st) {
-    if (L.c == 1)
+    if (L.c == 1 && L.pitch >= 1024) {
+        if (gemv_rows_per_wave() == 16) launch_gemv1_t<16>(L, ws, E, st);
+        else launch_gemv1_t<8>(L, ws, E, st);
+    } else if (L.c == 1) {
         launch_gemv_c<1>(L, ws, E, st);
-    else
+    } else if (lift_use_valu()) {
         launch_gemv_c<16>(L, ws, E, st);
+    } else {
+        dim3 grid((L.n + 4 * kMfmaRowsPerWave - 1) / (4 * kMfmaRowsPerWave), E, (L.c + 15) / 16);
+        hipLaunchKernelGGL(lift_mfma_kernel, grid, dim3(256), 0, st, (const int8_t*)(ws + L.off_S), L.n, L.pitch,
+                           L.c, (const int8_t*)(ws + L.off_rho), (const LiftParams*)(ws + L.off_params),
+                           (const int*)(ws + L.off_rowpos), ws + L.off_U);
+    }
     return hipGetLastError();
 }
 
@@ -772,8 +1053,7 @@ hipError_t launch_lift_residual(const Layout& L, uint8_t* ws, bool a32, const in
     if (a32) {
         const int32_t* A = (const int32_t*)(ws + L.off_A32);
         if (L.c == 1)
-            hipLaunchKernelGGL((residual_kernel<int32_t, 1>), grid, dim3(256), 0, st, A, L.n, L.c, R, xl, prm,
-                               rp, rho, L.pitch, 0);
+            hipLaunchKernelGGL(residual1_kernel, dim3(L.n), dim3(256), 0, st, A, L.n, R, xl, prm, rp, rho, L.pitch);
         else
             hipLaunchKernelGGL((residual_kernel<int32_t, 16>), grid, dim3(256), 0, st, A, L.n, L.c, R, xl,
                                prm, rp, rho, L.pitch, 0);

@@ -61,6 +61,21 @@ def test_primes_and_strerror():
         assert _lib.strerror(st)
 
 
+def test_round_up_reciprocal_gives_exact_quotients():
+    """The Gauss-Jordan step divides x = s + f v < 2^16 by q with no
+    correction: 256 x times ceil(2^24 / q), high 32 bits of the product, is
+    floor(x / q) for every x < 2^16 and every odd prime q < 256 (the
+    round-up reciprocal with 16 + 8 bits of precision).  Checked
+    exhaustively."""
+    x = np.arange(1 << 16, dtype=np.uint64)
+    for q in es.primes():
+        mq = -(-(1 << 24) // q)
+        assert mq < (1 << 24)
+        t = ((x << np.uint64(8)) * np.uint64(mq)) >> np.uint64(32)
+        assert np.array_equal(t, x // np.uint64(q)), q
+        assert int(x[-1] << np.uint64(8)) < (1 << 24)
+
+
 # ------------------------------------------------------------------ bignum
 
 def to_limbs(v):
