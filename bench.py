@@ -198,8 +198,20 @@ def rooflines(prof, info, n, c, traffic=None):
                                 "algorithmic_bytes_per_launch": int(bytes_per),
                                 "int8_tops": round(ops_per / avg_s / 1e12, 3),
                                 "int8_frac_of_peak": round(ops_per / avg_s / 1e12 / INT8_PEAK_TOPS, 5)}
-    for k in ("garner", "residual", "residues"):
-        ms, cnt = prof[k]
+    ms, cnt = prof.get("recon_gemm", (0.0, 0))
+    if cnt:
+        # one launch per chunk of components: the modular multiply of every component's
+        # digit bytes (42 m of them) by the weight rows (4 NW bytes wide, NW = words of M)
+        NC = n * c
+        nw_m = (info["modulus_bits"] + 31) // 32
+        ops = 2.0 * NC * (42 * info["m"]) * (4 * nw_m)
+        s = ms / 1e3
+        out["recon_gemm"] = {"bound": "mfma", "achieved": round(ops / s / 1e12, 2), "peak": INT8_PEAK_TOPS,
+                             "unit": "TOP/s", "frac": round(ops / s / 1e12 / INT8_PEAK_TOPS, 4),
+                             "avg_launch_us": round(s / cnt * 1e6, 2), "launches": cnt,
+                             "algorithmic_ops_total": ops}
+    for k in ("garner", "residual", "residues", "recon_other", "recon_gcd"):
+        ms, cnt = prof.get(k, (0.0, 0))
         if cnt:
             out[k] = {"avg_launch_us": round(ms / cnt * 1e3, 2), "launches": cnt, "total_ms": round(ms, 3)}
     return out

@@ -20,7 +20,7 @@ DIGIT_LIMBS = 6
 
 EXPORTS = ["es_strerror", "es_primes", "es_workspace_bytes", "es_solve_device", "es_solve",
            "es_solution_rows", "es_solution_cols", "es_solution_get", "es_solution_info",
-           "es_solution_free", "es_last_timings", "es_set_profiling", "es_kernel_profile",
+           "es_solution_free", "es_solution_modulus_bits", "es_set_gpu_reconstruction", "es_last_timings", "es_set_profiling", "es_kernel_profile",
            "es_batched_inverse", "es_lift_digits", "es_reconstruct"]
 
 _lib = None
@@ -66,8 +66,12 @@ def load():
     lib.es_solution_info.restype = ctypes.c_int
     lib.es_solution_free.argtypes = [c_vp]
     lib.es_solution_free.restype = None
+    lib.es_solution_modulus_bits.argtypes = [c_vp]
+    lib.es_solution_modulus_bits.restype = ctypes.c_int32
     lib.es_last_timings.argtypes = [ctypes.POINTER(ctypes.c_double)]
     lib.es_last_timings.restype = ctypes.c_int
+    lib.es_set_gpu_reconstruction.argtypes = [ctypes.c_int]
+    lib.es_set_gpu_reconstruction.restype = ctypes.c_int
     lib.es_set_profiling.argtypes = [ctypes.c_int]
     lib.es_set_profiling.restype = ctypes.c_int
     lib.es_kernel_profile.argtypes = [ctypes.POINTER(ctypes.c_double), c_i32p, ctypes.c_int32]
@@ -121,17 +125,24 @@ def solution_info(sol):
     lib = load()
     live, m, nb, db = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
     lib.es_solution_info(sol, ctypes.byref(live), ctypes.byref(m), ctypes.byref(nb), ctypes.byref(db))
-    return {"live_primes": live.value, "m": m.value, "num_bound_bits": nb.value, "den_bound_bits": db.value}
+    return {"live_primes": live.value, "m": m.value, "num_bound_bits": nb.value, "den_bound_bits": db.value,
+            "modulus_bits": lib.es_solution_modulus_bits(sol)}
 
 
 def last_timings():
     buf = (ctypes.c_double * 5)()
     load().es_last_timings(buf)
-    return {"checks_ms": buf[0], "inverse_ms": buf[1], "lift_ms": buf[2], "d2h_ms": buf[3],
+    return {"checks_ms": buf[0], "inverse_ms": buf[1], "lift_ms": buf[2], "recon_gpu_ms": buf[3],
             "reconstruct_ms": buf[4]}
 
 
-KERNEL_CLASSES = ["gj_step", "lift_contract", "garner", "residual", "residues"]
+KERNEL_CLASSES = ["gj_step", "lift_contract", "garner", "residual", "residues", "recon_gemm", "recon_other",
+                  "recon_gcd"]
+
+
+def set_gpu_reconstruction(on: bool):
+    """Reconstruct on the GPU (default) or on the host, for this thread."""
+    load().es_set_gpu_reconstruction(1 if on else 0)
 
 
 def set_profiling(on: bool):

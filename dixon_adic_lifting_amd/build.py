@@ -18,8 +18,8 @@ LIB = os.path.join(HERE, "libexact_solve.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-DEVICE_SOURCES = ["kernels.hip"]
-HOST_SOURCES = ["api.cpp", "host.cpp", "bignum.cpp", "debug.cpp"]
+DEVICE_SOURCES = ["kernels.hip", "recon.hip"]
+HOST_SOURCES = ["api.cpp", "host.cpp", "bignum.cpp", "debug.cpp", "recon_host.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{CSRC}",
           f"-I{os.path.join(os.path.dirname(HERE), 'include')}"]
 DEVICE_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

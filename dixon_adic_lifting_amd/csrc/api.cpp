@@ -18,6 +18,7 @@
 #include "../../include/es_solve.h"
 #include "es_internal.h"
 #include "host.h"
+#include "recon_host.h"
 
 using namespace es;
 
@@ -41,13 +42,15 @@ double ms_since(clk::time_point t0) {
 
 // Opt-in per-launch timing: a pair of HIP events on the solve's stream around
 // every launch of the hot kernels; totals are read after the final sync.
-enum KernelClass { KC_GJ = 0, KC_CONTRACT = 1, KC_GARNER = 2, KC_RESIDUAL = 3, KC_RESIDUES = 4, KC_COUNT = 5 };
+// Classes 5, 6 and 7 (reconstruction GEMM, other reconstruction kernels,
+// gcds) are declared with the reconstruction driver.
+enum KernelClass { KC_GJ = 0, KC_CONTRACT = 1, KC_GARNER = 2, KC_RESIDUAL = 3, KC_RESIDUES = 4, KC_COUNT = 8 };
 
 thread_local bool g_profiling = false;
-thread_local double g_kernel_ms[KC_COUNT] = {0, 0, 0, 0, 0};
-thread_local int32_t g_kernel_cnt[KC_COUNT] = {0, 0, 0, 0, 0};
+thread_local double g_kernel_ms[KC_COUNT] = {0, 0, 0, 0, 0, 0, 0, 0};
+thread_local int32_t g_kernel_cnt[KC_COUNT] = {0, 0, 0, 0, 0, 0, 0, 0};
 
-struct Profiler {
+struct Profiler : KernelTimer {
     bool on = false;
     hipStream_t st = nullptr;
     std::vector<hipEvent_t> pool;
@@ -67,7 +70,7 @@ struct Profiler {
         return pool[used++];
     }
     // returns the index of the start event (or -1 when off)
-    long start(int cls) {
+    long start(int cls) override {
         if (!on) return -1;
         hipEvent_t e = next();
         if (!e) return -1;
@@ -75,7 +78,7 @@ struct Profiler {
         marks.push_back({cls, used - 1});
         return (long)(used - 1);
     }
-    void stop(long idx) {
+    void stop(long idx) override {
         if (idx < 0) return;
         hipEvent_t e = next();
         if (e) (void)hipEventRecord(e, st);
@@ -194,10 +197,13 @@ struct PinnedBuffer {
 thread_local PinnedBuffer g_pinned;
 
 // Lift m steps; digits land in host [n*c][m][6].
+// With dig_dev set, the digits stay on the device ([n*c][m][6] at dig_dev)
+// and digits_host is unused.
 int run_lift(const int64_t* dA, const int64_t* db, uint8_t* ws, hipStream_t st, const Prep& pr,
-             const LiveSet& ls, int m, int64_t* digits_host, Profiler* prof) {
+             const LiveSet& ls, int m, int64_t* digits_host, Profiler* prof, uint64_t* dig_dev = nullptr) {
     Layout L = pr.L;
-    if (m <= L.kchunk) L.kchunk = m;  // one chunk: the device digits are laid out exactly as the host's
+    if (m <= L.kchunk || dig_dev) L.kchunk = m;  // one chunk: the device digits are laid out exactly as the host's
+    L.dig_dev = dig_dev;
     LiftParams prm;
     fill_lift_params(ls, &prm);
     HIP_CHECK(hipMemcpyAsync(ws + L.off_params, &prm, sizeof prm, hipMemcpyHostToDevice, st));
@@ -216,7 +222,9 @@ int run_lift(const int64_t* dA, const int64_t* db, uint8_t* ws, hipStream_t st, 
             HIP_CHECK(launch_lift_residual(L, ws, pr.a32, dA, st));
             prof->stop(ev);
         }
-        if (cnt == m) {
+        if (dig_dev) {
+            // digits stay on the device for the GPU reconstruction
+        } else if (cnt == m) {
             HIP_CHECK(hipMemcpyAsync(digits_host, ws + L.off_digits, NC * (size_t)m * kDigitLimbs * 8,
                                      hipMemcpyDeviceToHost, st));
         } else {
@@ -255,6 +263,11 @@ int es_primes(int32_t* q, int32_t cap) {
 size_t es_workspace_bytes(int32_t n, int32_t c) {
     if (!valid_shape(n, c)) return 0;
     return make_layout(n, c).total;
+}
+
+int es_set_gpu_reconstruction(int on) {
+    set_gpu_recon(on != 0);
+    return ES_OK;
 }
 
 int es_set_profiling(int on) {
@@ -302,18 +315,41 @@ int es_solve_device(const int64_t* dA, const int64_t* db, int32_t n, int32_t c, 
         if (ls.E == 0) return no_prime_decision(dA, n, pr, st);
         BigInt M;
         const int m = choose_m(ls.P, pr.nbits, pr.dbits, &M);
-        int64_t* digits = (int64_t*)g_pinned.get((size_t)n * c * m * kDigitLimbs * sizeof(int64_t));
-        if (!digits) return ES_ENOMEM;
-        t0 = clk::now();
-        rc = run_lift(dA, db, ws, st, pr, ls, m, digits, &prof);
-        g_timings[2] = ms_since(t0);
-        if (rc != ES_OK) return rc;
-        prof.collect();
-        t0 = clk::now();
-        es_solution* sol = new es_solution;
-        rc = reconstruct(digits, (size_t)m, n, c, m, ls.P, M, pr.nbits, pr.dbits, default_threads(),
-                         &sol->data);
-        g_timings[4] = ms_since(t0);
+        GpuReconPlan plan;
+        uint8_t* scr = nullptr;
+        if (!gpu_recon_disabled()) {
+            plan = plan_gpu_recon(n, c, m, M, pr.nbits);
+            if (plan.ok) scr = gpu_recon_scratch(plan);
+        }
+        es_solution* sol = nullptr;
+        if (scr) {
+            // lift into device digits, then the GEMM-based reconstruction
+            t0 = clk::now();
+            rc = run_lift(dA, db, ws, st, pr, ls, m, nullptr, &prof, (uint64_t*)(scr + plan.off_digits));
+            g_timings[2] = ms_since(t0);
+            if (rc != ES_OK) return rc;
+            t0 = clk::now();
+            sol = new es_solution;
+            GpuReconTimes rt;
+            rc = reconstruct_gpu(plan, scr, ls.P, M, pr.nbits, pr.dbits, default_threads(), st, &sol->data, &rt,
+                                 &prof);
+            g_timings[3] = rt.gpu_ms;
+            g_timings[4] = ms_since(t0);
+            prof.collect();
+        } else {
+            int64_t* digits = (int64_t*)g_pinned.get((size_t)n * c * m * kDigitLimbs * sizeof(int64_t));
+            if (!digits) return ES_ENOMEM;
+            t0 = clk::now();
+            rc = run_lift(dA, db, ws, st, pr, ls, m, digits, &prof);
+            g_timings[2] = ms_since(t0);
+            if (rc != ES_OK) return rc;
+            prof.collect();
+            t0 = clk::now();
+            sol = new es_solution;
+            rc = reconstruct(digits, (size_t)m, n, c, m, ls.P, M, pr.nbits, pr.dbits, default_threads(),
+                             &sol->data);
+            g_timings[4] = ms_since(t0);
+        }
         if (rc != ES_OK) {
             delete sol;
             return rc;
@@ -322,6 +358,7 @@ int es_solve_device(const int64_t* dA, const int64_t* db, int32_t n, int32_t c, 
         sol->data.m = m;
         sol->data.nbits = pr.nbits;
         sol->data.dbits = pr.dbits;
+        sol->data.mbits = (int)M.bit_length();
         *out = sol;
         return ES_OK;
     } catch (const std::bad_alloc&) {
@@ -379,6 +416,8 @@ int es_solution_info(const es_solution* s, int32_t* live_primes, int32_t* m, int
     if (den_bound_bits) *den_bound_bits = s->data.dbits;
     return ES_OK;
 }
+
+int32_t es_solution_modulus_bits(const es_solution* s) { return s ? s->data.mbits : 0; }
 
 void es_solution_free(es_solution* s) { delete s; }
 

@@ -110,6 +110,7 @@ struct Layout {
     size_t off_digits;    // uint64 [n*c][kchunk][6]   digits of a chunk of steps
     size_t off_params;    // LiftParams
     size_t total;
+    uint64_t* dig_dev;    // when set, the digits go here ([n*c][kchunk][6]) instead
 };
 
 Layout make_layout(int n, int c);
@@ -130,5 +131,20 @@ hipError_t launch_split_b(const int64_t* b, const Layout& L, uint8_t* ws, int E,
 hipError_t launch_lift_contract(const Layout& L, uint8_t* ws, int E, hipStream_t st);
 hipError_t launch_lift_garner(const Layout& L, uint8_t* ws, int slot, hipStream_t st);
 hipError_t launch_lift_residual(const Layout& L, uint8_t* ws, bool a32, const int64_t* A64, hipStream_t st);
+
+// reconstruction on the GPU (recon.hip); see the kernels for layouts
+hipError_t launch_digit_bytes(const uint64_t* digits, int dstride, int m, int j0, int valid_rows, int rows_pad,
+                              int Kpad, int8_t* S, int* rowsum, hipStream_t st);
+hipError_t launch_wchain(const uint32_t* T, const uint32_t* Mw, int m, int TM, double Md, int Ncolsp, uint8_t* W,
+                         hipStream_t st);
+int wchain_words_per_lane(int NW);  // 0 when NW words do not fit one wave
+hipError_t launch_transpose_offset(const uint8_t* W, int Kpad, int Ncolsp, int8_t* WT, hipStream_t st);
+hipError_t launch_recon_gemm(const int8_t* S, const int8_t* WT, int Kpad, int NCcp, int Ncolsp, int* VT,
+                             hipStream_t st);
+int gcd_words_per_lane(int words);  // 0 when the numbers do not fit one wave
+hipError_t launch_gcd(const uint32_t* Y, int nw, const int* status, int valid_rows, const uint32_t* Dw, int nwd,
+                      uint64_t* G, int* gstat, hipStream_t st);
+hipError_t launch_numer(const int* VT, const int* rowsum, int NCcp, int valid_rows, const uint32_t* Mw, int TM,
+                        double Mtop, int nbits, uint32_t* Y, int* status, hipStream_t st);
 
 }  // namespace es

@@ -262,7 +262,7 @@ static void parallel_for(size_t count, int nthreads, F&& fn) {
 }
 
 // X = sum_{i<m} x_i P^i from balanced 384-bit two's-complement digits (Horner).
-static BigInt assemble(const int64_t* dig, int m, const BigInt& P) {
+BigInt assemble(const int64_t* dig, int m, const BigInt& P) {
     BigInt X;
     for (int i = m - 1; i >= 0; i--)
         X = add(mul(X, P), BigInt::from_twos((const uint64_t*)(dig + (size_t)i * kDigitLimbs), kDigitLimbs));
@@ -275,6 +275,38 @@ static bool verbose() {
         return e && *e && *e != '0';
     }();
     return v;
+}
+
+void parallel_for_each(size_t count, int nthreads, const std::function<void(size_t)>& fn) {
+    parallel_for(count, nthreads, fn);
+}
+
+std::vector<size_t> sample_indices(size_t NC, int c) {
+    // the first row (one component of every right-hand side: their
+    // denominators can differ), then every ceil(NC / 4)-th component
+    const size_t step = std::max<size_t>(1, (NC + 3) / 4);
+    std::vector<size_t> sample;
+    for (size_t t = 0; t < (size_t)c && t < NC; t++) sample.push_back(t);
+    for (size_t j = 0; j < NC; j += step)
+        if (j >= (size_t)c) sample.push_back(j);
+    return sample;
+}
+
+bool sample_denominator(const std::vector<BigInt>& xs, const BigInt& M, int nbits, int dbits, int nthreads,
+                        BigInt* d) {
+    const BigInt Nb = shl(BigInt::from_u64(1), (size_t)nbits);
+    const BigInt Db = shl(BigInt::from_u64(1), (size_t)dbits);
+    std::vector<BigInt> sden(xs.size());
+    std::atomic<int> bad{0};
+    parallel_for(xs.size(), nthreads, [&](size_t s) {
+        BigInt a = mod_floor(xs[s], M), nu, de;
+        if (!rational_reconstruct(a, M, Nb, Db, &nu, &de)) bad = 1;
+        else sden[s] = de;
+    });
+    if (bad) return false;
+    *d = BigInt::from_u64(1);
+    for (auto& v : sden) *d = lcm(*d, v);
+    return true;
 }
 
 int reconstruct(const int64_t* digits, size_t stride_m, int n, int c, int m, const BigInt& P,
@@ -296,20 +328,11 @@ int reconstruct(const int64_t* digits, size_t stride_m, int n, int c, int m, con
     const BigInt Db = shl(BigInt::from_u64(1), (size_t)dbits);
     BigInt Mhalf = shr_abs(M, 1);
 
-    // common denominator from the sample: component 0, then every ceil(NC/4)-th
-    const size_t step = std::max<size_t>(1, (NC + 3) / 4);
-    std::vector<size_t> sample;
-    for (size_t j = 0; j < NC; j += step) sample.push_back(j);
-    std::vector<BigInt> sden(sample.size());
-    std::atomic<int> bad{0};
-    parallel_for(sample.size(), nthreads, [&](size_t s) {
-        BigInt a = mod_floor(X[sample[s]], M), nu, de;
-        if (!rational_reconstruct(a, M, Nb, Db, &nu, &de)) bad = 1;
-        else sden[s] = de;
-    });
-    if (bad) return ES_EINTERNAL;
-    BigInt d = BigInt::from_u64(1);
-    for (auto& v : sden) d = lcm(d, v);
+    // common denominator from the sample
+    std::vector<BigInt> xs;
+    for (size_t j : sample_indices(NC, c)) xs.push_back(X[j]);
+    BigInt d;
+    if (!sample_denominator(xs, M, nbits, dbits, nthreads, &d)) return ES_EINTERNAL;
     lap("sample");
 
     out->n = n;

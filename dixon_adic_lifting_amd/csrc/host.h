@@ -3,6 +3,7 @@
 // rational reconstruction.
 #pragma once
 #include <cstdint>
+#include <functional>
 #include <vector>
 
 #include "bignum.h"
@@ -14,6 +15,7 @@ struct SolutionData {
     int n = 0, c = 0;
     std::vector<BigInt> num, den;  // [n*c], lowest terms, den > 0
     int live = 0, m = 0, nbits = 0, dbits = 0;
+    int mbits = 0;  // bit length of M = P^m
 };
 
 // Live prime set: indices into the 53-prime table, ascending.
@@ -45,5 +47,21 @@ int reconstruct(const int64_t* digits, size_t stride_m, int n, int c, int m, con
                 const BigInt& M, int nbits, int dbits, int nthreads, SolutionData* out);
 
 int default_threads();
+
+// X = sum_{i<m} x_i P^i from one component's digits (int64 [m][6]).
+BigInt assemble(const int64_t* dig, int m, const BigInt& P);
+
+// Runs fn(i) for i in [0, count) on up to nthreads host threads.
+void parallel_for_each(size_t count, int nthreads, const std::function<void(size_t)>& fn);
+
+// The sampled common denominator (card, "Method"): d = lcm of the reduced
+// denominators of the sample components (the first row, i.e. one component
+// of every right-hand side, then every ceil(NC / 4)-th component in
+// row-major order), each found by Wang reconstruction of X mod M.  xs[k] is
+// the k-th sample's X.  Returns false if some sample has no fraction within
+// the bounds.
+std::vector<size_t> sample_indices(size_t NC, int c);
+bool sample_denominator(const std::vector<BigInt>& xs, const BigInt& M, int nbits, int dbits, int nthreads,
+                        BigInt* d);
 
 }  // namespace es

@@ -1039,7 +1039,8 @@ hipError_t launch_lift_garner(const Layout& L, uint8_t* ws, int slot, hipStream_
     const int NC = L.n * L.c;
     hipLaunchKernelGGL(garner_wave_kernel, dim3((NC + 3) / 4), dim3(256), 0, st,
                        (const LiftParams*)(ws + L.off_params), (const uint8_t*)(ws + L.off_U), NC,
-                       (uint64_t*)(ws + L.off_digits), L.kchunk, slot, (uint64_t*)(ws + L.off_xlow));
+                       L.dig_dev ? L.dig_dev : (uint64_t*)(ws + L.off_digits), L.kchunk, slot,
+                       (uint64_t*)(ws + L.off_xlow));
     return hipGetLastError();
 }
 

@@ -1,0 +1,572 @@
+// HIP kernels for the rational-reconstruction stage on CDNA4 (gfx950).
+//
+// Method (exact-solve card, phanerozoic/exact-solve, section "Method"): once
+// P^m exceeds twice the product of the Hadamard bounds, a common denominator
+// d comes from a small sample of components, and every numerator is then one
+// modular multiply, y = d X mods M with M = P^m and X = sum_i x_i P^i; y is
+// accepted when |y| <= N.  Here all numerators are formed at once as one
+// int8 GEMM on the matrix cores:
+//
+//   X_j = sum_{i, b} s_{j,i,b} 256^b P^i, where s_{j,i,b} are the balanced
+//   bytes of the balanced base-P digit x_i of component j, so
+//   d X_j = sum_{i, b} s_{j,i,b} W_{i,b}  (mod M),  W_{i,b} = 256^b P^i d mod M.
+//
+// Every weight lies in [0, 2M), so the GEMM's column sums (bytes of V_j)
+// carry a value |V_j| < K 256 M, and y_j = V_j - t_j M with a one-word
+// quotient t_j = round(V_j / M) that double precision gives exactly whenever
+// |y_j| is as small as an accepted numerator must be.
+//
+// Weight rows W_{i,0} = P^i d mod M come from the host (a chain with known
+// quotients); the rows for b = 1..41 are byte shifts reduced again, one wave
+// per i (wchain_kernel).  The matrix is transposed so that both GEMM operands
+// stream 16 bytes of the contraction index per lane.
+#include <hip/hip_runtime.h>
+
+#include "es_internal.h"
+
+namespace es {
+
+// ---------------------------------------------------------------- digit bytes
+// One block per component row: 42 balanced bytes (each in [-128, 127]) of
+// every 384-bit two's-complement digit x_i, |x_i| < 2^333, then 6 zero
+// bytes, so slot i occupies bytes [48 i, 48 i + 48) of the row; slots past m
+// and rows past the chunk's valid rows are zero.  rowsum = sum of the row's
+// bytes (the GEMM stores weights offset by -128, see recon_gemm_kernel).
+__global__ __launch_bounds__(256) void digit_bytes_kernel(const uint64_t* __restrict__ digits, int dstride,
+                                                          int m, int j0, int valid_rows, int Kpad,
+                                                          int8_t* __restrict__ S, int* __restrict__ rowsum) {
+    const int r = blockIdx.x;
+    const int nslot = Kpad / 48;
+    int sum = 0;
+    for (int i = threadIdx.x; i < nslot; i += 256) {
+        uint32_t outw[12];
+#pragma unroll
+        for (int w = 0; w < 12; w++) outw[w] = 0;
+        if (r < valid_rows && i < m) {
+            const uint64_t* x = digits + ((size_t)(j0 + r) * dstride + i) * kDigitLimbs;
+            uint64_t u[kDigitLimbs];
+#pragma unroll
+            for (int w = 0; w < kDigitLimbs; w++) u[w] = x[w];
+            int carry = 0;
+#pragma unroll
+            for (int b = 0; b < 41; b++) {
+                const int v = (int)((u[b >> 3] >> (8 * (b & 7))) & 0xffu) + carry;
+                const int s = v >= 128 ? v - 256 : v;
+                carry = v >= 128 ? 1 : 0;
+                sum += s;
+                outw[b >> 2] |= ((uint32_t)s & 0xffu) << (8 * (b & 3));
+            }
+            // bits 328..335 read as a signed byte are x >> 328 (in [-32, 31])
+            const int s41 = (int)(int8_t)((u[5] >> 8) & 0xffu) + carry;
+            sum += s41;
+            outw[10] |= ((uint32_t)s41 & 0xffu) << 8;
+        }
+        uint4* dst = (uint4*)(S + (size_t)r * Kpad + (size_t)i * 48);
+        dst[0] = make_uint4(outw[0], outw[1], outw[2], outw[3]);
+        dst[1] = make_uint4(outw[4], outw[5], outw[6], outw[7]);
+        dst[2] = make_uint4(outw[8], outw[9], outw[10], outw[11]);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+    __shared__ int part[4];
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = sum;
+    __syncthreads();
+    if (threadIdx.x == 0) rowsum[r] = part[0] + part[1] + part[2] + part[3];
+}
+
+// ---------------------------------------------------------------- weight chains
+// A wave-resident integer of NW = TM + 1 32-bit words (TM = index of the top
+// word of M); lane l holds words [l CW, l CW + CW).  One step replaces
+// R in [0, 2M) by 256 R - t M with t = max(0, floor(256 R / M - 2^-16)):
+// the quotient estimate from the top three words of R and M in double
+// precision is within 2^-19 of the true value, so t is the true floor or one
+// less and the result stays in [0, 2M) without a comparison.
+template <int CW>
+__device__ __forceinline__ void wave_mul_reduce(uint32_t (&R)[CW], const uint32_t (&Mr)[CW], int lane, int TM,
+                                                double Md, uint32_t s) {
+    // top-word approximation of R (same window as Md), summed in lane 0's order
+    double loc = 0.0;
+#pragma unroll
+    for (int c = 0; c < CW; c++) {
+        const int w = lane * CW + c;
+        const int e = w - TM;
+        if (e >= -2 && e <= 0) loc += (double)R[c] * (e == 0 ? 1.0 : e == -1 ? 0x1p-32 : 0x1p-64);
+    }
+    // at most two lanes hold the window: gather their parts into lane 0's sum
+    double tot = 0.0;
+    for (int src = (TM - 2) / CW; src <= TM / CW && src < 64; src++)
+        tot += __shfl(loc, src);
+    double q = (double)s * tot / Md - 0x1p-16;
+    int t = q <= 0.0 ? 0 : (int)q;
+    t = __builtin_amdgcn_readfirstlane(t);
+    // local multiply-subtract with a carry chain
+    int64_t carry = 0;
+#pragma unroll
+    for (int c = 0; c < CW; c++) {
+        const int64_t acc = carry + (int64_t)((uint64_t)s * R[c]) - (int64_t)((uint64_t)(uint32_t)t * Mr[c]);
+        R[c] = (uint32_t)acc;
+        carry = acc >> 32;
+    }
+    // carries into the next lane, then single-unit ripples until none remain
+    int64_t cin = __shfl_up(carry, 1);
+    if (lane == 0) cin = 0;
+    for (;;) {
+#pragma unroll
+        for (int c = 0; c < CW; c++) {  // a zero carry leaves the words unchanged
+            const int64_t v = (int64_t)R[c] + cin;
+            R[c] = (uint32_t)v;
+            cin = v >> 32;
+        }
+        // cin is now the unit carried out of this lane's words (0 or +-1)
+        int64_t up = __shfl_up(cin, 1);
+        if (lane == 0) up = 0;
+        if (__ballot(up != 0) == 0) break;
+        cin = up;
+    }
+}
+
+// Weight rows: block i holds T_i = P^i d mod M (host, words in [0, M)) and
+// writes rows 48 i + b, b < 42, of W [Kpad][Ncolsp] (u8, little-endian bytes
+// of R_{i,b} = 256^b T_i reduced into [0, 2M)); rows 48 i + 42 .. 48 i + 47
+// are zero.  Ncolsp / 4 <= 64 CW words per row are written, zero beyond TM.
+template <int CW>
+__global__ __launch_bounds__(64) void wchain_kernel(const uint32_t* __restrict__ T, const uint32_t* __restrict__ Mw,
+                                                    int TM, double Md, int Ncolsp, uint8_t* __restrict__ W) {
+    const int i = blockIdx.x;
+    const int lane = threadIdx.x;
+    uint32_t R[CW], Mr[CW];
+#pragma unroll
+    for (int c = 0; c < CW; c++) {
+        const int w = lane * CW + c;
+        R[c] = w <= TM ? T[(size_t)i * (TM + 1) + w] : 0u;
+        Mr[c] = w <= TM ? Mw[w] : 0u;
+    }
+    const int rowwords = Ncolsp / 4;
+    for (int b = 0; b < 48; b++) {
+        uint32_t* dst = (uint32_t*)(W + (size_t)(48 * i + b) * Ncolsp);
+#pragma unroll
+        for (int c = 0; c < CW; c++) {
+            const int w = lane * CW + c;
+            if (w < rowwords) dst[w] = b < 42 ? R[c] : 0u;
+        }
+        if (b < 41) wave_mul_reduce<CW>(R, Mr, lane, TM, Md, 256u);
+    }
+}
+
+// WT[col][k] = W[k][col] - 128 (as int8): 64 x 64 byte tiles through LDS.
+__global__ __launch_bounds__(256) void transpose_offset_kernel(const uint8_t* __restrict__ W, int Kpad, int Ncolsp,
+                                                               int8_t* __restrict__ WT) {
+    __shared__ uint8_t tile[64][64 + 4];
+    const int k0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+    const int t = threadIdx.x;
+    {
+        const int rr = t >> 2, cc = (t & 3) * 16;
+        const uint4 v = *(const uint4*)(W + (size_t)(k0 + rr) * Ncolsp + c0 + cc);
+        const uint32_t ws[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 16; q++) tile[rr][cc + q] = (uint8_t)(ws[q >> 2] >> (8 * (q & 3)));
+    }
+    __syncthreads();
+    {
+        const int cr = t >> 2, kk = (t & 3) * 16;  // output row (column of W), 16 k values
+        uint32_t ws[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int q = 0; q < 16; q++) ws[q >> 2] |= (uint32_t)(tile[kk + q][cr] ^ 0x80u) << (8 * (q & 3));
+        *(uint4*)(WT + (size_t)(c0 + cr) * Kpad + k0 + kk) = make_uint4(ws[0], ws[1], ws[2], ws[3]);
+    }
+}
+
+// ---------------------------------------------------------------- the GEMM
+// VT[col][j] = sum_k S[j][k] WT[col][k] (int8 x int8 -> int32) on
+// v_mfma_i32_16x16x64_i8.  Block tile 128 (rows j) x 128 (columns) staged in
+// LDS 64 bytes of k at a time; four waves in a 2 x 2 arrangement, each owning
+// a 64 x 64 tile as 4 x 4 MFMA tiles.  Operand lanes: lane l feeds row (or
+// column) l % 16 with the 16 bytes k in [16 (l / 16), +16) of the 64-byte
+// chunk; output lane l holds column l % 16, rows 4 (l / 16) + 0..3.  Row and
+// column counts are multiples of 128 and Kpad of 64 (the caller pads), so
+// nothing is bounds-checked.
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+constexpr int kGemmLds = 64 + 16;  // LDS row stride, bytes
+
+__global__ __launch_bounds__(256) void recon_gemm_kernel(const int8_t* __restrict__ S, const int8_t* __restrict__ WT,
+                                                         int Kpad, int NCcp, int* __restrict__ VT) {
+    __shared__ __attribute__((aligned(16))) int8_t As[128 * kGemmLds];
+    __shared__ __attribute__((aligned(16))) int8_t Bs[128 * kGemmLds];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int wr = wave >> 1, wc = wave & 1;
+    const int j0 = blockIdx.y * 128, c0 = blockIdx.x * 128;
+    const int lr = lane & 15, lg = lane >> 4;
+    v4i acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; a++)
+#pragma unroll
+        for (int b = 0; b < 4; b++) acc[a][b] = v4i{0, 0, 0, 0};
+    // global -> LDS: thread t moves rows t / 4 and t / 4 + 64, 16-byte chunk t % 4
+    const int gr = t >> 2, gc = (t & 3) * 16;
+    const int8_t* Ag0 = S + (size_t)(j0 + gr) * Kpad + gc;
+    const int8_t* Ag1 = S + (size_t)(j0 + gr + 64) * Kpad + gc;
+    const int8_t* Bg0 = WT + (size_t)(c0 + gr) * Kpad + gc;
+    const int8_t* Bg1 = WT + (size_t)(c0 + gr + 64) * Kpad + gc;
+    v4i ra0 = *(const v4i*)Ag0, ra1 = *(const v4i*)Ag1, rb0 = *(const v4i*)Bg0, rb1 = *(const v4i*)Bg1;
+    for (int k = 0; k < Kpad; k += 64) {
+        __syncthreads();  // previous chunk's fragments are read
+        *(v4i*)(As + gr * kGemmLds + gc) = ra0;
+        *(v4i*)(As + (gr + 64) * kGemmLds + gc) = ra1;
+        *(v4i*)(Bs + gr * kGemmLds + gc) = rb0;
+        *(v4i*)(Bs + (gr + 64) * kGemmLds + gc) = rb1;
+        __syncthreads();
+        if (k + 64 < Kpad) {  // next chunk's loads overlap this chunk's MFMAs
+            ra0 = *(const v4i*)(Ag0 + k + 64);
+            ra1 = *(const v4i*)(Ag1 + k + 64);
+            rb0 = *(const v4i*)(Bg0 + k + 64);
+            rb1 = *(const v4i*)(Bg1 + k + 64);
+        }
+        v4i fa[4], fb[4];
+#pragma unroll
+        for (int a = 0; a < 4; a++) fa[a] = *(const v4i*)(As + (64 * wr + 16 * a + lr) * kGemmLds + 16 * lg);
+#pragma unroll
+        for (int b = 0; b < 4; b++) fb[b] = *(const v4i*)(Bs + (64 * wc + 16 * b + lr) * kGemmLds + 16 * lg);
+#pragma unroll
+        for (int a = 0; a < 4; a++)
+#pragma unroll
+            for (int b = 0; b < 4; b++) acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[a], fb[b], acc[a][b], 0, 0, 0);
+    }
+#pragma unroll
+    for (int a = 0; a < 4; a++)
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+            const int col = c0 + 64 * wc + 16 * b + lr;
+            const int j = j0 + 64 * wr + 16 * a + 4 * lg;
+            *(v4i*)(VT + (size_t)col * NCcp + j) = acc[a][b];
+        }
+}
+
+// ---------------------------------------------------------------- numerators
+// One lane per component: V = sum_col (VT[col][j] + 128 rowsum_j) 256^col
+// (undoing the -128 offset of the weights), t = round(V / M) from the twelve
+// top columns in double precision (exact whenever |V - t M| is far below
+// M / 2, as for every acceptable numerator), y = V - t M in one carry pass
+// over the words.  status[j]: 0 when 0 <= y < 2^nbits, 1 when
+// -2^nbits <= y < 0 (Y[j] holds words 0 .. nbits / 32 of y, two's
+// complement), 2 otherwise (the host reconstructs that component alone).
+__global__ __launch_bounds__(256) void numer_kernel(const int* __restrict__ VT, const int* __restrict__ rowsum,
+                                                    int NCcp, int valid_rows, const uint32_t* __restrict__ Mw,
+                                                    int TM, double Mtop, int nbits, uint32_t* __restrict__ Y,
+                                                    int* __restrict__ status) {
+    const int j = blockIdx.x * 256 + threadIdx.x;
+    if (j >= valid_rows) return;
+    const int64_t off = 128 * (int64_t)rowsum[j];
+    const int NW = TM + 1;
+    const int hw = nbits / 32, hb = nbits % 32, nw = hw + 1;
+    const int* vj = VT + j;
+    // V / 2^(32 (TM - 2)) from the columns of words TM - 2 .. TM
+    double va = 0.0;
+    for (int cidx = 4 * NW - 1; cidx >= 4 * (TM - 2); cidx--) va = va * 256.0 + (double)((int64_t)vj[(size_t)cidx * NCcp] + off);
+    const int64_t t = (int64_t)rint(va / Mtop);
+    int64_t carry = 0;
+    bool allz = true, allo = true;
+    uint32_t yhw = 0;
+    uint32_t* yj = Y + (size_t)j * nw;
+    for (int w = 0; w <= NW; w++) {
+        int64_t acc = carry;
+        if (w < NW) {
+            const int64_t c0 = (int64_t)vj[(size_t)(4 * w) * NCcp] + off;
+            const int64_t c1 = (int64_t)vj[(size_t)(4 * w + 1) * NCcp] + off;
+            const int64_t c2 = (int64_t)vj[(size_t)(4 * w + 2) * NCcp] + off;
+            const int64_t c3 = (int64_t)vj[(size_t)(4 * w + 3) * NCcp] + off;
+            acc += c0 + c1 * 256 + c2 * 65536 + c3 * 16777216 - t * (int64_t)Mw[w];
+        }
+        const uint32_t yw = (uint32_t)acc;
+        carry = acc >> 32;
+        if (w < nw) yj[w] = yw;
+        if (w == hw) {
+            yhw = yw;
+        } else if (w > hw) {
+            allz = allz && yw == 0u;
+            allo = allo && yw == 0xffffffffu;
+        }
+    }
+    int st = 2;
+    if (carry == 0 && allz && (yhw >> hb) == 0u) st = 0;
+    else if (carry == -1 && allo && (yhw >> hb) == (0xffffffffu >> hb)) st = 1;
+    status[j] = st;
+}
+
+// ---------------------------------------------------------------- lowest terms
+// g_j = gcd(|y_j|, d) for every accepted component, one wave per component,
+// by Lehmer's method: the leading 62 bits of a >= b (aligned at a's top bit)
+// run single-precision Euclidean steps while the remainder keeps at least 31
+// bits, which bounds the cofactors by 2^31; the 2 x 2 cofactor matrix is then
+// applied to the full numbers, which lose about 30 bits per round.  Any
+// integer matrix of determinant +-1 keeps the gcd, and a negative result is
+// replaced by its absolute value, so the rounds are correct whatever the
+// leading bits decide; they only have to make progress, and a round that
+// cannot (a quotient of 2^30 or more, i.e. lengths more than 30 bits apart)
+// hands the component to the host.  The numbers sit in registers: lane l
+// holds 32-bit words [l CW, l CW + CW).  Results: gstat 0 and G = g when g
+// fits 64 bits, else gstat 1 (the host finishes that component).
+
+template <int CW>
+__device__ __forceinline__ void wave_highest(const uint32_t (&R)[CW], int lane, int* idx, uint32_t* word) {
+    int li = -1;
+    uint32_t lw = 0;
+#pragma unroll
+    for (int c = 0; c < CW; c++)
+        if (R[c] != 0u) {
+            li = c;
+            lw = R[c];
+        }
+    const uint64_t mask = __ballot(li >= 0);
+    if (mask == 0) {
+        *idx = -1;
+        *word = 0;
+        return;
+    }
+    const int tl = 63 - __builtin_clzll(mask);
+    *idx = tl * CW + __builtin_amdgcn_readlane(li, tl);
+    *word = (uint32_t)__builtin_amdgcn_readlane((int)lw, tl);
+}
+
+template <int CW>
+__device__ __forceinline__ int wave_bitlen(const uint32_t (&R)[CW], int lane) {
+    int idx;
+    uint32_t w;
+    wave_highest<CW>(R, lane, &idx, &w);
+    return idx < 0 ? 0 : 32 * idx + 32 - __builtin_clz(w);
+}
+
+// word idx (uniform, may be negative or past the end: 0)
+template <int CW>
+__device__ __forceinline__ uint32_t wave_word(const uint32_t (&R)[CW], int idx) {
+    if (idx < 0 || idx >= 64 * CW) return 0u;
+    const int c = idx % CW, owner = idx / CW;
+    uint32_t v = 0;
+#pragma unroll
+    for (int k = 0; k < CW; k++) v = (k == c) ? R[k] : v;
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, owner);
+}
+
+// 62 bits of R starting at bit s (uniform)
+template <int CW>
+__device__ __forceinline__ uint64_t wave_bits62(const uint32_t (&R)[CW], int s) {
+    const int w0 = s >> 5, o = s & 31;
+    const uint64_t lo = wave_word<CW>(R, w0), mid = wave_word<CW>(R, w0 + 1), hi = wave_word<CW>(R, w0 + 2);
+    const uint64_t v = (lo >> o) | (mid << (32 - o)) | (o ? (hi << (64 - o)) : 0ull);
+    return v & ((1ull << 62) - 1);
+}
+
+// -1, 0, 1 as a < b, a == b, a > b
+template <int CW>
+__device__ __forceinline__ int wave_cmp(const uint32_t (&a)[CW], const uint32_t (&b)[CW], int lane) {
+    int r = 0;
+#pragma unroll
+    for (int c = 0; c < CW; c++)
+        if (a[c] != b[c]) r = a[c] > b[c] ? 1 : -1;
+    const uint64_t mask = __ballot(r != 0);
+    if (mask == 0) return 0;
+    return __builtin_amdgcn_readlane(r, 63 - __builtin_clzll(mask));
+}
+
+// Adds the lane-local carries out (cout, signed) into the next lanes.
+template <int CW>
+__device__ __forceinline__ void wave_carry(uint32_t (&R)[CW], int64_t cout, int lane) {
+    int64_t cin = __shfl_up(cout, 1);
+    if (lane == 0) cin = 0;
+    for (;;) {
+#pragma unroll
+        for (int c = 0; c < CW; c++) {
+            const int64_t v = (int64_t)R[c] + cin;
+            R[c] = (uint32_t)v;
+            cin = v >> 32;
+        }
+        int64_t up = __shfl_up(cin, 1);
+        if (lane == 0) up = 0;
+        if (__ballot(up != 0) == 0) break;
+        cin = up;
+    }
+}
+
+// |R| for a two's-complement R whose sign bit is the top bit of word 64 CW - 1
+template <int CW>
+__device__ __forceinline__ void wave_abs(uint32_t (&R)[CW], int lane) {
+    const uint32_t top = (uint32_t)__builtin_amdgcn_readlane((int)R[CW - 1], 63);
+    if ((top >> 31) == 0) return;
+#pragma unroll
+    for (int c = 0; c < CW; c++) R[c] = ~R[c];
+    int64_t carry = lane == 0 ? 1 : 0;  // + 1 at word 0
+#pragma unroll
+    for (int c = 0; c < CW; c++) {
+        const int64_t v = (int64_t)R[c] + carry;
+        R[c] = (uint32_t)v;
+        carry = v >> 32;
+    }
+    wave_carry<CW>(R, carry, lane);
+}
+
+template <int CW>
+__global__ __launch_bounds__(256) void gcd_kernel(const uint32_t* __restrict__ Y, int nw,
+                                                  const int* __restrict__ status, int valid_rows,
+                                                  const uint32_t* __restrict__ Dw, int nwd,
+                                                  uint64_t* __restrict__ G, int* __restrict__ gstat) {
+    const int lane = threadIdx.x & 63;
+    const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (j >= valid_rows) return;
+    if (status[j] >= 2) {
+        if (lane == 0) gstat[j] = 1;
+        return;
+    }
+    // a = d, b = |y| (y arrives as nw two's-complement words, status 1 when negative)
+    const uint32_t ext = status[j] == 1 ? 0xffffffffu : 0u;
+    uint32_t a[CW], b[CW];
+#pragma unroll
+    for (int c = 0; c < CW; c++) {
+        const int w = lane * CW + c;
+        a[c] = w < nwd ? Dw[w] : 0u;
+        b[c] = w < nw ? Y[(size_t)j * nw + w] : ext;
+    }
+    wave_abs<CW>(b, lane);
+    int result = 1;
+    uint64_t g = 0;
+    const int max_rounds = (32 * (nw > nwd ? nw : nwd)) / 16 + 64;
+    for (int round = 0; round < max_rounds; round++) {
+        int la = wave_bitlen<CW>(a, lane), lb = wave_bitlen<CW>(b, lane);
+        if (la < lb || (la == lb && wave_cmp<CW>(a, b, lane) < 0)) {
+#pragma unroll
+            for (int c = 0; c < CW; c++) {
+                const uint32_t t = a[c];
+                a[c] = b[c];
+                b[c] = t;
+            }
+            const int t = la;
+            la = lb;
+            lb = t;
+        }
+        if (lb == 0) {  // gcd = a
+            if (la <= 64) {
+                g = ((uint64_t)wave_word<CW>(a, 1) << 32) | wave_word<CW>(a, 0);
+                result = 0;
+            }
+            break;
+        }
+        if (la <= 64) {  // finish on 64-bit values
+            uint64_t x = ((uint64_t)wave_word<CW>(a, 1) << 32) | wave_word<CW>(a, 0);
+            uint64_t y = ((uint64_t)wave_word<CW>(b, 1) << 32) | wave_word<CW>(b, 0);
+            while (y) {
+                const uint64_t t = x % y;
+                x = y;
+                y = t;
+            }
+            g = x;
+            result = 0;
+            break;
+        }
+        if (la - lb > 30) break;  // quotient of 2^30 or more: the host finishes
+        const int s = la - 62;  // > 0 here
+        int64_t x = (int64_t)wave_bits62<CW>(a, s), y = (int64_t)wave_bits62<CW>(b, s);
+        // single-precision Euclid on the leading bits; cofactors stay below 2^30
+        int64_t A = 1, B = 0, C = 0, D = 1;
+        int steps = 0;
+        while (y >= (1ll << 31)) {
+            const double qd = floor((double)x / (double)y);
+            int64_t q = (int64_t)qd;
+            int64_t r = x - q * y;
+            if (r < 0) { q -= 1; r += y; }
+            else if (r >= y) { q += 1; r -= y; }
+            const int64_t nC = A - q * C, nD = B - q * D;
+            if (q >= (1ll << 30) || nC > (1ll << 30) || nC < -(1ll << 30) || nD > (1ll << 30) ||
+                nD < -(1ll << 30))
+                break;
+            A = C; B = D; C = nC; D = nD;
+            x = y; y = r;
+            steps++;
+        }
+        if (steps == 0) break;  // no certain progress: the host finishes
+        // (a, b) <- (A a + B b, C a + D b); A, B (and C, D) have opposite signs
+        int64_t ca = 0, cb = 0;
+#pragma unroll
+        for (int c = 0; c < CW; c++) {
+            const int64_t av = (int64_t)a[c], bv = (int64_t)b[c];
+            const int64_t na = ca + A * av + B * bv, nb = cb + C * av + D * bv;
+            a[c] = (uint32_t)na;
+            b[c] = (uint32_t)nb;
+            ca = na >> 32;
+            cb = nb >> 32;
+        }
+        wave_carry<CW>(a, ca, lane);
+        wave_carry<CW>(b, cb, lane);
+        wave_abs<CW>(a, lane);
+        wave_abs<CW>(b, lane);
+    }
+    if (lane == 0) {
+        gstat[j] = result;
+        G[j] = g;
+    }
+}
+
+// ---------------------------------------------------------------- launchers
+
+hipError_t launch_digit_bytes(const uint64_t* digits, int dstride, int m, int j0, int valid_rows, int rows_pad,
+                              int Kpad, int8_t* S, int* rowsum, hipStream_t st) {
+    hipLaunchKernelGGL(digit_bytes_kernel, dim3(rows_pad), dim3(256), 0, st, digits, dstride, m, j0, valid_rows,
+                       Kpad, S, rowsum);
+    return hipGetLastError();
+}
+
+hipError_t launch_wchain(const uint32_t* T, const uint32_t* Mw, int m, int TM, double Md, int Ncolsp, uint8_t* W,
+                         hipStream_t st) {
+    const int NW = TM + 1;
+    if (NW <= 64 * 8)
+        hipLaunchKernelGGL(wchain_kernel<8>, dim3(m), dim3(64), 0, st, T, Mw, TM, Md, Ncolsp, W);
+    else if (NW <= 64 * 32)
+        hipLaunchKernelGGL(wchain_kernel<32>, dim3(m), dim3(64), 0, st, T, Mw, TM, Md, Ncolsp, W);
+    else if (NW <= 64 * 64)
+        hipLaunchKernelGGL(wchain_kernel<64>, dim3(m), dim3(64), 0, st, T, Mw, TM, Md, Ncolsp, W);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+int wchain_words_per_lane(int NW) { return NW <= 64 * 8 ? 8 : NW <= 64 * 32 ? 32 : NW <= 64 * 64 ? 64 : 0; }
+
+hipError_t launch_transpose_offset(const uint8_t* W, int Kpad, int Ncolsp, int8_t* WT, hipStream_t st) {
+    hipLaunchKernelGGL(transpose_offset_kernel, dim3(Ncolsp / 64, Kpad / 64), dim3(256), 0, st, W, Kpad, Ncolsp, WT);
+    return hipGetLastError();
+}
+
+hipError_t launch_recon_gemm(const int8_t* S, const int8_t* WT, int Kpad, int NCcp, int Ncolsp, int* VT,
+                             hipStream_t st) {
+    hipLaunchKernelGGL(recon_gemm_kernel, dim3(Ncolsp / 128, NCcp / 128), dim3(256), 0, st, S, WT, Kpad, NCcp, VT);
+    return hipGetLastError();
+}
+
+// Words per lane for numbers of up to `words` words, with two words of
+// headroom for the cofactor products (|A a + B b| < 2^31 max(a, b)).
+int gcd_words_per_lane(int words) {
+    words += 2;
+    return words <= 64 * 8 ? 8 : words <= 64 * 16 ? 16 : words <= 64 * 32 ? 32 : 0;
+}
+
+hipError_t launch_gcd(const uint32_t* Y, int nw, const int* status, int valid_rows, const uint32_t* Dw, int nwd,
+                      uint64_t* G, int* gstat, hipStream_t st) {
+    const int cw = gcd_words_per_lane(nw > nwd ? nw : nwd);  // includes two words of headroom
+    const dim3 grid((valid_rows + 3) / 4);
+    if (cw == 8)
+        hipLaunchKernelGGL(gcd_kernel<8>, grid, dim3(256), 0, st, Y, nw, status, valid_rows, Dw, nwd, G, gstat);
+    else if (cw == 16)
+        hipLaunchKernelGGL(gcd_kernel<16>, grid, dim3(256), 0, st, Y, nw, status, valid_rows, Dw, nwd, G, gstat);
+    else if (cw == 32)
+        hipLaunchKernelGGL(gcd_kernel<32>, grid, dim3(256), 0, st, Y, nw, status, valid_rows, Dw, nwd, G, gstat);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_numer(const int* VT, const int* rowsum, int NCcp, int valid_rows, const uint32_t* Mw, int TM,
+                        double Mtop, int nbits, uint32_t* Y, int* status, hipStream_t st) {
+    hipLaunchKernelGGL(numer_kernel, dim3((valid_rows + 255) / 256), dim3(256), 0, st, VT, rowsum, NCcp, valid_rows,
+                       Mw, TM, Mtop, nbits, Y, status);
+    return hipGetLastError();
+}
+
+}  // namespace es

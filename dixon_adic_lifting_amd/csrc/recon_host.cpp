@@ -1,0 +1,369 @@
+// Host side of the GPU reconstruction path (kernels in recon.hip).
+//
+// Method (exact-solve card, phanerozoic/exact-solve, section "Method"): the
+// common denominator d comes from a small sample of components (Wang
+// reconstruction on the host), then each numerator is one modular multiply
+// y = d X mods M, accepted when |y| <= N, and reduced to lowest terms by
+// gcd(y, d).  The modular multiplies of all components run on the GPU as one
+// int8 GEMM against weights 256^b P^i d mod M; this file computes the weight
+// seeds P^i d mod M, drives the kernels, and finishes each component.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <chrono>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "../../include/es_solve.h"
+#include "es_internal.h"
+#include "host.h"
+#include "recon_host.h"
+
+namespace es {
+
+namespace {
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Device scratch of the reconstruction path, kept per host thread and grown
+// on demand (never shrunk; the process's exit releases it).
+struct DeviceScratch {
+    void* p = nullptr;
+    size_t bytes = 0;
+    void* get(size_t need) {
+        if (need <= bytes) return p;
+        if (p) (void)hipFree(p);
+        p = nullptr;
+        bytes = 0;
+        if (hipMalloc(&p, need) != hipSuccess) {
+            p = nullptr;
+            return nullptr;
+        }
+        bytes = need;
+        return p;
+    }
+};
+thread_local DeviceScratch g_dev_scratch;
+
+// Pinned host staging for the device-to-host copies, per thread.
+struct PinnedStage {
+    void* p = nullptr;
+    size_t bytes = 0;
+    ~PinnedStage() {
+        if (p) (void)hipHostFree(p);
+    }
+    void* get(size_t need) {
+        if (need <= bytes) return p;
+        if (p) (void)hipHostFree(p);
+        p = nullptr;
+        bytes = 0;
+        if (hipHostMalloc(&p, need, hipHostMallocDefault) != hipSuccess) {
+            p = nullptr;
+            return nullptr;
+        }
+        bytes = need;
+        return p;
+    }
+};
+thread_local PinnedStage g_pinned_stage;
+
+// little-endian 32-bit words of a nonnegative BigInt, zero-padded to nw
+void to_words(const BigInt& v, uint32_t* w, int nw) {
+    for (int i = 0; i < nw; i++) {
+        const size_t limb = (size_t)i / 2;
+        const uint64_t x = limb < v.size() ? v.d[limb] : 0;
+        w[i] = (uint32_t)(i % 2 ? x >> 32 : x);
+    }
+}
+
+// signed integer from nw two's-complement words (negative when neg)
+BigInt from_words(const uint32_t* w, int nw, bool neg) {
+    std::vector<uint32_t> mag(w, w + nw);
+    if (neg) {  // magnitude = 2^(32 nw) - value
+        uint64_t carry = 1;
+        for (int i = 0; i < nw; i++) {
+            const uint64_t v = (uint64_t)(uint32_t)~mag[i] + carry;
+            mag[i] = (uint32_t)v;
+            carry = v >> 32;
+        }
+    }
+    BigInt r;
+    r.d.resize((size_t)(nw + 1) / 2);
+    for (int i = 0; i < nw; i++) r.d[(size_t)i / 2] |= (uint64_t)mag[i] << (32 * (i % 2));
+    r.trim();
+    r.neg = neg && !r.is_zero();
+    return r;
+}
+
+bool verbose() {
+    static const bool v = [] {
+        const char* e = std::getenv("ES_VERBOSE");
+        return e && *e && *e != '0';
+    }();
+    return v;
+}
+
+}  // namespace
+
+namespace {
+thread_local int g_gpu_recon = -1;  // -1: not set on this thread (environment decides)
+}
+
+void set_gpu_recon(bool on) { g_gpu_recon = on ? 1 : 0; }
+
+bool gpu_recon_disabled() {
+    static const bool env_off = [] {
+        const char* e = std::getenv("ES_RECON");
+        return e && std::strcmp(e, "host") == 0;
+    }();
+    return g_gpu_recon < 0 ? env_off : g_gpu_recon == 0;
+}
+
+GpuReconPlan plan_gpu_recon(int n, int c, int m, const BigInt& M, int nbits) {
+    GpuReconPlan pl;
+    pl.n = n;
+    pl.c = c;
+    pl.m = m;
+    pl.NC = (size_t)n * c;
+    const size_t mbits = M.bit_length();
+    pl.TM = (int)((mbits - 1) / 32);
+    pl.NW = pl.TM + 1;
+    pl.nw = nbits / 32 + 1;
+    // the quotient window needs three words of M; a weight row must fit one
+    // wave; 48 m contraction bytes keep every GEMM column sum within int32
+    if (pl.TM < 2 || wchain_words_per_lane(pl.NW) == 0 || 48 * (size_t)m > 65536 || pl.nw > pl.NW) return pl;
+    pl.Ncolsp = (int)round_up((size_t)4 * pl.NW, 128);
+    pl.Kpad = (int)round_up((size_t)48 * m, 192);
+    pl.NCc = (int)std::min<size_t>(pl.NC, 8192);
+    pl.NCcp = (int)round_up((size_t)pl.NCc, 128);
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o = round_up(o + bytes, 256);
+        return at;
+    };
+    pl.off_digits = take(pl.NC * (size_t)m * kDigitLimbs * sizeof(uint64_t));
+    pl.off_S = take((size_t)pl.NCcp * pl.Kpad);
+    pl.off_rowsum = take((size_t)pl.NCcp * sizeof(int));
+    pl.off_T = take((size_t)m * pl.NW * sizeof(uint32_t));
+    pl.off_Mw = take((size_t)pl.NW * sizeof(uint32_t));
+    pl.off_W = take((size_t)pl.Kpad * pl.Ncolsp);
+    pl.off_WT = take((size_t)pl.Kpad * pl.Ncolsp);
+    pl.off_VT = take((size_t)pl.Ncolsp * pl.NCcp * sizeof(int));
+    pl.off_Y = take((size_t)pl.NCcp * pl.nw * sizeof(uint32_t));
+    pl.off_status = take((size_t)pl.NCcp * sizeof(int));
+    pl.off_Dw = take((size_t)pl.NW * sizeof(uint32_t));
+    pl.off_G = take((size_t)pl.NCcp * sizeof(uint64_t));
+    pl.off_gstat = take((size_t)pl.NCcp * sizeof(int));
+    pl.total = o;
+    pl.ok = pl.total <= ((size_t)16 << 30);
+    return pl;
+}
+
+uint8_t* gpu_recon_scratch(const GpuReconPlan& pl) { return (uint8_t*)g_dev_scratch.get(pl.total); }
+
+#define HIPOK(expr)                                   \
+    do {                                              \
+        if ((expr) != hipSuccess) return ES_EHIP;     \
+    } while (0)
+
+int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const BigInt& M, int nbits, int dbits,
+                    int nthreads, hipStream_t st, SolutionData* out, GpuReconTimes* tm, KernelTimer* kt) {
+    typedef std::chrono::steady_clock clk;
+    auto t0 = clk::now();
+    auto lap = [&](double* slot, const char* what) {
+        auto t1 = clk::now();
+        const double ms = std::chrono::duration<double, std::milli>(t1 - t0).count();
+        if (slot) *slot = ms;
+        if (verbose()) fprintf(stderr, "[es] gpu reconstruct %-12s %8.3f ms\n", what, ms);
+        t0 = t1;
+    };
+    const int m = pl.m, NW = pl.NW, TM = pl.TM, nw = pl.nw;
+    const size_t NC = pl.NC;
+    const uint64_t* dig = (const uint64_t*)(scr + pl.off_digits);
+    const size_t dig_comp = (size_t)m * kDigitLimbs;  // int64 per component
+
+    // 1. common denominator from the sample (host)
+    const std::vector<size_t> sidx = sample_indices(NC, pl.c);
+    const size_t y_bytes = round_up(NC * nw * sizeof(uint32_t), 256), st_bytes = round_up(NC * sizeof(int), 256);
+    const size_t g_bytes = round_up(NC * sizeof(uint64_t), 256);
+    const size_t sd_bytes = sidx.size() * dig_comp * sizeof(int64_t);
+    uint8_t* pin = (uint8_t*)g_pinned_stage.get(y_bytes + 2 * st_bytes + g_bytes + sd_bytes);
+    if (!pin) return ES_ENOMEM;
+    uint32_t* Yh = (uint32_t*)pin;
+    int* sth = (int*)(pin + y_bytes);
+    int* gsth = (int*)(pin + y_bytes + st_bytes);
+    uint64_t* Gh = (uint64_t*)(pin + y_bytes + 2 * st_bytes);
+    int64_t* sd = (int64_t*)(pin + y_bytes + 2 * st_bytes + g_bytes);
+    for (size_t k = 0; k < sidx.size(); k++)
+        HIPOK(hipMemcpyAsync(sd + k * dig_comp, dig + sidx[k] * dig_comp, dig_comp * sizeof(int64_t),
+                             hipMemcpyDeviceToHost, st));
+    HIPOK(hipStreamSynchronize(st));
+    std::vector<BigInt> xs(sidx.size());
+    parallel_for_each(sidx.size(), nthreads, [&](size_t k) { xs[k] = assemble(sd + k * dig_comp, m, P); });
+    BigInt d;
+    if (!sample_denominator(xs, M, nbits, dbits, nthreads, &d)) return ES_EINTERNAL;
+    lap(tm ? &tm->sample_ms : nullptr, "sample");
+
+    uint32_t* Td = (uint32_t*)(scr + pl.off_T);
+    uint32_t* Mwd = (uint32_t*)(scr + pl.off_Mw);
+    uint8_t* W = scr + pl.off_W;
+    int8_t* WT = (int8_t*)(scr + pl.off_WT);
+    int8_t* S = (int8_t*)(scr + pl.off_S);
+    int* rowsum = (int*)(scr + pl.off_rowsum);
+    int* VT = (int*)(scr + pl.off_VT);
+    uint32_t* Yd = (uint32_t*)(scr + pl.off_Y);
+    int* std_ = (int*)(scr + pl.off_status);
+    uint32_t* Dwd = (uint32_t*)(scr + pl.off_Dw);
+    uint64_t* Gd = (uint64_t*)(scr + pl.off_G);
+    int* gstd = (int*)(scr + pl.off_gstat);
+    std::vector<uint32_t> T((size_t)m * NW), Mw(NW), Dwords(NW);
+    to_words(M, Mw.data(), NW);
+    HIPOK(hipMemcpyAsync(Mwd, Mw.data(), Mw.size() * sizeof(uint32_t), hipMemcpyHostToDevice, st));
+    const double Md = (double)Mw[TM] + (double)Mw[TM - 1] * 0x1p-32 + (double)Mw[TM - 2] * 0x1p-64;
+    const double Mtop = (double)Mw[TM] * 0x1p64 + (double)Mw[TM - 1] * 0x1p32 + (double)Mw[TM - 2];
+
+    // One pass of the numerators for every component under the current d:
+    // weight seeds T_i = P^i d mod M (host), weight rows, GEMM, numerators
+    // and gcds (GPU), results to the pinned arrays.
+    bool gpu_gcd = false;
+    auto gpu_pass = [&]() -> int {
+        BigInt Ti = mod_floor(d, M);
+        for (int i = 0; i < m; i++) {
+            to_words(Ti, &T[(size_t)i * NW], NW);
+            if (i + 1 < m) Ti = mod_floor(mul(Ti, P), M);
+        }
+        lap(tm ? &tm->seeds_ms : nullptr, "seeds");
+        const int nwd = (int)((d.bit_length() + 31) / 32);
+        gpu_gcd = nwd <= NW && gcd_words_per_lane(std::max(nw, nwd)) != 0;
+        to_words(d, Dwords.data(), NW);
+        HIPOK(hipMemcpyAsync(Td, T.data(), T.size() * sizeof(uint32_t), hipMemcpyHostToDevice, st));
+        HIPOK(hipMemcpyAsync(Dwd, Dwords.data(), Dwords.size() * sizeof(uint32_t), hipMemcpyHostToDevice, st));
+        long ev = kt->start(KC_RECON_OTHER);
+        HIPOK(launch_wchain(Td, Mwd, m, TM, Md, pl.Ncolsp, W, st));
+        HIPOK(launch_transpose_offset(W, pl.Kpad, pl.Ncolsp, WT, st));
+        kt->stop(ev);
+        for (size_t j0 = 0; j0 < NC; j0 += (size_t)pl.NCc) {
+            const int rows = (int)std::min<size_t>((size_t)pl.NCc, NC - j0);
+            ev = kt->start(KC_RECON_OTHER);
+            HIPOK(launch_digit_bytes(dig, m, m, (int)j0, rows, pl.NCcp, pl.Kpad, S, rowsum, st));
+            kt->stop(ev);
+            ev = kt->start(KC_RECON_GEMM);
+            HIPOK(launch_recon_gemm(S, WT, pl.Kpad, pl.NCcp, pl.Ncolsp, VT, st));
+            kt->stop(ev);
+            ev = kt->start(KC_RECON_OTHER);
+            HIPOK(launch_numer(VT, rowsum, pl.NCcp, rows, Mwd, TM, Mtop, nbits, Yd, std_, st));
+            kt->stop(ev);
+            if (gpu_gcd) {
+                ev = kt->start(KC_RECON_GCD);
+                HIPOK(launch_gcd(Yd, nw, std_, rows, Dwd, nwd, Gd, gstd, st));
+                kt->stop(ev);
+                HIPOK(hipMemcpyAsync(Gh + j0, Gd, (size_t)rows * sizeof(uint64_t), hipMemcpyDeviceToHost, st));
+                HIPOK(hipMemcpyAsync(gsth + j0, gstd, (size_t)rows * sizeof(int), hipMemcpyDeviceToHost, st));
+            }
+            HIPOK(hipMemcpyAsync(Yh + j0 * nw, Yd, (size_t)rows * nw * sizeof(uint32_t), hipMemcpyDeviceToHost,
+                                 st));
+            HIPOK(hipMemcpyAsync(sth + j0, std_, (size_t)rows * sizeof(int), hipMemcpyDeviceToHost, st));
+        }
+        HIPOK(hipStreamSynchronize(st));
+        if (!gpu_gcd)
+            for (size_t j = 0; j < NC; j++) gsth[j] = 1;
+        lap(tm ? &tm->gpu_ms : nullptr, "gpu");
+        return ES_OK;
+    };
+
+    // Lowest terms for the components of `which` that the last pass accepted.
+    std::atomic<size_t> host_gcds{0};
+    auto finish = [&](const std::vector<size_t>& which) {
+        parallel_for_each(which.size(), nthreads, [&](size_t k) {
+            const size_t j = which[k];
+            if (sth[j] != 0 && sth[j] != 1) return;
+            BigInt y = from_words(Yh + j * nw, nw, sth[j] == 1);
+            BigInt g;
+            if (gsth[j] == 0) {
+                g = BigInt::from_u64(Gh[j]);
+            } else {
+                g = gcd(y, d);
+                host_gcds++;
+            }
+            if (g.size() == 1 && g.d[0] == 1) {
+                out->num[j] = std::move(y);
+                out->den[j] = d;
+            } else {
+                out->num[j] = divexact(y, g);
+                out->den[j] = divexact(d, g);
+            }
+        });
+    };
+
+    out->n = pl.n;
+    out->c = pl.c;
+    out->num.assign(NC, BigInt());
+    out->den.assign(NC, BigInt());
+    std::vector<size_t> todo(NC);
+    for (size_t j = 0; j < NC; j++) todo[j] = j;
+    const BigInt Nb = shl(BigInt::from_u64(1), (size_t)nbits);
+    const BigInt Db = shl(BigInt::from_u64(1), (size_t)dbits);
+    // Digits of the listed components, copied to the host on the solve's stream.
+    auto fetch = [&](const std::vector<size_t>& which, std::vector<int64_t>* buf) -> int {
+        buf->resize(which.size() * dig_comp);
+        for (size_t k = 0; k < which.size(); k++)
+            HIPOK(hipMemcpyAsync(buf->data() + k * dig_comp, dig + which[k] * dig_comp, dig_comp * sizeof(int64_t),
+                                 hipMemcpyDeviceToHost, st));
+        HIPOK(hipStreamSynchronize(st));
+        return ES_OK;
+    };
+    // Reconstructs one component on its own from its digits (card, "Method": a
+    // numerator outside the bound means the sample missed part of its
+    // denominator).
+    auto alone = [&](const int64_t* digs, BigInt* nu, BigInt* de) -> bool {
+        BigInt a = mod_floor(assemble(digs, m, P), M);
+        return rational_reconstruct(a, M, Nb, Db, nu, de);
+    };
+    size_t failed_total = 0;
+    for (int pass = 0;; pass++) {
+        int rc = gpu_pass();
+        if (rc != ES_OK) return rc;
+        finish(todo);
+        std::vector<size_t> failed;
+        for (size_t j : todo)
+            if (sth[j] != 0 && sth[j] != 1) failed.push_back(j);
+        lap(tm ? &tm->finish_ms : nullptr, "lowest terms");
+        if (failed.empty()) break;
+        failed_total += failed.size();
+        if (verbose()) fprintf(stderr, "[es] gpu reconstruct: %zu components outside the bound\n", failed.size());
+        std::vector<int64_t> digs;
+        if (failed.size() <= (size_t)(2 * nthreads) || pass >= 3) {
+            // few left: each on its own, in parallel
+            rc = fetch(failed, &digs);
+            if (rc != ES_OK) return rc;
+            std::atomic<int> bad{0};
+            parallel_for_each(failed.size(), nthreads, [&](size_t k) {
+                BigInt nu, de;
+                if (!alone(digs.data() + k * dig_comp, &nu, &de)) bad = 1;
+                out->num[failed[k]] = nu;
+                out->den[failed[k]] = de;
+            });
+            if (bad) return ES_EINTERNAL;
+            break;
+        }
+        // many left: widen d by the first one's denominator and run them again
+        rc = fetch(std::vector<size_t>{failed[0]}, &digs);
+        if (rc != ES_OK) return rc;
+        BigInt nu, de;
+        if (!alone(digs.data(), &nu, &de)) return ES_EINTERNAL;
+        d = lcm(d, de);
+        todo.swap(failed);
+    }
+    if (tm) {
+        tm->failed = failed_total;
+        tm->host_gcds = host_gcds;
+    }
+    return ES_OK;
+}
+
+}  // namespace es

@@ -12,7 +12,8 @@
  * the wide base-P digit, and a one-limb residual update
  * (r_i - A x_i) P^-1 mod 2^64.  A host stage does the rational
  * reconstruction (common denominator from a sample, then one modular
- * multiply per numerator).
+ * multiply per numerator; the multiplies of all components run on the GPU
+ * as one int8 GEMM, the sample and the final gcds on the host).
  *
  * Range (card, "Method" and "Requirements and limits"): A is n x n and b is
  * n x c, both int64 row-major; n * max|A_ij| < 2^63 and 1 <= n <= 2^17.
@@ -100,14 +101,34 @@ int es_solution_get(const es_solution *s, int32_t i, int32_t k, int *num_sign,
 int es_solution_info(const es_solution *s, int32_t *live_primes, int32_t *m,
                      int32_t *num_bound_bits, int32_t *den_bound_bits);
 
+/* Bit length of the lifting modulus M = P^m of a solution (0 for NULL). */
+int32_t es_solution_modulus_bits(const es_solution *s);
+
 /* Frees everything the library allocated for a solution; NULL is a no-op. */
 void es_solution_free(es_solution *s);
 
 /* Host wall-clock stage timings of the last es_solve_device call on this
  * thread, in ms: [0] checks and bounds, [1] residues + batched inverse,
- * [2] lift including its device-to-host digit copies, [3] unused (0),
- * [4] host reconstruction. */
+ * [2] lift (with its device-to-host digit copies on the host-reconstruction
+ * path), [3] the GPU part of the reconstruction (weights, GEMM, numerators
+ * and their copy to the host; 0 on the host path), [4] the whole
+ * reconstruction. */
 int es_last_timings(double *ms5);
+
+/*
+ * Where the reconstruction runs for later solves on the calling thread.
+ * on = 1 (the default): the modular multiplies of all components run on the
+ * GPU as one int8 GEMM and the gcds that bring them to lowest terms run on
+ * the GPU too (the sample stays on the host, and so does any gcd whose
+ * Euclidean quotients the GPU rounds cannot handle); the host path is taken anyway when the GPU path does not
+ * apply (a modulus P^m of fewer than 65 bits, wider than 131072 bits, more
+ * than 1365 lift steps, or more than 16 GiB of scratch).  on = 0: every
+ * digit goes to the host and the host reconstructs.  Both give the same
+ * result.  The GPU path keeps a per-thread device scratch buffer, sized to
+ * the largest solve so far, until the process ends.  Without a call, the
+ * environment variable ES_RECON=host selects the host path.
+ */
+int es_set_gpu_reconstruction(int on);
 
 /*
  * Opt-in kernel timing for measurement.  With es_set_profiling(1) on a
@@ -116,8 +137,10 @@ int es_last_timings(double *ms5);
  * between launches; results are unchanged).  es_kernel_profile then gives,
  * for the last solve, the summed event time in ms and the launch count per
  * kernel class: [0] Gauss-Jordan step, [1] lift contraction (GEMV / GEMM),
- * [2] Garner, [3] residual update, [4] residues of A.  Writes min(cap, 5)
- * entries and returns 5.
+ * [2] Garner, [3] residual update, [4] residues of A, [5] reconstruction
+ * GEMM, [6] other reconstruction kernels (weight rows, digit bytes,
+ * numerators), [7] the gcds that bring the numerators to lowest terms.
+ * Writes min(cap, 8) entries and returns 8.
  */
 int es_set_profiling(int on);
 int es_kernel_profile(double *total_ms, int32_t *counts, int32_t cap);

@@ -14,7 +14,8 @@ Readings where the card is silent (each also listed with the design notes):
 the digits are balanced, x_i in [-(P-1)/2, (P-1)/2]; primes that divide det A
 are dropped from P; the bound is P^m > 2 N D with D the Hadamard bound on
 |det A| and N the Cramer-Hadamard bound on every numerator; the sample is
-component 0 and then every ceil(nc/4)-th component in row-major order.
+the first row (one component of each right-hand side) and then every
+ceil(nc/4)-th component in row-major order.
 """
 from __future__ import annotations
 
@@ -156,10 +157,12 @@ def rational_reconstruct(a: int, M: int, N: int, D: int):
     return r1, t1
 
 
-def sample_indices(total: int):
-    """Row-major component indices used to find the common denominator."""
+def sample_indices(total: int, c: int = 1):
+    """Row-major component indices used to find the common denominator: the
+    first row (one component of every right-hand side, whose denominators can
+    differ) and then every ceil(total/4)-th component."""
     step = max(1, -(-total // 4))
-    return list(range(0, total, step))
+    return list(range(min(c, total))) + [j for j in range(0, total, step) if j >= c]
 
 
 def reconstruct_solution(X, M: int, N: int, D: int):
@@ -174,7 +177,7 @@ def reconstruct_solution(X, M: int, N: int, D: int):
     c = len(X[0])
     flat = [X[r][t] for r in range(n) for t in range(c)]
     d = 1
-    for idx in sample_indices(len(flat)):
+    for idx in sample_indices(len(flat), c):
         f = rational_reconstruct(flat[idx], M, N, D)
         if f is None:
             return None
