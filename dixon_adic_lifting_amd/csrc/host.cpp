@@ -283,12 +283,15 @@ void parallel_for_each(size_t count, int nthreads, const std::function<void(size
 
 std::vector<size_t> sample_indices(size_t NC, int c) {
     // the first row (one component of every right-hand side: their
-    // denominators can differ), then every ceil(NC / 4)-th component
-    const size_t step = std::max<size_t>(1, (NC + 3) / 4);
+    // denominators can differ), then eight components spread over the rows,
+    // the k-th at index floor(k NC / 8) + (k mod c)
     std::vector<size_t> sample;
     for (size_t t = 0; t < (size_t)c && t < NC; t++) sample.push_back(t);
-    for (size_t j = 0; j < NC; j += step)
-        if (j >= (size_t)c) sample.push_back(j);
+    for (size_t k = 1; k < 8; k++) {
+        const size_t j = k * NC / 8 + k % (size_t)c;
+        if (j >= (size_t)c && j < NC && std::find(sample.begin(), sample.end(), j) == sample.end())
+            sample.push_back(j);
+    }
     return sample;
 }
 

@@ -56,8 +56,9 @@ void parallel_for_each(size_t count, int nthreads, const std::function<void(size
 
 // The sampled common denominator (card, "Method"): d = lcm of the reduced
 // denominators of the sample components (the first row, i.e. one component
-// of every right-hand side, then every ceil(NC / 4)-th component in
-// row-major order), each found by Wang reconstruction of X mod M.  xs[k] is
+// of every right-hand side, then the components floor(k NC / 8) + (k mod c)
+// for k = 1..7 in row-major order), each found by Wang reconstruction of
+// X mod M.  xs[k] is
 // the k-th sample's X.  Returns false if some sample has no fraction within
 // the bounds.
 std::vector<size_t> sample_indices(size_t NC, int c);

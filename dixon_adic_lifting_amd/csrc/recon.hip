@@ -295,65 +295,71 @@ __global__ __launch_bounds__(256) void numer_kernel(const int* __restrict__ VT, 
 
 // ---------------------------------------------------------------- lowest terms
 // g_j = gcd(|y_j|, d) for every accepted component, one wave per component,
-// by Lehmer's method: the leading 62 bits of a >= b (aligned at a's top bit)
-// run single-precision Euclidean steps while the remainder keeps at least 31
-// bits, which bounds the cofactors by 2^31; the 2 x 2 cofactor matrix is then
-// applied to the full numbers, which lose about 30 bits per round.  Any
-// integer matrix of determinant +-1 keeps the gcd, and a negative result is
-// replaced by its absolute value, so the rounds are correct whatever the
-// leading bits decide; they only have to make progress, and a round that
-// cannot (a quotient of 2^30 or more, i.e. lengths more than 30 bits apart)
-// hands the component to the host.  The numbers sit in registers: lane l
-// holds 32-bit words [l CW, l CW + CW).  Results: gstat 0 and G = g when g
-// fits 64 bits, else gstat 1 (the host finishes that component).
+// by Lehmer's method: the leading 52 bits of a >= b (aligned at a's top bit,
+// exact in double precision) run Euclidean steps while the remainder keeps
+// at least 26 bits, which bounds the cofactors by 2^26; the 2 x 2 cofactor
+// matrix is then applied to the full numbers, which lose about 26 bits per
+// round.  Any integer matrix of determinant +-1 keeps the gcd, and a
+// negative result is replaced by its absolute value, so a round is correct
+// whatever the leading bits decide; it only has to make progress, and a
+// round that cannot (a quotient of 2^26 or more: lengths more than about 26
+// bits apart) hands the component to the host.  The numbers sit in
+// registers: lane l holds 32-bit words [l CW, l CW + CW).  Results: gstat 0
+// and G = g when g fits 64 bits, else gstat 1 (the host finishes that
+// component).
 
+// highest nonzero word (index, value) of a and of b, -1 / 0 when zero
 template <int CW>
-__device__ __forceinline__ void wave_highest(const uint32_t (&R)[CW], int lane, int* idx, uint32_t* word) {
-    int li = -1;
-    uint32_t lw = 0;
+__device__ __forceinline__ void wave_highest2(const uint32_t (&a)[CW], const uint32_t (&b)[CW], int* ia,
+                                              uint32_t* wa, int* ib, uint32_t* wb) {
+    int la = -1, lb = -1;
+    uint32_t va = 0, vb = 0;
 #pragma unroll
-    for (int c = 0; c < CW; c++)
-        if (R[c] != 0u) {
-            li = c;
-            lw = R[c];
-        }
-    const uint64_t mask = __ballot(li >= 0);
-    if (mask == 0) {
-        *idx = -1;
-        *word = 0;
-        return;
+    for (int c = 0; c < CW; c++) {
+        if (a[c] != 0u) { la = c; va = a[c]; }
+        if (b[c] != 0u) { lb = c; vb = b[c]; }
     }
-    const int tl = 63 - __builtin_clzll(mask);
-    *idx = tl * CW + __builtin_amdgcn_readlane(li, tl);
-    *word = (uint32_t)__builtin_amdgcn_readlane((int)lw, tl);
+    const uint64_t ma = __ballot(la >= 0), mb = __ballot(lb >= 0);
+    if (ma == 0) {
+        *ia = -1;
+        *wa = 0;
+    } else {
+        const int tl = 63 - __builtin_clzll(ma);
+        *ia = tl * CW + __builtin_amdgcn_readlane(la, tl);
+        *wa = (uint32_t)__builtin_amdgcn_readlane((int)va, tl);
+    }
+    if (mb == 0) {
+        *ib = -1;
+        *wb = 0;
+    } else {
+        const int tl = 63 - __builtin_clzll(mb);
+        *ib = tl * CW + __builtin_amdgcn_readlane(lb, tl);
+        *wb = (uint32_t)__builtin_amdgcn_readlane((int)vb, tl);
+    }
 }
 
+// words w0, w0 + 1, w0 + 2 (uniform, w0 >= 0) of a and of b, one pass
 template <int CW>
-__device__ __forceinline__ int wave_bitlen(const uint32_t (&R)[CW], int lane) {
-    int idx;
-    uint32_t w;
-    wave_highest<CW>(R, lane, &idx, &w);
-    return idx < 0 ? 0 : 32 * idx + 32 - __builtin_clz(w);
-}
-
-// word idx (uniform, may be negative or past the end: 0)
-template <int CW>
-__device__ __forceinline__ uint32_t wave_word(const uint32_t (&R)[CW], int idx) {
-    if (idx < 0 || idx >= 64 * CW) return 0u;
-    const int c = idx % CW, owner = idx / CW;
-    uint32_t v = 0;
+__device__ __forceinline__ void wave_words3(const uint32_t (&a)[CW], const uint32_t (&b)[CW], int w0,
+                                            uint32_t (&ra)[3], uint32_t (&rb)[3]) {
+    uint32_t va[3] = {0, 0, 0}, vb[3] = {0, 0, 0};
+    const int c0 = w0 % CW;
 #pragma unroll
-    for (int k = 0; k < CW; k++) v = (k == c) ? R[k] : v;
-    return (uint32_t)__builtin_amdgcn_readlane((int)v, owner);
-}
-
-// 62 bits of R starting at bit s (uniform)
-template <int CW>
-__device__ __forceinline__ uint64_t wave_bits62(const uint32_t (&R)[CW], int s) {
-    const int w0 = s >> 5, o = s & 31;
-    const uint64_t lo = wave_word<CW>(R, w0), mid = wave_word<CW>(R, w0 + 1), hi = wave_word<CW>(R, w0 + 2);
-    const uint64_t v = (lo >> o) | (mid << (32 - o)) | (o ? (hi << (64 - o)) : 0ull);
-    return v & ((1ull << 62) - 1);
+    for (int k = 0; k < CW; k++) {
+#pragma unroll
+        for (int e = 0; e < 3; e++) {
+            const int ce = c0 + e >= CW ? c0 + e - CW : c0 + e;
+            va[e] = k == ce ? a[k] : va[e];
+            vb[e] = k == ce ? b[k] : vb[e];
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 3; e++) {
+        const int w = w0 + e;
+        const int owner = w / CW;
+        ra[e] = owner < 64 ? (uint32_t)__builtin_amdgcn_readlane((int)va[e], owner) : 0u;
+        rb[e] = owner < 64 ? (uint32_t)__builtin_amdgcn_readlane((int)vb[e], owner) : 0u;
+    }
 }
 
 // -1, 0, 1 as a < b, a == b, a > b
@@ -404,6 +410,20 @@ __device__ __forceinline__ void wave_abs(uint32_t (&R)[CW], int lane) {
     wave_carry<CW>(R, carry, lane);
 }
 
+// R <- p R - q S for magnitudes p, q < 2^27 (lane-local words, carries out)
+template <int CW>
+__device__ __forceinline__ int64_t lincomb(uint32_t (&out)[CW], const uint32_t (&R)[CW], const uint32_t (&S)[CW],
+                                           uint32_t p, uint32_t q) {
+    int64_t carry = 0;
+#pragma unroll
+    for (int c = 0; c < CW; c++) {
+        const int64_t v = carry + (int64_t)((uint64_t)p * R[c]) - (int64_t)((uint64_t)q * S[c]);
+        out[c] = (uint32_t)v;
+        carry = v >> 32;
+    }
+    return carry;
+}
+
 template <int CW>
 __global__ __launch_bounds__(256) void gcd_kernel(const uint32_t* __restrict__ Y, int nw,
                                                   const int* __restrict__ status, int valid_rows,
@@ -428,10 +448,14 @@ __global__ __launch_bounds__(256) void gcd_kernel(const uint32_t* __restrict__ Y
     wave_abs<CW>(b, lane);
     int result = 1;
     uint64_t g = 0;
-    const int max_rounds = (32 * (nw > nwd ? nw : nwd)) / 16 + 64;
+    const int max_rounds = (32 * (nw > nwd ? nw : nwd)) / 12 + 64;
     for (int round = 0; round < max_rounds; round++) {
-        int la = wave_bitlen<CW>(a, lane), lb = wave_bitlen<CW>(b, lane);
-        if (la < lb || (la == lb && wave_cmp<CW>(a, b, lane) < 0)) {
+        int ia, ib;
+        uint32_t wa, wb;
+        wave_highest2<CW>(a, b, &ia, &wa, &ib, &wb);
+        int la = ia < 0 ? 0 : 32 * ia + 32 - __builtin_clz(wa);
+        int lb = ib < 0 ? 0 : 32 * ib + 32 - __builtin_clz(wb);
+        if (la < lb || (la == lb && la > 0 && wave_cmp<CW>(a, b, lane) < 0)) {
 #pragma unroll
             for (int c = 0; c < CW; c++) {
                 const uint32_t t = a[c];
@@ -442,16 +466,11 @@ __global__ __launch_bounds__(256) void gcd_kernel(const uint32_t* __restrict__ Y
             la = lb;
             lb = t;
         }
-        if (lb == 0) {  // gcd = a
-            if (la <= 64) {
-                g = ((uint64_t)wave_word<CW>(a, 1) << 32) | wave_word<CW>(a, 0);
-                result = 0;
-            }
-            break;
-        }
-        if (la <= 64) {  // finish on 64-bit values
-            uint64_t x = ((uint64_t)wave_word<CW>(a, 1) << 32) | wave_word<CW>(a, 0);
-            uint64_t y = ((uint64_t)wave_word<CW>(b, 1) << 32) | wave_word<CW>(b, 0);
+        uint32_t ta[3], tb[3];
+        if (la <= 64 || lb == 0) {  // gcd of values within 64 bits, or gcd(a, 0) = a
+            if (la > 64) break;  // a multiword gcd: the host finishes
+            wave_words3<CW>(a, b, 0, ta, tb);
+            uint64_t x = ((uint64_t)ta[1] << 32) | ta[0], y = ((uint64_t)tb[1] << 32) | tb[0];
             while (y) {
                 const uint64_t t = x % y;
                 x = y;
@@ -461,37 +480,51 @@ __global__ __launch_bounds__(256) void gcd_kernel(const uint32_t* __restrict__ Y
             result = 0;
             break;
         }
-        if (la - lb > 30) break;  // quotient of 2^30 or more: the host finishes
-        const int s = la - 62;  // > 0 here
-        int64_t x = (int64_t)wave_bits62<CW>(a, s), y = (int64_t)wave_bits62<CW>(b, s);
-        // single-precision Euclid on the leading bits; cofactors stay below 2^30
-        int64_t A = 1, B = 0, C = 0, D = 1;
+        if (la - lb > 25) break;  // quotient of 2^25 or more: the host finishes
+        // 52 leading bits of a and the bits of b at the same position
+        const int s = la - 52;  // > 12 here
+        wave_words3<CW>(a, b, s >> 5, ta, tb);
+        const int o = s & 31;
+        const uint64_t mask52 = (1ull << 52) - 1;
+        const uint64_t xa = ((((uint64_t)ta[1] << 32) | ta[0]) >> o | ((uint64_t)ta[2] << (64 - o))) & mask52;
+        const uint64_t xb = ((((uint64_t)tb[1] << 32) | tb[0]) >> o | ((uint64_t)tb[2] << (64 - o))) & mask52;
+        // Euclid on the leading bits in double precision (every value an exact integer below 2^53)
+        double x = (double)xa, y = (double)xb;
+        double A = 1.0, B = 0.0, C = 0.0, D = 1.0;
         int steps = 0;
-        while (y >= (1ll << 31)) {
-            const double qd = floor((double)x / (double)y);
-            int64_t q = (int64_t)qd;
-            int64_t r = x - q * y;
-            if (r < 0) { q -= 1; r += y; }
-            else if (r >= y) { q += 1; r -= y; }
-            const int64_t nC = A - q * C, nD = B - q * D;
-            if (q >= (1ll << 30) || nC > (1ll << 30) || nC < -(1ll << 30) || nD > (1ll << 30) ||
-                nD < -(1ll << 30))
-                break;
-            A = C; B = D; C = nC; D = nD;
-            x = y; y = r;
+        while (y >= 0x1p26) {
+            double q = floor(x * __builtin_amdgcn_rcp(y));
+            double r = fma(-q, y, x);
+            if (r < 0.0) {
+                q -= 1.0;
+                r += y;
+            } else if (r >= y) {
+                q += 1.0;
+                r -= y;
+            }
+            const double nC = fma(-q, C, A), nD = fma(-q, D, B);
+            if (q >= 0x1p26 || fabs(nC) > 0x1p26 || fabs(nD) > 0x1p26) break;
+            A = C;
+            B = D;
+            C = nC;
+            D = nD;
+            x = y;
+            y = r;
             steps++;
         }
         if (steps == 0) break;  // no certain progress: the host finishes
-        // (a, b) <- (A a + B b, C a + D b); A, B (and C, D) have opposite signs
-        int64_t ca = 0, cb = 0;
+        // (a, b) <- (A a + B b, C a + D b): A and B (and C and D) have opposite
+        // signs, so each new number is sign * (|A| a - |B| b) or sign * (|B| b - |A| a)
+        const bool apos = A > 0.0, cpos = C > 0.0;
+        const uint32_t pa = (uint32_t)fabs(A), pb = (uint32_t)fabs(B);
+        const uint32_t pc = (uint32_t)fabs(C), pd = (uint32_t)fabs(D);
+        uint32_t na[CW], nb[CW];
+        const int64_t ca = apos ? lincomb<CW>(na, a, b, pa, pb) : lincomb<CW>(na, b, a, pb, pa);
+        const int64_t cb = cpos ? lincomb<CW>(nb, a, b, pc, pd) : lincomb<CW>(nb, b, a, pd, pc);
 #pragma unroll
         for (int c = 0; c < CW; c++) {
-            const int64_t av = (int64_t)a[c], bv = (int64_t)b[c];
-            const int64_t na = ca + A * av + B * bv, nb = cb + C * av + D * bv;
-            a[c] = (uint32_t)na;
-            b[c] = (uint32_t)nb;
-            ca = na >> 32;
-            cb = nb >> 32;
+            a[c] = na[c];
+            b[c] = nb[c];
         }
         wave_carry<CW>(a, ca, lane);
         wave_carry<CW>(b, cb, lane);

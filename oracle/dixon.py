@@ -14,8 +14,8 @@ Readings where the card is silent (each also listed with the design notes):
 the digits are balanced, x_i in [-(P-1)/2, (P-1)/2]; primes that divide det A
 are dropped from P; the bound is P^m > 2 N D with D the Hadamard bound on
 |det A| and N the Cramer-Hadamard bound on every numerator; the sample is
-the first row (one component of each right-hand side) and then every
-ceil(nc/4)-th component in row-major order.
+the first row (one component of each right-hand side) and then seven
+components spread over the rows, floor(k nc/8) + (k mod c) for k = 1..7.
 """
 from __future__ import annotations
 
@@ -160,9 +160,13 @@ def rational_reconstruct(a: int, M: int, N: int, D: int):
 def sample_indices(total: int, c: int = 1):
     """Row-major component indices used to find the common denominator: the
     first row (one component of every right-hand side, whose denominators can
-    differ) and then every ceil(total/4)-th component."""
-    step = max(1, -(-total // 4))
-    return list(range(min(c, total))) + [j for j in range(0, total, step) if j >= c]
+    differ) and then component floor(k total/8) + (k mod c) for k = 1..7."""
+    out = list(range(min(c, total)))
+    for k in range(1, 8):
+        j = k * total // 8 + k % c
+        if c <= j < total and j not in out:
+            out.append(j)
+    return out
 
 
 def reconstruct_solution(X, M: int, N: int, D: int):
