@@ -175,7 +175,7 @@ def rooflines(prof, info, n, c, traffic=None):
         pitch = -(-n // 64) * 64
     E = info["live_primes"]
     out = {}
-    ms, cnt = prof["gj_step"]
+    ms, cnt = prof.get("gj_step", (0.0, 0))
     if cnt:
         # each launch reads and writes every live prime's n x pitch u8 working matrix
         bytes_per = 2.0 * E * n * pitch
@@ -185,6 +185,25 @@ def rooflines(prof, info, n, c, traffic=None):
                           "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic.get("gj_step"),
                           "avg_launch_us": round(avg_s * 1e6, 2), "launches": cnt,
                           "algorithmic_bytes_per_launch": int(bytes_per)}
+    ms, cnt = prof.get("gj_update", (0.0, 0))
+    if cnt:
+        # blocked elimination update: every live prime's n x pitch matrix read and written once,
+        # the transposed old pivot rows read; ops of the rank-32 product
+        bytes_per = 2.0 * E * n * pitch + E * pitch * 64
+        ops_per = 2.0 * E * n * pitch * 32
+        avg_s = ms / cnt / 1e3
+        gbs = bytes_per / avg_s / 1e9
+        out["gj_update"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic.get("gj_update"),
+                            "avg_launch_us": round(avg_s * 1e6, 2), "launches": cnt,
+                            "algorithmic_bytes_per_launch": int(bytes_per),
+                            "int8_tops": round(ops_per / avg_s / 1e12, 2)}
+    ms, cnt = prof.get("gj_panel", (0.0, 0))
+    if cnt:
+        # 32 elimination steps on each live prime's n x 32 panel: read-modify-write of the panel
+        # in registers, one 1024-thread block per prime (latency-bound: 53 of 256 CUs)
+        out["gj_panel"] = {"avg_launch_us": round(ms / cnt * 1e3, 2), "launches": cnt, "total_ms": round(ms, 3),
+                           "element_updates_per_launch": int(32 * E * n * 32)}
     ms, cnt = prof["lift_contract"]
     if cnt:
         # B_j (int8, n x pitch) once per step, plus the residue vector in and the residues out
@@ -345,7 +364,8 @@ def main():
     max_bits = max(max(abs(p).bit_length(), q.bit_length()) for row in pairs for (p, q) in row)
     if args.copy_calib_mb:
         copy_calibration(args.copy_calib_mb)
-    dominant = max(("gj_step", "lift_contract"), key=lambda k: prof[k][0])
+    dominant = max((k for k in ("gj_step", "gj_update", "lift_contract", "recon_gemm") if k in rf),
+                   key=lambda k: prof[k][0])
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(A, b, args.cpu_budget_s)

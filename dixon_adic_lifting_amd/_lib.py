@@ -20,7 +20,8 @@ DIGIT_LIMBS = 6
 
 EXPORTS = ["es_strerror", "es_primes", "es_workspace_bytes", "es_solve_device", "es_solve",
            "es_solution_rows", "es_solution_cols", "es_solution_get", "es_solution_info",
-           "es_solution_free", "es_solution_modulus_bits", "es_set_gpu_reconstruction", "es_last_timings", "es_set_profiling", "es_kernel_profile",
+           "es_solution_free", "es_solution_modulus_bits", "es_set_gpu_reconstruction", "es_set_blocked_inverse",
+           "es_last_timings", "es_set_profiling", "es_kernel_profile",
            "es_batched_inverse", "es_lift_digits", "es_reconstruct"]
 
 _lib = None
@@ -70,6 +71,8 @@ def load():
     lib.es_solution_modulus_bits.restype = ctypes.c_int32
     lib.es_last_timings.argtypes = [ctypes.POINTER(ctypes.c_double)]
     lib.es_last_timings.restype = ctypes.c_int
+    lib.es_set_blocked_inverse.argtypes = [ctypes.c_int]
+    lib.es_set_blocked_inverse.restype = ctypes.c_int
     lib.es_set_gpu_reconstruction.argtypes = [ctypes.c_int]
     lib.es_set_gpu_reconstruction.restype = ctypes.c_int
     lib.es_set_profiling.argtypes = [ctypes.c_int]
@@ -137,7 +140,12 @@ def last_timings():
 
 
 KERNEL_CLASSES = ["gj_step", "lift_contract", "garner", "residual", "residues", "recon_gemm", "recon_other",
-                  "recon_gcd"]
+                  "recon_gcd", "gj_panel", "gj_update"]
+
+
+def set_blocked_inverse(on: bool):
+    """Blocked elimination with MFMA updates (default) or one launch per step, for this thread."""
+    load().es_set_blocked_inverse(1 if on else 0)
 
 
 def set_gpu_reconstruction(on: bool):
@@ -151,7 +159,7 @@ def set_profiling(on: bool):
 
 def kernel_profile():
     """{class: (total_ms, launches)} for the last solve on this thread (profiling on)."""
-    ms = (ctypes.c_double * 8)()
-    cnt = (ctypes.c_int32 * 8)()
-    k = load().es_kernel_profile(ms, cnt, 8)
+    ms = (ctypes.c_double * 16)()
+    cnt = (ctypes.c_int32 * 16)()
+    k = load().es_kernel_profile(ms, cnt, 16)
     return {KERNEL_CLASSES[i]: (ms[i], cnt[i]) for i in range(min(k, len(KERNEL_CLASSES)))}

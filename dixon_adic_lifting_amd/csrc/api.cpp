@@ -11,6 +11,7 @@
 
 #include <chrono>
 #include <climits>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <vector>
@@ -43,12 +44,16 @@ double ms_since(clk::time_point t0) {
 // Opt-in per-launch timing: a pair of HIP events on the solve's stream around
 // every launch of the hot kernels; totals are read after the final sync.
 // Classes 5, 6 and 7 (reconstruction GEMM, other reconstruction kernels,
-// gcds) are declared with the reconstruction driver.
-enum KernelClass { KC_GJ = 0, KC_CONTRACT = 1, KC_GARNER = 2, KC_RESIDUAL = 3, KC_RESIDUES = 4, KC_COUNT = 8 };
+// gcds) are declared with the reconstruction driver; 8 and 9 are the panel
+// and update launches of the blocked elimination.
+enum KernelClass {
+    KC_GJ = 0, KC_CONTRACT = 1, KC_GARNER = 2, KC_RESIDUAL = 3, KC_RESIDUES = 4,
+    KC_PANEL = 8, KC_UPDATE = 9, KC_COUNT = 10
+};
 
 thread_local bool g_profiling = false;
-thread_local double g_kernel_ms[KC_COUNT] = {0, 0, 0, 0, 0, 0, 0, 0};
-thread_local int32_t g_kernel_cnt[KC_COUNT] = {0, 0, 0, 0, 0, 0, 0, 0};
+thread_local double g_kernel_ms[KC_COUNT] = {};
+thread_local int32_t g_kernel_cnt[KC_COUNT] = {};
 
 struct Profiler : KernelTimer {
     bool on = false;
@@ -141,16 +146,40 @@ int prepare(const int64_t* dA, const int64_t* db, int32_t n, int32_t c, uint8_t*
     return ES_OK;
 }
 
-// Residues and the n Gauss-Jordan launches; flags to the host.
+// Blocked elimination (default) or one launch per elimination step, per thread.
+thread_local int g_blocked = -1;  // -1: not set on this thread (environment decides)
+
+bool use_blocked(const Layout& L) {
+    static const bool env_step = [] {
+        const char* e = std::getenv("ES_INVERSE");
+        return e && std::strcmp(e, "stepwise") == 0;
+    }();
+    const bool want = g_blocked < 0 ? !env_step : g_blocked == 1;
+    return want && blocked_inverse_fits(L);
+}
+
+// Residues and the Gauss-Jordan elimination; flags to the host.
 int run_inverse(const int64_t* dA, uint8_t* ws, hipStream_t st, Prep* pr, int* flags, Profiler* prof) {
     const Layout& L = pr->L;
+    const bool blocked = use_blocked(L);
     long ev = prof->start(KC_RESIDUES);
-    HIP_CHECK(launch_residues(dA, L, ws, pr->a32, st));
+    HIP_CHECK(launch_residues(dA, L, ws, pr->a32, st, blocked));
     prof->stop(ev);
-    for (int k = 0; k < L.n; k++) {
-        ev = prof->start(KC_GJ);
-        HIP_CHECK(launch_gj_step(L, ws, k, st));
-        prof->stop(ev);
+    if (blocked) {
+        for (int K = 0; K < L.n; K += kPanel) {
+            ev = prof->start(KC_PANEL);
+            HIP_CHECK(launch_gj_panel(L, ws, K, st));
+            prof->stop(ev);
+            ev = prof->start(KC_UPDATE);
+            HIP_CHECK(launch_gj_update(L, ws, K, st));
+            prof->stop(ev);
+        }
+    } else {
+        for (int k = 0; k < L.n; k++) {
+            ev = prof->start(KC_GJ);
+            HIP_CHECK(launch_gj_step(L, ws, k, st));
+            prof->stop(ev);
+        }
     }
     HIP_CHECK(hipMemcpyAsync(flags, ws + L.off_flags, kNumPrimes * sizeof(int), hipMemcpyDeviceToHost, st));
     HIP_CHECK(hipStreamSynchronize(st));
@@ -263,6 +292,11 @@ int es_primes(int32_t* q, int32_t cap) {
 size_t es_workspace_bytes(int32_t n, int32_t c) {
     if (!valid_shape(n, c)) return 0;
     return make_layout(n, c).total;
+}
+
+int es_set_blocked_inverse(int on) {
+    g_blocked = on ? 1 : 0;
+    return ES_OK;
 }
 
 int es_set_gpu_reconstruction(int on) {

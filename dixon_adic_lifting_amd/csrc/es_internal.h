@@ -95,6 +95,7 @@ struct Layout {
     size_t off_piv;       // int32 [53][n + 1]         pivot row per step
     size_t off_rowpos;    // int32 [53][n]             step at which a row pivoted
     size_t off_pend;      // u8 [2][53][pitch]         scaled pivot rows
+    size_t off_GT;        // int8 [53][pitch][64]      old pivot rows of a panel, transposed
     size_t off_flags;     // int32 [53]                singular mod q_j
     size_t off_rowmax;    // uint64 [n]                max |A_ij| per row
     size_t off_rownorm;   // double [n]                row norms^2 of A
@@ -122,8 +123,14 @@ hipError_t launch_fill_u32(uint32_t* p, size_t count, uint32_t value, hipStream_
 hipError_t launch_stats(const int64_t* A, const int64_t* b, const Layout& L, uint8_t* ws,
                         hipStream_t st);
 hipError_t launch_residues(const int64_t* A, const Layout& L, uint8_t* ws, bool make_a32,
-                           hipStream_t st);
+                           hipStream_t st, bool balanced_out = false);
 hipError_t launch_gj_step(const Layout& L, uint8_t* ws, int k, hipStream_t st);
+// blocked form of the same elimination: 32 steps per panel launch, then one
+// MFMA update launch (residues must be balanced: launch_residues(..., true))
+constexpr int kPanel = 32;
+bool blocked_inverse_fits(const Layout& L);
+hipError_t launch_gj_panel(const Layout& L, uint8_t* ws, int K, hipStream_t st);
+hipError_t launch_gj_update(const Layout& L, uint8_t* ws, int K, hipStream_t st);
 hipError_t launch_export_inverse(const Layout& L, const uint8_t* ws, int8_t* B, hipStream_t st);
 hipError_t launch_split_b(const int64_t* b, const Layout& L, uint8_t* ws, int E, hipStream_t st);
 // one lift step = contraction, then Garner (digit into chunk slot `slot`),

@@ -202,7 +202,7 @@ hipError_t launch_stats(const int64_t* A, const int64_t* b, const Layout& L, uin
 template <bool SMALL>  // SMALL: every |A_ij| < 2^32
 __global__ __launch_bounds__(256) void residue_kernel(const int64_t* __restrict__ A, int n, int pitch,
                                                       uint8_t* __restrict__ S,
-                                                      int32_t* __restrict__ A32, int make_a32) {
+                                                      int32_t* __restrict__ A32, int make_a32, int bal) {
     const int i = blockIdx.x;
     const int col = (blockIdx.y * 256 + threadIdx.x) * 4;
     if (col >= pitch) return;
@@ -222,6 +222,7 @@ __global__ __launch_bounds__(256) void residue_kernel(const int64_t* __restrict_
         for (int u = 0; u < 4; u++) {
             uint32_t r = SMALL ? red32((uint32_t)mag[u], q, mu32) : red64(mag[u], q, mu16, mu32, r32);
             if (neg[u] && r) r = q - r;
+            if (bal && r > (q >> 1)) r = (r - q) & 0xffu;  // balanced residue as a two's-complement byte
             w |= r << (8 * u);
         }
         *(uint32_t*)(S + ((size_t)j * n + i) * pitch + col) = w;
@@ -247,17 +248,18 @@ __global__ __launch_bounds__(256) void pivot0_kernel(const uint8_t* __restrict__
 }
 
 hipError_t launch_residues(const int64_t* A, const Layout& L, uint8_t* ws, bool make_a32,
-                           hipStream_t st) {
+                           hipStream_t st, bool balanced_out) {
     // caller guarantees small (< 2^32) entries whenever make_a32 is set
     dim3 grid(L.n, (L.pitch / 4 + 255) / 256);
     if (make_a32)
         hipLaunchKernelGGL(residue_kernel<true>, grid, dim3(256), 0, st, A, L.n, L.pitch,
-                           ws + L.off_S, (int32_t*)(ws + L.off_A32), 1);
+                           ws + L.off_S, (int32_t*)(ws + L.off_A32), 1, balanced_out ? 1 : 0);
     else
         hipLaunchKernelGGL(residue_kernel<false>, grid, dim3(256), 0, st, A, L.n, L.pitch,
-                           ws + L.off_S, (int32_t*)(ws + L.off_A32), 0);
-    hipLaunchKernelGGL(pivot0_kernel, dim3(kNumPrimes), dim3(256), 0, st,
-                       (const uint8_t*)(ws + L.off_S), L.n, L.pitch, (int*)(ws + L.off_piv));
+                           ws + L.off_S, (int32_t*)(ws + L.off_A32), 0, balanced_out ? 1 : 0);
+    if (!balanced_out)  // the step-wise elimination takes its first pivot from here
+        hipLaunchKernelGGL(pivot0_kernel, dim3(kNumPrimes), dim3(256), 0, st,
+                           (const uint8_t*)(ws + L.off_S), L.n, L.pitch, (int*)(ws + L.off_piv));
     return hipGetLastError();
 }
 
@@ -506,6 +508,294 @@ hipError_t launch_gj_step(const Layout& L, uint8_t* ws, int k, hipStream_t st) {
     if (k == L.n - 1)
         hipLaunchKernelGGL(gj_finalize_kernel, dim3(kNumPrimes), dim3(256), 0, st, ws + L.off_S, L.n,
                            L.pitch, (const int*)(ws + L.off_piv), (const uint8_t*)(ws + L.off_pend));
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- blocked elimination
+// The same in-place Gauss-Jordan (each step k exchanges row piv[k] with
+// column k: the pivot row is scaled by the inverse pivot, slot k keeps the
+// inverse-matrix entry, every other row loses its column-k multiple), run 32
+// steps at a time.  Exchanging b pivot pairs (rows p_c, columns K + c) at
+// once is the block form of that step: with the panel columns Kc and the
+// rest r, the panel after its own b steps holds S'[Pi, Kc] = S[Pi, Kc]^-1 and
+// S'[i, Kc] = -S[i, Kc] S[Pi, Kc]^-1 for the other rows, and every other
+// column follows as
+//     S'[i, r] = [i not a pivot of the panel] S[i, r] + sum_c S'[i, K + c] S[p_c, r],
+// a rank-32 update of the whole matrix by the old pivot rows: one int8 GEMM
+// per prime on the matrix cores.  Pivots are the same as the step-wise
+// kernel's (lowest unused row with a nonzero entry), so piv, rowpos and the
+// final S are identical.  Residues are kept balanced, as int8 operands need.
+
+// (x mod q) balanced, for |x| < 2^15 - 2^9 (every product of two residues
+// plus one): with off = q ceil(2^15 / q), x' = x + off lies in (0, 2^16), so
+// the round-up reciprocal mq24 gives the exact quotient
+__device__ __forceinline__ int bal_red16(int x, uint32_t q, uint32_t mq, int off) {
+    const uint32_t xs = (uint32_t)(x + off) << 8;  // 256 x', x' < 2^16
+    const uint32_t r = mad_i24(mulhi_u24(xs, mq), -(int)(q << 8), xs) >> 8;
+    return (int)r > (int)(q >> 1) ? (int)r - (int)q : (int)r;
+}
+
+// Panel: one block of 1024 threads per prime; thread t keeps rows t, t + 1024,
+// ... (RPT of them), each as the 32 panel bytes in eight registers.  Each
+// step: block-wide minimum of the candidate rows, the pivot's owner writes
+// the scaled pivot row to LDS, every row updates itself.  Afterwards the
+// panel goes back to S and the old pivot rows (all columns) go to GT
+// transposed, [col][c], zero-padded to 64 bytes, the GEMM's operand layout.
+template <int RPT>
+__global__ __launch_bounds__(1024) void gj_panel_kernel(int8_t* __restrict__ S, int n, int pitch, int K,
+                                                        int* __restrict__ piv, int* __restrict__ rowpos,
+                                                        int* __restrict__ flags, int8_t* __restrict__ GT) {
+    const int j = blockIdx.x;
+    if (flags[j]) return;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const uint32_t q = c_pt.q[j], mq = c_pt.mq24[j];
+    const int off = (int)(q * ((32768u + q - 1) / q));  // a multiple of q above every |x|
+    const int bw = min(kPanel, n - K);
+    int8_t* Sj = S + (size_t)j * n * pitch;
+    int* rpj = rowpos + (size_t)j * n;
+    int* pj = piv + (size_t)j * (n + 1);
+    __shared__ int red[2][16];
+    __shared__ uint32_t vrow[2][8];
+    __shared__ int plist[kPanel];
+
+    uint32_t pw[RPT][8];
+    bool used[RPT];
+#pragma unroll
+    for (int r = 0; r < RPT; r++) {
+        const int i = t + 1024 * r;
+        if (i < n) {
+            const uint4 a = *(const uint4*)(Sj + (size_t)i * pitch + K);
+            const uint4 b = *(const uint4*)(Sj + (size_t)i * pitch + K + 16);
+            pw[r][0] = a.x; pw[r][1] = a.y; pw[r][2] = a.z; pw[r][3] = a.w;
+            pw[r][4] = b.x; pw[r][5] = b.y; pw[r][6] = b.z; pw[r][7] = b.w;
+            used[r] = rpj[i] >= 0;
+        } else {
+#pragma unroll
+            for (int w = 0; w < 8; w++) pw[r][w] = 0;
+            used[r] = true;
+        }
+    }
+    for (int kk = 0; kk < bw; kk++) {
+        const int kw = kk >> 2, ks = 8 * (kk & 3), buf = kk & 1;
+        // byte kk of each row (signed)
+        int fk[RPT];
+#pragma unroll
+        for (int r = 0; r < RPT; r++) {
+            uint32_t w = pw[r][0];
+#pragma unroll
+            for (int e = 1; e < 8; e++) w = kw == e ? pw[r][e] : w;
+            fk[r] = (int)(int8_t)(w >> ks);
+        }
+        int cand = INT_MAX;
+#pragma unroll
+        for (int r = RPT - 1; r >= 0; r--)
+            if (!used[r] && fk[r] != 0) cand = t + 1024 * r;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) cand = min(cand, __shfl_xor(cand, o));
+        if (lane == 0) red[buf][wave] = cand;
+        __syncthreads();
+        int p = red[buf][0];
+#pragma unroll
+        for (int w = 1; w < 16; w++) p = min(p, red[buf][w]);
+        if (p == INT_MAX) {  // no pivot: singular modulo q_j
+            if (t == 0) flags[j] = 1;
+            return;
+        }
+        const int pt = p & 1023, pr = p >> 10;
+        if (t == pt) {
+#pragma unroll
+            for (int r = 0; r < RPT; r++) {
+                if (r != pr) continue;
+                const int x = fk[r];
+                const uint32_t pinv = c_inv.inv[j][x < 0 ? x + (int)q : x];
+                uint32_t vw[8];
+#pragma unroll
+                for (int w = 0; w < 8; w++) {
+                    uint32_t o4 = 0;
+#pragma unroll
+                    for (int bb = 0; bb < 4; bb++) {
+                        const int c = 4 * w + bb;
+                        const int xv = (int)(int8_t)(pw[r][w] >> (8 * bb));
+                        int v = bal_red16(xv * (int)pinv, q, mq, off);
+                        if (c == kk) v = (int)pinv > (int)(q >> 1) ? (int)pinv - (int)q : (int)pinv;
+                        o4 |= ((uint32_t)v & 0xffu) << (8 * bb);
+                    }
+                    vw[w] = o4;
+                }
+#pragma unroll
+                for (int w = 0; w < 8; w++) vrow[buf][w] = vw[w];
+                used[r] = true;
+            }
+            pj[K + kk] = p;
+            rpj[p] = K + kk;
+            plist[kk] = p;
+        }
+        __syncthreads();
+        uint32_t v[8];
+#pragma unroll
+        for (int w = 0; w < 8; w++) v[w] = vrow[buf][w];
+#pragma unroll
+        for (int r = 0; r < RPT; r++) {
+            const int i = t + 1024 * r;
+            if (i >= n) continue;
+            if (i == p) {
+#pragma unroll
+                for (int w = 0; w < 8; w++) pw[r][w] = v[w];
+                continue;
+            }
+            const int f = fk[r];
+            if (f == 0) continue;  // nothing to eliminate in this row
+#pragma unroll
+            for (int w = 0; w < 8; w++) {
+                uint32_t o4 = 0;
+#pragma unroll
+                for (int bb = 0; bb < 4; bb++) {
+                    const int c = 4 * w + bb;
+                    const int xr = c == kk ? 0 : (int)(int8_t)(pw[r][w] >> (8 * bb));
+                    const int vv = (int)(int8_t)(v[w] >> (8 * bb));
+                    o4 |= ((uint32_t)bal_red16(xr - f * vv, q, mq, off) & 0xffu) << (8 * bb);
+                }
+                pw[r][w] = o4;
+            }
+        }
+    }
+    // panel back to S
+#pragma unroll
+    for (int r = 0; r < RPT; r++) {
+        const int i = t + 1024 * r;
+        if (i >= n) continue;
+        *(uint4*)(Sj + (size_t)i * pitch + K) = make_uint4(pw[r][0], pw[r][1], pw[r][2], pw[r][3]);
+        *(uint4*)(Sj + (size_t)i * pitch + K + 16) = make_uint4(pw[r][4], pw[r][5], pw[r][6], pw[r][7]);
+    }
+    __syncthreads();
+    // old pivot rows, transposed (their panel columns are never read)
+    int8_t* GTj = GT + (size_t)j * pitch * 64;
+    for (int col = t; col < pitch; col += 1024) {
+        uint32_t o[8];
+#pragma unroll
+        for (int w = 0; w < 8; w++) {
+            uint32_t o4 = 0;
+#pragma unroll
+            for (int bb = 0; bb < 4; bb++) {
+                const int c = 4 * w + bb;
+                const uint32_t x = c < bw ? (uint32_t)(uint8_t)Sj[(size_t)plist[c] * pitch + col] : 0u;
+                o4 |= x << (8 * bb);
+            }
+            o[w] = o4;
+        }
+        uint4* dst = (uint4*)(GTj + (size_t)col * 64);
+        dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+        dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+        dst[2] = make_uint4(0, 0, 0, 0);
+        dst[3] = make_uint4(0, 0, 0, 0);
+    }
+}
+
+// Rank-32 update of every column outside the panel, all rows, one tile of
+// 128 columns x 128 rows per block, grid (column tiles, row tiles, primes).
+// v_mfma_i32_16x16x64_i8 with the old pivot rows (GT, [col][c]) as the first
+// operand and the new panel (S[i][K .. K + 32), zero beyond 32) as the
+// second, so each output lane holds four consecutive columns of one row:
+// C[i][col] = sum_c S'[i][K + c] S[p_c][col]; then
+// S'[i][col] = [i not pivot] S[i][col] + C, reduced balanced.
+typedef int v4i_t __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void gj_update_kernel(int8_t* __restrict__ S, int n, int pitch, int K,
+                                                        const int* __restrict__ rowpos,
+                                                        const int* __restrict__ flags,
+                                                        const int8_t* __restrict__ GT) {
+    const int j = blockIdx.z;
+    if (flags[j]) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int col0 = blockIdx.x * 128 + (wave & 1) * 64;  // this wave's 64 columns
+    const int row0 = blockIdx.y * 128 + (wave >> 1) * 64; // and 64 rows
+    const uint32_t q = c_pt.q[j];
+    // |x| < 32 * 125^2 + 125 < 2^19: x' = x + q ceil(2^19 / q) lies in (0, 2^20), where
+    // ceil(2^28 / q) is an exact round-up reciprocal (20 + 8 bits of precision)
+    const uint32_t m28 = (uint32_t)((268435456ull + q - 1) / q);
+    const int off = (int)(q * ((524288u + q - 1) / q));
+    int8_t* Sj = S + (size_t)j * n * pitch;
+    const int* rpj = rowpos + (size_t)j * n;
+    const int8_t* GTj = GT + (size_t)j * pitch * 64;
+    // operands: lanes of group lg supply k in [16 lg, 16 lg + 16); only k < 32 is nonzero
+    v4i_t ga[4], pb[4];
+#pragma unroll
+    for (int a = 0; a < 4; a++) {
+        const int col = col0 + 16 * a + lr;
+        ga[a] = (lg < 2 && col < pitch) ? *(const v4i_t*)(GTj + (size_t)col * 64 + 16 * lg) : v4i_t{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+        const int i = row0 + 16 * b + lr;
+        pb[b] = (lg < 2 && i < n) ? *(const v4i_t*)(Sj + (size_t)i * pitch + K + 16 * lg) : v4i_t{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+        const int i = row0 + 16 * b + lr;  // output lane: row i, columns 4 lg + 0..3 of each 16-column tile
+        const bool rowok = i < n;
+        const int rp = rowok ? rpj[i] : 0;
+        const bool pivot_row = rp >= K && rp < K + kPanel;
+#pragma unroll
+        for (int a = 0; a < 4; a++) {
+            const v4i_t acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(ga[a], pb[b], v4i_t{0, 0, 0, 0}, 0, 0, 0);
+            const int c4 = col0 + 16 * a + 4 * lg;  // four consecutive columns
+            if (!rowok || c4 >= pitch) continue;
+            if (c4 + 3 >= K && c4 < K + kPanel) {
+                // columns inside the panel keep the panel's values
+                bool any = false;
+#pragma unroll
+                for (int e = 0; e < 4; e++) any = any || (c4 + e < K || c4 + e >= K + kPanel);
+                if (!any) continue;
+            }
+            uint32_t old = *(const uint32_t*)(Sj + (size_t)i * pitch + c4);
+            uint32_t outw = 0;
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int col = c4 + e;
+                const int so = (int)(int8_t)(old >> (8 * e));
+                int v;
+                if (col >= K && col < K + kPanel) {
+                    v = so;  // panel column: unchanged
+                } else {
+                    const int x = (pivot_row ? 0 : so) + acc[e];
+                    const uint32_t xp = (uint32_t)(x + off);
+                    const uint32_t tq = __umulhi(xp << 4, m28);     // floor(xp / q)
+                    int r = (int)(xp - tq * q);
+                    v = r > (int)(q >> 1) ? r - (int)q : r;
+                }
+                outw |= ((uint32_t)v & 0xffu) << (8 * e);
+            }
+            *(uint32_t*)(Sj + (size_t)i * pitch + c4) = outw;
+        }
+    }
+}
+
+bool blocked_inverse_fits(const Layout& L) { return L.n <= 4096 && (L.pitch % 64) == 0; }
+
+hipError_t launch_gj_panel(const Layout& L, uint8_t* ws, int K, hipStream_t st) {
+    int8_t* S = (int8_t*)(ws + L.off_S);
+    int* piv = (int*)(ws + L.off_piv);
+    int* rowpos = (int*)(ws + L.off_rowpos);
+    int* flags = (int*)(ws + L.off_flags);
+    int8_t* GT = (int8_t*)(ws + L.off_GT);
+    if (L.n <= 1024)
+        hipLaunchKernelGGL(gj_panel_kernel<1>, dim3(kNumPrimes), dim3(1024), 0, st, S, L.n, L.pitch, K, piv, rowpos,
+                           flags, GT);
+    else if (L.n <= 2048)
+        hipLaunchKernelGGL(gj_panel_kernel<2>, dim3(kNumPrimes), dim3(1024), 0, st, S, L.n, L.pitch, K, piv, rowpos,
+                           flags, GT);
+    else
+        hipLaunchKernelGGL(gj_panel_kernel<4>, dim3(kNumPrimes), dim3(1024), 0, st, S, L.n, L.pitch, K, piv, rowpos,
+                           flags, GT);
+    return hipGetLastError();
+}
+
+hipError_t launch_gj_update(const Layout& L, uint8_t* ws, int K, hipStream_t st) {
+    dim3 grid((L.pitch + 127) / 128, (L.n + 127) / 128, kNumPrimes);
+    hipLaunchKernelGGL(gj_update_kernel, grid, dim3(256), 0, st, (int8_t*)(ws + L.off_S), L.n, L.pitch, K,
+                       (const int*)(ws + L.off_rowpos), (const int*)(ws + L.off_flags),
+                       (const int8_t*)(ws + L.off_GT));
     return hipGetLastError();
 }
 

@@ -6,8 +6,9 @@
  * B = A^-1 mod P for a squarefree odd P = prod q_j over primes q_j < 256,
  * r_0 = b, x_i = B r_i mod P, r_{i+1} = (r_i - A x_i) / P; the digits x_i
  * reconstruct x once P^m exceeds twice the Hadamard bound on numerator and
- * denominator.  A^-1 mod q_j comes from a batched Gauss-Jordan inverse (one
- * launch per elimination step across all primes, Barrett reduction); each
+ * denominator.  A^-1 mod q_j comes from a batched Gauss-Jordan inverse (all
+ * primes at once; one launch per elimination step, or blocked 32 steps per
+ * panel with an int8-MFMA rank-32 update; Barrett-style reduction); each
  * step's x_i is one int8 contraction per prime, a balanced Garner CRT into
  * the wide base-P digit, and a one-limb residual update
  * (r_i - A x_i) P^-1 mod 2^64.  A host stage does the rational
@@ -116,6 +117,17 @@ void es_solution_free(es_solution *s);
 int es_last_timings(double *ms5);
 
 /*
+ * How the batched inverse eliminates, for later calls on the calling thread.
+ * on = 1 (the default): blocked, 32 elimination steps per panel launch (one
+ * workgroup per prime) followed by one int8-MFMA launch that applies them to
+ * the rest of every prime's matrix as a rank-32 update; taken when n <= 4096.
+ * on = 0 (or n > 4096): one launch per elimination step across all primes.
+ * Both choose the same pivots and give identical results.  Without a call,
+ * the environment variable ES_INVERSE=stepwise selects the step-wise form.
+ */
+int es_set_blocked_inverse(int on);
+
+/*
  * Where the reconstruction runs for later solves on the calling thread.
  * on = 1 (the default): the modular multiplies of all components run on the
  * GPU as one int8 GEMM and the gcds that bring them to lowest terms run on
@@ -139,8 +151,9 @@ int es_set_gpu_reconstruction(int on);
  * kernel class: [0] Gauss-Jordan step, [1] lift contraction (GEMV / GEMM),
  * [2] Garner, [3] residual update, [4] residues of A, [5] reconstruction
  * GEMM, [6] other reconstruction kernels (weight rows, digit bytes,
- * numerators), [7] the gcds that bring the numerators to lowest terms.
- * Writes min(cap, 8) entries and returns 8.
+ * numerators), [7] the gcds that bring the numerators to lowest terms,
+ * [8] panel and [9] update launches of the blocked elimination.  Writes
+ * min(cap, 10) entries and returns 10.
  */
 int es_set_profiling(int on);
 int es_kernel_profile(double *total_ms, int32_t *counts, int32_t cap);

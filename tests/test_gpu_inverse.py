@@ -132,3 +132,50 @@ def test_inverse_ragged_two_passes(primes):
     A, _ = W.uniform_system(1090, 1, 24, 31)
     B, flags = es.batched_inverse(torch.as_tensor(A).cuda())
     check_identity_gpu(A, B, flags, primes)
+
+
+def both_inverses(A):
+    """(B, flags) from the blocked elimination and from one launch per step."""
+    from dixon_adic_lifting_amd import _lib
+    dA = torch.as_tensor(A).cuda()
+    try:
+        _lib.set_blocked_inverse(True)
+        Bb, fb = es.batched_inverse(dA)
+        _lib.set_blocked_inverse(False)
+        Bs, fs = es.batched_inverse(dA)
+    finally:
+        _lib.set_blocked_inverse(True)
+    return Bb, fb, Bs, fs
+
+
+@pytest.mark.parametrize("n,bits,seed", [(1, 8, 31), (31, 24, 32), (32, 24, 33), (33, 8, 34), (97, 24, 35),
+                                         (130, 4, 36), (300, 24, 37), (1090, 24, 38)])
+def test_blocked_and_stepwise_inverse_agree(n, bits, seed, primes):
+    # every prime's balanced inverse and every singular flag match bit for bit
+    # (4-bit entries at n = 130 make several primes divide det A); n = 1090
+    # has a ragged last panel and rows past one 1024-thread block
+    A, _ = W.uniform_system(n, 1, bits, seed)
+    Bb, fb, Bs, fs = both_inverses(A)
+    assert fb == fs
+    for j in range(53):
+        if not fb[j]:
+            assert torch.equal(Bb[j], Bs[j]), primes[j]
+
+
+def test_blocked_inverse_pivoting_and_singular_primes(primes):
+    # zero leading entries force pivots away from the diagonal; a rank-deficient
+    # block makes every prime singular at a known step
+    rng = np.random.default_rng(40)
+    n = 70
+    A = rng.integers(-50, 50, size=(n, n), dtype=np.int64)
+    A[:40, :3] = 0
+    Bb, fb, Bs, fs = both_inverses(A)
+    assert fb == fs
+    for j in range(53):
+        if not fb[j]:
+            assert torch.equal(Bb[j], Bs[j])
+    check_identity_gpu(A, Bb, fb, primes)
+    S = A.copy()
+    S[:, 45] = S[:, 3] + 2 * S[:, 7]           # singular over Q: singular mod every prime
+    Bb, fb, _, fs = both_inverses(S)
+    assert fb == fs == [1] * 53
