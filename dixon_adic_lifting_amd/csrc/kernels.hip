@@ -536,11 +536,17 @@ __device__ __forceinline__ int bal_red16(int x, uint32_t q, uint32_t mq, int off
 }
 
 // Panel: one block of 1024 threads per prime; thread t keeps rows t, t + 1024,
-// ... (RPT of them), each as the 32 panel bytes in eight registers.  Each
-// step: block-wide minimum of the candidate rows, the pivot's owner writes
-// the scaled pivot row to LDS, every row updates itself.  Afterwards the
-// panel goes back to S and the old pivot rows (all columns) go to GT
-// transposed, [col][c], zero-padded to 64 bytes, the GEMM's operand layout.
+// ... (RPT of them), each as the 32 panel bytes in eight registers, held as
+// residues in [0, q) during the panel.  Each step: block-wide minimum of the
+// candidate rows; the pivot's owner publishes its raw row and q-inverse in
+// LDS; every row then updates itself as base + factor * prow' (mod q), where
+// prow' is the raw pivot row with a 1 in slot kk, base is the row with slot
+// kk cleared (zero for the pivot row itself) and factor is -f pinv (pinv for
+// the pivot row): this is the scaled-pivot-row update with the scaling
+// folded into one factor per row, in the byte-up arithmetic of the step
+// kernel.  Afterwards the panel goes back to S (balanced) and the old pivot
+// rows (all columns) go to GT transposed, [col][c], zero-padded to 64 bytes,
+// the GEMM's operand layout.
 template <int RPT>
 __global__ __launch_bounds__(1024) void gj_panel_kernel(int8_t* __restrict__ S, int n, int pitch, int K,
                                                         int* __restrict__ piv, int* __restrict__ rowpos,
@@ -549,13 +555,13 @@ __global__ __launch_bounds__(1024) void gj_panel_kernel(int8_t* __restrict__ S, 
     if (flags[j]) return;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const uint32_t q = c_pt.q[j], mq = c_pt.mq24[j];
-    const int off = (int)(q * ((32768u + q - 1) / q));  // a multiple of q above every |x|
+    const int32_t nq8 = -(int32_t)(q << 8);
     const int bw = min(kPanel, n - K);
     int8_t* Sj = S + (size_t)j * n * pitch;
     int* rpj = rowpos + (size_t)j * n;
     int* pj = piv + (size_t)j * (n + 1);
     __shared__ int red[2][16];
-    __shared__ uint32_t vrow[2][8];
+    __shared__ uint32_t prow[2][9];  // raw pivot row (8 words) and pinv
     __shared__ int plist[kPanel];
 
     uint32_t pw[RPT][8];
@@ -566,30 +572,38 @@ __global__ __launch_bounds__(1024) void gj_panel_kernel(int8_t* __restrict__ S, 
         if (i < n) {
             const uint4 a = *(const uint4*)(Sj + (size_t)i * pitch + K);
             const uint4 b = *(const uint4*)(Sj + (size_t)i * pitch + K + 16);
-            pw[r][0] = a.x; pw[r][1] = a.y; pw[r][2] = a.z; pw[r][3] = a.w;
-            pw[r][4] = b.x; pw[r][5] = b.y; pw[r][6] = b.z; pw[r][7] = b.w;
+            const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int e = 0; e < 8; e++) {  // balanced bytes -> residues in [0, q)
+                uint32_t o = 0;
+#pragma unroll
+                for (int bb = 0; bb < 4; bb++) {
+                    const int x = (int)(int8_t)(w[e] >> (8 * bb));
+                    o |= (uint32_t)(x < 0 ? x + (int)q : x) << (8 * bb);
+                }
+                pw[r][e] = o;
+            }
             used[r] = rpj[i] >= 0;
         } else {
 #pragma unroll
-            for (int w = 0; w < 8; w++) pw[r][w] = 0;
+            for (int e = 0; e < 8; e++) pw[r][e] = 0;
             used[r] = true;
         }
     }
     for (int kk = 0; kk < bw; kk++) {
         const int kw = kk >> 2, ks = 8 * (kk & 3), buf = kk & 1;
-        // byte kk of each row (signed)
-        int fk[RPT];
+        uint32_t fk[RPT];  // byte kk of each row
 #pragma unroll
         for (int r = 0; r < RPT; r++) {
             uint32_t w = pw[r][0];
 #pragma unroll
             for (int e = 1; e < 8; e++) w = kw == e ? pw[r][e] : w;
-            fk[r] = (int)(int8_t)(w >> ks);
+            fk[r] = (w >> ks) & 0xffu;
         }
         int cand = INT_MAX;
 #pragma unroll
         for (int r = RPT - 1; r >= 0; r--)
-            if (!used[r] && fk[r] != 0) cand = t + 1024 * r;
+            if (!used[r] && fk[r] != 0u) cand = t + 1024 * r;
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) cand = min(cand, __shfl_xor(cand, o));
         if (lane == 0) red[buf][wave] = cand;
@@ -601,29 +615,14 @@ __global__ __launch_bounds__(1024) void gj_panel_kernel(int8_t* __restrict__ S, 
             if (t == 0) flags[j] = 1;
             return;
         }
-        const int pt = p & 1023, pr = p >> 10;
-        if (t == pt) {
+        if (t == (p & 1023)) {
+            const int pr = p >> 10;
 #pragma unroll
             for (int r = 0; r < RPT; r++) {
                 if (r != pr) continue;
-                const int x = fk[r];
-                const uint32_t pinv = c_inv.inv[j][x < 0 ? x + (int)q : x];
-                uint32_t vw[8];
 #pragma unroll
-                for (int w = 0; w < 8; w++) {
-                    uint32_t o4 = 0;
-#pragma unroll
-                    for (int bb = 0; bb < 4; bb++) {
-                        const int c = 4 * w + bb;
-                        const int xv = (int)(int8_t)(pw[r][w] >> (8 * bb));
-                        int v = bal_red16(xv * (int)pinv, q, mq, off);
-                        if (c == kk) v = (int)pinv > (int)(q >> 1) ? (int)pinv - (int)q : (int)pinv;
-                        o4 |= ((uint32_t)v & 0xffu) << (8 * bb);
-                    }
-                    vw[w] = o4;
-                }
-#pragma unroll
-                for (int w = 0; w < 8; w++) vrow[buf][w] = vw[w];
+                for (int e = 0; e < 8; e++) prow[buf][e] = pw[r][e];
+                prow[buf][8] = c_inv.inv[j][fk[r]];
                 used[r] = true;
             }
             pj[K + kk] = p;
@@ -631,41 +630,55 @@ __global__ __launch_bounds__(1024) void gj_panel_kernel(int8_t* __restrict__ S, 
             plist[kk] = p;
         }
         __syncthreads();
-        uint32_t v[8];
+        // prow' one byte up, with 1 in slot kk
+        uint32_t vs[32];
 #pragma unroll
-        for (int w = 0; w < 8; w++) v[w] = vrow[buf][w];
+        for (int e = 0; e < 8; e++) {
+            const uint32_t w = prow[buf][e];
+#pragma unroll
+            for (int bb = 0; bb < 4; bb++) vs[4 * e + bb] = (4 * e + bb == kk) ? 256u : byte_up(w, bb);
+        }
+        const uint32_t pinv = prow[buf][8];
+        uint32_t kmask[8];
+#pragma unroll
+        for (int e = 0; e < 8; e++) kmask[e] = e == kw ? ~(0xffu << ks) : 0xffffffffu;
 #pragma unroll
         for (int r = 0; r < RPT; r++) {
             const int i = t + 1024 * r;
             if (i >= n) continue;
-            if (i == p) {
+            const bool isp = i == p;
+            if (!isp && fk[r] == 0u) continue;  // nothing to eliminate in this row
+            // factor: -f pinv for other rows, pinv for the pivot row
+            const uint32_t g = red_up(__umul24(fk[r], pinv) << 8, mq, nq8) >> 8;
+            const uint32_t fac = isp ? pinv : (g ? q - g : 0u);
 #pragma unroll
-                for (int w = 0; w < 8; w++) pw[r][w] = v[w];
-                continue;
-            }
-            const int f = fk[r];
-            if (f == 0) continue;  // nothing to eliminate in this row
+            for (int e = 0; e < 8; e++) {
+                const uint32_t w = isp ? 0u : (pw[r][e] & kmask[e]);
+                uint32_t o[4];
 #pragma unroll
-            for (int w = 0; w < 8; w++) {
-                uint32_t o4 = 0;
-#pragma unroll
-                for (int bb = 0; bb < 4; bb++) {
-                    const int c = 4 * w + bb;
-                    const int xr = c == kk ? 0 : (int)(int8_t)(pw[r][w] >> (8 * bb));
-                    const int vv = (int)(int8_t)(v[w] >> (8 * bb));
-                    o4 |= ((uint32_t)bal_red16(xr - f * vv, q, mq, off) & 0xffu) << (8 * bb);
-                }
-                pw[r][w] = o4;
+                for (int bb = 0; bb < 4; bb++) o[bb] = red_up(byte_up(w, bb) + __umul24(fac, vs[4 * e + bb]), mq, nq8);
+                pw[r][e] = pack_up(o[0], o[1], o[2], o[3]);
             }
         }
     }
-    // panel back to S
+    // panel back to S, balanced
 #pragma unroll
     for (int r = 0; r < RPT; r++) {
         const int i = t + 1024 * r;
         if (i >= n) continue;
-        *(uint4*)(Sj + (size_t)i * pitch + K) = make_uint4(pw[r][0], pw[r][1], pw[r][2], pw[r][3]);
-        *(uint4*)(Sj + (size_t)i * pitch + K + 16) = make_uint4(pw[r][4], pw[r][5], pw[r][6], pw[r][7]);
+        uint32_t w[8];
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            uint32_t o = 0;
+#pragma unroll
+            for (int bb = 0; bb < 4; bb++) {
+                const uint32_t x = (pw[r][e] >> (8 * bb)) & 0xffu;
+                o |= ((x > (q >> 1) ? x - q : x) & 0xffu) << (8 * bb);
+            }
+            w[e] = o;
+        }
+        *(uint4*)(Sj + (size_t)i * pitch + K) = make_uint4(w[0], w[1], w[2], w[3]);
+        *(uint4*)(Sj + (size_t)i * pitch + K + 16) = make_uint4(w[4], w[5], w[6], w[7]);
     }
     __syncthreads();
     // old pivot rows, transposed (their panel columns are never read)
@@ -700,10 +713,19 @@ __global__ __launch_bounds__(1024) void gj_panel_kernel(int8_t* __restrict__ S, 
 // S'[i][col] = [i not pivot] S[i][col] + C, reduced balanced.
 typedef int v4i_t __attribute__((ext_vector_type(4)));
 
+// Orders this wave's LDS writes before its later LDS reads (no cross-wave sync).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __global__ __launch_bounds__(256) void gj_update_kernel(int8_t* __restrict__ S, int n, int pitch, int K,
                                                         const int* __restrict__ rowpos,
                                                         const int* __restrict__ flags,
                                                         const int8_t* __restrict__ GT) {
+    constexpr int LS = 80;  // LDS row stride, bytes (16-byte aligned, conflict-free for 4-byte access)
+    __shared__ __attribute__((aligned(16))) uint8_t stage[4][64 * LS];
     const int j = blockIdx.z;
     if (flags[j]) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -718,6 +740,7 @@ __global__ __launch_bounds__(256) void gj_update_kernel(int8_t* __restrict__ S, 
     int8_t* Sj = S + (size_t)j * n * pitch;
     const int* rpj = rowpos + (size_t)j * n;
     const int8_t* GTj = GT + (size_t)j * pitch * 64;
+    uint8_t* st = stage[wave];
     // operands: lanes of group lg supply k in [16 lg, 16 lg + 16); only k < 32 is nonzero
     v4i_t ga[4], pb[4];
 #pragma unroll
@@ -730,25 +753,23 @@ __global__ __launch_bounds__(256) void gj_update_kernel(int8_t* __restrict__ S, 
         const int i = row0 + 16 * b + lr;
         pb[b] = (lg < 2 && i < n) ? *(const v4i_t*)(Sj + (size_t)i * pitch + K + 16 * lg) : v4i_t{0, 0, 0, 0};
     }
+    const bool colblock = col0 < pitch;  // the wave's 64 columns exist (pitch is a multiple of 64)
 #pragma unroll
     for (int b = 0; b < 4; b++) {
-        const int i = row0 + 16 * b + lr;  // output lane: row i, columns 4 lg + 0..3 of each 16-column tile
-        const bool rowok = i < n;
+        // old S for rows row0 + 16 b + lr, 16 columns per lane, through LDS
+        const int i = row0 + 16 * b + lr;
+        const bool rowok = i < n && colblock;
+        const uint4 old16 = rowok ? *(const uint4*)(Sj + (size_t)i * pitch + col0 + 16 * lg) : make_uint4(0, 0, 0, 0);
+        *(uint4*)(st + lr * LS + 16 * lg) = old16;
         const int rp = rowok ? rpj[i] : 0;
         const bool pivot_row = rp >= K && rp < K + kPanel;
+        wave_lds_sync();
+        // accumulator layout: lane holds row lr, columns 16 a + 4 lg + 0..3
 #pragma unroll
         for (int a = 0; a < 4; a++) {
             const v4i_t acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(ga[a], pb[b], v4i_t{0, 0, 0, 0}, 0, 0, 0);
-            const int c4 = col0 + 16 * a + 4 * lg;  // four consecutive columns
-            if (!rowok || c4 >= pitch) continue;
-            if (c4 + 3 >= K && c4 < K + kPanel) {
-                // columns inside the panel keep the panel's values
-                bool any = false;
-#pragma unroll
-                for (int e = 0; e < 4; e++) any = any || (c4 + e < K || c4 + e >= K + kPanel);
-                if (!any) continue;
-            }
-            uint32_t old = *(const uint32_t*)(Sj + (size_t)i * pitch + c4);
+            const int c4 = col0 + 16 * a + 4 * lg;
+            const uint32_t old = *(const uint32_t*)(st + lr * LS + 16 * a + 4 * lg);
             uint32_t outw = 0;
 #pragma unroll
             for (int e = 0; e < 4; e++) {
@@ -756,18 +777,21 @@ __global__ __launch_bounds__(256) void gj_update_kernel(int8_t* __restrict__ S, 
                 const int so = (int)(int8_t)(old >> (8 * e));
                 int v;
                 if (col >= K && col < K + kPanel) {
-                    v = so;  // panel column: unchanged
+                    v = so;  // panel column: keeps the panel's value
                 } else {
                     const int x = (pivot_row ? 0 : so) + acc[e];
                     const uint32_t xp = (uint32_t)(x + off);
-                    const uint32_t tq = __umulhi(xp << 4, m28);     // floor(xp / q)
-                    int r = (int)(xp - tq * q);
+                    const uint32_t tq = __umulhi(xp << 4, m28);  // floor(xp / q)
+                    const int r = (int)(xp - tq * q);
                     v = r > (int)(q >> 1) ? r - (int)q : r;
                 }
                 outw |= ((uint32_t)v & 0xffu) << (8 * e);
             }
-            *(uint32_t*)(Sj + (size_t)i * pitch + c4) = outw;
+            *(uint32_t*)(st + lr * LS + 16 * a + 4 * lg) = outw;
         }
+        wave_lds_sync();
+        if (rowok) *(uint4*)(Sj + (size_t)i * pitch + col0 + 16 * lg) = *(const uint4*)(st + lr * LS + 16 * lg);
+        wave_lds_sync();
     }
 }
 
