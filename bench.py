@@ -144,25 +144,36 @@ def verify_mod_primes(A, b, pairs):
     return True
 
 
+def kernel_sources_sha256():
+    """SHA-256 over the HIP kernel sources (kernels.hip, recon.hip), in that order."""
+    h = hashlib.sha256()
+    for f in ("kernels.hip", "recon.hip"):
+        with open(os.path.join(ROOT, "dixon_adic_lifting_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
 def counter_traffic(workload):
     """Per-launch HBM bytes from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
     runs (profiles/pmc_traffic_<workload>.json), or None when absent or when
-    kernels.hip has changed since the counters were taken."""
+    the kernel sources have changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"pmc_traffic_{workload}.json")
     if not os.path.exists(path):
         return {}
     with open(path) as f:
         data = json.load(f)
-    with open(os.path.join(ROOT, "dixon_adic_lifting_amd", "csrc", "kernels.hip"), "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
-    if data.get("kernels_hip_sha256") != sha:
+    if data.get("kernel_sources_sha256") != kernel_sources_sha256():
         return {}
     out = {}
     for name, v in data["kernels"].items():
         if "gj_step_kernel" in name and "true>" not in name:
             out["gj_step"] = v["traffic_bytes"]
-        elif "lift_gemv_kernel" in name or "lift_mfma_kernel" in name:
+        elif "gj_update_kernel" in name:
+            out["gj_update"] = v["traffic_bytes"]
+        elif "lift_gemv" in name or "lift_mfma_kernel" in name:
             out["lift_contract"] = v["traffic_bytes"]
+        elif "recon_gemm_kernel" in name:
+            out["recon_gemm"] = v["traffic_bytes"]
     return out
 
 
@@ -227,6 +238,7 @@ def rooflines(prof, info, n, c, traffic=None):
         s = ms / 1e3
         out["recon_gemm"] = {"bound": "mfma", "achieved": round(ops / s / 1e12, 2), "peak": INT8_PEAK_TOPS,
                              "unit": "TOP/s", "frac": round(ops / s / 1e12 / INT8_PEAK_TOPS, 4),
+                             "traffic": traffic.get("recon_gemm"),
                              "avg_launch_us": round(s / cnt * 1e6, 2), "launches": cnt,
                              "algorithmic_ops_total": ops}
     for k in ("garner", "residual", "residues", "recon_other", "recon_gcd"):
