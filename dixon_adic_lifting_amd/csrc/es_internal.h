@@ -151,7 +151,8 @@ hipError_t launch_recon_gemm(const int8_t* S, const int8_t* WT, int Kpad, int NC
 int gcd_words_per_lane(int words);  // 0 when the numbers do not fit one wave
 hipError_t launch_gcd(const uint32_t* Y, int nw, const int* status, int valid_rows, const uint32_t* Dw, int nwd,
                       uint64_t* G, int* gstat, hipStream_t st);
-hipError_t launch_numer(const int* VT, const int* rowsum, int NCcp, int valid_rows, const uint32_t* Mw, int TM,
+int numer_words_per_lane(int NW);  // 0 when a numerator pass does not fit one wave
+hipError_t launch_numer(const int* V, int Ncolsp, const int* rowsum, int valid_rows, const uint32_t* Mw, int TM,
                         double Mtop, int nbits, uint32_t* Y, int* status, hipStream_t st);
 
 }  // namespace es

@@ -1132,7 +1132,7 @@ __global__ __launch_bounds__(256) void garner_wave_kernel(const LiftParams* __re
 #pragma unroll
     for (int l = 0; l < kNumPrimes; ++l) {
         if (l < E) {
-            const uint32_t ql = prm->q[l];
+            const uint32_t ql = (uint32_t)__builtin_amdgcn_readlane((int)qk, l);  // lane l holds q_l
             int vl = __builtin_amdgcn_readlane((int)t, l);
             vl = vl > (int)(ql >> 1) ? vl - (int)ql : vl;
             if (lane > l && live) {

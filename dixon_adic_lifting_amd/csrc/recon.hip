@@ -177,7 +177,7 @@ __global__ __launch_bounds__(256) void transpose_offset_kernel(const uint8_t* __
 }
 
 // ---------------------------------------------------------------- the GEMM
-// VT[col][j] = sum_k S[j][k] WT[col][k] (int8 x int8 -> int32) on
+// V[j][col] = sum_k S[j][k] WT[col][k] (int8 x int8 -> int32) on
 // v_mfma_i32_16x16x64_i8.  Block tile 128 (rows j) x 128 (columns) staged in
 // LDS 64 bytes of k at a time; four waves in a 2 x 2 arrangement, each owning
 // a 64 x 64 tile as 4 x 4 MFMA tiles.  Operand lanes: lane l feeds row (or
@@ -190,12 +190,12 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 constexpr int kGemmLds = 64 + 16;  // LDS row stride, bytes
 
 __global__ __launch_bounds__(256) void recon_gemm_kernel(const int8_t* __restrict__ S, const int8_t* __restrict__ WT,
-                                                         int Kpad, int NCcp, int* __restrict__ VT) {
+                                                         int Kpad, int Ncolsp, int* __restrict__ V) {
     __shared__ __attribute__((aligned(16))) int8_t As[128 * kGemmLds];
     __shared__ __attribute__((aligned(16))) int8_t Bs[128 * kGemmLds];
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int wr = wave >> 1, wc = wave & 1;
-    const int j0 = blockIdx.y * 128, c0 = blockIdx.x * 128;
+    const int j0 = blockIdx.x * 128, c0 = blockIdx.y * 128;
     const int lr = lane & 15, lg = lane >> 4;
     v4i acc[4][4];
 #pragma unroll
@@ -238,59 +238,9 @@ __global__ __launch_bounds__(256) void recon_gemm_kernel(const int8_t* __restric
         for (int b = 0; b < 4; b++) {
             const int col = c0 + 64 * wc + 16 * b + lr;
             const int j = j0 + 64 * wr + 16 * a + 4 * lg;
-            *(v4i*)(VT + (size_t)col * NCcp + j) = acc[a][b];
+#pragma unroll
+            for (int r = 0; r < 4; r++) V[(size_t)(j + r) * Ncolsp + col] = acc[a][b][r];
         }
-}
-
-// ---------------------------------------------------------------- numerators
-// One lane per component: V = sum_col (VT[col][j] + 128 rowsum_j) 256^col
-// (undoing the -128 offset of the weights), t = round(V / M) from the twelve
-// top columns in double precision (exact whenever |V - t M| is far below
-// M / 2, as for every acceptable numerator), y = V - t M in one carry pass
-// over the words.  status[j]: 0 when 0 <= y < 2^nbits, 1 when
-// -2^nbits <= y < 0 (Y[j] holds words 0 .. nbits / 32 of y, two's
-// complement), 2 otherwise (the host reconstructs that component alone).
-__global__ __launch_bounds__(256) void numer_kernel(const int* __restrict__ VT, const int* __restrict__ rowsum,
-                                                    int NCcp, int valid_rows, const uint32_t* __restrict__ Mw,
-                                                    int TM, double Mtop, int nbits, uint32_t* __restrict__ Y,
-                                                    int* __restrict__ status) {
-    const int j = blockIdx.x * 256 + threadIdx.x;
-    if (j >= valid_rows) return;
-    const int64_t off = 128 * (int64_t)rowsum[j];
-    const int NW = TM + 1;
-    const int hw = nbits / 32, hb = nbits % 32, nw = hw + 1;
-    const int* vj = VT + j;
-    // V / 2^(32 (TM - 2)) from the columns of words TM - 2 .. TM
-    double va = 0.0;
-    for (int cidx = 4 * NW - 1; cidx >= 4 * (TM - 2); cidx--) va = va * 256.0 + (double)((int64_t)vj[(size_t)cidx * NCcp] + off);
-    const int64_t t = (int64_t)rint(va / Mtop);
-    int64_t carry = 0;
-    bool allz = true, allo = true;
-    uint32_t yhw = 0;
-    uint32_t* yj = Y + (size_t)j * nw;
-    for (int w = 0; w <= NW; w++) {
-        int64_t acc = carry;
-        if (w < NW) {
-            const int64_t c0 = (int64_t)vj[(size_t)(4 * w) * NCcp] + off;
-            const int64_t c1 = (int64_t)vj[(size_t)(4 * w + 1) * NCcp] + off;
-            const int64_t c2 = (int64_t)vj[(size_t)(4 * w + 2) * NCcp] + off;
-            const int64_t c3 = (int64_t)vj[(size_t)(4 * w + 3) * NCcp] + off;
-            acc += c0 + c1 * 256 + c2 * 65536 + c3 * 16777216 - t * (int64_t)Mw[w];
-        }
-        const uint32_t yw = (uint32_t)acc;
-        carry = acc >> 32;
-        if (w < nw) yj[w] = yw;
-        if (w == hw) {
-            yhw = yw;
-        } else if (w > hw) {
-            allz = allz && yw == 0u;
-            allo = allo && yw == 0xffffffffu;
-        }
-    }
-    int st = 2;
-    if (carry == 0 && allz && (yhw >> hb) == 0u) st = 0;
-    else if (carry == -1 && allo && (yhw >> hb) == (0xffffffffu >> hb)) st = 1;
-    status[j] = st;
 }
 
 // ---------------------------------------------------------------- lowest terms
@@ -537,6 +487,60 @@ __global__ __launch_bounds__(256) void gcd_kernel(const uint32_t* __restrict__ Y
     }
 }
 
+// ---------------------------------------------------------------- numerators
+// One wave per component, lane l holding words [l CW, l CW + CW) of
+// V = sum_col (V[j][col] + 128 rowsum_j) 256^col (the +128 undoes the -128
+// offset of the weights).  t = round(V / M) comes from the twelve top columns
+// in double precision, read by every lane in the same order (exact whenever
+// |V - t M| is far below M / 2, as for every acceptable numerator); then
+// y = V - t M word by word with a lane-local carry chain and the wave carry.
+// status[j]: 0 when 0 <= y < 2^nbits, 1 when -2^nbits <= y < 0 (Y[j] holds
+// words 0 .. nbits / 32 of y, two's complement), 2 otherwise (the host
+// reconstructs that component alone).
+template <int CW>
+__global__ __launch_bounds__(256) void numer_kernel(const int* __restrict__ V, int Ncolsp,
+                                                    const int* __restrict__ rowsum, int valid_rows,
+                                                    const uint32_t* __restrict__ Mw, int TM, double Mtop, int nbits,
+                                                    uint32_t* __restrict__ Y, int* __restrict__ status) {
+    const int lane = threadIdx.x & 63;
+    const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (j >= valid_rows) return;
+    const int64_t off = 128 * (int64_t)rowsum[j];
+    const int NW = TM + 1;
+    const int hw = nbits / 32, hb = nbits % 32, nw = hw + 1;
+    const int* vj = V + (size_t)j * Ncolsp;
+    double va = 0.0;  // V / 2^(32 (TM - 2)) from the columns of words TM - 2 .. TM
+    for (int cidx = 4 * NW - 1; cidx >= 4 * (TM - 2); cidx--) va = va * 256.0 + (double)((int64_t)vj[cidx] + off);
+    const int64_t t = (int64_t)rint(va / Mtop);
+    uint32_t y[CW];
+    int64_t carry = 0;
+#pragma unroll
+    for (int c = 0; c < CW; c++) {
+        const int w = lane * CW + c;
+        int64_t acc = carry;
+        if (w < NW) {
+            const int4 v4 = *(const int4*)(vj + 4 * w);
+            acc += ((int64_t)v4.x + off) + ((int64_t)v4.y + off) * 256 + ((int64_t)v4.z + off) * 65536 +
+                   ((int64_t)v4.w + off) * 16777216 - t * (int64_t)Mw[w];
+        }
+        y[c] = (uint32_t)acc;
+        carry = acc >> 32;
+    }
+    wave_carry<CW>(y, carry, lane);
+    // sign: the top word of the wave's 64 CW words
+    const uint32_t sw = ((uint32_t)__builtin_amdgcn_readlane((int)y[CW - 1], 63) >> 31) ? 0xffffffffu : 0u;
+    bool ok = true;
+#pragma unroll
+    for (int c = 0; c < CW; c++) {
+        const int w = lane * CW + c;
+        if (w > hw) ok = ok && y[c] == sw;
+        if (w == hw) ok = ok && (y[c] >> hb) == (sw >> hb);
+        if (w < nw) Y[(size_t)j * nw + w] = y[c];
+    }
+    const bool accept = __ballot(!ok) == 0;
+    if (lane == 0) status[j] = accept ? (sw ? 1 : 0) : 2;
+}
+
 // ---------------------------------------------------------------- launchers
 
 hipError_t launch_digit_bytes(const uint64_t* digits, int dstride, int m, int j0, int valid_rows, int rows_pad,
@@ -567,9 +571,10 @@ hipError_t launch_transpose_offset(const uint8_t* W, int Kpad, int Ncolsp, int8_
     return hipGetLastError();
 }
 
-hipError_t launch_recon_gemm(const int8_t* S, const int8_t* WT, int Kpad, int NCcp, int Ncolsp, int* VT,
+hipError_t launch_recon_gemm(const int8_t* S, const int8_t* WT, int Kpad, int NCcp, int Ncolsp, int* V,
                              hipStream_t st) {
-    hipLaunchKernelGGL(recon_gemm_kernel, dim3(Ncolsp / 128, NCcp / 128), dim3(256), 0, st, S, WT, Kpad, NCcp, VT);
+    // component tiles vary fastest, so the blocks in flight share weight tiles
+    hipLaunchKernelGGL(recon_gemm_kernel, dim3(NCcp / 128, Ncolsp / 128), dim3(256), 0, st, S, WT, Kpad, Ncolsp, V);
     return hipGetLastError();
 }
 
@@ -595,10 +600,34 @@ hipError_t launch_gcd(const uint32_t* Y, int nw, const int* status, int valid_ro
     return hipGetLastError();
 }
 
-hipError_t launch_numer(const int* VT, const int* rowsum, int NCcp, int valid_rows, const uint32_t* Mw, int TM,
+int numer_words_per_lane(int NW) {
+    NW += 2;  // the result's sign word and one word of headroom
+    return NW <= 64 * 8 ? 8 : NW <= 64 * 16 ? 16 : NW <= 64 * 32 ? 32 : NW <= 64 * 64 ? 64 : 0;
+}
+
+hipError_t launch_numer(const int* V, int Ncolsp, const int* rowsum, int valid_rows, const uint32_t* Mw, int TM,
                         double Mtop, int nbits, uint32_t* Y, int* status, hipStream_t st) {
-    hipLaunchKernelGGL(numer_kernel, dim3((valid_rows + 255) / 256), dim3(256), 0, st, VT, rowsum, NCcp, valid_rows,
-                       Mw, TM, Mtop, nbits, Y, status);
+    const dim3 grid((valid_rows + 3) / 4);
+    switch (numer_words_per_lane(TM + 1)) {
+        case 8:
+            hipLaunchKernelGGL(numer_kernel<8>, grid, dim3(256), 0, st, V, Ncolsp, rowsum, valid_rows, Mw, TM, Mtop,
+                               nbits, Y, status);
+            break;
+        case 16:
+            hipLaunchKernelGGL(numer_kernel<16>, grid, dim3(256), 0, st, V, Ncolsp, rowsum, valid_rows, Mw, TM, Mtop,
+                               nbits, Y, status);
+            break;
+        case 32:
+            hipLaunchKernelGGL(numer_kernel<32>, grid, dim3(256), 0, st, V, Ncolsp, rowsum, valid_rows, Mw, TM, Mtop,
+                               nbits, Y, status);
+            break;
+        case 64:
+            hipLaunchKernelGGL(numer_kernel<64>, grid, dim3(256), 0, st, V, Ncolsp, rowsum, valid_rows, Mw, TM, Mtop,
+                               nbits, Y, status);
+            break;
+        default:
+            return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

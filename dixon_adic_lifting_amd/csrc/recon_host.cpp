@@ -135,7 +135,9 @@ GpuReconPlan plan_gpu_recon(int n, int c, int m, const BigInt& M, int nbits) {
     pl.nw = nbits / 32 + 1;
     // the quotient window needs three words of M; a weight row must fit one
     // wave; 48 m contraction bytes keep every GEMM column sum within int32
-    if (pl.TM < 2 || wchain_words_per_lane(pl.NW) == 0 || 48 * (size_t)m > 65536 || pl.nw > pl.NW) return pl;
+    if (pl.TM < 2 || wchain_words_per_lane(pl.NW) == 0 || numer_words_per_lane(pl.NW) == 0 || 48 * (size_t)m > 65536 ||
+        pl.nw > pl.NW)
+        return pl;
     pl.Ncolsp = (int)round_up((size_t)4 * pl.NW, 128);
     pl.Kpad = (int)round_up((size_t)48 * m, 192);
     pl.NCc = (int)std::min<size_t>(pl.NC, 8192);
@@ -256,7 +258,7 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
             HIPOK(launch_recon_gemm(S, WT, pl.Kpad, pl.NCcp, pl.Ncolsp, VT, st));
             kt->stop(ev);
             ev = kt->start(KC_RECON_OTHER);
-            HIPOK(launch_numer(VT, rowsum, pl.NCcp, rows, Mwd, TM, Mtop, nbits, Yd, std_, st));
+            HIPOK(launch_numer(VT, pl.Ncolsp, rowsum, rows, Mwd, TM, Mtop, nbits, Yd, std_, st));
             kt->stop(ev);
             if (gpu_gcd) {
                 ev = kt->start(KC_RECON_GCD);

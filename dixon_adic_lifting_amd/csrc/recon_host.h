@@ -30,7 +30,7 @@ struct GpuReconPlan {
     size_t off_Mw = 0;        // uint32 [NW]        M
     size_t off_W = 0;         // uint8 [Kpad][Ncolsp] weight rows
     size_t off_WT = 0;        // int8 [Ncolsp][Kpad]  transposed, offset by -128
-    size_t off_VT = 0;        // int32 [Ncolsp][NCcp] GEMM column sums
+    size_t off_VT = 0;        // int32 [NCcp][Ncolsp] GEMM column sums, one row per component
     size_t off_Y = 0;         // uint32 [NCcp][nw]  numerators
     size_t off_status = 0;    // int32 [NCcp]
     size_t off_Dw = 0;        // uint32 [NW]        the common denominator d
