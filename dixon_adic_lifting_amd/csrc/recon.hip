@@ -245,85 +245,252 @@ __global__ __launch_bounds__(256) void recon_gemm_kernel(const int8_t* __restric
 
 // ---------------------------------------------------------------- lowest terms
 // g_j = gcd(|y_j|, d) for every accepted component, one wave per component,
-// by Lehmer's method: the leading 52 bits of a >= b (aligned at a's top bit,
-// exact in double precision) run Euclidean steps while the remainder keeps
-// at least 26 bits, which bounds the cofactors by 2^26; the 2 x 2 cofactor
-// matrix is then applied to the full numbers, which lose about 26 bits per
-// round.  Any integer matrix of determinant +-1 keeps the gcd, and a
-// negative result is replaced by its absolute value, so a round is correct
-// whatever the leading bits decide; it only has to make progress, and a
-// round that cannot (a quotient of 2^26 or more: lengths more than about 26
-// bits apart) hands the component to the host.  The numbers sit in
-// registers: lane l holds 32-bit words [l CW, l CW + CW).  Results: gstat 0
-// and G = g when g fits 64 bits, else gstat 1 (the host finishes that
-// component).
+// by Lehmer's method on numbers held as signed radix-2^30 limbs,
+// sum_k l_k 2^(30 k) with every |l_k| < 0.58 2^30; limb k sits in lane
+// k % 64, slot k / 64, so a number's limbs fill the low slots and the work of
+// a round shrinks with the numbers.
+//
+// A round reads three limbs of each number at the larger one's top (in
+// double precision, a leading part with about 52 exact bits of a and the
+// bits of b at the same scale), runs Euclidean steps on them while the
+// divisor keeps 26 bits and the cofactors stay within 2^26, and applies the
+// 2 x 2 cofactor matrix [A B; C D] limb by limb: v = A a_k + B b_k is split
+// at once into a low part in [-2^29, 2^29), kept in the limb, and a high part
+// added to limb k + 1, so no carry ever ripples.  (With |l| <= L before the
+// round, |v| <= 2^27 L and the new limb is within 2^29 + L / 8 + 1/2; the
+// bound 0.58 2^30 is kept.)  The sign of a number is the sign of its top
+// limb, and a negative number is negated.  Any integer matrix of
+// determinant +-1 keeps the gcd, so a round is correct whatever the leading
+// bits decide; it only has to make progress, and a round that cannot (a
+// quotient of 2^26 or more: lengths more than about 26 bits apart) hands the
+// component to the host.  Once both numbers fit in four limbs they are read
+// out exactly and finished by the binary gcd.  Results: gstat 0 and G = g
+// when g fits 64 bits, else gstat 1 (the host finishes that component).
 
-// highest nonzero word (index, value) of a and of b, -1 / 0 when zero
+// lane l <- lane l - 1, lane 0 <- lane 63
+__device__ __forceinline__ int32_t wave_ror1(int32_t v) {
+    return __builtin_amdgcn_update_dpp(0, v, 0x13c, 0xf, 0xf, false);
+}
+
+// bits [30 k, 30 k + 30) of a little-endian word array (words past n read as ext)
+__device__ __forceinline__ int32_t chunk30(const uint32_t* __restrict__ W, int n, uint32_t ext, int k) {
+    const int bit = 30 * k, w = bit >> 5, o = bit & 31;
+    const uint32_t lo = w < n ? W[w] : ext;
+    const uint32_t hi = w + 1 < n ? W[w + 1] : ext;
+    return (int32_t)(__builtin_amdgcn_alignbit(hi, lo, o) & 0x3fffffffu);
+}
+
+// (a, b) <- (A a + B b, C a + D b) over slots [0, ns); limbs above the live
+// ones are zero and stay zero
 template <int CW>
-__device__ __forceinline__ void wave_highest2(const uint32_t (&a)[CW], const uint32_t (&b)[CW], int* ia,
-                                              uint32_t* wa, int* ib, uint32_t* wb) {
-    int la = -1, lb = -1;
-    uint32_t va = 0, vb = 0;
+__device__ __forceinline__ void limb_apply(int32_t (&a)[CW], int32_t (&b)[CW], int32_t A, int32_t B, int32_t C,
+                                           int32_t D, int ns, bool lane0) {
+    int32_t pa = 0, pb = 0;  // high parts of the slot below, rotated one lane up
 #pragma unroll
     for (int c = 0; c < CW; c++) {
-        if (a[c] != 0u) { la = c; va = a[c]; }
-        if (b[c] != 0u) { lb = c; vb = b[c]; }
-    }
-    const uint64_t ma = __ballot(la >= 0), mb = __ballot(lb >= 0);
-    if (ma == 0) {
-        *ia = -1;
-        *wa = 0;
-    } else {
-        const int tl = 63 - __builtin_clzll(ma);
-        *ia = tl * CW + __builtin_amdgcn_readlane(la, tl);
-        *wa = (uint32_t)__builtin_amdgcn_readlane((int)va, tl);
-    }
-    if (mb == 0) {
-        *ib = -1;
-        *wb = 0;
-    } else {
-        const int tl = 63 - __builtin_clzll(mb);
-        *ib = tl * CW + __builtin_amdgcn_readlane(lb, tl);
-        *wb = (uint32_t)__builtin_amdgcn_readlane((int)vb, tl);
+        if (c >= ns) continue;
+        // w = v + 2^29: high part floor(w / 2^30), low part (w mod 2^30) - 2^29
+        const int64_t wa = (int64_t)A * a[c] + ((int64_t)B * b[c] + (1 << 29));
+        const int64_t wb = (int64_t)C * a[c] + ((int64_t)D * b[c] + (1 << 29));
+        const uint32_t wal = (uint32_t)wa, wah = (uint32_t)((uint64_t)wa >> 32);
+        const uint32_t wbl = (uint32_t)wb, wbh = (uint32_t)((uint64_t)wb >> 32);
+        const int32_t ra = wave_ror1((int32_t)__builtin_amdgcn_alignbit(wah, wal, 30));
+        const int32_t rb = wave_ror1((int32_t)__builtin_amdgcn_alignbit(wbh, wbl, 30));
+        a[c] = (int32_t)(wal & 0x3fffffffu) - (1 << 29) + (lane0 ? pa : ra);
+        b[c] = (int32_t)(wbl & 0x3fffffffu) - (1 << 29) + (lane0 ? pb : rb);
+        pa = ra;
+        pb = rb;
     }
 }
 
-// words w0, w0 + 1, w0 + 2 (uniform, w0 >= 0) of a and of b, one pass
+// R <- -R over slots [0, ns)
 template <int CW>
-__device__ __forceinline__ void wave_words3(const uint32_t (&a)[CW], const uint32_t (&b)[CW], int w0,
-                                            uint32_t (&ra)[3], uint32_t (&rb)[3]) {
-    uint32_t va[3] = {0, 0, 0}, vb[3] = {0, 0, 0};
-    const int c0 = w0 % CW;
+__device__ __forceinline__ void limb_negate(int32_t (&R)[CW], int ns) {
 #pragma unroll
-    for (int k = 0; k < CW; k++) {
+    for (int c = 0; c < CW; c++) {
+        if (c >= ns) continue;
+        R[c] = -R[c];
+    }
+}
+
+// highest limb index below 64 ns at which a or b is nonzero (-1 when both are zero)
+template <int CW>
+__device__ __forceinline__ int top_limb(const int32_t (&a)[CW], const int32_t (&b)[CW], int ns) {
+    for (int s = ns - 1; s >= 0; s--) {
+        const uint64_t m = __ballot((a[s] | b[s]) != 0);
+        if (m != 0) return 64 * s + 63 - __builtin_clzll(m);
+    }
+    return -1;
+}
+
+// limbs k, k - 1, k - 2 of R (k >= 2) as l_k 2^60 + l_{k-1} 2^30 + l_{k-2}
+template <int CW>
+__device__ __forceinline__ double lead3(const int32_t (&R)[CW], int k) {
+    const int s = k >> 6, i = k & 63;
+    const int32_t v0 = R[s];
+    const int32_t v1 = s > 0 ? R[s - 1] : 0;
+    const int32_t l2 = __builtin_amdgcn_readlane(v0, i);
+    const int32_t l1 = i >= 1 ? __builtin_amdgcn_readlane(v0, i - 1) : __builtin_amdgcn_readlane(v1, 63);
+    const int32_t l0 = i >= 2 ? __builtin_amdgcn_readlane(v0, i - 2) : __builtin_amdgcn_readlane(v1, 62 + i);
+    return fma(fma((double)l2, 0x1p30, (double)l1), 0x1p30, (double)l0);
+}
+
+// One Euclidean step on (x, y) with cofactors (A, B; C, D).  The hardware
+// reciprocal r0 is good to about 2^-24; one Newton correction gives x / y
+// to about 2^-48 relative, far below the 2^-20 / 2^26 that the quotient
+// estimate takes off, so the estimate never exceeds the true quotient (for
+// quotients below 2^26) and the remainder is never negative.  An estimate
+// one short (an exact quotient always is) leaves r in [y, 2 y); taking the
+// quotient at least 1 whenever x >= y keeps every such step making
+// progress, so x = y cannot repeat.  True when the step is acceptable:
+// divisor of 26 bits or more, quotient and new cofactors within 2^26.
+__device__ __forceinline__ bool euclid_step(double x, double y, double A, double B, double C, double D,
+                                            double& nx, double& ny, double& nA, double& nB, double& nC,
+                                            double& nD) {
+    const double r0 = __builtin_amdgcn_rcp(y);
+    const double t = x * r0, e = fma(-y, r0, 1.0);
+    const double q = fmax(floor(fma(t, e, t - 0x1p-20)), x >= y ? 1.0 : 0.0);
+    nx = y;
+    ny = fma(-q, y, x);
+    nA = C;
+    nB = D;
+    nC = fma(-q, C, A);
+    nD = fma(-q, D, B);
+    return y >= 0x1p26 && q < 0x1p26 && fmax(fabs(nC), fabs(nD)) <= 0x1p26;
+}
+
+template <int CW>
+__global__ __launch_bounds__(256) void gcd_kernel(const uint32_t* __restrict__ Y, int nw,
+                                                  const int* __restrict__ status, int valid_rows,
+                                                  const uint32_t* __restrict__ Dw, int nwd,
+                                                  uint64_t* __restrict__ G, int* __restrict__ gstat) {
+    const int lane = threadIdx.x & 63;
+    const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (j >= valid_rows) return;
+    if (status[j] >= 2) {
+        if (lane == 0) gstat[j] = 1;
+        return;
+    }
+    const bool lane0 = lane == 0;
+    // a = d, b = y: 30-bit chunks of the two's-complement words (y's sign
+    // extended through every limb), then one split pass makes them signed
+    // limbs; the carry dropped off the top limb removes the extension
+    const uint32_t ext = status[j] == 1 ? 0xffffffffu : 0u;
+    const uint32_t* yj = Y + (size_t)j * nw;
+    int32_t a[CW], b[CW];
 #pragma unroll
-        for (int e = 0; e < 3; e++) {
-            const int ce = c0 + e >= CW ? c0 + e - CW : c0 + e;
-            va[e] = k == ce ? a[k] : va[e];
-            vb[e] = k == ce ? b[k] : vb[e];
+    for (int c = 0; c < CW; c++) {
+        a[c] = chunk30(Dw, nwd, 0u, 64 * c + lane);
+        b[c] = chunk30(yj, nw, ext, 64 * c + lane);
+    }
+    limb_apply<CW>(a, b, 1, 0, 0, 1, CW, lane0);
+    int result = 1;
+    uint64_t g = 0;
+    int ns = CW;
+    const int max_rounds = (32 * (nw > nwd ? nw : nwd)) / 12 + 64;
+    for (int round = 0; round < max_rounds; round++) {
+        const int h = top_limb<CW>(a, b, ns);
+        if (h < 0 || h >= 64 * CW - 2) break;  // both zero (cannot happen with d > 0), or no headroom left
+        ns = (h + 1) / 64 + 1;
+        if (h <= 3) {
+            // exact values from limbs 0..3, then the binary gcd
+            __int128 va = 0, vb = 0;
+#pragma unroll
+            for (int k = 3; k >= 0; k--) {
+                va = va * (1 << 30) + __builtin_amdgcn_readlane(a[0], k);
+                vb = vb * (1 << 30) + __builtin_amdgcn_readlane(b[0], k);
+            }
+            unsigned __int128 u = (unsigned __int128)(va < 0 ? -va : va);
+            unsigned __int128 v = (unsigned __int128)(vb < 0 ? -vb : vb);
+            auto ctz = [](unsigned __int128 x) -> int {
+                const uint64_t lo = (uint64_t)x;
+                return lo ? __builtin_ctzll(lo) : 64 + __builtin_ctzll((uint64_t)(x >> 64));
+            };
+            if (u == 0) {
+                u = v;
+            } else if (v != 0) {
+                const int sh = ctz(u | v);
+                u >>= ctz(u);
+                do {
+                    v >>= ctz(v);
+                    if (u > v) {
+                        const unsigned __int128 t = u;
+                        u = v;
+                        v = t;
+                    }
+                    v -= u;
+                } while (v != 0);
+                u <<= sh;
+            }
+            if ((uint64_t)(u >> 64) == 0) {
+                g = (uint64_t)u;
+                result = 0;
+            }
+            break;
         }
+        double fa = lead3<CW>(a, h), fb = lead3<CW>(b, h);
+        if (fa < 0.0) {
+            limb_negate<CW>(a, ns);
+            fa = -fa;
+        }
+        if (fb < 0.0) {
+            limb_negate<CW>(b, ns);
+            fb = -fb;
+        }
+        // both at one scale with the larger below 2^52
+        int e;
+        (void)frexp(fmax(fa, fb), &e);
+        double x = floor(ldexp(fa, 52 - e)), y = floor(ldexp(fb, 52 - e));
+        // Euclid on the leading parts (exact integers below 2^53, the same in
+        // every lane), four steps at a time; a step counts only when it and
+        // every step before it are acceptable
+        double A = 1.0, B = 0.0, C = 0.0, D = 1.0;
+        int steps = 0;
+        for (int it = 0; it < 16; it++) {
+            double x1, y1, A1, B1, C1, D1, x2, y2, A2, B2, C2, D2;
+            double x3, y3, A3, B3, C3, D3, x4, y4, A4, B4, C4, D4;
+            const bool o1 = euclid_step(x, y, A, B, C, D, x1, y1, A1, B1, C1, D1);
+            const bool o2 = euclid_step(x1, y1, A1, B1, C1, D1, x2, y2, A2, B2, C2, D2) && o1;
+            const bool o3 = euclid_step(x2, y2, A2, B2, C2, D2, x3, y3, A3, B3, C3, D3) && o2;
+            const bool o4 = euclid_step(x3, y3, A3, B3, C3, D3, x4, y4, A4, B4, C4, D4) && o3;
+            if (__ballot(o4) != 0) {
+                x = x4, y = y4, A = A4, B = B4, C = C4, D = D4;
+                steps += 4;
+                continue;
+            }
+            if (__ballot(o3) != 0) {
+                A = A3, B = B3, C = C3, D = D3;
+                steps += 3;
+            } else if (__ballot(o2) != 0) {
+                A = A2, B = B2, C = C2, D = D2;
+                steps += 2;
+            } else if (__ballot(o1) != 0) {
+                A = A1, B = B1, C = C1, D = D1;
+                steps += 1;
+            }
+            break;
+        }
+        if (steps == 0) break;  // no certain progress: the host finishes
+        limb_apply<CW>(a, b, __builtin_amdgcn_readfirstlane((int32_t)A), __builtin_amdgcn_readfirstlane((int32_t)B),
+                       __builtin_amdgcn_readfirstlane((int32_t)C), __builtin_amdgcn_readfirstlane((int32_t)D), ns,
+                       lane0);
     }
-#pragma unroll
-    for (int e = 0; e < 3; e++) {
-        const int w = w0 + e;
-        const int owner = w / CW;
-        ra[e] = owner < 64 ? (uint32_t)__builtin_amdgcn_readlane((int)va[e], owner) : 0u;
-        rb[e] = owner < 64 ? (uint32_t)__builtin_amdgcn_readlane((int)vb[e], owner) : 0u;
+    if (lane == 0) {
+        gstat[j] = result;
+        G[j] = g;
     }
 }
 
-// -1, 0, 1 as a < b, a == b, a > b
-template <int CW>
-__device__ __forceinline__ int wave_cmp(const uint32_t (&a)[CW], const uint32_t (&b)[CW], int lane) {
-    int r = 0;
-#pragma unroll
-    for (int c = 0; c < CW; c++)
-        if (a[c] != b[c]) r = a[c] > b[c] ? 1 : -1;
-    const uint64_t mask = __ballot(r != 0);
-    if (mask == 0) return 0;
-    return __builtin_amdgcn_readlane(r, 63 - __builtin_clzll(mask));
-}
-
+// ---------------------------------------------------------------- numerators
+// One wave per component, lane l holding words [l CW, l CW + CW) of
+// V = sum_col (V[j][col] + 128 rowsum_j) 256^col (the +128 undoes the -128
+// offset of the weights).  t = round(V / M) comes from the twelve top columns
+// in double precision, read by every lane in the same order (exact whenever
+// |V - t M| is far below M / 2, as for every acceptable numerator); then
+// y = V - t M word by word with a lane-local carry chain and the wave carry.
+// status[j]: 0 when 0 <= y < 2^nbits, 1 when -2^nbits <= y < 0 (Y[j] holds
+// words 0 .. nbits / 32 of y, two's complement), 2 otherwise (the host
+// reconstructs that component alone).
 // Adds the lane-local carries out (cout, signed) into the next lanes.
 template <int CW>
 __device__ __forceinline__ void wave_carry(uint32_t (&R)[CW], int64_t cout, int lane) {
@@ -343,160 +510,6 @@ __device__ __forceinline__ void wave_carry(uint32_t (&R)[CW], int64_t cout, int 
     }
 }
 
-// |R| for a two's-complement R whose sign bit is the top bit of word 64 CW - 1
-template <int CW>
-__device__ __forceinline__ void wave_abs(uint32_t (&R)[CW], int lane) {
-    const uint32_t top = (uint32_t)__builtin_amdgcn_readlane((int)R[CW - 1], 63);
-    if ((top >> 31) == 0) return;
-#pragma unroll
-    for (int c = 0; c < CW; c++) R[c] = ~R[c];
-    int64_t carry = lane == 0 ? 1 : 0;  // + 1 at word 0
-#pragma unroll
-    for (int c = 0; c < CW; c++) {
-        const int64_t v = (int64_t)R[c] + carry;
-        R[c] = (uint32_t)v;
-        carry = v >> 32;
-    }
-    wave_carry<CW>(R, carry, lane);
-}
-
-// R <- p R - q S for magnitudes p, q < 2^27 (lane-local words, carries out)
-template <int CW>
-__device__ __forceinline__ int64_t lincomb(uint32_t (&out)[CW], const uint32_t (&R)[CW], const uint32_t (&S)[CW],
-                                           uint32_t p, uint32_t q) {
-    int64_t carry = 0;
-#pragma unroll
-    for (int c = 0; c < CW; c++) {
-        const int64_t v = carry + (int64_t)((uint64_t)p * R[c]) - (int64_t)((uint64_t)q * S[c]);
-        out[c] = (uint32_t)v;
-        carry = v >> 32;
-    }
-    return carry;
-}
-
-template <int CW>
-__global__ __launch_bounds__(256) void gcd_kernel(const uint32_t* __restrict__ Y, int nw,
-                                                  const int* __restrict__ status, int valid_rows,
-                                                  const uint32_t* __restrict__ Dw, int nwd,
-                                                  uint64_t* __restrict__ G, int* __restrict__ gstat) {
-    const int lane = threadIdx.x & 63;
-    const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (j >= valid_rows) return;
-    if (status[j] >= 2) {
-        if (lane == 0) gstat[j] = 1;
-        return;
-    }
-    // a = d, b = |y| (y arrives as nw two's-complement words, status 1 when negative)
-    const uint32_t ext = status[j] == 1 ? 0xffffffffu : 0u;
-    uint32_t a[CW], b[CW];
-#pragma unroll
-    for (int c = 0; c < CW; c++) {
-        const int w = lane * CW + c;
-        a[c] = w < nwd ? Dw[w] : 0u;
-        b[c] = w < nw ? Y[(size_t)j * nw + w] : ext;
-    }
-    wave_abs<CW>(b, lane);
-    int result = 1;
-    uint64_t g = 0;
-    const int max_rounds = (32 * (nw > nwd ? nw : nwd)) / 12 + 64;
-    for (int round = 0; round < max_rounds; round++) {
-        int ia, ib;
-        uint32_t wa, wb;
-        wave_highest2<CW>(a, b, &ia, &wa, &ib, &wb);
-        int la = ia < 0 ? 0 : 32 * ia + 32 - __builtin_clz(wa);
-        int lb = ib < 0 ? 0 : 32 * ib + 32 - __builtin_clz(wb);
-        if (la < lb || (la == lb && la > 0 && wave_cmp<CW>(a, b, lane) < 0)) {
-#pragma unroll
-            for (int c = 0; c < CW; c++) {
-                const uint32_t t = a[c];
-                a[c] = b[c];
-                b[c] = t;
-            }
-            const int t = la;
-            la = lb;
-            lb = t;
-        }
-        uint32_t ta[3], tb[3];
-        if (la <= 64 || lb == 0) {  // gcd of values within 64 bits, or gcd(a, 0) = a
-            if (la > 64) break;  // a multiword gcd: the host finishes
-            wave_words3<CW>(a, b, 0, ta, tb);
-            uint64_t x = ((uint64_t)ta[1] << 32) | ta[0], y = ((uint64_t)tb[1] << 32) | tb[0];
-            while (y) {
-                const uint64_t t = x % y;
-                x = y;
-                y = t;
-            }
-            g = x;
-            result = 0;
-            break;
-        }
-        if (la - lb > 25) break;  // quotient of 2^25 or more: the host finishes
-        // 52 leading bits of a and the bits of b at the same position
-        const int s = la - 52;  // > 12 here
-        wave_words3<CW>(a, b, s >> 5, ta, tb);
-        const int o = s & 31;
-        const uint64_t mask52 = (1ull << 52) - 1;
-        const uint64_t xa = ((((uint64_t)ta[1] << 32) | ta[0]) >> o | ((uint64_t)ta[2] << (64 - o))) & mask52;
-        const uint64_t xb = ((((uint64_t)tb[1] << 32) | tb[0]) >> o | ((uint64_t)tb[2] << (64 - o))) & mask52;
-        // Euclid on the leading bits in double precision (every value an exact integer below 2^53)
-        double x = (double)xa, y = (double)xb;
-        double A = 1.0, B = 0.0, C = 0.0, D = 1.0;
-        int steps = 0;
-        while (y >= 0x1p26) {
-            double q = floor(x * __builtin_amdgcn_rcp(y));
-            double r = fma(-q, y, x);
-            if (r < 0.0) {
-                q -= 1.0;
-                r += y;
-            } else if (r >= y) {
-                q += 1.0;
-                r -= y;
-            }
-            const double nC = fma(-q, C, A), nD = fma(-q, D, B);
-            if (q >= 0x1p26 || fabs(nC) > 0x1p26 || fabs(nD) > 0x1p26) break;
-            A = C;
-            B = D;
-            C = nC;
-            D = nD;
-            x = y;
-            y = r;
-            steps++;
-        }
-        if (steps == 0) break;  // no certain progress: the host finishes
-        // (a, b) <- (A a + B b, C a + D b): A and B (and C and D) have opposite
-        // signs, so each new number is sign * (|A| a - |B| b) or sign * (|B| b - |A| a)
-        const bool apos = A > 0.0, cpos = C > 0.0;
-        const uint32_t pa = (uint32_t)fabs(A), pb = (uint32_t)fabs(B);
-        const uint32_t pc = (uint32_t)fabs(C), pd = (uint32_t)fabs(D);
-        uint32_t na[CW], nb[CW];
-        const int64_t ca = apos ? lincomb<CW>(na, a, b, pa, pb) : lincomb<CW>(na, b, a, pb, pa);
-        const int64_t cb = cpos ? lincomb<CW>(nb, a, b, pc, pd) : lincomb<CW>(nb, b, a, pd, pc);
-#pragma unroll
-        for (int c = 0; c < CW; c++) {
-            a[c] = na[c];
-            b[c] = nb[c];
-        }
-        wave_carry<CW>(a, ca, lane);
-        wave_carry<CW>(b, cb, lane);
-        wave_abs<CW>(a, lane);
-        wave_abs<CW>(b, lane);
-    }
-    if (lane == 0) {
-        gstat[j] = result;
-        G[j] = g;
-    }
-}
-
-// ---------------------------------------------------------------- numerators
-// One wave per component, lane l holding words [l CW, l CW + CW) of
-// V = sum_col (V[j][col] + 128 rowsum_j) 256^col (the +128 undoes the -128
-// offset of the weights).  t = round(V / M) comes from the twelve top columns
-// in double precision, read by every lane in the same order (exact whenever
-// |V - t M| is far below M / 2, as for every acceptable numerator); then
-// y = V - t M word by word with a lane-local carry chain and the wave carry.
-// status[j]: 0 when 0 <= y < 2^nbits, 1 when -2^nbits <= y < 0 (Y[j] holds
-// words 0 .. nbits / 32 of y, two's complement), 2 otherwise (the host
-// reconstructs that component alone).
 template <int CW>
 __global__ __launch_bounds__(256) void numer_kernel(const int* __restrict__ V, int Ncolsp,
                                                     const int* __restrict__ rowsum, int valid_rows,
@@ -578,16 +591,17 @@ hipError_t launch_recon_gemm(const int8_t* S, const int8_t* WT, int Kpad, int NC
     return hipGetLastError();
 }
 
-// Words per lane for numbers of up to `words` words, with two words of
-// headroom for the cofactor products (|A a + B b| < 2^31 max(a, b)).
+// Limb slots per lane for numbers of up to `words` 32-bit words: 30-bit
+// limbs with three limbs of headroom for the cofactor products
+// (|A a + B b| < 2^27 max(|a|, |b|)).
 int gcd_words_per_lane(int words) {
-    words += 2;
-    return words <= 64 * 8 ? 8 : words <= 64 * 16 ? 16 : words <= 64 * 32 ? 32 : 0;
+    const int limbs = (32 * words + 29) / 30 + 3;
+    return limbs <= 64 * 8 ? 8 : limbs <= 64 * 16 ? 16 : limbs <= 64 * 32 ? 32 : 0;
 }
 
 hipError_t launch_gcd(const uint32_t* Y, int nw, const int* status, int valid_rows, const uint32_t* Dw, int nwd,
                       uint64_t* G, int* gstat, hipStream_t st) {
-    const int cw = gcd_words_per_lane(nw > nwd ? nw : nwd);  // includes two words of headroom
+    const int cw = gcd_words_per_lane(nw > nwd ? nw : nwd);
     const dim3 grid((valid_rows + 3) / 4);
     if (cw == 8)
         hipLaunchKernelGGL(gcd_kernel<8>, grid, dim3(256), 0, st, Y, nw, status, valid_rows, Dw, nwd, G, gstat);
