@@ -455,41 +455,15 @@ static bool lehmer_matrix(int64_t xh, int64_t yh, int64_t* A, int64_t* B, int64_
     return b != 0;
 }
 
+static void lincomb_rem(limb_t* x, limb_t* y, size_t n, int64_t A, int64_t B, int64_t C, int64_t D);
+
 // (x, y) <- (A x + B y, C x + D y) in place, for nonnegative x, y whose
-// images are nonnegative (guaranteed by Algorithm L).  The cofactors come in
-// sign pattern (+, -, -, +) or (-, +, +, -), so each new limb is a difference
-// of two unsigned 64 x 64 -> 128-bit products.
+// images are nonnegative (guaranteed by Algorithm L).
 static void apply_matrix(BigInt& x, BigInt& y, int64_t A, int64_t B, int64_t C, int64_t D) {
     const size_t n = std::max(x.size(), y.size());
     x.d.resize(n, 0);
     y.d.resize(n, 0);
-    // new_x = p1 * u1 - p2 * u2, new_y = p3 * u3 - p4 * u4 with u in {x, y}
-    const bool even = A >= 0 && B <= 0 && C <= 0 && D >= 0;
-    const uint64_t a = (uint64_t)(A < 0 ? -A : A), b = (uint64_t)(B < 0 ? -B : B);
-    const uint64_t c = (uint64_t)(C < 0 ? -C : C), d = (uint64_t)(D < 0 ? -D : D);
-    limb_t* xp = x.d.data();
-    limb_t* yp = y.d.data();
-    u128 px = 0, mx = 0, py = 0, my = 0;  // running positive / negative partial sums (carries)
-    for (size_t i = 0; i < n; i++) {
-        const u128 xi = xp[i], yi = yp[i];
-        // new_x: even -> a x - b y ; odd -> b y - a x.  new_y: even -> d y - c x ; odd -> c x - d y
-        px += even ? a * xi : b * yi;
-        mx += even ? b * yi : a * xi;
-        py += even ? d * yi : c * xi;
-        my += even ? c * xi : d * yi;
-        // limb i of (px - mx): borrow handled by keeping both sums and carrying their high parts
-        const limb_t lx = (limb_t)px - (limb_t)mx;
-        const limb_t bx = (limb_t)px < (limb_t)mx;
-        const limb_t ly = (limb_t)py - (limb_t)my;
-        const limb_t by = (limb_t)py < (limb_t)my;
-        xp[i] = lx;
-        yp[i] = ly;
-        px = (px >> 64);
-        mx = (mx >> 64) + bx;
-        py = (py >> 64);
-        my = (my >> 64) + by;
-    }
-    if (px != mx || py != my) throw std::logic_error("Lehmer step left a carry");
+    lincomb_rem(x.d.data(), y.d.data(), n, A, B, C, D);
     x.trim();
     y.trim();
 }
@@ -526,43 +500,158 @@ BigInt lcm(const BigInt& a, const BigInt& b) {
     return r;
 }
 
+// Raw-limb pieces of the extended Euclid below.  Lengths are kept trimmed
+// (no leading zero limbs).
+static size_t trimmed(const limb_t* x, size_t n) {
+    while (n && x[n - 1] == 0) n--;
+    return n;
+}
+
+static size_t bits_of(const limb_t* x, size_t n) {
+    return n ? 64 * n - (size_t)__builtin_clzll(x[n - 1]) : 0;
+}
+
+// -1, 0, 1 as x < y, x == y, x > y
+static int cmp_limbs(const limb_t* x, size_t nx, const limb_t* y, size_t ny) {
+    if (nx != ny) return nx < ny ? -1 : 1;
+    for (size_t i = nx; i-- > 0;)
+        if (x[i] != y[i]) return x[i] < y[i] ? -1 : 1;
+    return 0;
+}
+
+// (x, y) <- (A x + B y, C x + D y) for nonnegative x, y (n limbs each, zero
+// padded) whose images are nonnegative; the cofactors have the sign pattern
+// (+, -, -, +) (EVEN) or (-, +, +, -) and magnitudes a, b, c, d below 2^63,
+// so every partial sum fits a signed 128-bit accumulator.
+template <bool EVEN>
+static void lincomb_rem_t(limb_t* x, limb_t* y, size_t n, uint64_t a, uint64_t b, uint64_t c, uint64_t d) {
+    i128 cx = 0, cy = 0;
+    for (size_t i = 0; i < n; i++) {
+        const uint64_t xi = x[i], yi = y[i];
+        if (EVEN) {
+            cx += (i128)((u128)a * xi) - (i128)((u128)b * yi);
+            cy += (i128)((u128)d * yi) - (i128)((u128)c * xi);
+        } else {
+            cx += (i128)((u128)b * yi) - (i128)((u128)a * xi);
+            cy += (i128)((u128)c * xi) - (i128)((u128)d * yi);
+        }
+        x[i] = (limb_t)cx;
+        y[i] = (limb_t)cy;
+        cx >>= 64;
+        cy >>= 64;
+    }
+    if (cx != 0 || cy != 0) throw std::logic_error("Lehmer step left a carry");
+}
+
+static void lincomb_rem(limb_t* x, limb_t* y, size_t n, int64_t A, int64_t B, int64_t C, int64_t D) {
+    const uint64_t a = (uint64_t)(A < 0 ? -A : A), b = (uint64_t)(B < 0 ? -B : B);
+    const uint64_t c = (uint64_t)(C < 0 ? -C : C), d = (uint64_t)(D < 0 ? -D : D);
+    if (A >= 0 && B <= 0) lincomb_rem_t<true>(x, y, n, a, b, c, d);
+    else lincomb_rem_t<false>(x, y, n, a, b, c, d);
+}
+
+// (s, t) <- (a s + b t, c s + d t) for magnitudes below 2^62 (a s_i + b t_i
+// plus the carry stays below 2^128); s, t hold n limbs and room for one more
+static size_t lincomb_mag(limb_t* s, limb_t* t, size_t n, uint64_t a, uint64_t b, uint64_t c, uint64_t d) {
+    if ((a | b | c | d) >> 62) throw std::logic_error("cofactor out of range");
+    u128 cs = 0, ct = 0;
+    for (size_t i = 0; i < n; i++) {
+        const uint64_t si = s[i], ti = t[i];
+        cs += (u128)a * si + (u128)b * ti;
+        ct += (u128)c * si + (u128)d * ti;
+        s[i] = (limb_t)cs;
+        t[i] = (limb_t)ct;
+        cs >>= 64;
+        ct >>= 64;
+    }
+    s[n] = (limb_t)cs;
+    t[n] = (limb_t)ct;
+    return cs || ct ? n + 1 : n;
+}
+
 bool rational_reconstruct(const BigInt& a, const BigInt& M, const BigInt& N, const BigInt& D,
-                          BigInt* num, BigInt* den) {
-    // extended Euclid on (M, a) tracking the cofactor of a
-    BigInt r0 = M, r1 = a, t0, t1 = BigInt::from_u64(1);
-    r1.neg = false;
+                          BigInt* num, BigInt* den, bool require_coprime) {
+    // extended Euclid on (M, a) tracking the cofactor of a: r_k = s_k M + t_k a.
+    // The t_k alternate in sign, so their magnitudes only add:
+    // |t_{k+1}| = |t_{k-1}| + q_k |t_k|, and a Lehmer matrix acts on them as
+    // (|A| |t0| + |B| |t1|, |C| |t0| + |D| |t1|).
+    const size_t L = M.size() + 2;
+    std::vector<limb_t> r0(L, 0), r1(L, 0), t0(L, 0), t1(L, 0);
+    std::copy(M.d.begin(), M.d.end(), r0.begin());
+    std::copy(a.d.begin(), a.d.end(), r1.begin());
+    size_t n0 = M.size(), n1 = trimmed(r1.data(), a.size()), nt = 1;
+    t1[0] = 1;
+    bool t1neg = false;  // t0 has the other sign (or is 0)
     const size_t nbits = N.bit_length();
-    while (cmp_abs(r1, N) > 0) {
-        if (r1.bit_length() > nbits + 64 && r0.size() > 1) {
-            int64_t xh, yh, A, B, C, D2;
-            leading_pair(r0, r1, &xh, &yh);
+    auto above_N = [&]() { return cmp_limbs(r1.data(), n1, N.d.data(), N.size()) > 0; };
+    while (above_N()) {
+        const size_t b0 = bits_of(r0.data(), n0);
+        if (bits_of(r1.data(), n1) > nbits + 64 && n0 > 1) {
+            // leading 62 bits of r0 and the bits of r1 at the same position
+            const size_t sh = b0 - 62;
+            auto lead = [&](const std::vector<limb_t>& v, size_t nv) -> int64_t {
+                const size_t w = sh / 64, o = sh % 64;
+                if (w >= nv) return 0;
+                uint64_t lo = v[w] >> o;
+                if (o && w + 1 < nv) lo |= v[w + 1] << (64 - o);
+                return (int64_t)(lo & ((1ULL << 63) - 1));
+            };
+            const int64_t xh = lead(r0, n0), yh = lead(r1, n1);
+            int64_t A, B, C, D2;
             if (yh != 0 && lehmer_matrix(xh, yh, &A, &B, &C, &D2)) {
-                apply_matrix(r0, r1, A, B, C, D2);
-                BigInt nt0 = add(mul_small(t0, A), mul_small(t1, B));
-                BigInt nt1 = add(mul_small(t0, C), mul_small(t1, D2));
-                t0 = std::move(nt0);
-                t1 = std::move(nt1);
-                if (cmp_abs(r0, N) <= 0) throw std::logic_error("Lehmer step passed the stopping point");
+                lincomb_rem(r0.data(), r1.data(), n0, A, B, C, D2);
+                n0 = trimmed(r0.data(), n0);
+                n1 = trimmed(r1.data(), n0 > n1 ? n0 : n1);
+                const uint64_t ua = (uint64_t)(A < 0 ? -A : A), ub = (uint64_t)(B < 0 ? -B : B);
+                const uint64_t uc = (uint64_t)(C < 0 ? -C : C), ud = (uint64_t)(D2 < 0 ? -D2 : D2);
+                nt = lincomb_mag(t0.data(), t1.data(), nt, ua, ub, uc, ud);
+                if (D2 < 0) t1neg = !t1neg;
+                if (cmp_limbs(r0.data(), n0, N.d.data(), N.size()) <= 0)
+                    throw std::logic_error("Lehmer step passed the stopping point");
                 continue;
             }
         }
-        BigInt q, r;
-        divmod_trunc(r0, r1, &q, &r);
-        BigInt t = sub(t0, mul(q, t1));
-        r0 = std::move(r1);
-        r1 = std::move(r);
-        t0 = std::move(t1);
-        t1 = std::move(t);
+        // one Euclidean step with a full division
+        BigInt x, y, q, r;
+        x.d.assign(r0.begin(), r0.begin() + n0);
+        y.d.assign(r1.begin(), r1.begin() + n1);
+        divmod_trunc(x, y, &q, &r);
+        // t0 <- |t0| + q |t1| (then swap): the new cofactor takes t0's sign
+        BigInt tm;
+        tm.d.assign(t1.begin(), t1.begin() + nt);
+        tm.trim();
+        BigInt prod = mul(q, tm);
+        BigInt t0b;
+        t0b.d.assign(t0.begin(), t0.begin() + nt);
+        t0b.trim();
+        BigInt nt0 = add(t0b, prod);
+        std::fill(r0.begin(), r0.end(), 0);
+        std::copy(r1.begin(), r1.begin() + n1, r0.begin());
+        n0 = n1;
+        std::fill(r1.begin(), r1.end(), 0);
+        std::copy(r.d.begin(), r.d.end(), r1.begin());
+        n1 = r.size();
+        std::fill(t0.begin(), t0.end(), 0);
+        std::copy(t1.begin(), t1.begin() + nt, t0.begin());
+        std::fill(t1.begin(), t1.end(), 0);
+        std::copy(nt0.d.begin(), nt0.d.end(), t1.begin());
+        nt = std::max(nt, nt0.size());
+        t1neg = !t1neg;
     }
-    if (t1.is_zero() || cmp_abs(t1, D) > 0) return false;
-    BigInt g = gcd(r1, t1);
-    if (!(g.size() == 1 && g.d[0] == 1)) return false;
-    *num = r1;
-    *den = t1;
-    if (t1.neg) {
-        num->neg = !r1.is_zero();
-        den->neg = false;
+    BigInt rr, tt;
+    rr.d.assign(r1.begin(), r1.begin() + n1);
+    rr.trim();
+    tt.d.assign(t1.begin(), t1.begin() + nt);
+    tt.trim();
+    if (tt.is_zero() || cmp_abs(tt, D) > 0) return false;
+    if (require_coprime) {
+        BigInt g = gcd(rr, tt);
+        if (!(g.size() == 1 && g.d[0] == 1)) return false;
     }
+    // a == r1 / t1 (mod M): a negative t1 moves its sign to the numerator
+    *num = rr;
+    num->neg = t1neg && !rr.is_zero();
+    *den = tt;
     return true;
 }
 

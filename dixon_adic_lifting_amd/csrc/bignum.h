@@ -53,9 +53,12 @@ BigInt lcm(const BigInt& a, const BigInt& b);       // >= 0
 
 // Wang's rational reconstruction: the unique num/den with num == a * den
 // (mod M), |num| <= N, 0 < den <= D, gcd(num, den) = 1, given 2 N D < M and
-// 0 <= a < M.  Returns false if there is none.
+// 0 <= a < M.  Returns false if there is none.  With require_coprime false
+// the final gcd(num, den) = 1 test is skipped: the result is then the
+// remainder / cofactor pair where the Euclidean sequence first drops to N,
+// whose den is the true denominator whenever such a fraction exists.
 bool rational_reconstruct(const BigInt& a, const BigInt& M, const BigInt& N,
-                          const BigInt& D, BigInt* num, BigInt* den);
+                          const BigInt& D, BigInt* num, BigInt* den, bool require_coprime = true);
 
 // low-level magnitude routines (exposed for tests)
 void mag_mul(limb_t* r, const limb_t* a, size_t la, const limb_t* b, size_t lb);
