@@ -79,10 +79,12 @@ struct LiftParams {
     uint32_t mu16[kNumPrimes];
     uint32_t mu32[kNumPrimes];
     uint32_t r32[kNumPrimes];
-    uint32_t pad1[3];
-    uint64_t corr[kDigitWords];   // 128 * sum_l Qw[l][w], see garner kernels
-    uint32_t Qw[kNumPrimes][kDigitWords];  // words of Q_l = prod_{l' < l} q_l'
-    uint8_t ginv[kNumPrimes][64];          // ginv[l][k] = q_l^-1 mod q_k (l < k)
+    uint32_t cinv[kNumPrimes];    // (P / q_l)^-1 mod q_l
+    uint32_t Pw[kDigitWords];     // words of P
+    uint32_t Phw[kDigitWords];    // words of (P - 1) / 2
+    uint32_t pad1[1];
+    double qrec[kNumPrimes];      // 1 / q_l
+    double Wd[kNumPrimes][kDigitWords];  // words of P / q_l (exact in double)
 };
 
 // Device workspace layout for an n x n system with c right-hand sides.

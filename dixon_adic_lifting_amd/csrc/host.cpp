@@ -121,22 +121,28 @@ void fill_lift_params(const LiveSet& ls, LiftParams* prm) {
         prm->mu32[l] = kPrimeTable.mu32[j];
         prm->r32[l] = kPrimeTable.r32[j];
     }
-    for (int l = 0; l < ls.E; l++)
-        for (int k = l + 1; k < ls.E; k++) prm->ginv[l][k] = (uint8_t)inv_mod_small(prm->q[l], prm->q[k]);
-    // Q_l = q_0 ... q_{l-1} as 32-bit words
-    BigInt Q = BigInt::from_u64(1);
+    // CRT constants: W_l = P / q_l, its inverse mod q_l, the words of P and
+    // of (P - 1) / 2
+    BigInt P = BigInt::from_u64(1);
+    for (int l = 0; l < ls.E; l++) P = mul_small(P, prm->q[l]);
+    auto word = [](const BigInt& v, int w) -> uint32_t {
+        const size_t limb = (size_t)w / 2;
+        const uint64_t x = limb < v.size() ? v.d[limb] : 0;
+        return (uint32_t)(w % 2 ? x >> 32 : x);
+    };
     for (int l = 0; l < ls.E; l++) {
-        for (int w = 0; w < kDigitWords; w++) {
-            size_t limb = (size_t)w / 2;
-            uint64_t v = limb < Q.size() ? Q.d[limb] : 0;
-            prm->Qw[l][w] = (uint32_t)(w % 2 ? v >> 32 : v);
-        }
-        Q = mul_small(Q, prm->q[l]);
+        const uint32_t q = prm->q[l];
+        const BigInt W = divexact(P, BigInt::from_u64(q));
+        uint64_t wmod = 0;  // W mod q, from the words
+        for (int w = kDigitWords - 1; w >= 0; w--) wmod = ((wmod << 32) | word(W, w)) % q;
+        prm->cinv[l] = (uint32_t)inv_mod_small((uint32_t)wmod, q);
+        prm->qrec[l] = 1.0 / (double)q;
+        for (int w = 0; w < kDigitWords; w++) prm->Wd[l][w] = (double)word(W, w);
     }
+    const BigInt Ph = shr_abs(P, 1);
     for (int w = 0; w < kDigitWords; w++) {
-        uint64_t s = 0;
-        for (int l = 0; l < ls.E; l++) s += prm->Qw[l][w];
-        prm->corr[w] = 128 * s;
+        prm->Pw[w] = word(P, w);
+        prm->Phw[w] = word(Ph, w);
     }
 }
 

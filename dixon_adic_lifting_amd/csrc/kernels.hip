@@ -1098,68 +1098,116 @@ __global__ __launch_bounds__(256) void lift_mfma_kernel(const int8_t* __restrict
     }
 }
 
-// ---------------------------------------------------------------- lift: balanced Garner
-// One wave per component, lane l holds the residue for live prime l.
-// Mixed-radix digits v_l (balanced, so x = sum v_l Q_l lies in
-// [-(P-1)/2, (P-1)/2], Q_l = q_0 ... q_{l-1}) come out one per iteration: v_l
-// is read from lane l, then every lane k > l replaces its value t_k by
-// (t_k - v_l) q_l^-1 mod q_k.  Lanes 0..11 accumulate word w of
-// sum (v_l + 128) Q_l (nonnegative factors for the unsigned multiply-add)
-// and subtract 128 sum Q_l at the end; a carry pass turns the 12 words into
-// the 384-bit two's-complement digit.  x mod 2^64 is kept for the residual.
-__global__ __launch_bounds__(256) void garner_wave_kernel(const LiftParams* __restrict__ prm,
-                                                          const uint8_t* __restrict__ U, int NC,
-                                                          uint64_t* __restrict__ digits, int kchunk,
-                                                          int slot, uint64_t* __restrict__ xlow) {
-    const int lane = threadIdx.x & 63;
-    const int comp = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (comp >= NC) return;
+// ---------------------------------------------------------------- lift: CRT
+// The balanced digit x (|x| <= (P - 1) / 2, x = r_l mod q_l for every live
+// prime) by the Chinese remainder formula with balanced coefficients:
+//   X = sum_l u_l W_l,  W_l = P / q_l,  u_l = (r_l c_l mod q_l) in (-q_l/2, q_l/2),
+//   c_l = W_l^-1 mod q_l,  so X = x (mod P) and |X| < E P / 2;
+//   x = X - k P with k = round(X / P) = round(sum_l u_l / q_l).
+// Four lanes per component, lane s taking the primes l = s mod 4; word w of
+// X accumulates sum_l u_l W_l[w] in double precision, exact (each term is
+// below 2^39 in magnitude, every partial sum below 2^45), and the four
+// partial sums are added across the lane quad.  k comes from the double sum
+// of u_l / q_l, whose error (about E 2^-54) can only matter when X / P is
+// within it of a half-integer; there an exact comparison with (P - 1) / 2
+// settles the representative.  x mod 2^64 is kept for the residual.
+
+// v + (v from lane l ^ X within the quad), for a double
+template <int X>
+__device__ __forceinline__ double quad_add(double v) {
+    constexpr int ctrl = X == 1 ? 0xb1 : 0x4e;  // quad_perm [1,0,3,2] / [2,3,0,1]
+    const uint64_t b = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, ctrl, 0xf, 0xf, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), ctrl, 0xf, 0xf, false);
+    return v + __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+
+__global__ __launch_bounds__(256) void crt_kernel(const LiftParams* __restrict__ prm, const uint8_t* __restrict__ U,
+                                                  int NC, uint64_t* __restrict__ digits, int kchunk, int slot,
+                                                  uint64_t* __restrict__ xlow) {
+    __shared__ double Wd[kNumPrimes][kDigitWords];
+    __shared__ double qrec[kNumPrimes];
+    __shared__ uint32_t qc[kNumPrimes][3];  // q, mu16, c
     const int E = prm->E;
-    const bool live = lane < E;
-    const bool wlane = lane < kDigitWords;
-    // Every per-lane constant of the serial loop is loaded up front, so the
-    // loop's E dependent iterations wait on no memory access.
-    uint32_t gi[kNumPrimes], qw[kNumPrimes];
-#pragma unroll
-    for (int l = 0; l < kNumPrimes; ++l) {
-        gi[l] = live ? prm->ginv[l][lane] : 0u;
-        qw[l] = wlane ? prm->Qw[l][lane] : 0u;
+    for (int i = threadIdx.x; i < kNumPrimes * kDigitWords; i += 256) (&Wd[0][0])[i] = (&prm->Wd[0][0])[i];
+    if (threadIdx.x < kNumPrimes) {
+        const int l = threadIdx.x;
+        qrec[l] = prm->qrec[l];
+        qc[l][0] = prm->q[l];
+        qc[l][1] = prm->mu16[l];
+        qc[l][2] = prm->cinv[l];
     }
-    const uint32_t qk = live ? prm->q[lane] : 1u;
-    const uint32_t muk = live ? prm->mu16[lane] : 0u;
-    uint32_t t = live ? U[(size_t)lane * NC + comp] : 0u;
-    uint64_t acc = 0;
+    __syncthreads();
+    const int s = threadIdx.x & 3;
+    const int comp = blockIdx.x * 64 + (threadIdx.x >> 2);
+    if (comp >= NC) return;  // the whole quad leaves together
+    constexpr int LPL = (kNumPrimes + 3) / 4;  // primes per lane
+    uint32_t res[LPL];
 #pragma unroll
-    for (int l = 0; l < kNumPrimes; ++l) {
-        if (l < E) {
-            const uint32_t ql = (uint32_t)__builtin_amdgcn_readlane((int)qk, l);  // lane l holds q_l
-            int vl = __builtin_amdgcn_readlane((int)t, l);
-            vl = vl > (int)(ql >> 1) ? vl - (int)ql : vl;
-            if (lane > l && live) {
-                int d = (int)t - vl;  // in (-q_k/2, 3q_k/2) since |v_l| < q_l/2 < q_k/2
-                d = d < 0 ? d + (int)qk : d;
-                d = d >= (int)qk ? d - (int)qk : d;
-                t = red16(__umul24((uint32_t)d, gi[l]), qk, muk);
+    for (int i = 0; i < LPL; i++) {
+        const int l = s + 4 * i;
+        res[i] = l < E ? U[(size_t)l * NC + comp] : 0u;
+    }
+    double acc[kDigitWords];
+#pragma unroll
+    for (int w = 0; w < kDigitWords; w++) acc[w] = 0.0;
+    double f = 0.0;
+#pragma unroll
+    for (int i = 0; i < LPL; i++) {
+        const int l = s + 4 * i;
+        if (l >= E) continue;
+        const uint32_t q = qc[l][0];
+        const uint32_t u = red16(res[i] * qc[l][2], q, qc[l][1]);
+        const double ud = (double)(u > (q >> 1) ? (int)u - (int)q : (int)u);
+        f = fma(ud, qrec[l], f);
+#pragma unroll
+        for (int w = 0; w < kDigitWords; w++) acc[w] = fma(ud, Wd[l][w], acc[w]);
+    }
+    f = quad_add<2>(quad_add<1>(f));
+#pragma unroll
+    for (int w = 0; w < kDigitWords; w++) acc[w] = quad_add<2>(quad_add<1>(acc[w]));
+    if (s != 0) return;
+    const double k = rint(f);
+    const int64_t ki = (int64_t)k;
+    uint32_t x[kDigitWords];
+    int64_t carry = 0;
+#pragma unroll
+    for (int w = 0; w < kDigitWords; w++) {
+        const int64_t v = (int64_t)acc[w] - ki * (int64_t)prm->Pw[w] + carry;
+        x[w] = (uint32_t)v;
+        carry = v >> 32;
+    }
+    if (fabs(f - k) > 0.5 - 0x1p-30) {
+        // near the boundary: compare with (P - 1) / 2 exactly
+        const bool neg = (int32_t)x[kDigitWords - 1] < 0;
+        // neg: is x + (P - 1) / 2 negative?  else: is x - (P - 1) / 2 positive?
+        int64_t c = 0;
+        uint32_t y[kDigitWords];
+#pragma unroll
+        for (int w = 0; w < kDigitWords; w++) {
+            const int64_t v = (int64_t)x[w] + (neg ? (int64_t)prm->Phw[w] : -(int64_t)prm->Phw[w]) + c;
+            y[w] = (uint32_t)v;
+            c = v >> 32;
+        }
+        bool nz = false;
+#pragma unroll
+        for (int w = 0; w < kDigitWords; w++) nz |= y[w] != 0u;
+        const bool out = neg ? (int32_t)y[kDigitWords - 1] < 0 : ((int32_t)y[kDigitWords - 1] >= 0 && nz);
+        if (out) {
+            c = 0;
+#pragma unroll
+            for (int w = 0; w < kDigitWords; w++) {
+                const int64_t v = (int64_t)x[w] + (neg ? (int64_t)prm->Pw[w] : -(int64_t)prm->Pw[w]) + c;
+                x[w] = (uint32_t)v;
+                c = v >> 32;
             }
-            acc += (uint64_t)(uint32_t)(vl + 128) * (uint64_t)qw[l];
         }
     }
-    if (lane < kDigitWords) acc -= prm->corr[lane];
-    const uint32_t alo = (uint32_t)acc, ahi = (uint32_t)(acc >> 32);
-    int64_t carry = 0;
-    uint32_t word = 0, word1 = 0;
-#pragma unroll
-    for (int w = 0; w < kDigitWords; ++w) {
-        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)alo, w);
-        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)ahi, w);
-        const int64_t s = (int64_t)(((uint64_t)hi << 32) | lo) + carry;
-        if (lane == w) word = (uint32_t)s;
-        if (w == 1) word1 = (uint32_t)s;
-        carry = s >> 32;
-    }
-    uint32_t* dst = (uint32_t*)(digits + ((size_t)comp * kchunk + slot) * kDigitLimbs);
-    if (lane < kDigitWords) dst[lane] = word;
-    if (lane == 0) xlow[comp] = ((uint64_t)word1 << 32) | word;
+    uint4* dst = (uint4*)(digits + ((size_t)comp * kchunk + slot) * kDigitLimbs);
+    dst[0] = make_uint4(x[0], x[1], x[2], x[3]);
+    dst[1] = make_uint4(x[4], x[5], x[6], x[7]);
+    dst[2] = make_uint4(x[8], x[9], x[10], x[11]);
+    xlow[comp] = ((uint64_t)x[1] << 32) | x[0];
 }
 
 // ---------------------------------------------------------------- lift: residual
@@ -1351,7 +1399,7 @@ hipError_t launch_lift_contract(const Layout& L, uint8_t* ws, int E, hipStream_t
 
 hipError_t launch_lift_garner(const Layout& L, uint8_t* ws, int slot, hipStream_t st) {
     const int NC = L.n * L.c;
-    hipLaunchKernelGGL(garner_wave_kernel, dim3((NC + 3) / 4), dim3(256), 0, st,
+    hipLaunchKernelGGL(crt_kernel, dim3((NC + 63) / 64), dim3(256), 0, st,
                        (const LiftParams*)(ws + L.off_params), (const uint8_t*)(ws + L.off_U), NC,
                        L.dig_dev ? L.dig_dev : (uint64_t*)(ws + L.off_digits), L.kchunk, slot,
                        (uint64_t*)(ws + L.off_xlow));
