@@ -10,14 +10,19 @@
 #include "host.h"
 
 #include <sched.h>
+#include <unistd.h>
 
 #include <algorithm>
 #include <atomic>
 #include <chrono>
 #include <cmath>
+#include <condition_variable>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <exception>
+#include <functional>
+#include <mutex>
 #include <thread>
 
 #include "../../include/es_solve.h"
@@ -250,22 +255,109 @@ int default_threads() {
     return h ? (int)h : 1;
 }
 
+// A pool of worker threads started on first use and kept for the life of
+// the process (thread start-up costs far more than the short host phases of
+// a solve).  One job at a time: a caller that finds the pool busy, or that
+// is itself a pool worker, runs its loop alone.  The first exception thrown
+// by the loop body is rethrown in the caller.
+namespace {
+thread_local bool t_pool_worker = false;
+
+struct ThreadPool {
+    std::mutex mu, serial;
+    std::condition_variable cv_work, cv_done;
+    uint64_t generation = 0;
+    const std::function<void(size_t)>* job = nullptr;
+    size_t count = 0;
+    std::atomic<size_t> next{0};
+    int busy = 0;
+    int nworkers;
+    std::exception_ptr error;
+
+    explicit ThreadPool(int n) : nworkers(n) {
+        for (int i = 0; i < n; i++) std::thread([this] { run(); }).detach();
+    }
+    void drain(const std::function<void(size_t)>& f, size_t cnt) {
+        for (;;) {
+            const size_t i = next.fetch_add(1);
+            if (i >= cnt) break;
+            try {
+                f(i);
+            } catch (...) {
+                std::lock_guard<std::mutex> lk(mu);
+                if (!error) error = std::current_exception();
+                next = cnt;  // stop handing out work
+            }
+        }
+    }
+    void run() {
+        t_pool_worker = true;
+        uint64_t seen = 0;
+        for (;;) {
+            const std::function<void(size_t)>* f;
+            size_t cnt;
+            {
+                std::unique_lock<std::mutex> lk(mu);
+                cv_work.wait(lk, [&] { return generation != seen; });
+                seen = generation;
+                f = job;
+                cnt = count;
+            }
+            drain(*f, cnt);
+            std::lock_guard<std::mutex> lk(mu);
+            if (--busy == 0) cv_done.notify_all();
+        }
+    }
+    // false when the pool is busy with another caller's job
+    bool parallel(size_t cnt, const std::function<void(size_t)>& f) {
+        std::unique_lock<std::mutex> one(serial, std::try_to_lock);
+        if (!one.owns_lock()) return false;
+        {
+            std::lock_guard<std::mutex> lk(mu);
+            job = &f;
+            count = cnt;
+            next = 0;
+            busy = nworkers;
+            error = nullptr;
+            generation++;
+        }
+        cv_work.notify_all();
+        drain(f, cnt);
+        std::exception_ptr e;
+        {
+            std::unique_lock<std::mutex> lk(mu);
+            cv_done.wait(lk, [&] { return busy == 0; });
+            e = error;
+            error = nullptr;
+        }
+        if (e) std::rethrow_exception(e);
+        return true;
+    }
+};
+
+ThreadPool* pool() {
+    // never destroyed: its workers wait on it until the process ends.  A
+    // forked child has none of the parent's workers and starts its own pool.
+    static std::mutex mu;
+    static ThreadPool* p = nullptr;
+    static pid_t owner = 0;
+    std::lock_guard<std::mutex> lk(mu);
+    if (!p || owner != getpid()) {
+        p = new ThreadPool(std::max(0, default_threads() - 1));
+        owner = getpid();
+    }
+    return p;
+}
+}  // namespace
+
 template <class F>
 static void parallel_for(size_t count, int nthreads, F&& fn) {
     if (count == 0) return;
-    nthreads = (int)std::max<size_t>(1, std::min<size_t>((size_t)nthreads, count));
-    std::atomic<size_t> next{0};
-    auto body = [&]() {
-        for (;;) {
-            size_t i = next.fetch_add(1);
-            if (i >= count) break;
-            fn(i);
-        }
-    };
-    std::vector<std::thread> th;
-    for (int t = 1; t < nthreads; t++) th.emplace_back(body);
-    body();
-    for (auto& t : th) t.join();
+    if (nthreads > 1 && count > 1 && !t_pool_worker) {
+        const std::function<void(size_t)> f = fn;
+        if (pool()->parallel(count, f)) return;
+    }
+    for (size_t i = 0; i < count; i++) fn(i);
 }
 
 // X = sum_{i<m} x_i P^i from balanced 384-bit two's-complement digits (Horner).

@@ -234,11 +234,17 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
     // and gcds (GPU), results to the pinned arrays.
     bool gpu_gcd = false;
     auto gpu_pass = [&]() -> int {
-        BigInt Ti = mod_floor(d, M);
-        for (int i = 0; i < m; i++) {
-            to_words(Ti, &T[(size_t)i * NW], NW);
-            if (i + 1 < m) Ti = mod_floor(mul(Ti, P), M);
-        }
+        // the chain T_{i+1} = T_i P mod M, cut into segments that each start
+        // from P^{i0} d mod M and run in parallel
+        const int nseg = std::max(1, std::min(nthreads, m / 16));
+        parallel_for_each((size_t)nseg, nthreads, [&](size_t sg) {
+            const int i0 = (int)(sg * (size_t)m / nseg), i1 = (int)((sg + 1) * (size_t)m / nseg);
+            BigInt Ti = mod_floor(i0 == 0 ? d : mul(d, pow_u(P, (unsigned)i0)), M);
+            for (int i = i0; i < i1; i++) {
+                to_words(Ti, &T[(size_t)i * NW], NW);
+                if (i + 1 < i1) Ti = mod_floor(mul(Ti, P), M);
+            }
+        });
         lap(tm ? &tm->seeds_ms : nullptr, "seeds");
         const int nwd = (int)((d.bit_length() + 31) / 32);
         gpu_gcd = nwd <= NW && gcd_words_per_lane(std::max(nw, nwd)) != 0;
