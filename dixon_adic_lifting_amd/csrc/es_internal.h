@@ -97,7 +97,7 @@ struct Layout {
     size_t off_piv;       // int32 [53][n + 1]         pivot row per step
     size_t off_rowpos;    // int32 [53][n]             step at which a row pivoted
     size_t off_pend;      // u8 [2][53][pitch]         scaled pivot rows
-    size_t off_GT;        // int8 [53][pitch][64]      old pivot rows of a panel, transposed
+    size_t off_GT;        // int8 [53][pitch][32]      old pivot rows of a panel, transposed
     size_t off_flags;     // int32 [53]                singular mod q_j
     size_t off_rowmax;    // uint64 [n]                max |A_ij| per row
     size_t off_rownorm;   // double [n]                row norms^2 of A

@@ -60,7 +60,7 @@ Layout make_layout(int n, int c) {
     L.off_piv = take(E * (n + 1) * sizeof(int32_t));
     L.off_rowpos = take(E * n * sizeof(int32_t));
     L.off_pend = take(2 * E * (size_t)L.pitch);
-    L.off_GT = take(n <= 4096 ? E * (size_t)L.pitch * 64 : 0);  // blocked elimination only
+    L.off_GT = take(n <= 4096 ? E * (size_t)L.pitch * kPanel : 0);  // blocked elimination only
     L.off_flags = take(E * sizeof(int32_t));
     L.off_rowmax = take((size_t)n * sizeof(uint64_t));
     L.off_rownorm = take((size_t)n * sizeof(double));

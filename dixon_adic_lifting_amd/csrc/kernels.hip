@@ -535,18 +535,122 @@ __device__ __forceinline__ int bal_red16(int x, uint32_t q, uint32_t mq, int off
     return (int)r > (int)(q >> 1) ? (int)r - (int)q : (int)r;
 }
 
-// Panel: one block of 1024 threads per prime; thread t keeps rows t, t + 1024,
-// ... (RPT of them), each as the 32 panel bytes in eight registers, held as
-// residues in [0, q) during the panel.  Each step: block-wide minimum of the
-// candidate rows; the pivot's owner publishes its raw row and q-inverse in
-// LDS; every row then updates itself as base + factor * prow' (mod q), where
-// prow' is the raw pivot row with a 1 in slot kk, base is the row with slot
-// kk cleared (zero for the pivot row itself) and factor is -f pinv (pinv for
-// the pivot row): this is the scaled-pivot-row update with the scaling
-// folded into one factor per row, in the byte-up arithmetic of the step
-// kernel.  Afterwards the panel goes back to S (balanced) and the old pivot
-// rows (all columns) go to GT transposed, [col][c], zero-padded to 64 bytes,
-// the GEMM's operand layout.
+typedef int v4i_t __attribute__((ext_vector_type(4)));
+
+// Panel pieces shared by both panel kernels.  Rows that pivoted in earlier
+// panels (clist[nc .. n)) get S'[i, Kc] = -S[i, Kc] Z, 16 rows per product;
+// first operand Z^T (16 output columns c' per product, k = c), second the
+// rows' panel bytes; each output lane holds one row and four consecutive
+// columns c'.
+__device__ __forceinline__ void panel_old_rows(int8_t* __restrict__ Sj, int n, int pitch, int K, int nc,
+                                               const int* clist, const int8_t (*Zt)[64], uint32_t q, int lane,
+                                               int wave) {
+    const int lr = lane & 15, lg = lane >> 4;
+    // |S Z| < 32 * 125^2 < 2^19: x' = x + q ceil(2^19 / q) lies in (0, 2^20)
+    const uint32_t m28 = (uint32_t)((268435456ull + q - 1) / q);
+    const int off = (int)(q * ((524288u + q - 1) / q));
+    v4i_t za[2];
+#pragma unroll
+    for (int a = 0; a < 2; a++) za[a] = lg < 2 ? *(const v4i_t*)(&Zt[16 * a + lr][16 * lg]) : v4i_t{0, 0, 0, 0};
+    const int nother = n - nc;
+    for (int tile = wave; 16 * tile < nother; tile += 16) {
+        const int k = nc + 16 * tile + lr;
+        const int i = k < n ? clist[k] : -1;
+        const v4i_t sb =
+            (lg < 2 && i >= 0) ? *(const v4i_t*)(Sj + (size_t)i * pitch + K + 16 * lg) : v4i_t{0, 0, 0, 0};
+#pragma unroll
+        for (int a = 0; a < 2; a++) {
+            const v4i_t acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(za[a], sb, v4i_t{0, 0, 0, 0}, 0, 0, 0);
+            uint32_t outw = 0;
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const uint32_t xp = (uint32_t)(off - acc[e]);
+                const uint32_t tq = __umulhi(xp << 4, m28);  // floor(xp / q)
+                const int rr = (int)(xp - tq * q);
+                const int v = rr > (int)(q >> 1) ? rr - (int)q : rr;
+                outw |= ((uint32_t)v & 0xffu) << (8 * e);
+            }
+            if (i >= 0) *(uint32_t*)(Sj + (size_t)i * pitch + K + 16 * a + 4 * lg) = outw;
+        }
+    }
+}
+
+// The panel's pivot rows (all columns) to GT transposed, [col][c] with 32
+// bytes per column (their panel columns are never read): 1024 columns at a
+// time, words read along the rows, bytes regrouped in LDS by column (gts,
+// 32 KB), then one 32-byte row of GT per column.  Every thread of the block
+// takes part (barriers inside).
+__device__ __forceinline__ void panel_gather_gt(const int8_t* __restrict__ Sj, int pitch, int bw,
+                                                const int* plist, uint8_t* gts, int8_t* __restrict__ GTj, int t) {
+    for (int c0 = 0; c0 < pitch; c0 += 1024) {
+        const int ncol = min(1024, pitch - c0);
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+            const int w = t + 1024 * u;  // word w: row c = w / 256, columns 4 (w % 256) .. + 3
+            const int c = w >> 8, cw = w & 255;
+            if (4 * cw >= ncol) continue;
+            const uint32_t v = c < bw ? *(const uint32_t*)(Sj + (size_t)plist[c] * pitch + c0 + 4 * cw) : 0u;
+#pragma unroll
+            for (int bb = 0; bb < 4; bb++) gts[(4 * cw + bb) * kPanel + c] = (uint8_t)(v >> (8 * bb));
+        }
+        __syncthreads();
+        if (t < ncol) {
+            const uint4* src = (const uint4*)(gts + t * kPanel);
+            uint4* dst = (uint4*)(GTj + (size_t)(c0 + t) * kPanel);
+            dst[0] = src[0];
+            dst[1] = src[1];
+        }
+        __syncthreads();
+    }
+}
+
+// The candidate rows (no pivot step yet, rowpos < 0) in row order at
+// clist[0 .. nc), the other rows after them; returns nc.  Every thread of the
+// block takes part (barriers inside).
+__device__ __forceinline__ int panel_list_rows(const int* __restrict__ rpj, int n, int* clist, int* wsum, int t,
+                                               int lane, int wave) {
+    int nc = 0;
+    for (int base = 0; base < n; base += 1024) {
+        const int i = base + t;
+        const bool cand = i < n && rpj[i] < 0;
+        const uint64_t m = __ballot(cand);
+        if (lane == 0) wsum[wave] = __popcll(m);
+        __syncthreads();
+        int before = 0, tot = 0;
+#pragma unroll
+        for (int w = 0; w < 16; w++) {
+            const int v = wsum[w];
+            before += w < wave ? v : 0;
+            tot += v;
+        }
+        const int pos = nc + before + __popcll(m & ((1ull << lane) - 1));
+        if (cand) clist[pos] = i;
+        else if (i < n) clist[n - 1 - (i - pos)] = i;  // the (i - pos)-th other row, listed from the end
+        nc += tot;
+        __syncthreads();
+    }
+    return nc;
+}
+
+// Panel: one block of 1024 threads per prime.  Only the rows that can still
+// become pivots (no pivot step yet, rowpos < 0) take part in the steps: a
+// block-wide prefix sum lists them in row order, and thread t keeps
+// candidates t, t + 1024, ... (RPT of them), each as the 32 panel bytes in
+// eight registers, held as residues in [0, q).  Each step: every wave finds
+// its lowest candidate with a nonzero byte kk and the owner publishes that
+// row in the wave's LDS slot; after one barrier every thread takes the lowest
+// of the sixteen and reads the row from its slot.  Every listed row then
+// updates itself as base + factor * prow' (mod q), where prow' is the raw
+// pivot row with a 1 in slot kk, base is the row with slot kk cleared (zero
+// for the pivot row itself) and factor is -f pinv (pinv for the pivot row):
+// the scaled-pivot-row update with the scaling folded into one factor per
+// row, in the byte-up arithmetic of the step kernel.  After the steps the
+// panel's pivot rows hold Z = S[Pi, Kc]^-1 (row c for the pivot of step c),
+// and every row that pivoted in an earlier panel takes the block form of the
+// same steps, S'[i, Kc] = -S[i, Kc] Z: one int8 product per 16 rows on the
+// matrix cores.  The panel goes back to S (balanced) and the old pivot rows
+// (all columns) go to GT transposed, [col][c] with 32 bytes per column, the
+// update's operand layout.
 template <int RPT>
 __global__ __launch_bounds__(1024) void gj_panel_kernel(int8_t* __restrict__ S, int n, int pitch, int K,
                                                         int* __restrict__ piv, int* __restrict__ rowpos,
@@ -560,16 +664,28 @@ __global__ __launch_bounds__(1024) void gj_panel_kernel(int8_t* __restrict__ S, 
     int8_t* Sj = S + (size_t)j * n * pitch;
     int* rpj = rowpos + (size_t)j * n;
     int* pj = piv + (size_t)j * (n + 1);
-    __shared__ int red[2][16];
-    __shared__ uint32_t prow[2][9];  // raw pivot row (8 words) and pinv
+    __shared__ int clist[1024 * RPT];      // candidate rows in row order, then the other rows
+    __shared__ int wsum[16];
+    __shared__ __attribute__((aligned(16))) uint32_t slot[2][16][8];  // per wave: its best candidate's row
+    __shared__ __attribute__((aligned(16))) int sidx[2][16];          // and that candidate's index
     __shared__ int plist[kPanel];
+    __shared__ __attribute__((aligned(16))) int8_t Zt[kPanel][64];  // Zt[c'][c] = Z[c][c'], zero-padded
+    __shared__ uint8_t inv[256];  // inverses mod q_j
+
+    ((int16_t*)&Zt[0][0])[t] = 0;  // 1024 threads x 2 bytes
+    if (t < 256) inv[t] = c_inv.inv[j][t];
+    const int nc = panel_list_rows(rpj, n, clist, wsum, t, lane, wave);
 
     uint32_t pw[RPT][8];
-    bool used[RPT];
+    bool live[RPT];
+    int pc[RPT];
 #pragma unroll
     for (int r = 0; r < RPT; r++) {
-        const int i = t + 1024 * r;
-        if (i < n) {
+        const int k = t + 1024 * r;
+        live[r] = k < nc;
+        pc[r] = -1;
+        if (live[r]) {
+            const int i = clist[k];
             const uint4 a = *(const uint4*)(Sj + (size_t)i * pitch + K);
             const uint4 b = *(const uint4*)(Sj + (size_t)i * pitch + K + 16);
             const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
@@ -583,11 +699,9 @@ __global__ __launch_bounds__(1024) void gj_panel_kernel(int8_t* __restrict__ S, 
                 }
                 pw[r][e] = o;
             }
-            used[r] = rpj[i] >= 0;
         } else {
 #pragma unroll
             for (int e = 0; e < 8; e++) pw[r][e] = 0;
-            used[r] = true;
         }
     }
     for (int kk = 0; kk < bw; kk++) {
@@ -600,17 +714,34 @@ __global__ __launch_bounds__(1024) void gj_panel_kernel(int8_t* __restrict__ S, 
             for (int e = 1; e < 8; e++) w = kw == e ? pw[r][e] : w;
             fk[r] = (w >> ks) & 0xffu;
         }
-        int cand = INT_MAX;
+        // this wave's lowest candidate with a nonzero byte kk: candidates
+        // t + 1024 r come in order of r, then of lane
+        int best = INT_MAX;
 #pragma unroll
-        for (int r = RPT - 1; r >= 0; r--)
-            if (!used[r] && fk[r] != 0u) cand = t + 1024 * r;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) cand = min(cand, __shfl_xor(cand, o));
-        if (lane == 0) red[buf][wave] = cand;
+        for (int r = 0; r < RPT; r++) {
+            const uint64_t m = __ballot(live[r] && fk[r] != 0u);
+            if (best == INT_MAX && m != 0) {
+                const int wl = __builtin_ctzll(m);
+                best = 64 * wave + wl + 1024 * r;
+                if (lane == wl) {
+                    uint4* dst = (uint4*)&slot[buf][wave][0];
+                    dst[0] = make_uint4(pw[r][0], pw[r][1], pw[r][2], pw[r][3]);
+                    dst[1] = make_uint4(pw[r][4], pw[r][5], pw[r][6], pw[r][7]);
+                }
+            }
+        }
+        if (lane == 0) sidx[buf][wave] = best;
         __syncthreads();
-        int p = red[buf][0];
+        int p = INT_MAX;
+        {
+            const int4* si = (const int4*)&sidx[buf][0];
 #pragma unroll
-        for (int w = 1; w < 16; w++) p = min(p, red[buf][w]);
+            for (int g = 0; g < 4; g++) {
+                const int4 v = si[g];
+                p = min(min(p, v.x), min(v.y, min(v.z, v.w)));
+            }
+        }
+        const int pwv = (p >> 6) & 15;  // candidate t + 1024 r is in wave t / 64
         if (p == INT_MAX) {  // no pivot: singular modulo q_j
             if (t == 0) flags[j] = 1;
             return;
@@ -620,33 +751,42 @@ __global__ __launch_bounds__(1024) void gj_panel_kernel(int8_t* __restrict__ S, 
 #pragma unroll
             for (int r = 0; r < RPT; r++) {
                 if (r != pr) continue;
-#pragma unroll
-                for (int e = 0; e < 8; e++) prow[buf][e] = pw[r][e];
-                prow[buf][8] = c_inv.inv[j][fk[r]];
-                used[r] = true;
+                live[r] = false;
+                pc[r] = kk;
             }
-            pj[K + kk] = p;
-            rpj[p] = K + kk;
-            plist[kk] = p;
+            const int prow_i = clist[p];
+            pj[K + kk] = prow_i;
+            rpj[prow_i] = K + kk;
+            plist[kk] = prow_i;
         }
-        __syncthreads();
         // prow' one byte up, with 1 in slot kk
         uint32_t vs[32];
-#pragma unroll
-        for (int e = 0; e < 8; e++) {
-            const uint32_t w = prow[buf][e];
-#pragma unroll
-            for (int bb = 0; bb < 4; bb++) vs[4 * e + bb] = (4 * e + bb == kk) ? 256u : byte_up(w, bb);
+        uint32_t prw[8];
+        {
+            const uint4* src = (const uint4*)&slot[buf][pwv][0];
+            const uint4 a = src[0], b = src[1];
+            prw[0] = a.x, prw[1] = a.y, prw[2] = a.z, prw[3] = a.w;
+            prw[4] = b.x, prw[5] = b.y, prw[6] = b.z, prw[7] = b.w;
         }
-        const uint32_t pinv = prow[buf][8];
+        uint32_t pkw = prw[0];
+#pragma unroll
+        for (int e = 1; e < 8; e++) pkw = kw == e ? prw[e] : pkw;
+        const uint32_t pinv = inv[(pkw >> ks) & 0xffu];
+        pkw = (pkw & ~(0xffu << ks)) | (1u << ks);  // the 1 in slot kk
+#pragma unroll
+        for (int e = 0; e < 8; e++) prw[e] = kw == e ? pkw : prw[e];
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+#pragma unroll
+            for (int bb = 0; bb < 4; bb++) vs[4 * e + bb] = byte_up(prw[e], bb);
         uint32_t kmask[8];
 #pragma unroll
         for (int e = 0; e < 8; e++) kmask[e] = e == kw ? ~(0xffu << ks) : 0xffffffffu;
 #pragma unroll
         for (int r = 0; r < RPT; r++) {
-            const int i = t + 1024 * r;
-            if (i >= n) continue;
-            const bool isp = i == p;
+            const int k = t + 1024 * r;
+            if (k >= nc) continue;
+            const bool isp = k == p;
             if (!isp && fk[r] == 0u) continue;  // nothing to eliminate in this row
             // factor: -f pinv for other rows, pinv for the pivot row
             const uint32_t g = red_up(__umul24(fk[r], pinv) << 8, mq, nq8) >> 8;
@@ -661,11 +801,12 @@ __global__ __launch_bounds__(1024) void gj_panel_kernel(int8_t* __restrict__ S, 
             }
         }
     }
-    // panel back to S, balanced
+    // listed rows back to S, balanced; the pivot rows' bytes also form Z
 #pragma unroll
     for (int r = 0; r < RPT; r++) {
-        const int i = t + 1024 * r;
-        if (i >= n) continue;
+        const int k = t + 1024 * r;
+        if (k >= nc) continue;
+        const int i = clist[k];
         uint32_t w[8];
 #pragma unroll
         for (int e = 0; e < 8; e++) {
@@ -679,29 +820,184 @@ __global__ __launch_bounds__(1024) void gj_panel_kernel(int8_t* __restrict__ S, 
         }
         *(uint4*)(Sj + (size_t)i * pitch + K) = make_uint4(w[0], w[1], w[2], w[3]);
         *(uint4*)(Sj + (size_t)i * pitch + K + 16) = make_uint4(w[4], w[5], w[6], w[7]);
+        if (pc[r] >= 0) {
+#pragma unroll
+            for (int cc = 0; cc < kPanel; cc++) Zt[cc][pc[r]] = (int8_t)(w[cc >> 2] >> (8 * (cc & 3)));
+        }
     }
     __syncthreads();
-    // old pivot rows, transposed (their panel columns are never read)
-    int8_t* GTj = GT + (size_t)j * pitch * 64;
-    for (int col = t; col < pitch; col += 1024) {
-        uint32_t o[8];
+    panel_old_rows(Sj, n, pitch, K, nc, clist, Zt, q, lane, wave);
+    __syncthreads();
+    __shared__ __attribute__((aligned(16))) uint8_t gts[1024 * kPanel];
+    panel_gather_gt(Sj, pitch, bw, plist, gts, GT + (size_t)j * pitch * kPanel, t);
+}
+
+// The same panel with every candidate row held unpacked: one register per
+// panel byte, in byte-up form (256 x, x in [0, q)), so a step costs three
+// instructions per element (x' = 256 base + fac 256 v, then the exact
+// round-up reduction); the steps are unrolled, so the byte of column kk is a
+// fixed register.  For up to 1024 rows (one row per thread: 32 registers);
+// the byte-packed kernel above covers larger systems.  Same pivots, same
+// results.
+template <int RPT>
+__global__ __launch_bounds__(1024) void gj_panel_up_kernel(int8_t* __restrict__ S, int n, int pitch, int K,
+                                                           int* __restrict__ piv, int* __restrict__ rowpos,
+                                                           int* __restrict__ flags, int8_t* __restrict__ GT) {
+    const int j = blockIdx.x;
+    if (flags[j]) return;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const uint32_t q = c_pt.q[j], mq = c_pt.mq24[j];
+    const int32_t nq8 = -(int32_t)(q << 8);
+    const int bw = kPanel;
+    int8_t* Sj = S + (size_t)j * n * pitch;
+    int* rpj = rowpos + (size_t)j * n;
+    int* pj = piv + (size_t)j * (n + 1);
+    __shared__ int clist[1024 * RPT];
+    __shared__ int wsum[16];
+    __shared__ __attribute__((aligned(16))) uint32_t slot[2][16][8];  // per wave: its best candidate's row
+    __shared__ __attribute__((aligned(16))) int sidx[2][16];          // and that candidate's index
+    __shared__ int plist[kPanel];
+    __shared__ __attribute__((aligned(16))) int8_t Zt[kPanel][64];  // Zt[c'][c] = Z[c][c'], zero-padded
+    __shared__ uint8_t inv[256];
+
+    ((int16_t*)&Zt[0][0])[t] = 0;
+    if (t < 256) inv[t] = c_inv.inv[j][t];
+    const int nc = panel_list_rows(rpj, n, clist, wsum, t, lane, wave);
+
+    uint32_t W[RPT][kPanel];  // 256 x residue
+    bool live[RPT];
+    int pc[RPT];
 #pragma unroll
-        for (int w = 0; w < 8; w++) {
-            uint32_t o4 = 0;
+    for (int r = 0; r < RPT; r++) {
+        const int k = t + 1024 * r;
+        live[r] = k < nc;
+        pc[r] = -1;
+        uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (live[r]) {
+            const int i = clist[k];
+            const uint4 a = *(const uint4*)(Sj + (size_t)i * pitch + K);
+            const uint4 b = *(const uint4*)(Sj + (size_t)i * pitch + K + 16);
+            w[0] = a.x, w[1] = a.y, w[2] = a.z, w[3] = a.w, w[4] = b.x, w[5] = b.y, w[6] = b.z, w[7] = b.w;
+        }
+#pragma unroll
+        for (int c = 0; c < kPanel; c++) {
+            const int x = (int)(int8_t)(w[c >> 2] >> (8 * (c & 3)));
+            W[r][c] = (uint32_t)(x < 0 ? x + (int)q : x) << 8;
+        }
+    }
+    // fully unrolled (a full panel: bw = 32), so that column kk is a fixed
+    // register in every step; a prime found singular runs the remaining steps
+    // without effect and leaves after them
+    bool dead = false;
+#pragma clang loop unroll(full)
+    for (int kk = 0; kk < kPanel; kk++) {
+        const int buf = kk & 1;
+        uint32_t fk[RPT];
+#pragma unroll
+        for (int r = 0; r < RPT; r++) fk[r] = W[r][kk] >> 8;
+        int best = INT_MAX;
+#pragma unroll
+        for (int r = 0; r < RPT; r++) {
+            const uint64_t m = __ballot(live[r] && fk[r] != 0u);
+            if (best == INT_MAX && m != 0) {
+                const int wl = __builtin_ctzll(m);
+                best = 64 * wave + wl + 1024 * r;
+                if (lane == wl) {
+                    uint32_t pk[8];
+#pragma unroll
+                    for (int e = 0; e < 8; e++)
+                        pk[e] = pack_up(W[r][4 * e], W[r][4 * e + 1], W[r][4 * e + 2], W[r][4 * e + 3]);
+                    uint4* dst = (uint4*)&slot[buf][wave][0];
+                    dst[0] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+                    dst[1] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+                }
+            }
+        }
+        if (lane == 0) sidx[buf][wave] = best;
+        __syncthreads();
+        int p = INT_MAX;
+        {
+            const int4* si = (const int4*)&sidx[buf][0];
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+                const int4 v = si[g];
+                p = min(min(p, v.x), min(v.y, min(v.z, v.w)));
+            }
+        }
+        const int pwv = (p >> 6) & 15;  // candidate t + 1024 r is in wave t / 64
+        if (p == INT_MAX) {  // no pivot: singular modulo q_j
+            if (t == 0 && !dead) flags[j] = 1;
+            dead = true;
+        }
+        if (!dead && t == (p & 1023)) {
+            const int pr = p >> 10;
+#pragma unroll
+            for (int r = 0; r < RPT; r++) {
+                if (r != pr) continue;
+                live[r] = false;
+                pc[r] = kk;
+            }
+            const int prow_i = clist[p];
+            pj[K + kk] = prow_i;
+            rpj[prow_i] = K + kk;
+            plist[kk] = prow_i;
+        }
+        // prow' one byte up, with 1 in slot kk
+        uint32_t vs[kPanel];
+        {
+            const uint4* src = (const uint4*)&slot[buf][pwv][0];
+            const uint4 a = src[0], b = src[1];
+            const uint32_t prw[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int c = 0; c < kPanel; c++) vs[c] = byte_up(prw[c >> 2], c & 3);
+        }
+        const uint32_t pinv = dead ? 0u : inv[vs[kk] >> 8];
+        vs[kk] = 256u;
+#pragma unroll
+        for (int r = 0; r < RPT; r++) {
+            // every row without a branch: base (slot kk cleared) + fac prow'
+            // with fac = -f pinv, which leaves a row with f = 0 as it is; the
+            // pivot row equals prow' outside slot kk, so fac = pinv - 1 scales
+            // it by pinv there, and its slot kk is set to pinv
+            const bool isp = t + 1024 * r == p;
+            const uint32_t g = red_up(__umul24(fk[r], pinv) << 8, mq, nq8) >> 8;
+            const uint32_t fac = isp ? pinv - 1u : (g ? q - g : 0u);
+            W[r][kk] = 0u;
+#pragma unroll
+            for (int c = 0; c < kPanel; c++) W[r][c] = red_up(__umul24(fac, vs[c]) + W[r][c], mq, nq8);
+            W[r][kk] = isp ? pinv << 8 : W[r][kk];
+        }
+    }
+    if (dead) return;
+    // listed rows back to S, balanced; the pivot rows' bytes also form Z
+#pragma unroll
+    for (int r = 0; r < RPT; r++) {
+        const int k = t + 1024 * r;
+        if (k >= nc) continue;
+        const int i = clist[k];
+        uint32_t w[8];
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            uint32_t o = 0;
 #pragma unroll
             for (int bb = 0; bb < 4; bb++) {
-                const int c = 4 * w + bb;
-                const uint32_t x = c < bw ? (uint32_t)(uint8_t)Sj[(size_t)plist[c] * pitch + col] : 0u;
-                o4 |= x << (8 * bb);
+                const uint32_t x = W[r][4 * e + bb] >> 8;
+                o |= ((x > (q >> 1) ? x - q : x) & 0xffu) << (8 * bb);
             }
-            o[w] = o4;
+            w[e] = o;
         }
-        uint4* dst = (uint4*)(GTj + (size_t)col * 64);
-        dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-        dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
-        dst[2] = make_uint4(0, 0, 0, 0);
-        dst[3] = make_uint4(0, 0, 0, 0);
+        *(uint4*)(Sj + (size_t)i * pitch + K) = make_uint4(w[0], w[1], w[2], w[3]);
+        *(uint4*)(Sj + (size_t)i * pitch + K + 16) = make_uint4(w[4], w[5], w[6], w[7]);
+        if (pc[r] >= 0) {
+#pragma unroll
+            for (int cc = 0; cc < kPanel; cc++) Zt[cc][pc[r]] = (int8_t)(w[cc >> 2] >> (8 * (cc & 3)));
+        }
     }
+    __syncthreads();
+    panel_old_rows(Sj, n, pitch, K, nc, clist, Zt, q, lane, wave);
+    __syncthreads();
+    __shared__ __attribute__((aligned(16))) uint8_t gts[1024 * kPanel];
+    panel_gather_gt(Sj, pitch, bw, plist, gts, GT + (size_t)j * pitch * kPanel, t);
 }
 
 // Rank-32 update of every column outside the panel, all rows, one tile of
@@ -711,7 +1007,6 @@ __global__ __launch_bounds__(1024) void gj_panel_kernel(int8_t* __restrict__ S, 
 // second, so each output lane holds four consecutive columns of one row:
 // C[i][col] = sum_c S'[i][K + c] S[p_c][col]; then
 // S'[i][col] = [i not pivot] S[i][col] + C, reduced balanced.
-typedef int v4i_t __attribute__((ext_vector_type(4)));
 
 // Orders this wave's LDS writes before its later LDS reads (no cross-wave sync).
 __device__ __forceinline__ void wave_lds_sync() {
@@ -739,14 +1034,14 @@ __global__ __launch_bounds__(256) void gj_update_kernel(int8_t* __restrict__ S, 
     const int off = (int)(q * ((524288u + q - 1) / q));
     int8_t* Sj = S + (size_t)j * n * pitch;
     const int* rpj = rowpos + (size_t)j * n;
-    const int8_t* GTj = GT + (size_t)j * pitch * 64;
+    const int8_t* GTj = GT + (size_t)j * pitch * kPanel;
     uint8_t* st = stage[wave];
     // operands: lanes of group lg supply k in [16 lg, 16 lg + 16); only k < 32 is nonzero
     v4i_t ga[4], pb[4];
 #pragma unroll
     for (int a = 0; a < 4; a++) {
         const int col = col0 + 16 * a + lr;
-        ga[a] = (lg < 2 && col < pitch) ? *(const v4i_t*)(GTj + (size_t)col * 64 + 16 * lg) : v4i_t{0, 0, 0, 0};
+        ga[a] = (lg < 2 && col < pitch) ? *(const v4i_t*)(GTj + (size_t)col * kPanel + 16 * lg) : v4i_t{0, 0, 0, 0};
     }
 #pragma unroll
     for (int b = 0; b < 4; b++) {
@@ -803,7 +1098,10 @@ hipError_t launch_gj_panel(const Layout& L, uint8_t* ws, int K, hipStream_t st) 
     int* rowpos = (int*)(ws + L.off_rowpos);
     int* flags = (int*)(ws + L.off_flags);
     int8_t* GT = (int8_t*)(ws + L.off_GT);
-    if (L.n <= 1024)
+    if (L.n <= 1024 && L.n - K >= kPanel)
+        hipLaunchKernelGGL(gj_panel_up_kernel<1>, dim3(kNumPrimes), dim3(1024), 0, st, S, L.n, L.pitch, K, piv,
+                           rowpos, flags, GT);
+    else if (L.n <= 1024)
         hipLaunchKernelGGL(gj_panel_kernel<1>, dim3(kNumPrimes), dim3(1024), 0, st, S, L.n, L.pitch, K, piv, rowpos,
                            flags, GT);
     else if (L.n <= 2048)
