@@ -158,6 +158,16 @@ bool use_blocked(const Layout& L) {
     return want && blocked_inverse_fits(L);
 }
 
+// The blocked inverse overlaps each panel with the previous panel's update
+// unless ES_LOOKAHEAD=0.
+bool use_lookahead() {
+    static const bool v = [] {
+        const char* e = std::getenv("ES_LOOKAHEAD");
+        return !(e && e[0] == '0');
+    }();
+    return v;
+}
+
 // Residues and the Gauss-Jordan elimination; flags to the host.
 int run_inverse(const int64_t* dA, uint8_t* ws, hipStream_t st, Prep* pr, int* flags, Profiler* prof) {
     const Layout& L = pr->L;
@@ -165,7 +175,15 @@ int run_inverse(const int64_t* dA, uint8_t* ws, hipStream_t st, Prep* pr, int* f
     long ev = prof->start(KC_RESIDUES);
     HIP_CHECK(launch_residues(dA, L, ws, pr->a32, st, blocked));
     prof->stop(ev);
-    if (blocked) {
+    if (blocked && !prof->on && use_lookahead()) {
+        // panel K runs together with the update of panel K - 32 (the columns
+        // the next panel needs are updated first, in the gather launch)
+        for (int K = 0; K < L.n + kPanel; K += kPanel) {
+            HIP_CHECK(launch_gj_panel_rest(L, ws, K, st));
+            if (K < L.n) HIP_CHECK(launch_gj_gather_next(L, ws, K, st));
+        }
+    } else if (blocked) {
+        // one kernel at a time (also the form that per-kernel timing measures)
         for (int K = 0; K < L.n; K += kPanel) {
             ev = prof->start(KC_PANEL);
             HIP_CHECK(launch_gj_panel(L, ws, K, st));

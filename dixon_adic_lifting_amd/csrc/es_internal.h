@@ -133,6 +133,12 @@ constexpr int kPanel = 32;
 bool blocked_inverse_fits(const Layout& L);
 hipError_t launch_gj_panel(const Layout& L, uint8_t* ws, int K, hipStream_t st);
 hipError_t launch_gj_update(const Layout& L, uint8_t* ws, int K, hipStream_t st);
+// lookahead form: panel K together with the update of panel K - 32 outside
+// the columns [K - 32, K + 32) (K = 0: the panel alone; K >= n: the update
+// alone), and after each panel its pivot rows to GT with the update of the
+// next panel's columns
+hipError_t launch_gj_panel_rest(const Layout& L, uint8_t* ws, int K, hipStream_t st);
+hipError_t launch_gj_gather_next(const Layout& L, uint8_t* ws, int K, hipStream_t st);
 hipError_t launch_export_inverse(const Layout& L, const uint8_t* ws, int8_t* B, hipStream_t st);
 hipError_t launch_split_b(const int64_t* b, const Layout& L, uint8_t* ws, int E, hipStream_t st);
 // one lift step = contraction, then Garner (digit into chunk slot `slot`),

@@ -581,7 +581,8 @@ __device__ __forceinline__ void panel_old_rows(int8_t* __restrict__ Sj, int n, i
 // 32 KB), then one 32-byte row of GT per column.  Every thread of the block
 // takes part (barriers inside).
 __device__ __forceinline__ void panel_gather_gt(const int8_t* __restrict__ Sj, int pitch, int bw,
-                                                const int* plist, uint8_t* gts, int8_t* __restrict__ GTj, int t) {
+                                                const int* __restrict__ plist, uint8_t* gts,
+                                                int8_t* __restrict__ GTj, int t) {
     for (int c0 = 0; c0 < pitch; c0 += 1024) {
         const int ncol = min(1024, pitch - c0);
 #pragma unroll
@@ -651,12 +652,13 @@ __device__ __forceinline__ int panel_list_rows(const int* __restrict__ rpj, int 
 // matrix cores.  The panel goes back to S (balanced) and the old pivot rows
 // (all columns) go to GT transposed, [col][c] with 32 bytes per column, the
 // update's operand layout.
+// (The bodies below run the panel of prime j in the calling block and return
+// false when the prime is, or turns out to be, singular.)
 template <int RPT>
-__global__ __launch_bounds__(1024) void gj_panel_kernel(int8_t* __restrict__ S, int n, int pitch, int K,
-                                                        int* __restrict__ piv, int* __restrict__ rowpos,
-                                                        int* __restrict__ flags, int8_t* __restrict__ GT) {
-    const int j = blockIdx.x;
-    if (flags[j]) return;
+__device__ __forceinline__ bool panel_packed_body(int8_t* __restrict__ S, int n, int pitch, int K,
+                                                  int* __restrict__ piv, int* __restrict__ rowpos,
+                                                  int* __restrict__ flags, int j) {
+    if (flags[j]) return false;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const uint32_t q = c_pt.q[j], mq = c_pt.mq24[j];
     const int32_t nq8 = -(int32_t)(q << 8);
@@ -744,7 +746,7 @@ __global__ __launch_bounds__(1024) void gj_panel_kernel(int8_t* __restrict__ S, 
         const int pwv = (p >> 6) & 15;  // candidate t + 1024 r is in wave t / 64
         if (p == INT_MAX) {  // no pivot: singular modulo q_j
             if (t == 0) flags[j] = 1;
-            return;
+            return false;
         }
         if (t == (p & 1023)) {
             const int pr = p >> 10;
@@ -827,9 +829,7 @@ __global__ __launch_bounds__(1024) void gj_panel_kernel(int8_t* __restrict__ S, 
     }
     __syncthreads();
     panel_old_rows(Sj, n, pitch, K, nc, clist, Zt, q, lane, wave);
-    __syncthreads();
-    __shared__ __attribute__((aligned(16))) uint8_t gts[1024 * kPanel];
-    panel_gather_gt(Sj, pitch, bw, plist, gts, GT + (size_t)j * pitch * kPanel, t);
+    return true;
 }
 
 // The same panel with every candidate row held unpacked: one register per
@@ -840,11 +840,10 @@ __global__ __launch_bounds__(1024) void gj_panel_kernel(int8_t* __restrict__ S, 
 // the byte-packed kernel above covers larger systems.  Same pivots, same
 // results.
 template <int RPT>
-__global__ __launch_bounds__(1024) void gj_panel_up_kernel(int8_t* __restrict__ S, int n, int pitch, int K,
-                                                           int* __restrict__ piv, int* __restrict__ rowpos,
-                                                           int* __restrict__ flags, int8_t* __restrict__ GT) {
-    const int j = blockIdx.x;
-    if (flags[j]) return;
+__device__ __forceinline__ bool panel_up_body(int8_t* __restrict__ S, int n, int pitch, int K,
+                                              int* __restrict__ piv, int* __restrict__ rowpos,
+                                              int* __restrict__ flags, int j) {
+    if (flags[j]) return false;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const uint32_t q = c_pt.q[j], mq = c_pt.mq24[j];
     const int32_t nq8 = -(int32_t)(q << 8);
@@ -968,7 +967,7 @@ __global__ __launch_bounds__(1024) void gj_panel_up_kernel(int8_t* __restrict__ 
             W[r][kk] = isp ? pinv << 8 : W[r][kk];
         }
     }
-    if (dead) return;
+    if (dead) return false;
     // listed rows back to S, balanced; the pivot rows' bytes also form Z
 #pragma unroll
     for (int r = 0; r < RPT; r++) {
@@ -995,18 +994,18 @@ __global__ __launch_bounds__(1024) void gj_panel_up_kernel(int8_t* __restrict__ 
     }
     __syncthreads();
     panel_old_rows(Sj, n, pitch, K, nc, clist, Zt, q, lane, wave);
-    __syncthreads();
-    __shared__ __attribute__((aligned(16))) uint8_t gts[1024 * kPanel];
-    panel_gather_gt(Sj, pitch, bw, plist, gts, GT + (size_t)j * pitch * kPanel, t);
+    return true;
 }
 
-// Rank-32 update of every column outside the panel, all rows, one tile of
-// 128 columns x 128 rows per block, grid (column tiles, row tiles, primes).
-// v_mfma_i32_16x16x64_i8 with the old pivot rows (GT, [col][c]) as the first
-// operand and the new panel (S[i][K .. K + 32), zero beyond 32) as the
-// second, so each output lane holds four consecutive columns of one row:
+// Rank-32 update of the columns outside the panel, all rows, one tile of
+// 128 columns x 128 rows per four waves.  v_mfma_i32_16x16x64_i8 with the
+// old pivot rows (GT, [col][c]) as the first operand and the new panel
+// (S[i][K .. K + 32), zero beyond 32) as the second, so each output lane
+// holds four consecutive columns of one row:
 // C[i][col] = sum_c S'[i][K + c] S[p_c][col]; then
-// S'[i][col] = [i not pivot] S[i][col] + C, reduced balanced.
+// S'[i][col] = [i not pivot] S[i][col] + C, reduced balanced.  The columns
+// in [skip0, skip1) (a multiple of 16 wide, holding the panel) are neither
+// changed nor written.
 
 // Orders this wave's LDS writes before its later LDS reads (no cross-wave sync).
 __device__ __forceinline__ void wave_lds_sync() {
@@ -1015,18 +1014,18 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__global__ __launch_bounds__(256) void gj_update_kernel(int8_t* __restrict__ S, int n, int pitch, int K,
-                                                        const int* __restrict__ rowpos,
-                                                        const int* __restrict__ flags,
-                                                        const int8_t* __restrict__ GT) {
-    constexpr int LS = 80;  // LDS row stride, bytes (16-byte aligned, conflict-free for 4-byte access)
-    __shared__ __attribute__((aligned(16))) uint8_t stage[4][64 * LS];
-    const int j = blockIdx.z;
-    if (flags[j]) return;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+constexpr int kUpdLS = 80;  // LDS row stride of the update staging, bytes (16-byte aligned,
+                            // conflict-free for 4-byte access)
+
+// One wave's 64 x 64 part (w4 = 0..3 within the four waves of the tile).
+__device__ __forceinline__ void update_tile(int8_t* __restrict__ S, int n, int pitch, int K,
+                                            const int* __restrict__ rowpos, const int8_t* __restrict__ GT,
+                                            int j, int tx, int ty, int w4, int lane, uint8_t* st, int skip0,
+                                            int skip1) {
     const int lr = lane & 15, lg = lane >> 4;
-    const int col0 = blockIdx.x * 128 + (wave & 1) * 64;  // this wave's 64 columns
-    const int row0 = blockIdx.y * 128 + (wave >> 1) * 64; // and 64 rows
+    const int col0 = tx * 128 + (w4 & 1) * 64;  // this wave's 64 columns
+    const int row0 = ty * 128 + (w4 >> 1) * 64; // and 64 rows
+    if (col0 >= pitch || row0 >= n || (col0 >= skip0 && col0 + 64 <= skip1)) return;  // wave-uniform
     const uint32_t q = c_pt.q[j];
     // |x| < 32 * 125^2 + 125 < 2^19: x' = x + q ceil(2^19 / q) lies in (0, 2^20), where
     // ceil(2^28 / q) is an exact round-up reciprocal (20 + 8 bits of precision)
@@ -1035,27 +1034,28 @@ __global__ __launch_bounds__(256) void gj_update_kernel(int8_t* __restrict__ S, 
     int8_t* Sj = S + (size_t)j * n * pitch;
     const int* rpj = rowpos + (size_t)j * n;
     const int8_t* GTj = GT + (size_t)j * pitch * kPanel;
-    uint8_t* st = stage[wave];
     // operands: lanes of group lg supply k in [16 lg, 16 lg + 16); only k < 32 is nonzero
     v4i_t ga[4], pb[4];
 #pragma unroll
     for (int a = 0; a < 4; a++) {
         const int col = col0 + 16 * a + lr;
-        ga[a] = (lg < 2 && col < pitch) ? *(const v4i_t*)(GTj + (size_t)col * kPanel + 16 * lg) : v4i_t{0, 0, 0, 0};
+        ga[a] = lg < 2 ? *(const v4i_t*)(GTj + (size_t)col * kPanel + 16 * lg) : v4i_t{0, 0, 0, 0};
     }
 #pragma unroll
     for (int b = 0; b < 4; b++) {
         const int i = row0 + 16 * b + lr;
         pb[b] = (lg < 2 && i < n) ? *(const v4i_t*)(Sj + (size_t)i * pitch + K + 16 * lg) : v4i_t{0, 0, 0, 0};
     }
-    const bool colblock = col0 < pitch;  // the wave's 64 columns exist (pitch is a multiple of 64)
+    // this lane's 16 columns col0 + 16 lg .. are written unless they lie in the skipped range
+    const int mycol = col0 + 16 * lg;
+    const bool wr = !(mycol >= skip0 && mycol < skip1);
 #pragma unroll
     for (int b = 0; b < 4; b++) {
         // old S for rows row0 + 16 b + lr, 16 columns per lane, through LDS
         const int i = row0 + 16 * b + lr;
-        const bool rowok = i < n && colblock;
-        const uint4 old16 = rowok ? *(const uint4*)(Sj + (size_t)i * pitch + col0 + 16 * lg) : make_uint4(0, 0, 0, 0);
-        *(uint4*)(st + lr * LS + 16 * lg) = old16;
+        const bool rowok = i < n;
+        const uint4 old16 = rowok ? *(const uint4*)(Sj + (size_t)i * pitch + mycol) : make_uint4(0, 0, 0, 0);
+        *(uint4*)(st + lr * kUpdLS + 16 * lg) = old16;
         const int rp = rowok ? rpj[i] : 0;
         const bool pivot_row = rp >= K && rp < K + kPanel;
         wave_lds_sync();
@@ -1063,34 +1063,143 @@ __global__ __launch_bounds__(256) void gj_update_kernel(int8_t* __restrict__ S, 
 #pragma unroll
         for (int a = 0; a < 4; a++) {
             const v4i_t acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(ga[a], pb[b], v4i_t{0, 0, 0, 0}, 0, 0, 0);
-            const int c4 = col0 + 16 * a + 4 * lg;
-            const uint32_t old = *(const uint32_t*)(st + lr * LS + 16 * a + 4 * lg);
+            const uint32_t old = *(const uint32_t*)(st + lr * kUpdLS + 16 * a + 4 * lg);
             uint32_t outw = 0;
 #pragma unroll
             for (int e = 0; e < 4; e++) {
-                const int col = c4 + e;
                 const int so = (int)(int8_t)(old >> (8 * e));
-                int v;
-                if (col >= K && col < K + kPanel) {
-                    v = so;  // panel column: keeps the panel's value
-                } else {
-                    const int x = (pivot_row ? 0 : so) + acc[e];
-                    const uint32_t xp = (uint32_t)(x + off);
-                    const uint32_t tq = __umulhi(xp << 4, m28);  // floor(xp / q)
-                    const int r = (int)(xp - tq * q);
-                    v = r > (int)(q >> 1) ? r - (int)q : r;
-                }
+                const int x = (pivot_row ? 0 : so) + acc[e];
+                const uint32_t xp = (uint32_t)(x + off);
+                const uint32_t tq = __umulhi(xp << 4, m28);  // floor(xp / q)
+                const int r = (int)(xp - tq * q);
+                const int v = r > (int)(q >> 1) ? r - (int)q : r;
                 outw |= ((uint32_t)v & 0xffu) << (8 * e);
             }
-            *(uint32_t*)(st + lr * LS + 16 * a + 4 * lg) = outw;
+            *(uint32_t*)(st + lr * kUpdLS + 16 * a + 4 * lg) = outw;
         }
         wave_lds_sync();
-        if (rowok) *(uint4*)(Sj + (size_t)i * pitch + col0 + 16 * lg) = *(const uint4*)(st + lr * LS + 16 * lg);
+        if (rowok && wr) *(uint4*)(Sj + (size_t)i * pitch + mycol) = *(const uint4*)(st + lr * kUpdLS + 16 * lg);
         wave_lds_sync();
     }
 }
 
+// Every column but the panel's [K, K + 32) (or the wider skipped range),
+// grid (column tiles, row tiles, primes).
+__global__ __launch_bounds__(256) void gj_update_kernel(int8_t* __restrict__ S, int n, int pitch, int K,
+                                                        const int* __restrict__ rowpos,
+                                                        const int* __restrict__ flags,
+                                                        const int8_t* __restrict__ GT, int skip1) {
+    __shared__ __attribute__((aligned(16))) uint8_t stage[4][64 * kUpdLS];
+    const int j = blockIdx.z;
+    if (flags[j]) return;
+    const int wave = threadIdx.x >> 6;
+    update_tile(S, n, pitch, K, rowpos, GT, j, blockIdx.x, blockIdx.y, wave, threadIdx.x & 63, stage[wave], K,
+                skip1);
+}
+
+// Panel K on its own (no other work in flight), then its pivot rows to GT.
+template <int RPT, bool UP>
+__global__ __launch_bounds__(1024) void gj_panel_kernel(int8_t* __restrict__ S, int n, int pitch, int K,
+                                                        int* __restrict__ piv, int* __restrict__ rowpos,
+                                                        int* __restrict__ flags, int8_t* __restrict__ GT) {
+    const int j = blockIdx.x;
+    const bool ok = UP ? panel_up_body<RPT>(S, n, pitch, K, piv, rowpos, flags, j)
+                       : panel_packed_body<RPT>(S, n, pitch, K, piv, rowpos, flags, j);
+    if (!ok) return;  // the whole block
+    __syncthreads();
+    __shared__ __attribute__((aligned(16))) uint8_t gts[1024 * kPanel];
+    panel_gather_gt(S + (size_t)j * n * pitch, pitch, min(kPanel, n - K), piv + (size_t)j * (n + 1) + K, gts,
+                    GT + (size_t)j * pitch * kPanel, threadIdx.x);
+}
+
+// Lookahead form: panel K (blocks 0 .. 52, one per prime) and, in the same
+// launch, the update of panel K - 32 on every column outside
+// [K - 32, K + 32) (the blocks after them, four 128 x 128 tiles each).  The
+// two touch disjoint columns; panel K's columns were updated beforehand by
+// gj_gather_next_kernel.  The panel blocks come first, so they are placed
+// first.  K >= n: the update part only.
+template <int RPT, bool UP>
+__global__ __launch_bounds__(1024) void gj_panel_rest_kernel(int8_t* __restrict__ S, int n, int pitch, int K,
+                                                             int* __restrict__ piv, int* __restrict__ rowpos,
+                                                             int* __restrict__ flags, const int8_t* __restrict__ GT,
+                                                             int ntx, int nty) {
+    const int np = K < n ? kNumPrimes : 0;
+    if ((int)blockIdx.x < np) {
+        if (UP) (void)panel_up_body<RPT>(S, n, pitch, K, piv, rowpos, flags, blockIdx.x);
+        else (void)panel_packed_body<RPT>(S, n, pitch, K, piv, rowpos, flags, blockIdx.x);
+        return;
+    }
+    __shared__ __attribute__((aligned(16))) uint8_t stage[16][64 * kUpdLS];
+    const int wave = threadIdx.x >> 6;
+    const int tile = 4 * ((int)blockIdx.x - np) + (wave >> 2);
+    const int j = tile / (ntx * nty), rem = tile % (ntx * nty);
+    if (j >= kNumPrimes || flags[j]) return;
+    const int Kr = K - kPanel;
+    update_tile(S, n, pitch, Kr, rowpos, GT, j, rem % ntx, rem / ntx, wave & 3, threadIdx.x & 63, stage[wave], Kr,
+                Kr + 2 * kPanel);
+}
+
+// After panel K: its pivot rows to GT (all columns), then, when K + 32 < n,
+// the update of the next panel's columns [K + 32, K + 64) on every row, one
+// block per prime (16 row tiles of 16 per wave, two 16-column halves).
+__global__ __launch_bounds__(1024) void gj_gather_next_kernel(int8_t* __restrict__ S, int n, int pitch, int K,
+                                                              const int* __restrict__ piv,
+                                                              const int* __restrict__ rowpos,
+                                                              const int* __restrict__ flags,
+                                                              int8_t* __restrict__ GT) {
+    const int j = blockIdx.x;
+    if (flags[j]) return;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    int8_t* Sj = S + (size_t)j * n * pitch;
+    int8_t* GTj = GT + (size_t)j * pitch * kPanel;
+    __shared__ __attribute__((aligned(16))) uint8_t gts[1024 * kPanel];
+    panel_gather_gt(Sj, pitch, min(kPanel, n - K), piv + (size_t)j * (n + 1) + K, gts, GTj, t);
+    if (K + kPanel >= n) return;
+    // the block's own GT writes are visible after the barriers in the gather
+    const int lr = lane & 15, lg = lane >> 4;
+    const uint32_t q = c_pt.q[j];
+    const uint32_t m28 = (uint32_t)((268435456ull + q - 1) / q);
+    const int off = (int)(q * ((524288u + q - 1) / q));
+    const int* rpj = rowpos + (size_t)j * n;
+    const int c0 = K + kPanel;
+    v4i_t ga[2];
+#pragma unroll
+    for (int a = 0; a < 2; a++)
+        ga[a] = lg < 2 ? *(const v4i_t*)(GTj + (size_t)(c0 + 16 * a + lr) * kPanel + 16 * lg) : v4i_t{0, 0, 0, 0};
+    for (int tr = wave; 16 * tr < n; tr += 16) {
+        const int i = 16 * tr + lr;
+        const bool rowok = i < n;
+        const v4i_t pb = (lg < 2 && rowok) ? *(const v4i_t*)(Sj + (size_t)i * pitch + K + 16 * lg) : v4i_t{0, 0, 0, 0};
+        const int rp = rowok ? rpj[i] : 0;
+        const bool pivot_row = rp >= K && rp < K + kPanel;
+#pragma unroll
+        for (int a = 0; a < 2; a++) {
+            const v4i_t acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(ga[a], pb, v4i_t{0, 0, 0, 0}, 0, 0, 0);
+            const int col = c0 + 16 * a + 4 * lg;
+            const uint32_t old = rowok ? *(const uint32_t*)(Sj + (size_t)i * pitch + col) : 0u;
+            uint32_t outw = 0;
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int so = (int)(int8_t)(old >> (8 * e));
+                const int x = (pivot_row ? 0 : so) + acc[e];
+                const uint32_t xp = (uint32_t)(x + off);
+                const uint32_t tq = __umulhi(xp << 4, m28);
+                const int r = (int)(xp - tq * q);
+                const int v = r > (int)(q >> 1) ? r - (int)q : r;
+                outw |= ((uint32_t)v & 0xffu) << (8 * e);
+            }
+            if (rowok) *(uint32_t*)(Sj + (size_t)i * pitch + col) = outw;
+        }
+    }
+}
+
 bool blocked_inverse_fits(const Layout& L) { return L.n <= 4096 && (L.pitch % 64) == 0; }
+
+// the panel variant for panel K: unpacked for full panels of up to 1024 rows
+static int panel_kind(const Layout& L, int K) {
+    if (L.n <= 1024) return L.n - K >= kPanel ? 0 : 1;
+    return L.n <= 2048 ? 2 : 4;
+}
 
 hipError_t launch_gj_panel(const Layout& L, uint8_t* ws, int K, hipStream_t st) {
     int8_t* S = (int8_t*)(ws + L.off_S);
@@ -1098,18 +1207,13 @@ hipError_t launch_gj_panel(const Layout& L, uint8_t* ws, int K, hipStream_t st) 
     int* rowpos = (int*)(ws + L.off_rowpos);
     int* flags = (int*)(ws + L.off_flags);
     int8_t* GT = (int8_t*)(ws + L.off_GT);
-    if (L.n <= 1024 && L.n - K >= kPanel)
-        hipLaunchKernelGGL(gj_panel_up_kernel<1>, dim3(kNumPrimes), dim3(1024), 0, st, S, L.n, L.pitch, K, piv,
-                           rowpos, flags, GT);
-    else if (L.n <= 1024)
-        hipLaunchKernelGGL(gj_panel_kernel<1>, dim3(kNumPrimes), dim3(1024), 0, st, S, L.n, L.pitch, K, piv, rowpos,
-                           flags, GT);
-    else if (L.n <= 2048)
-        hipLaunchKernelGGL(gj_panel_kernel<2>, dim3(kNumPrimes), dim3(1024), 0, st, S, L.n, L.pitch, K, piv, rowpos,
-                           flags, GT);
-    else
-        hipLaunchKernelGGL(gj_panel_kernel<4>, dim3(kNumPrimes), dim3(1024), 0, st, S, L.n, L.pitch, K, piv, rowpos,
-                           flags, GT);
+    const dim3 g(kNumPrimes), b(1024);
+    switch (panel_kind(L, K)) {
+        case 0: hipLaunchKernelGGL((gj_panel_kernel<1, true>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT); break;
+        case 1: hipLaunchKernelGGL((gj_panel_kernel<1, false>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT); break;
+        case 2: hipLaunchKernelGGL((gj_panel_kernel<2, false>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT); break;
+        default: hipLaunchKernelGGL((gj_panel_kernel<4, false>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT); break;
+    }
     return hipGetLastError();
 }
 
@@ -1117,7 +1221,34 @@ hipError_t launch_gj_update(const Layout& L, uint8_t* ws, int K, hipStream_t st)
     dim3 grid((L.pitch + 127) / 128, (L.n + 127) / 128, kNumPrimes);
     hipLaunchKernelGGL(gj_update_kernel, grid, dim3(256), 0, st, (int8_t*)(ws + L.off_S), L.n, L.pitch, K,
                        (const int*)(ws + L.off_rowpos), (const int*)(ws + L.off_flags),
-                       (const int8_t*)(ws + L.off_GT));
+                       (const int8_t*)(ws + L.off_GT), K + kPanel);
+    return hipGetLastError();
+}
+
+hipError_t launch_gj_panel_rest(const Layout& L, uint8_t* ws, int K, hipStream_t st) {
+    int8_t* S = (int8_t*)(ws + L.off_S);
+    int* piv = (int*)(ws + L.off_piv);
+    int* rowpos = (int*)(ws + L.off_rowpos);
+    int* flags = (int*)(ws + L.off_flags);
+    const int8_t* GT = (const int8_t*)(ws + L.off_GT);
+    const int ntx = (L.pitch + 127) / 128, nty = (L.n + 127) / 128;
+    const int nupd = K > 0 ? (ntx * nty * kNumPrimes + 3) / 4 : 0;
+    const int np = K < L.n ? kNumPrimes : 0;
+    const dim3 g(np + nupd), b(1024);
+    if (np + nupd == 0) return hipSuccess;
+    switch (K < L.n ? panel_kind(L, K) : 1) {
+        case 0: hipLaunchKernelGGL((gj_panel_rest_kernel<1, true>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT, ntx, nty); break;
+        case 1: hipLaunchKernelGGL((gj_panel_rest_kernel<1, false>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT, ntx, nty); break;
+        case 2: hipLaunchKernelGGL((gj_panel_rest_kernel<2, false>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT, ntx, nty); break;
+        default: hipLaunchKernelGGL((gj_panel_rest_kernel<4, false>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT, ntx, nty); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gj_gather_next(const Layout& L, uint8_t* ws, int K, hipStream_t st) {
+    hipLaunchKernelGGL(gj_gather_next_kernel, dim3(kNumPrimes), dim3(1024), 0, st, (int8_t*)(ws + L.off_S), L.n,
+                       L.pitch, K, (const int*)(ws + L.off_piv), (const int*)(ws + L.off_rowpos),
+                       (const int*)(ws + L.off_flags), (int8_t*)(ws + L.off_GT));
     return hipGetLastError();
 }
 

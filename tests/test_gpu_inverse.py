@@ -135,15 +135,26 @@ def test_inverse_ragged_two_passes(primes):
 
 
 def both_inverses(A):
-    """(B, flags) from the blocked elimination and from one launch per step."""
+    """(B, flags) from the blocked elimination and from one launch per step.
+    The blocked form runs twice: with each panel overlapping the previous
+    panel's update (the default), and one kernel at a time (the form used
+    while kernels are timed); the two must agree exactly."""
     from dixon_adic_lifting_amd import _lib
     dA = torch.as_tensor(A).cuda()
     try:
         _lib.set_blocked_inverse(True)
         Bb, fb = es.batched_inverse(dA)
+        _lib.set_profiling(True)
+        Bp, fp = es.batched_inverse(dA)
+        _lib.set_profiling(False)
+        assert fp == fb
+        for j in range(53):
+            if not fb[j]:
+                assert torch.equal(Bb[j], Bp[j]), j
         _lib.set_blocked_inverse(False)
         Bs, fs = es.batched_inverse(dA)
     finally:
+        _lib.set_profiling(False)
         _lib.set_blocked_inverse(True)
     return Bb, fb, Bs, fs
 
