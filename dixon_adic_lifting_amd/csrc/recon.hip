@@ -244,7 +244,7 @@ __global__ __launch_bounds__(256) void recon_gemm_kernel(const int8_t* __restric
 }
 
 // ---------------------------------------------------------------- lowest terms
-// g_j = gcd(|y_j|, d) for every accepted component, one wave per component,
+// g_j = gcd(|y_j|, d) for every accepted component, two waves per component,
 // by Lehmer's method on numbers held as signed radix-2^30 limbs,
 // sum_k l_k 2^(30 k) with every |l_k| < 0.58 2^30; limb k sits in lane
 // k % 64, slot k / 64, so a number's limbs fill the low slots and the work of
@@ -266,6 +266,17 @@ __global__ __launch_bounds__(256) void recon_gemm_kernel(const int8_t* __restric
 // component to the host.  Once both numbers fit in four limbs they are read
 // out exactly and finished by the binary gcd.  Results: gstat 0 and G = g
 // when g fits 64 bits, else gstat 1 (the host finishes that component).
+//
+// The two waves of a component overlap the two halves of a round: wave 1
+// holds the limbs and applies each round's matrix; wave 0 runs the
+// Euclidean steps of the next round meanwhile.  A matrix changes limb k
+// using limbs k and k - 1 only, so the six limbs h - 4 .. h + 1 around the
+// top h, which wave 1 hands over after every apply, give wave 0 the exact
+// limbs h - 3 .. h + 2 after the next matrix (one lane per limb): enough for
+// the next leading parts.  (When the top falls too far for that window, or
+// the numbers reach the last four limbs, wave 0 issues the identity once and
+// reads a fresh window.)  One barrier per round; matrices, commands and
+// windows are double-buffered in LDS.
 
 // lane l <- lane l - 1, lane 0 <- lane 63
 __device__ __forceinline__ int32_t wave_ror1(int32_t v) {
@@ -280,15 +291,18 @@ __device__ __forceinline__ int32_t chunk30(const uint32_t* __restrict__ W, int n
     return (int32_t)(__builtin_amdgcn_alignbit(hi, lo, o) & 0x3fffffffu);
 }
 
-// (a, b) <- (A a + B b, C a + D b) over slots [0, ns); limbs above the live
-// ones are zero and stay zero
+// (a, b) <- (A a + B b, C a + D b) over slots [s0, ns), the high parts
+// entering slot s0 from slot s0 - 1 given (pa0, pb0, held by lane 0); the
+// high parts leaving slot ns - 1 are dropped (limbs above the live ones are
+// zero and stay zero)
 template <int CW>
 __device__ __forceinline__ void limb_apply(int32_t (&a)[CW], int32_t (&b)[CW], int32_t A, int32_t B, int32_t C,
-                                           int32_t D, int ns, bool lane0) {
-    int32_t pa = 0, pb = 0;  // high parts of the slot below, rotated one lane up
+                                           int32_t D, int ns, bool lane0, int s0 = 0, int32_t pa0 = 0,
+                                           int32_t pb0 = 0) {
+    int32_t pa = pa0, pb = pb0;  // high parts of the slot below, rotated one lane up
 #pragma unroll
     for (int c = 0; c < CW; c++) {
-        if (c >= ns) continue;
+        if (c < s0 || c >= ns) continue;
         // w = v + 2^29: high part floor(w / 2^30), low part (w mod 2^30) - 2^29
         const int64_t wa = (int64_t)A * a[c] + ((int64_t)B * b[c] + (1 << 29));
         const int64_t wb = (int64_t)C * a[c] + ((int64_t)D * b[c] + (1 << 29));
@@ -301,6 +315,19 @@ __device__ __forceinline__ void limb_apply(int32_t (&a)[CW], int32_t (&b)[CW], i
         pa = ra;
         pb = rb;
     }
+}
+
+// The high parts that slot c - 1 (c >= 1) passes into slot c under
+// [A B; C D], rotated so that lane 0 holds them (the values limb_apply's
+// first slot takes as pa0, pb0)
+template <int CW>
+__device__ __forceinline__ void limb_carry_into(const int32_t (&a)[CW], const int32_t (&b)[CW], int32_t A, int32_t B,
+                                               int32_t C, int32_t D, int c, int32_t* pa, int32_t* pb) {
+    const int32_t x = a[c - 1], y = b[c - 1];
+    const int64_t wa = (int64_t)A * x + ((int64_t)B * y + (1 << 29));
+    const int64_t wb = (int64_t)C * x + ((int64_t)D * y + (1 << 29));
+    *pa = wave_ror1((int32_t)__builtin_amdgcn_alignbit((uint32_t)((uint64_t)wa >> 32), (uint32_t)wa, 30));
+    *pb = wave_ror1((int32_t)__builtin_amdgcn_alignbit((uint32_t)((uint64_t)wb >> 32), (uint32_t)wb, 30));
 }
 
 // R <- -R over slots [0, ns)
@@ -323,17 +350,7 @@ __device__ __forceinline__ int top_limb(const int32_t (&a)[CW], const int32_t (&
     return -1;
 }
 
-// limbs k, k - 1, k - 2 of R (k >= 2) as l_k 2^60 + l_{k-1} 2^30 + l_{k-2}
-template <int CW>
-__device__ __forceinline__ double lead3(const int32_t (&R)[CW], int k) {
-    const int s = k >> 6, i = k & 63;
-    const int32_t v0 = R[s];
-    const int32_t v1 = s > 0 ? R[s - 1] : 0;
-    const int32_t l2 = __builtin_amdgcn_readlane(v0, i);
-    const int32_t l1 = i >= 1 ? __builtin_amdgcn_readlane(v0, i - 1) : __builtin_amdgcn_readlane(v1, 63);
-    const int32_t l0 = i >= 2 ? __builtin_amdgcn_readlane(v0, i - 2) : __builtin_amdgcn_readlane(v1, 62 + i);
-    return fma(fma((double)l2, 0x1p30, (double)l1), 0x1p30, (double)l0);
-}
+constexpr int kGcdSeg = 6;  // limbs handed from the limb wave to the Euclid wave
 
 // One Euclidean step on (x, y) with cofactors (A, B; C, D).  The hardware
 // reciprocal r0 is good to about 2^-24; one Newton correction gives x / y
@@ -360,45 +377,111 @@ __device__ __forceinline__ bool euclid_step(double x, double y, double A, double
 }
 
 template <int CW>
-__global__ __launch_bounds__(256) void gcd_kernel(const uint32_t* __restrict__ Y, int nw,
+__global__ __launch_bounds__(128) void gcd_kernel(const uint32_t* __restrict__ Y, int nw,
                                                   const int* __restrict__ status, int valid_rows,
                                                   const uint32_t* __restrict__ Dw, int nwd,
                                                   uint64_t* __restrict__ G, int* __restrict__ gstat) {
-    const int lane = threadIdx.x & 63;
-    const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int j = blockIdx.x;
     if (j >= valid_rows) return;
     if (status[j] >= 2) {
-        if (lane == 0) gstat[j] = 1;
+        if (threadIdx.x == 0) gstat[j] = 1;
         return;
     }
+    const int lane = threadIdx.x & 63;
     const bool lane0 = lane == 0;
-    // a = d, b = y: 30-bit chunks of the two's-complement words (y's sign
-    // extended through every limb), then one split pass makes them signed
-    // limbs; the carry dropped off the top limb removes the extension
-    const uint32_t ext = status[j] == 1 ? 0xffffffffu : 0u;
-    const uint32_t* yj = Y + (size_t)j * nw;
-    int32_t a[CW], b[CW];
+    __shared__ int32_t sM[2][4];             // the round's matrix [A B; C D]
+    __shared__ int sCmd[2];                  // 0: apply it, 1: stop
+    __shared__ int32_t sSeg[2][2][kGcdSeg];  // limbs h - 4 .. h + 1 of a and b
+    __shared__ int sTop[2];                  // h
+    const int max_rounds = (32 * (nw > nwd ? nw : nwd)) / 12 + 64;
+
+    if (threadIdx.x >= 64) {
+        // ---- limb wave: a = d, b = y as 30-bit chunks of the two's-complement
+        // words (y's sign extended through every limb), then one split pass
+        // makes them signed limbs; the carry dropped off the top limb removes
+        // the extension
+        const uint32_t ext = status[j] == 1 ? 0xffffffffu : 0u;
+        const uint32_t* yj = Y + (size_t)j * nw;
+        int32_t a[CW], b[CW];
 #pragma unroll
-    for (int c = 0; c < CW; c++) {
-        a[c] = chunk30(Dw, nwd, 0u, 64 * c + lane);
-        b[c] = chunk30(yj, nw, ext, 64 * c + lane);
+        for (int c = 0; c < CW; c++) {
+            a[c] = chunk30(Dw, nwd, 0u, 64 * c + lane);
+            b[c] = chunk30(yj, nw, ext, 64 * c + lane);
+        }
+        limb_apply<CW>(a, b, 1, 0, 0, 1, CW, lane0);
+        int ns = CW;
+        auto hand_over = [&](int buf) {  // the top h and the six limbs h - 4 .. h + 1
+            const int h = top_limb<CW>(a, b, ns);
+            ns = h < 0 ? 1 : min(CW, (h + 1) / 64 + 1);
+#pragma unroll
+            for (int e = 0; e < kGcdSeg; e++) {
+                const int k = h - 4 + e;
+                if (k < 0) {
+                    if (lane0) sSeg[buf][0][e] = 0, sSeg[buf][1][e] = 0;
+                } else if (lane == (k & 63)) {
+                    sSeg[buf][0][e] = a[k >> 6];
+                    sSeg[buf][1][e] = b[k >> 6];
+                }
+            }
+            if (lane0) sTop[buf] = h;
+        };
+        hand_over(0);
+        __syncthreads();
+        for (int r = 1;; r++) {
+            __syncthreads();  // matrix r is ready (and the window after matrix r - 1 was read)
+            const int buf = r & 1;
+            if (sCmd[buf] != 0) break;
+            const int32_t A = sM[buf][0], B = sM[buf][1], C = sM[buf][2], D = sM[buf][3];
+            if (!(A == 1 && B == 0 && C == 0 && D == 1)) limb_apply<CW>(a, b, A, B, C, D, ns, lane0);
+            hand_over(buf);
+        }
+        return;
     }
-    limb_apply<CW>(a, b, 1, 0, 0, 1, CW, lane0);
+
+    // ---- Euclid wave: its control flow is uniform; lanes 0 .. 6 carry the
+    // window (lane e: limb base + e of a and of b)
+    __syncthreads();
+    int32_t wa = 0, wb = 0;
+    int base = 0;
+    auto read_window = [&](int buf) {
+        wa = lane < kGcdSeg ? sSeg[buf][0][lane] : 0;
+        wb = lane < kGcdSeg ? sSeg[buf][1][lane] : 0;
+        base = sTop[buf] - 4;
+    };
+    read_window(0);
+    int32_t M0 = 1, M1 = 0, M2 = 0, M3 = 1;  // the matrix issued last (applied by now to the limbs)
     int result = 1;
     uint64_t g = 0;
-    int ns = CW;
-    const int max_rounds = (32 * (nw > nwd ? nw : nwd)) / 12 + 64;
-    for (int round = 0; round < max_rounds; round++) {
-        const int h = top_limb<CW>(a, b, ns);
-        if (h < 0 || h >= 64 * CW - 2) break;  // both zero (cannot happen with d > 0), or no headroom left
-        ns = (h + 1) / 64 + 1;
-        if (h <= 3) {
+    for (int r = 1;; r++) {
+        // the window after the matrix issued last: limb k changes from limbs k
+        // and k - 1 only, so lanes 1 .. 6 become exact (lane 0 lacks the high
+        // parts entering from below)
+        int lo_lane = 0;
+        if (!(M0 == 1 && M1 == 0 && M2 == 0 && M3 == 1)) {
+            const int64_t va = (int64_t)M0 * wa + ((int64_t)M1 * wb + (1 << 29));
+            const int64_t vb = (int64_t)M2 * wa + ((int64_t)M3 * wb + (1 << 29));
+            const int32_t ha = (int32_t)(va >> 30), hb = (int32_t)(vb >> 30);
+            const int32_t ia = __builtin_amdgcn_update_dpp(0, ha, 0x111, 0xf, 0xf, false);  // row_shr:1
+            const int32_t ib = __builtin_amdgcn_update_dpp(0, hb, 0x111, 0xf, 0xf, false);
+            wa = lane <= kGcdSeg ? (int32_t)((uint32_t)va & 0x3fffffffu) - (1 << 29) + ia : 0;
+            wb = lane <= kGcdSeg ? (int32_t)((uint32_t)vb & 0x3fffffffu) - (1 << 29) + ib : 0;
+            lo_lane = 1;
+        }
+        const uint64_t nzm = __ballot((wa != 0 || wb != 0) && lane >= lo_lane && lane <= kGcdSeg);
+        const int top = nzm ? 63 - __builtin_clzll(nzm) : -1;  // lane of the top limb
+        const int h = base + top;
+        int cmd = 0;
+        int32_t nM[4] = {1, 0, 0, 1};
+        if (r > max_rounds || top < 0 || h >= 64 * CW - 3) {
+            cmd = 1;  // no progress in sight, no limb in view or no headroom left: the host finishes
+        } else if (h <= 3 && base + lo_lane <= 0) {
             // exact values from limbs 0..3, then the binary gcd
             __int128 va = 0, vb = 0;
 #pragma unroll
             for (int k = 3; k >= 0; k--) {
-                va = va * (1 << 30) + __builtin_amdgcn_readlane(a[0], k);
-                vb = vb * (1 << 30) + __builtin_amdgcn_readlane(b[0], k);
+                const int e = k - base;
+                va = va * (1 << 30) + __builtin_amdgcn_readlane(wa, e);
+                vb = vb * (1 << 30) + __builtin_amdgcn_readlane(wb, e);
             }
             unsigned __int128 u = (unsigned __int128)(va < 0 ? -va : va);
             unsigned __int128 v = (unsigned __int128)(vb < 0 ? -vb : vb);
@@ -426,56 +509,72 @@ __global__ __launch_bounds__(256) void gcd_kernel(const uint32_t* __restrict__ Y
                 g = (uint64_t)u;
                 result = 0;
             }
-            break;
-        }
-        double fa = lead3<CW>(a, h), fb = lead3<CW>(b, h);
-        if (fa < 0.0) {
-            limb_negate<CW>(a, ns);
-            fa = -fa;
-        }
-        if (fb < 0.0) {
-            limb_negate<CW>(b, ns);
-            fb = -fb;
-        }
-        // both at one scale with the larger below 2^52
-        int e;
-        (void)frexp(fmax(fa, fb), &e);
-        double x = floor(ldexp(fa, 52 - e)), y = floor(ldexp(fb, 52 - e));
-        // Euclid on the leading parts (exact integers below 2^53, the same in
-        // every lane), four steps at a time; a step counts only when it and
-        // every step before it are acceptable
-        double A = 1.0, B = 0.0, C = 0.0, D = 1.0;
-        int steps = 0;
-        for (int it = 0; it < 16; it++) {
-            double x1, y1, A1, B1, C1, D1, x2, y2, A2, B2, C2, D2;
-            double x3, y3, A3, B3, C3, D3, x4, y4, A4, B4, C4, D4;
-            const bool o1 = euclid_step(x, y, A, B, C, D, x1, y1, A1, B1, C1, D1);
-            const bool o2 = euclid_step(x1, y1, A1, B1, C1, D1, x2, y2, A2, B2, C2, D2) && o1;
-            const bool o3 = euclid_step(x2, y2, A2, B2, C2, D2, x3, y3, A3, B3, C3, D3) && o2;
-            const bool o4 = euclid_step(x3, y3, A3, B3, C3, D3, x4, y4, A4, B4, C4, D4) && o3;
-            if (__ballot(o4) != 0) {
-                x = x4, y = y4, A = A4, B = B4, C = C4, D = D4;
-                steps += 4;
-                continue;
+            cmd = 1;
+        } else if (top - 2 < lo_lane || h <= 3) {
+            // the window lacks the limbs the leading parts (or the last four
+            // limbs) need: issue the identity and read a fresh window
+        } else {
+            // leading parts from limbs h, h - 1, h - 2
+            double fa = fma(fma((double)__builtin_amdgcn_readlane(wa, top), 0x1p30,
+                                (double)__builtin_amdgcn_readlane(wa, top - 1)),
+                            0x1p30, (double)__builtin_amdgcn_readlane(wa, top - 2));
+            double fb = fma(fma((double)__builtin_amdgcn_readlane(wb, top), 0x1p30,
+                                (double)__builtin_amdgcn_readlane(wb, top - 1)),
+                            0x1p30, (double)__builtin_amdgcn_readlane(wb, top - 2));
+            const int32_t ga = fa < 0.0 ? -1 : 1, gb = fb < 0.0 ? -1 : 1;  // signs folded into the matrix
+            fa = fabs(fa);
+            fb = fabs(fb);
+            int ex;
+            (void)frexp(fmax(fa, fb), &ex);
+            double x = floor(ldexp(fa, 52 - ex)), y = floor(ldexp(fb, 52 - ex));
+            double A = 1.0, B = 0.0, C = 0.0, D = 1.0;
+            int steps = 0;
+            for (int it = 0; it < 16; it++) {
+                double x1, y1, A1, B1, C1, D1, x2, y2, A2, B2, C2, D2;
+                double x3, y3, A3, B3, C3, D3, x4, y4, A4, B4, C4, D4;
+                const bool o1 = euclid_step(x, y, A, B, C, D, x1, y1, A1, B1, C1, D1);
+                const bool o2 = euclid_step(x1, y1, A1, B1, C1, D1, x2, y2, A2, B2, C2, D2) && o1;
+                const bool o3 = euclid_step(x2, y2, A2, B2, C2, D2, x3, y3, A3, B3, C3, D3) && o2;
+                const bool o4 = euclid_step(x3, y3, A3, B3, C3, D3, x4, y4, A4, B4, C4, D4) && o3;
+                if (__ballot(o4) != 0) {
+                    x = x4, y = y4, A = A4, B = B4, C = C4, D = D4;
+                    steps += 4;
+                    continue;
+                }
+                if (__ballot(o3) != 0) {
+                    A = A3, B = B3, C = C3, D = D3;
+                    steps += 3;
+                } else if (__ballot(o2) != 0) {
+                    A = A2, B = B2, C = C2, D = D2;
+                    steps += 2;
+                } else if (__ballot(o1) != 0) {
+                    A = A1, B = B1, C = C1, D = D1;
+                    steps += 1;
+                }
+                break;
             }
-            if (__ballot(o3) != 0) {
-                A = A3, B = B3, C = C3, D = D3;
-                steps += 3;
-            } else if (__ballot(o2) != 0) {
-                A = A2, B = B2, C = C2, D = D2;
-                steps += 2;
-            } else if (__ballot(o1) != 0) {
-                A = A1, B = B1, C = C1, D = D1;
-                steps += 1;
+            if (steps == 0) {
+                cmd = 1;  // no certain progress: the host finishes
+            } else {
+                nM[0] = (int32_t)A * ga;
+                nM[1] = (int32_t)B * gb;
+                nM[2] = (int32_t)C * ga;
+                nM[3] = (int32_t)D * gb;
             }
-            break;
         }
-        if (steps == 0) break;  // no certain progress: the host finishes
-        limb_apply<CW>(a, b, __builtin_amdgcn_readfirstlane((int32_t)A), __builtin_amdgcn_readfirstlane((int32_t)B),
-                       __builtin_amdgcn_readfirstlane((int32_t)C), __builtin_amdgcn_readfirstlane((int32_t)D), ns,
-                       lane0);
+        const int buf = r & 1;
+        if (lane0) {
+            sCmd[buf] = cmd;
+            sM[buf][0] = nM[0], sM[buf][1] = nM[1], sM[buf][2] = nM[2], sM[buf][3] = nM[3];
+        }
+        __syncthreads();  // matrix r is ready; the window after matrix r - 1 is ready
+        if (cmd != 0) break;
+        // the window handed over after matrix r - 1; the next iteration
+        // applies matrix r to it
+        read_window(buf ^ 1);
+        M0 = nM[0], M1 = nM[1], M2 = nM[2], M3 = nM[3];
     }
-    if (lane == 0) {
+    if (lane0) {
         gstat[j] = result;
         G[j] = g;
     }
@@ -602,13 +701,13 @@ int gcd_words_per_lane(int words) {
 hipError_t launch_gcd(const uint32_t* Y, int nw, const int* status, int valid_rows, const uint32_t* Dw, int nwd,
                       uint64_t* G, int* gstat, hipStream_t st) {
     const int cw = gcd_words_per_lane(nw > nwd ? nw : nwd);
-    const dim3 grid((valid_rows + 3) / 4);
+    const dim3 grid(valid_rows);
     if (cw == 8)
-        hipLaunchKernelGGL(gcd_kernel<8>, grid, dim3(256), 0, st, Y, nw, status, valid_rows, Dw, nwd, G, gstat);
+        hipLaunchKernelGGL(gcd_kernel<8>, grid, dim3(128), 0, st, Y, nw, status, valid_rows, Dw, nwd, G, gstat);
     else if (cw == 16)
-        hipLaunchKernelGGL(gcd_kernel<16>, grid, dim3(256), 0, st, Y, nw, status, valid_rows, Dw, nwd, G, gstat);
+        hipLaunchKernelGGL(gcd_kernel<16>, grid, dim3(128), 0, st, Y, nw, status, valid_rows, Dw, nwd, G, gstat);
     else if (cw == 32)
-        hipLaunchKernelGGL(gcd_kernel<32>, grid, dim3(256), 0, st, Y, nw, status, valid_rows, Dw, nwd, G, gstat);
+        hipLaunchKernelGGL(gcd_kernel<32>, grid, dim3(128), 0, st, Y, nw, status, valid_rows, Dw, nwd, G, gstat);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
