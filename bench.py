@@ -203,8 +203,8 @@ def rooflines(prof, info, n, c, traffic=None):
     ms, cnt = prof.get("gj_update", (0.0, 0))
     if cnt:
         # blocked elimination update: every live prime's n x pitch matrix read and written once,
-        # the transposed old pivot rows read; ops of the rank-32 product
-        bytes_per = 2.0 * E * n * pitch + E * pitch * 64
+        # the transposed old pivot rows (32 bytes per column) read; ops of the rank-32 product
+        bytes_per = 2.0 * E * n * pitch + E * pitch * 32
         ops_per = 2.0 * E * n * pitch * 32
         avg_s = ms / cnt / 1e3
         gbs = bytes_per / avg_s / 1e9
@@ -215,8 +215,8 @@ def rooflines(prof, info, n, c, traffic=None):
                             "int8_tops": round(ops_per / avg_s / 1e12, 2)}
     ms, cnt = prof.get("gj_panel", (0.0, 0))
     if cnt:
-        # 32 elimination steps on each live prime's n x 32 panel: read-modify-write of the panel
-        # in registers, one 1024-thread block per prime (latency-bound: 53 of 256 CUs)
+        # 32 elimination steps on each live prime's n x 32 panel (the rows that can still pivot,
+        # in registers), one 1024-thread block per prime (latency-bound: 53 of 256 CUs)
         out["gj_panel"] = {"avg_launch_us": round(ms / cnt * 1e3, 2), "launches": cnt, "total_ms": round(ms, 3),
                            "element_updates_per_launch": int(32 * E * n * 32)}
     ms, cnt = prof["lift_contract"]
@@ -245,7 +245,7 @@ def rooflines(prof, info, n, c, traffic=None):
                              "traffic": traffic.get("recon_gemm"),
                              "avg_launch_us": round(s / cnt * 1e6, 2), "launches": cnt,
                              "algorithmic_ops_total": ops}
-    for k in ("garner", "residual", "residues", "recon_other", "recon_gcd"):
+    for k in ("crt", "residual", "residues", "recon_other", "recon_gcd"):
         ms, cnt = prof.get(k, (0.0, 0))
         if cnt:
             out[k] = {"avg_launch_us": round(ms / cnt * 1e3, 2), "launches": cnt, "total_ms": round(ms, 3)}

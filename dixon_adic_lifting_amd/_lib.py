@@ -139,7 +139,7 @@ def last_timings():
             "reconstruct_ms": buf[4]}
 
 
-KERNEL_CLASSES = ["gj_step", "lift_contract", "garner", "residual", "residues", "recon_gemm", "recon_other",
+KERNEL_CLASSES = ["gj_step", "lift_contract", "crt", "residual", "residues", "recon_gemm", "recon_other",
                   "recon_gcd", "gj_panel", "gj_update"]
 
 

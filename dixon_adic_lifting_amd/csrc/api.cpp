@@ -4,7 +4,7 @@
 // Stages (exact-solve card, phanerozoic/exact-solve, section "Method"):
 //   checks + bounds -> residues of A -> batched Gauss-Jordan inverse (one
 //   launch per elimination step, all 53 primes) -> prime-set selection and
-//   step count -> m lift steps (contraction, Garner, residual) -> one
+//   step count -> m lift steps (contraction, CRT, residual) -> one
 //   device-to-host copy of the digits per chunk of steps -> host rational
 //   reconstruction.
 #include <hip/hip_runtime.h>
@@ -47,7 +47,7 @@ double ms_since(clk::time_point t0) {
 // gcds) are declared with the reconstruction driver; 8 and 9 are the panel
 // and update launches of the blocked elimination.
 enum KernelClass {
-    KC_GJ = 0, KC_CONTRACT = 1, KC_GARNER = 2, KC_RESIDUAL = 3, KC_RESIDUES = 4,
+    KC_GJ = 0, KC_CONTRACT = 1, KC_CRT = 2, KC_RESIDUAL = 3, KC_RESIDUES = 4,
     KC_PANEL = 8, KC_UPDATE = 9, KC_COUNT = 10
 };
 
@@ -262,8 +262,8 @@ int run_lift(const int64_t* dA, const int64_t* db, uint8_t* ws, hipStream_t st, 
             long ev = prof->start(KC_CONTRACT);
             HIP_CHECK(launch_lift_contract(L, ws, ls.E, st));
             prof->stop(ev);
-            ev = prof->start(KC_GARNER);
-            HIP_CHECK(launch_lift_garner(L, ws, s, st));
+            ev = prof->start(KC_CRT);
+            HIP_CHECK(launch_lift_crt(L, ws, s, st));
             prof->stop(ev);
             ev = prof->start(KC_RESIDUAL);
             HIP_CHECK(launch_lift_residual(L, ws, pr.a32, dA, st));

@@ -141,10 +141,10 @@ hipError_t launch_gj_panel_rest(const Layout& L, uint8_t* ws, int K, hipStream_t
 hipError_t launch_gj_gather_next(const Layout& L, uint8_t* ws, int K, hipStream_t st);
 hipError_t launch_export_inverse(const Layout& L, const uint8_t* ws, int8_t* B, hipStream_t st);
 hipError_t launch_split_b(const int64_t* b, const Layout& L, uint8_t* ws, int E, hipStream_t st);
-// one lift step = contraction, then Garner (digit into chunk slot `slot`),
+// one lift step = contraction, then the CRT (digit into chunk slot `slot`),
 // then the residual update with the split of the new residual
 hipError_t launch_lift_contract(const Layout& L, uint8_t* ws, int E, hipStream_t st);
-hipError_t launch_lift_garner(const Layout& L, uint8_t* ws, int slot, hipStream_t st);
+hipError_t launch_lift_crt(const Layout& L, uint8_t* ws, int slot, hipStream_t st);
 hipError_t launch_lift_residual(const Layout& L, uint8_t* ws, bool a32, const int64_t* A64, hipStream_t st);
 
 // reconstruction on the GPU (recon.hip); see the kernels for layouts

@@ -5,7 +5,7 @@
 //     q_j < 256 at once, one launch per elimination step across all primes,
 //     Barrett reduction instead of a hardware modulo;
 //   * lift step: per-prime balanced-residue int8 contraction with int32
-//     accumulation, balanced Garner CRT into the wide base-P digit, and the
+//     accumulation, a balanced CRT into the wide base-P digit, and the
 //     one-limb residual update (r_i - A x_i) P^-1 mod 2^64 (P odd);
 //   * range limits (card, "Method"/"Requirements"): n * max|A_ij| < 2^63 so
 //     the residual is one signed 64-bit limb; n <= 2^17 so int8 x int8
@@ -1826,7 +1826,7 @@ hipError_t launch_lift_contract(const Layout& L, uint8_t* ws, int E, hipStream_t
     return hipGetLastError();
 }
 
-hipError_t launch_lift_garner(const Layout& L, uint8_t* ws, int slot, hipStream_t st) {
+hipError_t launch_lift_crt(const Layout& L, uint8_t* ws, int slot, hipStream_t st) {
     const int NC = L.n * L.c;
     hipLaunchKernelGGL(crt_kernel, dim3((NC + 63) / 64), dim3(256), 0, st,
                        (const LiftParams*)(ws + L.off_params), (const uint8_t*)(ws + L.off_U), NC,

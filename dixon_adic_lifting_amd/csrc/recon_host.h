@@ -23,7 +23,7 @@ struct GpuReconPlan {
     int nw = 0;               // words kept per numerator (nbits / 32 + 1)
     int Ncolsp = 0, Kpad = 0; // GEMM columns (bytes of a weight row, padded), contraction bytes
     int NCc = 0, NCcp = 0;    // components per GEMM chunk, padded to 128
-    size_t off_digits = 0;    // uint64 [NC][m][6]  lift digits (written by Garner)
+    size_t off_digits = 0;    // uint64 [NC][m][6]  lift digits (written by the CRT kernel)
     size_t off_S = 0;         // int8 [NCcp][Kpad]  balanced digit bytes of a chunk
     size_t off_rowsum = 0;    // int32 [NCcp]
     size_t off_T = 0;         // uint32 [m][NW]     P^i d mod M

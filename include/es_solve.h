@@ -9,8 +9,8 @@
  * denominator.  A^-1 mod q_j comes from a batched Gauss-Jordan inverse (all
  * primes at once; one launch per elimination step, or blocked 32 steps per
  * panel with an int8-MFMA rank-32 update; Barrett-style reduction); each
- * step's x_i is one int8 contraction per prime, a balanced Garner CRT into
- * the wide base-P digit, and a one-limb residual update
+ * step's x_i is one int8 contraction per prime, a balanced CRT into the
+ * wide base-P digit, and a one-limb residual update
  * (r_i - A x_i) P^-1 mod 2^64.  A host stage does the rational
  * reconstruction (common denominator from a sample, then one modular
  * multiply per numerator; the multiplies of all components run on the GPU
@@ -146,10 +146,12 @@ int es_set_gpu_reconstruction(int on);
  * Opt-in kernel timing for measurement.  With es_set_profiling(1) on a
  * thread, later solves on that thread bracket every launch of the hot
  * kernels with a pair of HIP events on the solve's stream (small added gaps
- * between launches; results are unchanged).  es_kernel_profile then gives,
+ * between launches; results are unchanged); while it is on, the blocked
+ * elimination runs one kernel at a time instead of overlapping each panel
+ * with the previous panel's update.  es_kernel_profile then gives,
  * for the last solve, the summed event time in ms and the launch count per
  * kernel class: [0] Gauss-Jordan step, [1] lift contraction (GEMV / GEMM),
- * [2] Garner, [3] residual update, [4] residues of A, [5] reconstruction
+ * [2] CRT of the digit, [3] residual update, [4] residues of A, [5] reconstruction
  * GEMM, [6] other reconstruction kernels (weight rows, digit bytes,
  * numerators), [7] the gcds that bring the numerators to lowest terms,
  * [8] panel and [9] update launches of the blocked elimination.  Writes
