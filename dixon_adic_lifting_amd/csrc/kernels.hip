@@ -1116,7 +1116,7 @@ __global__ __launch_bounds__(1024) void gj_panel_kernel(int8_t* __restrict__ S, 
 // launch, the update of panel K - 32 on every column outside
 // [K - 32, K + 32) (the blocks after them, four 128 x 128 tiles each).  The
 // two touch disjoint columns; panel K's columns were updated beforehand by
-// gj_gather_next_kernel.  The panel blocks come first, so they are placed
+// gj_next_kernel.  The panel blocks come first, so they are placed
 // first.  K >= n: the update part only.
 template <int RPT, bool UP>
 __global__ __launch_bounds__(1024) void gj_panel_rest_kernel(int8_t* __restrict__ S, int n, int pitch, int K,
@@ -1139,24 +1139,51 @@ __global__ __launch_bounds__(1024) void gj_panel_rest_kernel(int8_t* __restrict_
                 Kr + 2 * kPanel);
 }
 
-// After panel K: its pivot rows to GT (all columns), then, when K + 32 < n,
-// the update of the next panel's columns [K + 32, K + 64) on every row, one
-// block per prime (16 row tiles of 16 per wave, two 16-column halves).
-__global__ __launch_bounds__(1024) void gj_gather_next_kernel(int8_t* __restrict__ S, int n, int pitch, int K,
-                                                              const int* __restrict__ piv,
-                                                              const int* __restrict__ rowpos,
-                                                              const int* __restrict__ flags,
-                                                              int8_t* __restrict__ GT) {
-    const int j = blockIdx.x;
+// After panel K: its pivot rows to GT, 256 columns per block (grid
+// (column chunks, primes)), words read along the rows and regrouped by
+// column in LDS, one 32-byte row of GT per column.
+__global__ __launch_bounds__(256) void gj_gather_kernel(const int8_t* __restrict__ S, int n, int pitch, int K,
+                                                        const int* __restrict__ piv, const int* __restrict__ flags,
+                                                        int8_t* __restrict__ GT) {
+    const int j = blockIdx.y;
     if (flags[j]) return;
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    int8_t* Sj = S + (size_t)j * n * pitch;
-    int8_t* GTj = GT + (size_t)j * pitch * kPanel;
-    __shared__ __attribute__((aligned(16))) uint8_t gts[1024 * kPanel];
-    panel_gather_gt(Sj, pitch, min(kPanel, n - K), piv + (size_t)j * (n + 1) + K, gts, GTj, t);
-    if (K + kPanel >= n) return;
-    // the block's own GT writes are visible after the barriers in the gather
+    const int t = threadIdx.x;
+    const int c0 = blockIdx.x * 256;
+    const int ncol = min(256, pitch - c0);
+    const int bw = min(kPanel, n - K);
+    const int8_t* Sj = S + (size_t)j * n * pitch;
+    const int* plist = piv + (size_t)j * (n + 1) + K;
+    __shared__ __attribute__((aligned(16))) uint8_t gts[256 * kPanel];
+#pragma unroll
+    for (int u = 0; u < 8; u++) {
+        const int w = t + 256 * u;  // word w: row c = w / 64, columns 4 (w % 64) .. + 3
+        const int c = w >> 6, cw = w & 63;
+        if (4 * cw >= ncol) continue;
+        const uint32_t v = c < bw ? *(const uint32_t*)(Sj + (size_t)plist[c] * pitch + c0 + 4 * cw) : 0u;
+#pragma unroll
+        for (int bb = 0; bb < 4; bb++) gts[(4 * cw + bb) * kPanel + c] = (uint8_t)(v >> (8 * bb));
+    }
+    __syncthreads();
+    if (t < ncol) {
+        const uint4* src = (const uint4*)(gts + t * kPanel);
+        uint4* dst = (uint4*)(GT + ((size_t)j * pitch + c0 + t) * kPanel);
+        dst[0] = src[0];
+        dst[1] = src[1];
+    }
+}
+
+// Then, when K + 32 < n, the update of the next panel's columns
+// [K + 32, K + 64) on every row: 64 rows per block (grid (row chunks,
+// primes)), one 16-row tile per wave, two 16-column halves.
+__global__ __launch_bounds__(256) void gj_next_kernel(int8_t* __restrict__ S, int n, int pitch, int K,
+                                                      const int* __restrict__ rowpos, const int* __restrict__ flags,
+                                                      const int8_t* __restrict__ GT) {
+    const int j = blockIdx.y;
+    if (flags[j]) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lr = lane & 15, lg = lane >> 4;
+    int8_t* Sj = S + (size_t)j * n * pitch;
+    const int8_t* GTj = GT + (size_t)j * pitch * kPanel;
     const uint32_t q = c_pt.q[j];
     const uint32_t m28 = (uint32_t)((268435456ull + q - 1) / q);
     const int off = (int)(q * ((524288u + q - 1) / q));
@@ -1166,30 +1193,28 @@ __global__ __launch_bounds__(1024) void gj_gather_next_kernel(int8_t* __restrict
 #pragma unroll
     for (int a = 0; a < 2; a++)
         ga[a] = lg < 2 ? *(const v4i_t*)(GTj + (size_t)(c0 + 16 * a + lr) * kPanel + 16 * lg) : v4i_t{0, 0, 0, 0};
-    for (int tr = wave; 16 * tr < n; tr += 16) {
-        const int i = 16 * tr + lr;
-        const bool rowok = i < n;
-        const v4i_t pb = (lg < 2 && rowok) ? *(const v4i_t*)(Sj + (size_t)i * pitch + K + 16 * lg) : v4i_t{0, 0, 0, 0};
-        const int rp = rowok ? rpj[i] : 0;
-        const bool pivot_row = rp >= K && rp < K + kPanel;
+    const int i = blockIdx.x * 64 + 16 * wave + lr;
+    const bool rowok = i < n;
+    const v4i_t pb = (lg < 2 && rowok) ? *(const v4i_t*)(Sj + (size_t)i * pitch + K + 16 * lg) : v4i_t{0, 0, 0, 0};
+    const int rp = rowok ? rpj[i] : 0;
+    const bool pivot_row = rp >= K && rp < K + kPanel;
 #pragma unroll
-        for (int a = 0; a < 2; a++) {
-            const v4i_t acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(ga[a], pb, v4i_t{0, 0, 0, 0}, 0, 0, 0);
-            const int col = c0 + 16 * a + 4 * lg;
-            const uint32_t old = rowok ? *(const uint32_t*)(Sj + (size_t)i * pitch + col) : 0u;
-            uint32_t outw = 0;
+    for (int a = 0; a < 2; a++) {
+        const v4i_t acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(ga[a], pb, v4i_t{0, 0, 0, 0}, 0, 0, 0);
+        const int col = c0 + 16 * a + 4 * lg;
+        const uint32_t old = rowok ? *(const uint32_t*)(Sj + (size_t)i * pitch + col) : 0u;
+        uint32_t outw = 0;
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const int so = (int)(int8_t)(old >> (8 * e));
-                const int x = (pivot_row ? 0 : so) + acc[e];
-                const uint32_t xp = (uint32_t)(x + off);
-                const uint32_t tq = __umulhi(xp << 4, m28);
-                const int r = (int)(xp - tq * q);
-                const int v = r > (int)(q >> 1) ? r - (int)q : r;
-                outw |= ((uint32_t)v & 0xffu) << (8 * e);
-            }
-            if (rowok) *(uint32_t*)(Sj + (size_t)i * pitch + col) = outw;
+        for (int e = 0; e < 4; e++) {
+            const int so = (int)(int8_t)(old >> (8 * e));
+            const int x = (pivot_row ? 0 : so) + acc[e];
+            const uint32_t xp = (uint32_t)(x + off);
+            const uint32_t tq = __umulhi(xp << 4, m28);
+            const int r = (int)(xp - tq * q);
+            const int v = r > (int)(q >> 1) ? r - (int)q : r;
+            outw |= ((uint32_t)v & 0xffu) << (8 * e);
         }
+        if (rowok) *(uint32_t*)(Sj + (size_t)i * pitch + col) = outw;
     }
 }
 
@@ -1246,9 +1271,13 @@ hipError_t launch_gj_panel_rest(const Layout& L, uint8_t* ws, int K, hipStream_t
 }
 
 hipError_t launch_gj_gather_next(const Layout& L, uint8_t* ws, int K, hipStream_t st) {
-    hipLaunchKernelGGL(gj_gather_next_kernel, dim3(kNumPrimes), dim3(1024), 0, st, (int8_t*)(ws + L.off_S), L.n,
-                       L.pitch, K, (const int*)(ws + L.off_piv), (const int*)(ws + L.off_rowpos),
+    hipLaunchKernelGGL(gj_gather_kernel, dim3((L.pitch + 255) / 256, kNumPrimes), dim3(256), 0, st,
+                       (const int8_t*)(ws + L.off_S), L.n, L.pitch, K, (const int*)(ws + L.off_piv),
                        (const int*)(ws + L.off_flags), (int8_t*)(ws + L.off_GT));
+    if (K + kPanel < L.n)
+        hipLaunchKernelGGL(gj_next_kernel, dim3((L.n + 63) / 64, kNumPrimes), dim3(256), 0, st,
+                           (int8_t*)(ws + L.off_S), L.n, L.pitch, K, (const int*)(ws + L.off_rowpos),
+                           (const int*)(ws + L.off_flags), (const int8_t*)(ws + L.off_GT));
     return hipGetLastError();
 }
 
