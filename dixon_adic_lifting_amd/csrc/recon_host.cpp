@@ -16,6 +16,8 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <memory>
+#include <mutex>
 #include <vector>
 
 #include "../../include/es_solve.h"
@@ -173,6 +175,22 @@ uint8_t* gpu_recon_scratch(const GpuReconPlan& pl) { return (uint8_t*)g_dev_scra
         if ((expr) != hipSuccess) return ES_EHIP;     \
     } while (0)
 
+// P^0 .. P^m, kept for the last (P, m) asked for: repeated solves of one
+// size use the same powers.
+static std::shared_ptr<const std::vector<BigInt>> powers_of(const BigInt& P, int m) {
+    static std::mutex mu;
+    static std::shared_ptr<const std::vector<BigInt>> cached;
+    static BigInt cachedP;
+    std::lock_guard<std::mutex> lk(mu);
+    if (cached && (int)cached->size() == m + 1 && cmp(cachedP, P) == 0) return cached;
+    auto v = std::make_shared<std::vector<BigInt>>(m + 1);
+    (*v)[0] = BigInt::from_u64(1);
+    for (int i = 1; i <= m; i++) (*v)[i] = mul((*v)[i - 1], P);
+    cached = v;
+    cachedP = P;
+    return cached;
+}
+
 int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const BigInt& M, int nbits, int dbits,
                     int nthreads, hipStream_t st, SolutionData* out, GpuReconTimes* tm, KernelTimer* kt) {
     typedef std::chrono::steady_clock clk;
@@ -235,11 +253,13 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
     bool gpu_gcd = false;
     auto gpu_pass = [&]() -> int {
         // the chain T_{i+1} = T_i P mod M, cut into segments that each start
-        // from P^{i0} d mod M and run in parallel
-        const int nseg = std::max(1, std::min(nthreads, m / 16));
+        // from P^{i0} d mod M = (d mod P^{m - i0}) P^{i0} (M = P^m: the
+        // product is below M, no division by M) and run in parallel
+        const auto pw = powers_of(P, m);
+        const int nseg = std::max(1, std::min(nthreads, m / 8));
         parallel_for_each((size_t)nseg, nthreads, [&](size_t sg) {
             const int i0 = (int)(sg * (size_t)m / nseg), i1 = (int)((sg + 1) * (size_t)m / nseg);
-            BigInt Ti = mod_floor(i0 == 0 ? d : mul(d, pow_u(P, (unsigned)i0)), M);
+            BigInt Ti = i0 == 0 ? mod_floor(d, M) : mul(mod_floor(d, (*pw)[m - i0]), (*pw)[i0]);
             for (int i = i0; i < i1; i++) {
                 to_words(Ti, &T[(size_t)i * NW], NW);
                 if (i + 1 < i1) Ti = mod_floor(mul(Ti, P), M);
