@@ -23,6 +23,7 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
+#include <type_traits>
 #include <cstdlib>
 
 #include "es_internal.h"
@@ -1562,18 +1563,22 @@ __global__ __launch_bounds__(256) void lift_mfma_kernel(const int8_t* __restrict
 //   X = sum_l u_l W_l,  W_l = P / q_l,  u_l = (r_l c_l mod q_l) in (-q_l/2, q_l/2),
 //   c_l = W_l^-1 mod q_l,  so X = x (mod P) and |X| < E P / 2;
 //   x = X - k P with k = round(X / P) = round(sum_l u_l / q_l).
-// Four lanes per component, lane s taking the primes l = s mod 4; word w of
-// X accumulates sum_l u_l W_l[w] in double precision, exact (each term is
-// below 2^39 in magnitude, every partial sum below 2^45), and the four
-// partial sums are added across the lane quad.  k comes from the double sum
+// Sixteen lanes per component, lane s taking the primes l = s mod 16; word w
+// of X accumulates sum_l u_l W_l[w] in double precision, exact (each term is
+// below 2^39 in magnitude, every partial sum below 2^45), and the sixteen
+// partial sums are added across the lanes.  k comes from the double sum
 // of u_l / q_l, whose error (about E 2^-54) can only matter when X / P is
 // within it of a half-integer; there an exact comparison with (P - 1) / 2
 // settles the representative.  x mod 2^64 is kept for the residual.
 
-// v + (v from lane l ^ X within the quad), for a double
+// v + (v from a partner lane), for a double: X = 1, 2 pair lanes l ^ 1,
+// l ^ 2 in each quad; X = 4 pairs l with 7 - l in each eight lanes and
+// X = 8 pairs l with 15 - l in each sixteen.  After the levels below X every
+// lane holds the sum of its aligned group of X, so each level doubles it.
 template <int X>
 __device__ __forceinline__ double quad_add(double v) {
-    constexpr int ctrl = X == 1 ? 0xb1 : 0x4e;  // quad_perm [1,0,3,2] / [2,3,0,1]
+    // quad_perm [1,0,3,2] / [2,3,0,1] / row_half_mirror / row_mirror
+    constexpr int ctrl = X == 1 ? 0xb1 : X == 2 ? 0x4e : X == 4 ? 0x141 : 0x140;
     const uint64_t b = __double_as_longlong(v);
     const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, ctrl, 0xf, 0xf, false);
     const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), ctrl, 0xf, 0xf, false);
@@ -1596,14 +1601,14 @@ __global__ __launch_bounds__(256) void crt_kernel(const LiftParams* __restrict__
         qc[l][2] = prm->cinv[l];
     }
     __syncthreads();
-    const int s = threadIdx.x & 3;
-    const int comp = blockIdx.x * 64 + (threadIdx.x >> 2);
-    if (comp >= NC) return;  // the whole quad leaves together
-    constexpr int LPL = (kNumPrimes + 3) / 4;  // primes per lane
+    const int s = threadIdx.x & 15;
+    const int comp = blockIdx.x * 16 + (threadIdx.x >> 4);
+    if (comp >= NC) return;  // the component's sixteen lanes leave together
+    constexpr int LPL = (kNumPrimes + 15) / 16;  // primes per lane
     uint32_t res[LPL];
 #pragma unroll
     for (int i = 0; i < LPL; i++) {
-        const int l = s + 4 * i;
+        const int l = s + 16 * i;
         res[i] = l < E ? U[(size_t)l * NC + comp] : 0u;
     }
     double acc[kDigitWords];
@@ -1612,7 +1617,7 @@ __global__ __launch_bounds__(256) void crt_kernel(const LiftParams* __restrict__
     double f = 0.0;
 #pragma unroll
     for (int i = 0; i < LPL; i++) {
-        const int l = s + 4 * i;
+        const int l = s + 16 * i;
         if (l >= E) continue;
         const uint32_t q = qc[l][0];
         const uint32_t u = red16(res[i] * qc[l][2], q, qc[l][1]);
@@ -1621,9 +1626,9 @@ __global__ __launch_bounds__(256) void crt_kernel(const LiftParams* __restrict__
 #pragma unroll
         for (int w = 0; w < kDigitWords; w++) acc[w] = fma(ud, Wd[l][w], acc[w]);
     }
-    f = quad_add<2>(quad_add<1>(f));
+    f = quad_add<8>(quad_add<4>(quad_add<2>(quad_add<1>(f))));
 #pragma unroll
-    for (int w = 0; w < kDigitWords; w++) acc[w] = quad_add<2>(quad_add<1>(acc[w]));
+    for (int w = 0; w < kDigitWords; w++) acc[w] = quad_add<8>(quad_add<4>(quad_add<2>(quad_add<1>(acc[w]))));
     if (s != 0) return;
     const double k = rint(f);
     const int64_t ki = (int64_t)k;
@@ -1728,22 +1733,39 @@ __global__ __launch_bounds__(256) void residual_kernel(const AT* __restrict__ A,
     }
 }
 
-// The same update for one right-hand side, one block per row: 256 threads
-// cover 1024 columns per pass with 16-byte loads of A (int32) and x_low, the
-// 64-bit sums meet in a wave butterfly and then in LDS, and the first wave
-// writes r_{i+1} and its balanced residues.
+// 64-bit sum over the wave, in every lane (the butterfly of the GEMV's row sums)
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v, int lane) {
+    auto level = [&](auto bit) {
+        constexpr int B = decltype(bit)::value;
+        const int lo = xchg_bit<B>((int)(uint32_t)v, lane);
+        const int hi = xchg_bit<B>((int)(uint32_t)(v >> 32), lane);
+        v += ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+    };
+    level(std::integral_constant<int, 32>{});
+    level(std::integral_constant<int, 16>{});
+    level(std::integral_constant<int, 8>{});
+    level(std::integral_constant<int, 4>{});
+    level(std::integral_constant<int, 2>{});
+    level(std::integral_constant<int, 1>{});
+    return v;
+}
+
+// The same update for one right-hand side (int32 A): one wave per row, 16-byte
+// loads of A and x_low, the 64-bit sums meet in a wave butterfly, and lanes
+// below E write the balanced residues of r_{i+1}.
 __global__ __launch_bounds__(256) void residual1_kernel(const int32_t* __restrict__ A, int n,
                                                         int64_t* __restrict__ R,
                                                         const uint64_t* __restrict__ xlow,
                                                         const LiftParams* __restrict__ prm,
                                                         const int* __restrict__ rowpos,
                                                         int8_t* __restrict__ rho, int pitch) {
-    const int r = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lane = threadIdx.x & 63;
+    const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= n) return;
     const int32_t* a = A + (size_t)r * n;
     uint64_t acc = 0;
     if ((n & 3) == 0) {  // rows start 16-byte aligned
-        for (int j0 = tid * 4; j0 < n; j0 += 1024) {
+        for (int j0 = lane * 4; j0 < n; j0 += 256) {
             const int4 av = *(const int4*)(a + j0);
             const ulonglong2 x01 = *(const ulonglong2*)(xlow + j0);
             const ulonglong2 x23 = *(const ulonglong2*)(xlow + j0 + 2);
@@ -1751,15 +1773,9 @@ __global__ __launch_bounds__(256) void residual1_kernel(const int32_t* __restric
                    (uint64_t)(int64_t)av.z * x23.x + (uint64_t)(int64_t)av.w * x23.y;
         }
     } else {
-        for (int jc = tid; jc < n; jc += 256) acc += (uint64_t)(int64_t)a[jc] * xlow[jc];
+        for (int jc = lane; jc < n; jc += 64) acc += (uint64_t)(int64_t)a[jc] * xlow[jc];
     }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-    __shared__ uint64_t part[4];
-    if (lane == 0) part[wave] = acc;
-    __syncthreads();
-    if (wave != 0) return;
-    acc = part[0] + part[1] + part[2] + part[3];
+    acc = wave_sum_u64(acc, lane);
     const int E = prm->E;
     const uint64_t val = ((uint64_t)R[r] - acc) * prm->Pinv;
     if (lane == 0) R[r] = (int64_t)val;
@@ -1857,7 +1873,7 @@ hipError_t launch_lift_contract(const Layout& L, uint8_t* ws, int E, hipStream_t
 
 hipError_t launch_lift_crt(const Layout& L, uint8_t* ws, int slot, hipStream_t st) {
     const int NC = L.n * L.c;
-    hipLaunchKernelGGL(crt_kernel, dim3((NC + 63) / 64), dim3(256), 0, st,
+    hipLaunchKernelGGL(crt_kernel, dim3((NC + 15) / 16), dim3(256), 0, st,
                        (const LiftParams*)(ws + L.off_params), (const uint8_t*)(ws + L.off_U), NC,
                        L.dig_dev ? L.dig_dev : (uint64_t*)(ws + L.off_digits), L.kchunk, slot,
                        (uint64_t*)(ws + L.off_xlow));
@@ -1874,7 +1890,8 @@ hipError_t launch_lift_residual(const Layout& L, uint8_t* ws, bool a32, const in
     if (a32) {
         const int32_t* A = (const int32_t*)(ws + L.off_A32);
         if (L.c == 1)
-            hipLaunchKernelGGL(residual1_kernel, dim3(L.n), dim3(256), 0, st, A, L.n, R, xl, prm, rp, rho, L.pitch);
+            hipLaunchKernelGGL(residual1_kernel, dim3((L.n + 3) / 4), dim3(256), 0, st, A, L.n, R, xl, prm, rp, rho,
+                               L.pitch);
         else
             hipLaunchKernelGGL((residual_kernel<int32_t, 16>), grid, dim3(256), 0, st, A, L.n, L.c, R, xl,
                                prm, rp, rho, L.pitch, 0);

@@ -280,7 +280,7 @@ __global__ __launch_bounds__(256) void recon_gemm_kernel(const int8_t* __restric
 
 // lane l <- lane l - 1, lane 0 <- lane 63
 __device__ __forceinline__ int32_t wave_ror1(int32_t v) {
-    return __builtin_amdgcn_update_dpp(0, v, 0x13c, 0xf, 0xf, false);
+    return __builtin_amdgcn_mov_dpp(v, 0x13c, 0xf, 0xf, false);
 }
 
 // bits [30 k, 30 k + 30) of a little-endian word array (words past n read as ext)
@@ -291,18 +291,16 @@ __device__ __forceinline__ int32_t chunk30(const uint32_t* __restrict__ W, int n
     return (int32_t)(__builtin_amdgcn_alignbit(hi, lo, o) & 0x3fffffffu);
 }
 
-// (a, b) <- (A a + B b, C a + D b) over slots [s0, ns), the high parts
-// entering slot s0 from slot s0 - 1 given (pa0, pb0, held by lane 0); the
-// high parts leaving slot ns - 1 are dropped (limbs above the live ones are
-// zero and stay zero)
+// (a, b) <- (A a + B b, C a + D b) over slots [0, ns); the high parts
+// leaving slot ns - 1 are dropped (the limbs above the live ones are zero,
+// and the top live limb lies below the last lane of slot ns - 1)
 template <int CW>
 __device__ __forceinline__ void limb_apply(int32_t (&a)[CW], int32_t (&b)[CW], int32_t A, int32_t B, int32_t C,
-                                           int32_t D, int ns, bool lane0, int s0 = 0, int32_t pa0 = 0,
-                                           int32_t pb0 = 0) {
-    int32_t pa = pa0, pb = pb0;  // high parts of the slot below, rotated one lane up
+                                           int32_t D, int ns, bool lane0) {
+    int32_t pa = 0, pb = 0;  // high parts of the slot below, rotated one lane up
 #pragma unroll
     for (int c = 0; c < CW; c++) {
-        if (c < s0 || c >= ns) continue;
+        if (c >= ns) continue;
         // w = v + 2^29: high part floor(w / 2^30), low part (w mod 2^30) - 2^29
         const int64_t wa = (int64_t)A * a[c] + ((int64_t)B * b[c] + (1 << 29));
         const int64_t wb = (int64_t)C * a[c] + ((int64_t)D * b[c] + (1 << 29));
@@ -314,29 +312,6 @@ __device__ __forceinline__ void limb_apply(int32_t (&a)[CW], int32_t (&b)[CW], i
         b[c] = (int32_t)(wbl & 0x3fffffffu) - (1 << 29) + (lane0 ? pb : rb);
         pa = ra;
         pb = rb;
-    }
-}
-
-// The high parts that slot c - 1 (c >= 1) passes into slot c under
-// [A B; C D], rotated so that lane 0 holds them (the values limb_apply's
-// first slot takes as pa0, pb0)
-template <int CW>
-__device__ __forceinline__ void limb_carry_into(const int32_t (&a)[CW], const int32_t (&b)[CW], int32_t A, int32_t B,
-                                               int32_t C, int32_t D, int c, int32_t* pa, int32_t* pb) {
-    const int32_t x = a[c - 1], y = b[c - 1];
-    const int64_t wa = (int64_t)A * x + ((int64_t)B * y + (1 << 29));
-    const int64_t wb = (int64_t)C * x + ((int64_t)D * y + (1 << 29));
-    *pa = wave_ror1((int32_t)__builtin_amdgcn_alignbit((uint32_t)((uint64_t)wa >> 32), (uint32_t)wa, 30));
-    *pb = wave_ror1((int32_t)__builtin_amdgcn_alignbit((uint32_t)((uint64_t)wb >> 32), (uint32_t)wb, 30));
-}
-
-// R <- -R over slots [0, ns)
-template <int CW>
-__device__ __forceinline__ void limb_negate(int32_t (&R)[CW], int ns) {
-#pragma unroll
-    for (int c = 0; c < CW; c++) {
-        if (c >= ns) continue;
-        R[c] = -R[c];
     }
 }
 
@@ -352,28 +327,38 @@ __device__ __forceinline__ int top_limb(const int32_t (&a)[CW], const int32_t (&
 
 constexpr int kGcdSeg = 6;  // limbs handed from the limb wave to the Euclid wave
 
-// One Euclidean step on (x, y) with cofactors (A, B; C, D).  The hardware
-// reciprocal r0 is good to about 2^-24; one Newton correction gives x / y
-// to about 2^-48 relative, far below the 2^-20 / 2^26 that the quotient
-// estimate takes off, so the estimate never exceeds the true quotient (for
-// quotients below 2^26) and the remainder is never negative.  An estimate
-// one short (an exact quotient always is) leaves r in [y, 2 y); taking the
-// quotient at least 1 whenever x >= y keeps every such step making
-// progress, so x = y cannot repeat.  True when the step is acceptable:
-// divisor of 26 bits or more, quotient and new cofactors within 2^26.
-__device__ __forceinline__ bool euclid_step(double x, double y, double A, double B, double C, double D,
-                                            double& nx, double& ny, double& nA, double& nB, double& nC,
-                                            double& nD) {
-    const double r0 = __builtin_amdgcn_rcp(y);
-    const double t = x * r0, e = fma(-y, r0, 1.0);
-    const double q = fmax(floor(fma(t, e, t - 0x1p-20)), x >= y ? 1.0 : 0.0);
-    nx = y;
+// One Euclidean step on the leading parts: (x, y) -> (y, x - q y) with the
+// cofactor rows (A, B), (C, D) -> (C, D), (A - q C, B - q D).  xs is x
+// shrunk by 2^-22 relative (computed a step ahead, as y (1 - 2^-22) for the
+// next step); the hardware reciprocal of y is within about 2^-24 relative,
+// so floor(xs / y estimate) never exceeds the true quotient, and falls short
+// of it only for quotients near 2^21 or above, or when x / y is that close
+// above an integer (a short quotient leaves a remainder of at least y, which
+// the next steps take up).  The quotient is at least 1 whenever x >= y (the
+// high word of +0.0 raised to that of 1.0), so x = y cannot repeat.  Every
+// value stays in vector registers: no step waits on the scalar unit.
+__device__ __forceinline__ void euclid_step(double x, double xs, double y, double A, double B, double C, double D,
+                                            double& ys, double& ny, double& nC, double& nD) {
+    const double r = __builtin_amdgcn_rcp(y);
+    ys = y * (1.0 - 0x1p-22);
+    const uint32_t g = x >= y ? 0x3ff00000u : 0u;
+    const uint64_t f = __double_as_longlong(floor(xs * r));
+    const uint32_t fh = (uint32_t)(f >> 32);
+    const double q = __longlong_as_double((long long)(((uint64_t)(fh > g ? fh : g) << 32) | (uint32_t)f));
     ny = fma(-q, y, x);
-    nA = C;
-    nB = D;
     nC = fma(-q, C, A);
     nD = fma(-q, D, B);
-    return y >= 0x1p26 && q < 0x1p26 && fmax(fabs(nC), fabs(nD)) <= 0x1p26;
+}
+
+// Largest |entry| of two cofactor rows.  With q >= 0 throughout and the
+// signs of each column alternating down the sequence of rows, every new row
+// dominates the row two before it (|A - q C| = |A| + q |C|), so the two
+// latest rows bound every earlier one; likewise each divisor is at most the
+// one two steps before it.  A run of steps is acceptable when its last two
+// divisors are at least 2^26 and its last two rows stay below 2^26 (which
+// also keeps every quotient below 2^26).
+__device__ __forceinline__ double row_max(double C1, double D1, double C2, double D2) {
+    return fmax(fmax(fabs(C1), fabs(D1)), fmax(fabs(C2), fabs(D2)));
 }
 
 template <int CW>
@@ -389,9 +374,8 @@ __global__ __launch_bounds__(128) void gcd_kernel(const uint32_t* __restrict__ Y
     }
     const int lane = threadIdx.x & 63;
     const bool lane0 = lane == 0;
-    __shared__ int32_t sM[2][4];             // the round's matrix [A B; C D]
-    __shared__ int sCmd[2];                  // 0: apply it, 1: stop
-    __shared__ int32_t sSeg[2][2][kGcdSeg];  // limbs h - 4 .. h + 1 of a and b
+    __shared__ int4 sM[2];                   // the round's matrix [A B; C D]; all zero: stop
+    __shared__ int32_t sSeg[2][2][8];        // limbs h - 4 .. h + 1 of a and b
     __shared__ int sTop[2];                  // h
     const int max_rounds = (32 * (nw > nwd ? nw : nwd)) / 12 + 64;
 
@@ -410,18 +394,21 @@ __global__ __launch_bounds__(128) void gcd_kernel(const uint32_t* __restrict__ Y
         }
         limb_apply<CW>(a, b, 1, 0, 0, 1, CW, lane0);
         int ns = CW;
-        auto hand_over = [&](int buf) {  // the top h and the six limbs h - 4 .. h + 1
+        // the top h and the six limbs h - 4 .. h + 1 (zero below limb 0): the
+        // lane holding limb k0 + e writes entry e, from slot k >> 6, which is
+        // one of the two slots the window touches
+        auto hand_over = [&](int buf) {
             const int h = top_limb<CW>(a, b, ns);
             ns = h < 0 ? 1 : min(CW, (h + 1) / 64 + 1);
-#pragma unroll
-            for (int e = 0; e < kGcdSeg; e++) {
-                const int k = h - 4 + e;
-                if (k < 0) {
-                    if (lane0) sSeg[buf][0][e] = 0, sSeg[buf][1][e] = 0;
-                } else if (lane == (k & 63)) {
-                    sSeg[buf][0][e] = a[k >> 6];
-                    sSeg[buf][1][e] = b[k >> 6];
-                }
+            const int k0 = h - 4;
+            const int e = (lane - k0) & 63;
+            const int k = k0 + e;
+            const int slo = k0 < 0 ? 0 : k0 >> 6, shi = (h + 1) >> 6;
+            const int32_t alo = a[slo], ahi = a[shi], blo = b[slo], bhi = b[shi];
+            if (e < kGcdSeg) {
+                const bool up = (k >> 6) != slo;
+                sSeg[buf][0][e] = k < 0 ? 0 : (up ? ahi : alo);
+                sSeg[buf][1][e] = k < 0 ? 0 : (up ? bhi : blo);
             }
             if (lane0) sTop[buf] = h;
         };
@@ -429,11 +416,12 @@ __global__ __launch_bounds__(128) void gcd_kernel(const uint32_t* __restrict__ Y
         __syncthreads();
         for (int r = 1;; r++) {
             __syncthreads();  // matrix r is ready (and the window after matrix r - 1 was read)
-            const int buf = r & 1;
-            if (sCmd[buf] != 0) break;
-            const int32_t A = sM[buf][0], B = sM[buf][1], C = sM[buf][2], D = sM[buf][3];
+            const int4 m = sM[r & 1];
+            const int32_t A = __builtin_amdgcn_readfirstlane(m.x), B = __builtin_amdgcn_readfirstlane(m.y);
+            const int32_t C = __builtin_amdgcn_readfirstlane(m.z), D = __builtin_amdgcn_readfirstlane(m.w);
+            if ((A | B | C | D) == 0) break;
             if (!(A == 1 && B == 0 && C == 0 && D == 1)) limb_apply<CW>(a, b, A, B, C, D, ns, lane0);
-            hand_over(buf);
+            hand_over(r & 1);
         }
         return;
     }
@@ -444,9 +432,11 @@ __global__ __launch_bounds__(128) void gcd_kernel(const uint32_t* __restrict__ Y
     int32_t wa = 0, wb = 0;
     int base = 0;
     auto read_window = [&](int buf) {
-        wa = lane < kGcdSeg ? sSeg[buf][0][lane] : 0;
-        wb = lane < kGcdSeg ? sSeg[buf][1][lane] : 0;
-        base = sTop[buf] - 4;
+        const int e = lane < kGcdSeg ? lane : kGcdSeg - 1;
+        const int32_t va = sSeg[buf][0][e], vb = sSeg[buf][1][e];
+        wa = lane < kGcdSeg ? va : 0;
+        wb = lane < kGcdSeg ? vb : 0;
+        base = __builtin_amdgcn_readfirstlane(sTop[buf]) - 4;
     };
     read_window(0);
     int32_t M0 = 1, M1 = 0, M2 = 0, M3 = 1;  // the matrix issued last (applied by now to the limbs)
@@ -470,10 +460,10 @@ __global__ __launch_bounds__(128) void gcd_kernel(const uint32_t* __restrict__ Y
         const uint64_t nzm = __ballot((wa != 0 || wb != 0) && lane >= lo_lane && lane <= kGcdSeg);
         const int top = nzm ? 63 - __builtin_clzll(nzm) : -1;  // lane of the top limb
         const int h = base + top;
-        int cmd = 0;
+        bool stop = false;
         int32_t nM[4] = {1, 0, 0, 1};
         if (r > max_rounds || top < 0 || h >= 64 * CW - 3) {
-            cmd = 1;  // no progress in sight, no limb in view or no headroom left: the host finishes
+            stop = true;  // no progress in sight, no limb in view or no headroom left: the host finishes
         } else if (h <= 3 && base + lo_lane <= 0) {
             // exact values from limbs 0..3, then the binary gcd
             __int128 va = 0, vb = 0;
@@ -509,70 +499,69 @@ __global__ __launch_bounds__(128) void gcd_kernel(const uint32_t* __restrict__ Y
                 g = (uint64_t)u;
                 result = 0;
             }
-            cmd = 1;
+            stop = true;
         } else if (top - 2 < lo_lane || h <= 3) {
             // the window lacks the limbs the leading parts (or the last four
             // limbs) need: issue the identity and read a fresh window
         } else {
-            // leading parts from limbs h, h - 1, h - 2
-            double fa = fma(fma((double)__builtin_amdgcn_readlane(wa, top), 0x1p30,
-                                (double)__builtin_amdgcn_readlane(wa, top - 1)),
-                            0x1p30, (double)__builtin_amdgcn_readlane(wa, top - 2));
-            double fb = fma(fma((double)__builtin_amdgcn_readlane(wb, top), 0x1p30,
-                                (double)__builtin_amdgcn_readlane(wb, top - 1)),
-                            0x1p30, (double)__builtin_amdgcn_readlane(wb, top - 2));
-            const int32_t ga = fa < 0.0 ? -1 : 1, gb = fb < 0.0 ? -1 : 1;  // signs folded into the matrix
-            fa = fabs(fa);
-            fb = fabs(fb);
+            // leading parts from limbs h, h - 1, h - 2; their signs start the
+            // cofactor matrix, so the steps run on magnitudes
+            const double fa = fma(fma((double)__builtin_amdgcn_readlane(wa, top), 0x1p30,
+                                      (double)__builtin_amdgcn_readlane(wa, top - 1)),
+                                  0x1p30, (double)__builtin_amdgcn_readlane(wa, top - 2));
+            const double fb = fma(fma((double)__builtin_amdgcn_readlane(wb, top), 0x1p30,
+                                      (double)__builtin_amdgcn_readlane(wb, top - 1)),
+                                  0x1p30, (double)__builtin_amdgcn_readlane(wb, top - 2));
             int ex;
-            (void)frexp(fmax(fa, fb), &ex);
-            double x = floor(ldexp(fa, 52 - ex)), y = floor(ldexp(fb, 52 - ex));
-            double A = 1.0, B = 0.0, C = 0.0, D = 1.0;
+            (void)frexp(fmax(fabs(fa), fabs(fb)), &ex);
+            double x = floor(ldexp(fabs(fa), 52 - ex)), y = floor(ldexp(fabs(fb), 52 - ex));
+            double xs = x * (1.0 - 0x1p-22);
+            double A = fa < 0.0 ? -1.0 : 1.0, B = 0.0, C = 0.0, D = fb < 0.0 ? -1.0 : 1.0;
             int steps = 0;
             for (int it = 0; it < 16; it++) {
-                double x1, y1, A1, B1, C1, D1, x2, y2, A2, B2, C2, D2;
-                double x3, y3, A3, B3, C3, D3, x4, y4, A4, B4, C4, D4;
-                const bool o1 = euclid_step(x, y, A, B, C, D, x1, y1, A1, B1, C1, D1);
-                const bool o2 = euclid_step(x1, y1, A1, B1, C1, D1, x2, y2, A2, B2, C2, D2) && o1;
-                const bool o3 = euclid_step(x2, y2, A2, B2, C2, D2, x3, y3, A3, B3, C3, D3) && o2;
-                const bool o4 = euclid_step(x3, y3, A3, B3, C3, D3, x4, y4, A4, B4, C4, D4) && o3;
-                if (__ballot(o4) != 0) {
-                    x = x4, y = y4, A = A4, B = B4, C = C4, D = D4;
+                // four steps; divisors y, y1, y2, y3; new rows (C1, D1) .. (C4, D4)
+                double s1, y1, C1, D1, s2, y2, C2, D2, s3, y3, C3, D3, s4, y4, C4, D4;
+                euclid_step(x, xs, y, A, B, C, D, s1, y1, C1, D1);
+                euclid_step(y, s1, y1, C, D, C1, D1, s2, y2, C2, D2);
+                euclid_step(y1, s2, y2, C1, D1, C2, D2, s3, y3, C3, D3);
+                euclid_step(y2, s3, y3, C2, D2, C3, D3, s4, y4, C4, D4);
+                if ((fmin(y2, y3) >= 0x1p26) & (row_max(C3, D3, C4, D4) < 0x1p26)) {
+                    x = y3, xs = s4, y = y4;
+                    A = C3, B = D3, C = C4, D = D4;
                     steps += 4;
                     continue;
                 }
-                if (__ballot(o3) != 0) {
-                    A = A3, B = B3, C = C3, D = D3;
+                // the last block: keep its longest acceptable prefix
+                if ((fmin(y1, y2) >= 0x1p26) & (row_max(C2, D2, C3, D3) < 0x1p26)) {
+                    A = C2, B = D2, C = C3, D = D3;
                     steps += 3;
-                } else if (__ballot(o2) != 0) {
-                    A = A2, B = B2, C = C2, D = D2;
+                } else if ((fmin(y, y1) >= 0x1p26) & (row_max(C1, D1, C2, D2) < 0x1p26)) {
+                    A = C1, B = D1, C = C2, D = D2;
                     steps += 2;
-                } else if (__ballot(o1) != 0) {
-                    A = A1, B = B1, C = C1, D = D1;
+                } else if ((y >= 0x1p26) & (row_max(C1, D1, C1, D1) < 0x1p26)) {
+                    A = C, B = D, C = C1, D = D1;
                     steps += 1;
                 }
                 break;
             }
             if (steps == 0) {
-                cmd = 1;  // no certain progress: the host finishes
+                stop = true;  // no certain progress: the host finishes
             } else {
-                nM[0] = (int32_t)A * ga;
-                nM[1] = (int32_t)B * gb;
-                nM[2] = (int32_t)C * ga;
-                nM[3] = (int32_t)D * gb;
+                nM[0] = (int32_t)A;
+                nM[1] = (int32_t)B;
+                nM[2] = (int32_t)C;
+                nM[3] = (int32_t)D;
             }
         }
         const int buf = r & 1;
-        if (lane0) {
-            sCmd[buf] = cmd;
-            sM[buf][0] = nM[0], sM[buf][1] = nM[1], sM[buf][2] = nM[2], sM[buf][3] = nM[3];
-        }
+        if (lane0) sM[buf] = stop ? make_int4(0, 0, 0, 0) : make_int4(nM[0], nM[1], nM[2], nM[3]);
         __syncthreads();  // matrix r is ready; the window after matrix r - 1 is ready
-        if (cmd != 0) break;
+        if (stop) break;
         // the window handed over after matrix r - 1; the next iteration
         // applies matrix r to it
         read_window(buf ^ 1);
-        M0 = nM[0], M1 = nM[1], M2 = nM[2], M3 = nM[3];
+        M0 = __builtin_amdgcn_readfirstlane(nM[0]), M1 = __builtin_amdgcn_readfirstlane(nM[1]);
+        M2 = __builtin_amdgcn_readfirstlane(nM[2]), M3 = __builtin_amdgcn_readfirstlane(nM[3]);
     }
     if (lane0) {
         gstat[j] = result;
