@@ -407,6 +407,35 @@ BigInt divexact(const BigInt& a, const BigInt& b) {
     return q;
 }
 
+// Exact division by one word: the factor 2^t of b shifts out, then the odd
+// part's inverse modulo 2^64 (Newton's iteration, each pass doubling the
+// correct low bits from 3) turns the division into a product, limb by limb
+// from the bottom, carrying the high words of q_i b' as a borrow (Hensel).
+BigInt divexact_u64(const BigInt& a, uint64_t b) {
+    if (b == 0) throw std::domain_error("division by zero");
+    const int t = __builtin_ctzll(b);
+    const uint64_t bo = b >> t;
+    uint64_t inv = bo;
+    for (int i = 0; i < 5; i++) inv *= 2 - bo * inv;
+    const size_t n = a.size();
+    BigInt q;
+    q.d.resize(n);
+    uint64_t borrow = 0;
+    for (size_t i = 0; i < n; i++) {
+        // limb i of a >> t
+        const uint64_t ai = t ? (a.d[i] >> t) | (i + 1 < n ? a.d[i + 1] << (64 - t) : 0) : a.d[i];
+        if (t && (i == 0) && (a.d[0] & ((1ULL << t) - 1))) throw std::logic_error("inexact division");
+        const uint64_t s = ai - borrow;
+        const uint64_t qi = s * inv;
+        borrow = (uint64_t)(((u128)qi * bo) >> 64) + (ai < borrow);
+        q.d[i] = qi;
+    }
+    if (borrow != 0) throw std::logic_error("inexact division");
+    q.trim();
+    q.neg = a.neg && !q.is_zero();
+    return q;
+}
+
 BigInt pow_u(const BigInt& a, unsigned e) {
     BigInt result = BigInt::from_u64(1), base = a;
     while (e) {
@@ -456,6 +485,70 @@ static bool lehmer_matrix(int64_t xh, int64_t yh, int64_t* A, int64_t* B, int64_
 }
 
 static void lincomb_rem(limb_t* x, limb_t* y, size_t n, int64_t A, int64_t B, int64_t C, int64_t D);
+
+// u128 to double, within about 2^-52 relative
+static inline double u128_to_double(u128 v) {
+    return (double)(uint64_t)(v >> 64) * 0x1p64 + (double)(uint64_t)v;
+}
+
+// floor(num / den) for num < 2^127, 0 < den < 2^127, when it is below 2^40
+// (false otherwise): a double estimate within one of it, then exact
+// corrections (the products stay below num + den)
+static bool small_quotient(u128 num, u128 den, uint64_t* q) {
+    const double e = u128_to_double(num) / u128_to_double(den);
+    if (!(e < 0x1p40)) return false;
+    uint64_t qe = (uint64_t)e;
+    u128 prod = (u128)qe * den;
+    while (prod > num) {
+        qe--;
+        prod -= den;
+    }
+    while (num - prod >= den) {
+        qe++;
+        prod += den;
+    }
+    if (qe >> 40) return false;
+    *q = qe;
+    return true;
+}
+
+// Algorithm L on two-word leading parts x >= y (below 2^124, taken at the
+// same bit position): the cofactor matrix of as many Euclidean steps as
+// they determine, each quotient accepted when both bounds of the true
+// ratio, (x + A) / (y + C) and (x + B) / (y + D), give it.  The cofactor
+// magnitudes stay below 2^62 (so a matrix covers about 62 bits, twice the
+// one-word form).  Returns false when not even one step is certain.
+static bool lehmer_matrix2(u128 xh, u128 yh, int64_t* A, int64_t* B, int64_t* C, int64_t* D) {
+    int64_t a = 1, b = 0, c = 0, d = 1;
+    i128 x = (i128)xh, y = (i128)yh;
+    for (;;) {
+        const i128 den1 = y + c, den2 = y + d;
+        if (den1 <= 0 || den2 <= 0) break;
+        const i128 num1 = x + a, num2 = x + b;
+        if (num1 < 0 || num2 < 0) break;
+        uint64_t q, q2;
+        if (!small_quotient((u128)num1, (u128)den1, &q) || !small_quotient((u128)num2, (u128)den2, &q2) ||
+            q != q2)
+            break;
+        // |a - q c| <= |a| + q |c| (equal, as the signs alternate), likewise for b, d
+        const u128 mc = (u128)(a < 0 ? -(i128)a : (i128)a) + (u128)q * (u128)(c < 0 ? -(i128)c : (i128)c);
+        const u128 md = (u128)(b < 0 ? -(i128)b : (i128)b) + (u128)q * (u128)(d < 0 ? -(i128)d : (i128)d);
+        if ((mc >> 62) != 0 || (md >> 62) != 0) break;
+        const int64_t nc = (int64_t)((i128)a - (i128)q * c), nd = (int64_t)((i128)b - (i128)q * d);
+        a = c;
+        c = nc;
+        b = d;
+        d = nd;
+        const i128 ny = x - (i128)q * y;  // |q y| < 2^126: q < 2^40 and y below 2^124
+        x = y;
+        y = ny;
+    }
+    *A = a;
+    *B = b;
+    *C = c;
+    *D = d;
+    return b != 0;
+}
 
 // (x, y) <- (A x + B y, C x + D y) in place, for nonnegative x, y whose
 // images are nonnegative (guaranteed by Algorithm L).
@@ -584,9 +677,41 @@ bool rational_reconstruct(const BigInt& a, const BigInt& M, const BigInt& N, con
     bool t1neg = false;  // t0 has the other sign (or is 0)
     const size_t nbits = N.bit_length();
     auto above_N = [&]() { return cmp_limbs(r1.data(), n1, N.d.data(), N.size()) > 0; };
+    // a Lehmer matrix applied to the remainders and the cofactor magnitudes
+    auto apply = [&](int64_t A, int64_t B, int64_t C, int64_t D2) {
+        lincomb_rem(r0.data(), r1.data(), n0, A, B, C, D2);
+        n0 = trimmed(r0.data(), n0);
+        n1 = trimmed(r1.data(), n0 > n1 ? n0 : n1);
+        const uint64_t ua = (uint64_t)(A < 0 ? -A : A), ub = (uint64_t)(B < 0 ? -B : B);
+        const uint64_t uc = (uint64_t)(C < 0 ? -C : C), ud = (uint64_t)(D2 < 0 ? -D2 : D2);
+        nt = lincomb_mag(t0.data(), t1.data(), nt, ua, ub, uc, ud);
+        if (D2 < 0) t1neg = !t1neg;
+        if (cmp_limbs(r0.data(), n0, N.d.data(), N.size()) <= 0)
+            throw std::logic_error("Lehmer step passed the stopping point");
+    };
     while (above_N()) {
         const size_t b0 = bits_of(r0.data(), n0);
-        if (bits_of(r1.data(), n1) > nbits + 64 && n0 > 1) {
+        const size_t b1 = bits_of(r1.data(), n1);
+        if (b1 > nbits + 130 && b0 > 124) {
+            // two-word leading parts: the top 124 bits of r0 and the bits of
+            // r1 at the same position (a matrix of up to 62-bit cofactors
+            // shrinks r0 by at most about 2^64, so it stops above N)
+            const size_t sh = b0 - 124;
+            auto lead2 = [&](const std::vector<limb_t>& v, size_t nv) -> u128 {
+                const size_t w = sh / 64, o = sh % 64;
+                auto word = [&](size_t i) -> uint64_t { return i < nv ? v[i] : 0; };
+                u128 lo = ((u128)word(w + 1) << 64) | word(w);
+                if (o) lo = (lo >> o) | ((u128)word(w + 2) << (128 - o));
+                return lo & (((u128)1 << 124) - 1);
+            };
+            const u128 xh = lead2(r0, n0), yh = lead2(r1, n1);
+            int64_t A, B, C, D2;
+            if (yh != 0 && lehmer_matrix2(xh, yh, &A, &B, &C, &D2)) {
+                apply(A, B, C, D2);
+                continue;
+            }
+        }
+        if (b1 > nbits + 64 && n0 > 1) {
             // leading 62 bits of r0 and the bits of r1 at the same position
             const size_t sh = b0 - 62;
             auto lead = [&](const std::vector<limb_t>& v, size_t nv) -> int64_t {
@@ -599,15 +724,7 @@ bool rational_reconstruct(const BigInt& a, const BigInt& M, const BigInt& N, con
             const int64_t xh = lead(r0, n0), yh = lead(r1, n1);
             int64_t A, B, C, D2;
             if (yh != 0 && lehmer_matrix(xh, yh, &A, &B, &C, &D2)) {
-                lincomb_rem(r0.data(), r1.data(), n0, A, B, C, D2);
-                n0 = trimmed(r0.data(), n0);
-                n1 = trimmed(r1.data(), n0 > n1 ? n0 : n1);
-                const uint64_t ua = (uint64_t)(A < 0 ? -A : A), ub = (uint64_t)(B < 0 ? -B : B);
-                const uint64_t uc = (uint64_t)(C < 0 ? -C : C), ud = (uint64_t)(D2 < 0 ? -D2 : D2);
-                nt = lincomb_mag(t0.data(), t1.data(), nt, ua, ub, uc, ud);
-                if (D2 < 0) t1neg = !t1neg;
-                if (cmp_limbs(r0.data(), n0, N.d.data(), N.size()) <= 0)
-                    throw std::logic_error("Lehmer step passed the stopping point");
+                apply(A, B, C, D2);
                 continue;
             }
         }

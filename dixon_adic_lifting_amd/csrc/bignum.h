@@ -44,6 +44,7 @@ void divmod_trunc(const BigInt& a, const BigInt& b, BigInt* q, BigInt* r);
 // r = a mod m in [0, m) for m > 0
 BigInt mod_floor(const BigInt& a, const BigInt& m);
 BigInt divexact(const BigInt& a, const BigInt& b);  // a / b, exact (checked)
+BigInt divexact_u64(const BigInt& a, uint64_t b);  // a / b for 0 < b < 2^64, exact (checked)
 BigInt shl(const BigInt& a, size_t bits);
 BigInt shr_abs(const BigInt& a, size_t bits);       // |a| >> bits
 BigInt pow_u(const BigInt& a, unsigned e);

@@ -73,6 +73,17 @@ struct PinnedStage {
 };
 thread_local PinnedStage g_pinned_stage;
 
+// Marks the arrival of the numerator words on the host, per thread (kept
+// until the process ends).
+struct ReadyEvent {
+    hipEvent_t e = nullptr;
+    hipEvent_t get() {
+        if (!e && hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) e = nullptr;
+        return e;
+    }
+};
+thread_local ReadyEvent g_words_ready;
+
 // little-endian 32-bit words of a nonnegative BigInt, zero-padded to nw
 void to_words(const BigInt& v, uint32_t* w, int nw) {
     for (int i = 0; i < nw; i++) {
@@ -251,6 +262,8 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
     // weight seeds T_i = P^i d mod M (host), weight rows, GEMM, numerators
     // and gcds (GPU), results to the pinned arrays.
     bool gpu_gcd = false;
+    hipEvent_t words_ready = g_words_ready.get();
+    if (!words_ready) return ES_EHIP;
     auto gpu_pass = [&]() -> int {
         // the chain T_{i+1} = T_i P mod M, cut into segments that each start
         // from P^{i0} d mod M = (d mod P^{m - i0}) P^{i0} (M = P^m: the
@@ -286,6 +299,12 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
             ev = kt->start(KC_RECON_OTHER);
             HIPOK(launch_numer(VT, pl.Ncolsp, rowsum, rows, Mwd, TM, Mtop, nbits, Yd, std_, st));
             kt->stop(ev);
+            // the numerator words leave before the gcds, so the host converts
+            // them while the gcd kernel runs
+            HIPOK(hipMemcpyAsync(Yh + j0 * nw, Yd, (size_t)rows * nw * sizeof(uint32_t), hipMemcpyDeviceToHost,
+                                 st));
+            HIPOK(hipMemcpyAsync(sth + j0, std_, (size_t)rows * sizeof(int), hipMemcpyDeviceToHost, st));
+            HIPOK(hipEventRecord(words_ready, st));
             if (gpu_gcd) {
                 ev = kt->start(KC_RECON_GCD);
                 HIPOK(launch_gcd(Yd, nw, std_, rows, Dwd, nwd, Gd, gstd, st));
@@ -293,38 +312,46 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
                 HIPOK(hipMemcpyAsync(Gh + j0, Gd, (size_t)rows * sizeof(uint64_t), hipMemcpyDeviceToHost, st));
                 HIPOK(hipMemcpyAsync(gsth + j0, gstd, (size_t)rows * sizeof(int), hipMemcpyDeviceToHost, st));
             }
-            HIPOK(hipMemcpyAsync(Yh + j0 * nw, Yd, (size_t)rows * nw * sizeof(uint32_t), hipMemcpyDeviceToHost,
-                                 st));
-            HIPOK(hipMemcpyAsync(sth + j0, std_, (size_t)rows * sizeof(int), hipMemcpyDeviceToHost, st));
         }
-        HIPOK(hipStreamSynchronize(st));
-        if (!gpu_gcd)
-            for (size_t j = 0; j < NC; j++) gsth[j] = 1;
-        lap(tm ? &tm->gpu_ms : nullptr, "gpu");
         return ES_OK;
     };
 
-    // Lowest terms for the components of `which` that the last pass accepted.
+    // The components of `which` that the last pass accepted: first y / d
+    // from the numerator words (while the gcds run), then lowest terms
+    // where the gcd is not 1.
     std::atomic<size_t> host_gcds{0};
-    auto finish = [&](const std::vector<size_t>& which) {
+    auto convert = [&](const std::vector<size_t>& which) {
         parallel_for_each(which.size(), nthreads, [&](size_t k) {
             const size_t j = which[k];
             if (sth[j] != 0 && sth[j] != 1) return;
-            BigInt y = from_words(Yh + j * nw, nw, sth[j] == 1);
-            BigInt g;
+            out->num[j] = from_words(Yh + j * nw, nw, sth[j] == 1);
+            out->den[j] = d;
+        });
+    };
+    auto reduce = [&](const std::vector<size_t>& which) {
+        std::vector<size_t> need;
+        std::vector<uint64_t> gs;  // the distinct one-word gcds other than 1
+        for (size_t j : which) {
+            if ((sth[j] != 0 && sth[j] != 1) || (gsth[j] == 0 && Gh[j] == 1)) continue;
+            need.push_back(j);
+            if (gsth[j] == 0) gs.push_back(Gh[j]);
+        }
+        std::sort(gs.begin(), gs.end());
+        gs.erase(std::unique(gs.begin(), gs.end()), gs.end());
+        std::vector<BigInt> dg(gs.size());  // d / g for each of them
+        parallel_for_each(gs.size(), nthreads, [&](size_t k) { dg[k] = divexact_u64(d, gs[k]); });
+        parallel_for_each(need.size(), nthreads, [&](size_t k) {
+            const size_t j = need[k];
             if (gsth[j] == 0) {
-                g = BigInt::from_u64(Gh[j]);
-            } else {
-                g = gcd(y, d);
-                host_gcds++;
+                out->num[j] = divexact_u64(out->num[j], Gh[j]);
+                out->den[j] = dg[(size_t)(std::lower_bound(gs.begin(), gs.end(), Gh[j]) - gs.begin())];
+                return;
             }
-            if (g.size() == 1 && g.d[0] == 1) {
-                out->num[j] = std::move(y);
-                out->den[j] = d;
-            } else {
-                out->num[j] = divexact(y, g);
-                out->den[j] = divexact(d, g);
-            }
+            const BigInt g = gcd(out->num[j], d);
+            host_gcds++;
+            if (g.size() == 1 && g.d[0] == 1) return;
+            out->num[j] = divexact(out->num[j], g);
+            out->den[j] = divexact(d, g);
         });
     };
 
@@ -356,7 +383,13 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
     for (int pass = 0;; pass++) {
         int rc = gpu_pass();
         if (rc != ES_OK) return rc;
-        finish(todo);
+        HIPOK(hipEventSynchronize(words_ready));
+        convert(todo);
+        HIPOK(hipStreamSynchronize(st));
+        if (!gpu_gcd)
+            for (size_t j = 0; j < NC; j++) gsth[j] = 1;
+        lap(tm ? &tm->gpu_ms : nullptr, "gpu");
+        reduce(todo);
         std::vector<size_t> failed;
         for (size_t j : todo)
             if (sth[j] != 0 && sth[j] != 1) failed.push_back(j);
@@ -387,6 +420,9 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
         d = lcm(d, de);
         todo.swap(failed);
     }
+    if (verbose())
+        fprintf(stderr, "[es] gpu reconstruct: %zu gcds finished on the host, %zu components alone\n",
+                (size_t)host_gcds, failed_total);
     if (tm) {
         tm->failed = failed_total;
         tm->host_gcds = host_gcds;
