@@ -255,16 +255,25 @@ int run_lift(const int64_t* dA, const int64_t* db, uint8_t* ws, hipStream_t st, 
     fill_lift_params(ls, &prm);
     HIP_CHECK(hipMemcpyAsync(ws + L.off_params, &prm, sizeof prm, hipMemcpyHostToDevice, st));
     HIP_CHECK(launch_split_b(db, L, ws, ls.E, st));
+    const bool fused = lift_fused_fits(L);
+    if (fused) HIP_CHECK(launch_lift_rows(L, ws, ls.E, st));
     const size_t NC = (size_t)L.n * L.c;
     for (int i0 = 0; i0 < m; i0 += L.kchunk) {
         const int cnt = std::min(L.kchunk, m - i0);
         for (int s = 0; s < cnt; s++) {
-            long ev = prof->start(KC_CONTRACT);
-            HIP_CHECK(launch_lift_contract(L, ws, ls.E, st));
-            prof->stop(ev);
-            ev = prof->start(KC_CRT);
-            HIP_CHECK(launch_lift_crt(L, ws, s, st));
-            prof->stop(ev);
+            long ev;
+            if (fused) {
+                ev = prof->start(KC_CONTRACT);
+                HIP_CHECK(launch_lift_contract_crt(L, ws, ls.E, s, st));
+                prof->stop(ev);
+            } else {
+                ev = prof->start(KC_CONTRACT);
+                HIP_CHECK(launch_lift_contract(L, ws, ls.E, st));
+                prof->stop(ev);
+                ev = prof->start(KC_CRT);
+                HIP_CHECK(launch_lift_crt(L, ws, s, st));
+                prof->stop(ev);
+            }
             ev = prof->start(KC_RESIDUAL);
             HIP_CHECK(launch_lift_residual(L, ws, pr.a32, dA, st));
             prof->stop(ev);

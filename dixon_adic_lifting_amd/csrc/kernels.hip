@@ -23,8 +23,9 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
-#include <type_traits>
 #include <cstdlib>
+#include <string>
+#include <type_traits>
 
 #include "es_internal.h"
 
@@ -1585,46 +1586,48 @@ __device__ __forceinline__ double quad_add(double v) {
     return v + __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
 }
 
-__global__ __launch_bounds__(256) void crt_kernel(const LiftParams* __restrict__ prm, const uint8_t* __restrict__ U,
-                                                  int NC, uint64_t* __restrict__ digits, int kchunk, int slot,
-                                                  uint64_t* __restrict__ xlow) {
-    __shared__ double Wd[kNumPrimes][kDigitWords];
-    __shared__ double qrec[kNumPrimes];
-    __shared__ uint32_t qc[kNumPrimes][3];  // q, mu16, c
-    const int E = prm->E;
-    for (int i = threadIdx.x; i < kNumPrimes * kDigitWords; i += 256) (&Wd[0][0])[i] = (&prm->Wd[0][0])[i];
-    if (threadIdx.x < kNumPrimes) {
-        const int l = threadIdx.x;
-        qrec[l] = prm->qrec[l];
-        qc[l][0] = prm->q[l];
-        qc[l][1] = prm->mu16[l];
-        qc[l][2] = prm->cinv[l];
+// the CRT constants of the live primes, staged in LDS
+struct CrtTables {
+    double Wd[kNumPrimes][kDigitWords];
+    double qrec[kNumPrimes];
+    uint32_t qc[kNumPrimes][3];  // q, mu16, c
+};
+
+__device__ __forceinline__ void load_crt_tables(CrtTables& T, const LiftParams* __restrict__ prm, int tid,
+                                                int nthreads) {
+    for (int i = tid; i < kNumPrimes * kDigitWords; i += nthreads) (&T.Wd[0][0])[i] = (&prm->Wd[0][0])[i];
+    for (int l = tid; l < kNumPrimes; l += nthreads) {
+        T.qrec[l] = prm->qrec[l];
+        T.qc[l][0] = prm->q[l];
+        T.qc[l][1] = prm->mu16[l];
+        T.qc[l][2] = prm->cinv[l];
     }
-    __syncthreads();
-    const int s = threadIdx.x & 15;
-    const int comp = blockIdx.x * 16 + (threadIdx.x >> 4);
-    if (comp >= NC) return;  // the component's sixteen lanes leave together
-    constexpr int LPL = (kNumPrimes + 15) / 16;  // primes per lane
-    uint32_t res[LPL];
-#pragma unroll
-    for (int i = 0; i < LPL; i++) {
-        const int l = s + 16 * i;
-        res[i] = l < E ? U[(size_t)l * NC + comp] : 0u;
-    }
+}
+
+constexpr int kCrtLanes = 16;                                          // lanes per component
+constexpr int kCrtPrimesPerLane = (kNumPrimes + kCrtLanes - 1) / kCrtLanes;
+
+// The digit of one component from its residues: lane s of the component's
+// sixteen holds res[i] = r_l for l = s + 16 i (l < E).  Writes the digit
+// (twelve words) into slot `slot` of the component's chunk and x mod 2^64.
+__device__ __forceinline__ void crt_digit(const CrtTables& T, const LiftParams* __restrict__ prm, int E, int s,
+                                          const uint32_t (&res)[kCrtPrimesPerLane], int comp,
+                                          uint64_t* __restrict__ digits, int kchunk, int slot,
+                                          uint64_t* __restrict__ xlow) {
     double acc[kDigitWords];
 #pragma unroll
     for (int w = 0; w < kDigitWords; w++) acc[w] = 0.0;
     double f = 0.0;
 #pragma unroll
-    for (int i = 0; i < LPL; i++) {
-        const int l = s + 16 * i;
+    for (int i = 0; i < kCrtPrimesPerLane; i++) {
+        const int l = s + kCrtLanes * i;
         if (l >= E) continue;
-        const uint32_t q = qc[l][0];
-        const uint32_t u = red16(res[i] * qc[l][2], q, qc[l][1]);
+        const uint32_t q = T.qc[l][0];
+        const uint32_t u = red16(res[i] * T.qc[l][2], q, T.qc[l][1]);
         const double ud = (double)(u > (q >> 1) ? (int)u - (int)q : (int)u);
-        f = fma(ud, qrec[l], f);
+        f = fma(ud, T.qrec[l], f);
 #pragma unroll
-        for (int w = 0; w < kDigitWords; w++) acc[w] = fma(ud, Wd[l][w], acc[w]);
+        for (int w = 0; w < kDigitWords; w++) acc[w] = fma(ud, T.Wd[l][w], acc[w]);
     }
     f = quad_add<8>(quad_add<4>(quad_add<2>(quad_add<1>(f))));
 #pragma unroll
@@ -1671,6 +1674,120 @@ __global__ __launch_bounds__(256) void crt_kernel(const LiftParams* __restrict__
     dst[1] = make_uint4(x[4], x[5], x[6], x[7]);
     dst[2] = make_uint4(x[8], x[9], x[10], x[11]);
     xlow[comp] = ((uint64_t)x[1] << 32) | x[0];
+}
+
+__global__ __launch_bounds__(256) void crt_kernel(const LiftParams* __restrict__ prm, const uint8_t* __restrict__ U,
+                                                  int NC, uint64_t* __restrict__ digits, int kchunk, int slot,
+                                                  uint64_t* __restrict__ xlow) {
+    __shared__ CrtTables T;
+    const int E = prm->E;
+    load_crt_tables(T, prm, threadIdx.x, 256);
+    __syncthreads();
+    const int s = threadIdx.x & (kCrtLanes - 1);
+    const int comp = blockIdx.x * (256 / kCrtLanes) + threadIdx.x / kCrtLanes;
+    if (comp >= NC) return;  // the component's sixteen lanes leave together
+    uint32_t res[kCrtPrimesPerLane];
+#pragma unroll
+    for (int i = 0; i < kCrtPrimesPerLane; i++) {
+        const int l = s + kCrtLanes * i;
+        res[i] = l < E ? U[(size_t)l * NC + comp] : 0u;
+    }
+    crt_digit(T, prm, E, s, res, comp, digits, kchunk, slot, xlow);
+}
+
+// ---------------------------------------------------------------- lift: contraction + CRT, one right-hand side
+// For one right-hand side with rows of at least 1 KB, the contraction and
+// the CRT share a launch: a block owns kFusedComps components and forms
+// every live prime's residue for them, so the residues stay in LDS and the
+// CRT follows in the same block.  Row k of B_j (in component order) is row
+// comprow[j][k] of the elimination's result.  The block's rows (prime, component)
+// go eight to a wave as in the plain contraction (the sums meet in the same
+// transposed butterfly); the last wave's tail rows are duplicates whose
+// results are dropped.
+
+// Row index of B_j for each component, per live prime: the inverse of rowpos.
+__global__ __launch_bounds__(256) void lift_rows_kernel(const int* __restrict__ rowpos, const LiftParams* __restrict__ prm,
+                                                        int n, int* __restrict__ comprow) {
+    const int jl = blockIdx.y;
+    const int J = prm->qidx[jl];
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) comprow[(size_t)jl * n + rowpos[(size_t)J * n + i]] = i;
+}
+
+template <int kFusedComps, int kFusedWaves>
+__global__ __launch_bounds__(kFusedWaves * 64) void lift_gemv_crt_kernel(
+    const int8_t* __restrict__ S, int n, int pitch, const int8_t* __restrict__ rho,
+    const LiftParams* __restrict__ prm, const int* __restrict__ comprow, uint64_t* __restrict__ digits, int kchunk,
+    int slot, uint64_t* __restrict__ xlow) {
+    __shared__ CrtTables T;
+    __shared__ uint32_t sU[kNumPrimes][kFusedComps];
+    const int E = prm->E;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int c0 = blockIdx.x * kFusedComps;
+    load_crt_tables(T, prm, threadIdx.x, kFusedWaves * 64);
+    const int nrows = E * kFusedComps;
+    for (int rb = wave * 8; rb < nrows; rb += kFusedWaves * 8) {
+        // rows rb .. rb + 7 (row r: prime r / kFusedComps, component r mod kFusedComps)
+        const int8_t* rowp[8];
+#pragma unroll
+        for (int r = 0; r < 8; r++) {
+            const int rr = min(rb + r, nrows - 1);
+            const int jl = rr / kFusedComps, comp = min(c0 + rr % kFusedComps, n - 1);
+            const int J = prm->qidx[jl];
+            const int row = min((unsigned)comprow[(size_t)jl * n + comp], (unsigned)(n - 1));  // a permutation; clamped all the same
+            rowp[r] = S + ((size_t)J * n + row) * pitch;
+        }
+        // the batch's primes: row r takes prime rb / kFusedComps + r / kFusedComps
+        constexpr int NP = kFusedComps >= 8 ? 1 : 8 / kFusedComps;
+        const int8_t* rvp[NP];
+#pragma unroll
+        for (int p = 0; p < NP; p++) rvp[p] = rho + (size_t)min(rb / kFusedComps + p, E - 1) * pitch;
+        int acc[8];
+#pragma unroll
+        for (int r = 0; r < 8; r++) acc[r] = 0;
+        for (int col0 = 0; col0 < pitch; col0 += 1024) {
+            const int col = col0 + lane * 16;
+            const bool cin = col < pitch;
+            const int colc = cin ? col : col0;
+            uint4 rvs[NP];
+#pragma unroll
+            for (int p = 0; p < NP; p++) rvs[p] = cin ? *(const uint4*)(rvp[p] + colc) : make_uint4(0, 0, 0, 0);
+            uint4 sv[8];
+#pragma unroll
+            for (int r = 0; r < 8; r++) sv[r] = *(const uint4*)(rowp[r] + colc);
+#pragma unroll
+            for (int r = 0; r < 8; r++) {
+                const uint4 rv = rvs[NP == 1 ? 0 : r / kFusedComps];
+                int a = acc[r];
+                a = __builtin_amdgcn_sdot4((int)sv[r].x, (int)rv.x, a, false);
+                a = __builtin_amdgcn_sdot4((int)sv[r].y, (int)rv.y, a, false);
+                a = __builtin_amdgcn_sdot4((int)sv[r].z, (int)rv.z, a, false);
+                a = __builtin_amdgcn_sdot4((int)sv[r].w, (int)rv.w, a, false);
+                acc[r] = a;
+            }
+        }
+        wave_sum_rows<8>(acc, lane);
+        if ((lane & 7) == 0) {
+            const int rr = rb + ((lane >> 3) & 7);
+            if (rr < nrows) {
+                const int jl = rr / kFusedComps;
+                sU[jl][rr % kFusedComps] = mod_i32(acc[0], prm->q[jl], prm->mu32[jl]);
+            }
+        }
+    }
+    __syncthreads();
+    // the CRT: sixteen lanes per component, four components per wave
+    if (wave * 4 >= kFusedComps) return;
+    const int s = lane & (kCrtLanes - 1), cl = wave * 4 + lane / kCrtLanes;
+    const int comp = c0 + cl;
+    if (cl >= kFusedComps || comp >= n) return;  // the component's sixteen lanes leave together
+    uint32_t res[kCrtPrimesPerLane];
+#pragma unroll
+    for (int i = 0; i < kCrtPrimesPerLane; i++) {
+        const int l = s + kCrtLanes * i;
+        res[i] = l < E ? sU[l][cl] : 0u;
+    }
+    crt_digit(T, prm, E, s, res, comp, digits, kchunk, slot, xlow);
 }
 
 // ---------------------------------------------------------------- lift: residual
@@ -1867,6 +1984,55 @@ hipError_t launch_lift_contract(const Layout& L, uint8_t* ws, int E, hipStream_t
         hipLaunchKernelGGL(lift_mfma_kernel, grid, dim3(256), 0, st, (const int8_t*)(ws + L.off_S), L.n, L.pitch,
                            L.c, (const int8_t*)(ws + L.off_rho), (const LiftParams*)(ws + L.off_params),
                            (const int*)(ws + L.off_rowpos), ws + L.off_U);
+    }
+    return hipGetLastError();
+}
+
+bool lift_fused_fits(const Layout& L) {
+    static const bool off = [] {
+        const char* e = std::getenv("ES_FUSED_CRT");
+        return e && e[0] == '0';
+    }();
+    return !off && L.c == 1 && L.pitch >= 1024;
+}
+
+hipError_t launch_lift_rows(const Layout& L, uint8_t* ws, int E, hipStream_t st) {
+    hipLaunchKernelGGL(lift_rows_kernel, dim3((L.n + 255) / 256, E), dim3(256), 0, st,
+                       (const int*)(ws + L.off_rowpos), (const LiftParams*)(ws + L.off_params), L.n,
+                       (int*)(ws + L.off_comprow));
+    return hipGetLastError();
+}
+
+template <int C, int W>
+static void launch_fused_t(const Layout& L, uint8_t* ws, int slot, hipStream_t st) {
+    static_assert((C == 2 || C % 4 == 0) && C <= 4 * W, "the CRT takes four components per wave");
+    hipLaunchKernelGGL((lift_gemv_crt_kernel<C, W>), dim3((L.n + C - 1) / C), dim3(W * 64), 0, st,
+                       (const int8_t*)(ws + L.off_S), L.n, L.pitch, (const int8_t*)(ws + L.off_rho),
+                       (const LiftParams*)(ws + L.off_params), (const int*)(ws + L.off_comprow),
+                       L.dig_dev ? L.dig_dev : (uint64_t*)(ws + L.off_digits), L.kchunk, slot,
+                       (uint64_t*)(ws + L.off_xlow));
+}
+
+// block shape of the fused launch: components x waves (ES_FUSED_CFG=4x8 etc.)
+static int fused_cfg() {
+    static const int cfg = [] {
+        const char* e = std::getenv("ES_FUSED_CFG");
+        if (!e) return 0;
+        const std::string v(e);
+        return v == "4x8" ? 1 : v == "8x16" ? 2 : v == "8x8" ? 3 : v == "2x16" ? 4 : v == "2x8" ? 5 : 0;
+    }();
+    return cfg;
+}
+
+hipError_t launch_lift_contract_crt(const Layout& L, uint8_t* ws, int E, int slot, hipStream_t st) {
+    (void)E;
+    switch (fused_cfg()) {
+        case 1: launch_fused_t<4, 8>(L, ws, slot, st); break;
+        case 2: launch_fused_t<8, 16>(L, ws, slot, st); break;
+        case 3: launch_fused_t<8, 8>(L, ws, slot, st); break;
+        case 4: launch_fused_t<2, 16>(L, ws, slot, st); break;
+        case 5: launch_fused_t<2, 8>(L, ws, slot, st); break;
+        default: launch_fused_t<4, 16>(L, ws, slot, st); break;
     }
     return hipGetLastError();
 }
