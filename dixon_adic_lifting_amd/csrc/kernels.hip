@@ -954,6 +954,10 @@ __device__ __forceinline__ bool panel_up_body(int8_t* __restrict__ S, int n, int
         }
         const uint32_t pinv = dead ? 0u : inv[vs[kk] >> 8];
         vs[kk] = 256u;
+        // a wave whose slots lie past the candidate list holds only zeros,
+        // which the update leaves as they are: it skips the update (the list
+        // shrinks by 64 rows a wave as the panels advance)
+        if (64 * wave >= nc) continue;
 #pragma unroll
         for (int r = 0; r < RPT; r++) {
             // every row without a branch: base (slot kk cleared) + fac prow'
