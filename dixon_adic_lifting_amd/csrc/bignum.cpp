@@ -2,8 +2,11 @@
 #include "bignum.h"
 
 #include <algorithm>
+#include <atomic>
 #include <cstring>
+#include <exception>
 #include <stdexcept>
+#include <thread>
 
 namespace es {
 
@@ -662,6 +665,117 @@ static size_t lincomb_mag(limb_t* s, limb_t* t, size_t n, uint64_t a, uint64_t b
     return cs || ct ? n + 1 : n;
 }
 
+// The cofactor magnitudes |t0|, |t1| of the extended Euclid below: Lehmer
+// matrices and full-division steps act on them in order.  They depend on
+// the remainders only through those matrices and quotients, so for long
+// inputs the updates run on a second thread, fed through a single-producer
+// ring, while the caller's thread works on the remainders.
+class CofactorTrack {
+  public:
+    CofactorTrack(size_t L, bool threaded) : t0_(L, 0), t1_(L, 0), ring_(threaded ? kRing : 0) {
+        t1_[0] = 1;
+        if (threaded) {
+            try {
+                th_ = std::thread([this] { run(); });
+            } catch (...) {
+                ring_.clear();  // no thread: the updates run inline
+            }
+        }
+    }
+    ~CofactorTrack() {
+        if (th_.joinable()) {
+            done_.store(true, std::memory_order_release);
+            th_.join();
+        }
+    }
+    // (t0, t1) <- (a t0 + b t1, c t0 + d t1) on the magnitudes
+    void matrix(uint64_t a, uint64_t b, uint64_t c, uint64_t d) {
+        Op op{a, b, c, d, false, BigInt()};
+        push(std::move(op));
+    }
+    // (t0, t1) <- (t1, t0 + q t1)
+    void division(BigInt&& q) {
+        Op op{0, 0, 0, 0, true, std::move(q)};
+        push(std::move(op));
+    }
+    // |t1| once every update has been applied
+    BigInt finish() {
+        if (th_.joinable()) {
+            done_.store(true, std::memory_order_release);
+            th_.join();
+        }
+        if (err_) std::rethrow_exception(err_);
+        BigInt tt;
+        tt.d.assign(t1_.begin(), t1_.begin() + nt_);
+        tt.trim();
+        return tt;
+    }
+
+  private:
+    struct Op {
+        uint64_t a, b, c, d;
+        bool div;
+        BigInt q;
+    };
+    static constexpr size_t kRing = 256;
+
+    void apply(Op& op) {
+        if (!op.div) {
+            nt_ = lincomb_mag(t0_.data(), t1_.data(), nt_, op.a, op.b, op.c, op.d);
+            return;
+        }
+        BigInt tm;
+        tm.d.assign(t1_.begin(), t1_.begin() + nt_);
+        tm.trim();
+        BigInt t0b;
+        t0b.d.assign(t0_.begin(), t0_.begin() + nt_);
+        t0b.trim();
+        const BigInt nt0 = add(t0b, mul(op.q, tm));
+        std::fill(t0_.begin(), t0_.end(), 0);
+        std::copy(t1_.begin(), t1_.begin() + nt_, t0_.begin());
+        std::fill(t1_.begin(), t1_.end(), 0);
+        std::copy(nt0.d.begin(), nt0.d.end(), t1_.begin());
+        nt_ = std::max(nt_, nt0.size());
+    }
+    void push(Op&& op) {
+        if (ring_.empty()) {
+            apply(op);
+            return;
+        }
+        const size_t h = head_.load(std::memory_order_relaxed);
+        while (h - tail_.load(std::memory_order_acquire) >= kRing) std::this_thread::yield();
+        ring_[h % kRing] = std::move(op);
+        head_.store(h + 1, std::memory_order_release);
+    }
+    void run() {
+        size_t t = 0;
+        for (;;) {
+            if (t < head_.load(std::memory_order_acquire)) {
+                if (!err_) {
+                    try {
+                        apply(ring_[t % kRing]);
+                    } catch (...) {
+                        err_ = std::current_exception();
+                    }
+                }
+                ring_[t % kRing].q = BigInt();
+                tail_.store(++t, std::memory_order_release);
+                continue;
+            }
+            if (done_.load(std::memory_order_acquire) && head_.load(std::memory_order_acquire) == t) break;
+            __builtin_ia32_pause();
+        }
+    }
+
+    std::vector<limb_t> t0_, t1_;
+    size_t nt_ = 1;
+    std::vector<Op> ring_;
+    std::atomic<size_t> head_{0}, tail_{0};
+    std::atomic<bool> done_{false};
+    std::thread th_;
+    std::exception_ptr err_;
+};
+
 bool rational_reconstruct(const BigInt& a, const BigInt& M, const BigInt& N, const BigInt& D,
                           BigInt* num, BigInt* den, bool require_coprime) {
     // extended Euclid on (M, a) tracking the cofactor of a: r_k = s_k M + t_k a.
@@ -669,11 +783,11 @@ bool rational_reconstruct(const BigInt& a, const BigInt& M, const BigInt& N, con
     // |t_{k+1}| = |t_{k-1}| + q_k |t_k|, and a Lehmer matrix acts on them as
     // (|A| |t0| + |B| |t1|, |C| |t0| + |D| |t1|).
     const size_t L = M.size() + 2;
-    std::vector<limb_t> r0(L, 0), r1(L, 0), t0(L, 0), t1(L, 0);
+    std::vector<limb_t> r0(L, 0), r1(L, 0);
     std::copy(M.d.begin(), M.d.end(), r0.begin());
     std::copy(a.d.begin(), a.d.end(), r1.begin());
-    size_t n0 = M.size(), n1 = trimmed(r1.data(), a.size()), nt = 1;
-    t1[0] = 1;
+    size_t n0 = M.size(), n1 = trimmed(r1.data(), a.size());
+    CofactorTrack tr(L, L > 256);
     bool t1neg = false;  // t0 has the other sign (or is 0)
     const size_t nbits = N.bit_length();
     auto above_N = [&]() { return cmp_limbs(r1.data(), n1, N.d.data(), N.size()) > 0; };
@@ -684,7 +798,8 @@ bool rational_reconstruct(const BigInt& a, const BigInt& M, const BigInt& N, con
         n1 = trimmed(r1.data(), n0 > n1 ? n0 : n1);
         const uint64_t ua = (uint64_t)(A < 0 ? -A : A), ub = (uint64_t)(B < 0 ? -B : B);
         const uint64_t uc = (uint64_t)(C < 0 ? -C : C), ud = (uint64_t)(D2 < 0 ? -D2 : D2);
-        nt = lincomb_mag(t0.data(), t1.data(), nt, ua, ub, uc, ud);
+        if ((ua | ub | uc | ud) >> 62) throw std::logic_error("cofactor out of range");
+        tr.matrix(ua, ub, uc, ud);
         if (D2 < 0) t1neg = !t1neg;
         if (cmp_limbs(r0.data(), n0, N.d.data(), N.size()) <= 0)
             throw std::logic_error("Lehmer step passed the stopping point");
@@ -734,32 +849,19 @@ bool rational_reconstruct(const BigInt& a, const BigInt& M, const BigInt& N, con
         y.d.assign(r1.begin(), r1.begin() + n1);
         divmod_trunc(x, y, &q, &r);
         // t0 <- |t0| + q |t1| (then swap): the new cofactor takes t0's sign
-        BigInt tm;
-        tm.d.assign(t1.begin(), t1.begin() + nt);
-        tm.trim();
-        BigInt prod = mul(q, tm);
-        BigInt t0b;
-        t0b.d.assign(t0.begin(), t0.begin() + nt);
-        t0b.trim();
-        BigInt nt0 = add(t0b, prod);
+        tr.division(std::move(q));
         std::fill(r0.begin(), r0.end(), 0);
         std::copy(r1.begin(), r1.begin() + n1, r0.begin());
         n0 = n1;
         std::fill(r1.begin(), r1.end(), 0);
         std::copy(r.d.begin(), r.d.end(), r1.begin());
         n1 = r.size();
-        std::fill(t0.begin(), t0.end(), 0);
-        std::copy(t1.begin(), t1.begin() + nt, t0.begin());
-        std::fill(t1.begin(), t1.end(), 0);
-        std::copy(nt0.d.begin(), nt0.d.end(), t1.begin());
-        nt = std::max(nt, nt0.size());
         t1neg = !t1neg;
     }
-    BigInt rr, tt;
+    BigInt rr;
     rr.d.assign(r1.begin(), r1.begin() + n1);
     rr.trim();
-    tt.d.assign(t1.begin(), t1.begin() + nt);
-    tt.trim();
+    const BigInt tt = tr.finish();
     if (tt.is_zero() || cmp_abs(tt, D) > 0) return false;
     if (require_coprime) {
         BigInt g = gcd(rr, tt);

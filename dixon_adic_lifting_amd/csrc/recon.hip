@@ -687,16 +687,36 @@ int gcd_words_per_lane(int words) {
     return limbs <= 64 * 8 ? 8 : limbs <= 64 * 16 ? 16 : limbs <= 64 * 32 ? 32 : 0;
 }
 
+// Unused dynamic LDS per gcd block that caps the blocks a CU can hold at
+// ceil(blocks / CUs): the components are latency-bound chains, and an even
+// spread keeps every CU at the same small number of them.  Zero when the cap
+// would need more than 48 KB (few blocks) or the device does not say.
+static size_t gcd_lds_pad(int blocks) {
+    static int cus = -1, lds = 0;
+    if (cus < 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess)
+            cus = 0;
+    }
+    if (cus <= 0 || lds <= 0 || blocks <= 0) return 0;
+    const int cap = (blocks + cus - 1) / cus;
+    const int pad = lds / cap - 2048;  // room for the kernel's own LDS
+    return pad > 0 && pad <= 48 * 1024 ? (size_t)pad : 0;
+}
+
 hipError_t launch_gcd(const uint32_t* Y, int nw, const int* status, int valid_rows, const uint32_t* Dw, int nwd,
                       uint64_t* G, int* gstat, hipStream_t st) {
     const int cw = gcd_words_per_lane(nw > nwd ? nw : nwd);
     const dim3 grid(valid_rows);
+    const size_t pad = gcd_lds_pad(valid_rows);
     if (cw == 8)
-        hipLaunchKernelGGL(gcd_kernel<8>, grid, dim3(128), 0, st, Y, nw, status, valid_rows, Dw, nwd, G, gstat);
+        hipLaunchKernelGGL(gcd_kernel<8>, grid, dim3(128), pad, st, Y, nw, status, valid_rows, Dw, nwd, G, gstat);
     else if (cw == 16)
-        hipLaunchKernelGGL(gcd_kernel<16>, grid, dim3(128), 0, st, Y, nw, status, valid_rows, Dw, nwd, G, gstat);
+        hipLaunchKernelGGL(gcd_kernel<16>, grid, dim3(128), pad, st, Y, nw, status, valid_rows, Dw, nwd, G, gstat);
     else if (cw == 32)
-        hipLaunchKernelGGL(gcd_kernel<32>, grid, dim3(128), 0, st, Y, nw, status, valid_rows, Dw, nwd, G, gstat);
+        hipLaunchKernelGGL(gcd_kernel<32>, grid, dim3(128), pad, st, Y, nw, status, valid_rows, Dw, nwd, G, gstat);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
