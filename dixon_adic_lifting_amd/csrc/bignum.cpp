@@ -777,7 +777,7 @@ class CofactorTrack {
 };
 
 bool rational_reconstruct(const BigInt& a, const BigInt& M, const BigInt& N, const BigInt& D,
-                          BigInt* num, BigInt* den, bool require_coprime) {
+                          BigInt* num, BigInt* den, bool require_coprime, bool split_cofactors) {
     // extended Euclid on (M, a) tracking the cofactor of a: r_k = s_k M + t_k a.
     // The t_k alternate in sign, so their magnitudes only add:
     // |t_{k+1}| = |t_{k-1}| + q_k |t_k|, and a Lehmer matrix acts on them as
@@ -787,7 +787,7 @@ bool rational_reconstruct(const BigInt& a, const BigInt& M, const BigInt& N, con
     std::copy(M.d.begin(), M.d.end(), r0.begin());
     std::copy(a.d.begin(), a.d.end(), r1.begin());
     size_t n0 = M.size(), n1 = trimmed(r1.data(), a.size());
-    CofactorTrack tr(L, L > 256);
+    CofactorTrack tr(L, split_cofactors && L > 256);
     bool t1neg = false;  // t0 has the other sign (or is 0)
     const size_t nbits = N.bit_length();
     auto above_N = [&]() { return cmp_limbs(r1.data(), n1, N.d.data(), N.size()) > 0; };

@@ -58,8 +58,11 @@ BigInt lcm(const BigInt& a, const BigInt& b);       // >= 0
 // the final gcd(num, den) = 1 test is skipped: the result is then the
 // remainder / cofactor pair where the Euclidean sequence first drops to N,
 // whose den is the true denominator whenever such a fraction exists.
+// split_cofactors runs the cofactor updates on a second thread (worth it for
+// long inputs when cores are idle).
 bool rational_reconstruct(const BigInt& a, const BigInt& M, const BigInt& N,
-                          const BigInt& D, BigInt* num, BigInt* den, bool require_coprime = true);
+                          const BigInt& D, BigInt* num, BigInt* den, bool require_coprime = true,
+                          bool split_cofactors = false);
 
 // low-level magnitude routines (exposed for tests)
 void mag_mul(limb_t* r, const limb_t* a, size_t la, const limb_t* b, size_t lb);

@@ -401,13 +401,16 @@ bool sample_denominator(const std::vector<BigInt>& xs, const BigInt& M, int nbit
     const BigInt Db = shl(BigInt::from_u64(1), (size_t)dbits);
     std::vector<BigInt> sden(xs.size());
     std::atomic<int> bad{0};
+    // a second thread per reconstruction only while the samples leave most
+    // cores idle (both threads of every sample busy otherwise crowd them out)
+    const bool split = 4 * xs.size() <= (size_t)nthreads;
     parallel_for(xs.size(), nthreads, [&](size_t s) {
         // the remainder / cofactor pair where the Euclidean sequence first
         // drops to N: its cofactor is x's denominator (a solution within the
         // bounds exists), and every numerator formed with d is checked
         // against N afterwards, so the coprimality test is not needed here
         BigInt a = mod_floor(xs[s], M), nu, de;
-        if (!rational_reconstruct(a, M, Nb, Db, &nu, &de, false)) bad = 1;
+        if (!rational_reconstruct(a, M, Nb, Db, &nu, &de, false, split)) bad = 1;
         else sden[s] = de;
     });
     if (bad) return false;

@@ -375,9 +375,9 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
     // Reconstructs one component on its own from its digits (card, "Method": a
     // numerator outside the bound means the sample missed part of its
     // denominator).
-    auto alone = [&](const int64_t* digs, BigInt* nu, BigInt* de) -> bool {
+    auto alone = [&](const int64_t* digs, BigInt* nu, BigInt* de, bool split) -> bool {
         BigInt a = mod_floor(assemble(digs, m, P), M);
-        return rational_reconstruct(a, M, Nb, Db, nu, de);
+        return rational_reconstruct(a, M, Nb, Db, nu, de, true, split);
     };
     size_t failed_total = 0;
     for (int pass = 0;; pass++) {
@@ -405,7 +405,7 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
             std::atomic<int> bad{0};
             parallel_for_each(failed.size(), nthreads, [&](size_t k) {
                 BigInt nu, de;
-                if (!alone(digs.data() + k * dig_comp, &nu, &de)) bad = 1;
+                if (!alone(digs.data() + k * dig_comp, &nu, &de, 4 * failed.size() <= (size_t)nthreads)) bad = 1;
                 out->num[failed[k]] = nu;
                 out->den[failed[k]] = de;
             });
@@ -416,7 +416,7 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
         rc = fetch(std::vector<size_t>{failed[0]}, &digs);
         if (rc != ES_OK) return rc;
         BigInt nu, de;
-        if (!alone(digs.data(), &nu, &de)) return ES_EINTERNAL;
+        if (!alone(digs.data(), &nu, &de, true)) return ES_EINTERNAL;
         d = lcm(d, de);
         todo.swap(failed);
     }
