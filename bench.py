@@ -221,8 +221,11 @@ def rooflines(prof, info, n, c, traffic=None):
                            "element_updates_per_launch": int(32 * E * n * 32)}
     ms, cnt = prof["lift_contract"]
     if cnt:
-        # B_j (int8, n x pitch) once per step, plus the residue vector in and the residues out
-        bytes_per = E * n * pitch + E * c * pitch + E * n * c
+        # B_j (int8, n x pitch) once per step, plus the residue vector in and the residues out;
+        # with one right-hand side and rows of 1 KB or more the CRT runs in the same kernel,
+        # which writes the digit (48 bytes) and x mod 2^64 (8 bytes) per component instead
+        fused = c == 1 and pitch >= 1024
+        bytes_per = E * n * pitch + E * c * pitch + (56 * n if fused else E * n * c)
         ops_per = 2.0 * E * n * n * c
         avg_s = ms / cnt / 1e3
         gbs = bytes_per / avg_s / 1e9
