@@ -110,7 +110,7 @@ struct Layout {
     size_t off_rho;       // int8 [53][c][pitch]       r_i mods q_j, permuted
     size_t off_U;         // u8 [53][n*c]              (B_j r_i) mod q_j
     size_t off_xlow;      // uint64 [n][c]             x_i mod 2^64
-    size_t off_comprow;   // int32 [53][n]             (c = 1) row of B_j holding component k, live primes in order
+    size_t off_Sperm;     // int8 [53][n][pitch]       (c = 1, pitch >= 1024) B_j rows in component order, live primes
     size_t off_digits;    // uint64 [n*c][kchunk][6]   digits of a chunk of steps
     size_t off_params;    // LiftParams
     size_t total;
@@ -147,7 +147,8 @@ hipError_t launch_split_b(const int64_t* b, const Layout& L, uint8_t* ws, int E,
 hipError_t launch_lift_contract(const Layout& L, uint8_t* ws, int E, hipStream_t st);
 hipError_t launch_lift_crt(const Layout& L, uint8_t* ws, int slot, hipStream_t st);
 // one right-hand side: the contraction and the CRT in one launch (after
-// launch_lift_rows once per lift); false when the layout does not take it
+// launch_lift_rows once per lift, which copies the live primes' B_j rows
+// into component order); false when the layout does not take it
 bool lift_fused_fits(const Layout& L);
 hipError_t launch_lift_rows(const Layout& L, uint8_t* ws, int E, hipStream_t st);
 hipError_t launch_lift_contract_crt(const Layout& L, uint8_t* ws, int E, int slot, hipStream_t st);

@@ -73,7 +73,7 @@ Layout make_layout(int n, int c) {
     L.off_rho = take(E * c * (size_t)L.pitch);
     L.off_U = take(E * NC);
     L.off_xlow = take(NC * sizeof(uint64_t));
-    L.off_comprow = take(c == 1 ? E * n * sizeof(int32_t) : 0);
+    L.off_Sperm = take(c == 1 && L.pitch >= 1024 ? E * n * (size_t)L.pitch : 0);
     L.off_digits = take(NC * (size_t)L.kchunk * kDigitLimbs * sizeof(uint64_t));
     L.off_params = take(sizeof(LiftParams));
     L.total = o;

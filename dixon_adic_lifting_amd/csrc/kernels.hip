@@ -1701,28 +1701,35 @@ __global__ __launch_bounds__(256) void crt_kernel(const LiftParams* __restrict__
 
 // ---------------------------------------------------------------- lift: contraction + CRT, one right-hand side
 // For one right-hand side with rows of at least 1 KB, the contraction and
-// the CRT share a launch: a block owns kFusedComps components and forms
-// every live prime's residue for them, so the residues stay in LDS and the
-// CRT follows in the same block.  Row k of B_j (in component order) is row
-// comprow[j][k] of the elimination's result.  The block's rows (prime, component)
-// go eight to a wave as in the plain contraction (the sums meet in the same
+// the CRT share a launch: a block owns kFusedComps consecutive components and
+// forms every live prime's residue for them, so the residues stay in LDS and
+// the CRT follows in the same block.  The live primes' B_j rows are copied
+// once per lift into component order (row k of Sperm_j is the row of S_j
+// that pivoted at step k), so a block reads 4 KB runs and the grid sweeps
+// every matrix front to back.  The block's rows (prime, component) go eight
+// to a wave as in the plain contraction (the sums meet in the same
 // transposed butterfly); the last wave's tail rows are duplicates whose
 // results are dropped.
 
-// Row index of B_j for each component, per live prime: the inverse of rowpos.
-__global__ __launch_bounds__(256) void lift_rows_kernel(const int* __restrict__ rowpos, const LiftParams* __restrict__ prm,
-                                                        int n, int* __restrict__ comprow) {
+// Sperm[jl][rowpos[J][i]] = S[J][i]: one wave per row, 1 KB per load
+__global__ __launch_bounds__(256) void lift_rows_kernel(const int8_t* __restrict__ S, const int* __restrict__ rowpos,
+                                                        const LiftParams* __restrict__ prm, int n, int pitch,
+                                                        int8_t* __restrict__ Sperm) {
     const int jl = blockIdx.y;
     const int J = prm->qidx[jl];
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i < n) comprow[(size_t)jl * n + rowpos[(size_t)J * n + i]] = i;
+    const int i = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (i >= n) return;
+    const int k = min((unsigned)rowpos[(size_t)J * n + i], (unsigned)(n - 1));  // a permutation; clamped all the same
+    const int8_t* src = S + ((size_t)J * n + i) * pitch;
+    int8_t* dst = Sperm + ((size_t)jl * n + k) * pitch;
+    for (int col = lane * 16; col < pitch; col += 1024) *(uint4*)(dst + col) = *(const uint4*)(src + col);
 }
 
 template <int kFusedComps, int kFusedWaves>
 __global__ __launch_bounds__(kFusedWaves * 64) void lift_gemv_crt_kernel(
-    const int8_t* __restrict__ S, int n, int pitch, const int8_t* __restrict__ rho,
-    const LiftParams* __restrict__ prm, const int* __restrict__ comprow, uint64_t* __restrict__ digits, int kchunk,
-    int slot, uint64_t* __restrict__ xlow) {
+    const int8_t* __restrict__ Sperm, int n, int pitch, const int8_t* __restrict__ rho,
+    const LiftParams* __restrict__ prm, uint64_t* __restrict__ digits, int kchunk, int slot,
+    uint64_t* __restrict__ xlow) {
     __shared__ CrtTables T;
     __shared__ uint32_t sU[kNumPrimes][kFusedComps];
     const int E = prm->E;
@@ -1737,9 +1744,7 @@ __global__ __launch_bounds__(kFusedWaves * 64) void lift_gemv_crt_kernel(
         for (int r = 0; r < 8; r++) {
             const int rr = min(rb + r, nrows - 1);
             const int jl = rr / kFusedComps, comp = min(c0 + rr % kFusedComps, n - 1);
-            const int J = prm->qidx[jl];
-            const int row = min((unsigned)comprow[(size_t)jl * n + comp], (unsigned)(n - 1));  // a permutation; clamped all the same
-            rowp[r] = S + ((size_t)J * n + row) * pitch;
+            rowp[r] = Sperm + ((size_t)jl * n + comp) * pitch;
         }
         // the batch's primes: row r takes prime rb / kFusedComps + r / kFusedComps
         constexpr int NP = kFusedComps >= 8 ? 1 : 8 / kFusedComps;
@@ -2001,9 +2006,9 @@ bool lift_fused_fits(const Layout& L) {
 }
 
 hipError_t launch_lift_rows(const Layout& L, uint8_t* ws, int E, hipStream_t st) {
-    hipLaunchKernelGGL(lift_rows_kernel, dim3((L.n + 255) / 256, E), dim3(256), 0, st,
-                       (const int*)(ws + L.off_rowpos), (const LiftParams*)(ws + L.off_params), L.n,
-                       (int*)(ws + L.off_comprow));
+    hipLaunchKernelGGL(lift_rows_kernel, dim3((L.n + 3) / 4, E), dim3(256), 0, st, (const int8_t*)(ws + L.off_S),
+                       (const int*)(ws + L.off_rowpos), (const LiftParams*)(ws + L.off_params), L.n, L.pitch,
+                       (int8_t*)(ws + L.off_Sperm));
     return hipGetLastError();
 }
 
@@ -2011,10 +2016,9 @@ template <int C, int W>
 static void launch_fused_t(const Layout& L, uint8_t* ws, int slot, hipStream_t st) {
     static_assert((C == 2 || C % 4 == 0) && C <= 4 * W, "the CRT takes four components per wave");
     hipLaunchKernelGGL((lift_gemv_crt_kernel<C, W>), dim3((L.n + C - 1) / C), dim3(W * 64), 0, st,
-                       (const int8_t*)(ws + L.off_S), L.n, L.pitch, (const int8_t*)(ws + L.off_rho),
-                       (const LiftParams*)(ws + L.off_params), (const int*)(ws + L.off_comprow),
-                       L.dig_dev ? L.dig_dev : (uint64_t*)(ws + L.off_digits), L.kchunk, slot,
-                       (uint64_t*)(ws + L.off_xlow));
+                       (const int8_t*)(ws + L.off_Sperm), L.n, L.pitch, (const int8_t*)(ws + L.off_rho),
+                       (const LiftParams*)(ws + L.off_params), L.dig_dev ? L.dig_dev : (uint64_t*)(ws + L.off_digits),
+                       L.kchunk, slot, (uint64_t*)(ws + L.off_xlow));
 }
 
 // block shape of the fused launch: components x waves (ES_FUSED_CFG=4x8 etc.)
