@@ -855,7 +855,7 @@ __device__ __forceinline__ bool panel_up_body(int8_t* __restrict__ S, int n, int
     int* pj = piv + (size_t)j * (n + 1);
     __shared__ int clist[1024 * RPT];
     __shared__ int wsum[16];
-    __shared__ __attribute__((aligned(16))) uint32_t slot[2][16][8];  // per wave: its best candidate's row
+    __shared__ __attribute__((aligned(16))) uint32_t slot[2][16][kPanel];  // per wave: its best candidate's row (byte-up)
     __shared__ __attribute__((aligned(16))) int sidx[2][16];          // and that candidate's index
     __shared__ int plist[kPanel];
     __shared__ __attribute__((aligned(16))) int8_t Zt[kPanel][64];  // Zt[c'][c] = Z[c][c'], zero-padded
@@ -904,13 +904,11 @@ __device__ __forceinline__ bool panel_up_body(int8_t* __restrict__ S, int n, int
                 const int wl = __builtin_ctzll(m);
                 best = 64 * wave + wl + 1024 * r;
                 if (lane == wl) {
-                    uint32_t pk[8];
-#pragma unroll
-                    for (int e = 0; e < 8; e++)
-                        pk[e] = pack_up(W[r][4 * e], W[r][4 * e + 1], W[r][4 * e + 2], W[r][4 * e + 3]);
+                    // published as held (one byte up), so no lane unpacks it
                     uint4* dst = (uint4*)&slot[buf][wave][0];
-                    dst[0] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-                    dst[1] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+#pragma unroll
+                    for (int e = 0; e < kPanel / 4; e++)
+                        dst[e] = make_uint4(W[r][4 * e], W[r][4 * e + 1], W[r][4 * e + 2], W[r][4 * e + 3]);
                 }
             }
         }
@@ -947,10 +945,11 @@ __device__ __forceinline__ bool panel_up_body(int8_t* __restrict__ S, int n, int
         uint32_t vs[kPanel];
         {
             const uint4* src = (const uint4*)&slot[buf][pwv][0];
-            const uint4 a = src[0], b = src[1];
-            const uint32_t prw[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
-            for (int c = 0; c < kPanel; c++) vs[c] = byte_up(prw[c >> 2], c & 3);
+            for (int e = 0; e < kPanel / 4; e++) {
+                const uint4 v = src[e];
+                vs[4 * e] = v.x, vs[4 * e + 1] = v.y, vs[4 * e + 2] = v.z, vs[4 * e + 3] = v.w;
+            }
         }
         const uint32_t pinv = dead ? 0u : inv[vs[kk] >> 8];
         vs[kk] = 256u;
