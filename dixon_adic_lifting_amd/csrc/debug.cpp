@@ -39,6 +39,10 @@ extern "C" int es_dbg_bignum(int op, const uint64_t* a, int32_t la, int a_neg, c
             case ES_DBG_GCD: x = es::gcd(A, B); break;
             case ES_DBG_ADD: x = es::add(A, B); break;
             case ES_DBG_SUB: x = es::sub(A, B); break;
+            case ES_DBG_DIVEXACT1:
+                if (B.size() != 1 || B.neg) return -1;
+                x = es::divexact_u64(A, B.d[0]);
+                break;
             default: return -1;
         }
         if (!put(x, r1, l1, n1, cap)) return -1;
@@ -53,9 +57,12 @@ extern "C" int es_dbg_ratrec(const uint64_t* a, int32_t la, const uint64_t* M, i
                              int32_t lN, const uint64_t* D, int32_t lD, uint64_t* num, int32_t* lnum, int* nneg,
                              uint64_t* den, int32_t* lden, int32_t cap) {
     try {
-        BigInt nu, de;
-        if (!es::rational_reconstruct(make(a, la, 0), make(M, lM, 0), make(N, lN, 0), make(D, lD, 0), &nu, &de))
-            return 1;
+        const BigInt A = make(a, la, 0), Mm = make(M, lM, 0), Nn = make(N, lN, 0), Dd = make(D, lD, 0);
+        BigInt nu, de, nu2, de2;
+        const bool ok = es::rational_reconstruct(A, Mm, Nn, Dd, &nu, &de);
+        const bool ok2 = es::rational_reconstruct(A, Mm, Nn, Dd, &nu2, &de2, true, true);
+        if (ok != ok2 || (ok && (es::cmp(nu, nu2) != 0 || es::cmp(de, de2) != 0))) return -2;
+        if (!ok) return 1;
         if (!put(nu, num, lnum, nneg, cap) || !put(de, den, lden, nullptr, cap)) return -1;
         return 0;
     } catch (...) {

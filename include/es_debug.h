@@ -16,16 +16,20 @@
 extern "C" {
 #endif
 
-enum { ES_DBG_MUL = 0, ES_DBG_DIVMOD = 1, ES_DBG_GCD = 2, ES_DBG_ADD = 3, ES_DBG_SUB = 4 };
+enum { ES_DBG_MUL = 0, ES_DBG_DIVMOD = 1, ES_DBG_GCD = 2, ES_DBG_ADD = 3, ES_DBG_SUB = 4, ES_DBG_DIVEXACT1 = 5 };
 
 /* op(a, b): MUL r1 = a*b; DIVMOD r1 = trunc(a/b), r2 = a - r1*b (b != 0);
- * GCD r1 = gcd(a, b) >= 0; ADD r1 = a + b; SUB r1 = a - b. */
+ * GCD r1 = gcd(a, b) >= 0; ADD r1 = a + b; SUB r1 = a - b; DIVEXACT1
+ * r1 = a / b for a positive one-limb b that divides a (the one-word Hensel
+ * division of the lowest-terms step; -1 otherwise). */
 int es_dbg_bignum(int op, const uint64_t *a, int32_t la, int a_neg, const uint64_t *b, int32_t lb,
                   int b_neg, uint64_t *r1, int32_t *l1, int *n1, uint64_t *r2, int32_t *l2, int *n2,
                   int32_t cap);
 
 /* Wang rational reconstruction of a (0 <= a < M) with bounds N, D: returns 0
- * and num/den (den > 0) if a fraction exists, 1 if none, -1 on bad input. */
+ * and num/den (den > 0) if a fraction exists, 1 if none, -1 on bad input.
+ * The reconstruction runs twice, once on the calling thread alone and once
+ * with the cofactor updates on a second thread; -2 if the two disagree. */
 int es_dbg_ratrec(const uint64_t *a, int32_t la, const uint64_t *M, int32_t lM, const uint64_t *N,
                   int32_t lN, const uint64_t *D, int32_t lD, uint64_t *num, int32_t *lnum, int *nneg,
                   uint64_t *den, int32_t *lden, int32_t cap);

@@ -121,3 +121,16 @@ def test_lift_full_c4_identity(primes):
     words, mask, m = es.lift_digits(torch.as_tensor(A).cuda(), torch.as_tensor(b).cuda())
     assert m > 100
     check_padic_identity(A, b, words, mask, m, primes, rows=range(0, 1024, 1))
+
+
+@pytest.mark.parametrize("n,seed", [(517, 21), (1027, 22)])
+def test_lift_fused_contraction_ragged(n, seed, primes):
+    """One right-hand side with rows of 1 KB or more: the contraction and the CRT
+    run in one kernel over groups of four consecutive components (517 and 1027
+    leave a partial group; 1027 also takes two column passes per row).  Every
+    row of A X = b (mod P^m) is checked with balanced digits, which fixes every
+    digit of every component."""
+    A, b = W.uniform_system(n, 1, 24, seed)
+    words, mask, m = es.lift_digits(torch.as_tensor(A).cuda(), torch.as_tensor(b).cuda(), m=3)
+    assert m == 3
+    check_padic_identity(A, b, words, mask, m, primes, rows=range(n))

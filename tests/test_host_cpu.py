@@ -172,6 +172,27 @@ def test_bignum_add_sub():
         assert dbg(4, a, b)[0] == a - b
 
 
+def test_divexact_one_word():
+    rng = random.Random(9)
+    for la in [0, 1, 2, 5, 40, 300]:
+        for _ in range(6):
+            a = rand_int(rng, la)
+            b = rng.getrandbits(64) >> rng.randrange(64) or 1
+            if rng.random() < 0.3:
+                b = (b << rng.randrange(8)) % (1 << 64) or 2
+            assert dbg(5, a * b, b)[0] == a
+    # not exact, or b wider than one limb: refused
+    L = ctypes.CDLL(_lib.LIB_PATH)
+    for a, b in [(7, 2), (3 << 70, 1 << 65), (10, 0)]:
+        pa, la_ = arr(to_limbs(a))
+        pb, lb_ = arr(to_limbs(b))
+        r = (ctypes.c_uint64 * 64)()
+        l1, n1 = ctypes.c_int32(), ctypes.c_int()
+        st = L.es_dbg_bignum(5, pa, la_, 0, pb, lb_, 0, r, ctypes.byref(l1), ctypes.byref(n1), r,
+                             ctypes.byref(l1), ctypes.byref(n1), 64)
+        assert st != 0
+
+
 def ratrec(a, M, N, D, cap=4096):
     L = ctypes.CDLL(_lib.LIB_PATH)
     args = []
@@ -193,7 +214,9 @@ def ratrec(a, M, N, D, cap=4096):
 def test_ratrec_matches_oracle():
     rng = random.Random(3)
     P = math.prod(modular.odd_primes_below(256))
-    for k in [1, 2, 8, 40]:
+    # k = 50: M has more than 256 limbs, so the second run (cofactor updates on
+    # a second thread) takes that path; both runs must agree (the hook checks)
+    for k in [1, 2, 8, 40, 50]:
         M = P ** k
         half = (M.bit_length() - 2) // 2
         for _ in range(12):
