@@ -24,7 +24,6 @@
 
 #include <climits>
 #include <cstdlib>
-#include <string>
 #include <type_traits>
 
 #include "es_internal.h"
@@ -783,6 +782,8 @@ __device__ __forceinline__ bool panel_packed_body(int8_t* __restrict__ S, int n,
         for (int e = 0; e < 8; e++)
 #pragma unroll
             for (int bb = 0; bb < 4; bb++) vs[4 * e + bb] = byte_up(prw[e], bb);
+        // a wave whose slots all lie past the candidate list has nothing to update
+        if (64 * wave >= nc) continue;
         uint32_t kmask[8];
 #pragma unroll
         for (int e = 0; e < 8; e++) kmask[e] = e == kw ? ~(0xffu << ks) : 0xffffffffu;
@@ -2011,36 +2012,15 @@ hipError_t launch_lift_rows(const Layout& L, uint8_t* ws, int E, hipStream_t st)
     return hipGetLastError();
 }
 
-template <int C, int W>
-static void launch_fused_t(const Layout& L, uint8_t* ws, int slot, hipStream_t st) {
-    static_assert((C == 2 || C % 4 == 0) && C <= 4 * W, "the CRT takes four components per wave");
+hipError_t launch_lift_contract_crt(const Layout& L, uint8_t* ws, int E, int slot, hipStream_t st) {
+    (void)E;
+    // four components and sixteen waves per block (two, eight components and
+    // eight-wave blocks measured slower at n = 1024)
+    constexpr int C = 4, W = 16;
     hipLaunchKernelGGL((lift_gemv_crt_kernel<C, W>), dim3((L.n + C - 1) / C), dim3(W * 64), 0, st,
                        (const int8_t*)(ws + L.off_Sperm), L.n, L.pitch, (const int8_t*)(ws + L.off_rho),
                        (const LiftParams*)(ws + L.off_params), L.dig_dev ? L.dig_dev : (uint64_t*)(ws + L.off_digits),
                        L.kchunk, slot, (uint64_t*)(ws + L.off_xlow));
-}
-
-// block shape of the fused launch: components x waves (ES_FUSED_CFG=4x8 etc.)
-static int fused_cfg() {
-    static const int cfg = [] {
-        const char* e = std::getenv("ES_FUSED_CFG");
-        if (!e) return 0;
-        const std::string v(e);
-        return v == "4x8" ? 1 : v == "8x16" ? 2 : v == "8x8" ? 3 : v == "2x16" ? 4 : v == "2x8" ? 5 : 0;
-    }();
-    return cfg;
-}
-
-hipError_t launch_lift_contract_crt(const Layout& L, uint8_t* ws, int E, int slot, hipStream_t st) {
-    (void)E;
-    switch (fused_cfg()) {
-        case 1: launch_fused_t<4, 8>(L, ws, slot, st); break;
-        case 2: launch_fused_t<8, 16>(L, ws, slot, st); break;
-        case 3: launch_fused_t<8, 8>(L, ws, slot, st); break;
-        case 4: launch_fused_t<2, 16>(L, ws, slot, st); break;
-        case 5: launch_fused_t<2, 8>(L, ws, slot, st); break;
-        default: launch_fused_t<4, 16>(L, ws, slot, st); break;
-    }
     return hipGetLastError();
 }
 
