@@ -222,10 +222,12 @@ def rooflines(prof, info, n, c, traffic=None):
     ms, cnt = prof["lift_contract"]
     if cnt:
         # B_j (int8, n x pitch) once per step, plus the residue vector in and the residues out;
-        # with one right-hand side and rows of 1 KB or more the CRT runs in the same kernel,
-        # which writes the digit (48 bytes) and x mod 2^64 (8 bytes) per component instead
-        fused = c == 1 and pitch >= 1024
-        bytes_per = E * n * pitch + E * c * pitch + (56 * n if fused else E * n * c)
+        # with one right-hand side and rows of 1 KB or more the step's share of the CRT runs
+        # in the same kernel, which writes per component a record of the E balanced residues
+        # and k (E + 1 bytes) and x mod 2^64 (8 bytes) instead; the digits are formed from
+        # the records by a later launch per run of steps
+        fused = c == 1 and pitch >= 1024 and 53 * n * pitch <= 0x7fffffff
+        bytes_per = E * n * pitch + E * c * pitch + ((E + 9) * n if fused else E * n * c)
         ops_per = 2.0 * E * n * n * c
         avg_s = ms / cnt / 1e3
         gbs = bytes_per / avg_s / 1e9

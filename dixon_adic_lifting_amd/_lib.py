@@ -21,6 +21,7 @@ DIGIT_LIMBS = 6
 EXPORTS = ["es_strerror", "es_primes", "es_workspace_bytes", "es_solve_device", "es_solve",
            "es_solution_rows", "es_solution_cols", "es_solution_get", "es_solution_info",
            "es_solution_free", "es_solution_modulus_bits", "es_set_gpu_reconstruction", "es_set_blocked_inverse",
+           "es_set_lift_record_steps",
            "es_last_timings", "es_set_profiling", "es_kernel_profile",
            "es_batched_inverse", "es_lift_digits", "es_reconstruct"]
 
@@ -73,6 +74,8 @@ def load():
     lib.es_last_timings.restype = ctypes.c_int
     lib.es_set_blocked_inverse.argtypes = [ctypes.c_int]
     lib.es_set_blocked_inverse.restype = ctypes.c_int
+    lib.es_set_lift_record_steps.argtypes = [ctypes.c_int32]
+    lib.es_set_lift_record_steps.restype = ctypes.c_int
     lib.es_set_gpu_reconstruction.argtypes = [ctypes.c_int]
     lib.es_set_gpu_reconstruction.restype = ctypes.c_int
     lib.es_set_profiling.argtypes = [ctypes.c_int]
@@ -146,6 +149,13 @@ KERNEL_CLASSES = ["gj_step", "lift_contract", "crt", "residual", "residues", "re
 def set_blocked_inverse(on: bool):
     """Blocked elimination with MFMA updates (default) or one launch per step, for this thread."""
     load().es_set_blocked_inverse(1 if on else 0)
+
+
+def set_lift_record_steps(steps: int):
+    """Lift steps whose CRT records are held before one launch forms their digits (0: default), for this thread."""
+    st = load().es_set_lift_record_steps(int(steps))
+    if st != 0:
+        raise ValueError(strerror(st))
 
 
 def set_gpu_reconstruction(on: bool):

@@ -264,7 +264,7 @@ int run_lift(const int64_t* dA, const int64_t* db, uint8_t* ws, hipStream_t st, 
             long ev;
             if (fused) {
                 ev = prof->start(KC_CONTRACT);
-                HIP_CHECK(launch_lift_contract_crt(L, ws, ls.E, s, st));
+                HIP_CHECK(launch_lift_contract_crt(L, ws, ls.E, s % L.krec, st));
                 prof->stop(ev);
             } else {
                 ev = prof->start(KC_CONTRACT);
@@ -277,6 +277,12 @@ int run_lift(const int64_t* dA, const int64_t* db, uint8_t* ws, hipStream_t st, 
             ev = prof->start(KC_RESIDUAL);
             HIP_CHECK(launch_lift_residual(L, ws, pr.a32, dA, st));
             prof->stop(ev);
+            if (fused && (s % L.krec == L.krec - 1 || s == cnt - 1)) {
+                // the digits of the steps whose records are held
+                ev = prof->start(KC_CRT);
+                HIP_CHECK(launch_lift_crt_records(L, ws, s % L.krec + 1, s - s % L.krec, st));
+                prof->stop(ev);
+            }
         }
         if (dig_dev) {
             // digits stay on the device for the GPU reconstruction
@@ -319,6 +325,12 @@ int es_primes(int32_t* q, int32_t cap) {
 size_t es_workspace_bytes(int32_t n, int32_t c) {
     if (!valid_shape(n, c)) return 0;
     return make_layout(n, c).total;
+}
+
+int es_set_lift_record_steps(int32_t steps) {
+    if (steps < 0) return ES_EINVAL;
+    set_lift_record_cap(steps);
+    return ES_OK;
 }
 
 int es_set_blocked_inverse(int on) {

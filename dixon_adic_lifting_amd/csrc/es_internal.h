@@ -111,13 +111,24 @@ struct Layout {
     size_t off_U;         // u8 [53][n*c]              (B_j r_i) mod q_j
     size_t off_xlow;      // uint64 [n][c]             x_i mod 2^64
     size_t off_Sperm;     // int8 [53][n][pitch]       (c = 1, pitch >= 1024) B_j rows in component order, live primes
+    size_t off_urec;      // u8 [krec][n][64]          (same condition) per step: balanced CRT residues, k at byte 63
+    int krec;             // lift steps whose records the device buffer holds
     size_t off_digits;    // uint64 [n*c][kchunk][6]   digits of a chunk of steps
     size_t off_params;    // LiftParams
     size_t total;
     uint64_t* dig_dev;    // when set, the digits go here ([n*c][kchunk][6]) instead
 };
 
+// Shapes that take the fused lift (contraction and the step's CRT share in
+// one kernel): one right-hand side, rows of at least 1 KB, and every prime's
+// matrix within one 2 GiB buffer resource.
+inline bool fused_lift_shape(int n, int c, int pitch) {
+    return c == 1 && pitch >= 1024 && (size_t)kNumPrimes * n * pitch <= (size_t)0x7fffffff;
+}
+
 Layout make_layout(int n, int c);
+// cap on Layout::krec for later layouts on the calling thread (0: none)
+void set_lift_record_cap(int steps);
 
 // ---------------------------------------------------------------- launchers
 // Each enqueues on `st` and returns the launch status.
@@ -150,6 +161,9 @@ hipError_t launch_lift_crt(const Layout& L, uint8_t* ws, int slot, hipStream_t s
 // launch_lift_rows once per lift, which copies the live primes' B_j rows
 // into component order); false when the layout does not take it
 bool lift_fused_fits(const Layout& L);
+// digits of records [0, nrec) of the record buffer into digit slots
+// slot0 .. slot0 + nrec - 1 of the current chunk
+hipError_t launch_lift_crt_records(const Layout& L, uint8_t* ws, int nrec, int slot0, hipStream_t st);
 hipError_t launch_lift_rows(const Layout& L, uint8_t* ws, int E, hipStream_t st);
 hipError_t launch_lift_contract_crt(const Layout& L, uint8_t* ws, int E, int slot, hipStream_t st);
 hipError_t launch_lift_residual(const Layout& L, uint8_t* ws, bool a32, const int64_t* A64, hipStream_t st);

@@ -33,6 +33,10 @@ typedef unsigned __int128 u128;
 
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+static thread_local int g_krec_cap = 0;  // 0: the default record chunk
+
+void set_lift_record_cap(int steps) { g_krec_cap = steps; }
+
 Layout make_layout(int n, int c) {
     Layout L{};
     L.n = n;
@@ -73,7 +77,12 @@ Layout make_layout(int n, int c) {
     L.off_rho = take(E * c * (size_t)L.pitch);
     L.off_U = take(E * NC);
     L.off_xlow = take(NC * sizeof(uint64_t));
-    L.off_Sperm = take(c == 1 && L.pitch >= 1024 ? E * n * (size_t)L.pitch : 0);
+    const bool fused = fused_lift_shape(n, c, L.pitch);
+    L.off_Sperm = take(fused ? E * n * (size_t)L.pitch : 0);
+    size_t kr = std::min<size_t>(((size_t)16 << 20) / ((size_t)n * 64), (size_t)L.kchunk);
+    if (g_krec_cap > 0) kr = std::min<size_t>(kr, (size_t)g_krec_cap);
+    L.krec = (int)std::max<size_t>(1, kr);
+    L.off_urec = take(fused ? (size_t)L.krec * n * 64 : 0);
     L.off_digits = take(NC * (size_t)L.kchunk * kDigitLimbs * sizeof(uint64_t));
     L.off_params = take(sizeof(LiftParams));
     L.total = o;

@@ -1594,7 +1594,7 @@ __device__ __forceinline__ double quad_add(double v) {
 struct CrtTables {
     double Wd[kNumPrimes][kDigitWords];
     double qrec[kNumPrimes];
-    uint32_t qc[kNumPrimes][3];  // q, mu16, c
+    uint32_t qc[kNumPrimes][4];  // q, mu16, c, mu32
 };
 
 __device__ __forceinline__ void load_crt_tables(CrtTables& T, const LiftParams* __restrict__ prm, int tid,
@@ -1605,7 +1605,57 @@ __device__ __forceinline__ void load_crt_tables(CrtTables& T, const LiftParams* 
         T.qc[l][0] = prm->q[l];
         T.qc[l][1] = prm->mu16[l];
         T.qc[l][2] = prm->cinv[l];
+        T.qc[l][3] = prm->mu32[l];
     }
+}
+
+// x = X - k P as twelve 32-bit words (two's complement), X given by its
+// exact word sums acc[w] (X = sum_w acc[w] 2^(32 w))
+__device__ __forceinline__ void crt_sub_kP(const double (&acc)[kDigitWords], int64_t ki,
+                                           const LiftParams* __restrict__ prm, uint32_t (&x)[kDigitWords]) {
+    int64_t carry = 0;
+#pragma unroll
+    for (int w = 0; w < kDigitWords; w++) {
+        const int64_t v = (int64_t)acc[w] - ki * (int64_t)prm->Pw[w] + carry;
+        x[w] = (uint32_t)v;
+        carry = v >> 32;
+    }
+}
+
+// k = round(X / P) from f = sum_l u_l / q_l, and x = X - k P.  When f lies
+// within 2^-30 of a half-integer the representative is settled by an exact
+// comparison of x with (P - 1) / 2, and k moves by one with it.
+__device__ __forceinline__ int64_t crt_finish(const double (&acc)[kDigitWords], double f,
+                                              const LiftParams* __restrict__ prm, uint32_t (&x)[kDigitWords]) {
+    int64_t ki = (int64_t)rint(f);
+    crt_sub_kP(acc, ki, prm, x);
+    if (fabs(f - (double)ki) > 0.5 - 0x1p-30) {
+        // neg: is x + (P - 1) / 2 negative?  else: is x - (P - 1) / 2 positive?
+        const bool neg = (int32_t)x[kDigitWords - 1] < 0;
+        int64_t c = 0;
+        uint32_t y[kDigitWords];
+#pragma unroll
+        for (int w = 0; w < kDigitWords; w++) {
+            const int64_t v = (int64_t)x[w] + (neg ? (int64_t)prm->Phw[w] : -(int64_t)prm->Phw[w]) + c;
+            y[w] = (uint32_t)v;
+            c = v >> 32;
+        }
+        bool nz = false;
+#pragma unroll
+        for (int w = 0; w < kDigitWords; w++) nz |= y[w] != 0u;
+        const bool out = neg ? (int32_t)y[kDigitWords - 1] < 0 : ((int32_t)y[kDigitWords - 1] >= 0 && nz);
+        if (out) {
+            ki += neg ? -1 : 1;
+            c = 0;
+#pragma unroll
+            for (int w = 0; w < kDigitWords; w++) {
+                const int64_t v = (int64_t)x[w] + (neg ? (int64_t)prm->Pw[w] : -(int64_t)prm->Pw[w]) + c;
+                x[w] = (uint32_t)v;
+                c = v >> 32;
+            }
+        }
+    }
+    return ki;
 }
 
 constexpr int kCrtLanes = 16;                                          // lanes per component
@@ -1637,42 +1687,8 @@ __device__ __forceinline__ void crt_digit(const CrtTables& T, const LiftParams* 
 #pragma unroll
     for (int w = 0; w < kDigitWords; w++) acc[w] = quad_add<8>(quad_add<4>(quad_add<2>(quad_add<1>(acc[w]))));
     if (s != 0) return;
-    const double k = rint(f);
-    const int64_t ki = (int64_t)k;
     uint32_t x[kDigitWords];
-    int64_t carry = 0;
-#pragma unroll
-    for (int w = 0; w < kDigitWords; w++) {
-        const int64_t v = (int64_t)acc[w] - ki * (int64_t)prm->Pw[w] + carry;
-        x[w] = (uint32_t)v;
-        carry = v >> 32;
-    }
-    if (fabs(f - k) > 0.5 - 0x1p-30) {
-        // near the boundary: compare with (P - 1) / 2 exactly
-        const bool neg = (int32_t)x[kDigitWords - 1] < 0;
-        // neg: is x + (P - 1) / 2 negative?  else: is x - (P - 1) / 2 positive?
-        int64_t c = 0;
-        uint32_t y[kDigitWords];
-#pragma unroll
-        for (int w = 0; w < kDigitWords; w++) {
-            const int64_t v = (int64_t)x[w] + (neg ? (int64_t)prm->Phw[w] : -(int64_t)prm->Phw[w]) + c;
-            y[w] = (uint32_t)v;
-            c = v >> 32;
-        }
-        bool nz = false;
-#pragma unroll
-        for (int w = 0; w < kDigitWords; w++) nz |= y[w] != 0u;
-        const bool out = neg ? (int32_t)y[kDigitWords - 1] < 0 : ((int32_t)y[kDigitWords - 1] >= 0 && nz);
-        if (out) {
-            c = 0;
-#pragma unroll
-            for (int w = 0; w < kDigitWords; w++) {
-                const int64_t v = (int64_t)x[w] + (neg ? (int64_t)prm->Pw[w] : -(int64_t)prm->Pw[w]) + c;
-                x[w] = (uint32_t)v;
-                c = v >> 32;
-            }
-        }
-    }
+    (void)crt_finish(acc, f, prm, x);
     uint4* dst = (uint4*)(digits + ((size_t)comp * kchunk + slot) * kDigitLimbs);
     dst[0] = make_uint4(x[0], x[1], x[2], x[3]);
     dst[1] = make_uint4(x[4], x[5], x[6], x[7]);
@@ -1725,78 +1741,219 @@ __global__ __launch_bounds__(256) void lift_rows_kernel(const int8_t* __restrict
     for (int col = lane * 16; col < pitch; col += 1024) *(uint4*)(dst + col) = *(const uint4*)(src + col);
 }
 
-template <int kFusedComps, int kFusedWaves>
-__global__ __launch_bounds__(kFusedWaves * 64) void lift_gemv_crt_kernel(
-    const int8_t* __restrict__ Sperm, int n, int pitch, const int8_t* __restrict__ rho,
-    const LiftParams* __restrict__ prm, uint64_t* __restrict__ digits, int kchunk, int slot,
-    uint64_t* __restrict__ xlow) {
+// The block has ceil(batches / 2) waves (batch: eight rows), each holding
+// two batches' loads in flight at once; at least kFusedMinThreads threads so
+// that every CRT constant has a thread to fetch it.
+constexpr int kFusedComps = 4, kFusedBatches = 2;
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+// buffer resource word 3 for raw byte-addressed loads (32-bit data format),
+// and the cache-policy operand of a non-temporal load
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kCacheNT = 2;
+constexpr int kFusedMinThreads = kNumPrimes * (kDigitWords + 1);
+
+__global__ __launch_bounds__(1024) void lift_gemv_crt_kernel(const int8_t* __restrict__ Sperm, int n, int pitch,
+                                                            int E, const int8_t* __restrict__ rho,
+                                                            const LiftParams* __restrict__ prm,
+                                                            uint8_t* __restrict__ urec,
+                                                            uint64_t* __restrict__ xlow) {
+    constexpr int C = kFusedComps, KB = kFusedBatches;
+    constexpr int kTabD = kNumPrimes * (kDigitWords + 1), kTabU = kNumPrimes * 4;
+    constexpr int NP = 8 / C;  // primes per batch
+    static_assert(kTabU <= kTabD && kTabD == kFusedMinThreads, "table fetch");
     __shared__ CrtTables T;
-    __shared__ uint32_t sU[kNumPrimes][kFusedComps];
-    const int E = prm->E;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int c0 = blockIdx.x * kFusedComps;
-    load_crt_tables(T, prm, threadIdx.x, kFusedWaves * 64);
-    const int nrows = E * kFusedComps;
-    for (int rb = wave * 8; rb < nrows; rb += kFusedWaves * 8) {
-        // rows rb .. rb + 7 (row r: prime r / kFusedComps, component r mod kFusedComps)
-        const int8_t* rowp[8];
+    __shared__ int sY[kNumPrimes][C];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: row addresses stay scalar
+    const int nw = blockDim.x >> 6;
+    const int c0 = blockIdx.x * C;
+    // The CRT constants are fetched now and stored to LDS after the
+    // contraction, so the fetch overlaps the row loads instead of preceding them.
+    const double tabd = tid < kNumPrimes * kDigitWords ? (&prm->Wd[0][0])[tid]
+                        : tid < kTabD                ? prm->qrec[tid - kNumPrimes * kDigitWords]
+                                                     : 0.0;
+    uint32_t tabu = 0;
+    if (tid < kTabU) {
+        const int l = tid >> 2, f = tid & 3;
+        tabu = f == 0 ? prm->q[l] : f == 1 ? prm->mu16[l] : f == 2 ? prm->cinv[l] : prm->mu32[l];
+    }
+    // rows (prime r / C, component r mod C); batch b holds rows 8 b .. 8 b + 7
+    // and wave w the batches w and w + nw.  Batches past the last re-read it
+    // and rows past the last re-read it too; their sums are dropped.
+    const int nrows = E * C, nb = (nrows + 7) >> 3;
+    // the rows are read through one buffer resource over the live primes'
+    // matrices (at most 53 n pitch < 2^32 bytes), each at a scalar offset
+    const __amdgpu_buffer_rsrc_t srs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)Sperm, 0, (int)((size_t)E * n * pitch), kBufferWord3);
+    uint32_t rowo[KB][8];
+    const int8_t* rvp[KB][NP];
+#pragma unroll
+    for (int kb = 0; kb < KB; kb++) {
+        const int rb = 8 * min(wave + nw * kb, nb - 1);
 #pragma unroll
         for (int r = 0; r < 8; r++) {
             const int rr = min(rb + r, nrows - 1);
-            const int jl = rr / kFusedComps, comp = min(c0 + rr % kFusedComps, n - 1);
-            rowp[r] = Sperm + ((size_t)jl * n + comp) * pitch;
+            const int jl = rr / C, comp = min(c0 + rr % C, n - 1);
+            rowo[kb][r] = (uint32_t)(((size_t)jl * n + comp) * pitch);
         }
-        // the batch's primes: row r takes prime rb / kFusedComps + r / kFusedComps
-        constexpr int NP = kFusedComps >= 8 ? 1 : 8 / kFusedComps;
-        const int8_t* rvp[NP];
 #pragma unroll
-        for (int p = 0; p < NP; p++) rvp[p] = rho + (size_t)min(rb / kFusedComps + p, E - 1) * pitch;
-        int acc[8];
+        for (int p = 0; p < NP; p++) rvp[kb][p] = rho + (size_t)min(rb / C + p, E - 1) * pitch;
+    }
+    int acc[KB][8];
 #pragma unroll
-        for (int r = 0; r < 8; r++) acc[r] = 0;
-        for (int col0 = 0; col0 < pitch; col0 += 1024) {
-            const int col = col0 + lane * 16;
-            const bool cin = col < pitch;
-            const int colc = cin ? col : col0;
-            uint4 rvs[NP];
+    for (int kb = 0; kb < KB; kb++)
 #pragma unroll
-            for (int p = 0; p < NP; p++) rvs[p] = cin ? *(const uint4*)(rvp[p] + colc) : make_uint4(0, 0, 0, 0);
-            uint4 sv[8];
+        for (int r = 0; r < 8; r++) acc[kb][r] = 0;
+    for (int col0 = 0; col0 < pitch; col0 += 1024) {
+        const int col = col0 + lane * 16;
+        const bool cin = col < pitch;
+        const uint32_t colc = cin ? col : col0;
+        // every load is issued before any is used; lanes past the pitch
+        // re-read the pass's first column and take rho as zero
+        uint4 sv[KB][8], rvs[KB][NP];
 #pragma unroll
-            for (int r = 0; r < 8; r++) sv[r] = *(const uint4*)(rowp[r] + colc);
+        for (int kb = 0; kb < KB; kb++) {
+#pragma unroll
+            for (int p = 0; p < NP; p++) rvs[kb][p] = *(const uint4*)(rvp[kb][p] + colc);
 #pragma unroll
             for (int r = 0; r < 8; r++) {
-                const uint4 rv = rvs[NP == 1 ? 0 : r / kFusedComps];
-                int a = acc[r];
-                a = __builtin_amdgcn_sdot4((int)sv[r].x, (int)rv.x, a, false);
-                a = __builtin_amdgcn_sdot4((int)sv[r].y, (int)rv.y, a, false);
-                a = __builtin_amdgcn_sdot4((int)sv[r].z, (int)rv.z, a, false);
-                a = __builtin_amdgcn_sdot4((int)sv[r].w, (int)rv.w, a, false);
-                acc[r] = a;
+                // each row is read once per step: a non-temporal (streaming) load
+                const v4u t = __builtin_amdgcn_raw_buffer_load_b128(srs, colc, rowo[kb][r], kCacheNT);
+                sv[kb][r] = make_uint4(t.x, t.y, t.z, t.w);
             }
         }
-        wave_sum_rows<8>(acc, lane);
-        if ((lane & 7) == 0) {
-            const int rr = rb + ((lane >> 3) & 7);
-            if (rr < nrows) {
-                const int jl = rr / kFusedComps;
-                sU[jl][rr % kFusedComps] = mod_i32(acc[0], prm->q[jl], prm->mu32[jl]);
+#pragma unroll
+        for (int kb = 0; kb < KB; kb++)
+#pragma unroll
+            for (int p = 0; p < NP; p++) {
+                rvs[kb][p].x = cin ? rvs[kb][p].x : 0u;
+                rvs[kb][p].y = cin ? rvs[kb][p].y : 0u;
+                rvs[kb][p].z = cin ? rvs[kb][p].z : 0u;
+                rvs[kb][p].w = cin ? rvs[kb][p].w : 0u;
+            }
+#pragma unroll
+        for (int kb = 0; kb < KB; kb++) {
+#pragma unroll
+            for (int r = 0; r < 8; r++) {
+                const uint4 rv = rvs[kb][r / C];
+                int a = acc[kb][r];
+                a = __builtin_amdgcn_sdot4((int)sv[kb][r].x, (int)rv.x, a, false);
+                a = __builtin_amdgcn_sdot4((int)sv[kb][r].y, (int)rv.y, a, false);
+                a = __builtin_amdgcn_sdot4((int)sv[kb][r].z, (int)rv.z, a, false);
+                a = __builtin_amdgcn_sdot4((int)sv[kb][r].w, (int)rv.w, a, false);
+                acc[kb][r] = a;
             }
         }
     }
+#pragma unroll
+    for (int kb = 0; kb < KB; kb++) {
+        const int b = wave + nw * kb;
+        if (b >= nb) continue;
+        wave_sum_rows<8>(acc[kb], lane);
+        const int rr = 8 * b + ((lane >> 3) & 7);
+        if ((lane & 7) == 0 && rr < nrows) sY[rr / C][rr % C] = acc[kb][0];
+    }
+    if (tid < kTabD) {
+        if (tid < kNumPrimes * kDigitWords) (&T.Wd[0][0])[tid] = tabd;
+        else T.qrec[tid - kNumPrimes * kDigitWords] = tabd;
+    }
+    if (tid < kTabU) (&T.qc[0][0])[tid] = tabu;
     __syncthreads();
-    // the CRT: sixteen lanes per component, four components per wave
-    if (wave * 4 >= kFusedComps) return;
-    const int s = lane & (kCrtLanes - 1), cl = wave * 4 + lane / kCrtLanes;
+    // The step's share of the CRT, sixteen lanes per component and the
+    // block's four components in wave 0: the balanced u_l, k = round(X / P)
+    // and x mod 2^64 = (acc_0 + acc_1 2^32 - k P) mod 2^64, which need only
+    // the two low words of X.  The full digit is formed later from the
+    // record (u_l, k) this step stores.
+    static_assert(C * kCrtLanes == 64, "one wave of CRT lanes");
+    if (wave != 0) return;
+    const int s = lane & (kCrtLanes - 1), cl = lane / kCrtLanes;
     const int comp = c0 + cl;
-    if (cl >= kFusedComps || comp >= n) return;  // the component's sixteen lanes leave together
-    uint32_t res[kCrtPrimesPerLane];
+    if (comp >= n) return;  // the component's sixteen lanes leave together
+    int ub[kCrtPrimesPerLane];
+    double f = 0.0, a0 = 0.0, a1 = 0.0;
 #pragma unroll
     for (int i = 0; i < kCrtPrimesPerLane; i++) {
         const int l = s + kCrtLanes * i;
-        res[i] = l < E ? sU[l][cl] : 0u;
+        ub[i] = 0;
+        if (l >= E) continue;
+        const uint32_t q = T.qc[l][0];
+        const uint32_t u = red16(mod_i32(sY[l][cl], q, T.qc[l][3]) * T.qc[l][2], q, T.qc[l][1]);
+        ub[i] = balanced(u, q);
+        f = fma((double)ub[i], T.qrec[l], f);
+        a0 = fma((double)ub[i], T.Wd[l][0], a0);
+        a1 = fma((double)ub[i], T.Wd[l][1], a1);
     }
-    crt_digit(T, prm, E, s, res, comp, digits, kchunk, slot, xlow);
+    f = quad_add<8>(quad_add<4>(quad_add<2>(quad_add<1>(f))));
+    a0 = quad_add<8>(quad_add<4>(quad_add<2>(quad_add<1>(a0))));
+    a1 = quad_add<8>(quad_add<4>(quad_add<2>(quad_add<1>(a1))));
+    int64_t ki = (int64_t)rint(f);
+    const bool near = fabs(f - (double)ki) > 0.5 - 0x1p-30;
+    if (__builtin_amdgcn_ballot_w64(near) != 0) {
+        // rare: some component's X / P lies near a half-integer, so its k
+        // needs every word of X (the whole wave takes this branch)
+        double acc[kDigitWords];
+#pragma unroll
+        for (int w = 0; w < kDigitWords; w++) acc[w] = 0.0;
+#pragma unroll
+        for (int i = 0; i < kCrtPrimesPerLane; i++) {
+            const int l = min(s + kCrtLanes * i, kNumPrimes - 1);  // ub = 0 past E
+#pragma unroll
+            for (int w = 0; w < kDigitWords; w++) acc[w] = fma((double)ub[i], T.Wd[l][w], acc[w]);
+        }
+#pragma unroll
+        for (int w = 0; w < kDigitWords; w++) acc[w] = quad_add<8>(quad_add<4>(quad_add<2>(quad_add<1>(acc[w]))));
+        uint32_t x[kDigitWords];
+        ki = crt_finish(acc, f, prm, x);
+    }
+    uint8_t* rec = urec + (size_t)comp * 64;
+#pragma unroll
+    for (int i = 0; i < kCrtPrimesPerLane; i++) {
+        const int l = s + kCrtLanes * i;
+        if (l < E) rec[l] = (uint8_t)ub[i];
+    }
+    if (s == 0) {
+        rec[63] = (uint8_t)ki;
+        const uint64_t P64 = ((uint64_t)prm->Pw[1] << 32) | prm->Pw[0];
+        xlow[comp] = (uint64_t)(int64_t)a0 + ((uint64_t)(int64_t)a1 << 32) - (uint64_t)ki * P64;
+    }
+}
+
+// The digits of a run of steps from their records: one thread per (step,
+// component) forms X = sum_l u_l (P / q_l) word by word (exact in double, as
+// above) and subtracts the recorded k P.
+__global__ __launch_bounds__(256) void crt_records_kernel(const uint8_t* __restrict__ urec, int nrec, int n,
+                                                          const LiftParams* __restrict__ prm,
+                                                          uint64_t* __restrict__ digits, int dstride, int slot0) {
+    __shared__ double sW[kNumPrimes][kDigitWords];
+    for (int i = threadIdx.x; i < kNumPrimes * kDigitWords; i += 256) (&sW[0][0])[i] = (&prm->Wd[0][0])[i];
+    __syncthreads();
+    const int E = prm->E;
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (size_t)nrec * n) return;
+    const int rs = (int)(idx / n), comp = (int)(idx % n);
+    const uint4* rp = (const uint4*)(urec + idx * 64);
+    uint32_t wv[16];
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+        const uint4 t = rp[v];
+        wv[4 * v] = t.x, wv[4 * v + 1] = t.y, wv[4 * v + 2] = t.z, wv[4 * v + 3] = t.w;
+    }
+    double acc[kDigitWords];
+#pragma unroll
+    for (int w = 0; w < kDigitWords; w++) acc[w] = 0.0;
+#pragma unroll
+    for (int l = 0; l < kNumPrimes; l++) {
+        if (l >= E) break;
+        const double u = (double)(int8_t)(wv[l >> 2] >> (8 * (l & 3)));
+#pragma unroll
+        for (int w = 0; w < kDigitWords; w++) acc[w] = fma(u, sW[l][w], acc[w]);
+    }
+    uint32_t x[kDigitWords];
+    crt_sub_kP(acc, (int64_t)(int8_t)(wv[15] >> 24), prm, x);
+    uint4* dst = (uint4*)(digits + ((size_t)comp * dstride + slot0 + rs) * kDigitLimbs);
+    dst[0] = make_uint4(x[0], x[1], x[2], x[3]);
+    dst[1] = make_uint4(x[4], x[5], x[6], x[7]);
+    dst[2] = make_uint4(x[8], x[9], x[10], x[11]);
 }
 
 // ---------------------------------------------------------------- lift: residual
@@ -2002,7 +2159,7 @@ bool lift_fused_fits(const Layout& L) {
         const char* e = std::getenv("ES_FUSED_CRT");
         return e && e[0] == '0';
     }();
-    return !off && L.c == 1 && L.pitch >= 1024;
+    return !off && fused_lift_shape(L.n, L.c, L.pitch);
 }
 
 hipError_t launch_lift_rows(const Layout& L, uint8_t* ws, int E, hipStream_t st) {
@@ -2013,14 +2170,25 @@ hipError_t launch_lift_rows(const Layout& L, uint8_t* ws, int E, hipStream_t st)
 }
 
 hipError_t launch_lift_contract_crt(const Layout& L, uint8_t* ws, int E, int slot, hipStream_t st) {
-    (void)E;
-    // four components and sixteen waves per block (two, eight components and
-    // eight-wave blocks measured slower at n = 1024)
-    constexpr int C = 4, W = 16;
-    hipLaunchKernelGGL((lift_gemv_crt_kernel<C, W>), dim3((L.n + C - 1) / C), dim3(W * 64), 0, st,
-                       (const int8_t*)(ws + L.off_Sperm), L.n, L.pitch, (const int8_t*)(ws + L.off_rho),
-                       (const LiftParams*)(ws + L.off_params), L.dig_dev ? L.dig_dev : (uint64_t*)(ws + L.off_digits),
-                       L.kchunk, slot, (uint64_t*)(ws + L.off_xlow));
+    if (E < 1 || E > kNumPrimes) return hipErrorInvalidValue;
+    if (!fused_lift_shape(L.n, L.c, L.pitch)) return hipErrorInvalidValue;
+    // four components per block (two and eight measured slower at n = 1024)
+    const int nb = (E * kFusedComps + 7) / 8;
+    const int waves = max((nb + kFusedBatches - 1) / kFusedBatches, (kFusedMinThreads + 63) / 64);
+    if (slot < 0 || slot >= L.krec) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(lift_gemv_crt_kernel, dim3((L.n + kFusedComps - 1) / kFusedComps), dim3(waves * 64), 0, st,
+                       (const int8_t*)(ws + L.off_Sperm), L.n, L.pitch, E, (const int8_t*)(ws + L.off_rho),
+                       (const LiftParams*)(ws + L.off_params), ws + L.off_urec + (size_t)slot * L.n * 64,
+                       (uint64_t*)(ws + L.off_xlow));
+    return hipGetLastError();
+}
+
+hipError_t launch_lift_crt_records(const Layout& L, uint8_t* ws, int nrec, int slot0, hipStream_t st) {
+    if (nrec < 1 || nrec > L.krec || slot0 < 0 || slot0 + nrec > L.kchunk) return hipErrorInvalidValue;
+    const size_t threads = (size_t)nrec * L.n;
+    hipLaunchKernelGGL(crt_records_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
+                       (const uint8_t*)(ws + L.off_urec), nrec, L.n, (const LiftParams*)(ws + L.off_params),
+                       L.dig_dev ? L.dig_dev : (uint64_t*)(ws + L.off_digits), L.kchunk, slot0);
     return hipGetLastError();
 }
 

@@ -143,6 +143,18 @@ int es_set_blocked_inverse(int on);
 int es_set_gpu_reconstruction(int on);
 
 /*
+ * For later solves on the calling thread with one right-hand side and
+ * n > 512: each lift step stores, per component, its balanced residues and
+ * the CRT quotient k in a 64-byte record on the device, and one launch turns
+ * up to `steps` steps' records into their digits.  steps = 0 restores the
+ * default (16 MiB of records); a larger value than the default is taken as
+ * the default.  Results are unchanged: smaller values only add launches and
+ * shrink the workspace (so es_workspace_bytes, called on the same thread
+ * afterwards, may return less).  Returns ES_EINVAL for steps < 0.
+ */
+int es_set_lift_record_steps(int32_t steps);
+
+/*
  * Opt-in kernel timing for measurement.  With es_set_profiling(1) on a
  * thread, later solves on that thread bracket every launch of the hot
  * kernels with a pair of HIP events on the solve's stream (small added gaps

@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import dixon_adic_lifting_amd as es
-from dixon_adic_lifting_amd import workloads as W
+from dixon_adic_lifting_amd import _lib, workloads as W
 from oracle import dixon
 
 pytestmark = pytest.mark.gpu
@@ -134,3 +134,22 @@ def test_lift_fused_contraction_ragged(n, seed, primes):
     words, mask, m = es.lift_digits(torch.as_tensor(A).cuda(), torch.as_tensor(b).cuda(), m=3)
     assert m == 3
     check_padic_identity(A, b, words, mask, m, primes, rows=range(n))
+
+
+def test_lift_records_in_chunks(primes):
+    """With one right-hand side and n > 512 each step keeps (u_l, k) records
+    and a later launch forms the digits.  Holding three steps' records at a
+    time (chunks 3, 3, 1 over seven steps) must give the same digits as the
+    default (all seven at once), and those digits satisfy A X = b mod P^m."""
+    n = 517
+    A, b = W.uniform_system(n, 1, 24, 23)
+    dA, db = torch.as_tensor(A).cuda(), torch.as_tensor(b).cuda()
+    ref, mask, m = es.lift_digits(dA, db, m=7)
+    try:
+        _lib.set_lift_record_steps(3)
+        got, mask2, m2 = es.lift_digits(dA, db, m=7)
+    finally:
+        _lib.set_lift_record_steps(0)
+    assert (mask2, m2) == (mask, m)
+    assert np.array_equal(np.asarray(got), np.asarray(ref))
+    check_padic_identity(A, b, got, mask, m, primes, rows=range(0, n, 7))
