@@ -83,7 +83,18 @@ struct Profiler : KernelTimer {
         marks.push_back({cls, used - 1});
         return (long)(used - 1);
     }
+    // one kernel: the next launch records the pair itself; stop() records nothing
+    long start_one(int cls) override {
+        if (!on) return -1;
+        hipEvent_t e0 = next();
+        hipEvent_t e1 = e0 ? next() : nullptr;
+        if (!e1) return -1;
+        pending_launch_events() = LaunchEvents{e0, e1};
+        marks.push_back({cls, used - 2});
+        return -1;
+    }
     void stop(long idx) override {
+        pending_launch_events() = LaunchEvents{};  // unused if the launch did not happen
         if (idx < 0) return;
         hipEvent_t e = next();
         if (e) (void)hipEventRecord(e, st);
@@ -185,10 +196,10 @@ int run_inverse(const int64_t* dA, uint8_t* ws, hipStream_t st, Prep* pr, int* f
     } else if (blocked) {
         // one kernel at a time (also the form that per-kernel timing measures)
         for (int K = 0; K < L.n; K += kPanel) {
-            ev = prof->start(KC_PANEL);
+            ev = prof->start_one(KC_PANEL);
             HIP_CHECK(launch_gj_panel(L, ws, K, st));
             prof->stop(ev);
-            ev = prof->start(KC_UPDATE);
+            ev = prof->start_one(KC_UPDATE);
             HIP_CHECK(launch_gj_update(L, ws, K, st));
             prof->stop(ev);
         }
@@ -263,23 +274,23 @@ int run_lift(const int64_t* dA, const int64_t* db, uint8_t* ws, hipStream_t st, 
         for (int s = 0; s < cnt; s++) {
             long ev;
             if (fused) {
-                ev = prof->start(KC_CONTRACT);
+                ev = prof->start_one(KC_CONTRACT);
                 HIP_CHECK(launch_lift_contract_crt(L, ws, ls.E, s % L.krec, st));
                 prof->stop(ev);
             } else {
-                ev = prof->start(KC_CONTRACT);
+                ev = prof->start_one(KC_CONTRACT);
                 HIP_CHECK(launch_lift_contract(L, ws, ls.E, st));
                 prof->stop(ev);
-                ev = prof->start(KC_CRT);
+                ev = prof->start_one(KC_CRT);
                 HIP_CHECK(launch_lift_crt(L, ws, s, st));
                 prof->stop(ev);
             }
-            ev = prof->start(KC_RESIDUAL);
+            ev = prof->start_one(KC_RESIDUAL);
             HIP_CHECK(launch_lift_residual(L, ws, pr.a32, dA, st));
             prof->stop(ev);
             if (fused && (s % L.krec == L.krec - 1 || s == cnt - 1)) {
                 // the digits of the steps whose records are held
-                ev = prof->start(KC_CRT);
+                ev = prof->start_one(KC_CRT);
                 HIP_CHECK(launch_lift_crt_records(L, ws, s % L.krec + 1, s - s % L.krec, st));
                 prof->stop(ev);
             }

@@ -1,12 +1,30 @@
 // Internal declarations shared by the host runtime (api.cpp, host.cpp) and
 // the HIP kernels (kernels.hip).  Not part of the public C ABI.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
 #include <cstdint>
 
 namespace es {
+
+// Events that the next kernel launched on this thread records at its own
+// start and end (from its dispatch, with no marker packets around it); set
+// by the per-kernel timer, empty otherwise.
+struct LaunchEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchEvents& pending_launch_events();
+
+// Every kernel launch of the library goes through here.
+template <typename F, typename... Args>
+inline void es_launch(F kernel, const dim3& grid, const dim3& block, uint32_t shmem, hipStream_t st, Args... args) {
+    LaunchEvents& pe = pending_launch_events();
+    const LaunchEvents ev = pe;
+    pe = LaunchEvents{};
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, ev.start, ev.stop, 0u, args...);
+}
 
 constexpr int kNumPrimes = 53;   // odd primes below 256
 constexpr int kDigitLimbs = 6;   // one base-P digit, 384-bit two's complement

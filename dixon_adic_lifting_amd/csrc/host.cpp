@@ -33,6 +33,11 @@ typedef unsigned __int128 u128;
 
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+LaunchEvents& pending_launch_events() {
+    static thread_local LaunchEvents ev;
+    return ev;
+}
+
 static thread_local int g_krec_cap = 0;  // 0: the default record chunk
 
 void set_lift_record_cap(int steps) { g_krec_cap = steps; }

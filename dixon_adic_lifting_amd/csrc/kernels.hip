@@ -120,7 +120,7 @@ hipError_t launch_fill_u32(uint32_t* p, size_t count, uint32_t value, hipStream_
     if (count == 0) return hipSuccess;
     size_t blocks = (count + 255) / 256;
     if (blocks > 8192) blocks = 8192;
-    hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p, count, value);
+    es_launch(fill_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p, count, value);
     return hipGetLastError();
 }
 
@@ -184,15 +184,15 @@ __global__ __launch_bounds__(256) void col_final_kernel(const double* __restrict
 hipError_t launch_stats(const int64_t* A, const int64_t* b, const Layout& L, uint8_t* ws,
                         hipStream_t st) {
     const int n = L.n, c = L.c, nrb = (n + 63) / 64;
-    hipLaunchKernelGGL(row_stats_kernel, dim3((n + 3) / 4), dim3(256), 0, st, A, n,
+    es_launch(row_stats_kernel, dim3((n + 3) / 4), dim3(256), 0, st, A, n,
                        (uint64_t*)(ws + L.off_rowmax), (double*)(ws + L.off_rownorm));
-    hipLaunchKernelGGL(col_part_kernel, dim3((n + 255) / 256, nrb), dim3(256), 0, st, A, n, n,
+    es_launch(col_part_kernel, dim3((n + 255) / 256, nrb), dim3(256), 0, st, A, n, n,
                        (double*)(ws + L.off_colpart));
-    hipLaunchKernelGGL(col_final_kernel, dim3((n + 255) / 256), dim3(256), 0, st,
+    es_launch(col_final_kernel, dim3((n + 255) / 256), dim3(256), 0, st,
                        (const double*)(ws + L.off_colpart), nrb, n, (double*)(ws + L.off_colnorm));
-    hipLaunchKernelGGL(col_part_kernel, dim3((c + 255) / 256, nrb), dim3(256), 0, st, b, n, c,
+    es_launch(col_part_kernel, dim3((c + 255) / 256, nrb), dim3(256), 0, st, b, n, c,
                        (double*)(ws + L.off_bpart));
-    hipLaunchKernelGGL(col_final_kernel, dim3((c + 255) / 256), dim3(256), 0, st,
+    es_launch(col_final_kernel, dim3((c + 255) / 256), dim3(256), 0, st,
                        (const double*)(ws + L.off_bpart), nrb, c, (double*)(ws + L.off_bnorm));
     return hipGetLastError();
 }
@@ -253,13 +253,13 @@ hipError_t launch_residues(const int64_t* A, const Layout& L, uint8_t* ws, bool 
     // caller guarantees small (< 2^32) entries whenever make_a32 is set
     dim3 grid(L.n, (L.pitch / 4 + 255) / 256);
     if (make_a32)
-        hipLaunchKernelGGL(residue_kernel<true>, grid, dim3(256), 0, st, A, L.n, L.pitch,
+        es_launch(residue_kernel<true>, grid, dim3(256), 0, st, A, L.n, L.pitch,
                            ws + L.off_S, (int32_t*)(ws + L.off_A32), 1, balanced_out ? 1 : 0);
     else
-        hipLaunchKernelGGL(residue_kernel<false>, grid, dim3(256), 0, st, A, L.n, L.pitch,
+        es_launch(residue_kernel<false>, grid, dim3(256), 0, st, A, L.n, L.pitch,
                            ws + L.off_S, (int32_t*)(ws + L.off_A32), 0, balanced_out ? 1 : 0);
     if (!balanced_out)  // the step-wise elimination takes its first pivot from here
-        hipLaunchKernelGGL(pivot0_kernel, dim3(kNumPrimes), dim3(256), 0, st,
+        es_launch(pivot0_kernel, dim3(kNumPrimes), dim3(256), 0, st,
                            (const uint8_t*)(ws + L.off_S), L.n, L.pitch, (int*)(ws + L.off_piv));
     return hipGetLastError();
 }
@@ -486,11 +486,11 @@ static void launch_gj_t(const Layout& L, uint8_t* ws, int k, hipStream_t st) {
     constexpr int ROWS = 4 * (64 / LPR) * RI;
     dim3 grid((L.n + ROWS - 1) / ROWS, kNumPrimes);
     if (k == L.n - 1)
-        hipLaunchKernelGGL((gj_step_kernel<LPR, RI, true>), grid, dim3(256), 0, st, ws + L.off_S, L.n, L.pitch,
+        es_launch((gj_step_kernel<LPR, RI, true>), grid, dim3(256), 0, st, ws + L.off_S, L.n, L.pitch,
                            k, (int*)(ws + L.off_piv), (int*)(ws + L.off_rowpos), ws + L.off_pend,
                            (int*)(ws + L.off_flags));
     else
-        hipLaunchKernelGGL((gj_step_kernel<LPR, RI, false>), grid, dim3(256), 0, st, ws + L.off_S, L.n,
+        es_launch((gj_step_kernel<LPR, RI, false>), grid, dim3(256), 0, st, ws + L.off_S, L.n,
                            L.pitch, k, (int*)(ws + L.off_piv), (int*)(ws + L.off_rowpos), ws + L.off_pend,
                            (int*)(ws + L.off_flags));
 }
@@ -507,7 +507,7 @@ hipError_t launch_gj_step(const Layout& L, uint8_t* ws, int k, hipStream_t st) {
             break;
     }
     if (k == L.n - 1)
-        hipLaunchKernelGGL(gj_finalize_kernel, dim3(kNumPrimes), dim3(256), 0, st, ws + L.off_S, L.n,
+        es_launch(gj_finalize_kernel, dim3(kNumPrimes), dim3(256), 0, st, ws + L.off_S, L.n,
                            L.pitch, (const int*)(ws + L.off_piv), (const uint8_t*)(ws + L.off_pend));
     return hipGetLastError();
 }
@@ -1240,17 +1240,17 @@ hipError_t launch_gj_panel(const Layout& L, uint8_t* ws, int K, hipStream_t st) 
     int8_t* GT = (int8_t*)(ws + L.off_GT);
     const dim3 g(kNumPrimes), b(1024);
     switch (panel_kind(L, K)) {
-        case 0: hipLaunchKernelGGL((gj_panel_kernel<1, true>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT); break;
-        case 1: hipLaunchKernelGGL((gj_panel_kernel<1, false>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT); break;
-        case 2: hipLaunchKernelGGL((gj_panel_kernel<2, false>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT); break;
-        default: hipLaunchKernelGGL((gj_panel_kernel<4, false>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT); break;
+        case 0: es_launch((gj_panel_kernel<1, true>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT); break;
+        case 1: es_launch((gj_panel_kernel<1, false>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT); break;
+        case 2: es_launch((gj_panel_kernel<2, false>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT); break;
+        default: es_launch((gj_panel_kernel<4, false>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT); break;
     }
     return hipGetLastError();
 }
 
 hipError_t launch_gj_update(const Layout& L, uint8_t* ws, int K, hipStream_t st) {
     dim3 grid((L.pitch + 127) / 128, (L.n + 127) / 128, kNumPrimes);
-    hipLaunchKernelGGL(gj_update_kernel, grid, dim3(256), 0, st, (int8_t*)(ws + L.off_S), L.n, L.pitch, K,
+    es_launch(gj_update_kernel, grid, dim3(256), 0, st, (int8_t*)(ws + L.off_S), L.n, L.pitch, K,
                        (const int*)(ws + L.off_rowpos), (const int*)(ws + L.off_flags),
                        (const int8_t*)(ws + L.off_GT), K + kPanel);
     return hipGetLastError();
@@ -1268,20 +1268,20 @@ hipError_t launch_gj_panel_rest(const Layout& L, uint8_t* ws, int K, hipStream_t
     const dim3 g(np + nupd), b(1024);
     if (np + nupd == 0) return hipSuccess;
     switch (K < L.n ? panel_kind(L, K) : 1) {
-        case 0: hipLaunchKernelGGL((gj_panel_rest_kernel<1, true>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT, ntx, nty); break;
-        case 1: hipLaunchKernelGGL((gj_panel_rest_kernel<1, false>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT, ntx, nty); break;
-        case 2: hipLaunchKernelGGL((gj_panel_rest_kernel<2, false>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT, ntx, nty); break;
-        default: hipLaunchKernelGGL((gj_panel_rest_kernel<4, false>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT, ntx, nty); break;
+        case 0: es_launch((gj_panel_rest_kernel<1, true>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT, ntx, nty); break;
+        case 1: es_launch((gj_panel_rest_kernel<1, false>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT, ntx, nty); break;
+        case 2: es_launch((gj_panel_rest_kernel<2, false>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT, ntx, nty); break;
+        default: es_launch((gj_panel_rest_kernel<4, false>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT, ntx, nty); break;
     }
     return hipGetLastError();
 }
 
 hipError_t launch_gj_gather_next(const Layout& L, uint8_t* ws, int K, hipStream_t st) {
-    hipLaunchKernelGGL(gj_gather_kernel, dim3((L.pitch + 255) / 256, kNumPrimes), dim3(256), 0, st,
+    es_launch(gj_gather_kernel, dim3((L.pitch + 255) / 256, kNumPrimes), dim3(256), 0, st,
                        (const int8_t*)(ws + L.off_S), L.n, L.pitch, K, (const int*)(ws + L.off_piv),
                        (const int*)(ws + L.off_flags), (int8_t*)(ws + L.off_GT));
     if (K + kPanel < L.n)
-        hipLaunchKernelGGL(gj_next_kernel, dim3((L.n + 63) / 64, kNumPrimes), dim3(256), 0, st,
+        es_launch(gj_next_kernel, dim3((L.n + 63) / 64, kNumPrimes), dim3(256), 0, st,
                            (int8_t*)(ws + L.off_S), L.n, L.pitch, K, (const int*)(ws + L.off_rowpos),
                            (const int*)(ws + L.off_flags), (const int8_t*)(ws + L.off_GT));
     return hipGetLastError();
@@ -1303,7 +1303,7 @@ __global__ __launch_bounds__(256) void export_inverse_kernel(const int8_t* __res
 }
 
 hipError_t launch_export_inverse(const Layout& L, const uint8_t* ws, int8_t* B, hipStream_t st) {
-    hipLaunchKernelGGL(export_inverse_kernel, dim3(L.n, kNumPrimes), dim3(256), 0, st,
+    es_launch(export_inverse_kernel, dim3(L.n, kNumPrimes), dim3(256), 0, st,
                        (const int8_t*)(ws + L.off_S), L.n, L.pitch, (const int*)(ws + L.off_piv),
                        (const int*)(ws + L.off_rowpos), (const int*)(ws + L.off_flags), B);
     return hipGetLastError();
@@ -2076,12 +2076,12 @@ hipError_t launch_split_b(const int64_t* b, const Layout& L, uint8_t* ws, int E,
     if (e != hipSuccess) return e;
     const dim3 grid((L.n + 3) / 4);
     if (L.c == 1)
-        hipLaunchKernelGGL((residual_kernel<int64_t, 1>), grid, dim3(256), 0, st, (const int64_t*)nullptr,
+        es_launch((residual_kernel<int64_t, 1>), grid, dim3(256), 0, st, (const int64_t*)nullptr,
                            L.n, L.c, (int64_t*)(ws + L.off_R), (const uint64_t*)(ws + L.off_xlow),
                            (const LiftParams*)(ws + L.off_params), (const int*)(ws + L.off_rowpos),
                            (int8_t*)(ws + L.off_rho), L.pitch, 1);
     else
-        hipLaunchKernelGGL((residual_kernel<int64_t, 16>), grid, dim3(256), 0, st, (const int64_t*)nullptr,
+        es_launch((residual_kernel<int64_t, 16>), grid, dim3(256), 0, st, (const int64_t*)nullptr,
                            L.n, L.c, (int64_t*)(ws + L.off_R), (const uint64_t*)(ws + L.off_xlow),
                            (const LiftParams*)(ws + L.off_params), (const int*)(ws + L.off_rowpos),
                            (int8_t*)(ws + L.off_rho), L.pitch, 1);
@@ -2092,7 +2092,7 @@ template <int LPR, int RI, int CT>
 static void launch_gemv_t(const Layout& L, uint8_t* ws, int E, hipStream_t st) {
     constexpr int ROWS = 4 * (64 / LPR) * RI;
     dim3 grid((L.n + ROWS - 1) / ROWS, E);
-    hipLaunchKernelGGL((lift_gemv_kernel<LPR, RI, CT>), grid, dim3(256), 0, st,
+    es_launch((lift_gemv_kernel<LPR, RI, CT>), grid, dim3(256), 0, st,
                        (const int8_t*)(ws + L.off_S), L.n, L.pitch, L.c, (const int8_t*)(ws + L.off_rho),
                        (const LiftParams*)(ws + L.off_params), (const int*)(ws + L.off_rowpos),
                        ws + L.off_U);
@@ -2132,7 +2132,7 @@ static int gemv_rows_per_wave() {
 template <int RI>
 static void launch_gemv1_t(const Layout& L, uint8_t* ws, int E, hipStream_t st) {
     dim3 grid((L.n + 4 * RI - 1) / (4 * RI), E);
-    hipLaunchKernelGGL(lift_gemv1_kernel<RI>, grid, dim3(256), 0, st, (const int8_t*)(ws + L.off_S), L.n, L.pitch,
+    es_launch(lift_gemv1_kernel<RI>, grid, dim3(256), 0, st, (const int8_t*)(ws + L.off_S), L.n, L.pitch,
                        (const int8_t*)(ws + L.off_rho), (const LiftParams*)(ws + L.off_params),
                        (const int*)(ws + L.off_rowpos), ws + L.off_U);
 }
@@ -2147,7 +2147,7 @@ hipError_t launch_lift_contract(const Layout& L, uint8_t* ws, int E, hipStream_t
         launch_gemv_c<16>(L, ws, E, st);
     } else {
         dim3 grid((L.n + 4 * kMfmaRowsPerWave - 1) / (4 * kMfmaRowsPerWave), E, (L.c + 15) / 16);
-        hipLaunchKernelGGL(lift_mfma_kernel, grid, dim3(256), 0, st, (const int8_t*)(ws + L.off_S), L.n, L.pitch,
+        es_launch(lift_mfma_kernel, grid, dim3(256), 0, st, (const int8_t*)(ws + L.off_S), L.n, L.pitch,
                            L.c, (const int8_t*)(ws + L.off_rho), (const LiftParams*)(ws + L.off_params),
                            (const int*)(ws + L.off_rowpos), ws + L.off_U);
     }
@@ -2163,7 +2163,7 @@ bool lift_fused_fits(const Layout& L) {
 }
 
 hipError_t launch_lift_rows(const Layout& L, uint8_t* ws, int E, hipStream_t st) {
-    hipLaunchKernelGGL(lift_rows_kernel, dim3((L.n + 3) / 4, E), dim3(256), 0, st, (const int8_t*)(ws + L.off_S),
+    es_launch(lift_rows_kernel, dim3((L.n + 3) / 4, E), dim3(256), 0, st, (const int8_t*)(ws + L.off_S),
                        (const int*)(ws + L.off_rowpos), (const LiftParams*)(ws + L.off_params), L.n, L.pitch,
                        (int8_t*)(ws + L.off_Sperm));
     return hipGetLastError();
@@ -2176,7 +2176,7 @@ hipError_t launch_lift_contract_crt(const Layout& L, uint8_t* ws, int E, int slo
     const int nb = (E * kFusedComps + 7) / 8;
     const int waves = max((nb + kFusedBatches - 1) / kFusedBatches, (kFusedMinThreads + 63) / 64);
     if (slot < 0 || slot >= L.krec) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(lift_gemv_crt_kernel, dim3((L.n + kFusedComps - 1) / kFusedComps), dim3(waves * 64), 0, st,
+    es_launch(lift_gemv_crt_kernel, dim3((L.n + kFusedComps - 1) / kFusedComps), dim3(waves * 64), 0, st,
                        (const int8_t*)(ws + L.off_Sperm), L.n, L.pitch, E, (const int8_t*)(ws + L.off_rho),
                        (const LiftParams*)(ws + L.off_params), ws + L.off_urec + (size_t)slot * L.n * 64,
                        (uint64_t*)(ws + L.off_xlow));
@@ -2186,7 +2186,7 @@ hipError_t launch_lift_contract_crt(const Layout& L, uint8_t* ws, int E, int slo
 hipError_t launch_lift_crt_records(const Layout& L, uint8_t* ws, int nrec, int slot0, hipStream_t st) {
     if (nrec < 1 || nrec > L.krec || slot0 < 0 || slot0 + nrec > L.kchunk) return hipErrorInvalidValue;
     const size_t threads = (size_t)nrec * L.n;
-    hipLaunchKernelGGL(crt_records_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
+    es_launch(crt_records_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
                        (const uint8_t*)(ws + L.off_urec), nrec, L.n, (const LiftParams*)(ws + L.off_params),
                        L.dig_dev ? L.dig_dev : (uint64_t*)(ws + L.off_digits), L.kchunk, slot0);
     return hipGetLastError();
@@ -2194,7 +2194,7 @@ hipError_t launch_lift_crt_records(const Layout& L, uint8_t* ws, int nrec, int s
 
 hipError_t launch_lift_crt(const Layout& L, uint8_t* ws, int slot, hipStream_t st) {
     const int NC = L.n * L.c;
-    hipLaunchKernelGGL(crt_kernel, dim3((NC + 15) / 16), dim3(256), 0, st,
+    es_launch(crt_kernel, dim3((NC + 15) / 16), dim3(256), 0, st,
                        (const LiftParams*)(ws + L.off_params), (const uint8_t*)(ws + L.off_U), NC,
                        L.dig_dev ? L.dig_dev : (uint64_t*)(ws + L.off_digits), L.kchunk, slot,
                        (uint64_t*)(ws + L.off_xlow));
@@ -2211,17 +2211,17 @@ hipError_t launch_lift_residual(const Layout& L, uint8_t* ws, bool a32, const in
     if (a32) {
         const int32_t* A = (const int32_t*)(ws + L.off_A32);
         if (L.c == 1)
-            hipLaunchKernelGGL(residual1_kernel, dim3((L.n + 3) / 4), dim3(256), 0, st, A, L.n, R, xl, prm, rp, rho,
+            es_launch(residual1_kernel, dim3((L.n + 3) / 4), dim3(256), 0, st, A, L.n, R, xl, prm, rp, rho,
                                L.pitch);
         else
-            hipLaunchKernelGGL((residual_kernel<int32_t, 16>), grid, dim3(256), 0, st, A, L.n, L.c, R, xl,
+            es_launch((residual_kernel<int32_t, 16>), grid, dim3(256), 0, st, A, L.n, L.c, R, xl,
                                prm, rp, rho, L.pitch, 0);
     } else {
         if (L.c == 1)
-            hipLaunchKernelGGL((residual_kernel<int64_t, 1>), grid, dim3(256), 0, st, A64, L.n, L.c, R, xl,
+            es_launch((residual_kernel<int64_t, 1>), grid, dim3(256), 0, st, A64, L.n, L.c, R, xl,
                                prm, rp, rho, L.pitch, 0);
         else
-            hipLaunchKernelGGL((residual_kernel<int64_t, 16>), grid, dim3(256), 0, st, A64, L.n, L.c, R, xl,
+            es_launch((residual_kernel<int64_t, 16>), grid, dim3(256), 0, st, A64, L.n, L.c, R, xl,
                                prm, rp, rho, L.pitch, 0);
     }
     return hipGetLastError();

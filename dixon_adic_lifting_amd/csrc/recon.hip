@@ -646,7 +646,7 @@ __global__ __launch_bounds__(256) void numer_kernel(const int* __restrict__ V, i
 
 hipError_t launch_digit_bytes(const uint64_t* digits, int dstride, int m, int j0, int valid_rows, int rows_pad,
                               int Kpad, int8_t* S, int* rowsum, hipStream_t st) {
-    hipLaunchKernelGGL(digit_bytes_kernel, dim3(rows_pad), dim3(256), 0, st, digits, dstride, m, j0, valid_rows,
+    es_launch(digit_bytes_kernel, dim3(rows_pad), dim3(256), 0, st, digits, dstride, m, j0, valid_rows,
                        Kpad, S, rowsum);
     return hipGetLastError();
 }
@@ -655,11 +655,11 @@ hipError_t launch_wchain(const uint32_t* T, const uint32_t* Mw, int m, int TM, d
                          hipStream_t st) {
     const int NW = TM + 1;
     if (NW <= 64 * 8)
-        hipLaunchKernelGGL(wchain_kernel<8>, dim3(m), dim3(64), 0, st, T, Mw, TM, Md, Ncolsp, W);
+        es_launch(wchain_kernel<8>, dim3(m), dim3(64), 0, st, T, Mw, TM, Md, Ncolsp, W);
     else if (NW <= 64 * 32)
-        hipLaunchKernelGGL(wchain_kernel<32>, dim3(m), dim3(64), 0, st, T, Mw, TM, Md, Ncolsp, W);
+        es_launch(wchain_kernel<32>, dim3(m), dim3(64), 0, st, T, Mw, TM, Md, Ncolsp, W);
     else if (NW <= 64 * 64)
-        hipLaunchKernelGGL(wchain_kernel<64>, dim3(m), dim3(64), 0, st, T, Mw, TM, Md, Ncolsp, W);
+        es_launch(wchain_kernel<64>, dim3(m), dim3(64), 0, st, T, Mw, TM, Md, Ncolsp, W);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
@@ -668,14 +668,14 @@ hipError_t launch_wchain(const uint32_t* T, const uint32_t* Mw, int m, int TM, d
 int wchain_words_per_lane(int NW) { return NW <= 64 * 8 ? 8 : NW <= 64 * 32 ? 32 : NW <= 64 * 64 ? 64 : 0; }
 
 hipError_t launch_transpose_offset(const uint8_t* W, int Kpad, int Ncolsp, int8_t* WT, hipStream_t st) {
-    hipLaunchKernelGGL(transpose_offset_kernel, dim3(Ncolsp / 64, Kpad / 64), dim3(256), 0, st, W, Kpad, Ncolsp, WT);
+    es_launch(transpose_offset_kernel, dim3(Ncolsp / 64, Kpad / 64), dim3(256), 0, st, W, Kpad, Ncolsp, WT);
     return hipGetLastError();
 }
 
 hipError_t launch_recon_gemm(const int8_t* S, const int8_t* WT, int Kpad, int NCcp, int Ncolsp, int* V,
                              hipStream_t st) {
     // component tiles vary fastest, so the blocks in flight share weight tiles
-    hipLaunchKernelGGL(recon_gemm_kernel, dim3(NCcp / 128, Ncolsp / 128), dim3(256), 0, st, S, WT, Kpad, Ncolsp, V);
+    es_launch(recon_gemm_kernel, dim3(NCcp / 128, Ncolsp / 128), dim3(256), 0, st, S, WT, Kpad, Ncolsp, V);
     return hipGetLastError();
 }
 
@@ -712,11 +712,11 @@ hipError_t launch_gcd(const uint32_t* Y, int nw, const int* status, int valid_ro
     const dim3 grid(valid_rows);
     const size_t pad = gcd_lds_pad(valid_rows);
     if (cw == 8)
-        hipLaunchKernelGGL(gcd_kernel<8>, grid, dim3(128), pad, st, Y, nw, status, valid_rows, Dw, nwd, G, gstat);
+        es_launch(gcd_kernel<8>, grid, dim3(128), pad, st, Y, nw, status, valid_rows, Dw, nwd, G, gstat);
     else if (cw == 16)
-        hipLaunchKernelGGL(gcd_kernel<16>, grid, dim3(128), pad, st, Y, nw, status, valid_rows, Dw, nwd, G, gstat);
+        es_launch(gcd_kernel<16>, grid, dim3(128), pad, st, Y, nw, status, valid_rows, Dw, nwd, G, gstat);
     else if (cw == 32)
-        hipLaunchKernelGGL(gcd_kernel<32>, grid, dim3(128), pad, st, Y, nw, status, valid_rows, Dw, nwd, G, gstat);
+        es_launch(gcd_kernel<32>, grid, dim3(128), pad, st, Y, nw, status, valid_rows, Dw, nwd, G, gstat);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
@@ -732,19 +732,19 @@ hipError_t launch_numer(const int* V, int Ncolsp, const int* rowsum, int valid_r
     const dim3 grid((valid_rows + 3) / 4);
     switch (numer_words_per_lane(TM + 1)) {
         case 8:
-            hipLaunchKernelGGL(numer_kernel<8>, grid, dim3(256), 0, st, V, Ncolsp, rowsum, valid_rows, Mw, TM, Mtop,
+            es_launch(numer_kernel<8>, grid, dim3(256), 0, st, V, Ncolsp, rowsum, valid_rows, Mw, TM, Mtop,
                                nbits, Y, status);
             break;
         case 16:
-            hipLaunchKernelGGL(numer_kernel<16>, grid, dim3(256), 0, st, V, Ncolsp, rowsum, valid_rows, Mw, TM, Mtop,
+            es_launch(numer_kernel<16>, grid, dim3(256), 0, st, V, Ncolsp, rowsum, valid_rows, Mw, TM, Mtop,
                                nbits, Y, status);
             break;
         case 32:
-            hipLaunchKernelGGL(numer_kernel<32>, grid, dim3(256), 0, st, V, Ncolsp, rowsum, valid_rows, Mw, TM, Mtop,
+            es_launch(numer_kernel<32>, grid, dim3(256), 0, st, V, Ncolsp, rowsum, valid_rows, Mw, TM, Mtop,
                                nbits, Y, status);
             break;
         case 64:
-            hipLaunchKernelGGL(numer_kernel<64>, grid, dim3(256), 0, st, V, Ncolsp, rowsum, valid_rows, Mw, TM, Mtop,
+            es_launch(numer_kernel<64>, grid, dim3(256), 0, st, V, Ncolsp, rowsum, valid_rows, Mw, TM, Mtop,
                                nbits, Y, status);
             break;
         default:

@@ -293,7 +293,7 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
             ev = kt->start(KC_RECON_OTHER);
             HIPOK(launch_digit_bytes(dig, m, m, (int)j0, rows, pl.NCcp, pl.Kpad, S, rowsum, st));
             kt->stop(ev);
-            ev = kt->start(KC_RECON_GEMM);
+            ev = kt->start_one(KC_RECON_GEMM);
             HIPOK(launch_recon_gemm(S, WT, pl.Kpad, pl.NCcp, pl.Ncolsp, VT, st));
             kt->stop(ev);
             ev = kt->start(KC_RECON_OTHER);
@@ -306,7 +306,7 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
             HIPOK(hipMemcpyAsync(sth + j0, std_, (size_t)rows * sizeof(int), hipMemcpyDeviceToHost, st));
             HIPOK(hipEventRecord(words_ready, st));
             if (gpu_gcd) {
-                ev = kt->start(KC_RECON_GCD);
+                ev = kt->start_one(KC_RECON_GCD);
                 HIPOK(launch_gcd(Yd, nw, std_, rows, Dwd, nwd, Gd, gstd, st));
                 kt->stop(ev);
                 HIPOK(hipMemcpyAsync(Gh + j0, Gd, (size_t)rows * sizeof(uint64_t), hipMemcpyDeviceToHost, st));

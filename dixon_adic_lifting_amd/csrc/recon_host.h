@@ -42,6 +42,9 @@ struct GpuReconPlan {
 // Event timing hooks for the hot kernels (no-ops unless profiling is on).
 struct KernelTimer {
     virtual long start(int cls) = 0;
+    // the same for a bracket that holds exactly one kernel launch, timed by
+    // that kernel's own dispatch
+    virtual long start_one(int cls) { return start(cls); }
     virtual void stop(long idx) = 0;
     virtual ~KernelTimer() = default;
 };
