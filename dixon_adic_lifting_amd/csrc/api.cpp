@@ -265,6 +265,7 @@ int run_lift(const int64_t* dA, const int64_t* db, uint8_t* ws, hipStream_t st, 
     LiftParams prm;
     fill_lift_params(ls, &prm);
     HIP_CHECK(hipMemcpyAsync(ws + L.off_params, &prm, sizeof prm, hipMemcpyHostToDevice, st));
+    HIP_CHECK(launch_lift_positions(L, ws, st));
     HIP_CHECK(launch_split_b(db, L, ws, ls.E, st));
     const bool fused = lift_fused_fits(L);
     if (fused) HIP_CHECK(launch_lift_rows(L, ws, ls.E, st));

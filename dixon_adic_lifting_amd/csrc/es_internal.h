@@ -128,6 +128,7 @@ struct Layout {
     size_t off_rho;       // int8 [53][c][pitch]       r_i mods q_j, permuted
     size_t off_U;         // u8 [53][n*c]              (B_j r_i) mod q_j
     size_t off_xlow;      // uint64 [n][c]             x_i mod 2^64
+    size_t off_rpos;      // int32 [n][64]             (c = 1) row i's position in live prime l's order, l < E
     size_t off_Sperm;     // int8 [53][n][pitch]       (c = 1, pitch >= 1024) B_j rows in component order, live primes
     size_t off_urec;      // u8 [krec][n][64]          (same condition) per step: balanced CRT residues, k at byte 63
     int krec;             // lift steps whose records the device buffer holds
@@ -182,6 +183,8 @@ bool lift_fused_fits(const Layout& L);
 // digits of records [0, nrec) of the record buffer into digit slots
 // slot0 .. slot0 + nrec - 1 of the current chunk
 hipError_t launch_lift_crt_records(const Layout& L, uint8_t* ws, int nrec, int slot0, hipStream_t st);
+// the residual's position table (c = 1), once per lift
+hipError_t launch_lift_positions(const Layout& L, uint8_t* ws, hipStream_t st);
 hipError_t launch_lift_rows(const Layout& L, uint8_t* ws, int E, hipStream_t st);
 hipError_t launch_lift_contract_crt(const Layout& L, uint8_t* ws, int E, int slot, hipStream_t st);
 hipError_t launch_lift_residual(const Layout& L, uint8_t* ws, bool a32, const int64_t* A64, hipStream_t st);

@@ -82,6 +82,7 @@ Layout make_layout(int n, int c) {
     L.off_rho = take(E * c * (size_t)L.pitch);
     L.off_U = take(E * NC);
     L.off_xlow = take(NC * sizeof(uint64_t));
+    L.off_rpos = take(c == 1 ? (size_t)n * 64 * sizeof(int32_t) : 0);
     const bool fused = fused_lift_shape(n, c, L.pitch);
     L.off_Sperm = take(fused ? E * n * (size_t)L.pitch : 0);
     size_t kr = std::min<size_t>(((size_t)16 << 20) / ((size_t)n * 64), (size_t)L.kchunk);

@@ -2035,37 +2035,76 @@ __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v, int lane) {
 
 // The same update for one right-hand side (int32 A): one wave per row, 16-byte
 // loads of A and x_low, the 64-bit sums meet in a wave butterfly, and lanes
-// below E write the balanced residues of r_{i+1}.
+// below E write the balanced residues of r_{i+1}.  Everything the tail needs
+// (the prime constants, the row's position in each prime's order, r_i) is
+// fetched first, and a row's loads of A and x_low go out four passes at a
+// time, so the wave waits on memory about once.
+// rpos[i][l] = rowpos[qidx[l]][i] for the live primes l < E: where row i's
+// residue goes in each prime's order (one wave per row)
+__global__ __launch_bounds__(256) void lift_positions_kernel(const int* __restrict__ rowpos,
+                                                             const LiftParams* __restrict__ prm, int n,
+                                                             int* __restrict__ rpos) {
+    const int lane = threadIdx.x & 63;
+    const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= n || lane >= prm->E) return;
+    rpos[(size_t)r * 64 + lane] = rowpos[(size_t)prm->qidx[lane] * n + r];
+}
+
+template <bool kAligned>  // n % 4 == 0: rows start 16-byte aligned
 __global__ __launch_bounds__(256) void residual1_kernel(const int32_t* __restrict__ A, int n,
                                                         int64_t* __restrict__ R,
                                                         const uint64_t* __restrict__ xlow,
                                                         const LiftParams* __restrict__ prm,
-                                                        const int* __restrict__ rowpos,
+                                                        const int* __restrict__ rpos,
                                                         int8_t* __restrict__ rho, int pitch) {
     const int lane = threadIdx.x & 63;
     const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (r >= n) return;
+    const int E = prm->E;
+    const bool split = lane < E;
+    const int pl = split ? lane : 0;
+    // independent loads only: the tail's operands, then the row
+    const uint32_t q = prm->q[pl], mu16 = prm->mu16[pl], mu32 = prm->mu32[pl], r32 = prm->r32[pl];
+    const int pos = rpos[(size_t)r * 64 + pl];
+    const uint64_t Rr = (uint64_t)R[r];
     const int32_t* a = A + (size_t)r * n;
     uint64_t acc = 0;
-    if ((n & 3) == 0) {  // rows start 16-byte aligned
-        for (int j0 = lane * 4; j0 < n; j0 += 256) {
-            const int4 av = *(const int4*)(a + j0);
-            const ulonglong2 x01 = *(const ulonglong2*)(xlow + j0);
-            const ulonglong2 x23 = *(const ulonglong2*)(xlow + j0 + 2);
-            acc += (uint64_t)(int64_t)av.x * x01.x + (uint64_t)(int64_t)av.y * x01.y +
-                   (uint64_t)(int64_t)av.z * x23.x + (uint64_t)(int64_t)av.w * x23.y;
+    if constexpr (kAligned) {
+        int j0 = lane * 4;
+        int4 av[4];
+        ulonglong2 x01[4], x23[4];
+        // the first four passes (n >= 1024 covers them all at n = 1024)
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            // lanes past the row re-read its start; their terms are dropped below
+            const int jc = j0 + 256 * u < n ? j0 + 256 * u : 0;
+            av[u] = *(const int4*)(a + jc);
+            x01[u] = *(const ulonglong2*)(xlow + jc);
+            x23[u] = *(const ulonglong2*)(xlow + jc + 2);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // every load above is issued before the first use
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const uint64_t t = (uint64_t)(int64_t)av[u].x * x01[u].x + (uint64_t)(int64_t)av[u].y * x01[u].y +
+                               (uint64_t)(int64_t)av[u].z * x23[u].x + (uint64_t)(int64_t)av[u].w * x23[u].y;
+            acc += j0 + 256 * u < n ? t : 0;
+        }
+        for (j0 += 1024; j0 < n; j0 += 256) {
+            const int4 v = *(const int4*)(a + j0);
+            const ulonglong2 y01 = *(const ulonglong2*)(xlow + j0);
+            const ulonglong2 y23 = *(const ulonglong2*)(xlow + j0 + 2);
+            acc += (uint64_t)(int64_t)v.x * y01.x + (uint64_t)(int64_t)v.y * y01.y +
+                   (uint64_t)(int64_t)v.z * y23.x + (uint64_t)(int64_t)v.w * y23.y;
         }
     } else {
         for (int jc = lane; jc < n; jc += 64) acc += (uint64_t)(int64_t)a[jc] * xlow[jc];
     }
     acc = wave_sum_u64(acc, lane);
-    const int E = prm->E;
-    const uint64_t val = ((uint64_t)R[r] - acc) * prm->Pinv;
+    const uint64_t val = (Rr - acc) * prm->Pinv;
     if (lane == 0) R[r] = (int64_t)val;
-    if (lane < E) {
-        const uint32_t q = prm->q[lane];
-        const uint32_t res = mod_i64((int64_t)val, q, prm->mu16[lane], prm->mu32[lane], prm->r32[lane]);
-        rho[(size_t)lane * pitch + rowpos[(size_t)prm->qidx[lane] * n + r]] = (int8_t)balanced(res, q);
+    if (split) {
+        const uint32_t res = mod_i64((int64_t)val, q, mu16, mu32, r32);
+        rho[(size_t)lane * pitch + pos] = (int8_t)balanced(res, q);
     }
 }
 
@@ -2162,6 +2201,13 @@ bool lift_fused_fits(const Layout& L) {
     return !off && fused_lift_shape(L.n, L.c, L.pitch);
 }
 
+hipError_t launch_lift_positions(const Layout& L, uint8_t* ws, hipStream_t st) {
+    if (L.c != 1) return hipSuccess;
+    es_launch(lift_positions_kernel, dim3((L.n + 3) / 4), dim3(256), 0, st, (const int*)(ws + L.off_rowpos),
+              (const LiftParams*)(ws + L.off_params), L.n, (int*)(ws + L.off_rpos));
+    return hipGetLastError();
+}
+
 hipError_t launch_lift_rows(const Layout& L, uint8_t* ws, int E, hipStream_t st) {
     es_launch(lift_rows_kernel, dim3((L.n + 3) / 4, E), dim3(256), 0, st, (const int8_t*)(ws + L.off_S),
                        (const int*)(ws + L.off_rowpos), (const LiftParams*)(ws + L.off_params), L.n, L.pitch,
@@ -2210,9 +2256,13 @@ hipError_t launch_lift_residual(const Layout& L, uint8_t* ws, bool a32, const in
     int8_t* rho = (int8_t*)(ws + L.off_rho);
     if (a32) {
         const int32_t* A = (const int32_t*)(ws + L.off_A32);
-        if (L.c == 1)
-            es_launch(residual1_kernel, dim3((L.n + 3) / 4), dim3(256), 0, st, A, L.n, R, xl, prm, rp, rho,
-                               L.pitch);
+        const int* rpos = (const int*)(ws + L.off_rpos);
+        if (L.c == 1 && L.n % 4 == 0)
+            es_launch(residual1_kernel<true>, dim3((L.n + 3) / 4), dim3(256), 0, st, A, L.n, R, xl, prm, rpos, rho,
+                      L.pitch);
+        else if (L.c == 1)
+            es_launch(residual1_kernel<false>, dim3((L.n + 3) / 4), dim3(256), 0, st, A, L.n, R, xl, prm, rpos,
+                      rho, L.pitch);
         else
             es_launch((residual_kernel<int32_t, 16>), grid, dim3(256), 0, st, A, L.n, L.c, R, xl,
                                prm, rp, rho, L.pitch, 0);
