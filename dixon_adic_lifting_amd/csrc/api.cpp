@@ -266,6 +266,8 @@ int run_lift(const int64_t* dA, const int64_t* db, uint8_t* ws, hipStream_t st, 
     fill_lift_params(ls, &prm);
     HIP_CHECK(hipMemcpyAsync(ws + L.off_params, &prm, sizeof prm, hipMemcpyHostToDevice, st));
     HIP_CHECK(launch_lift_positions(L, ws, st));
+    const bool rmfma = residual_mfma_fits(L, pr.a32, pr.maxabs);
+    if (rmfma) HIP_CHECK(launch_a_planes(L, ws, st));
     HIP_CHECK(launch_split_b(db, L, ws, ls.E, st));
     const bool fused = lift_fused_fits(L);
     if (fused) HIP_CHECK(launch_lift_rows(L, ws, ls.E, st));
@@ -283,11 +285,11 @@ int run_lift(const int64_t* dA, const int64_t* db, uint8_t* ws, hipStream_t st, 
                 HIP_CHECK(launch_lift_contract(L, ws, ls.E, st));
                 prof->stop(ev);
                 ev = prof->start_one(KC_CRT);
-                HIP_CHECK(launch_lift_crt(L, ws, s, st));
+                HIP_CHECK(launch_lift_crt(L, ws, s, rmfma, st));
                 prof->stop(ev);
             }
             ev = prof->start_one(KC_RESIDUAL);
-            HIP_CHECK(launch_lift_residual(L, ws, pr.a32, dA, st));
+            HIP_CHECK(launch_lift_residual(L, ws, pr.a32, dA, rmfma, st));
             prof->stop(ev);
             if (fused && (s % L.krec == L.krec - 1 || s == cnt - 1)) {
                 // the digits of the steps whose records are held

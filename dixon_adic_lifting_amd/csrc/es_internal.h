@@ -129,6 +129,8 @@ struct Layout {
     size_t off_U;         // u8 [53][n*c]              (B_j r_i) mod q_j
     size_t off_xlow;      // uint64 [n][c]             x_i mod 2^64
     size_t off_rpos;      // int32 [n][64]             (c = 1) row i's position in live prime l's order, l < E
+    size_t off_Ab;        // int8 [4][n][pitch]        (c > 1) A as four balanced byte planes, for the MFMA residual
+    size_t off_xp;        // int8 [8 c][pitch]         (c > 1) x_low as eight balanced byte planes, row 8 b c + t
     size_t off_Sperm;     // int8 [53][n][pitch]       (c = 1, pitch >= 1024) B_j rows in component order, live primes
     size_t off_urec;      // u8 [krec][n][64]          (same condition) per step: balanced CRT residues, k at byte 63
     int krec;             // lift steps whose records the device buffer holds
@@ -175,7 +177,7 @@ hipError_t launch_split_b(const int64_t* b, const Layout& L, uint8_t* ws, int E,
 // one lift step = contraction, then the CRT (digit into chunk slot `slot`),
 // then the residual update with the split of the new residual
 hipError_t launch_lift_contract(const Layout& L, uint8_t* ws, int E, hipStream_t st);
-hipError_t launch_lift_crt(const Layout& L, uint8_t* ws, int slot, hipStream_t st);
+hipError_t launch_lift_crt(const Layout& L, uint8_t* ws, int slot, bool planes, hipStream_t st);
 // one right-hand side: the contraction and the CRT in one launch (after
 // launch_lift_rows once per lift, which copies the live primes' B_j rows
 // into component order); false when the layout does not take it
@@ -183,11 +185,16 @@ bool lift_fused_fits(const Layout& L);
 // digits of records [0, nrec) of the record buffer into digit slots
 // slot0 .. slot0 + nrec - 1 of the current chunk
 hipError_t launch_lift_crt_records(const Layout& L, uint8_t* ws, int nrec, int slot0, hipStream_t st);
+// The residual as int8 MFMA products of byte planes (c > 1, |A| < 2^30):
+// A's planes once per lift, then per step the CRT also writes x_low's planes.
+bool residual_mfma_fits(const Layout& L, bool a32, uint64_t maxabs);
+hipError_t launch_a_planes(const Layout& L, uint8_t* ws, hipStream_t st);
 // the residual's position table (c = 1), once per lift
 hipError_t launch_lift_positions(const Layout& L, uint8_t* ws, hipStream_t st);
 hipError_t launch_lift_rows(const Layout& L, uint8_t* ws, int E, hipStream_t st);
 hipError_t launch_lift_contract_crt(const Layout& L, uint8_t* ws, int E, int slot, hipStream_t st);
-hipError_t launch_lift_residual(const Layout& L, uint8_t* ws, bool a32, const int64_t* A64, hipStream_t st);
+hipError_t launch_lift_residual(const Layout& L, uint8_t* ws, bool a32, const int64_t* A64, bool mfma,
+                                hipStream_t st);
 
 // reconstruction on the GPU (recon.hip); see the kernels for layouts
 hipError_t launch_digit_bytes(const uint64_t* digits, int dstride, int m, int j0, int valid_rows, int rows_pad,

@@ -83,6 +83,8 @@ Layout make_layout(int n, int c) {
     L.off_U = take(E * NC);
     L.off_xlow = take(NC * sizeof(uint64_t));
     L.off_rpos = take(c == 1 ? (size_t)n * 64 * sizeof(int32_t) : 0);
+    L.off_Ab = take(c > 1 ? 4 * (size_t)n * L.pitch : 0);
+    L.off_xp = take(c > 1 ? 8 * (size_t)c * L.pitch : 0);
     const bool fused = fused_lift_shape(n, c, L.pitch);
     L.off_Sperm = take(fused ? E * n * (size_t)L.pitch : 0);
     size_t kr = std::min<size_t>(((size_t)16 << 20) / ((size_t)n * 64), (size_t)L.kchunk);

@@ -1664,7 +1664,7 @@ constexpr int kCrtPrimesPerLane = (kNumPrimes + kCrtLanes - 1) / kCrtLanes;
 // The digit of one component from its residues: lane s of the component's
 // sixteen holds res[i] = r_l for l = s + 16 i (l < E).  Writes the digit
 // (twelve words) into slot `slot` of the component's chunk and x mod 2^64.
-__device__ __forceinline__ void crt_digit(const CrtTables& T, const LiftParams* __restrict__ prm, int E, int s,
+__device__ __forceinline__ uint64_t crt_digit(const CrtTables& T, const LiftParams* __restrict__ prm, int E, int s,
                                           const uint32_t (&res)[kCrtPrimesPerLane], int comp,
                                           uint64_t* __restrict__ digits, int kchunk, int slot,
                                           uint64_t* __restrict__ xlow) {
@@ -1686,19 +1686,26 @@ __device__ __forceinline__ void crt_digit(const CrtTables& T, const LiftParams* 
     f = quad_add<8>(quad_add<4>(quad_add<2>(quad_add<1>(f))));
 #pragma unroll
     for (int w = 0; w < kDigitWords; w++) acc[w] = quad_add<8>(quad_add<4>(quad_add<2>(quad_add<1>(acc[w]))));
-    if (s != 0) return;
+    if (s != 0) return 0;
     uint32_t x[kDigitWords];
     (void)crt_finish(acc, f, prm, x);
     uint4* dst = (uint4*)(digits + ((size_t)comp * kchunk + slot) * kDigitLimbs);
     dst[0] = make_uint4(x[0], x[1], x[2], x[3]);
     dst[1] = make_uint4(x[4], x[5], x[6], x[7]);
     dst[2] = make_uint4(x[8], x[9], x[10], x[11]);
-    xlow[comp] = ((uint64_t)x[1] << 32) | x[0];
+    const uint64_t xl = ((uint64_t)x[1] << 32) | x[0];
+    xlow[comp] = xl;
+    return xl;
 }
 
+// With xp set (c right-hand sides, rows of `pitch` bytes), x mod 2^64 of
+// component k c + t also goes out as eight balanced bytes, byte b to
+// xp[(b c + t) pitch + k] (x = sum_b byte_b 256^b mod 2^64), the operand of
+// the MFMA residual.
 __global__ __launch_bounds__(256) void crt_kernel(const LiftParams* __restrict__ prm, const uint8_t* __restrict__ U,
                                                   int NC, uint64_t* __restrict__ digits, int kchunk, int slot,
-                                                  uint64_t* __restrict__ xlow) {
+                                                  uint64_t* __restrict__ xlow, int8_t* __restrict__ xp, int c,
+                                                  int pitch) {
     __shared__ CrtTables T;
     const int E = prm->E;
     load_crt_tables(T, prm, threadIdx.x, 256);
@@ -1712,7 +1719,15 @@ __global__ __launch_bounds__(256) void crt_kernel(const LiftParams* __restrict__
         const int l = s + kCrtLanes * i;
         res[i] = l < E ? U[(size_t)l * NC + comp] : 0u;
     }
-    crt_digit(T, prm, E, s, res, comp, digits, kchunk, slot, xlow);
+    uint64_t v = crt_digit(T, prm, E, s, res, comp, digits, kchunk, slot, xlow);
+    if (xp == nullptr || s != 0) return;
+    const int k = comp / c, t = comp % c;
+#pragma unroll
+    for (int b = 0; b < 8; b++) {
+        const int8_t d = (int8_t)(v & 0xffu);  // balanced: the low byte read as signed
+        xp[(size_t)(b * c + t) * pitch + k] = d;
+        v = (v - (uint64_t)(int64_t)d) >> 8;
+    }
 }
 
 // ---------------------------------------------------------------- lift: contraction + CRT, one right-hand side
@@ -2108,6 +2123,170 @@ __global__ __launch_bounds__(256) void residual1_kernel(const int32_t* __restric
     }
 }
 
+// ---------------------------------------------------------------- lift: residual on MFMA
+// For c right-hand sides the product A x_low (mod 2^64) is a sum of int8
+// matrix products: A = sum_a A_a 256^a with balanced byte planes A_a (four
+// planes cover |A| < 2^30), x_low = sum_b X_b 256^b (mod 2^64) with eight
+// balanced byte planes, and modulo 2^64 only the 26 pairs a + b < 8 matter:
+//   A x_low = sum_{a + b < 8} 256^(a + b) (A_a X_b)  (mod 2^64),
+// each A_a X_b exact in int32 (|entry| <= n 128^2 < 2^31 for n < 2^17).
+
+// A_a[i][k] for k < pitch (zero past n), four columns a thread
+__global__ __launch_bounds__(256) void a_planes_kernel(const int32_t* __restrict__ A, int n, int pitch,
+                                                       int8_t* __restrict__ Ab) {
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const int q4 = pitch / 4;
+    if (idx >= (size_t)n * q4) return;
+    const int i = (int)(idx / q4), k0 = (int)(idx % q4) * 4;
+    uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        int32_t v = k0 + e < n ? A[(size_t)i * n + k0 + e] : 0;
+#pragma unroll
+        for (int a = 0; a < 4; a++) {
+            const int8_t d = (int8_t)(v & 0xff);
+            w[a] |= (uint32_t)(uint8_t)d << (8 * e);
+            v = (v - d) >> 8;
+        }
+    }
+    const size_t plane = (size_t)n * pitch;
+#pragma unroll
+    for (int a = 0; a < 4; a++) *(uint32_t*)(Ab + a * plane + (size_t)i * pitch + k0) = w[a];
+}
+
+constexpr int kResWaves = 8;  // waves of a block, splitting the contraction
+
+// Block: rows i0 .. i0 + 15 and columns t0 .. t0 + 15; wave w takes the
+// 64-byte chunks w, w + 8, ... of the contraction.  Then r <- (r - A x_low)
+// P^-1 and the next step's balanced residues, as in the other residual kernels.
+__global__ __launch_bounds__(kResWaves * 64) void residual_mfma_kernel(
+    const int8_t* __restrict__ Ab, const int8_t* __restrict__ xp, int n, int c, int pitch,
+    int64_t* __restrict__ R, const LiftParams* __restrict__ prm, const int* __restrict__ rowpos,
+    int8_t* __restrict__ rho) {
+    typedef int v4i_r __attribute__((ext_vector_type(4)));
+    __shared__ uint64_t part[kResWaves][4][64];
+    __shared__ uint64_t sval[16][16];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int i0 = blockIdx.x * 16, t0 = blockIdx.y * 16;
+    // planes through buffer resources: one 32-bit lane offset per operand,
+    // each plane at a scalar offset (both arrays below 2^31 bytes)
+    const uint32_t plane = (uint32_t)n * pitch, bstride = (uint32_t)c * pitch;
+    const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc((void*)Ab, 0, (int)(4 * plane), kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc((void*)xp, 0, (int)(8 * bstride), kBufferWord3);
+    const uint32_t arow = (uint32_t)min(i0 + lr, n - 1) * pitch;  // rows past n: dropped below
+    const int tb = t0 + lr;
+    const bool okB = tb < c;
+    const uint32_t xcol = (uint32_t)(okB ? tb : 0) * pitch;
+    v4i_r acc[26];
+#pragma unroll
+    for (int p = 0; p < 26; p++) acc[p] = v4i_r{0, 0, 0, 0};
+    const int nch = pitch / 64;
+    // A (from HBM) in two buffers taken in turn: the next chunk's A loads are
+    // in flight while the current chunk's x planes (from L2) arrive and its
+    // 26 products run; past the end a buffer re-reads its own chunk, unused
+    v4i_r a0[4], a1[4], bv[8];
+    auto loadA = [&](int ch, v4i_r (&A4)[4]) {
+        const uint32_t k = ch * 64 + 16 * lg;
+#pragma unroll
+        for (int a = 0; a < 4; a++) A4[a] = (v4i_r)__builtin_amdgcn_raw_buffer_load_b128(rsA, arow + k, a * plane, 0);
+    };
+    auto loadB = [&](int ch) {
+        const uint32_t k = ch * 64 + 16 * lg;
+#pragma unroll
+        for (int b = 0; b < 8; b++) bv[b] = (v4i_r)__builtin_amdgcn_raw_buffer_load_b128(rsB, xcol + k, b * bstride, 0);
+    };
+    auto products = [&](v4i_r (&A4)[4]) {
+        if (!okB) {
+#pragma unroll
+            for (int b = 0; b < 8; b++) bv[b] = v4i_r{0, 0, 0, 0};
+        }
+        int p = 0;
+#pragma unroll
+        for (int a = 0; a < 4; a++)
+#pragma unroll
+            for (int b = 0; b + a < 8; b++, p++) acc[p] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A4[a], bv[b], acc[p], 0, 0, 0);
+    };
+    if (wave < nch) loadA(wave, a0);
+    for (int ch = wave; ch < nch; ch += 2 * kResWaves) {
+        const int c1 = ch + kResWaves, c2 = ch + 2 * kResWaves;
+        loadB(ch);
+        loadA(c1 < nch ? c1 : ch, a1);
+        __builtin_amdgcn_sched_barrier(0);
+        products(a0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (c1 >= nch) break;
+        loadB(c1);
+        loadA(c2 < nch ? c2 : c1, a0);
+        __builtin_amdgcn_sched_barrier(0);
+        products(a1);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // lane: column t0 + lr, rows i0 + 4 lg + 0..3; fold the pairs into 64 bits
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+        uint64_t v = 0;
+        int p = 0;
+#pragma unroll
+        for (int a = 0; a < 4; a++)
+#pragma unroll
+            for (int b = 0; b + a < 8; b++, p++) v += (uint64_t)(int64_t)acc[p][r] << (8 * (a + b));
+        part[wave][r][lane] = v;
+    }
+    __syncthreads();
+    const uint64_t Pinv = prm->Pinv;
+    if (tid < 256) {
+        const int rho_ = tid >> 4, tt = tid & 15;  // element (row i0 + rho_, column t0 + tt)
+        const int ln = 16 * (rho_ >> 2) + tt, r = rho_ & 3;
+        uint64_t sum = 0;
+#pragma unroll
+        for (int w = 0; w < kResWaves; w++) sum += part[w][r][ln];
+        const int i = i0 + rho_, t = t0 + tt;
+        uint64_t val = 0;
+        if (i < n && t < c) {
+            int64_t* rp = R + (size_t)i * c + t;
+            val = ((uint64_t)*rp - sum) * Pinv;
+            *rp = (int64_t)val;
+        }
+        sval[rho_][tt] = val;
+    }
+    __syncthreads();
+    // next residues: lane l is live prime l, the eight waves take two rows each
+    const int E = prm->E;
+    if (lane >= E) return;
+    const uint32_t q = prm->q[lane], mu16 = prm->mu16[lane], mu32 = prm->mu32[lane], r32 = prm->r32[lane];
+    const int J = prm->qidx[lane];
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        const int rr = 2 * wave + h, i = i0 + rr;
+        if (i >= n) continue;
+        const int pos = rowpos[(size_t)J * n + i];
+#pragma unroll
+        for (int tt = 0; tt < 16; tt++) {
+            const int t = t0 + tt;
+            if (t >= c) break;
+            const uint32_t res = mod_i64((int64_t)sval[rr][tt], q, mu16, mu32, r32);
+            rho[((size_t)lane * c + t) * pitch + pos] = (int8_t)balanced(res, q);
+        }
+    }
+}
+
+bool residual_mfma_fits(const Layout& L, bool a32, uint64_t maxabs) {
+    static const bool off = [] {
+        const char* e = std::getenv("ES_RESIDUAL_VALU");
+        return e && e[0] == '1';
+    }();
+    return !off && L.c > 1 && a32 && maxabs < ((uint64_t)1 << 30) && L.pitch % 64 == 0 &&
+           4 * (size_t)L.n * L.pitch <= (size_t)0x7fffffff && 8 * (size_t)L.c * L.pitch <= (size_t)0x7fffffff;
+}
+
+hipError_t launch_a_planes(const Layout& L, uint8_t* ws, hipStream_t st) {
+    const size_t threads = (size_t)L.n * (L.pitch / 4);
+    es_launch(a_planes_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
+              (const int32_t*)(ws + L.off_A32), L.n, L.pitch, (int8_t*)(ws + L.off_Ab));
+    return hipGetLastError();
+}
+
 hipError_t launch_split_b(const int64_t* b, const Layout& L, uint8_t* ws, int E, hipStream_t st) {
     (void)E;
     hipError_t e = hipMemcpyAsync(ws + L.off_R, b, (size_t)L.n * L.c * sizeof(int64_t),
@@ -2238,16 +2417,27 @@ hipError_t launch_lift_crt_records(const Layout& L, uint8_t* ws, int nrec, int s
     return hipGetLastError();
 }
 
-hipError_t launch_lift_crt(const Layout& L, uint8_t* ws, int slot, hipStream_t st) {
+hipError_t launch_lift_crt(const Layout& L, uint8_t* ws, int slot, bool planes, hipStream_t st) {
+    if (planes && L.c < 2) return hipErrorInvalidValue;
     const int NC = L.n * L.c;
     es_launch(crt_kernel, dim3((NC + 15) / 16), dim3(256), 0, st,
                        (const LiftParams*)(ws + L.off_params), (const uint8_t*)(ws + L.off_U), NC,
                        L.dig_dev ? L.dig_dev : (uint64_t*)(ws + L.off_digits), L.kchunk, slot,
-                       (uint64_t*)(ws + L.off_xlow));
+                       (uint64_t*)(ws + L.off_xlow), planes ? (int8_t*)(ws + L.off_xp) : (int8_t*)nullptr, L.c,
+                       L.pitch);
     return hipGetLastError();
 }
 
-hipError_t launch_lift_residual(const Layout& L, uint8_t* ws, bool a32, const int64_t* A64, hipStream_t st) {
+hipError_t launch_lift_residual(const Layout& L, uint8_t* ws, bool a32, const int64_t* A64, bool mfma,
+                                hipStream_t st) {
+    if (mfma) {
+        if (!a32 || L.c < 2 || L.pitch % 64 != 0) return hipErrorInvalidValue;
+        es_launch(residual_mfma_kernel, dim3((L.n + 15) / 16, (L.c + 15) / 16), dim3(kResWaves * 64), 0, st,
+                  (const int8_t*)(ws + L.off_Ab), (const int8_t*)(ws + L.off_xp), L.n, L.c, L.pitch,
+                  (int64_t*)(ws + L.off_R), (const LiftParams*)(ws + L.off_params),
+                  (const int*)(ws + L.off_rowpos), (int8_t*)(ws + L.off_rho));
+        return hipGetLastError();
+    }
     const dim3 grid((L.n + 3) / 4);
     const LiftParams* prm = (const LiftParams*)(ws + L.off_params);
     int64_t* R = (int64_t*)(ws + L.off_R);
