@@ -14,6 +14,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <new>
+#include <future>
 #include <vector>
 
 #include "../../include/es_solve.h"
@@ -400,14 +401,22 @@ int es_solve_device(const int64_t* dA, const int64_t* db, int32_t n, int32_t c, 
         if (rc != ES_OK) return rc;
         LiveSet ls = make_live_set(flags);
         if (ls.E == 0) return no_prime_decision(dA, n, pr, st);
-        BigInt M;
-        const int m = choose_m(ls.P, pr.nbits, pr.dbits, &M);
+        size_t mbits = 0;
+        const int m = choose_m_bits(ls.P, pr.nbits, pr.dbits, &mbits);
+        // M = P^m is needed only by the reconstruction: formed on a host
+        // thread while the GPU lifts
+        std::future<BigInt> fM = std::async(std::launch::async, [&ls, m] { return pow_u(ls.P, (unsigned)m); });
+        auto take_M = [&](BigInt* M) {
+            *M = fM.get();
+            return M->bit_length() == mbits;
+        };
         GpuReconPlan plan;
         uint8_t* scr = nullptr;
         if (!gpu_recon_disabled()) {
-            plan = plan_gpu_recon(n, c, m, M, pr.nbits);
+            plan = plan_gpu_recon(n, c, m, mbits, pr.nbits);
             if (plan.ok) scr = gpu_recon_scratch(plan);
         }
+        BigInt M;
         es_solution* sol = nullptr;
         if (scr) {
             // lift into device digits, then the GEMM-based reconstruction
@@ -416,6 +425,7 @@ int es_solve_device(const int64_t* dA, const int64_t* db, int32_t n, int32_t c, 
             g_timings[2] = ms_since(t0);
             if (rc != ES_OK) return rc;
             t0 = clk::now();
+            if (!take_M(&M)) return ES_EINTERNAL;
             sol = new es_solution;
             GpuReconTimes rt;
             rc = reconstruct_gpu(plan, scr, ls.P, M, pr.nbits, pr.dbits, default_threads(), st, &sol->data, &rt,
@@ -432,6 +442,7 @@ int es_solve_device(const int64_t* dA, const int64_t* db, int32_t n, int32_t c, 
             if (rc != ES_OK) return rc;
             prof.collect();
             t0 = clk::now();
+            if (!take_M(&M)) return ES_EINTERNAL;
             sol = new es_solution;
             rc = reconstruct(digits, (size_t)m, n, c, m, ls.P, M, pr.nbits, pr.dbits, default_threads(),
                              &sol->data);

@@ -2,6 +2,7 @@
 #include "../../include/es_debug.h"
 
 #include "bignum.h"
+#include "host.h"
 
 using es::BigInt;
 
@@ -64,6 +65,25 @@ extern "C" int es_dbg_ratrec(const uint64_t* a, int32_t la, const uint64_t* M, i
         if (ok != ok2 || (ok && (es::cmp(nu, nu2) != 0 || es::cmp(de, de2) != 0))) return -2;
         if (!ok) return 1;
         if (!put(nu, num, lnum, nneg, cap) || !put(de, den, lden, nullptr, cap)) return -1;
+        return 0;
+    } catch (...) {
+        return -6;
+    }
+}
+
+extern "C" int es_dbg_step_count(uint64_t mask, int32_t nbits, int32_t dbits, int32_t* m_exact, int64_t* bits_exact,
+                                 int32_t* m_fast, int64_t* bits_fast) {
+    if ((mask & ((1ULL << es::kNumPrimes) - 1)) == 0 || nbits < 1 || dbits < 1 || !m_exact || !bits_exact ||
+        !m_fast || !bits_fast)
+        return -1;
+    try {
+        const es::LiveSet ls = es::live_set_from_mask(mask);
+        BigInt M;
+        *m_exact = es::choose_m(ls.P, nbits, dbits, &M);
+        *bits_exact = (int64_t)M.bit_length();
+        size_t b = 0;
+        *m_fast = es::choose_m_bits(ls.P, nbits, dbits, &b);
+        *bits_fast = (int64_t)b;
         return 0;
     } catch (...) {
         return -6;

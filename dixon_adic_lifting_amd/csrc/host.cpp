@@ -214,6 +214,45 @@ int choose_m(const BigInt& P, int nbits, int dbits, BigInt* M) {
     return m;
 }
 
+int choose_m_bits(const BigInt& P, int nbits, int dbits, size_t* mbits) {
+    // The same m without forming P^m: P^k has bit length floor(k log2 P) + 1.
+    // log2 P from P's top 64 bits is within about 1e-13 (the rounding of the
+    // top word to a double and of log2 itself), so k log2 P is within 2e-9
+    // for k up to 2^14; where it lies within 1e-6 of an integer the exact
+    // power decides.
+    const size_t need = (size_t)nbits + dbits + 2;
+    const size_t bl = P.bit_length();
+    const BigInt top = shr_abs(P, bl > 64 ? bl - 64 : 0);
+    const double l2p = std::log2((double)top.d[0]) + (double)(bl > 64 ? bl - 64 : 0);
+    auto bits = [&](int k, size_t* out) {
+        const double x = (double)k * l2p, f = std::floor(x);
+        if (x - f < 1e-6 || f + 1.0 - x < 1e-6 || k > (1 << 14)) return false;
+        *out = (size_t)f + 1;
+        return true;
+    };
+    auto exact = [&]() {
+        BigInt M;
+        const int m = choose_m(P, nbits, dbits, &M);
+        *mbits = M.bit_length();
+        return m;
+    };
+    int m = std::max(1, (int)std::floor((double)(need - 1) / l2p));
+    size_t b = 0;
+    for (;;) {
+        if (!bits(m, &b)) return exact();
+        if (b >= need) break;
+        m++;
+    }
+    while (m > 1) {
+        size_t b1;
+        if (!bits(m - 1, &b1)) return exact();
+        if (b1 < need) break;
+        m--, b = b1;
+    }
+    *mbits = b;
+    return m;
+}
+
 // ---------------------------------------------------------------- singular decision
 
 static uint64_t mulmod62(uint64_t a, uint64_t b, uint64_t p) { return (uint64_t)((u128)a * b % p); }

@@ -37,6 +37,8 @@ void hadamard_bits(const double* rownorm, const double* colnorm, const double* b
 
 // Least m with P^m > 2^(nbits + dbits + 1); also returns M = P^m.
 int choose_m(const BigInt& P, int nbits, int dbits, BigInt* M);
+// the same m, and the bit length of M = P^m, without forming M
+int choose_m_bits(const BigInt& P, int nbits, int dbits, size_t* mbits);
 
 // Exact rank test of A modulo a 62-bit prime (host Gaussian elimination).
 bool full_rank_mod(const int64_t* A, int n, uint64_t p);

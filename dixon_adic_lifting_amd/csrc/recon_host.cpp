@@ -136,13 +136,12 @@ bool gpu_recon_disabled() {
     return g_gpu_recon < 0 ? env_off : g_gpu_recon == 0;
 }
 
-GpuReconPlan plan_gpu_recon(int n, int c, int m, const BigInt& M, int nbits) {
+GpuReconPlan plan_gpu_recon(int n, int c, int m, size_t mbits, int nbits) {
     GpuReconPlan pl;
     pl.n = n;
     pl.c = c;
     pl.m = m;
     pl.NC = (size_t)n * c;
-    const size_t mbits = M.bit_length();
     pl.TM = (int)((mbits - 1) / 32);
     pl.NW = pl.TM + 1;
     pl.nw = nbits / 32 + 1;

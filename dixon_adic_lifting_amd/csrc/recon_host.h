@@ -61,7 +61,7 @@ struct GpuReconTimes {
 bool gpu_recon_disabled();
 void set_gpu_recon(bool on);
 
-GpuReconPlan plan_gpu_recon(int n, int c, int m, const BigInt& M, int nbits);
+GpuReconPlan plan_gpu_recon(int n, int c, int m, size_t mbits, int nbits);  // mbits: bit length of M = P^m
 
 // Per-thread device scratch of at least pl.total bytes (NULL on failure).
 uint8_t* gpu_recon_scratch(const GpuReconPlan& pl);

@@ -34,6 +34,14 @@ int es_dbg_ratrec(const uint64_t *a, int32_t la, const uint64_t *M, int32_t lM, 
                   int32_t lN, const uint64_t *D, int32_t lD, uint64_t *num, int32_t *lnum, int *nneg,
                   uint64_t *den, int32_t *lden, int32_t cap);
 
+/* The lift's step count for live-prime set `mask` (bit j: the j-th odd
+ * prime below 256) and bounds of nbits / dbits bits: m_exact and bits_exact
+ * from P^m formed exactly, m_fast and bits_fast (the bit length of P^m) as
+ * the solve takes them, from log2 P without forming P^m.  Returns 0, or -1
+ * for an empty mask or bounds below 1. */
+int es_dbg_step_count(uint64_t mask, int32_t nbits, int32_t dbits, int32_t *m_exact, int64_t *bits_exact,
+                      int32_t *m_fast, int64_t *bits_fast);
+
 #ifdef __cplusplus
 }
 #endif

@@ -287,3 +287,41 @@ def test_reconstruct_rejects_short_precision(primes):
     words, mask, nbits, dbits = oracle_case(A, b, primes)
     with pytest.raises(ValueError):
         es.reconstruct(words[:, :1], 6, 1, mask, nbits + 400, dbits + 400)
+
+
+def test_step_count_without_forming_the_modulus():
+    """The solve takes the lift's step count m (the least m with
+    P^m > 2^(nbits + dbits + 1), card "Method") and the bit length of P^m from
+    log2 P, forming P^m only while the GPU lifts.  It must agree with the
+    exact powers, here also recomputed with Python integers, over random
+    prime sets and bounds, including bounds that put k log2 P near an integer."""
+    import random
+    L = lib()
+    f = L.es_dbg_step_count
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
+                  ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)]
+    primes = modular.odd_primes_below(256)
+    rng = random.Random(5)
+    me, be, mf, bf = ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int64()
+    cases = []
+    for _ in range(150):
+        mask = rng.getrandbits(53) | 1
+        cases.append((mask, rng.randrange(1, 40000), rng.randrange(1, 40000)))
+    full = (1 << 53) - 1
+    P = math.prod(primes)
+    for k in (1, 2, 7, 50, 171, 172, 180):  # bounds that make P^k's bit length the exact threshold
+        b = (P ** k).bit_length()
+        cases += [(full, b - 2 - 1, 1), (full, b - 2, 1), (full, b - 2 + 1, 1)]
+    for mask, nb, db in cases:
+        if nb < 1:
+            continue
+        assert f(mask, nb, db, ctypes.byref(me), ctypes.byref(be), ctypes.byref(mf), ctypes.byref(bf)) == 0
+        Pm = math.prod(q for j, q in enumerate(primes) if (mask >> j) & 1)
+        need = nb + db + 2
+        m = 1
+        while (Pm ** m).bit_length() < need:
+            m += 1
+        assert (me.value, be.value) == (m, (Pm ** m).bit_length()), (mask, nb, db)
+        assert (mf.value, bf.value) == (me.value, be.value), (mask, nb, db)
+    assert f(0, 10, 10, ctypes.byref(me), ctypes.byref(be), ctypes.byref(mf), ctypes.byref(bf)) == -1
