@@ -1118,11 +1118,47 @@ __global__ __launch_bounds__(1024) void gj_panel_kernel(int8_t* __restrict__ S, 
                     GT + (size_t)j * pitch * kPanel, threadIdx.x);
 }
 
+// Start of panel K's block (lookahead form, K >= 32): the pivot rows of
+// panel K - 32 in panel K's columns, which the gather-next launch left:
+// S[p][K + col] = sum_c S[p][K - 32 + c] S[piv[K - 32 + c]][K + col] (mod q),
+// the same sum the other rows got there.  The old 32 x 32 blocks are read
+// into LDS before any is written.
+__device__ __forceinline__ void finish_pivot_rows(int8_t* __restrict__ S, int n, int pitch, int K,
+                                                  const int* __restrict__ piv, int j) {
+    const int t = threadIdx.x;
+    int8_t* Sj = S + (size_t)j * n * pitch;
+    const int* pl = piv + (size_t)j * (n + 1) + K - kPanel;
+    __shared__ __attribute__((aligned(16))) int8_t oldb[kPanel][kPanel];  // oldb[c][col] = S[pl[c]][K + col]
+    __shared__ __attribute__((aligned(16))) int8_t mul[kPanel][kPanel];   // mul[r][c] = S[pl[r]][K - 32 + c]
+    if (t < 2 * kPanel) {
+        const int c = t >> 1, h = t & 1;
+        *(uint4*)&oldb[c][16 * h] = *(const uint4*)(Sj + (size_t)pl[c] * pitch + K + 16 * h);
+    } else if (t < 4 * kPanel) {
+        const int r = (t - 2 * kPanel) >> 1, h = t & 1;
+        *(uint4*)&mul[r][16 * h] = *(const uint4*)(Sj + (size_t)pl[r] * pitch + K - kPanel + 16 * h);
+    }
+    __syncthreads();
+    if (t < kPanel * kPanel) {
+        const int r = t >> 5, col = t & 31;
+        int acc = 0;
+#pragma unroll
+        for (int c = 0; c < kPanel; c++) acc += (int)mul[r][c] * (int)oldb[c][col];
+        const uint32_t q = c_pt.q[j];
+        const uint32_t m28 = (uint32_t)((268435456ull + q - 1) / q);
+        const int off = (int)(q * ((524288u + q - 1) / q));
+        const uint32_t xp = (uint32_t)(acc + off);
+        const uint32_t tq = __umulhi(xp << 4, m28);
+        const int rr = (int)(xp - tq * q);
+        Sj[(size_t)pl[r] * pitch + K + col] = (int8_t)(rr > (int)(q >> 1) ? rr - (int)q : rr);
+    }
+    __syncthreads();
+}
+
 // Lookahead form: panel K (blocks 0 .. 52, one per prime) and, in the same
 // launch, the update of panel K - 32 on every column outside
 // [K - 32, K + 32) (the blocks after them, four 128 x 128 tiles each).  The
 // two touch disjoint columns; panel K's columns were updated beforehand by
-// gj_next_kernel.  The panel blocks come first, so they are placed
+// gj_gather_next_kernel.  The panel blocks come first, so they are placed
 // first.  K >= n: the update part only.
 template <int RPT, bool UP>
 __global__ __launch_bounds__(1024) void gj_panel_rest_kernel(int8_t* __restrict__ S, int n, int pitch, int K,
@@ -1131,6 +1167,7 @@ __global__ __launch_bounds__(1024) void gj_panel_rest_kernel(int8_t* __restrict_
                                                              int ntx, int nty) {
     const int np = K < n ? kNumPrimes : 0;
     if ((int)blockIdx.x < np) {
+        if (K >= kPanel && !flags[blockIdx.x]) finish_pivot_rows(S, n, pitch, K, piv, blockIdx.x);
         if (UP) (void)panel_up_body<RPT>(S, n, pitch, K, piv, rowpos, flags, blockIdx.x);
         else (void)panel_packed_body<RPT>(S, n, pitch, K, piv, rowpos, flags, blockIdx.x);
         return;
@@ -1148,13 +1185,11 @@ __global__ __launch_bounds__(1024) void gj_panel_rest_kernel(int8_t* __restrict_
 // After panel K: its pivot rows to GT, 256 columns per block (grid
 // (column chunks, primes)), words read along the rows and regrouped by
 // column in LDS, one 32-byte row of GT per column.
-__global__ __launch_bounds__(256) void gj_gather_kernel(const int8_t* __restrict__ S, int n, int pitch, int K,
-                                                        const int* __restrict__ piv, const int* __restrict__ flags,
-                                                        int8_t* __restrict__ GT) {
-    const int j = blockIdx.y;
-    if (flags[j]) return;
+__device__ __forceinline__ void gather_gt_block(const int8_t* __restrict__ S, int n, int pitch, int K,
+                                                const int* __restrict__ piv, int8_t* __restrict__ GT, int j,
+                                                int bx) {
     const int t = threadIdx.x;
-    const int c0 = blockIdx.x * 256;
+    const int c0 = bx * 256;
     const int ncol = min(256, pitch - c0);
     const int bw = min(kPanel, n - K);
     const int8_t* Sj = S + (size_t)j * n * pitch;
@@ -1179,27 +1214,39 @@ __global__ __launch_bounds__(256) void gj_gather_kernel(const int8_t* __restrict
 }
 
 // Then, when K + 32 < n, the update of the next panel's columns
-// [K + 32, K + 64) on every row: 64 rows per block (grid (row chunks,
-// primes)), one 16-row tile per wave, two 16-column halves.
-__global__ __launch_bounds__(256) void gj_next_kernel(int8_t* __restrict__ S, int n, int pitch, int K,
-                                                      const int* __restrict__ rowpos, const int* __restrict__ flags,
-                                                      const int8_t* __restrict__ GT) {
-    const int j = blockIdx.y;
-    if (flags[j]) return;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// [K + 32, K + 64) on every row: 64 rows per block, one 16-row tile per
+// wave, two 16-column halves.  The panel's pivot rows in those columns (a
+// 32 x 32 byte block) come straight from S through LDS, so this part does
+// not wait for GT and shares a launch with the gather.
+__device__ __forceinline__ void next_cols_block(int8_t* __restrict__ S, int n, int pitch, int K,
+                                                const int* __restrict__ piv, const int* __restrict__ rowpos,
+                                                int j, int bx) {
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int lr = lane & 15, lg = lane >> 4;
     int8_t* Sj = S + (size_t)j * n * pitch;
-    const int8_t* GTj = GT + (size_t)j * pitch * kPanel;
     const uint32_t q = c_pt.q[j];
     const uint32_t m28 = (uint32_t)((268435456ull + q - 1) / q);
     const int off = (int)(q * ((524288u + q - 1) / q));
     const int* rpj = rowpos + (size_t)j * n;
     const int c0 = K + kPanel;
+    __shared__ __attribute__((aligned(16))) int8_t prs[kPanel][kPanel];  // prs[c][col] = S[piv[K + c]][c0 + col]
+    if (t < 2 * kPanel) {
+        const int c = t >> 1, h = t & 1;
+        const int pr = piv[(size_t)j * (n + 1) + K + c];
+        *(uint4*)&prs[c][16 * h] = *(const uint4*)(Sj + (size_t)pr * pitch + c0 + 16 * h);
+    }
+    __syncthreads();
     v4i_t ga[2];
 #pragma unroll
-    for (int a = 0; a < 2; a++)
-        ga[a] = lg < 2 ? *(const v4i_t*)(GTj + (size_t)(c0 + 16 * a + lr) * kPanel + 16 * lg) : v4i_t{0, 0, 0, 0};
-    const int i = blockIdx.x * 64 + 16 * wave + lr;
+    for (int a = 0; a < 2; a++) {
+        uint32_t w[4] = {0, 0, 0, 0};
+        if (lg < 2) {
+#pragma unroll
+            for (int e = 0; e < 16; e++) w[e >> 2] |= (uint32_t)(uint8_t)prs[16 * lg + e][16 * a + lr] << (8 * (e & 3));
+        }
+        ga[a] = v4i_t{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+    }
+    const int i = bx * 64 + 16 * wave + lr;
     const bool rowok = i < n;
     const v4i_t pb = (lg < 2 && rowok) ? *(const v4i_t*)(Sj + (size_t)i * pitch + K + 16 * lg) : v4i_t{0, 0, 0, 0};
     const int rp = rowok ? rpj[i] : 0;
@@ -1220,8 +1267,24 @@ __global__ __launch_bounds__(256) void gj_next_kernel(int8_t* __restrict__ S, in
             const int v = r > (int)(q >> 1) ? r - (int)q : r;
             outw |= ((uint32_t)v & 0xffu) << (8 * e);
         }
-        if (rowok) *(uint32_t*)(Sj + (size_t)i * pitch + col) = outw;
+        // the panel's own pivot rows are read by every block of this launch
+        // (prs): the next panel's block updates them (finish_pivot_rows)
+        if (rowok && !pivot_row) *(uint32_t*)(Sj + (size_t)i * pitch + col) = outw;
     }
+}
+
+// After panel K: blocks [0, G) gather its pivot rows into GT (for the next
+// update), blocks [G, G + N) update the next panel's columns (N = 0 on the
+// last panel); grid (G + N, primes).
+__global__ __launch_bounds__(256) void gj_gather_next_kernel(int8_t* __restrict__ S, int n, int pitch, int K,
+                                                             const int* __restrict__ piv,
+                                                             const int* __restrict__ rowpos,
+                                                             const int* __restrict__ flags, int8_t* __restrict__ GT,
+                                                             int G) {
+    const int j = blockIdx.y;
+    if (flags[j]) return;
+    if ((int)blockIdx.x < G) gather_gt_block(S, n, pitch, K, piv, GT, j, blockIdx.x);
+    else next_cols_block(S, n, pitch, K, piv, rowpos, j, blockIdx.x - G);
 }
 
 bool blocked_inverse_fits(const Layout& L) { return L.n <= 4096 && (L.pitch % 64) == 0; }
@@ -1277,13 +1340,10 @@ hipError_t launch_gj_panel_rest(const Layout& L, uint8_t* ws, int K, hipStream_t
 }
 
 hipError_t launch_gj_gather_next(const Layout& L, uint8_t* ws, int K, hipStream_t st) {
-    es_launch(gj_gather_kernel, dim3((L.pitch + 255) / 256, kNumPrimes), dim3(256), 0, st,
-                       (const int8_t*)(ws + L.off_S), L.n, L.pitch, K, (const int*)(ws + L.off_piv),
-                       (const int*)(ws + L.off_flags), (int8_t*)(ws + L.off_GT));
-    if (K + kPanel < L.n)
-        es_launch(gj_next_kernel, dim3((L.n + 63) / 64, kNumPrimes), dim3(256), 0, st,
-                           (int8_t*)(ws + L.off_S), L.n, L.pitch, K, (const int*)(ws + L.off_rowpos),
-                           (const int*)(ws + L.off_flags), (const int8_t*)(ws + L.off_GT));
+    const int G = (L.pitch + 255) / 256, N = K + kPanel < L.n ? (L.n + 63) / 64 : 0;
+    es_launch(gj_gather_next_kernel, dim3(G + N, kNumPrimes), dim3(256), 0, st, (int8_t*)(ws + L.off_S), L.n,
+              L.pitch, K, (const int*)(ws + L.off_piv), (const int*)(ws + L.off_rowpos),
+              (const int*)(ws + L.off_flags), (int8_t*)(ws + L.off_GT), G);
     return hipGetLastError();
 }
 
