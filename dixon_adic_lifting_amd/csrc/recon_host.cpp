@@ -18,6 +18,7 @@
 #include <cstring>
 #include <memory>
 #include <mutex>
+#include <thread>
 #include <vector>
 
 #include "../../include/es_solve.h"
@@ -235,8 +236,45 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
     HIPOK(hipStreamSynchronize(st));
     std::vector<BigInt> xs(sidx.size());
     parallel_for_each(sidx.size(), nthreads, [&](size_t k) { xs[k] = assemble(sd + k * dig_comp, m, P); });
-    BigInt d;
-    if (!sample_denominator(xs, M, nbits, dbits, nthreads, &d)) return ES_EINTERNAL;
+    // The sample's denominators (Wang reconstruction of each X mod M; their
+    // lcm is d).  The first two run first, each with a second thread for its
+    // cofactors, and the GPU pass starts from their lcm; the others finish on
+    // threads of their own meanwhile, and if the whole sample's lcm differs
+    // the pass is run again with it before any of its results are used.
+    const BigInt Nb = shl(BigInt::from_u64(1), (size_t)nbits);
+    const BigInt Db = shl(BigInt::from_u64(1), (size_t)dbits);
+    std::vector<BigInt> sden(xs.size());
+    std::atomic<int> bad{0};
+    auto sample_rr = [&](size_t k, bool split) {
+        try {
+            BigInt a = mod_floor(xs[k], M), nu, de;
+            if (!rational_reconstruct(a, M, Nb, Db, &nu, &de, false, split)) bad = 1;
+            else sden[k] = de;
+        } catch (...) {
+            bad = 1;
+        }
+    };
+    const size_t nfirst = std::min<size_t>(2, xs.size());
+    std::vector<std::thread> rest;
+    struct Joiner {
+        std::vector<std::thread>& v;
+        void join() {
+            for (auto& t : v)
+                if (t.joinable()) t.join();
+        }
+        ~Joiner() { join(); }
+    } rest_join{rest};
+    for (size_t k = nfirst; k < xs.size(); k++) rest.emplace_back(sample_rr, k, false);
+    {
+        std::thread second;
+        if (nfirst > 1) second = std::thread(sample_rr, (size_t)1, true);
+        sample_rr(0, true);
+        if (second.joinable()) second.join();
+    }
+    if (bad) return ES_EINTERNAL;
+    BigInt d = sden[0];
+    for (size_t k = 1; k < nfirst; k++) d = lcm(d, sden[k]);
+    bool sample_checked = rest.empty();
     lap(tm ? &tm->sample_ms : nullptr, "sample");
 
     uint32_t* Td = (uint32_t*)(scr + pl.off_T);
@@ -360,8 +398,6 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
     out->den.assign(NC, BigInt());
     std::vector<size_t> todo(NC);
     for (size_t j = 0; j < NC; j++) todo[j] = j;
-    const BigInt Nb = shl(BigInt::from_u64(1), (size_t)nbits);
-    const BigInt Db = shl(BigInt::from_u64(1), (size_t)dbits);
     // Digits of the listed components, copied to the host on the solve's stream.
     auto fetch = [&](const std::vector<size_t>& which, std::vector<int64_t>* buf) -> int {
         buf->resize(which.size() * dig_comp);
@@ -382,6 +418,22 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
     for (int pass = 0;; pass++) {
         int rc = gpu_pass();
         if (rc != ES_OK) return rc;
+        if (!sample_checked) {
+            rest_join.join();
+            sample_checked = true;
+            if (bad) return ES_EINTERNAL;
+            BigInt dall = d;
+            for (size_t k = nfirst; k < sden.size(); k++) dall = lcm(dall, sden[k]);
+            if (cmp(dall, d) != 0) {
+                // the first samples missed part of the denominator: this
+                // pass is dropped and run again with the whole sample's lcm
+                if (verbose()) fprintf(stderr, "[es] gpu reconstruct: the sample widened d, pass again\n");
+                HIPOK(hipStreamSynchronize(st));
+                d = dall;
+                pass--;
+                continue;
+            }
+        }
         HIPOK(hipEventSynchronize(words_ready));
         convert(todo);
         HIPOK(hipStreamSynchronize(st));

@@ -241,3 +241,31 @@ def test_bad_arguments():
         es.solve_pairs(torch.zeros((4, 5), dtype=torch.int64, device="cuda"), torch.zeros((4, 1), dtype=torch.int64, device="cuda"))
     with pytest.raises(ValueError):
         es.solve_pairs(A.double(), torch.zeros((4, 1), dtype=torch.int64, device="cuda"))
+
+
+def test_first_samples_miss_a_factor_of_the_denominator():
+    """The GPU reconstruction starts its pass from the lcm of the first two
+    sample components' denominators and checks it against the whole sample's
+    lcm (card, "Method": d is the lcm over the sample).  Here x = u + v / 7
+    with v zero at the first two sample indices (0 and 2 for n = 16), so those
+    two are integers while other components have denominator 7: the first
+    pass is dropped and run again with d = 7 lcm(...), and the result must
+    still be the exact solution."""
+    n = 16
+    rng = np.random.default_rng(31)
+    A = rng.integers(-50, 50, size=(n, n), dtype=np.int64)
+    u = rng.integers(-1000, 1000, size=n, dtype=np.int64)
+    v = rng.integers(1, 7, size=n, dtype=np.int64)
+    v[0] = v[2] = 0
+    # column 5 makes A v = 0 (mod 7): v_5 is invertible mod 7
+    k = 5
+    rest = (A @ v - A[:, k] * v[k]) % 7
+    inv = pow(int(v[k]), -1, 7)
+    A[:, k] = (-(rest * inv) % 7) + 7 * rng.integers(-5, 5, size=n)
+    assert np.all((A @ v) % 7 == 0)
+    b = (A @ u + (A @ v) // 7).reshape(n, 1)
+    got = solve_gpu(A, b)
+    ref = exact.solve(A, b)
+    assert got == ref
+    assert ref[0][0][1] == 1 and ref[2][0][1] == 1
+    assert math.lcm(*(row[0][1] for row in ref)) % 7 == 0
