@@ -196,7 +196,7 @@ def test_planted_integer_solution():
 
 
 @pytest.mark.parametrize("n,c,bits,seed", [(33, 17, 24, 1), (100, 5, 30, 2), (129, 1, 24, 3),
-                                           (300, 2, 16, 4), (64, 16, 40, 5)])
+                                           (300, 2, 16, 4), (64, 16, 40, 5), (40, 3, 32, 7)])
 def test_random_shapes_vs_c_oracle(n, c, bits, seed):
     A, b = W.uniform_system(n, c, bits, seed)
     X = solve_gpu(A, b)
@@ -269,3 +269,19 @@ def test_first_samples_miss_a_factor_of_the_denominator():
     assert got == ref
     assert ref[0][0][1] == 1 and ref[2][0][1] == 1
     assert math.lcm(*(row[0][1] for row in ref)) % 7 == 0
+
+
+def test_mfma_residual_plane_extremes():
+    """Several right-hand sides with |A| < 2^30 take the residual as int8 MFMA
+    products of A's four balanced byte planes and x's eight; entries at
+    +-(2^30 - 1), +-2^23 and -1, 0, 1 exercise every plane's extremes (the
+    top plane of 2^30 - 1 is 64, of -(2^30 - 1) is -64)."""
+    n, c = 24, 3
+    A, b = W.uniform_system(n, c, 24, 17)
+    A[0, 0] = (1 << 30) - 1
+    A[1, 5] = -((1 << 30) - 1)
+    A[2, 7] = 1 << 23
+    A[3, 9] = -(1 << 23)
+    A[4, 4], A[5, 5], A[6, 6] = -1, 0, 1
+    X = solve_gpu(A, b)
+    assert X == cbareiss.solve(A, b)
