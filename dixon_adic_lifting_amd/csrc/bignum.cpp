@@ -521,6 +521,32 @@ static bool small_quotient(u128 num, u128 den, uint64_t* q) {
 // ratio, (x + A) / (y + C) and (x + B) / (y + D), give it.  The cofactor
 // magnitudes stay below 2^62 (so a matrix covers about 62 bits, twice the
 // one-word form).  Returns false when not even one step is certain.
+// floor(num / den), den > 0, when it is below 2^40 (false otherwise): the
+// quotients 0 to 3 (about two in three of a Euclidean sequence's) by
+// subtraction, larger ones by small_quotient
+static inline bool quotient_below_2p40(u128 num, u128 den, uint64_t* q) {
+    // den < 2^125 here (y + |c| with y below 2^124), so 4 den does not wrap;
+    // the count of multiples reached is the quotient when it is below 4
+    const u128 d2 = den << 1, d3 = d2 + den;
+    const uint64_t k = (uint64_t)(num >= den) + (uint64_t)(num >= d2) + (uint64_t)(num >= d3);
+    if (k < 3 || num < d3 + den) {
+        *q = k;
+        return true;
+    }
+    return small_quotient(num, den, q);
+}
+
+// whether floor(num / den) == q (den > 0, q < 2^40): q den <= num and
+// num - q den < den, with q den formed without overflowing 128 bits
+static inline bool quotient_is(u128 num, u128 den, uint64_t q) {
+    const u128 hi = (den >> 64) * (u128)q;  // below 2^104
+    if (hi >> 64) return false;             // q den >= 2^128 > num
+    const u128 lo = (u128)(uint64_t)den * q;
+    const u128 p = (hi << 64) + lo;
+    if (p < lo || p > num) return false;    // wrapped (q den >= 2^128), or above num
+    return num - p < den;
+}
+
 static bool lehmer_matrix2(u128 xh, u128 yh, int64_t* A, int64_t* B, int64_t* C, int64_t* D) {
     int64_t a = 1, b = 0, c = 0, d = 1;
     i128 x = (i128)xh, y = (i128)yh;
@@ -529,10 +555,9 @@ static bool lehmer_matrix2(u128 xh, u128 yh, int64_t* A, int64_t* B, int64_t* C,
         if (den1 <= 0 || den2 <= 0) break;
         const i128 num1 = x + a, num2 = x + b;
         if (num1 < 0 || num2 < 0) break;
-        uint64_t q, q2;
-        if (!small_quotient((u128)num1, (u128)den1, &q) || !small_quotient((u128)num2, (u128)den2, &q2) ||
-            q != q2)
-            break;
+        // the step is certain when both bounds of the true ratio give the same quotient
+        uint64_t q;
+        if (!quotient_below_2p40((u128)num1, (u128)den1, &q) || !quotient_is((u128)num2, (u128)den2, q)) break;
         // |a - q c| <= |a| + q |c| (equal, as the signs alternate), likewise for b, d
         const u128 mc = (u128)(a < 0 ? -(i128)a : (i128)a) + (u128)q * (u128)(c < 0 ? -(i128)c : (i128)c);
         const u128 md = (u128)(b < 0 ? -(i128)b : (i128)b) + (u128)q * (u128)(d < 0 ? -(i128)d : (i128)d);
@@ -618,23 +643,25 @@ static int cmp_limbs(const limb_t* x, size_t nx, const limb_t* y, size_t ny) {
 // (x, y) <- (A x + B y, C x + D y) for nonnegative x, y (n limbs each, zero
 // padded) whose images are nonnegative; the cofactors have the sign pattern
 // (+, -, -, +) (EVEN) or (-, +, +, -) and magnitudes a, b, c, d below 2^63,
-// so every partial sum fits a signed 128-bit accumulator.
+// so every partial sum lies within +-2^127: formed modulo 2^128, its high
+// word read as signed is the next carry.
 template <bool EVEN>
 static void lincomb_rem_t(limb_t* x, limb_t* y, size_t n, uint64_t a, uint64_t b, uint64_t c, uint64_t d) {
-    i128 cx = 0, cy = 0;
+    int64_t cx = 0, cy = 0;
     for (size_t i = 0; i < n; i++) {
         const uint64_t xi = x[i], yi = y[i];
+        u128 tx, ty;
         if (EVEN) {
-            cx += (i128)((u128)a * xi) - (i128)((u128)b * yi);
-            cy += (i128)((u128)d * yi) - (i128)((u128)c * xi);
+            tx = (u128)a * xi - (u128)b * yi + (u128)(i128)cx;
+            ty = (u128)d * yi - (u128)c * xi + (u128)(i128)cy;
         } else {
-            cx += (i128)((u128)b * yi) - (i128)((u128)a * xi);
-            cy += (i128)((u128)c * xi) - (i128)((u128)d * yi);
+            tx = (u128)b * yi - (u128)a * xi + (u128)(i128)cx;
+            ty = (u128)c * xi - (u128)d * yi + (u128)(i128)cy;
         }
-        x[i] = (limb_t)cx;
-        y[i] = (limb_t)cy;
-        cx >>= 64;
-        cy >>= 64;
+        x[i] = (limb_t)tx;
+        y[i] = (limb_t)ty;
+        cx = (int64_t)(uint64_t)(tx >> 64);
+        cy = (int64_t)(uint64_t)(ty >> 64);
     }
     if (cx != 0 || cy != 0) throw std::logic_error("Lehmer step left a carry");
 }
