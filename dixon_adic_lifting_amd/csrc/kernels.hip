@@ -1792,15 +1792,16 @@ __global__ __launch_bounds__(256) void crt_kernel(const LiftParams* __restrict__
 
 // ---------------------------------------------------------------- lift: contraction + CRT, one right-hand side
 // For one right-hand side with rows of at least 1 KB, the contraction and
-// the CRT share a launch: a block owns kFusedComps consecutive components and
-// forms every live prime's residue for them, so the residues stay in LDS and
-// the CRT follows in the same block.  The live primes' B_j rows are copied
-// once per lift into component order (row k of Sperm_j is the row of S_j
-// that pivoted at step k), so a block reads 4 KB runs and the grid sweeps
-// every matrix front to back.  The block's rows (prime, component) go eight
-// to a wave as in the plain contraction (the sums meet in the same
-// transposed butterfly); the last wave's tail rows are duplicates whose
-// results are dropped.
+// the step's share of the CRT share a launch: a block owns kFusedComps
+// consecutive components and forms every live prime's residue for them, so
+// the residues stay in LDS and the CRT's step share (k and x mod 2^64, the
+// only part the next step needs) follows in the same block; the digits are
+// formed later from the stored (u_l, k) records.  The live primes' B_j rows
+// are copied once per lift into component order (row k of Sperm_j is the
+// row of S_j that pivoted at step k), so a block reads 4 KB runs and the
+// grid sweeps every matrix front to back.  The block's rows (prime,
+// component) go eight to a wave as in the plain contraction (the sums meet
+// in the same transposed butterfly).
 
 // Sperm[jl][rowpos[J][i]] = S[J][i]: one wave per row, 1 KB per load
 __global__ __launch_bounds__(256) void lift_rows_kernel(const int8_t* __restrict__ S, const int* __restrict__ rowpos,
