@@ -267,9 +267,14 @@ int run_lift(const int64_t* dA, const int64_t* db, uint8_t* ws, hipStream_t st, 
     fill_lift_params(ls, &prm);
     HIP_CHECK(hipMemcpyAsync(ws + L.off_params, &prm, sizeof prm, hipMemcpyHostToDevice, st));
     HIP_CHECK(launch_lift_positions(L, ws, st));
+    // several right-hand sides with |A| < 2^30: the residual on MFMA, and
+    // B_j's columns and the residues in natural row order
     const bool rmfma = residual_mfma_fits(L, pr.a32, pr.maxabs);
-    if (rmfma) HIP_CHECK(launch_a_planes(L, ws, st));
-    HIP_CHECK(launch_split_b(db, L, ws, ls.E, st));
+    if (rmfma) {
+        HIP_CHECK(launch_a_planes(L, ws, st));
+        HIP_CHECK(launch_natural_cols(L, ws, ls.E, st));
+    }
+    HIP_CHECK(launch_split_b(db, L, ws, ls.E, rmfma, st));
     const bool fused = lift_fused_fits(L);
     if (fused) HIP_CHECK(launch_lift_rows(L, ws, ls.E, st));
     const size_t NC = (size_t)L.n * L.c;

@@ -173,7 +173,8 @@ hipError_t launch_gj_update(const Layout& L, uint8_t* ws, int K, hipStream_t st)
 hipError_t launch_gj_panel_rest(const Layout& L, uint8_t* ws, int K, hipStream_t st);
 hipError_t launch_gj_gather_next(const Layout& L, uint8_t* ws, int K, hipStream_t st);
 hipError_t launch_export_inverse(const Layout& L, const uint8_t* ws, int8_t* B, hipStream_t st);
-hipError_t launch_split_b(const int64_t* b, const Layout& L, uint8_t* ws, int E, hipStream_t st);
+// r = b and its residues (natural: in natural row order, the MFMA residual's path)
+hipError_t launch_split_b(const int64_t* b, const Layout& L, uint8_t* ws, int E, bool natural, hipStream_t st);
 // one lift step = contraction, then the CRT (digit into chunk slot `slot`),
 // then the residual update with the split of the new residual
 hipError_t launch_lift_contract(const Layout& L, uint8_t* ws, int E, hipStream_t st);
@@ -189,6 +190,9 @@ hipError_t launch_lift_crt_records(const Layout& L, uint8_t* ws, int nrec, int s
 // A's planes once per lift, then per step the CRT also writes x_low's planes.
 bool residual_mfma_fits(const Layout& L, bool a32, uint64_t maxabs);
 hipError_t launch_a_planes(const Layout& L, uint8_t* ws, hipStream_t st);
+// S's live-prime rows in natural column order (the MFMA residual's path;
+// the lift's residues are then in natural order too)
+hipError_t launch_natural_cols(const Layout& L, uint8_t* ws, int E, hipStream_t st);
 // the residual's position table (c = 1), once per lift
 hipError_t launch_lift_positions(const Layout& L, uint8_t* ws, hipStream_t st);
 hipError_t launch_lift_rows(const Layout& L, uint8_t* ws, int E, hipStream_t st);

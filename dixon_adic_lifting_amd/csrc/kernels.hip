@@ -2057,7 +2057,7 @@ __global__ __launch_bounds__(256) void residual_kernel(const AT* __restrict__ A,
         mu16 = prm->mu16[lane];
         mu32 = prm->mu32[lane];
         r32 = prm->r32[lane];
-        pos = rowpos[(size_t)prm->qidx[lane] * n + r];
+        pos = rowpos ? rowpos[(size_t)prm->qidx[lane] * n + r] : r;  // null: natural order
     }
     for (int t0 = 0; t0 < c; t0 += CT) {
         uint64_t acc[CT];
@@ -2219,11 +2219,10 @@ constexpr int kResWaves = 8;  // waves of a block, splitting the contraction
 
 // Block: rows i0 .. i0 + 15 and columns t0 .. t0 + 15; wave w takes the
 // 64-byte chunks w, w + 8, ... of the contraction.  Then r <- (r - A x_low)
-// P^-1 and the next step's balanced residues, as in the other residual kernels.
+// P^-1 and the next step's balanced residues, in natural row order.
 __global__ __launch_bounds__(kResWaves * 64) void residual_mfma_kernel(
     const int8_t* __restrict__ Ab, const int8_t* __restrict__ xp, int n, int c, int pitch,
-    int64_t* __restrict__ R, const LiftParams* __restrict__ prm, const int* __restrict__ rowpos,
-    int8_t* __restrict__ rho) {
+    int64_t* __restrict__ R, const LiftParams* __restrict__ prm, int8_t* __restrict__ rho) {
     typedef int v4i_r __attribute__((ext_vector_type(4)));
     __shared__ uint64_t part[kResWaves][4][64];
     __shared__ uint64_t sval[16][16];
@@ -2312,23 +2311,49 @@ __global__ __launch_bounds__(kResWaves * 64) void residual_mfma_kernel(
         sval[rho_][tt] = val;
     }
     __syncthreads();
-    // next residues: lane l is live prime l, the eight waves take two rows each
+    // next residues in natural row order (the lift reads B_j with its
+    // columns in that order): wave w takes the live primes w, w + 8, ...;
+    // lane (t, g) the column t0 + t and rows 4 g .. 4 g + 3, one word a store
     const int E = prm->E;
-    if (lane >= E) return;
-    const uint32_t q = prm->q[lane], mu16 = prm->mu16[lane], mu32 = prm->mu32[lane], r32 = prm->r32[lane];
-    const int J = prm->qidx[lane];
+    const int t = lane >> 2, g = lane & 3;
+    const bool colok = t0 + t < c;
+    const int r0 = i0 + 4 * g;
+    for (int jl = wave; jl < E; jl += kResWaves) {
+        const uint32_t q = prm->q[jl], mu16 = prm->mu16[jl], mu32 = prm->mu32[jl], r32 = prm->r32[jl];
+        if (!colok) continue;
+        uint32_t w = 0;
 #pragma unroll
-    for (int h = 0; h < 2; h++) {
-        const int rr = 2 * wave + h, i = i0 + rr;
-        if (i >= n) continue;
-        const int pos = rowpos[(size_t)J * n + i];
-#pragma unroll
-        for (int tt = 0; tt < 16; tt++) {
-            const int t = t0 + tt;
-            if (t >= c) break;
-            const uint32_t res = mod_i64((int64_t)sval[rr][tt], q, mu16, mu32, r32);
-            rho[((size_t)lane * c + t) * pitch + pos] = (int8_t)balanced(res, q);
+        for (int e = 0; e < 4; e++) {
+            const uint32_t res = mod_i64((int64_t)sval[4 * g + e][t], q, mu16, mu32, r32);
+            w |= ((uint32_t)balanced(res, q) & 0xffu) << (8 * e);
         }
+        int8_t* dst = rho + ((size_t)jl * c + t0 + t) * pitch + r0;
+        if (r0 + 4 <= n) {
+            *(uint32_t*)dst = w;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+                if (r0 + e < n) dst[e] = (int8_t)(w >> (8 * e));
+        }
+    }
+}
+
+// Once per lift on the MFMA residual's path: every live prime's row of S
+// rewritten in natural column order, S[J][i][r] <- S[J][i][rowpos[J][r]]
+// (zero past n), so the contraction takes its residues in natural order.
+// One block per (row, prime); the row goes through LDS.
+__global__ __launch_bounds__(256) void natural_cols_kernel(int8_t* __restrict__ S, const int* __restrict__ rowpos,
+                                                           const LiftParams* __restrict__ prm, int n, int pitch) {
+    extern __shared__ __attribute__((aligned(16))) int8_t rowbuf[];
+    const int J = prm->qidx[blockIdx.y];
+    const int i = blockIdx.x;
+    int8_t* row = S + ((size_t)J * n + i) * pitch;
+    for (int k = threadIdx.x * 16; k < pitch; k += 256 * 16) *(uint4*)(rowbuf + k) = *(const uint4*)(row + k);
+    __syncthreads();
+    const int* rp = rowpos + (size_t)J * n;
+    for (int r = threadIdx.x; r < pitch; r += 256) {
+        const int k = r < n ? rp[r] : -1;
+        row[r] = (k >= 0 && k < pitch) ? rowbuf[k] : (int8_t)0;
     }
 }
 
@@ -2337,8 +2362,15 @@ bool residual_mfma_fits(const Layout& L, bool a32, uint64_t maxabs) {
         const char* e = std::getenv("ES_RESIDUAL_VALU");
         return e && e[0] == '1';
     }();
-    return !off && L.c > 1 && a32 && maxabs < ((uint64_t)1 << 30) && L.pitch % 64 == 0 &&
+    return !off && L.c > 1 && a32 && maxabs < ((uint64_t)1 << 30) && L.pitch % 64 == 0 && L.pitch <= 48 * 1024 &&
            4 * (size_t)L.n * L.pitch <= (size_t)0x7fffffff && 8 * (size_t)L.c * L.pitch <= (size_t)0x7fffffff;
+}
+
+hipError_t launch_natural_cols(const Layout& L, uint8_t* ws, int E, hipStream_t st) {
+    if (E < 1 || E > kNumPrimes || L.pitch > 48 * 1024) return hipErrorInvalidValue;
+    es_launch(natural_cols_kernel, dim3(L.n, E), dim3(256), (uint32_t)L.pitch, st, (int8_t*)(ws + L.off_S),
+              (const int*)(ws + L.off_rowpos), (const LiftParams*)(ws + L.off_params), L.n, L.pitch);
+    return hipGetLastError();
 }
 
 hipError_t launch_a_planes(const Layout& L, uint8_t* ws, hipStream_t st) {
@@ -2348,7 +2380,7 @@ hipError_t launch_a_planes(const Layout& L, uint8_t* ws, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_split_b(const int64_t* b, const Layout& L, uint8_t* ws, int E, hipStream_t st) {
+hipError_t launch_split_b(const int64_t* b, const Layout& L, uint8_t* ws, int E, bool natural, hipStream_t st) {
     (void)E;
     hipError_t e = hipMemcpyAsync(ws + L.off_R, b, (size_t)L.n * L.c * sizeof(int64_t),
                                   hipMemcpyDeviceToDevice, st);
@@ -2362,7 +2394,8 @@ hipError_t launch_split_b(const int64_t* b, const Layout& L, uint8_t* ws, int E,
     else
         es_launch((residual_kernel<int64_t, 16>), grid, dim3(256), 0, st, (const int64_t*)nullptr,
                            L.n, L.c, (int64_t*)(ws + L.off_R), (const uint64_t*)(ws + L.off_xlow),
-                           (const LiftParams*)(ws + L.off_params), (const int*)(ws + L.off_rowpos),
+                           (const LiftParams*)(ws + L.off_params),
+                           natural ? (const int*)nullptr : (const int*)(ws + L.off_rowpos),
                            (int8_t*)(ws + L.off_rho), L.pitch, 1);
     return hipGetLastError();
 }
@@ -2495,8 +2528,7 @@ hipError_t launch_lift_residual(const Layout& L, uint8_t* ws, bool a32, const in
         if (!a32 || L.c < 2 || L.pitch % 64 != 0) return hipErrorInvalidValue;
         es_launch(residual_mfma_kernel, dim3((L.n + 15) / 16, (L.c + 15) / 16), dim3(kResWaves * 64), 0, st,
                   (const int8_t*)(ws + L.off_Ab), (const int8_t*)(ws + L.off_xp), L.n, L.c, L.pitch,
-                  (int64_t*)(ws + L.off_R), (const LiftParams*)(ws + L.off_params),
-                  (const int*)(ws + L.off_rowpos), (int8_t*)(ws + L.off_rho));
+                  (int64_t*)(ws + L.off_R), (const LiftParams*)(ws + L.off_params), (int8_t*)(ws + L.off_rho));
         return hipGetLastError();
     }
     const dim3 grid((L.n + 3) / 4);

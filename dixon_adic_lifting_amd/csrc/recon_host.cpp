@@ -237,10 +237,13 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
     std::vector<BigInt> xs(sidx.size());
     parallel_for_each(sidx.size(), nthreads, [&](size_t k) { xs[k] = assemble(sd + k * dig_comp, m, P); });
     // The sample's denominators (Wang reconstruction of each X mod M; their
-    // lcm is d).  The first two run first, each with a second thread for its
-    // cofactors, and the GPU pass starts from their lcm; the others finish on
-    // threads of their own meanwhile, and if the whole sample's lcm differs
-    // the pass is run again with it before any of its results are used.
+    // lcm is d).  With one right-hand side the first two run first, with a
+    // second thread each for the cofactors, and the GPU pass starts from
+    // their lcm; the others finish on threads of their own meanwhile, and if
+    // the whole sample's lcm differs the pass is run again with it before any
+    // of its results are used.  With several right-hand sides (whose
+    // denominators differ, so a part of the sample misses factors far more
+    // often) the whole sample runs first.
     const BigInt Nb = shl(BigInt::from_u64(1), (size_t)nbits);
     const BigInt Db = shl(BigInt::from_u64(1), (size_t)dbits);
     std::vector<BigInt> sden(xs.size());
@@ -254,7 +257,8 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
             bad = 1;
         }
     };
-    const size_t nfirst = std::min<size_t>(2, xs.size());
+    const size_t nfirst = pl.c == 1 ? std::min<size_t>(2, xs.size()) : xs.size();
+    const bool split_first = 4 * nfirst <= (size_t)nthreads;
     std::vector<std::thread> rest;
     struct Joiner {
         std::vector<std::thread>& v;
@@ -264,13 +268,21 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
         }
         ~Joiner() { join(); }
     } rest_join{rest};
-    for (size_t k = nfirst; k < xs.size(); k++) rest.emplace_back(sample_rr, k, false);
-    {
+    auto start_rest = [&]() {
+        for (size_t k = nfirst; k < xs.size(); k++) rest.emplace_back(sample_rr, k, false);
+    };
+    // the others start at once when they and the first ones fit the cores
+    const bool rest_now = nfirst * (split_first ? 2 : 1) + (xs.size() - nfirst) <= (size_t)nthreads;
+    if (rest_now) start_rest();
+    if (nfirst <= 2) {
         std::thread second;
-        if (nfirst > 1) second = std::thread(sample_rr, (size_t)1, true);
-        sample_rr(0, true);
+        if (nfirst > 1) second = std::thread(sample_rr, (size_t)1, split_first);
+        sample_rr(0, split_first);
         if (second.joinable()) second.join();
+    } else {
+        parallel_for_each(nfirst, nthreads, [&](size_t k) { sample_rr(k, split_first); });
     }
+    if (!rest_now) start_rest();
     if (bad) return ES_EINTERNAL;
     BigInt d = sden[0];
     for (size_t k = 1; k < nfirst; k++) d = lcm(d, sden[k]);

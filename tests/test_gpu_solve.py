@@ -243,32 +243,39 @@ def test_bad_arguments():
         es.solve_pairs(A.double(), torch.zeros((4, 1), dtype=torch.int64, device="cuda"))
 
 
-def test_first_samples_miss_a_factor_of_the_denominator():
-    """The GPU reconstruction starts its pass from the lcm of the first two
-    sample components' denominators and checks it against the whole sample's
-    lcm (card, "Method": d is the lcm over the sample).  Here x = u + v / 7
-    with v zero at the first two sample indices (0 and 2 for n = 16), so those
-    two are integers while other components have denominator 7: the first
-    pass is dropped and run again with d = 7 lcm(...), and the result must
-    still be the exact solution."""
+@pytest.mark.parametrize("c", [1, 2])
+def test_first_samples_miss_a_factor_of_the_denominator(c):
+    """With one right-hand side the GPU reconstruction starts its pass from
+    the lcm of the first two sample components' denominators and checks it
+    against the whole sample's lcm (card, "Method": d is the lcm over the
+    sample); with several it waits for the whole sample.  Here every column
+    of x is u + v / 7 with v zero in rows 0 and 2 (for n = 16 the first two
+    samples are components 0 and 2 at c = 1), so those are integers while
+    other components have denominator 7: at c = 1 the first pass is dropped
+    and run again with the whole sample's d; at c = 2 the whole sample gives
+    d at once.  Either way the result must be exact."""
     n = 16
     rng = np.random.default_rng(31)
     A = rng.integers(-50, 50, size=(n, n), dtype=np.int64)
-    u = rng.integers(-1000, 1000, size=n, dtype=np.int64)
-    v = rng.integers(1, 7, size=n, dtype=np.int64)
-    v[0] = v[2] = 0
-    # column 5 makes A v = 0 (mod 7): v_5 is invertible mod 7
+    U = rng.integers(-1000, 1000, size=(n, c), dtype=np.int64)
+    V = rng.integers(1, 7, size=(n, c), dtype=np.int64)
+    V[0, :] = V[2, :] = 0
+    # column 5 of A makes A V = 0 (mod 7) for the first column of V ...
     k = 5
+    v = V[:, 0]
     rest = (A @ v - A[:, k] * v[k]) % 7
-    inv = pow(int(v[k]), -1, 7)
-    A[:, k] = (-(rest * inv) % 7) + 7 * rng.integers(-5, 5, size=n)
-    assert np.all((A @ v) % 7 == 0)
-    b = (A @ u + (A @ v) // 7).reshape(n, 1)
+    A[:, k] = (-(rest * pow(int(v[k]), -1, 7)) % 7) + 7 * rng.integers(-5, 5, size=n)
+    # ... and the other columns of V are multiples of it mod 7
+    for t in range(1, c):
+        V[:, t] = (V[:, 0] * (t + 1)) % 7
+    assert np.all((A @ V) % 7 == 0)
+    b = A @ U + (A @ V) // 7
     got = solve_gpu(A, b)
     ref = exact.solve(A, b)
     assert got == ref
-    assert ref[0][0][1] == 1 and ref[2][0][1] == 1
-    assert math.lcm(*(row[0][1] for row in ref)) % 7 == 0
+    for t in range(c):
+        assert ref[0][t][1] == 1 and ref[2][t][1] == 1
+        assert math.lcm(*(row[t][1] for row in ref)) % 7 == 0
 
 
 def test_mfma_residual_plane_extremes():
