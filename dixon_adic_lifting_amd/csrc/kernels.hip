@@ -1289,10 +1289,13 @@ __global__ __launch_bounds__(256) void gj_gather_next_kernel(int8_t* __restrict_
 
 bool blocked_inverse_fits(const Layout& L) { return L.n <= 4096 && (L.pitch % 64) == 0; }
 
-// the panel variant for panel K: unpacked for full panels of up to 1024 rows
+// the panel variant for panel K: unpacked for full panels of up to 2048 rows
+// (one or two rows a thread), byte-packed otherwise
 static int panel_kind(const Layout& L, int K) {
-    if (L.n <= 1024) return L.n - K >= kPanel ? 0 : 1;
-    return L.n <= 2048 ? 2 : 4;
+    const bool full = L.n - K >= kPanel;
+    if (L.n <= 1024) return full ? 0 : 1;
+    if (L.n <= 2048) return full ? 5 : 2;
+    return 4;
 }
 
 hipError_t launch_gj_panel(const Layout& L, uint8_t* ws, int K, hipStream_t st) {
@@ -1306,6 +1309,7 @@ hipError_t launch_gj_panel(const Layout& L, uint8_t* ws, int K, hipStream_t st) 
         case 0: es_launch((gj_panel_kernel<1, true>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT); break;
         case 1: es_launch((gj_panel_kernel<1, false>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT); break;
         case 2: es_launch((gj_panel_kernel<2, false>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT); break;
+        case 5: es_launch((gj_panel_kernel<2, true>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT); break;
         default: es_launch((gj_panel_kernel<4, false>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT); break;
     }
     return hipGetLastError();
@@ -1334,6 +1338,7 @@ hipError_t launch_gj_panel_rest(const Layout& L, uint8_t* ws, int K, hipStream_t
         case 0: es_launch((gj_panel_rest_kernel<1, true>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT, ntx, nty); break;
         case 1: es_launch((gj_panel_rest_kernel<1, false>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT, ntx, nty); break;
         case 2: es_launch((gj_panel_rest_kernel<2, false>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT, ntx, nty); break;
+        case 5: es_launch((gj_panel_rest_kernel<2, true>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT, ntx, nty); break;
         default: es_launch((gj_panel_rest_kernel<4, false>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT, ntx, nty); break;
     }
     return hipGetLastError();
