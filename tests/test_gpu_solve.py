@@ -104,6 +104,22 @@ def test_solve_c5():
     check_mod_primes(A, b, X, rows=[0, 1, 1023, 2047])
 
 
+@pytest.mark.parametrize("n,c", [(128, 1), (512, 1), (256, 16), (512, 16)])
+def test_card_table_shapes(n, c):
+    """The card's other measured shapes (24-bit entries), drawn as the bench
+    sweep draws them.  Up to 8192 unknowns A x = b is checked exactly (the
+    solution is unique, so this fixes every bit); above, modulo five primes
+    plus exact rows."""
+    A, b = W.uniform_system(n, c, 24, 1000 + n + c)
+    X = solve_gpu(A, b)
+    assert len(X) == n and len(X[0]) == c
+    assert_normal_form(X)
+    if n * c <= 4096:
+        assert exact.check_solution(A, b, X)
+    else:
+        check_mod_primes(A, b, X, rows=[0, n // 2, n - 1])
+
+
 # ------------------------------------------------------------------ edge families
 
 def test_n1():
