@@ -135,6 +135,14 @@ def solution_info(sol):
             "modulus_bits": lib.es_solution_modulus_bits(sol)}
 
 
+def last_recon_counts():
+    """(components reconstructed alone on the host, gcds finished on the host)
+    for the last GPU reconstruction on this thread; (-1, -1) if none ran."""
+    a, g = ctypes.c_int64(), ctypes.c_int64()
+    load().es_dbg_last_recon_counts(ctypes.byref(a), ctypes.byref(g))
+    return a.value, g.value
+
+
 def last_timings():
     buf = (ctypes.c_double * 5)()
     load().es_last_timings(buf)

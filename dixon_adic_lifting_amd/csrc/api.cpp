@@ -53,6 +53,9 @@ enum KernelClass {
 };
 
 thread_local bool g_profiling = false;
+// components the last GPU reconstruction on this thread finished on the host
+// (outside the numerator bound: reconstructed alone; or gcds left to the host)
+thread_local int64_t g_recon_alone = -1, g_recon_host_gcds = -1;
 thread_local double g_kernel_ms[KC_COUNT] = {};
 thread_local int32_t g_kernel_cnt[KC_COUNT] = {};
 
@@ -377,6 +380,13 @@ int es_kernel_profile(double* total_ms, int32_t* counts, int32_t cap) {
     return KC_COUNT;
 }
 
+int es_dbg_last_recon_counts(int64_t* alone, int64_t* host_gcds) {
+    if (!alone || !host_gcds) return ES_EINVAL;
+    *alone = g_recon_alone;
+    *host_gcds = g_recon_host_gcds;
+    return ES_OK;
+}
+
 int es_last_timings(double* ms5) {
     if (!ms5) return ES_EINVAL;
     for (int i = 0; i < 5; i++) ms5[i] = g_timings[i];
@@ -437,6 +447,8 @@ int es_solve_device(const int64_t* dA, const int64_t* db, int32_t n, int32_t c, 
                                  &prof);
             g_timings[3] = rt.gpu_ms;
             g_timings[4] = ms_since(t0);
+            g_recon_alone = (int64_t)rt.failed;
+            g_recon_host_gcds = (int64_t)rt.host_gcds;
             prof.collect();
         } else {
             int64_t* digits = (int64_t*)g_pinned.get((size_t)n * c * m * kDigitLimbs * sizeof(int64_t));

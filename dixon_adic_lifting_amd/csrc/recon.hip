@@ -76,11 +76,13 @@ __global__ __launch_bounds__(256) void digit_bytes_kernel(const uint64_t* __rest
 
 // ---------------------------------------------------------------- weight chains
 // A wave-resident integer of NW = TM + 1 32-bit words (TM = index of the top
-// word of M); lane l holds words [l CW, l CW + CW).  One step replaces
-// R in [0, 2M) by 256 R - t M with t = max(0, floor(256 R / M - 2^-16)):
-// the quotient estimate from the top three words of R and M in double
-// precision is within 2^-19 of the true value, so t is the true floor or one
-// less and the result stays in [0, 2M) without a comparison.
+// word of 2M, so M's own top word may be zero); lane l holds words
+// [l CW, l CW + CW).  One step replaces R in [0, 2M) by s R - t M with
+// t = max(0, floor(s R / M - 2^-16)) for s <= 2^24.  The windows of R and M
+// (three words from TM down, at least 63 significant bits of M) and the
+// double-precision quotient put the estimate within about s 2^-50 <= 2^-26
+// of s R / M, so t is the true floor or one less and the result stays in
+// [0, 2M) without a comparison.
 template <int CW>
 __device__ __forceinline__ void wave_mul_reduce(uint32_t (&R)[CW], const uint32_t (&Mr)[CW], int lane, int TM,
                                                 double Md, uint32_t s) {
@@ -129,11 +131,16 @@ __device__ __forceinline__ void wave_mul_reduce(uint32_t (&R)[CW], const uint32_
 // writes rows 48 i + b, b < 42, of W [Kpad][Ncolsp] (u8, little-endian bytes
 // of R_{i,b} = 256^b T_i reduced into [0, 2M)); rows 48 i + 42 .. 48 i + 47
 // are zero.  Ncolsp / 4 <= 64 CW words per row are written, zero beyond TM.
+// Wave w of the block takes the rows b = w (mod 3): one step by 256^w, then
+// steps by 2^24, so the three chains of 14 steps run side by side.  With
+// s = 2^24 the quotient estimate's error (about 2^-28) stays far inside the
+// 2^-16 margin, so each step still lands in [0, 2M).
 template <int CW>
-__global__ __launch_bounds__(64) void wchain_kernel(const uint32_t* __restrict__ T, const uint32_t* __restrict__ Mw,
-                                                    int TM, double Md, int Ncolsp, uint8_t* __restrict__ W) {
+__global__ __launch_bounds__(192) void wchain_kernel(const uint32_t* __restrict__ T, const uint32_t* __restrict__ Mw,
+                                                     int TM, double Md, int Ncolsp, uint8_t* __restrict__ W) {
     const int i = blockIdx.x;
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int w0 = threadIdx.x >> 6;
     uint32_t R[CW], Mr[CW];
 #pragma unroll
     for (int c = 0; c < CW; c++) {
@@ -141,15 +148,16 @@ __global__ __launch_bounds__(64) void wchain_kernel(const uint32_t* __restrict__
         R[c] = w <= TM ? T[(size_t)i * (TM + 1) + w] : 0u;
         Mr[c] = w <= TM ? Mw[w] : 0u;
     }
+    if (w0 > 0) wave_mul_reduce<CW>(R, Mr, lane, TM, Md, 1u << (8 * w0));
     const int rowwords = Ncolsp / 4;
-    for (int b = 0; b < 48; b++) {
+    for (int b = w0; b < 48; b += 3) {
         uint32_t* dst = (uint32_t*)(W + (size_t)(48 * i + b) * Ncolsp);
 #pragma unroll
         for (int c = 0; c < CW; c++) {
             const int w = lane * CW + c;
             if (w < rowwords) dst[w] = b < 42 ? R[c] : 0u;
         }
-        if (b < 41) wave_mul_reduce<CW>(R, Mr, lane, TM, Md, 256u);
+        if (b + 3 < 42) wave_mul_reduce<CW>(R, Mr, lane, TM, Md, 1u << 24);
     }
 }
 
@@ -655,11 +663,11 @@ hipError_t launch_wchain(const uint32_t* T, const uint32_t* Mw, int m, int TM, d
                          hipStream_t st) {
     const int NW = TM + 1;
     if (NW <= 64 * 8)
-        es_launch(wchain_kernel<8>, dim3(m), dim3(64), 0, st, T, Mw, TM, Md, Ncolsp, W);
+        es_launch(wchain_kernel<8>, dim3(m), dim3(192), 0, st, T, Mw, TM, Md, Ncolsp, W);
     else if (NW <= 64 * 32)
-        es_launch(wchain_kernel<32>, dim3(m), dim3(64), 0, st, T, Mw, TM, Md, Ncolsp, W);
+        es_launch(wchain_kernel<32>, dim3(m), dim3(192), 0, st, T, Mw, TM, Md, Ncolsp, W);
     else if (NW <= 64 * 64)
-        es_launch(wchain_kernel<64>, dim3(m), dim3(64), 0, st, T, Mw, TM, Md, Ncolsp, W);
+        es_launch(wchain_kernel<64>, dim3(m), dim3(192), 0, st, T, Mw, TM, Md, Ncolsp, W);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

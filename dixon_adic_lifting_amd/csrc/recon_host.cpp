@@ -143,7 +143,10 @@ GpuReconPlan plan_gpu_recon(int n, int c, int m, size_t mbits, int nbits) {
     pl.c = c;
     pl.m = m;
     pl.NC = (size_t)n * c;
-    pl.TM = (int)((mbits - 1) / 32);
+    // words 0 .. TM hold every value in [0, 2M) (weights and numerators are
+    // kept in that range), so M's own top word may be zero: the three-word
+    // windows of M below then still carry at least 63 bits
+    pl.TM = (int)(mbits / 32);
     pl.NW = pl.TM + 1;
     pl.nw = nbits / 32 + 1;
     // the quotient window needs three words of M; a weight row must fit one

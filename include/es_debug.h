@@ -42,6 +42,13 @@ int es_dbg_ratrec(const uint64_t *a, int32_t la, const uint64_t *M, int32_t lM, 
 int es_dbg_step_count(uint64_t mask, int32_t nbits, int32_t dbits, int32_t *m_exact, int64_t *bits_exact,
                       int32_t *m_fast, int64_t *bits_fast);
 
+/* For the last solve on the calling thread that took the GPU
+ * reconstruction: `alone` = components whose GPU numerator fell outside the
+ * bound and were reconstructed alone on the host; `host_gcds` = components
+ * whose gcd the host finished.  Both -1 if no such solve has run on this
+ * thread.  Returns 0, or -1 for a null pointer. */
+int es_dbg_last_recon_counts(int64_t *alone, int64_t *host_gcds);
+
 #ifdef __cplusplus
 }
 #endif

@@ -17,7 +17,7 @@ import pytest
 import torch
 
 import dixon_adic_lifting_amd as es
-from dixon_adic_lifting_amd import workloads as W
+from dixon_adic_lifting_amd import _lib, workloads as W
 from oracle import cbareiss, exact, modular
 
 pytestmark = pytest.mark.gpu
@@ -308,3 +308,28 @@ def test_mfma_residual_plane_extremes():
     A[4, 4], A[5, 5], A[6, 6] = -1, 0, 1
     X = solve_gpu(A, b)
     assert X == cbareiss.solve(A, b)
+
+
+def test_modulus_with_a_full_top_word():
+    """A modulus M = P^m whose bit length is a multiple of 32 (its top 32-bit
+    word at least 2^31).  The GPU reconstruction keeps weights and numerators
+    in [0, 2M), one bit above M, so its word window must reach past M's top
+    word; otherwise every numerator leaves the bound and falls back to the
+    host.  With all 53 primes live, m = 23 gives such a modulus; 64 x 64
+    systems with 50-56-bit entries land near it."""
+    hit = None
+    for bits in range(50, 57):
+        for seed in range(12):
+            A, b = W.uniform_system(64, 1, bits, 7000 + 100 * bits + seed)
+            X, info = es.solve_info(torch.as_tensor(A).cuda(), torch.as_tensor(b).cuda())
+            if X is not None and info["modulus_bits"] % 32 == 0:
+                hit = (A, b, X)
+                break
+        if hit:
+            break
+    assert hit is not None, "no 32-aligned modulus among the draws"
+    A, b, X = hit
+    alone, host_gcds = _lib.last_recon_counts()
+    assert alone == 0 and host_gcds >= 0, (alone, host_gcds)
+    assert_normal_form(X)
+    assert exact.check_solution(A, b, X)
