@@ -3,10 +3,10 @@
 // Prime set and step count follow the exact-solve card (phanerozoic/
 // exact-solve), section "Method": P is a squarefree product of odd primes
 // below 256 (odd so that P^-1 mod 2^64 exists), and the lift runs until P^m
-// exceeds twice the product of the Hadamard bounds on numerator and
-// denominator.  Reconstruction follows the same section: a common
-// denominator from a small sample of components, then one modular multiply
-// per numerator.
+// is larger than 2 N D, with N and D the Hadamard-type bounds on the
+// numerators and the denominator.  Reconstruction follows the same section:
+// the shared denominator is found from a few components, and each numerator
+// then takes one product modulo P^m.
 #include "host.h"
 
 #include <sched.h>

@@ -1,10 +1,11 @@
 // HIP kernels for the rational-reconstruction stage on CDNA4 (gfx950).
 //
-// Method (exact-solve card, phanerozoic/exact-solve, section "Method"): once
-// P^m exceeds twice the product of the Hadamard bounds, a common denominator
-// d comes from a small sample of components, and every numerator is then one
-// modular multiply, y = d X mods M with M = P^m and X = sum_i x_i P^i; y is
-// accepted when |y| <= N.  Here all numerators are formed at once as one
+// Method (exact-solve card, phanerozoic/exact-solve, section "Method"): the
+// lift stops when M = P^m is larger than 2 N D (N, D the Hadamard-type
+// bounds on numerators and denominator); the denominator d shared by the
+// components is found from a few of them, and each numerator is then a
+// single product modulo M, y = d X mods M with X = sum_i x_i P^i, accepted
+// when |y| <= N.  Here all numerators are formed at once as one
 // int8 GEMM on the matrix cores:
 //
 //   X_j = sum_{i, b} s_{j,i,b} 256^b P^i, where s_{j,i,b} are the balanced

@@ -1,7 +1,7 @@
 // Host side of the GPU reconstruction path (kernels in recon.hip).
 //
 // Method (exact-solve card, phanerozoic/exact-solve, section "Method"): the
-// common denominator d comes from a small sample of components (Wang
+// denominator d shared by the components is found from a few of them (Wang
 // reconstruction on the host), then each numerator is one modular multiply
 // y = d X mods M, accepted when |y| <= N, and reduced to lowest terms by
 // gcd(y, d).  The modular multiplies of all components run on the GPU as one

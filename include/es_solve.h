@@ -4,9 +4,9 @@
  *
  * Method (exact-solve card, phanerozoic/exact-solve, section "Method"):
  * B = A^-1 mod P for a squarefree odd P = prod q_j over primes q_j < 256,
- * r_0 = b, x_i = B r_i mod P, r_{i+1} = (r_i - A x_i) / P; the digits x_i
- * reconstruct x once P^m exceeds twice the Hadamard bound on numerator and
- * denominator.  A^-1 mod q_j comes from a batched Gauss-Jordan inverse (all
+ * r_0 = b, x_i = B r_i mod P, r_{i+1} = (r_i - A x_i) / P; m digits
+ * determine x once P^m is larger than 2 N D, N and D being Hadamard-type
+ * bounds on the numerators and the denominator.  A^-1 mod q_j comes from a batched Gauss-Jordan inverse (all
  * primes at once; one launch per elimination step, or blocked 32 steps per
  * panel with an int8-MFMA rank-32 update; Barrett-style reduction); each
  * step's x_i is one int8 contraction per prime, a balanced CRT into the
@@ -179,8 +179,9 @@ int es_kernel_profile(double *total_ms, int32_t *counts, int32_t cap);
 
 /*
  * Batched modular inverse (card, "Method": A^-1 mod q_j for every prime by
- * Gauss-Jordan over the augmented matrix, one grid per elimination step
- * spanning all primes, Barrett reduction in place of hardware modulo).
+ * Gauss-Jordan elimination of [A | I], each elimination step one launch
+ * over every prime, reductions by precomputed reciprocals rather than the
+ * hardware remainder).
  * dA: device int64 [n][n]; d_ws: workspace as for es_solve_device with c = 1.
  * dB_out: device int8 [53][n][n]; row-major A^-1 mod q_j with entries in the
  * balanced range [-(q_j-1)/2, (q_j-1)/2]; rows of a prime with flag 1 are
@@ -210,7 +211,7 @@ int es_lift_digits(const int64_t *dA, const int64_t *db, int32_t n, int32_t c,
 
 /*
  * Host rational reconstruction (card, "Method": common denominator from a
- * small sample of components, then one modular multiply per numerator).
+ * few components, then each numerator by one product modulo P^m).
  * digits: host int64 [n*c][m][6] as written by es_lift_digits; live_mask
  * selects the primes whose product is P; x = A^-1 b is recovered from
  * X = sum x_i P^i given |numerators| <= 2^num_bits and

@@ -16,8 +16,11 @@
  *   2. d = M[n-1][n-1] = +-det A; back substitution
  *      N_i = (d M[i][n+t] - sum_{j>i} M[i][j] N_j) / M[i][i], exact by Cramer.
  *   3. x_i = N_i / d reduced by gcd, sign moved to the numerator.
- * Big integers: sign-magnitude, 64-bit limbs, schoolbook multiplication,
- * Knuth's Algorithm D for division, Euclid for gcd.  Nothing is tuned.
+ * Big integers: sign-magnitude, 64-bit limbs, schoolbook multiplication.
+ * Every division the method makes is exact (Bareiss's quotients, the back
+ * substitution by Cramer's rule, lowest terms by the gcd), so division is
+ * the 2-adic exact division, checked; the gcd is the binary algorithm.
+ * Nothing is tuned.
  */
 #include <pthread.h>
 #include <stdint.h>
@@ -154,130 +157,151 @@ static void bz_addsub(bz *r, const bz *a, const bz *b, int sgn, bz *tmp) {
     bz_copy(r, tmp);
 }
 
-static int clz64(uint64_t x) { return __builtin_clzll(x); }
+/* number of trailing zero bits of a nonzero magnitude */
+static long mag_ctz(const uint64_t *a, int la) {
+    long z = 0;
+    int i = 0;
+    while (i < la && a[i] == 0) { i++; z += 64; }
+    if (i == la) die("trailing zeros of zero");
+    return z + __builtin_ctzll(a[i]);
+}
 
-/*
- * Knuth, TAOCP vol. 2, 4.3.1, Algorithm D on 64-bit limbs.
- * q gets la - lb + 1 limbs, rem gets lb limbs.  Requires lb >= 1, la >= lb,
- * b[lb-1] != 0.  Scratch: un (la + 1 limbs), vn (lb limbs).
- */
-static void mag_divmod(uint64_t *q, uint64_t *rem, const uint64_t *a, int la,
-                       const uint64_t *b, int lb, uint64_t *un, uint64_t *vn) {
-    if (lb == 1) {
-        uint64_t r = 0;
-        for (int i = la - 1; i >= 0; i--) {
-            u128 cur = ((u128)r << 64) | a[i];
-            q[i] = (uint64_t)(cur / b[0]);
-            r = (uint64_t)(cur % b[0]);
-        }
-        rem[0] = r;
-        return;
+/* r = a >> sh (r may be a itself: limb i reads limbs at or above i); returns
+   the normalised length */
+static int mag_shr(uint64_t *r, const uint64_t *a, int la, long sh) {
+    int limbs = (int)(sh / 64), bits = (int)(sh % 64);
+    int lr = la - limbs;
+    if (lr <= 0) return 0;
+    for (int i = 0; i < lr; i++) {
+        uint64_t v = a[i + limbs] >> bits;
+        if (bits && i + limbs + 1 < la) v |= a[i + limbs + 1] << (64 - bits);
+        r[i] = v;
     }
-    int s = clz64(b[lb - 1]);
-    for (int i = lb - 1; i > 0; i--)
-        vn[i] = s ? (b[i] << s) | (b[i - 1] >> (64 - s)) : b[i];
-    vn[0] = b[0] << s;
-    un[la] = s ? a[la - 1] >> (64 - s) : 0;
-    for (int i = la - 1; i > 0; i--)
-        un[i] = s ? (a[i] << s) | (a[i - 1] >> (64 - s)) : a[i];
-    un[0] = a[0] << s;
+    while (lr > 0 && r[lr - 1] == 0) lr--;
+    return lr;
+}
 
-    for (int j = la - lb; j >= 0; j--) {
-        u128 num = ((u128)un[j + lb] << 64) | un[j + lb - 1];
-        u128 qhat = num / vn[lb - 1];
-        u128 rhat = num % vn[lb - 1];
-        while (qhat >> 64 || qhat * vn[lb - 2] > ((rhat << 64) | un[j + lb - 2])) {
-            qhat--;
-            rhat += vn[lb - 1];
-            if (rhat >> 64) break;
-        }
-        /* multiply and subtract */
-        uint64_t borrow = 0, carry = 0;
-        for (int i = 0; i < lb; i++) {
-            u128 p = qhat * vn[i] + carry;
-            carry = (uint64_t)(p >> 64);
-            uint64_t plo = (uint64_t)p;
-            uint64_t t = un[i + j] - plo;
-            uint64_t b1 = un[i + j] < plo;
-            uint64_t t2 = t - borrow;
-            uint64_t b2 = t < borrow;
-            un[i + j] = t2;
-            borrow = b1 | b2;
-        }
-        uint64_t top = un[j + lb];
-        uint64_t t = top - carry;
-        uint64_t b1 = top < carry;
-        uint64_t t2 = t - borrow;
-        uint64_t b2 = t < borrow;
-        un[j + lb] = t2;
-        if (b1 | b2) {
-            /* qhat was one too large: add back */
-            qhat--;
-            uint64_t c = 0;
-            for (int i = 0; i < lb; i++) {
-                u128 sum = (u128)un[i + j] + vn[i] + c;
-                un[i + j] = (uint64_t)sum;
-                c = (uint64_t)(sum >> 64);
-            }
-            un[j + lb] += c;
-        }
-        q[j] = (uint64_t)qhat;
+/* r = a << sh, r has room for la + sh/64 + 1 limbs and does not alias a;
+   returns the normalised length */
+static int mag_shl(uint64_t *r, const uint64_t *a, int la, long sh) {
+    int limbs = (int)(sh / 64), bits = (int)(sh % 64);
+    memset(r, 0, (size_t)(la + limbs + 1) * sizeof(uint64_t));
+    for (int i = 0; i < la; i++) {
+        r[i + limbs] |= a[i] << bits;
+        r[i + limbs + 1] = bits ? a[i] >> (64 - bits) : 0;
     }
-    for (int i = 0; i < lb - 1; i++)
-        rem[i] = s ? (un[i] >> s) | (un[i + 1] << (64 - s)) : un[i];
-    rem[lb - 1] = un[lb - 1] >> s;
+    int lr = la + limbs + 1;
+    while (lr > 0 && r[lr - 1] == 0) lr--;
+    return lr;
 }
 
 typedef struct {
-    bz t1, t2, t3, un, vn;
+    bz t1, w, v, q;
 } scratch;
 
 static void scratch_free(scratch *s) {
-    bz_clear(&s->t1); bz_clear(&s->t2); bz_clear(&s->t3); bz_clear(&s->un); bz_clear(&s->vn);
+    bz_clear(&s->t1); bz_clear(&s->w); bz_clear(&s->v); bz_clear(&s->q);
 }
 
-/* truncated division of magnitudes: q = |a| / |b|, r = |a| % |b| (signs set by caller) */
-static void bz_divmod_mag(bz *q, bz *r, const bz *a, const bz *b, scratch *s) {
+/*
+ * Exact division by the 2-adic method (Jebelean, "An algorithm for exact
+ * division", 1993): q = |a| / |b| when |b| divides |a|.  Both are shifted
+ * right by the divisor's trailing zero bits, which makes the divisor odd and
+ * so invertible modulo 2^64; then the quotient is built from its lowest limb
+ * up: limb i is the running remainder's limb i times that inverse (mod 2^64),
+ * and that multiple of the divisor, shifted by i limbs, is subtracted.  When
+ * the division is exact the remainder ends at zero; any other outcome
+ * (a bit of |a| below the divisor's lowest set bit, a borrow out of the top,
+ * or a nonzero limb left over) means it was not.  Returns 0 and sets q's
+ * magnitude, or -1 if |b| does not divide |a|.
+ */
+static int mag_divexact(bz *q, const bz *a, const bz *b, scratch *s) {
     if (b->len == 0) die("division by zero");
-    if (mag_cmp(a->d, a->len, b->d, b->len) < 0) {
-        if (q) { q->len = 0; q->neg = 0; }
-        if (r) { bz_copy(r, a); r->neg = 0; }
-        return;
+    if (a->len == 0) { q->len = 0; q->neg = 0; return 0; }
+    long sh = mag_ctz(b->d, b->len);
+    if (mag_ctz(a->d, a->len) < sh) return -1;
+    bz_reserve(&s->w, a->len);
+    bz_reserve(&s->v, b->len);
+    int la = mag_shr(s->w.d, a->d, a->len, sh);
+    int lb = mag_shr(s->v.d, b->d, b->len, sh);
+    uint64_t *w = s->w.d;
+    const uint64_t *v = s->v.d;
+    if (la < lb) return -1;
+    int lq = la - lb + 1;
+    /* Newton's iteration x <- x (2 - v0 x) doubles the correct low bits of
+       an inverse of the odd v0; v0 itself is one modulo 8 */
+    uint64_t inv = v[0];
+    for (int it = 0; it < 5; it++) inv *= 2 - v[0] * inv;
+    bz_reserve(&s->q, lq);
+    uint64_t *qd = s->q.d;
+    for (int i = 0; i < lq; i++) {
+        uint64_t qi = w[i] * inv;
+        qd[i] = qi;
+        /* w -= qi * v * 2^(64 i), with a signed running carry */
+        __int128 acc = 0;
+        for (int j = 0; j < lb; j++) {
+            u128 p = (u128)qi * v[j];
+            acc += (__int128)w[i + j] - (__int128)(uint64_t)p;
+            w[i + j] = (uint64_t)acc;
+            acc >>= 64;
+            acc -= (__int128)(uint64_t)(p >> 64);
+        }
+        for (int k = i + lb; acc != 0 && k < la; k++) {
+            acc += (__int128)w[k];
+            w[k] = (uint64_t)acc;
+            acc >>= 64;
+        }
+        if (acc != 0) return -1;          /* the remainder went negative */
     }
-    int la = a->len, lb = b->len;
-    bz_reserve(&s->un, la + 1);
-    bz_reserve(&s->vn, lb);
-    bz_reserve(&s->t2, la - lb + 1);
-    bz_reserve(&s->t3, lb);
-    mag_divmod(s->t2.d, s->t3.d, a->d, la, b->d, lb, s->un.d, s->vn.d);
-    s->t2.len = la - lb + 1; s->t2.neg = 0; bz_norm(&s->t2);
-    s->t3.len = lb; s->t3.neg = 0; bz_norm(&s->t3);
-    if (q) bz_copy(q, &s->t2);
-    if (r) bz_copy(r, &s->t3);
+    for (int k = 0; k < la; k++)
+        if (w[k] != 0) return -1;
+    bz_reserve(q, lq);
+    memcpy(q->d, qd, (size_t)lq * sizeof(uint64_t));
+    q->len = lq;
+    q->neg = 0;
+    bz_norm(q);
+    return 0;
 }
 
 /* q = a / b, the division being exact (checked) */
 static void bz_divexact(bz *q, const bz *a, const bz *b, scratch *s) {
-    if (a->len == 0) { q->len = 0; q->neg = 0; return; }
-    bz_reserve(&s->t1, 1);
-    bz_divmod_mag(q, &s->t1, a, b, s);
-    if (s->t1.len != 0) die("inexact division");
     int neg = a->neg ^ b->neg;
+    if (mag_divexact(q, a, b, s) != 0) die("inexact division");
     q->neg = q->len ? neg : 0;
 }
 
-/* g = gcd(|a|, |b|) by Euclid's algorithm */
+/*
+ * g = gcd(|a|, |b|) by the binary algorithm (Stein, 1967; Knuth, TAOCP
+ * vol. 2, 4.5.2, Algorithm B): the common power of two is set aside, both
+ * numbers are made odd, and the smaller is subtracted from the larger, whose
+ * factors of two are then removed, until the two are equal.
+ */
 static void bz_gcd(bz *g, const bz *a, const bz *b, scratch *s) {
-    bz x = {0}, y = {0}, r = {0};
+    (void)s;
+    if (a->len == 0 || b->len == 0) {
+        bz_copy(g, a->len ? a : b);
+        g->neg = 0;
+        return;
+    }
+    bz x = {0}, y = {0};
     bz_copy(&x, a); x.neg = 0;
     bz_copy(&y, b); y.neg = 0;
-    while (y.len != 0) {
-        bz_divmod_mag(NULL, &r, &x, &y, s);
-        bz_copy(&x, &y);
-        bz_copy(&y, &r);
+    long za = mag_ctz(x.d, x.len), zb = mag_ctz(y.d, y.len);
+    long common = za < zb ? za : zb;
+    x.len = mag_shr(x.d, x.d, x.len, za);
+    y.len = mag_shr(y.d, y.d, y.len, zb);
+    for (;;) {
+        int c = mag_cmp(x.d, x.len, y.d, y.len);
+        if (c == 0) break;
+        if (c < 0) { bz t = x; x = y; y = t; }
+        x.len = mag_sub(x.d, x.d, x.len, y.d, y.len);   /* even and nonzero */
+        while (x.len > 0 && x.d[x.len - 1] == 0) x.len--;
+        x.len = mag_shr(x.d, x.d, x.len, mag_ctz(x.d, x.len));
     }
-    bz_copy(g, &x);
-    bz_clear(&x); bz_clear(&y); bz_clear(&r);
+    bz_reserve(g, x.len + (int)(common / 64) + 2);
+    g->len = mag_shl(g->d, x.d, x.len, common);
+    g->neg = 0;
+    bz_clear(&x); bz_clear(&y);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -478,3 +502,53 @@ int oracle_solve(const int64_t *A, const int64_t *b, int n, int c, int nthreads,
 }
 
 void oracle_free(char *p) { free(p); }
+
+/* ------------------------------------------------------------------------
+ * Test hooks: the exact division and the gcd on magnitudes given as
+ * little-endian uint64 limbs, so the tests can check them against Python
+ * integers.  The result is written to r (room for cap limbs), its length to
+ * *lr.  oracle_dbg_divexact returns 0, or 1 when b does not divide a exactly;
+ * oracle_dbg_gcd returns 0.  Both return -1 when b is zero (divexact) or the
+ * result does not fit.
+ */
+static void bz_from_limbs(bz *x, const uint64_t *a, int la) {
+    bz_reserve(x, la > 0 ? la : 1);
+    if (la) memcpy(x->d, a, (size_t)la * sizeof(uint64_t));
+    x->len = la;
+    x->neg = 0;
+    bz_norm(x);
+}
+
+int oracle_dbg_divexact(const uint64_t *a, int la, const uint64_t *b, int lb, uint64_t *r, int *lr, int cap) {
+    bz A = {0}, B = {0}, Q = {0};
+    scratch s;
+    memset(&s, 0, sizeof s);
+    bz_from_limbs(&A, a, la);
+    bz_from_limbs(&B, b, lb);
+    int rc = -1;
+    if (B.len != 0) {
+        rc = mag_divexact(&Q, &A, &B, &s) == 0 ? 0 : 1;
+        if (rc == 0) {
+            if (Q.len > cap) rc = -1;
+            else { memcpy(r, Q.d, (size_t)Q.len * sizeof(uint64_t)); *lr = Q.len; }
+        }
+    }
+    bz_clear(&A); bz_clear(&B); bz_clear(&Q);
+    scratch_free(&s);
+    return rc;
+}
+
+int oracle_dbg_gcd(const uint64_t *a, int la, const uint64_t *b, int lb, uint64_t *r, int *lr, int cap) {
+    bz A = {0}, B = {0}, G = {0};
+    scratch s;
+    memset(&s, 0, sizeof s);
+    bz_from_limbs(&A, a, la);
+    bz_from_limbs(&B, b, lb);
+    bz_gcd(&G, &A, &B, &s);
+    int rc = 0;
+    if (G.len > cap) rc = -1;
+    else { if (G.len) memcpy(r, G.d, (size_t)G.len * sizeof(uint64_t)); *lr = G.len; }
+    bz_clear(&A); bz_clear(&B); bz_clear(&G);
+    scratch_free(&s);
+    return rc;
+}

@@ -40,6 +40,11 @@ def _load():
         lib.oracle_solve_timed.restype = ctypes.c_int
         lib.oracle_free.argtypes = [ctypes.c_char_p]
         lib.oracle_free.restype = None
+        u64p = ctypes.POINTER(ctypes.c_uint64)
+        for fn in (lib.oracle_dbg_divexact, lib.oracle_dbg_gcd):
+            fn.argtypes = [u64p, ctypes.c_int, u64p, ctypes.c_int, u64p, ctypes.POINTER(ctypes.c_int),
+                           ctypes.c_int]
+            fn.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -90,3 +95,40 @@ def solve(A, b, threads: int | None = None):
     vals = [tuple(int(tok, 16) for tok in line.split()) for line in text.splitlines()]
     assert len(vals) == n * c
     return [vals[r * c:(r + 1) * c] for r in range(n)]
+
+
+def _limbs(v: int):
+    v = abs(v)
+    out = []
+    while v:
+        out.append(v & (2**64 - 1))
+        v >>= 64
+    return (ctypes.c_uint64 * max(1, len(out)))(*out), len(out)
+
+
+def _bignum_call(fn, a: int, b: int):
+    lib = _load()
+    A, la = _limbs(a)
+    B, lb = _limbs(b)
+    cap = max(la, lb) + 2
+    R = (ctypes.c_uint64 * cap)()
+    lr = ctypes.c_int(0)
+    st = getattr(lib, fn)(A, la, B, lb, R, ctypes.byref(lr), cap)
+    return st, sum(int(R[i]) << (64 * i) for i in range(lr.value))
+
+
+def divexact_magnitudes(a: int, b: int):
+    """|a| / |b| by the C oracle's exact division, or None if it reports that
+    |b| does not divide |a| (test hook)."""
+    st, q = _bignum_call("oracle_dbg_divexact", a, b)
+    if st == 1:
+        return None
+    assert st == 0
+    return q
+
+
+def gcd_magnitudes(a: int, b: int) -> int:
+    """gcd(|a|, |b|) by the C oracle's binary gcd (test hook)."""
+    st, g = _bignum_call("oracle_dbg_gcd", a, b)
+    assert st == 0
+    return g

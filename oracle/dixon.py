@@ -5,17 +5,17 @@ its order and notation:
 
 * modulus P = prod(q_j), a squarefree product of odd primes q_j < 256;
 * B = A^-1 mod P, r_0 = b, x_i = B r_i mod P, r_{i+1} = (r_i - A x_i) / P;
-* the digits x_i reconstruct x once P^m exceeds twice the Hadamard bound on
-  numerator and denominator;
-* the final rational reconstruction takes a common denominator from a small
-  sample of components, then one modular multiply per numerator.
+* m digits suffice once P^m is larger than 2 N D, N and D being the
+  Hadamard-type bounds on the numerators and on the denominator;
+* the rational reconstruction finds the denominator shared by the
+  components from a few of them, then each numerator by a single product
+  modulo P^m.
 
 Readings where the card is silent (each also listed with the design notes):
 the digits are balanced, x_i in [-(P-1)/2, (P-1)/2]; primes that divide det A
 are dropped from P; the bound is P^m > 2 N D with D the Hadamard bound on
 |det A| and N the Cramer-Hadamard bound on every numerator; the sample is
-the first row (one component of each right-hand side) and then seven
-components spread over the rows, floor(k nc/8) + (k mod c) for k = 1..7.
+the first four components in row-major order.
 """
 from __future__ import annotations
 
@@ -157,16 +157,16 @@ def rational_reconstruct(a: int, M: int, N: int, D: int):
     return r1, t1
 
 
-def sample_indices(total: int, c: int = 1):
-    """Row-major component indices used to find the common denominator: the
-    first row (one component of every right-hand side, whose denominators can
-    differ) and then component floor(k total/8) + (k mod c) for k = 1..7."""
-    out = list(range(min(c, total)))
-    for k in range(1, 8):
-        j = k * total // 8 + k % c
-        if c <= j < total and j not in out:
-            out.append(j)
-    return out
+SAMPLE_SIZE = 4
+
+
+def sample_indices(total: int):
+    """Components whose reconstructed denominators form the common
+    denominator.  The card asks only for a few sampled components; the
+    plainest reading is the first few in row-major order, here four.  The
+    result does not depend on the choice: a component whose numerator falls
+    outside the bound is reconstructed on its own and widens d."""
+    return list(range(min(total, SAMPLE_SIZE)))
 
 
 def reconstruct_solution(X, M: int, N: int, D: int):
@@ -181,7 +181,7 @@ def reconstruct_solution(X, M: int, N: int, D: int):
     c = len(X[0])
     flat = [X[r][t] for r in range(n) for t in range(c)]
     d = 1
-    for idx in sample_indices(len(flat), c):
+    for idx in sample_indices(len(flat)):
         f = rational_reconstruct(flat[idx], M, N, D)
         if f is None:
             return None

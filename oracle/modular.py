@@ -21,12 +21,6 @@ def odd_primes_below(bound: int = 256):
     return out
 
 
-def balanced(v: int, q: int) -> int:
-    """Representative of v mod q in [-(q-1)/2, (q-1)/2] (q odd)."""
-    r = v % q
-    return r - q if r > (q - 1) // 2 else r
-
-
 def inverse_mod(A, q: int):
     """A^-1 mod q as an int64 array with entries in [0, q), or None.
 

@@ -227,6 +227,26 @@ def test_solution_identity_every_output():
         assert not exact.check_solution(A, b, bad)
 
 
+def test_check_identity_rejects_wrong_numerators_or_denominator():
+    """The card's identity A N == d b holds for Bareiss's numerators and
+    determinant, and fails for a changed numerator, a changed d, a numerator
+    vector scaled against d, or N and d both negated in only one place."""
+    for seed in range(4):
+        A, b = W.uniform_system(12, 2, 20, 300 + seed)
+        N, d = exact.bareiss_solve_numerators(A, b)
+        assert exact.check_identity(A, b, N, d)
+        assert exact.check_identity(A, b, [[-v for v in row] for row in N], -d)   # same fraction
+        bad = [list(r) for r in N]
+        bad[5][1] += 1
+        assert not exact.check_identity(A, b, bad, d)
+        assert not exact.check_identity(A, b, N, d + 1)
+        assert not exact.check_identity(A, b, N, -d)
+        assert not exact.check_identity(A, b, [[2 * v for v in row] for row in N], d)
+        swapped = [list(r) for r in N]
+        swapped[0], swapped[1] = swapped[1], swapped[0]
+        assert not exact.check_identity(A, b, swapped, d)
+
+
 # ---------------------------------------------------------------- C oracle
 
 @pytest.mark.parametrize("n,c,bits,seed", [(1, 1, 8, 0), (3, 4, 8, 1), (17, 2, 24, 2),
@@ -255,6 +275,53 @@ def test_c_oracle_thread_count_invariant():
     ref = cbareiss.solve(A, b, 1)
     for T in (2, 5, 8):
         assert cbareiss.solve(A, b, T) == ref
+
+
+def _rand_big(rng, limbs):
+    v = rng.getrandbits(64 * limbs)
+    return v | (1 << (64 * limbs - 1)) if limbs else 0
+
+
+@pytest.mark.parametrize("la,lb", [(1, 1), (3, 1), (8, 3), (40, 17), (120, 60), (300, 299)])
+def test_c_oracle_exact_division_vs_python(la, lb):
+    """The C oracle's 2-adic exact division against Python's integer division:
+    quotients of exact multiples (odd divisors, divisors with many trailing
+    zero bits, divisor 1, quotient 1), and rejection of every inexact case."""
+    rng = random.Random(1000 * la + lb)
+    for trial in range(12):
+        b = _rand_big(rng, lb)
+        if trial % 3 == 1:
+            b <<= rng.randrange(1, 200)               # even divisor, zero limbs at the bottom
+        elif trial % 3 == 2:
+            b |= 1
+        q = _rand_big(rng, max(1, la - lb + 1))
+        assert cbareiss.divexact_magnitudes(q * b, b) == q
+        assert cbareiss.divexact_magnitudes(-q * b, b) == q          # magnitudes
+        assert cbareiss.divexact_magnitudes(q * b, q) == b
+        # inexact: a remainder in the low bits, in the top limbs, or |a| < |b|
+        assert cbareiss.divexact_magnitudes(q * b + 1, b) is None or b == 1
+        if b > 1:
+            assert cbareiss.divexact_magnitudes(q * b + b // 2 + 1, b) is None
+            assert cbareiss.divexact_magnitudes(b - 1, b) is None
+        assert cbareiss.divexact_magnitudes(q * b + (b << (64 * (la + 1))), b) == q + (1 << (64 * (la + 1)))
+    assert cbareiss.divexact_magnitudes(0, 12345) == 0
+    assert cbareiss.divexact_magnitudes(5, 1) == 5
+    assert cbareiss.divexact_magnitudes(6, 4) is None                 # fewer trailing zeros than b
+    assert cbareiss.divexact_magnitudes(1 << 200, 1 << 137) == 1 << 63
+
+
+@pytest.mark.parametrize("la,lb", [(1, 1), (2, 5), (17, 17), (60, 33)])
+def test_c_oracle_binary_gcd_vs_python(la, lb):
+    rng = random.Random(7 * la + lb)
+    for trial in range(10):
+        a, b = _rand_big(rng, la), _rand_big(rng, lb)
+        g = _rand_big(rng, 1 + trial % 3) << rng.randrange(0, 130)
+        for x, y in ((a, b), (a * g, b * g), (a * g, g), (g, g)):
+            assert cbareiss.gcd_magnitudes(x, y) == math.gcd(x, y)
+            assert cbareiss.gcd_magnitudes(-x, y) == math.gcd(x, y)
+    assert cbareiss.gcd_magnitudes(0, 0) == 0
+    assert cbareiss.gcd_magnitudes(0, 99) == 99
+    assert cbareiss.gcd_magnitudes(1 << 300, 3 << 200) == 1 << 200
 
 
 # ---------------------------------------------------------------- modular inverse
