@@ -29,6 +29,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, TOP/s
+# VALU rates from the unit counts: 256 CUs x 4 SIMDs x 16 lanes at 2.4 GHz for a
+# full-rate 32-bit operation; a 64-bit integer multiply-add (v_mad_u64_u32) issues
+# at a quarter of that
+INT32_VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12          # 39.3
+INT64_MAD_PEAK_TOPS = INT32_VALU_PEAK_TOPS / 4               # 9.83
 PAGES_MS_C4 = {"rtx_pro_6000": 2411.0, "h200": 2235.0}   # card, "Measured" table, n=1024 c=1
 
 
@@ -44,7 +49,12 @@ def parse():
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--sweep", action="store_true", help="time every workload and print a table")
+    ap.add_argument("--no-multi-column", dest="multi_column", action="store_false",
+                    help="skip the short n = 2048, c = 16 block")
     return ap.parse_args()
+
+
+MULTI_COLUMN = "c5_n2048_c16_int24"
 
 
 def digest(pairs):
@@ -54,24 +64,29 @@ def digest(pairs):
 
 
 class Solver:
-    """Raw C-ABI solve on torch-allocated device memory and the current stream."""
+    """Raw C-ABI solves on torch-allocated device memory and the current stream.
 
-    def __init__(self, A, b):
+    Holds several inputs of one shape, all resident in HBM: input 0 is the
+    workload's canonical draw, the others are its seeded redraws, so that
+    consecutive solves never see the same system."""
+
+    def __init__(self, inputs):
         import torch
         import dixon_adic_lifting_amd as es
         from dixon_adic_lifting_amd import _lib
         self.torch, self.es, self._lib = torch, es, _lib
         self.lib = _lib.load()
         self.dev = torch.device("cuda", 0)
-        self.A = torch.as_tensor(A, device=self.dev).contiguous()
-        self.b = torch.as_tensor(b, device=self.dev).contiguous()
-        self.n, self.c = self.A.shape[0], self.b.shape[1]
+        self.inputs = [(torch.as_tensor(A, device=self.dev).contiguous(), torch.as_tensor(b, device=self.dev).contiguous())
+                       for (A, b) in inputs]
+        self.n, self.c = self.inputs[0][0].shape[0], self.inputs[0][1].shape[1]
         self.ws = torch.empty(es.workspace_bytes(self.n, self.c), dtype=torch.uint8, device=self.dev)
         self.stream = ctypes.c_void_p(torch.cuda.current_stream(self.dev).cuda_stream)
 
-    def solve(self, keep=False):
+    def solve(self, idx=0, keep=False):
+        A, b = self.inputs[idx % len(self.inputs)]
         sol = ctypes.c_void_p()
-        st = self.lib.es_solve_device(ctypes.c_void_p(self.A.data_ptr()), ctypes.c_void_p(self.b.data_ptr()),
+        st = self.lib.es_solve_device(ctypes.c_void_p(A.data_ptr()), ctypes.c_void_p(b.data_ptr()),
                                       self.n, self.c, ctypes.c_void_p(self.ws.data_ptr()), self.ws.numel(),
                                       self.stream, ctypes.byref(sol))
         if st != 0:
@@ -85,22 +100,35 @@ class Solver:
         self.torch.cuda.synchronize(self.dev)
 
 
+MAX_DISTINCT_INPUTS = 32
+
+
+def workload_inputs(name, count):
+    """The workload's canonical draw and count - 1 seeded redraws (at most
+    MAX_DISTINCT_INPUTS in all; a longer run cycles through them)."""
+    from dixon_adic_lifting_amd import workloads as W
+    return [W.generate(name, attempt=k) for k in range(max(1, min(count, MAX_DISTINCT_INPUTS)))]
+
+
 def progress(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def time_solves(S, steps, warmup):
+    """W warm-up solves on redraws 1..W, then K timed solves: the canonical
+    draw, then redraws W+1, W+2, ... (each input once while there are enough)."""
     for w in range(warmup):
         t1 = time.perf_counter()
-        S.solve()
+        S.solve(1 + w)
         progress(f"warmup {w + 1}/{warmup}: {1e3 * (time.perf_counter() - t1):.1f} ms")
     S.sync()
     per = []
     stage_runs = []
+    order = [0] + [warmup + k for k in range(1, steps)]
     t0 = time.perf_counter()
     for k in range(steps):
         t1 = time.perf_counter()
-        S.solve()
+        S.solve(order[k])
         per.append(time.perf_counter() - t1)
         stage_runs.append(S._lib.last_timings())
         progress(f"step {k + 1}/{steps}: {1e3 * per[-1]:.1f} ms")
@@ -254,6 +282,37 @@ def rooflines(prof, info, n, c, traffic=None):
         ms, cnt = prof.get(k, (0.0, 0))
         if cnt:
             out[k] = {"avg_launch_us": round(ms / cnt * 1e3, 2), "launches": cnt, "total_ms": round(ms, 3)}
+    if c == 1 and "residual" in out:
+        # one right-hand side: A as int32 once per step, r in and out, the next residues out
+        bytes_per = 4.0 * n * n + 16.0 * n + E * pitch
+        gbs = bytes_per / (out["residual"]["avg_launch_us"] / 1e6) / 1e9
+        out["residual"].update({"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                                "algorithmic_bytes_per_launch": int(bytes_per)})
+    if "residues" in out:
+        # A (int64) read once; every prime's residue matrix and the int32 copy of A written
+        bytes_per = 8.0 * n * n + 53.0 * n * pitch + 4.0 * n * n
+        gbs = bytes_per / (out["residues"]["avg_launch_us"] / 1e6) / 1e9
+        out["residues"].update({"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                                "algorithmic_bytes_per_launch": int(bytes_per)})
+    if "gj_panel" in out:
+        # the panel's element updates, four 32-bit integer operations each (multiply-add,
+        # reduction), against the chip's 32-bit integer VALU rate
+        ops = 4.0 * out["gj_panel"]["element_updates_per_launch"]
+        r = ops / (out["gj_panel"]["avg_launch_us"] / 1e6) / 1e12
+        out["gj_panel"].update({"bound": "alu", "achieved": round(r, 3), "peak": INT32_VALU_PEAK_TOPS,
+                                "unit": "TOP/s", "frac": round(r / INT32_VALU_PEAK_TOPS, 5), "traffic": None})
+    if "recon_gcd" in out and info.get("gcd_bits"):
+        # Lehmer gcd of every component's numerator and d: rounds of about 28 quotient bits,
+        # each applying a 2 x 2 matrix to both numbers' live 30-bit limbs (4 multiply-adds a
+        # limb), so about B^2 / 420 64-bit multiply-adds for B-bit operands
+        B = info["gcd_bits"]
+        ops = n * c * B * B / 420.0
+        r = ops / (out["recon_gcd"]["total_ms"] / 1e3) / 1e12
+        out["recon_gcd"].update({"bound": "alu", "achieved": round(r, 3), "peak": INT64_MAD_PEAK_TOPS,
+                                 "unit": "T mul-add/s", "frac": round(r / INT64_MAD_PEAK_TOPS, 4), "traffic": None,
+                                 "algorithmic_mul_adds_total": ops})
     if c > 1 and info.get("entry_bits", 64) <= 30 and "residual" in out:
         # several right-hand sides: A x mod 2^64 as int8 MFMA products of 4 byte planes of A
         # and 8 of x (the 26 plane pairs below 2^64), 2 n^2 c ops each
@@ -265,65 +324,100 @@ def rooflines(prof, info, n, c, traffic=None):
     return out
 
 
-def cpu_baseline(A, b, budget_s):
-    """Time the plain-C Bareiss oracle on the first K elimination steps of this
-    very system (K sized to the CPU budget) and project a full solve.
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None if unreadable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
-    The oracle reports each step's wall time; a least-squares fit of
-    t_k = a e_k + b e_k L_k^2 (e_k entries updated at step k, each about L_k
-    64-bit limbs: entries after step k are (k+1)-minors) is summed over all
-    n steps.  Back substitution (O(n^4) limb operations against O(n^5) for the
-    elimination) is left out, so the projection is a lower bound.
-    """
+
+def _oracle_projection(A, b, threads, K):
+    """Time the plain-C Bareiss oracle on the first K elimination steps of
+    (A, b) and project the whole solve.
+
+    The oracle reports each step's wall time.  Step k updates
+    e_k = (n - k - 1)(n + c - k - 1) entries, each two products, a difference
+    and an exact division of (k + 1)-minors of about L_k 64-bit limbs
+    (Hadamard: (k + 1)(log2 max|A| + log2(k + 1) / 2) bits), so
+    t_k = e_k (a + c L_k + d L_k^2) is fitted by least squares over the
+    sampled steps and summed over all n.  Back substitution takes n products
+    per row of numbers up to L_n limbs, about a (c n^2 L_n^2 / 2) share, and
+    is added with the fitted d."""
     import numpy as np
     from oracle import cbareiss
     n, c = A.shape[0], b.shape[1]
-    threads = cbareiss.default_threads()
-    amax = max(2, int(np.abs(A).max()))
-    bits_entry = math.log2(amax)
+    bits_entry = math.log2(max(2, int(np.abs(A).max())))
 
-    def model(k):
+    def limbs(k):
+        return (k + 1) * (bits_entry + 0.5 * math.log2(k + 1) + 1.0) / 64.0 + 1.0
+
+    def feats(k):
         e = (n - k - 1) * (n + c - k - 1)
-        limbs = (k + 1) * (bits_entry + 0.5 * math.log2(k + 1) + 1.0) / 64.0 + 1.0
-        return e, e * limbs * limbs
+        L = limbs(k)
+        return [e, e * L, e * L * L]
 
-    def run(K):
-        st = np.zeros(n, dtype=np.float64)
-        t0 = time.perf_counter()
-        cbareiss.run(A, b, threads=threads, max_steps=K, step_seconds=st)
-        return time.perf_counter() - t0, st[:K]
+    st = np.zeros(n, dtype=np.float64)
+    t0 = time.perf_counter()
+    cbareiss.run(A, b, threads=threads, max_steps=K, step_seconds=st)
+    dt = time.perf_counter() - t0
+    lo = min(4, K // 4)
+    X = np.array([feats(k) for k in range(lo, K)], dtype=np.float64)
+    coef, *_ = np.linalg.lstsq(X, st[lo:K], rcond=None)
+    coef = np.maximum(coef, 0.0)
+    elim = sum(float(np.dot(coef, feats(k))) for k in range(n))
+    Ln = limbs(n - 1)
+    back = coef[2] * c * n * n * Ln * Ln / 2.0 / threads
 
-    def fit(ts, lo):
-        X = np.array([model(k) for k in range(lo, len(ts))], dtype=np.float64)
-        y = ts[lo:]
-        coef, *_ = np.linalg.lstsq(X, y, rcond=None)
-        return max(coef[0], 0.0), max(coef[1], 0.0)
+    def steps_within(seconds):
+        """the number of leading steps whose fitted times sum to about `seconds`"""
+        acc, k = 0.0, 0
+        while k < n and acc < seconds:
+            acc += float(np.dot(coef, feats(k)))
+            k += 1
+        return k
+    return elim + back, dt, coef, steps_within
 
-    K = min(n, 48)
-    dt, ts = run(K)
+
+def cpu_baseline(A, b, budget_s):
+    """The CPU oracle on the host cores: a bounded sample of this very system
+    (its first elimination steps, sized to the budget) projected to a full
+    solve; the same projection checked against a full timed oracle run of
+    the n = 256 system (from its first 6% of steps)."""
+    from dixon_adic_lifting_amd import workloads as W
+    from oracle import cbareiss
+    n, c = A.shape[0], b.shape[1]
+    threads = cbareiss.default_threads()
+    # steps that fit the budget: try a short prefix, then extend
+    K = min(n, 32)
+    est, dt, coef, steps_within = _oracle_projection(A, b, threads, K)
     spent = dt
-    a_, b_ = fit(ts, 4)
-    # choose K so that the sampled steps take about the remaining budget
     if K < n:
-        acc, K2 = 0.0, 0
-        while K2 < n and acc < max(budget_s - spent, 1.0):
-            e, w = model(K2)
-            acc += a_ * e + b_ * w
-            K2 += 1
-        K2 = max(K2, K + 16)
-        K = min(n, K2)
-        dt, ts = run(K)
+        K = min(n, max(K + 16, steps_within(max(budget_s - spent, 1.0))))
+        est, dt, coef, _ = _oracle_projection(A, b, threads, K)
         spent += dt
-        a_, b_ = fit(ts, 4)
-    full = sum(a_ * model(k)[0] + b_ * model(k)[1] for k in range(n))
-    return {"value": round(full * 1e3, 1), "unit": "ms per full solve (projected from the sample)",
-            "cores": threads, "kind": "oracle",
+    # validation on the n = 256 workload: projection from its first 16 of 256 steps
+    A3, b3 = W.generate("c3_n256_int24")
+    est3, dt3, _, _ = _oracle_projection(A3, b3, threads, 16)
+    t0 = time.perf_counter()
+    cbareiss.run(A3, b3, threads=threads)
+    full3 = time.perf_counter() - t0
+    spent += dt3 + full3
+    return {"value": round(est * 1e3, 1), "unit": "ms per full solve (projected from the sample)",
+            "cores": threads, "cpu_model": cpu_model(), "kind": "oracle",
             "sample": (f"plain-C Bareiss oracle (oracle/bareiss.c) on this {n}x{n}, c={c} system, {threads} "
                        f"threads: first {K} of {n} elimination steps in {dt:.2f} s; per-step times fitted "
-                       f"with t_k = a e_k + b e_k L_k^2 and summed over all n steps (back substitution "
-                       f"not included)"),
+                       f"with t_k = e_k (a + c L_k + d L_k^2) and summed over all n steps, plus a back "
+                       f"substitution term"),
             "sample_steps": K, "sample_seconds": round(dt, 3), "cpu_seconds_spent": round(spent, 2),
-            "fit": {"a_s_per_entry": a_, "b_s_per_entry_limb2": b_}}
+            "fit": {"a_s_per_entry": coef[0], "c_s_per_entry_limb": coef[1], "d_s_per_entry_limb2": coef[2]},
+            "validation_n256": {"projected_s": round(est3, 3), "measured_full_s": round(full3, 3),
+                                "relative_error": round((est3 - full3) / full3, 4),
+                                "sample": "first 16 of 256 steps of the c3_n256_int24 system"}}
 
 
 def copy_calibration(mb):
@@ -338,24 +432,59 @@ def copy_calibration(mb):
     return {"copy_bytes_each_way": mb << 20, "copies": 3}
 
 
+def analyse(S, name, traffic=None):
+    """Profiled pass on the canonical draw: per-kernel rooflines, the output
+    checks, and the dominant kernel (largest total event time, any class)."""
+    import numpy as np
+    from dixon_adic_lifting_amd import workloads as W
+    A, b = W.generate(name)
+    prof, info, stages_prof, pairs = profiled_pass(S)
+    info = dict(info, entry_bits=int(np.abs(A).max()).bit_length(),
+                gcd_bits=max(q.bit_length() for row in pairs for (_, q) in row))
+    rf = rooflines(prof, info, S.n, S.c, traffic)
+    timed = {k: v for k, v in rf.items() if "bound" in v}
+    dominant = max(timed, key=lambda k: prof[k][0]) if timed else None
+    return {"prof": prof, "info": info, "stages_prof": stages_prof, "pairs": pairs, "rf": rf,
+            "dominant": dominant, "A": A, "b": b}
+
+
+def multi_column_block(name, warmup, steps):
+    """A short run of the multi-column workload for the same JSON line: ms per
+    solve over distinct inputs, stage split, per-kernel rooflines (the lift's
+    int8 MFMA rate among them) and the mod-prime output check."""
+    S = Solver(workload_inputs(name, warmup + steps))
+    total, per, stages = time_solves(S, steps, warmup)
+    an = analyse(S, name, counter_traffic(name))
+    ok = verify_mod_primes(an["A"], an["b"], an["pairs"])
+    progress(f"{name}: {1e3 * total / steps:.1f} ms per solve, A x = b mod primes {ok}")
+    rf = an["rf"]
+    out = {"workload": name, "ms_per_solve": round(1e3 * total / steps, 2), "steps": steps, "warmup": warmup,
+           "ms_each": [round(1e3 * t, 2) for t in per], "solves_per_s": round(steps / total, 3),
+           "m": an["info"]["m"], "live_primes": an["info"]["live_primes"],
+           "stages_ms": {k: round(v, 2) for k, v in stages.items()},
+           "output_check_Ax_eq_b_mod_primes": ok, "dominant_kernel": an["dominant"], "kernels": rf}
+    if "lift_contract" in rf:
+        out["lift_int8_mfma_frac_of_peak"] = rf["lift_contract"].get("int8_frac_of_peak")
+    del S
+    return out
+
+
 def sweep(args):
     from dixon_adic_lifting_amd import workloads as W
-    from dixon_adic_lifting_amd import _lib
     rows = []
     for name in list(W.WORKLOADS):
-        A, b = W.generate(name)
-        S = Solver(A, b)
+        A, _ = W.generate(name)
         steps = 3 if A.shape[0] >= 2048 else 5
+        S = Solver(workload_inputs(name, steps + 1))
         total, per, stages = time_solves(S, steps, 1)
-        prof, info, _, pairs = profiled_pass(S)
-        rf = rooflines(prof, dict(info, entry_bits=int(abs(A).max()).bit_length()), S.n, S.c)
+        an = analyse(S, name)
         rows.append({"workload": name, "ms_median": round(1e3 * sorted(per)[len(per) // 2], 2),
                      "ms_min": round(1e3 * min(per), 2), "stages_ms": {k: round(v, 2) for k, v in stages.items()},
-                     "m": info["m"], "live": info["live_primes"], "roofline": rf})
+                     "m": an["info"]["m"], "live": an["info"]["live_primes"], "dominant": an["dominant"],
+                     "roofline": an["rf"]})
         print(json.dumps(rows[-1]), flush=True)
     for (n, c) in W.CARD_SHAPES:
-        A, b = W.uniform_system(n, c, 24, 1000 + n + c)
-        S = Solver(A, b)
+        S = Solver([W.uniform_system(n, c, 24, 1000 + n + c + 100000 * k) for k in range(6)])
         total, per, stages = time_solves(S, 5, 1)
         print(json.dumps({"workload": f"card_n{n}_c{c}_int24", "ms_median": round(1e3 * sorted(per)[len(per) // 2], 2),
                           "ms_min": round(1e3 * min(per), 2), "stages_ms": {k: round(v, 2) for k, v in stages.items()}}),
@@ -374,14 +503,12 @@ def main():
         sweep(args)
         return
     from dixon_adic_lifting_amd import workloads as W
-    A, b = W.generate(args.workload)
-    S = Solver(A, b)
+    S = Solver(workload_inputs(args.workload, args.warmup + args.steps))
     total, per, stages = time_solves(S, args.steps, args.warmup)
     ms_per = total / args.steps * 1e3
-    prof, info, stages_prof, pairs = profiled_pass(S)
-    progress(f"profiled pass done: stages {stages_prof}")
-    info = dict(info, entry_bits=int(abs(A).max()).bit_length())
-    rf = rooflines(prof, info, S.n, S.c, counter_traffic(args.workload))
+    an = analyse(S, args.workload, counter_traffic(args.workload))
+    progress(f"profiled pass done: stages {an['stages_prof']}")
+    A, b, pairs, info, rf, dominant = an["A"], an["b"], an["pairs"], an["info"], an["rf"], an["dominant"]
     # parity of the benched output: the oracle's stored digest
     gold = None
     gpath = os.path.join(ROOT, "tests", "golden", "oracle_digests.json")
@@ -394,8 +521,10 @@ def main():
     max_bits = max(max(abs(p).bit_length(), q.bit_length()) for row in pairs for (p, q) in row)
     if args.copy_calib_mb:
         copy_calibration(args.copy_calib_mb)
-    dominant = max((k for k in ("gj_step", "gj_update", "lift_contract", "recon_gemm") if k in rf),
-                   key=lambda k: prof[k][0])
+    del S
+    multi = None
+    if args.multi_column and args.workload != MULTI_COLUMN:
+        multi = multi_column_block(MULTI_COLUMN, 1, 2)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(A, b, args.cpu_budget_s)
@@ -416,17 +545,19 @@ def main():
         "scaling": "weak",
         "vs_baseline": round(ms_per / PAGES_MS_C4["h200"], 5) if wl.name == "c4_n1024_int24" else None,
         "dtype": "int8/int32/int64 (exact)",
-        "data": "synthetic (seeded, i.i.d. uniform 24-bit entries)",
+        "data": "synthetic (seeded, i.i.d. uniform 24-bit entries; every solve a distinct draw)",
         "config": {"workload": wl.name, "n": wl.n, "c": wl.c, "entries": "uniform [-2^23, 2^23)",
-                   "seed": wl.seed, "m": info["m"], "live_primes": info["live_primes"]},
+                   "seed": wl.seed, "distinct_inputs": min(args.warmup + args.steps, MAX_DISTINCT_INPUTS),
+                   "m": info["m"], "live_primes": info["live_primes"]},
         "parity_vs_oracle_digest": parity,
         "output_check_Ax_eq_b_mod_primes": identity_ok,
         "output_max_bits": max_bits,
         "stages_ms": {k: round(v, 3) for k, v in stages.items()},
-        "stages_ms_profiled": {k: round(v, 3) for k, v in stages_prof.items()},
+        "stages_ms_profiled": {k: round(v, 3) for k, v in an["stages_prof"].items()},
         "roofline": {**{k: rf[dominant][k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")},
-                     "kernel": dominant},
+                     "kernel": dominant} if dominant else None,
         "kernels": rf,
+        "multi_column": multi,
         "pages_context_ms": PAGES_MS_C4,
         "cpu_baseline": cpu,
     }

@@ -264,6 +264,7 @@ thread_local PinnedBuffer g_pinned;
 int run_lift(const int64_t* dA, const int64_t* db, uint8_t* ws, hipStream_t st, const Prep& pr,
              const LiveSet& ls, int m, int64_t* digits_host, Profiler* prof, uint64_t* dig_dev = nullptr) {
     Layout L = pr.L;
+    L.krec = lift_record_steps(L);
     if (m <= L.kchunk || dig_dev) L.kchunk = m;  // one chunk: the device digits are laid out exactly as the host's
     L.dig_dev = dig_dev;
     LiftParams prm;
@@ -347,7 +348,11 @@ int es_primes(int32_t* q, int32_t cap) {
 
 size_t es_workspace_bytes(int32_t n, int32_t c) {
     if (!valid_shape(n, c)) return 0;
-    return make_layout(n, c).total;
+    try {
+        return make_layout(n, c).total + gpu_recon_reserve(n, c);
+    } catch (...) {
+        return 0;
+    }
 }
 
 int es_set_lift_record_steps(int32_t steps) {
@@ -399,7 +404,7 @@ int es_solve_device(const int64_t* dA, const int64_t* db, int32_t n, int32_t c, 
     if (!out || !dA || !db || !d_ws || !valid_shape(n, c)) return ES_EINVAL;
     Prep pr;
     pr.L = make_layout(n, c);
-    if (ws_bytes < pr.L.total) return ES_EINVAL;
+    if (ws_bytes < es_workspace_bytes(n, c)) return ES_EINVAL;
     for (double& t : g_timings) t = 0;
     hipStream_t st = (hipStream_t)stream;
     uint8_t* ws = (uint8_t*)d_ws;
@@ -418,18 +423,29 @@ int es_solve_device(const int64_t* dA, const int64_t* db, int32_t n, int32_t c, 
         if (ls.E == 0) return no_prime_decision(dA, n, pr, st);
         size_t mbits = 0;
         const int m = choose_m_bits(ls.P, pr.nbits, pr.dbits, &mbits);
-        // M = P^m is needed only by the reconstruction: formed on a host
-        // thread while the GPU lifts
-        std::future<BigInt> fM = std::async(std::launch::async, [&ls, m] { return pow_u(ls.P, (unsigned)m); });
+        // P^0 .. P^m (M = P^m) are needed only by the reconstruction: formed
+        // on a host thread while the GPU lifts
+        std::future<std::vector<BigInt>> fpw = std::async(std::launch::async, [&ls, m] {
+            std::vector<BigInt> pw((size_t)m + 1);
+            pw[0] = BigInt::from_u64(1);
+            for (int i = 1; i <= m; i++) pw[i] = mul(pw[i - 1], ls.P);
+            return pw;
+        });
+        std::vector<BigInt> pw;
         auto take_M = [&](BigInt* M) {
-            *M = fM.get();
+            pw = fpw.get();
+            *M = pw[(size_t)m];
             return M->bit_length() == mbits;
         };
+        // the reconstruction's scratch follows the lift's part of the
+        // workspace; an input whose plan outgrows the reserve (more than
+        // kReserveDrops primes dividing det A near the range limit) takes
+        // the host reconstruction
         GpuReconPlan plan;
         uint8_t* scr = nullptr;
         if (!gpu_recon_disabled()) {
             plan = plan_gpu_recon(n, c, m, mbits, pr.nbits);
-            if (plan.ok) scr = gpu_recon_scratch(plan);
+            if (plan.ok && plan.total <= ws_bytes - pr.L.total) scr = ws + pr.L.total;
         }
         BigInt M;
         es_solution* sol = nullptr;
@@ -443,7 +459,7 @@ int es_solve_device(const int64_t* dA, const int64_t* db, int32_t n, int32_t c, 
             if (!take_M(&M)) return ES_EINTERNAL;
             sol = new es_solution;
             GpuReconTimes rt;
-            rc = reconstruct_gpu(plan, scr, ls.P, M, pr.nbits, pr.dbits, default_threads(), st, &sol->data, &rt,
+            rc = reconstruct_gpu(plan, scr, ls.P, pw, pr.nbits, pr.dbits, default_threads(), st, &sol->data, &rt,
                                  &prof);
             g_timings[3] = rt.gpu_ms;
             g_timings[4] = ms_since(t0);

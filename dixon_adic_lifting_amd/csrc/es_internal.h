@@ -147,9 +147,13 @@ inline bool fused_lift_shape(int n, int c, int pitch) {
     return c == 1 && pitch >= 1024 && (size_t)kNumPrimes * n * pitch <= (size_t)0x7fffffff;
 }
 
+// The layout depends on (n, c) only.
 Layout make_layout(int n, int c);
-// cap on Layout::krec for later layouts on the calling thread (0: none)
+// cap on the record steps that later lifts on the calling thread use per
+// launch (0: none); the layout keeps room for its default count either way
 void set_lift_record_cap(int steps);
+// record steps per launch for a lift with layout L on the calling thread
+int lift_record_steps(const Layout& L);
 
 // ---------------------------------------------------------------- launchers
 // Each enqueues on `st` and returns the launch status.

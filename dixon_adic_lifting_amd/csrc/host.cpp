@@ -42,6 +42,8 @@ static thread_local int g_krec_cap = 0;  // 0: the default record chunk
 
 void set_lift_record_cap(int steps) { g_krec_cap = steps; }
 
+int lift_record_steps(const Layout& L) { return g_krec_cap > 0 ? std::min(L.krec, g_krec_cap) : L.krec; }
+
 Layout make_layout(int n, int c) {
     Layout L{};
     L.n = n;
@@ -87,8 +89,7 @@ Layout make_layout(int n, int c) {
     L.off_xp = take(c > 1 ? 8 * (size_t)c * L.pitch : 0);
     const bool fused = fused_lift_shape(n, c, L.pitch);
     L.off_Sperm = take(fused ? E * n * (size_t)L.pitch : 0);
-    size_t kr = std::min<size_t>(((size_t)16 << 20) / ((size_t)n * 64), (size_t)L.kchunk);
-    if (g_krec_cap > 0) kr = std::min<size_t>(kr, (size_t)g_krec_cap);
+    const size_t kr = std::min<size_t>(((size_t)16 << 20) / ((size_t)n * 64), (size_t)L.kchunk);
     L.krec = (int)std::max<size_t>(1, kr);
     L.off_urec = take(fused ? (size_t)L.krec * n * 64 : 0);
     L.off_digits = take(NC * (size_t)L.kchunk * kDigitLimbs * sizeof(uint64_t));

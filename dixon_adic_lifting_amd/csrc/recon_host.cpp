@@ -32,26 +32,6 @@ namespace {
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Device scratch of the reconstruction path, kept per host thread and grown
-// on demand (never shrunk; the process's exit releases it).
-struct DeviceScratch {
-    void* p = nullptr;
-    size_t bytes = 0;
-    void* get(size_t need) {
-        if (need <= bytes) return p;
-        if (p) (void)hipFree(p);
-        p = nullptr;
-        bytes = 0;
-        if (hipMalloc(&p, need) != hipSuccess) {
-            p = nullptr;
-            return nullptr;
-        }
-        bytes = need;
-        return p;
-    }
-};
-thread_local DeviceScratch g_dev_scratch;
-
 // Pinned host staging for the device-to-host copies, per thread.
 struct PinnedStage {
     void* p = nullptr;
@@ -182,31 +162,45 @@ GpuReconPlan plan_gpu_recon(int n, int c, int m, size_t mbits, int nbits) {
     return pl;
 }
 
-uint8_t* gpu_recon_scratch(const GpuReconPlan& pl) { return (uint8_t*)g_dev_scratch.get(pl.total); }
+size_t gpu_recon_reserve(int n, int c) {
+    // The largest bounds within the range limit n max|A| < 2^63: every entry
+    // of A at 2^63 / n and every entry of b at 2^63 in magnitude.
+    const double amax = std::ldexp(1.0, 63) / n;
+    std::vector<double> an((size_t)n, (double)n * amax * amax), bn((size_t)c, (double)n * std::ldexp(1.0, 126));
+    int nb = 0, db = 0;
+    hadamard_bits(an.data(), an.data(), bn.data(), n, c, &nb, &db);
+    // The smallest P with at most kReserveDrops primes dropped: the product
+    // of the others, the largest ones dropped.
+    BigInt P = BigInt::from_u64(1);
+    for (int j = 0; j < kNumPrimes - kReserveDrops; j++) P = mul_small(P, kPrimeTable.q[j]);
+    const double l2p = std::log2((double)shr_abs(P, P.bit_length() - 64).d[0]) + (double)(P.bit_length() - 64);
+    const size_t need = (size_t)nb + db + 2;
+    // The least m with P^m of bit length >= need has P^(m - 1) < 2^need, so
+    // M = P^m < 2^need P: at most need + 334 bits whatever the live primes.
+    size_t mb = need + 335;
+    // the widest M the GPU path takes (its weight and numerator rows fit one wave)
+    size_t mb_cap = 0;
+    for (size_t w = 3; wchain_words_per_lane((int)w) != 0 && numer_words_per_lane((int)w) != 0; w++)
+        mb_cap = 32 * w - 1;
+    mb = std::min(mb, mb_cap);
+    // steps for any P at least as large, at the capped width
+    int m = (int)std::min<double>(std::ceil((double)need / l2p) + 1.0, std::floor((double)mb / l2p) + 2.0);
+    m = std::min(m, 65536 / 48);
+    nb = (int)std::min<size_t>((size_t)nb, mb);
+    const GpuReconPlan pl = plan_gpu_recon(n, c, m, mb, nb);
+    return pl.ok ? pl.total : 0;
+}
 
 #define HIPOK(expr)                                   \
     do {                                              \
         if ((expr) != hipSuccess) return ES_EHIP;     \
     } while (0)
 
-// P^0 .. P^m, kept for the last (P, m) asked for: repeated solves of one
-// size use the same powers.
-static std::shared_ptr<const std::vector<BigInt>> powers_of(const BigInt& P, int m) {
-    static std::mutex mu;
-    static std::shared_ptr<const std::vector<BigInt>> cached;
-    static BigInt cachedP;
-    std::lock_guard<std::mutex> lk(mu);
-    if (cached && (int)cached->size() == m + 1 && cmp(cachedP, P) == 0) return cached;
-    auto v = std::make_shared<std::vector<BigInt>>(m + 1);
-    (*v)[0] = BigInt::from_u64(1);
-    for (int i = 1; i <= m; i++) (*v)[i] = mul((*v)[i - 1], P);
-    cached = v;
-    cachedP = P;
-    return cached;
-}
-
-int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const BigInt& M, int nbits, int dbits,
-                    int nthreads, hipStream_t st, SolutionData* out, GpuReconTimes* tm, KernelTimer* kt) {
+int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const std::vector<BigInt>& pw,
+                    int nbits, int dbits, int nthreads, hipStream_t st, SolutionData* out, GpuReconTimes* tm,
+                    KernelTimer* kt) {
+    if ((int)pw.size() != pl.m + 1) return ES_EINTERNAL;
+    const BigInt& M = pw[pl.m];
     typedef std::chrono::steady_clock clk;
     auto t0 = clk::now();
     auto lap = [&](double* slot, const char* what) {
@@ -320,11 +314,10 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
         // the chain T_{i+1} = T_i P mod M, cut into segments that each start
         // from P^{i0} d mod M = (d mod P^{m - i0}) P^{i0} (M = P^m: the
         // product is below M, no division by M) and run in parallel
-        const auto pw = powers_of(P, m);
         const int nseg = std::max(1, std::min(nthreads, m / 8));
         parallel_for_each((size_t)nseg, nthreads, [&](size_t sg) {
             const int i0 = (int)(sg * (size_t)m / nseg), i1 = (int)((sg + 1) * (size_t)m / nseg);
-            BigInt Ti = i0 == 0 ? mod_floor(d, M) : mul(mod_floor(d, (*pw)[m - i0]), (*pw)[i0]);
+            BigInt Ti = i0 == 0 ? mod_floor(d, M) : mul(mod_floor(d, pw[m - i0]), pw[i0]);
             for (int i = i0; i < i1; i++) {
                 to_words(Ti, &T[(size_t)i * NW], NW);
                 if (i + 1 < i1) Ti = mod_floor(mul(Ti, P), M);

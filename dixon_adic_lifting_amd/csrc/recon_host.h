@@ -5,13 +5,14 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <vector>
 
 #include "bignum.h"
 #include "host.h"
 
 namespace es {
 
-// Sizes and device-scratch layout for one solve.  ok is false when the GPU
+// Sizes and scratch layout for one solve.  ok is false when the GPU
 // path does not apply (too few words in M, rows wider than one wave can
 // hold, more than 1365 lift steps, or more than 16 GiB of scratch); the
 // host path then reconstructs from digits copied to the host.
@@ -63,12 +64,21 @@ void set_gpu_recon(bool on);
 
 GpuReconPlan plan_gpu_recon(int n, int c, int m, size_t mbits, int nbits);  // mbits: bit length of M = P^m
 
-// Per-thread device scratch of at least pl.total bytes (NULL on failure).
-uint8_t* gpu_recon_scratch(const GpuReconPlan& pl);
+// Scratch bytes that the workspace of an n x n system with c right-hand
+// sides reserves for the GPU reconstruction (0 when the path never applies
+// to that shape): the largest plan over every input within the range limit
+// n max|A| < 2^63 for which at most kReserveDrops primes divide det A,
+// capped at the widest modulus the GPU path takes.  The plan's sizes grow
+// with m, the bit length of M and the numerator bound, so every such input's
+// plan fits; any other input takes the host reconstruction (same result).
+constexpr int kReserveDrops = 5;
+size_t gpu_recon_reserve(int n, int c);
 
-// Reconstruction from the digits at scr + pl.off_digits.  Returns ES_OK,
-// ES_EHIP, ES_ENOMEM or ES_EINTERNAL.
-int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const BigInt& M, int nbits, int dbits,
-                    int nthreads, hipStream_t st, SolutionData* out, GpuReconTimes* tm, KernelTimer* kt);
+// Reconstruction from the digits at scr + pl.off_digits (scr: pl.total bytes
+// of device memory, part of the caller's workspace).  pw holds P^0 .. P^m,
+// so M = pw[m].  Returns ES_OK, ES_EHIP, ES_ENOMEM or ES_EINTERNAL.
+int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const std::vector<BigInt>& pw,
+                    int nbits, int dbits, int nthreads, hipStream_t st, SolutionData* out, GpuReconTimes* tm,
+                    KernelTimer* kt);
 
 }  // namespace es

@@ -63,8 +63,13 @@ const char *es_strerror(int status);
 int es_primes(int32_t *q, int32_t cap);
 
 /* Bytes of device workspace es_solve_device needs for an n x n system with c
- * right-hand sides (worst case over all inputs within the range limit);
- * 0 if n or c is out of range. */
+ * right-hand sides; 0 if n or c is out of range.  Depends on (n, c) only,
+ * the same on every thread.  It holds the lift's buffers and the scratch of
+ * the GPU reconstruction, sized for the largest case over every input within
+ * the range limit for which at most five primes divide det A (at n = 1024,
+ * c = 1 about 0.9 GB; at n = 2048, c = 16 about 2.6 GB).  An input outside
+ * that case is still solved, with the reconstruction on the host.  The
+ * library allocates no device memory of its own in es_solve_device. */
 size_t es_workspace_bytes(int32_t n, int32_t c);
 
 /*
@@ -134,11 +139,11 @@ int es_set_blocked_inverse(int on);
  * the GPU too (the sample stays on the host, and so does any gcd whose
  * Euclidean quotients the GPU rounds cannot handle); the host path is taken anyway when the GPU path does not
  * apply (a modulus P^m of fewer than 65 bits, wider than 131072 bits, more
- * than 1365 lift steps, or more than 16 GiB of scratch).  on = 0: every
- * digit goes to the host and the host reconstructs.  Both give the same
- * result.  The GPU path keeps a per-thread device scratch buffer, sized to
- * the largest solve so far, until the process ends.  Without a call, the
- * environment variable ES_RECON=host selects the host path.
+ * than 1365 lift steps, more than 16 GiB of scratch, or more scratch than
+ * the workspace reserves).  on = 0: every digit goes to the host and the
+ * host reconstructs.  Both give the same result.  The GPU path's scratch is
+ * part of the caller's workspace.  Without a call, the environment variable
+ * ES_RECON=host selects the host path.
  */
 int es_set_gpu_reconstruction(int on);
 
@@ -148,9 +153,8 @@ int es_set_gpu_reconstruction(int on);
  * the CRT quotient k in a 64-byte record on the device, and one launch turns
  * up to `steps` steps' records into their digits.  steps = 0 restores the
  * default (16 MiB of records); a larger value than the default is taken as
- * the default.  Results are unchanged: smaller values only add launches and
- * shrink the workspace (so es_workspace_bytes, called on the same thread
- * afterwards, may return less).  Returns ES_EINVAL for steps < 0.
+ * the default.  Results are unchanged: smaller values only add launches (the
+ * workspace size does not depend on it).  Returns ES_EINVAL for steps < 0.
  */
 int es_set_lift_record_steps(int32_t steps);
 

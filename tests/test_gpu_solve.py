@@ -20,6 +20,8 @@ import dixon_adic_lifting_amd as es
 from dixon_adic_lifting_amd import _lib, workloads as W
 from oracle import cbareiss, exact, modular
 
+from exact_check import exact_limb_check
+
 pytestmark = pytest.mark.gpu
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "oracle_digests.json")
@@ -97,27 +99,37 @@ def check_mod_primes(A, b, X, rows, primes=MOD_PRIMES):
 
 
 def test_solve_c5():
+    """n = 2048, c = 16: complete exact check (every row and column) and
+    lowest terms; the solve allocates no device memory beyond the inputs and
+    the workspace it is handed."""
     A, b = W.generate("c5_n2048_c16_int24")
-    X = solve_gpu(A, b)
+    dA, db = torch.as_tensor(A).cuda(), torch.as_tensor(b).cuda()
+    ws = torch.empty(es.workspace_bytes(2048, 16), dtype=torch.uint8, device="cuda")
+    solve_gpu(A[:64, :64].copy(), b[:64].copy())        # the library's code objects are loaded
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    alloc0 = torch.cuda.memory_allocated()
+    X = es.solve_pairs(dA, db, workspace=ws)
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    assert torch.cuda.memory_allocated() == alloc0
+    assert free0 - free1 < (2 << 20), (free0, free1)
     assert len(X) == 2048 and len(X[0]) == 16
     assert_normal_form(X)
-    check_mod_primes(A, b, X, rows=[0, 1, 1023, 2047])
+    assert exact_limb_check(A, b, X)
 
 
 @pytest.mark.parametrize("n,c", [(128, 1), (512, 1), (256, 16), (512, 16)])
 def test_card_table_shapes(n, c):
     """The card's other measured shapes (24-bit entries), drawn as the bench
-    sweep draws them.  Up to 8192 unknowns A x = b is checked exactly (the
-    solution is unique, so this fixes every bit); above, modulo five primes
-    plus exact rows."""
+    sweep draws them, checked completely: lowest terms and A x = b exactly
+    on every row and column (the solution is unique, so this fixes every
+    bit)."""
     A, b = W.uniform_system(n, c, 24, 1000 + n + c)
     X = solve_gpu(A, b)
     assert len(X) == n and len(X[0]) == c
     assert_normal_form(X)
-    if n * c <= 4096:
-        assert exact.check_solution(A, b, X)
-    else:
-        check_mod_primes(A, b, X, rows=[0, n // 2, n - 1])
+    assert exact_limb_check(A, b, X)
 
 
 # ------------------------------------------------------------------ edge families

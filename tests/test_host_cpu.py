@@ -55,6 +55,30 @@ def test_workspace_bytes_limits():
     assert es.workspace_bytes(1024, 1) < es.workspace_bytes(2048, 16)
 
 
+def test_workspace_bytes_same_on_every_thread():
+    """The size query depends on (n, c) only: the same on other threads,
+    also after one of them caps the lift's record steps."""
+    import threading
+    shapes = [(1, 1), (32, 1), (300, 2), (1024, 1), (2048, 16)]
+    ref = [es.workspace_bytes(n, c) for n, c in shapes]
+    got = {}
+
+    def worker(k, cap):
+        lib = _lib.load()
+        if cap:
+            assert lib.es_set_lift_record_steps(cap) == 0
+        got[k] = [es.workspace_bytes(n, c) for n, c in shapes]
+        if cap:
+            lib.es_set_lift_record_steps(0)
+
+    threads = [threading.Thread(target=worker, args=(k, cap)) for k, cap in enumerate([0, 3, 1, 0])]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert all(v == ref for v in got.values()) and len(got) == 4
+
+
 def test_primes_and_strerror():
     assert es.primes() == modular.odd_primes_below(256)
     for st in (0, 1, -1, -2, -3, -4, -5, -6):
