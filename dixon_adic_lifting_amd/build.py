@@ -19,6 +19,11 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 DEVICE_SOURCES = ["kernels.hip", "recon.hip"]
+# per-source device flags: the gcd kernel's limb arrays (up to 64 registers,
+# indexed by wave-uniform slot numbers) stay in registers only with a higher
+# promotion limit than the default, which sends them to scratch at 1024
+# threads per block
+SOURCE_FLAGS = {"recon.hip": ["-mllvm", "-amdgpu-promote-alloca-to-vector-limit=1024"]}
 HOST_SOURCES = ["api.cpp", "host.cpp", "bignum.cpp", "debug.cpp", "recon_host.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{CSRC}",
           f"-I{os.path.join(os.path.dirname(HERE), 'include')}"]
@@ -41,7 +46,7 @@ def build(verbose: bool = False) -> str:
     objs = []
     for src in DEVICE_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
-        _run([HIPCC, *COMMON, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        _run([HIPCC, *COMMON, *DEVICE_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     for src in HOST_SOURCES:
         obj = os.path.join(BUILD, src + ".o")

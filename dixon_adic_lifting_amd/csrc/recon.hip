@@ -23,6 +23,9 @@
 // stream 16 bytes of the contraction index per lane.
 #include <hip/hip_runtime.h>
 
+#include <cstdio>
+#include <cstdlib>
+
 #include "es_internal.h"
 
 namespace es {
@@ -303,31 +306,42 @@ __device__ __forceinline__ int32_t chunk30(const uint32_t* __restrict__ W, int n
 // (a, b) <- (A a + B b, C a + D b) over slots [0, ns); the high parts
 // leaving slot ns - 1 are dropped (the limbs above the live ones are zero,
 // and the top live limb lies below the last lane of slot ns - 1)
+constexpr int kSlotGroup = 4;  // slots a limb pass takes at a time (straight-line code)
+
+// (a, b) <- (A a + B b, C a + D b) over slots [0, ns) rounded up to whole
+// groups of kSlotGroup slots (ns wave-uniform); the slots above the live
+// ones hold zeros and stay zero, and the high parts leaving the last slot
+// taken are dropped (the limbs above the live ones are zero, and the top
+// live limb lies below the last lane of slot ns - 1)
 template <int CW>
 __device__ __forceinline__ void limb_apply(int32_t (&a)[CW], int32_t (&b)[CW], int32_t A, int32_t B, int32_t C,
                                            int32_t D, int ns, bool lane0) {
     int32_t pa = 0, pb = 0;  // high parts of the slot below, rotated one lane up
 #pragma unroll
-    for (int c = 0; c < CW; c++) {
-        if (c >= ns) continue;
-        // w = v + 2^29: high part floor(w / 2^30), low part (w mod 2^30) - 2^29
-        const int64_t wa = (int64_t)A * a[c] + ((int64_t)B * b[c] + (1 << 29));
-        const int64_t wb = (int64_t)C * a[c] + ((int64_t)D * b[c] + (1 << 29));
-        const uint32_t wal = (uint32_t)wa, wah = (uint32_t)((uint64_t)wa >> 32);
-        const uint32_t wbl = (uint32_t)wb, wbh = (uint32_t)((uint64_t)wb >> 32);
-        const int32_t ra = wave_ror1((int32_t)__builtin_amdgcn_alignbit(wah, wal, 30));
-        const int32_t rb = wave_ror1((int32_t)__builtin_amdgcn_alignbit(wbh, wbl, 30));
-        a[c] = (int32_t)(wal & 0x3fffffffu) - (1 << 29) + (lane0 ? pa : ra);
-        b[c] = (int32_t)(wbl & 0x3fffffffu) - (1 << 29) + (lane0 ? pb : rb);
-        pa = ra;
-        pb = rb;
+    for (int c0 = 0; c0 < CW; c0 += kSlotGroup) {
+        if (c0 >= ns) break;
+#pragma unroll
+        for (int c = c0; c < c0 + kSlotGroup && c < CW; c++) {
+            // w = v + 2^29: high part floor(w / 2^30), low part (w mod 2^30) - 2^29
+            const int64_t wa = (int64_t)A * a[c] + ((int64_t)B * b[c] + (1 << 29));
+            const int64_t wb = (int64_t)C * a[c] + ((int64_t)D * b[c] + (1 << 29));
+            const uint32_t wal = (uint32_t)wa, wah = (uint32_t)((uint64_t)wa >> 32);
+            const uint32_t wbl = (uint32_t)wb, wbh = (uint32_t)((uint64_t)wb >> 32);
+            const int32_t ra = wave_ror1((int32_t)__builtin_amdgcn_alignbit(wah, wal, 30));
+            const int32_t rb = wave_ror1((int32_t)__builtin_amdgcn_alignbit(wbh, wbl, 30));
+            a[c] = (int32_t)(wal & 0x3fffffffu) - (1 << 29) + (lane0 ? pa : ra);
+            b[c] = (int32_t)(wbl & 0x3fffffffu) - (1 << 29) + (lane0 ? pb : rb);
+            pa = ra;
+            pb = rb;
+        }
     }
 }
 
-// highest limb index below 64 ns at which a or b is nonzero (-1 when both are zero)
+// highest limb index at or below slot s_hi at which a or b is nonzero (-1
+// when both are zero there)
 template <int CW>
-__device__ __forceinline__ int top_limb(const int32_t (&a)[CW], const int32_t (&b)[CW], int ns) {
-    for (int s = ns - 1; s >= 0; s--) {
+__device__ __forceinline__ int top_limb(const int32_t (&a)[CW], const int32_t (&b)[CW], int s_hi) {
+    for (int s = s_hi; s >= 0; s--) {
         const uint64_t m = __ballot((a[s] | b[s]) != 0);
         if (m != 0) return 64 * s + 63 - __builtin_clzll(m);
     }
@@ -370,211 +384,272 @@ __device__ __forceinline__ double row_max(double C1, double D1, double C2, doubl
     return fmax(fmax(fabs(C1), fabs(D1)), fmax(fabs(C2), fabs(D2)));
 }
 
-template <int CW>
-__global__ __launch_bounds__(128) void gcd_kernel(const uint32_t* __restrict__ Y, int nw,
-                                                  const int* __restrict__ status, int valid_rows,
-                                                  const uint32_t* __restrict__ Dw, int nwd,
-                                                  uint64_t* __restrict__ G, int* __restrict__ gstat) {
-    const int j = blockIdx.x;
-    if (j >= valid_rows) return;
-    if (status[j] >= 2) {
-        if (threadIdx.x == 0) gstat[j] = 1;
+// Waves of a gcd block.  Waves are dealt round-robin to the four SIMDs, so
+// waves 0, 4, 8 and 12 share a SIMD: they run the Euclidean steps (wave 0,
+// and wave 4 when the block has more than eight components) or stay idle,
+// so that the latency-bound Euclid chains never wait behind limb work; every
+// other wave holds one component's limbs.  Up to twelve components in a
+// 1024-thread block.
+constexpr int kGcdMaxGroup = 12;
+__host__ __device__ constexpr int gcd_limb_wave(int g) { return g + 1 + g / 3; }
+__host__ __device__ constexpr int gcd_block_waves(int G) { return gcd_limb_wave(G - 1) + 1; }
+static_assert(gcd_block_waves(kGcdMaxGroup) == 16, "gcd block layout");
+
+// A block serves G components.  Eight lanes of a Euclid wave serve one
+// component, lane e holding entry e of its window (limbs base + e of a and
+// b; entries 6 and 7 are zero when a window is read): the matrix applied
+// last updates the window lane-parallel, and the leading parts come from
+// three of its entries.  Per round the Euclid waves turn each window into
+// the component's next matrix while the limb waves apply the previous one;
+// one barrier per round for the whole block, and per Euclid wave a flag
+// raised once all its components are done, so that all waves leave the loop
+// at the same barrier.
+template <int CW, int GMAX>
+__global__ __launch_bounds__(64 * gcd_block_waves(GMAX)) void gcd_kernel(const uint32_t* __restrict__ Y, int nw,
+                                                                          const int* __restrict__ status,
+                                                                          int valid_rows,
+                                                                          const uint32_t* __restrict__ Dw, int nwd,
+                                                                          int G, uint64_t* __restrict__ Gout,
+                                                                          int* __restrict__ gstat) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const bool lane0 = lane == 0;
+    __shared__ int4 sM[2][GMAX];                 // round matrices [A B; C D]; all zero: that component is done
+    __shared__ int32_t sSeg[2][GMAX][2][8];      // limbs h - 4 .. h + 1 of a and b
+    __shared__ int sTop[2][GMAX];                // h
+    __shared__ int sDone[2][2];                  // per Euclid wave: all its components are done
+    const int max_rounds = (32 * (nw > nwd ? nw : nwd)) / 12 + 64;
+    const int j0 = blockIdx.x * G;
+    if (threadIdx.x == 0 && G <= 8) sDone[0][1] = sDone[1][1] = 1;  // no second Euclid wave
+
+    const bool euclid = wave == 0 || (wave == 4 && G > 8);
+    if ((wave & 3) == 0 && !euclid) {
+        // ---- idle wave: keeps the Euclid waves' SIMD free; joins the barriers
+        __syncthreads();
+        for (int r = 1;; r++) {
+            __syncthreads();
+            if (sDone[r & 1][0] & sDone[r & 1][1]) break;
+        }
         return;
     }
-    const int lane = threadIdx.x & 63;
-    const bool lane0 = lane == 0;
-    __shared__ int4 sM[2];                   // the round's matrix [A B; C D]; all zero: stop
-    __shared__ int32_t sSeg[2][2][8];        // limbs h - 4 .. h + 1 of a and b
-    __shared__ int sTop[2];                  // h
-    const int max_rounds = (32 * (nw > nwd ? nw : nwd)) / 12 + 64;
-
-    if (threadIdx.x >= 64) {
-        // ---- limb wave: a = d, b = y as 30-bit chunks of the two's-complement
-        // words (y's sign extended through every limb), then one split pass
-        // makes them signed limbs; the carry dropped off the top limb removes
-        // the extension
-        const uint32_t ext = status[j] == 1 ? 0xffffffffu : 0u;
-        const uint32_t* yj = Y + (size_t)j * nw;
+    if (!euclid) {
+        // ---- limb wave of component g: a = d, b = y as 30-bit chunks of
+        // the two's-complement words (y's sign extended through every
+        // limb), then one split pass makes them signed limbs; the carry
+        // dropped off the top limb removes the extension
+        const int g = wave - 1 - wave / 4;
+        const int j = j0 + g;
+        const bool valid = g < G && j < valid_rows && status[j] < 2;
+        const uint32_t ext = valid && status[j] == 1 ? 0xffffffffu : 0u;
+        const uint32_t* yj = Y + (size_t)(valid ? j : 0) * nw;
         int32_t a[CW], b[CW];
 #pragma unroll
         for (int c = 0; c < CW; c++) {
-            a[c] = chunk30(Dw, nwd, 0u, 64 * c + lane);
-            b[c] = chunk30(yj, nw, ext, 64 * c + lane);
+            a[c] = valid ? chunk30(Dw, nwd, 0u, 64 * c + lane) : 0;
+            b[c] = valid ? chunk30(yj, nw, ext, 64 * c + lane) : 0;
         }
         limb_apply<CW>(a, b, 1, 0, 0, 1, CW, lane0);
-        int ns = CW;
-        // the top h and the six limbs h - 4 .. h + 1 (zero below limb 0): the
-        // lane holding limb k0 + e writes entry e, from slot k >> 6, which is
-        // one of the two slots the window touches
+        int ns = CW, hprev = 64 * CW - 1;
+        // the top h (at most one limb above the last one: a matrix entry is
+        // below 2^26) and the six limbs h - 4 .. h + 1 (zero below limb 0):
+        // the lane holding limb k0 + e writes entry e, from slot k >> 6, which
+        // is one of the two slots the window touches
         auto hand_over = [&](int buf) {
-            const int h = top_limb<CW>(a, b, ns);
+            const int h = __builtin_amdgcn_readfirstlane(top_limb<CW>(a, b, min(CW - 1, (hprev + 1) >> 6)));
+            hprev = h;
             ns = h < 0 ? 1 : min(CW, (h + 1) / 64 + 1);
             const int k0 = h - 4;
             const int e = (lane - k0) & 63;
             const int k = k0 + e;
             const int slo = k0 < 0 ? 0 : k0 >> 6, shi = (h + 1) >> 6;
-            const int32_t alo = a[slo], ahi = a[shi], blo = b[slo], bhi = b[shi];
+            const int32_t alo = a[slo], ahi = a[min(shi, CW - 1)], blo = b[slo], bhi = b[min(shi, CW - 1)];
             if (e < kGcdSeg) {
                 const bool up = (k >> 6) != slo;
-                sSeg[buf][0][e] = k < 0 ? 0 : (up ? ahi : alo);
-                sSeg[buf][1][e] = k < 0 ? 0 : (up ? bhi : blo);
+                sSeg[buf][g][0][e] = k < 0 ? 0 : (up ? ahi : alo);
+                sSeg[buf][g][1][e] = k < 0 ? 0 : (up ? bhi : blo);
             }
-            if (lane0) sTop[buf] = h;
+            if (lane0) sTop[buf][g] = h;
         };
-        hand_over(0);
+        if (valid) hand_over(0);
         __syncthreads();
+        bool alive = valid;
         for (int r = 1;; r++) {
-            __syncthreads();  // matrix r is ready (and the window after matrix r - 1 was read)
-            const int4 m = sM[r & 1];
+            __syncthreads();  // matrices r are ready (and the windows after matrices r - 1 were read)
+            if (sDone[r & 1][0] & sDone[r & 1][1]) break;
+            if (!alive) continue;
+            const int4 m = sM[r & 1][g];
             const int32_t A = __builtin_amdgcn_readfirstlane(m.x), B = __builtin_amdgcn_readfirstlane(m.y);
             const int32_t C = __builtin_amdgcn_readfirstlane(m.z), D = __builtin_amdgcn_readfirstlane(m.w);
-            if ((A | B | C | D) == 0) break;
+            if ((A | B | C | D) == 0) {
+                alive = false;
+                continue;
+            }
             if (!(A == 1 && B == 0 && C == 0 && D == 1)) limb_apply<CW>(a, b, A, B, C, D, ns, lane0);
             hand_over(r & 1);
         }
         return;
     }
 
-    // ---- Euclid wave: its control flow is uniform; lanes 0 .. 6 carry the
-    // window (lane e: limb base + e of a and of b)
-    __syncthreads();
+    // ---- Euclid wave ew: lane 8 q + e serves component g = 8 ew + q,
+    // entry e of its window.  Every decision below is uniform over a
+    // component's eight lanes.
+    __builtin_amdgcn_s_setprio(3);
+    const int ew = wave >> 2, q = lane >> 3, e = lane & 7;
+    const int g = 8 * ew + q;
+    const int j = j0 + g;
+    bool stopped = !(g < G && j < valid_rows);
+    if (!stopped && status[j] >= 2) {
+        if (e == 0) gstat[j] = 1;  // outside the bound: the host reconstructs it
+        stopped = true;
+    }
+    __syncthreads();  // the windows after the split are in buffer 0
     int32_t wa = 0, wb = 0;
     int base = 0;
     auto read_window = [&](int buf) {
-        const int e = lane < kGcdSeg ? lane : kGcdSeg - 1;
-        const int32_t va = sSeg[buf][0][e], vb = sSeg[buf][1][e];
-        wa = lane < kGcdSeg ? va : 0;
-        wb = lane < kGcdSeg ? vb : 0;
-        base = __builtin_amdgcn_readfirstlane(sTop[buf]) - 4;
+        const int ee = e < kGcdSeg ? e : kGcdSeg - 1;
+        const int32_t va = sSeg[buf][g][0][ee], vb = sSeg[buf][g][1][ee];
+        wa = e < kGcdSeg ? va : 0;
+        wb = e < kGcdSeg ? vb : 0;
+        base = sTop[buf][g] - 4;
     };
-    read_window(0);
+    // entry x of this component's window (x in 0 .. 7)
+    auto entry = [&](int32_t v, int x) { return __shfl(v, 8 * q + x); };
+    if (!stopped) read_window(0);
     int32_t M0 = 1, M1 = 0, M2 = 0, M3 = 1;  // the matrix issued last (applied by now to the limbs)
-    int result = 1;
-    uint64_t g = 0;
     for (int r = 1;; r++) {
-        // the window after the matrix issued last: limb k changes from limbs k
-        // and k - 1 only, so lanes 1 .. 6 become exact (lane 0 lacks the high
-        // parts entering from below)
-        int lo_lane = 0;
-        if (!(M0 == 1 && M1 == 0 && M2 == 0 && M3 == 1)) {
-            const int64_t va = (int64_t)M0 * wa + ((int64_t)M1 * wb + (1 << 29));
-            const int64_t vb = (int64_t)M2 * wa + ((int64_t)M3 * wb + (1 << 29));
-            const int32_t ha = (int32_t)(va >> 30), hb = (int32_t)(vb >> 30);
-            const int32_t ia = __builtin_amdgcn_update_dpp(0, ha, 0x111, 0xf, 0xf, false);  // row_shr:1
-            const int32_t ib = __builtin_amdgcn_update_dpp(0, hb, 0x111, 0xf, 0xf, false);
-            wa = lane <= kGcdSeg ? (int32_t)((uint32_t)va & 0x3fffffffu) - (1 << 29) + ia : 0;
-            wb = lane <= kGcdSeg ? (int32_t)((uint32_t)vb & 0x3fffffffu) - (1 << 29) + ib : 0;
-            lo_lane = 1;
-        }
-        const uint64_t nzm = __ballot((wa != 0 || wb != 0) && lane >= lo_lane && lane <= kGcdSeg);
-        const int top = nzm ? 63 - __builtin_clzll(nzm) : -1;  // lane of the top limb
-        const int h = base + top;
-        bool stop = false;
-        int32_t nM[4] = {1, 0, 0, 1};
-        if (r > max_rounds || top < 0 || h >= 64 * CW - 3) {
-            stop = true;  // no progress in sight, no limb in view or no headroom left: the host finishes
-        } else if (h <= 3 && base + lo_lane <= 0) {
-            // exact values from limbs 0..3, then the binary gcd
-            __int128 va = 0, vb = 0;
+        int32_t nM0 = 0, nM1 = 0, nM2 = 0, nM3 = 0;
+        if (!stopped) {
+            // the window after the matrix issued last: limb k changes from
+            // limbs k and k - 1 only, so entries 1 .. 6 become exact (entry 0
+            // lacks the high part entering from below)
+            int lo_lane = 0;
+            if (!(M0 == 1 && M1 == 0 && M2 == 0 && M3 == 1)) {
+                const int64_t va = (int64_t)M0 * wa + ((int64_t)M1 * wb + (1 << 29));
+                const int64_t vb = (int64_t)M2 * wa + ((int64_t)M3 * wb + (1 << 29));
+                const int32_t ha = (int32_t)(va >> 30), hb = (int32_t)(vb >> 30);
+                const int32_t ia = __builtin_amdgcn_update_dpp(0, ha, 0x111, 0xf, 0xf, false);  // row_shr:1
+                const int32_t ib = __builtin_amdgcn_update_dpp(0, hb, 0x111, 0xf, 0xf, false);
+                wa = e <= kGcdSeg ? (int32_t)((uint32_t)va & 0x3fffffffu) - (1 << 29) + (e == 0 ? 0 : ia) : 0;
+                wb = e <= kGcdSeg ? (int32_t)((uint32_t)vb & 0x3fffffffu) - (1 << 29) + (e == 0 ? 0 : ib) : 0;
+                lo_lane = 1;
+            }
+            const uint64_t nzm = __ballot((wa != 0 || wb != 0) && e >= lo_lane && e <= kGcdSeg);
+            const uint32_t gb = (uint32_t)(nzm >> (8 * q)) & 0xffu;
+            const int top = gb ? 31 - __builtin_clz(gb) : -1;  // entry of the top limb
+            const int h = base + top;
+            int result = 1;
+            uint64_t gv = 0;
+            bool stop = false, identity = false;
+            if (r > max_rounds || top < 0 || h >= 64 * CW - 3) {
+                stop = true;  // no progress in sight, no limb in view or no headroom left: the host finishes
+            } else if (h <= 3 && base + lo_lane <= 0) {
+                // exact values from limbs 0..3, then the binary gcd (entries
+                // past 7 are above the top and zero)
+                __int128 xa = 0, xb = 0;
 #pragma unroll
-            for (int k = 3; k >= 0; k--) {
-                const int e = k - base;
-                va = va * (1 << 30) + __builtin_amdgcn_readlane(wa, e);
-                vb = vb * (1 << 30) + __builtin_amdgcn_readlane(wb, e);
-            }
-            unsigned __int128 u = (unsigned __int128)(va < 0 ? -va : va);
-            unsigned __int128 v = (unsigned __int128)(vb < 0 ? -vb : vb);
-            auto ctz = [](unsigned __int128 x) -> int {
-                const uint64_t lo = (uint64_t)x;
-                return lo ? __builtin_ctzll(lo) : 64 + __builtin_ctzll((uint64_t)(x >> 64));
-            };
-            if (u == 0) {
-                u = v;
-            } else if (v != 0) {
-                const int sh = ctz(u | v);
-                u >>= ctz(u);
-                do {
-                    v >>= ctz(v);
-                    if (u > v) {
-                        const unsigned __int128 t = u;
-                        u = v;
-                        v = t;
-                    }
-                    v -= u;
-                } while (v != 0);
-                u <<= sh;
-            }
-            if ((uint64_t)(u >> 64) == 0) {
-                g = (uint64_t)u;
-                result = 0;
-            }
-            stop = true;
-        } else if (top - 2 < lo_lane || h <= 3) {
-            // the window lacks the limbs the leading parts (or the last four
-            // limbs) need: issue the identity and read a fresh window
-        } else {
-            // leading parts from limbs h, h - 1, h - 2; their signs start the
-            // cofactor matrix, so the steps run on magnitudes
-            const double fa = fma(fma((double)__builtin_amdgcn_readlane(wa, top), 0x1p30,
-                                      (double)__builtin_amdgcn_readlane(wa, top - 1)),
-                                  0x1p30, (double)__builtin_amdgcn_readlane(wa, top - 2));
-            const double fb = fma(fma((double)__builtin_amdgcn_readlane(wb, top), 0x1p30,
-                                      (double)__builtin_amdgcn_readlane(wb, top - 1)),
-                                  0x1p30, (double)__builtin_amdgcn_readlane(wb, top - 2));
-            int ex;
-            (void)frexp(fmax(fabs(fa), fabs(fb)), &ex);
-            double x = floor(ldexp(fabs(fa), 52 - ex)), y = floor(ldexp(fabs(fb), 52 - ex));
-            double xs = x * (1.0 - 0x1p-22);
-            double A = fa < 0.0 ? -1.0 : 1.0, B = 0.0, C = 0.0, D = fb < 0.0 ? -1.0 : 1.0;
-            int steps = 0;
-            for (int it = 0; it < 16; it++) {
-                // four steps; divisors y, y1, y2, y3; new rows (C1, D1) .. (C4, D4)
-                double s1, y1, C1, D1, s2, y2, C2, D2, s3, y3, C3, D3, s4, y4, C4, D4;
-                euclid_step(x, xs, y, A, B, C, D, s1, y1, C1, D1);
-                euclid_step(y, s1, y1, C, D, C1, D1, s2, y2, C2, D2);
-                euclid_step(y1, s2, y2, C1, D1, C2, D2, s3, y3, C3, D3);
-                euclid_step(y2, s3, y3, C2, D2, C3, D3, s4, y4, C4, D4);
-                if ((fmin(y2, y3) >= 0x1p26) & (row_max(C3, D3, C4, D4) < 0x1p26)) {
-                    x = y3, xs = s4, y = y4;
-                    A = C3, B = D3, C = C4, D = D4;
-                    steps += 4;
-                    continue;
+                for (int k = 3; k >= 0; k--) {
+                    const int x = k - base;
+                    const int32_t la = entry(wa, x < 8 ? x : 7), lb = entry(wb, x < 8 ? x : 7);
+                    xa = xa * (1 << 30) + (x < 8 ? la : 0);
+                    xb = xb * (1 << 30) + (x < 8 ? lb : 0);
                 }
-                // the last block: keep its longest acceptable prefix
-                if ((fmin(y1, y2) >= 0x1p26) & (row_max(C2, D2, C3, D3) < 0x1p26)) {
-                    A = C2, B = D2, C = C3, D = D3;
-                    steps += 3;
-                } else if ((fmin(y, y1) >= 0x1p26) & (row_max(C1, D1, C2, D2) < 0x1p26)) {
-                    A = C1, B = D1, C = C2, D = D2;
-                    steps += 2;
-                } else if ((y >= 0x1p26) & (row_max(C1, D1, C1, D1) < 0x1p26)) {
-                    A = C, B = D, C = C1, D = D1;
-                    steps += 1;
+                unsigned __int128 u = (unsigned __int128)(xa < 0 ? -xa : xa);
+                unsigned __int128 v = (unsigned __int128)(xb < 0 ? -xb : xb);
+                auto ctz = [](unsigned __int128 x) -> int {
+                    const uint64_t lo = (uint64_t)x;
+                    return lo ? __builtin_ctzll(lo) : 64 + __builtin_ctzll((uint64_t)(x >> 64));
+                };
+                if (u == 0) {
+                    u = v;
+                } else if (v != 0) {
+                    const int sh = ctz(u | v);
+                    u >>= ctz(u);
+                    do {
+                        v >>= ctz(v);
+                        if (u > v) {
+                            const unsigned __int128 t = u;
+                            u = v;
+                            v = t;
+                        }
+                        v -= u;
+                    } while (v != 0);
+                    u <<= sh;
                 }
-                break;
-            }
-            if (steps == 0) {
-                stop = true;  // no certain progress: the host finishes
+                if ((uint64_t)(u >> 64) == 0) {
+                    gv = (uint64_t)u;
+                    result = 0;
+                }
+                stop = true;
+            } else if (top - 2 < lo_lane || h <= 3) {
+                // the window lacks the limbs the leading parts (or the last
+                // four limbs) need: issue the identity and read a fresh window
+                identity = true;
             } else {
-                nM[0] = (int32_t)A;
-                nM[1] = (int32_t)B;
-                nM[2] = (int32_t)C;
-                nM[3] = (int32_t)D;
+                // leading parts from limbs h, h - 1, h - 2; their signs start
+                // the cofactor matrix, so the steps run on magnitudes
+                const double fa = fma(fma((double)entry(wa, top), 0x1p30, (double)entry(wa, top - 1)), 0x1p30,
+                                      (double)entry(wa, top - 2));
+                const double fb = fma(fma((double)entry(wb, top), 0x1p30, (double)entry(wb, top - 1)), 0x1p30,
+                                      (double)entry(wb, top - 2));
+                int ex;
+                (void)frexp(fmax(fabs(fa), fabs(fb)), &ex);
+                double x = floor(ldexp(fabs(fa), 52 - ex)), y = floor(ldexp(fabs(fb), 52 - ex));
+                double xs = x * (1.0 - 0x1p-22);
+                double A = fa < 0.0 ? -1.0 : 1.0, B = 0.0, C = 0.0, D = fb < 0.0 ? -1.0 : 1.0;
+                int steps = 0;
+                for (int it = 0; it < 16; it++) {
+                    // four steps; divisors y, y1, y2, y3; new rows (C1, D1) .. (C4, D4)
+                    double s1, y1, C1, D1, s2, y2, C2, D2, s3, y3, C3, D3, s4, y4, C4, D4;
+                    euclid_step(x, xs, y, A, B, C, D, s1, y1, C1, D1);
+                    euclid_step(y, s1, y1, C, D, C1, D1, s2, y2, C2, D2);
+                    euclid_step(y1, s2, y2, C1, D1, C2, D2, s3, y3, C3, D3);
+                    euclid_step(y2, s3, y3, C2, D2, C3, D3, s4, y4, C4, D4);
+                    if ((fmin(y2, y3) >= 0x1p26) & (row_max(C3, D3, C4, D4) < 0x1p26)) {
+                        x = y3, xs = s4, y = y4;
+                        A = C3, B = D3, C = C4, D = D4;
+                        steps += 4;
+                        continue;
+                    }
+                    // the last block: keep its longest acceptable prefix
+                    if ((fmin(y1, y2) >= 0x1p26) & (row_max(C2, D2, C3, D3) < 0x1p26)) {
+                        A = C2, B = D2, C = C3, D = D3;
+                        steps += 3;
+                    } else if ((fmin(y, y1) >= 0x1p26) & (row_max(C1, D1, C2, D2) < 0x1p26)) {
+                        A = C1, B = D1, C = C2, D = D2;
+                        steps += 2;
+                    } else if ((y >= 0x1p26) & (row_max(C1, D1, C1, D1) < 0x1p26)) {
+                        A = C, B = D, C = C1, D = D1;
+                        steps += 1;
+                    }
+                    break;
+                }
+                if (steps == 0) {
+                    stop = true;  // no certain progress: the host finishes
+                } else {
+                    nM0 = (int32_t)A;
+                    nM1 = (int32_t)B;
+                    nM2 = (int32_t)C;
+                    nM3 = (int32_t)D;
+                }
+            }
+            if (identity) nM0 = 1, nM1 = 0, nM2 = 0, nM3 = 1;
+            if (stop) {
+                if (e == 0) {
+                    gstat[j] = result;
+                    Gout[j] = gv;
+                }
+                stopped = true;
+                nM0 = nM1 = nM2 = nM3 = 0;
             }
         }
-        const int buf = r & 1;
-        if (lane0) sM[buf] = stop ? make_int4(0, 0, 0, 0) : make_int4(nM[0], nM[1], nM[2], nM[3]);
-        __syncthreads();  // matrix r is ready; the window after matrix r - 1 is ready
-        if (stop) break;
-        // the window handed over after matrix r - 1; the next iteration
-        // applies matrix r to it
-        read_window(buf ^ 1);
-        M0 = __builtin_amdgcn_readfirstlane(nM[0]), M1 = __builtin_amdgcn_readfirstlane(nM[1]);
-        M2 = __builtin_amdgcn_readfirstlane(nM[2]), M3 = __builtin_amdgcn_readfirstlane(nM[3]);
-    }
-    if (lane0) {
-        gstat[j] = result;
-        G[j] = g;
+        if (e == 0 && g < G) sM[r & 1][g] = make_int4(nM0, nM1, nM2, nM3);
+        const bool all_done = __ballot(!stopped) == 0;
+        if (lane0) sDone[r & 1][ew] = all_done ? 1 : 0;
+        __syncthreads();  // matrices r are ready; the windows after matrices r - 1 are ready
+        if (sDone[r & 1][0] & sDone[r & 1][1]) break;
+        // the windows handed over after matrices r - 1; the next iteration
+        // applies matrices r to them
+        if (!stopped) read_window((r & 1) ^ 1);
+        M0 = nM0, M1 = nM1, M2 = nM2, M3 = nM3;
     }
 }
 
@@ -696,36 +771,80 @@ int gcd_words_per_lane(int words) {
     return limbs <= 64 * 8 ? 8 : limbs <= 64 * 16 ? 16 : limbs <= 64 * 32 ? 32 : 0;
 }
 
-// Unused dynamic LDS per gcd block that caps the blocks a CU can hold at
-// ceil(blocks / CUs): the components are latency-bound chains, and an even
-// spread keeps every CU at the same small number of them.  Zero when the cap
-// would need more than 48 KB (few blocks) or the device does not say.
-static size_t gcd_lds_pad(int blocks) {
-    static int cus = -1, lds = 0;
+// Compute units of the current device (0 if the device does not say).
+static int device_cus() {
+    static int cus = -1;
     if (cus < 0) {
         int dev = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess)
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             cus = 0;
     }
-    if (cus <= 0 || lds <= 0 || blocks <= 0) return 0;
+    return cus;
+}
+
+// Unused dynamic LDS per gcd block that caps the blocks a CU can hold at
+// ceil(blocks / CUs): the components are latency-bound chains, and an even
+// spread keeps every CU at the same small number of them.  Above 48 KB the
+// kernel's dynamic LDS limit is raised first; zero when the device does not
+// say or does not allow it.
+static size_t gcd_lds_pad(const void* kernel, int blocks) {
+    static int lds_cu = -1, lds_blk = 0;
+    if (lds_cu < 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess ||
+            hipDeviceGetAttribute(&lds_blk, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+            lds_cu = 0;
+    }
+    const int cus = device_cus();
+    if (cus <= 0 || lds_cu <= 0 || blocks <= 0) return 0;
     const int cap = (blocks + cus - 1) / cus;
-    const int pad = lds / cap - 2048;  // room for the kernel's own LDS
-    return pad > 0 && pad <= 48 * 1024 ? (size_t)pad : 0;
+    const int pad = lds_cu / cap - 4096;  // room for the kernel's own LDS
+    if (pad <= 0 || pad + 4096 > lds_blk) return 0;
+    if (pad > 48 * 1024 && hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, pad) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    return (size_t)pad;
+}
+
+// Components per gcd block: the components spread evenly over the compute
+// units, at most gmax per block (gmax + 1 waves must fit one CU).
+static int gcd_group(int rows, int gmax) {
+    const int cus = device_cus();
+    int G = cus > 0 ? (rows + cus - 1) / cus : 4;
+    return G < 1 ? 1 : (G > gmax ? gmax : G);
+}
+
+template <int CW, int GMAX>
+static void launch_gcd_as(const uint32_t* Y, int nw, const int* status, int valid_rows, const uint32_t* Dw,
+                          int nwd, uint64_t* G, int* gstat, hipStream_t st) {
+    const int grp = gcd_group(valid_rows, GMAX);
+    const int blocks = (valid_rows + grp - 1) / grp;
+    const int waves = gcd_block_waves(grp);
+    const size_t pad = gcd_lds_pad((const void*)gcd_kernel<CW, GMAX>, blocks);
+    static const bool verbose = [] {
+        const char* e = std::getenv("ES_VERBOSE");
+        return e && *e && *e != '0';
+    }();
+    if (verbose)
+        fprintf(stderr, "[es] gcd: %d components, %d per block, %d blocks, %zu bytes of LDS padding, %d slots\n",
+                valid_rows, grp, blocks, pad, CW);
+    es_launch(gcd_kernel<CW, GMAX>, dim3(blocks), dim3(64 * waves), pad, st, Y, nw, status, valid_rows, Dw, nwd,
+              grp, G, gstat);
 }
 
 hipError_t launch_gcd(const uint32_t* Y, int nw, const int* status, int valid_rows, const uint32_t* Dw, int nwd,
                       uint64_t* G, int* gstat, hipStream_t st) {
     const int cw = gcd_words_per_lane(nw > nwd ? nw : nwd);
-    const dim3 grid(valid_rows);
-    const size_t pad = gcd_lds_pad(valid_rows);
+    if (valid_rows <= 0) return hipSuccess;
     if (cw == 8)
-        es_launch(gcd_kernel<8>, grid, dim3(128), pad, st, Y, nw, status, valid_rows, Dw, nwd, G, gstat);
+        launch_gcd_as<8, kGcdMaxGroup>(Y, nw, status, valid_rows, Dw, nwd, G, gstat, st);
     else if (cw == 16)
-        es_launch(gcd_kernel<16>, grid, dim3(128), pad, st, Y, nw, status, valid_rows, Dw, nwd, G, gstat);
+        launch_gcd_as<16, kGcdMaxGroup>(Y, nw, status, valid_rows, Dw, nwd, G, gstat, st);
     else if (cw == 32)
-        es_launch(gcd_kernel<32>, grid, dim3(128), pad, st, Y, nw, status, valid_rows, Dw, nwd, G, gstat);
+        launch_gcd_as<32, kGcdMaxGroup>(Y, nw, status, valid_rows, Dw, nwd, G, gstat, st);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

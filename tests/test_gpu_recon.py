@@ -80,3 +80,27 @@ def test_signs_and_zero_numerators():
     b0 = np.zeros((n, 1), dtype=np.int64)
     Xg, _ = solve_both(A, b0)
     assert Xg == [[(0, 1)] for _ in range(n)]
+
+
+@pytest.mark.parametrize("n,c,seed", [(257, 1, 31), (300, 4, 32), (520, 8, 33)])
+def test_gcd_groups_and_partial_blocks(n, c, seed):
+    """The gcd kernel runs several components per block (one Euclid wave for
+    all of them, one limb wave each), as many as the component count spread
+    over the compute units asks for, up to fifteen.  n c = 257, 1200 and
+    4160 components give groups of 2, 5 and 15 with a partial last block;
+    the GPU path must match the host path and reconstruct no component
+    alone.  A gcd goes back to the host only when a Euclidean quotient
+    reaches 2^26 (about 2e-8 per step by the Gauss-Kuzmin law, so about once
+    in the 3e7 steps of the largest case) or the gcd exceeds 64 bits."""
+    A, b = W.uniform_system(n, c, 24, seed)
+    dA, db = torch.as_tensor(A).cuda(), torch.as_tensor(b).cuda()
+    Xg = es.solve_pairs(dA, db)
+    alone, host_gcds = _lib.last_recon_counts()
+    assert alone == 0 and 0 <= host_gcds <= 3, (alone, host_gcds)
+    try:
+        _lib.set_gpu_reconstruction(False)
+        Xh = es.solve_pairs(dA, db)
+    finally:
+        _lib.set_gpu_reconstruction(True)
+    assert Xg == Xh
+    assert any(q != max(qq for row in Xg for (_, qq) in row) for row in Xg for (_, q) in row) or n * c < 300
