@@ -17,8 +17,8 @@ import numpy as np
 
 from . import _lib
 
-__all__ = ["solve", "solve_pairs", "batched_inverse", "lift_digits", "reconstruct", "primes",
-           "workspace_bytes", "last_timings", "SolveError"]
+__all__ = ["solve", "solve_pairs", "batched_inverse", "batched_inverse_noalloc", "noalloc_max_n", "lift_digits",
+           "reconstruct", "primes", "workspace_bytes", "last_timings", "SolveError"]
 
 NUM_PRIMES = _lib.NUM_PRIMES
 
@@ -30,7 +30,7 @@ class SolveError(RuntimeError):
 
 
 def _raise(status: int):
-    if status in (_lib.ES_EINVAL, _lib.ES_ERANGE):
+    if status in (_lib.ES_EINVAL, _lib.ES_ERANGE, _lib.ES_ETOOBIG):
         raise ValueError(f"{_lib.strerror(status)} (status {status})")
     raise SolveError(status)
 
@@ -144,6 +144,29 @@ def batched_inverse(A, workspace=None):
     if st != _lib.ES_OK:
         _raise(st)
     return B, list(flags)
+
+
+def batched_inverse_noalloc(A, out=None):
+    """The same as ``batched_inverse`` through the entry point that allocates
+    nothing on the device (fixed scratch, n <= noalloc_max_n()).  ``out`` may
+    supply the int8 [53][n][n] result tensor."""
+    import torch
+    lib = _lib.load()
+    A, _, dev = _device_inputs(A)
+    n = A.shape[0]
+    B = out if out is not None else torch.empty((NUM_PRIMES, n, n), dtype=torch.int8, device=dev)
+    if B.dtype != torch.int8 or tuple(B.shape) != (NUM_PRIMES, n, n) or not B.is_contiguous():
+        raise ValueError("out must be a contiguous int8 [53][n][n] tensor")
+    flags = (ctypes.c_int32 * NUM_PRIMES)()
+    st = lib.es_batched_inverse_noalloc(ctypes.c_void_p(A.data_ptr()), n, _stream(dev), ctypes.c_void_p(B.data_ptr()),
+                                        flags)
+    if st != _lib.ES_OK:
+        _raise(st)
+    return B, list(flags)
+
+
+def noalloc_max_n() -> int:
+    return int(_lib.load().es_noalloc_max_n())
 
 
 def lift_digits(A, b, m: int = 0, workspace=None):

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libexact_solve.so")
 
 ES_OK, ES_SINGULAR = 0, 1
-ES_EINVAL, ES_ERANGE, ES_ENOPRIME, ES_EHIP, ES_ENOMEM, ES_EINTERNAL = -1, -2, -3, -4, -5, -6
+ES_EINVAL, ES_ERANGE, ES_ENOPRIME, ES_EHIP, ES_ENOMEM, ES_EINTERNAL, ES_ETOOBIG = -1, -2, -3, -4, -5, -6, -7
 NUM_PRIMES = 53
 DIGIT_LIMBS = 6
 
@@ -23,7 +23,8 @@ EXPORTS = ["es_strerror", "es_primes", "es_workspace_bytes", "es_solve_device", 
            "es_solution_free", "es_solution_modulus_bits", "es_set_gpu_reconstruction", "es_set_blocked_inverse",
            "es_set_lift_record_steps",
            "es_last_timings", "es_set_profiling", "es_kernel_profile",
-           "es_batched_inverse", "es_lift_digits", "es_reconstruct"]
+           "es_batched_inverse", "es_batched_inverse_noalloc", "es_noalloc_max_n", "es_lift_digits",
+           "es_reconstruct"]
 
 _lib = None
 
@@ -84,6 +85,10 @@ def load():
     lib.es_kernel_profile.restype = ctypes.c_int
     lib.es_batched_inverse.argtypes = [c_vp, ctypes.c_int32, c_vp, ctypes.c_size_t, c_vp, c_vp, c_i32p]
     lib.es_batched_inverse.restype = ctypes.c_int
+    lib.es_batched_inverse_noalloc.argtypes = [c_vp, ctypes.c_int32, c_vp, c_vp, c_i32p]
+    lib.es_batched_inverse_noalloc.restype = ctypes.c_int
+    lib.es_noalloc_max_n.argtypes = []
+    lib.es_noalloc_max_n.restype = ctypes.c_int32
     lib.es_lift_digits.argtypes = [c_vp, c_vp, ctypes.c_int32, ctypes.c_int32, c_vp, ctypes.c_size_t, c_vp,
                                    ctypes.c_int32, c_i64p, ctypes.c_size_t, c_u64p, c_i32p]
     lib.es_lift_digits.restype = ctypes.c_int

@@ -337,6 +337,7 @@ const char* es_strerror(int status) {
         case ES_EHIP: return "HIP runtime error";
         case ES_ENOMEM: return "out of memory";
         case ES_EINTERNAL: return "internal consistency check failed";
+        case ES_ETOOBIG: return "n exceeds what the fixed scratch of the non-allocating entry point holds";
         default: return "unknown status";
     }
 }
@@ -552,27 +553,64 @@ int32_t es_solution_modulus_bits(const es_solution* s) { return s ? s->data.mbit
 
 void es_solution_free(es_solution* s) { delete s; }
 
+}  // extern "C"
+
+namespace {
+
+// The batched inverse in the first inverse_bytes(L) bytes of ws.
+int batched_inverse_in(const int64_t* dA, const Layout& L, uint8_t* ws, hipStream_t st, int8_t* dB_out,
+                       int32_t* flags_host) {
+    Prep pr;
+    pr.L = L;
+    // the norms of b are not needed here; A stands in for it
+    int rc = prepare(dA, dA, L.n, 1, ws, st, &pr);
+    if (rc == ES_SINGULAR) rc = ES_OK;  // a zero row/column just makes every prime singular
+    if (rc != ES_OK) return rc;
+    int flags[kNumPrimes];
+    Profiler prof(st);
+    rc = run_inverse(dA, ws, st, &pr, flags, &prof);
+    if (rc != ES_OK) return rc;
+    HIP_CHECK(launch_export_inverse(pr.L, ws, dB_out, st));
+    HIP_CHECK(hipStreamSynchronize(st));
+    for (int j = 0; j < kNumPrimes; j++) flags_host[j] = flags[j] ? 1 : 0;
+    return ES_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int es_batched_inverse(const int64_t* dA, int32_t n, void* d_ws, size_t ws_bytes, void* stream, int8_t* dB_out,
                        int32_t* flags_host) {
     if (!dA || !d_ws || !dB_out || !flags_host || !valid_shape(n, 1)) return ES_EINVAL;
-    Prep pr;
-    pr.L = make_layout(n, 1);
-    if (ws_bytes < pr.L.total) return ES_EINVAL;
-    hipStream_t st = (hipStream_t)stream;
-    uint8_t* ws = (uint8_t*)d_ws;
+    const Layout L = make_layout(n, 1);
+    if (ws_bytes < L.total) return ES_EINVAL;
     try {
-        // the norms of b are not needed here; A stands in for it
-        int rc = prepare(dA, dA, n, 1, ws, st, &pr);
-        if (rc == ES_SINGULAR) rc = ES_OK;  // a zero row/column just makes every prime singular
-        if (rc != ES_OK) return rc;
-        int flags[kNumPrimes];
-        Profiler prof(st);
-        rc = run_inverse(dA, ws, st, &pr, flags, &prof);
-        if (rc != ES_OK) return rc;
-        HIP_CHECK(launch_export_inverse(pr.L, ws, dB_out, st));
-        HIP_CHECK(hipStreamSynchronize(st));
-        for (int j = 0; j < kNumPrimes; j++) flags_host[j] = flags[j] ? 1 : 0;
-        return ES_OK;
+        return batched_inverse_in(dA, L, (uint8_t*)d_ws, (hipStream_t)stream, dB_out, flags_host);
+    } catch (...) {
+        return ES_EINTERNAL;
+    }
+}
+
+int32_t es_noalloc_max_n(void) {
+    // the largest n whose inverse fits the fixed scratch (the bytes grow with n)
+    int32_t lo = 0, hi = 1 << 16;
+    while (lo < hi) {
+        const int32_t mid = lo + (hi - lo + 1) / 2;
+        if (inverse_bytes(make_layout(mid, 1)) <= fixed_scratch_bytes()) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+int es_batched_inverse_noalloc(const int64_t* dA, int32_t n, void* stream, int8_t* dB_out, int32_t* flags_host) {
+    if (!dA || !dB_out || !flags_host || !valid_shape(n, 1)) return ES_EINVAL;
+    try {
+        const Layout L = make_layout(n, 1);
+        if (inverse_bytes(L) > fixed_scratch_bytes()) return ES_ETOOBIG;
+        uint8_t* ws = fixed_scratch();
+        if (!ws) return ES_EHIP;
+        return batched_inverse_in(dA, L, ws, (hipStream_t)stream, dB_out, flags_host);
     } catch (...) {
         return ES_EINTERNAL;
     }

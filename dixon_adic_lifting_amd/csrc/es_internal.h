@@ -149,6 +149,15 @@ inline bool fused_lift_shape(int n, int c, int pitch) {
 
 // The layout depends on (n, c) only.
 Layout make_layout(int n, int c);
+// bytes at the start of a layout that the batched inverse touches (its
+// matrices, pivots, panels, norms, the int32 copy of A and the residues the
+// set-up clears)
+size_t inverse_bytes(const Layout& L);
+// Fixed device scratch of the entry point that allocates nothing (one copy
+// per device, shared by every call on it): its size, and this device's copy
+// (NULL if the address lookup fails).
+size_t fixed_scratch_bytes();
+uint8_t* fixed_scratch();
 // cap on the record steps that later lifts on the calling thread use per
 // launch (0: none); the layout keeps room for its default count either way
 void set_lift_record_cap(int steps);

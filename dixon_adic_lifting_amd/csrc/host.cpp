@@ -98,6 +98,10 @@ Layout make_layout(int n, int c) {
     return L;
 }
 
+size_t inverse_bytes(const Layout& L) {
+    return align_up(L.off_rho + (size_t)kNumPrimes * L.c * L.pitch, 256);
+}
+
 // ---------------------------------------------------------------- primes
 
 LiveSet make_live_set(const int* flags) {

@@ -24,6 +24,7 @@
 
 #include <climits>
 #include <cstdlib>
+#include <mutex>
 #include <type_traits>
 
 #include "es_internal.h"
@@ -2563,6 +2564,36 @@ hipError_t launch_lift_residual(const Layout& L, uint8_t* ws, bool a32, const in
                                prm, rp, rho, L.pitch, 0);
     }
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- fixed scratch
+// Device memory for es_batched_inverse_noalloc, the entry point for callers
+// that cannot allocate: a file-scope array, one copy per device, held until
+// the process ends.  Host code never passes the array's name to a kernel
+// (on the host it is only a stand-in for the symbol); the device address of
+// this device's copy is looked up once per device, with that device current,
+// and kept.
+constexpr size_t kFixedScratchBytes = (size_t)24 << 20;
+static __device__ __align__(256) uint8_t scratch[kFixedScratchBytes];
+
+size_t fixed_scratch_bytes() { return kFixedScratchBytes; }
+
+uint8_t* fixed_scratch() {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* ptr[kMaxDevices] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lk(mu);
+    if (!ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        ptr[dev] = p;
+    }
+    return (uint8_t*)ptr[dev];
 }
 
 }  // namespace es

@@ -46,7 +46,8 @@ enum {
     ES_ENOPRIME = -3,   /* det A is a nonzero multiple of every odd prime < 256 */
     ES_EHIP = -4,       /* a HIP runtime call failed */
     ES_ENOMEM = -5,     /* host or device allocation failed */
-    ES_EINTERNAL = -6   /* an internal consistency check failed */
+    ES_EINTERNAL = -6,  /* an internal consistency check failed */
+    ES_ETOOBIG = -7     /* n beyond es_noalloc_max_n() for es_batched_inverse_noalloc */
 };
 
 #define ES_NUM_PRIMES 53      /* odd primes 3 .. 251 */
@@ -194,6 +195,24 @@ int es_kernel_profile(double *total_ms, int32_t *counts, int32_t cap);
  */
 int es_batched_inverse(const int64_t *dA, int32_t n, void *d_ws, size_t ws_bytes,
                        void *stream, int8_t *dB_out, int32_t *flags_host);
+
+/*
+ * es_batched_inverse for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation and the same results, with no workspace
+ * argument.  Its kernels work in a fixed scratch array of 24 MiB that the
+ * library holds on each device until the process ends; the call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine).  n must not
+ * exceed es_noalloc_max_n() (512): larger n returns ES_ETOOBIG.  dA, dB_out,
+ * flags_host and stream as for es_batched_inverse.  Every call on one device
+ * shares that device's scratch (each call overwrites it), so calls that
+ * overlap on one device, from several threads or streams, race.
+ */
+int es_batched_inverse_noalloc(const int64_t *dA, int32_t n, void *stream, int8_t *dB_out,
+                               int32_t *flags_host);
+
+/* Largest n that es_batched_inverse_noalloc takes. */
+int32_t es_noalloc_max_n(void);
 
 /*
  * The lift alone (card, "Method"): runs the batched inverse, drops primes
