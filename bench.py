@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--workload", default="c4_n1024_int24")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0,
-                    help="approximate CPU seconds for the bounded oracle sample")
+                    help="approximate seconds for the oracle's measured first steps")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--sweep", action="store_true", help="time every workload and print a table")
@@ -206,6 +206,34 @@ def counter_traffic(workload):
             out["lift_contract"] = v["traffic_bytes"]
         elif "recon_gemm_kernel" in name:
             out["recon_gemm"] = v["traffic_bytes"]
+        elif "residual1_kernel" in name or "residual_mfma_kernel" in name:
+            out["residual"] = v["traffic_bytes"]
+        elif "residue_kernel" in name:
+            out["residues"] = v["traffic_bytes"]
+        elif "gcd_kernel" in name:
+            out["recon_gcd"] = v["traffic_bytes"]
+    return out
+
+
+def mfma_counters(workload):
+    """Int8 MFMA counters per kernel class from the committed rocprofv3 run
+    (profiles/pmc_mfma_<workload>.json: SQ_INSTS_VALU_MFMA_MOPS_I8 as int8
+    operations per dispatch and SQ_VALU_MFMA_BUSY_CYCLES as the share of
+    SIMD cycles), or {} when absent or taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"pmc_mfma_{workload}.json")
+    if not os.path.exists(path):
+        return {}
+    with open(path) as f:
+        data = json.load(f)
+    if data.get("kernel_sources_sha256") != kernel_sources_sha256():
+        return {}
+    names = {"lift_mfma_kernel": "lift_contract", "residual_mfma_kernel": "residual", "gj_update_kernel": "gj_update",
+             "recon_gemm_kernel": "recon_gemm"}
+    out = {}
+    for name, v in data["kernels"].items():
+        for key, cls in names.items():
+            if key in name:
+                out[cls] = {"int8_ops_per_launch": v["int8_ops_per_dispatch"], "mfma_busy": round(v["mfma_busy"], 5)}
     return out
 
 
@@ -287,14 +315,14 @@ def rooflines(prof, info, n, c, traffic=None):
         bytes_per = 4.0 * n * n + 16.0 * n + E * pitch
         gbs = bytes_per / (out["residual"]["avg_launch_us"] / 1e6) / 1e9
         out["residual"].update({"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic.get("residual"),
                                 "algorithmic_bytes_per_launch": int(bytes_per)})
     if "residues" in out:
         # A (int64) read once; every prime's residue matrix and the int32 copy of A written
         bytes_per = 8.0 * n * n + 53.0 * n * pitch + 4.0 * n * n
         gbs = bytes_per / (out["residues"]["avg_launch_us"] / 1e6) / 1e9
         out["residues"].update({"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic.get("residues"),
                                 "algorithmic_bytes_per_launch": int(bytes_per)})
     if "gj_panel" in out:
         # the panel's element updates, four 32-bit integer operations each (multiply-add,
@@ -311,7 +339,8 @@ def rooflines(prof, info, n, c, traffic=None):
         ops = n * c * B * B / 420.0
         r = ops / (out["recon_gcd"]["total_ms"] / 1e3) / 1e12
         out["recon_gcd"].update({"bound": "alu", "achieved": round(r, 3), "peak": INT64_MAD_PEAK_TOPS,
-                                 "unit": "T mul-add/s", "frac": round(r / INT64_MAD_PEAK_TOPS, 4), "traffic": None,
+                                 "unit": "T mul-add/s", "frac": round(r / INT64_MAD_PEAK_TOPS, 4),
+                                 "traffic": traffic.get("recon_gcd"),
                                  "algorithmic_mul_adds_total": ops})
     if c > 1 and info.get("entry_bits", 64) <= 30 and "residual" in out:
         # several right-hand sides: A x mod 2^64 as int8 MFMA products of 4 byte planes of A
@@ -336,88 +365,136 @@ def cpu_model():
     return None
 
 
-def _oracle_projection(A, b, threads, K):
-    """Time the plain-C Bareiss oracle on the first K elimination steps of
-    (A, b) and project the whole solve.
+def _minor_limbs(k, log2_sigma):
+    """64-bit limbs of a (k + 1)-minor of a matrix with i.i.d. entries of RMS
+    2^log2_sigma: log2 |det| is about (k + 1) log2 sigma + log2 sqrt((k + 1)!)."""
+    bits = (k + 1) * log2_sigma + 0.5 * math.lgamma(k + 2) / math.log(2.0)
+    return max(1.0, bits / 64.0 + 1.0)
 
-    The oracle reports each step's wall time.  Step k updates
-    e_k = (n - k - 1)(n + c - k - 1) entries, each two products, a difference
-    and an exact division of (k + 1)-minors of about L_k 64-bit limbs
-    (Hadamard: (k + 1)(log2 max|A| + log2(k + 1) / 2) bits), so
-    t_k = e_k (a + c L_k + d L_k^2) is fitted by least squares over the
-    sampled steps and summed over all n.  Back substitution takes n products
-    per row of numbers up to L_n limbs, about a (c n^2 L_n^2 / 2) share, and
-    is added with the fitted d."""
-    import numpy as np
+
+def _entry_cost_table(threads, max_limbs):
+    """Seconds per elimination entry update of the C oracle at operand sizes
+    on a geometric grid up to max_limbs, every thread running at once."""
     from oracle import cbareiss
-    n, c = A.shape[0], b.shape[1]
-    bits_entry = math.log2(max(2, int(np.abs(A).max())))
+    grid, L = [], 1.0
+    while L < 1.15 * max_limbs:
+        grid.append(int(round(L)))
+        L *= 1.35
+    grid.append(int(math.ceil(1.15 * max_limbs)))
+    table = []
+    for L in sorted(set(grid)):
+        reps = max(3, int(0.02 / (1e-7 + 4e-9 * L * L)))
+        table.append((L, cbareiss.entry_update_seconds(L, max(1, L - 1), reps, threads)))
+    return table
 
-    def limbs(k):
-        return (k + 1) * (bits_entry + 0.5 * math.log2(k + 1) + 1.0) / 64.0 + 1.0
 
-    def feats(k):
-        e = (n - k - 1) * (n + c - k - 1)
-        L = limbs(k)
-        return [e, e * L, e * L * L]
+def _cost(table, L):
+    """log-log interpolation in the measured table"""
+    if L <= table[0][0]:
+        return table[0][1]
+    for (L0, t0), (L1, t1) in zip(table, table[1:]):
+        if L <= L1:
+            w = math.log(L / L0) / math.log(L1 / L0)
+            return math.exp((1 - w) * math.log(t0) + w * math.log(t1))
+    return table[-1][1] * (L / table[-1][0]) ** 2
 
-    st = np.zeros(n, dtype=np.float64)
+
+def _project(A, c, threads, table, gcd_s, steps=None, first=0):
+    """Projected wall time of the oracle (oracle/bareiss.c) on an n x n system
+    with entries like A's, from elimination step `first` on (the steps before
+    it are timed by running them): per elimination step, each thread updates
+    ceil((n - k - 1) / T) rows of n + c - k - 1 entries at the measured cost
+    for the step's operand size; back substitution takes per row the row's
+    share of products of an L_i-limb by an L_n-limb number (a third of an
+    entry update at their geometric mean size); lowest terms take one binary
+    gcd of L_n-limb numbers per component.  With `steps`, only elimination
+    steps [first, steps) are projected."""
+    import numpy as np
+    n = A.shape[0]
+    log2_sigma = 0.5 * math.log2(max(1.0, float(np.mean(A.astype(np.float64) ** 2))))
+    K = n if steps is None else steps
+    elim = 0.0
+    for k in range(first, K):
+        rows = -(-(n - k - 1) // threads)
+        elim += rows * (n + c - k - 1) * _cost(table, _minor_limbs(k, log2_sigma))
+    if steps is not None:
+        return elim
+    Ln = _minor_limbs(n - 1, log2_sigma)
+    back = 0.0
+    for i in range(n):
+        Li = _minor_limbs(i, log2_sigma)
+        back += (-(-(n - i - 1) // threads) + 2) * _cost(table, math.sqrt(Li * Ln)) / 3.0
+    back *= c
+    lowest = -(-(n * c) // threads) * gcd_s
+    return elim + back + lowest
+
+
+def _gcd_seconds(limbs):
+    """Seconds per binary gcd of two limbs-limb numbers in the C oracle."""
+    import random
+    from oracle import cbareiss
+    rng = random.Random(7)
+    a, b = rng.getrandbits(64 * limbs) | 1, rng.getrandbits(64 * limbs) | 1
     t0 = time.perf_counter()
-    cbareiss.run(A, b, threads=threads, max_steps=K, step_seconds=st)
-    dt = time.perf_counter() - t0
-    lo = min(4, K // 4)
-    X = np.array([feats(k) for k in range(lo, K)], dtype=np.float64)
-    coef, *_ = np.linalg.lstsq(X, st[lo:K], rcond=None)
-    coef = np.maximum(coef, 0.0)
-    elim = sum(float(np.dot(coef, feats(k))) for k in range(n))
-    Ln = limbs(n - 1)
-    back = coef[2] * c * n * n * Ln * Ln / 2.0 / threads
-
-    def steps_within(seconds):
-        """the number of leading steps whose fitted times sum to about `seconds`"""
-        acc, k = 0.0, 0
-        while k < n and acc < seconds:
-            acc += float(np.dot(coef, feats(k)))
-            k += 1
-        return k
-    return elim + back, dt, coef, steps_within
+    for _ in range(3):
+        cbareiss.gcd_magnitudes(a, b)
+    return (time.perf_counter() - t0) / 3
 
 
 def cpu_baseline(A, b, budget_s):
-    """The CPU oracle on the host cores: a bounded sample of this very system
-    (its first elimination steps, sized to the budget) projected to a full
-    solve; the same projection checked against a full timed oracle run of
-    the n = 256 system (from its first 6% of steps)."""
+    """The CPU oracle on the host cores for a full solve of this system: its
+    first elimination steps actually run and timed (a bounded sample of the
+    workload, sized to the budget), the remaining steps projected from the
+    oracle's measured cost per entry update at each step's operand size
+    (small entries carry memory and allocation costs that the measured first
+    steps include; large ones are bound by the limb arithmetic that the
+    per-entry timing captures).
+
+    Checked in the same run the same way on the n = 256 workload: its first
+    steps timed, the rest projected, against a full timed oracle run."""
+    import numpy as np
     from dixon_adic_lifting_amd import workloads as W
     from oracle import cbareiss
     n, c = A.shape[0], b.shape[1]
     threads = cbareiss.default_threads()
-    # steps that fit the budget: try a short prefix, then extend
-    K = min(n, 32)
-    est, dt, coef, steps_within = _oracle_projection(A, b, threads, K)
-    spent = dt
-    if K < n:
-        K = min(n, max(K + 16, steps_within(max(budget_s - spent, 1.0))))
-        est, dt, coef, _ = _oracle_projection(A, b, threads, K)
-        spent += dt
-    # validation on the n = 256 workload: projection from its first 16 of 256 steps
+    t_start = time.perf_counter()
+    log2_sigma = 0.5 * math.log2(max(1.0, float(np.mean(A.astype(np.float64) ** 2))))
+    table = _entry_cost_table(threads, _minor_limbs(n - 1, log2_sigma))
+    gcd_s = _gcd_seconds(int(_minor_limbs(n - 1, log2_sigma)))
+
+    def prefix_and_rest(A_, b_, budget, gcd_):
+        n_, c_ = A_.shape[0], b_.shape[1]
+        K = min(n_, 16)
+        while K < n_ and _project(A_, c_, threads, table, gcd_, steps=2 * K) < 0.6 * budget:
+            K *= 2
+        t0 = time.perf_counter()
+        cbareiss.run(A_, b_, threads=threads, max_steps=K)
+        measured = time.perf_counter() - t0
+        rest = _project(A_, c_, threads, table, gcd_, first=K)
+        return K, measured, rest
+
+    K, measured, rest = prefix_and_rest(A, b, budget_s, gcd_s)
+    est = measured + rest
     A3, b3 = W.generate("c3_n256_int24")
-    est3, dt3, _, _ = _oracle_projection(A3, b3, threads, 16)
+    gcd3 = _gcd_seconds(int(_minor_limbs(255, log2_sigma)))
+    K3, m3, r3 = prefix_and_rest(A3, b3, 1.0, gcd3)
     t0 = time.perf_counter()
     cbareiss.run(A3, b3, threads=threads)
     full3 = time.perf_counter() - t0
-    spent += dt3 + full3
-    return {"value": round(est * 1e3, 1), "unit": "ms per full solve (projected from the sample)",
+    est3 = m3 + r3
+    spent = time.perf_counter() - t_start
+    return {"value": round(est * 1e3, 1), "unit": "ms per full solve (first steps timed, rest projected)",
             "cores": threads, "cpu_model": cpu_model(), "kind": "oracle",
-            "sample": (f"plain-C Bareiss oracle (oracle/bareiss.c) on this {n}x{n}, c={c} system, {threads} "
-                       f"threads: first {K} of {n} elimination steps in {dt:.2f} s; per-step times fitted "
-                       f"with t_k = e_k (a + c L_k + d L_k^2) and summed over all n steps, plus a back "
-                       f"substitution term"),
-            "sample_steps": K, "sample_seconds": round(dt, 3), "cpu_seconds_spent": round(spent, 2),
-            "fit": {"a_s_per_entry": coef[0], "c_s_per_entry_limb": coef[1], "d_s_per_entry_limb2": coef[2]},
-            "validation_n256": {"projected_s": round(est3, 3), "measured_full_s": round(full3, 3),
-                                "relative_error": round((est3 - full3) / full3, 4),
-                                "sample": "first 16 of 256 steps of the c3_n256_int24 system"}}
+            "sample": (f"plain-C Bareiss oracle (oracle/bareiss.c), {threads} threads, on this {n}x{n}, c={c} "
+                       f"system: its first {K} of {n} elimination steps run and timed ({measured:.2f} s); the other "
+                       f"steps, back substitution and lowest terms projected ({rest:.1f} s) from the oracle's entry "
+                       f"update (two products, difference, exact division) timed at {len(table)} operand sizes up "
+                       f"to {table[-1][0]} limbs with every thread busy, over each step's exact entry count"),
+            "sample_steps": K, "sample_seconds": round(measured, 3), "projected_seconds": round(rest, 2),
+            "cpu_seconds_spent": round(spent, 2),
+            "check_full_n256": {"measured_s": round(full3, 3), "projected_s": round(est3, 3),
+                                "relative_error": round((est3 - full3) / full3, 4), "timed_steps": K3,
+                                "workload": "c3_n256_int24"}}
 
 
 def copy_calibration(mb):
@@ -465,6 +542,17 @@ def multi_column_block(name, warmup, steps):
            "output_check_Ax_eq_b_mod_primes": ok, "dominant_kernel": an["dominant"], "kernels": rf}
     if "lift_contract" in rf:
         out["lift_int8_mfma_frac_of_peak"] = rf["lift_contract"].get("int8_frac_of_peak")
+    # the committed counter run's int8 operations per launch, against the
+    # algorithmic count the fractions above use, and its MFMA busy share
+    cnt = mfma_counters(name)
+    if cnt:
+        E, n, c = an["info"]["live_primes"], S.n, S.c
+        algo = {"lift_contract": 2.0 * E * n * n * c, "residual": 26 * 2.0 * n * n * c}
+        for cls, v in cnt.items():
+            if cls in algo:
+                v["algorithmic_ops_per_launch"] = algo[cls]
+                v["counter_over_algorithmic"] = round(v["int8_ops_per_launch"] / algo[cls], 4)
+        out["mfma_counters"] = cnt
     del S
     return out
 

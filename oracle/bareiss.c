@@ -552,3 +552,79 @@ int oracle_dbg_gcd(const uint64_t *a, int la, const uint64_t *b, int lb, uint64_
     scratch_free(&s);
     return rc;
 }
+
+/* ------------------------------------------------------------------------
+ * Measurement hook for the CPU baseline: the wall time of one entry update of
+ * the elimination -- the two products of L-limb numbers, their difference
+ * and the exact division by an Lp-limb number -- averaged over `reps` updates
+ * on each of `nthreads` threads that run at once (so the figure includes
+ * what running every core costs each one).  The operands are arbitrary
+ * numbers of those sizes, built as multiples of the divisor so that the
+ * division is exact.  Returns the mean over the threads, in seconds.
+ */
+typedef struct {
+    int L, Lp, reps;
+    unsigned long long seed;
+    double seconds;
+} ubench_arg;
+
+static uint64_t ub_next(unsigned long long *s) {
+    /* xorshift64* */
+    *s ^= *s >> 12; *s ^= *s << 25; *s ^= *s >> 27;
+    return *s * 2685821657736338717ULL;
+}
+
+static void ub_random(bz *x, int limbs, unsigned long long *s) {
+    bz_reserve(x, limbs);
+    for (int i = 0; i < limbs; i++) x->d[i] = ub_next(s);
+    x->d[limbs - 1] |= 1ULL << 62;
+    x->len = limbs;
+    x->neg = 0;
+}
+
+static void *ubench_worker(void *p) {
+    ubench_arg *u = (ubench_arg *)p;
+    scratch s;
+    memset(&s, 0, sizeof s);
+    bz prev = {0}, f1 = {0}, f2 = {0}, akk = {0}, aik = {0}, rij = {0}, rkj = {0}, a = {0}, b = {0}, q = {0};
+    int Lf = u->L - u->Lp + 1 > 1 ? u->L - u->Lp + 1 : 1;
+    ub_random(&prev, u->Lp, &u->seed);
+    ub_random(&f1, Lf, &u->seed);
+    ub_random(&f2, Lf, &u->seed);
+    bz_mul(&akk, &prev, &f1, &s.t1);           /* akk, aik multiples of prev: the */
+    bz_mul(&aik, &prev, &f2, &s.t1);           /* difference below divides exactly */
+    ub_random(&rij, u->L, &u->seed);
+    ub_random(&rkj, u->L, &u->seed);
+    aik.neg = 1;
+    double t0 = now_s();
+    for (int r = 0; r < u->reps; r++) {
+        bz_mul(&a, &akk, &rij, &s.t1);
+        bz_mul(&b, &aik, &rkj, &s.t1);
+        bz_addsub(&a, &a, &b, -1, &s.t1);
+        bz_divexact(&q, &a, &prev, &s);
+    }
+    u->seconds = (now_s() - t0) / u->reps;
+    bz_clear(&prev); bz_clear(&f1); bz_clear(&f2); bz_clear(&akk); bz_clear(&aik);
+    bz_clear(&rij); bz_clear(&rkj); bz_clear(&a); bz_clear(&b); bz_clear(&q);
+    scratch_free(&s);
+    return NULL;
+}
+
+double oracle_entry_update_seconds(int L, int Lp, int reps, int nthreads) {
+    if (L < 1 || Lp < 1 || Lp > L || reps < 1 || nthreads < 1) return -1.0;
+    pthread_t *th = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+    ubench_arg *ua = (ubench_arg *)calloc((size_t)nthreads, sizeof(ubench_arg));
+    for (int t = 0; t < nthreads; t++) {
+        ua[t].L = L; ua[t].Lp = Lp; ua[t].reps = reps;
+        ua[t].seed = 0x9e3779b97f4a7c15ULL * (unsigned long long)(t + 1);
+        if (t > 0) pthread_create(&th[t], NULL, ubench_worker, &ua[t]);
+    }
+    ubench_worker(&ua[0]);
+    double sum = ua[0].seconds;
+    for (int t = 1; t < nthreads; t++) {
+        pthread_join(th[t], NULL);
+        sum += ua[t].seconds;
+    }
+    free(th); free(ua);
+    return sum / nthreads;
+}

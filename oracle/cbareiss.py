@@ -40,6 +40,8 @@ def _load():
         lib.oracle_solve_timed.restype = ctypes.c_int
         lib.oracle_free.argtypes = [ctypes.c_char_p]
         lib.oracle_free.restype = None
+        lib.oracle_entry_update_seconds.argtypes = [ctypes.c_int] * 4
+        lib.oracle_entry_update_seconds.restype = ctypes.c_double
         u64p = ctypes.POINTER(ctypes.c_uint64)
         for fn in (lib.oracle_dbg_divexact, lib.oracle_dbg_gcd):
             fn.argtypes = [u64p, ctypes.c_int, u64p, ctypes.c_int, u64p, ctypes.POINTER(ctypes.c_int),
@@ -132,3 +134,14 @@ def gcd_magnitudes(a: int, b: int) -> int:
     st, g = _bignum_call("oracle_dbg_gcd", a, b)
     assert st == 0
     return g
+
+
+def entry_update_seconds(limbs: int, prev_limbs: int, reps: int, threads: int) -> float:
+    """Mean wall time of one elimination entry update (two products of
+    `limbs`-limb numbers, their difference, the exact division by a
+    `prev_limbs`-limb number) with `threads` threads running at once
+    (measurement hook for the CPU baseline)."""
+    v = _load().oracle_entry_update_seconds(int(limbs), int(prev_limbs), int(reps), int(threads))
+    if v < 0:
+        raise ValueError("bad arguments")
+    return v
