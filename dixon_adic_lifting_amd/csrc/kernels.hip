@@ -836,6 +836,96 @@ __device__ __forceinline__ bool panel_packed_body(int8_t* __restrict__ S, int n,
     return true;
 }
 
+// The panel's 32 steps on the first candidates only.  The pivot of step kk
+// is the lowest listed candidate with a nonzero entry in column kk after the
+// earlier steps, so when the first T = min(nc, 64) candidates hold one for
+// every step, the pivots found among them are those of the whole list, and
+// every other row (candidate or earlier pivot) leaves the panel as
+// S'[i, Kc] = -S[i, Kc] Z, the block form the earlier pivot rows take.  One
+// wave runs the steps with no barrier: lane l holds candidate l's panel
+// bytes (byte-up residues, as in the panel below), the pivot is the lowest
+// lane of a ballot, and its row reaches every lane through readlane.
+// Nothing is written unless all 32 steps find their pivot among the T rows:
+// then the T rows go back to S (balanced), Z to Zt, and the pivots to piv,
+// rowpos and plist, and the function returns T; otherwise it returns 0 and
+// the caller runs the panel over the whole list.  Called by wave 0 only.
+__device__ __forceinline__ int panel_top_steps(int8_t* __restrict__ Sj, int pitch, int K, int nc,
+                                               const int* clist, int* __restrict__ pj, int* __restrict__ rpj,
+                                               int* plist, int8_t (*Zt)[64], const uint8_t* inv, uint32_t q,
+                                               uint32_t mq, int32_t nq8, int lane) {
+    const int T = min(nc, 64);
+    const bool mine = lane < T;
+    uint32_t W[kPanel];
+    {
+        uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (mine) {
+            const int i = clist[lane];
+            const uint4 a = *(const uint4*)(Sj + (size_t)i * pitch + K);
+            const uint4 b = *(const uint4*)(Sj + (size_t)i * pitch + K + 16);
+            w[0] = a.x, w[1] = a.y, w[2] = a.z, w[3] = a.w, w[4] = b.x, w[5] = b.y, w[6] = b.z, w[7] = b.w;
+        }
+#pragma unroll
+        for (int c = 0; c < kPanel; c++) {
+            const int x = (int)(int8_t)(w[c >> 2] >> (8 * (c & 3)));
+            W[c] = (uint32_t)(x < 0 ? x + (int)q : x) << 8;
+        }
+    }
+    bool live = mine;
+    int pcol = -1;
+    int pl[kPanel];  // the candidate index (lane) of each step's pivot
+#pragma clang loop unroll(full)
+    for (int kk = 0; kk < kPanel; kk++) {
+        const uint32_t fk = W[kk] >> 8;
+        const uint64_t m = __ballot(live && fk != 0u);
+        if (m == 0) return 0;  // no pivot among the first T candidates
+        const int p = __builtin_ctzll(m);
+        pl[kk] = p;
+        uint32_t vs[kPanel];
+#pragma unroll
+        for (int c = 0; c < kPanel; c++) vs[c] = (uint32_t)__builtin_amdgcn_readlane((int)W[c], p);
+        const uint32_t pinv = inv[vs[kk] >> 8];
+        vs[kk] = 256u;
+        const bool isp = lane == p;
+        if (isp) {
+            live = false;
+            pcol = kk;
+        }
+        // as in the panel below: base (slot kk cleared) + fac prow'
+        const uint32_t g = red_up(__umul24(fk, pinv) << 8, mq, nq8) >> 8;
+        const uint32_t fac = isp ? pinv - 1u : (g ? q - g : 0u);
+        W[kk] = 0u;
+#pragma unroll
+        for (int c = 0; c < kPanel; c++) W[c] = red_up(__umul24(fac, vs[c]) + W[c], mq, nq8);
+        W[kk] = isp ? pinv << 8 : W[kk];
+    }
+    // every step found its pivot: the T rows back to S, Z, the pivots
+    if (mine) {
+        const int i = clist[lane];
+        uint32_t w[8];
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            uint32_t o = 0;
+#pragma unroll
+            for (int bb = 0; bb < 4; bb++) {
+                const uint32_t x = W[4 * e + bb] >> 8;
+                o |= ((x > (q >> 1) ? x - q : x) & 0xffu) << (8 * bb);
+            }
+            w[e] = o;
+        }
+        *(uint4*)(Sj + (size_t)i * pitch + K) = make_uint4(w[0], w[1], w[2], w[3]);
+        *(uint4*)(Sj + (size_t)i * pitch + K + 16) = make_uint4(w[4], w[5], w[6], w[7]);
+        if (pcol >= 0) {
+#pragma unroll
+            for (int cc = 0; cc < kPanel; cc++) Zt[cc][pcol] = (int8_t)(w[cc >> 2] >> (8 * (cc & 3)));
+            pj[K + pcol] = i;
+            rpj[i] = K + pcol;
+            plist[pcol] = i;
+        }
+    }
+    (void)pl;
+    return T;
+}
+
 // The same panel with every candidate row held unpacked: one register per
 // panel byte, in byte-up form (256 x, x in [0, q)), so a step costs three
 // instructions per element (x' = 256 base + fac 256 v, then the exact
@@ -866,6 +956,21 @@ __device__ __forceinline__ bool panel_up_body(int8_t* __restrict__ S, int n, int
     ((int16_t*)&Zt[0][0])[t] = 0;
     if (t < 256) inv[t] = c_inv.inv[j][t];
     const int nc = panel_list_rows(rpj, n, clist, wsum, t, lane, wave);
+    {
+        // the steps on the first candidates alone (almost always enough);
+        // then every other row by the block formula
+        __shared__ int topT;
+        if (wave == 0) {
+            const int T = panel_top_steps(Sj, pitch, K, nc, clist, pj, rpj, plist, Zt, inv, q, mq, nq8, lane);
+            if (lane == 0) topT = T;
+        }
+        __syncthreads();
+        const int T = topT;
+        if (T > 0) {
+            panel_old_rows(Sj, n, pitch, K, T, clist, Zt, q, lane, wave);
+            return true;
+        }
+    }
 
     uint32_t W[RPT][kPanel];  // 256 x residue
     bool live[RPT];
@@ -1090,18 +1195,35 @@ __device__ __forceinline__ void update_tile(int8_t* __restrict__ S, int n, int p
     }
 }
 
-// Every column but the panel's [K, K + 32) (or the wider skipped range),
-// grid (column tiles, row tiles, primes).
+// Which 128 x 128 tile the u-th update unit on XCD x takes.  Blocks are
+// dealt to the eight XCDs round-robin by their index, and each XCD has its
+// own L2; every column tile of a row tile reads the rows' panel bytes (32
+// bytes of each row's 128-byte line), so all column tiles of a row tile go
+// to one XCD: XCD x takes the row tiles x, x + 8, ... (a row tile is one
+// prime's 128 rows), and only the transposed pivot rows GT (32 dense bytes a
+// column) are read on every XCD.  Returns false past the last row tile.
+__device__ __forceinline__ bool update_unit(int x, int u, int ntx, int nty, int* j, int* tx, int* ty) {
+    const int r = x + 8 * (u / ntx);
+    if (r >= nty * kNumPrimes) return false;
+    *tx = u % ntx;
+    *j = r / nty;
+    *ty = r % nty;
+    return true;
+}
+
+// Every column but the panel's [K, K + 32) (or the wider skipped range):
+// one 128 x 128 tile per block, 8 ntx ceil(nty 53 / 8) blocks in a row,
+// mapped to tiles by update_unit.
 __global__ __launch_bounds__(256) void gj_update_kernel(int8_t* __restrict__ S, int n, int pitch, int K,
                                                         const int* __restrict__ rowpos,
                                                         const int* __restrict__ flags,
-                                                        const int8_t* __restrict__ GT, int skip1) {
+                                                        const int8_t* __restrict__ GT, int skip1, int ntx,
+                                                        int nty) {
     __shared__ __attribute__((aligned(16))) uint8_t stage[4][64 * kUpdLS];
-    const int j = blockIdx.z;
-    if (flags[j]) return;
+    int j, tx, ty;
+    if (!update_unit(blockIdx.x & 7, blockIdx.x >> 3, ntx, nty, &j, &tx, &ty) || flags[j]) return;
     const int wave = threadIdx.x >> 6;
-    update_tile(S, n, pitch, K, rowpos, GT, j, blockIdx.x, blockIdx.y, wave, threadIdx.x & 63, stage[wave], K,
-                skip1);
+    update_tile(S, n, pitch, K, rowpos, GT, j, tx, ty, wave, threadIdx.x & 63, stage[wave], K, skip1);
 }
 
 // Panel K on its own (no other work in flight), then its pivot rows to GT.
@@ -1175,12 +1297,15 @@ __global__ __launch_bounds__(1024) void gj_panel_rest_kernel(int8_t* __restrict_
     }
     __shared__ __attribute__((aligned(16))) uint8_t stage[16][64 * kUpdLS];
     const int wave = threadIdx.x >> 6;
-    const int tile = 4 * ((int)blockIdx.x - np) + (wave >> 2);
-    const int j = tile / (ntx * nty), rem = tile % (ntx * nty);
-    if (j >= kNumPrimes || flags[j]) return;
+    // the k-th update block on XCD x (blocks are dealt round-robin from
+    // index 0, panel blocks included) takes that XCD's units 4k .. 4k + 3
+    const int x = (int)blockIdx.x & 7;
+    const int first = np + (((x - np) % 8) + 8) % 8;  // this XCD's first update block
+    const int k = ((int)blockIdx.x - first) >> 3;
+    int j, tx, ty;
+    if (!update_unit(x, 4 * k + (wave >> 2), ntx, nty, &j, &tx, &ty) || flags[j]) return;
     const int Kr = K - kPanel;
-    update_tile(S, n, pitch, Kr, rowpos, GT, j, rem % ntx, rem / ntx, wave & 3, threadIdx.x & 63, stage[wave], Kr,
-                Kr + 2 * kPanel);
+    update_tile(S, n, pitch, Kr, rowpos, GT, j, tx, ty, wave & 3, threadIdx.x & 63, stage[wave], Kr, Kr + 2 * kPanel);
 }
 
 // After panel K: its pivot rows to GT, 256 columns per block (grid
@@ -1317,10 +1442,11 @@ hipError_t launch_gj_panel(const Layout& L, uint8_t* ws, int K, hipStream_t st) 
 }
 
 hipError_t launch_gj_update(const Layout& L, uint8_t* ws, int K, hipStream_t st) {
-    dim3 grid((L.pitch + 127) / 128, (L.n + 127) / 128, kNumPrimes);
-    es_launch(gj_update_kernel, grid, dim3(256), 0, st, (int8_t*)(ws + L.off_S), L.n, L.pitch, K,
-                       (const int*)(ws + L.off_rowpos), (const int*)(ws + L.off_flags),
-                       (const int8_t*)(ws + L.off_GT), K + kPanel);
+    const int ntx = (L.pitch + 127) / 128, nty = (L.n + 127) / 128;
+    const int per_xcd = ntx * ((nty * kNumPrimes + 7) / 8);  // units (tiles) per XCD
+    es_launch(gj_update_kernel, dim3(8 * per_xcd), dim3(256), 0, st, (int8_t*)(ws + L.off_S), L.n, L.pitch, K,
+              (const int*)(ws + L.off_rowpos), (const int*)(ws + L.off_flags), (const int8_t*)(ws + L.off_GT),
+              K + kPanel, ntx, nty);
     return hipGetLastError();
 }
 
@@ -1331,7 +1457,8 @@ hipError_t launch_gj_panel_rest(const Layout& L, uint8_t* ws, int K, hipStream_t
     int* flags = (int*)(ws + L.off_flags);
     const int8_t* GT = (const int8_t*)(ws + L.off_GT);
     const int ntx = (L.pitch + 127) / 128, nty = (L.n + 127) / 128;
-    const int nupd = K > 0 ? (ntx * nty * kNumPrimes + 3) / 4 : 0;
+    // four units a block, dealt per XCD (update_unit): 8 ceil(units per XCD / 4) blocks
+    const int nupd = K > 0 ? 8 * ((ntx * ((nty * kNumPrimes + 7) / 8) + 3) / 4) : 0;
     const int np = K < L.n ? kNumPrimes : 0;
     const dim3 g(np + nupd), b(1024);
     if (np + nupd == 0) return hipSuccess;
