@@ -1961,6 +1961,68 @@ constexpr int kBufferWord3 = 0x00020000;
 constexpr int kCacheNT = 2;
 constexpr int kFusedMinThreads = kNumPrimes * (kDigitWords + 1);
 
+// The step's share of the CRT for a block's kFusedComps components (one wave:
+// sixteen lanes per component): the balanced u_l = y_l (P / q_l)^-1 mod q_l,
+// k = round(X / P) and x mod 2^64 = (acc_0 + acc_1 2^32 - k P) mod 2^64,
+// which need only the two low words of X.  The record (u_l, k) goes to
+// urec (64 bytes a component) and x mod 2^64 to xlow; the full digit is
+// formed later from the record.
+__device__ __forceinline__ void fused_crt_share(const CrtTables& T, const int (&sY)[kNumPrimes][kFusedComps],
+                                                const LiftParams* __restrict__ prm, int E, int c0, int n, int lane,
+                                                uint8_t* __restrict__ urec, uint64_t* __restrict__ xlow) {
+    static_assert(kFusedComps * kCrtLanes == 64, "one wave of CRT lanes");
+    const int s = lane & (kCrtLanes - 1), cl = lane / kCrtLanes;
+    const int comp = c0 + cl;
+    if (comp >= n) return;  // the component's sixteen lanes leave together
+    int ub[kCrtPrimesPerLane];
+    double f = 0.0, a0 = 0.0, a1 = 0.0;
+#pragma unroll
+    for (int i = 0; i < kCrtPrimesPerLane; i++) {
+        const int l = s + kCrtLanes * i;
+        ub[i] = 0;
+        if (l >= E) continue;
+        const uint32_t q = T.qc[l][0];
+        const uint32_t u = red16(mod_i32(sY[l][cl], q, T.qc[l][3]) * T.qc[l][2], q, T.qc[l][1]);
+        ub[i] = balanced(u, q);
+        f = fma((double)ub[i], T.qrec[l], f);
+        a0 = fma((double)ub[i], T.Wd[l][0], a0);
+        a1 = fma((double)ub[i], T.Wd[l][1], a1);
+    }
+    f = quad_add<8>(quad_add<4>(quad_add<2>(quad_add<1>(f))));
+    a0 = quad_add<8>(quad_add<4>(quad_add<2>(quad_add<1>(a0))));
+    a1 = quad_add<8>(quad_add<4>(quad_add<2>(quad_add<1>(a1))));
+    int64_t ki = (int64_t)rint(f);
+    const bool near = fabs(f - (double)ki) > 0.5 - 0x1p-30;
+    if (__builtin_amdgcn_ballot_w64(near) != 0) {
+        // rare: some component's X / P lies near a half-integer, so its k
+        // needs every word of X (the lanes still here take this branch)
+        double acc[kDigitWords];
+#pragma unroll
+        for (int w = 0; w < kDigitWords; w++) acc[w] = 0.0;
+#pragma unroll
+        for (int i = 0; i < kCrtPrimesPerLane; i++) {
+            const int l = min(s + kCrtLanes * i, kNumPrimes - 1);  // ub = 0 past E
+#pragma unroll
+            for (int w = 0; w < kDigitWords; w++) acc[w] = fma((double)ub[i], T.Wd[l][w], acc[w]);
+        }
+#pragma unroll
+        for (int w = 0; w < kDigitWords; w++) acc[w] = quad_add<8>(quad_add<4>(quad_add<2>(quad_add<1>(acc[w]))));
+        uint32_t x[kDigitWords];
+        ki = crt_finish(acc, f, prm, x);
+    }
+    uint8_t* rec = urec + (size_t)comp * 64;
+#pragma unroll
+    for (int i = 0; i < kCrtPrimesPerLane; i++) {
+        const int l = s + kCrtLanes * i;
+        if (l < E) rec[l] = (uint8_t)ub[i];
+    }
+    if (s == 0) {
+        rec[63] = (uint8_t)ki;
+        const uint64_t P64 = ((uint64_t)prm->Pw[1] << 32) | prm->Pw[0];
+        xlow[comp] = (uint64_t)(int64_t)a0 + ((uint64_t)(int64_t)a1 << 32) - (uint64_t)ki * P64;
+    }
+}
+
 __global__ __launch_bounds__(1024) void lift_gemv_crt_kernel(const int8_t* __restrict__ Sperm, int n, int pitch,
                                                             int E, const int8_t* __restrict__ rho,
                                                             const LiftParams* __restrict__ prm,
@@ -2068,63 +2130,7 @@ __global__ __launch_bounds__(1024) void lift_gemv_crt_kernel(const int8_t* __res
     }
     if (tid < kTabU) (&T.qc[0][0])[tid] = tabu;
     __syncthreads();
-    // The step's share of the CRT, sixteen lanes per component and the
-    // block's four components in wave 0: the balanced u_l, k = round(X / P)
-    // and x mod 2^64 = (acc_0 + acc_1 2^32 - k P) mod 2^64, which need only
-    // the two low words of X.  The full digit is formed later from the
-    // record (u_l, k) this step stores.
-    static_assert(C * kCrtLanes == 64, "one wave of CRT lanes");
-    if (wave != 0) return;
-    const int s = lane & (kCrtLanes - 1), cl = lane / kCrtLanes;
-    const int comp = c0 + cl;
-    if (comp >= n) return;  // the component's sixteen lanes leave together
-    int ub[kCrtPrimesPerLane];
-    double f = 0.0, a0 = 0.0, a1 = 0.0;
-#pragma unroll
-    for (int i = 0; i < kCrtPrimesPerLane; i++) {
-        const int l = s + kCrtLanes * i;
-        ub[i] = 0;
-        if (l >= E) continue;
-        const uint32_t q = T.qc[l][0];
-        const uint32_t u = red16(mod_i32(sY[l][cl], q, T.qc[l][3]) * T.qc[l][2], q, T.qc[l][1]);
-        ub[i] = balanced(u, q);
-        f = fma((double)ub[i], T.qrec[l], f);
-        a0 = fma((double)ub[i], T.Wd[l][0], a0);
-        a1 = fma((double)ub[i], T.Wd[l][1], a1);
-    }
-    f = quad_add<8>(quad_add<4>(quad_add<2>(quad_add<1>(f))));
-    a0 = quad_add<8>(quad_add<4>(quad_add<2>(quad_add<1>(a0))));
-    a1 = quad_add<8>(quad_add<4>(quad_add<2>(quad_add<1>(a1))));
-    int64_t ki = (int64_t)rint(f);
-    const bool near = fabs(f - (double)ki) > 0.5 - 0x1p-30;
-    if (__builtin_amdgcn_ballot_w64(near) != 0) {
-        // rare: some component's X / P lies near a half-integer, so its k
-        // needs every word of X (the whole wave takes this branch)
-        double acc[kDigitWords];
-#pragma unroll
-        for (int w = 0; w < kDigitWords; w++) acc[w] = 0.0;
-#pragma unroll
-        for (int i = 0; i < kCrtPrimesPerLane; i++) {
-            const int l = min(s + kCrtLanes * i, kNumPrimes - 1);  // ub = 0 past E
-#pragma unroll
-            for (int w = 0; w < kDigitWords; w++) acc[w] = fma((double)ub[i], T.Wd[l][w], acc[w]);
-        }
-#pragma unroll
-        for (int w = 0; w < kDigitWords; w++) acc[w] = quad_add<8>(quad_add<4>(quad_add<2>(quad_add<1>(acc[w]))));
-        uint32_t x[kDigitWords];
-        ki = crt_finish(acc, f, prm, x);
-    }
-    uint8_t* rec = urec + (size_t)comp * 64;
-#pragma unroll
-    for (int i = 0; i < kCrtPrimesPerLane; i++) {
-        const int l = s + kCrtLanes * i;
-        if (l < E) rec[l] = (uint8_t)ub[i];
-    }
-    if (s == 0) {
-        rec[63] = (uint8_t)ki;
-        const uint64_t P64 = ((uint64_t)prm->Pw[1] << 32) | prm->Pw[0];
-        xlow[comp] = (uint64_t)(int64_t)a0 + ((uint64_t)(int64_t)a1 << 32) - (uint64_t)ki * P64;
-    }
+    if (wave == 0) fused_crt_share(T, sY, prm, E, c0, n, lane, urec, xlow);
 }
 
 // The digits of a run of steps from their records: one thread per (step,
