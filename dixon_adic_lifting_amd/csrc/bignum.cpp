@@ -646,9 +646,10 @@ static int cmp_limbs(const limb_t* x, size_t nx, const limb_t* y, size_t ny) {
 // so every partial sum lies within +-2^127: formed modulo 2^128, its high
 // word read as signed is the next carry.
 template <bool EVEN>
-static void lincomb_rem_t(limb_t* x, limb_t* y, size_t n, uint64_t a, uint64_t b, uint64_t c, uint64_t d) {
+static void lincomb_rem_range(limb_t* x, limb_t* y, size_t lo, size_t hi, uint64_t a, uint64_t b, uint64_t c,
+                              uint64_t d, int64_t* cxo, int64_t* cyo) {
     int64_t cx = 0, cy = 0;
-    for (size_t i = 0; i < n; i++) {
+    for (size_t i = lo; i < hi; i++) {
         const uint64_t xi = x[i], yi = y[i];
         u128 tx, ty;
         if (EVEN) {
@@ -663,14 +664,25 @@ static void lincomb_rem_t(limb_t* x, limb_t* y, size_t n, uint64_t a, uint64_t b
         cx = (int64_t)(uint64_t)(tx >> 64);
         cy = (int64_t)(uint64_t)(ty >> 64);
     }
-    if (cx != 0 || cy != 0) throw std::logic_error("Lehmer step left a carry");
+    *cxo = cx;
+    *cyo = cy;
+}
+
+// the limbs [lo, hi) of (x, y) <- (A x + B y, C x + D y), the signed carries
+// out of limb hi - 1 returned (the sum over the range is the range's new
+// limbs plus carry 2^(64 hi))
+static void lincomb_rem_part(limb_t* x, limb_t* y, size_t lo, size_t hi, int64_t A, int64_t B, int64_t C, int64_t D,
+                             int64_t* cx, int64_t* cy) {
+    const uint64_t a = (uint64_t)(A < 0 ? -A : A), b = (uint64_t)(B < 0 ? -B : B);
+    const uint64_t c = (uint64_t)(C < 0 ? -C : C), d = (uint64_t)(D < 0 ? -D : D);
+    if (A >= 0 && B <= 0) lincomb_rem_range<true>(x, y, lo, hi, a, b, c, d, cx, cy);
+    else lincomb_rem_range<false>(x, y, lo, hi, a, b, c, d, cx, cy);
 }
 
 static void lincomb_rem(limb_t* x, limb_t* y, size_t n, int64_t A, int64_t B, int64_t C, int64_t D) {
-    const uint64_t a = (uint64_t)(A < 0 ? -A : A), b = (uint64_t)(B < 0 ? -B : B);
-    const uint64_t c = (uint64_t)(C < 0 ? -C : C), d = (uint64_t)(D < 0 ? -D : D);
-    if (A >= 0 && B <= 0) lincomb_rem_t<true>(x, y, n, a, b, c, d);
-    else lincomb_rem_t<false>(x, y, n, a, b, c, d);
+    int64_t cx, cy;
+    lincomb_rem_part(x, y, 0, n, A, B, C, D, &cx, &cy);
+    if (cx != 0 || cy != 0) throw std::logic_error("Lehmer step left a carry");
 }
 
 // (s, t) <- (a s + b t, c s + d t) for magnitudes below 2^62 (a s_i + b t_i
@@ -690,6 +702,51 @@ static size_t lincomb_mag(limb_t* s, limb_t* t, size_t n, uint64_t a, uint64_t b
     s[n] = (limb_t)cs;
     t[n] = (limb_t)ct;
     return cs || ct ? n + 1 : n;
+}
+
+// 124 bits of v (n limbs) from bit sh up (zero above the top)
+static u128 bits124_at(const limb_t* v, size_t n, size_t sh) {
+    const size_t w = sh / 64, o = sh % 64;
+    auto word = [&](size_t i) -> uint64_t { return i < n ? v[i] : 0; };
+    u128 lo = ((u128)word(w + 1) << 64) | word(w);
+    if (o) lo = (lo >> o) | ((u128)word(w + 2) << (128 - o));
+    return lo & (((u128)1 << 124) - 1);
+}
+
+// One Euclidean step in place, x <- x - q y with q = floor(x / y), for
+// trimmed x >= y > 0 whose quotient is below 2^62 (false, nothing changed,
+// otherwise).  q starts from the leading 124 bits of x and y's bits at the
+// same position: x >= xh 2^sh and y < (yh + 1) 2^sh, so floor(xh / (yh + 1))
+// never exceeds q, and with yh >= 2^63 (lengths at most 60 bits apart) it
+// falls short by at most two, which the comparisons afterwards add back
+// (for x below 2^124 the leading parts are the numbers and q is exact).
+static bool small_division_step(limb_t* x, size_t* nx, const limb_t* y, size_t ny, uint64_t* qo) {
+    const size_t bx = bits_of(x, *nx), by = bits_of(y, ny);
+    if (by == 0 || bx < by || bx - by > 60) return false;
+    const size_t sh = bx > 124 ? bx - 124 : 0;
+    const u128 xh = bits124_at(x, *nx, sh), yh = bits124_at(y, ny, sh);
+    const u128 qe = sh == 0 ? xh / yh : xh / (yh + 1);
+    if (qe >> 62) return false;
+    uint64_t q = (uint64_t)qe;
+    // x -= q y (q y <= x): multiply-subtract with a product carry and a borrow
+    uint64_t mc = 0, br = 0;
+    for (size_t i = 0; i < *nx; i++) {
+        const u128 p = (i < ny ? (u128)q * y[i] : 0) + mc;
+        mc = (uint64_t)(p >> 64);
+        const uint64_t pl = (uint64_t)p, xi = x[i];
+        const uint64_t t = xi - pl, t2 = t - br;
+        br = (uint64_t)(xi < pl) + (uint64_t)(t < br);
+        x[i] = t2;
+    }
+    if (mc != 0 || br != 0) throw std::logic_error("division step went below zero");
+    *nx = trimmed(x, *nx);
+    while (cmp_limbs(x, *nx, y, ny) >= 0) {
+        sub_in(x, *nx, y, ny);
+        *nx = trimmed(x, *nx);
+        if (++q >> 62) throw std::logic_error("division step quotient out of range");
+    }
+    *qo = q;
+    return true;
 }
 
 // The cofactor magnitudes |t0|, |t1| of the extended Euclid below: Lehmer
@@ -870,7 +927,17 @@ bool rational_reconstruct(const BigInt& a, const BigInt& M, const BigInt& N, con
                 continue;
             }
         }
-        // one Euclidean step with a full division
+        // one Euclidean step: in place when its quotient fits 62 bits
+        // (the steps near N, where a Lehmer matrix could pass it), else a
+        // full division
+        uint64_t qs;
+        if (small_division_step(r0.data(), &n0, r1.data(), n1, &qs)) {
+            std::swap(r0, r1);
+            std::swap(n0, n1);
+            tr.matrix(0, 1, 1, qs);  // (t0, t1) <- (t1, t0 + q t1)
+            t1neg = !t1neg;
+            continue;
+        }
         BigInt x, y, q, r;
         x.d.assign(r0.begin(), r0.begin() + n0);
         y.d.assign(r1.begin(), r1.begin() + n1);

@@ -430,6 +430,26 @@ BigInt assemble(const int64_t* dig, int m, const BigInt& P) {
     return X;
 }
 
+// digits [lo, hi) as sum_i x_i P^(i - lo): halves joined by one product with
+// a power of P, so the long products are balanced (and use Karatsuba)
+static BigInt assemble_range(const int64_t* dig, int lo, int hi, const std::vector<BigInt>& pw) {
+    if (hi - lo <= 8) {
+        BigInt X;
+        for (int i = hi - 1; i >= lo; i--)
+            X = add(mul(X, pw[1]),
+                    BigInt::from_twos((const uint64_t*)(dig + (size_t)i * kDigitLimbs), kDigitLimbs));
+        return X;
+    }
+    const int mid = lo + (hi - lo) / 2;
+    return add(assemble_range(dig, lo, mid, pw), mul(pw[mid - lo], assemble_range(dig, mid, hi, pw)));
+}
+
+BigInt assemble(const int64_t* dig, int m, const std::vector<BigInt>& pw) {
+    if (m < 1) return BigInt();
+    if (pw.size() < 2 || (int)pw.size() <= m / 2 + 1) return assemble(dig, m, pw.empty() ? BigInt() : pw.back());
+    return assemble_range(dig, 0, m, pw);
+}
+
 static bool verbose() {
     static const bool v = [] {
         const char* e = std::getenv("ES_VERBOSE");

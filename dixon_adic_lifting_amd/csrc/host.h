@@ -52,6 +52,8 @@ int default_threads();
 
 // X = sum_{i<m} x_i P^i from one component's digits (int64 [m][6]).
 BigInt assemble(const int64_t* dig, int m, const BigInt& P);
+// the same from the powers pw[k] = P^k, k <= m (halves joined by one product)
+BigInt assemble(const int64_t* dig, int m, const std::vector<BigInt>& pw);
 
 // Runs fn(i) for i in [0, count) on up to nthreads host threads.
 void parallel_for_each(size_t count, int nthreads, const std::function<void(size_t)>& fn);

@@ -232,7 +232,7 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
                              hipMemcpyDeviceToHost, st));
     HIPOK(hipStreamSynchronize(st));
     std::vector<BigInt> xs(sidx.size());
-    parallel_for_each(sidx.size(), nthreads, [&](size_t k) { xs[k] = assemble(sd + k * dig_comp, m, P); });
+    parallel_for_each(sidx.size(), nthreads, [&](size_t k) { xs[k] = assemble(sd + k * dig_comp, m, pw); });
     // The sample's denominators (Wang reconstruction of each X mod M; their
     // lcm is d).  With one right-hand side the first two run first, with a
     // second thread each for the cofactors, and the GPU pass starts from
@@ -419,7 +419,7 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
     // numerator outside the bound means the sample missed part of its
     // denominator).
     auto alone = [&](const int64_t* digs, BigInt* nu, BigInt* de, bool split) -> bool {
-        BigInt a = mod_floor(assemble(digs, m, P), M);
+        BigInt a = mod_floor(assemble(digs, m, pw), M);
         return rational_reconstruct(a, M, Nb, Db, nu, de, true, split);
     };
     size_t failed_total = 0;
