@@ -256,6 +256,34 @@ def test_ratrec_matches_oracle():
         assert ratrec(a, M, 1 << half, 1 << half) == dixon.rational_reconstruct(a, M, 1 << half, 1 << half)
 
 
+def test_ratrec_unbalanced_bounds_and_large_quotients():
+    """Wang's stopping point away from the middle (N and D of different
+    sizes), and remainder sequences with quotients of 2^62 and more (a full
+    division) next to the one-word steps taken in place."""
+    rng = random.Random(11)
+    P = math.prod(modular.odd_primes_below(256))
+    for k in [3, 20, 45]:
+        M = P ** k
+        bits = M.bit_length() - 2
+        for nb in (bits // 5, bits // 2, (4 * bits) // 5):
+            db = bits - nb
+            N, D = 1 << nb, 1 << db
+            for _ in range(6):
+                den = rng.randrange(1, D)
+                num = rng.randrange(-N + 1, N)
+                if math.gcd(den, M) != 1:
+                    continue
+                a = num * pow(den, -1, M) % M
+                assert ratrec(a, M, N, D) == dixon.rational_reconstruct(a, M, N, D)
+            # quotients far above 2^62 early and late in the sequence
+            for shift in (70, 200, nb // 2 + 64):
+                a = M // (1 << shift) + rng.randrange(1 << 40)
+                assert ratrec(a, M, N, D) == dixon.rational_reconstruct(a, M, N, D)
+                small = rng.randrange(1, 1 << min(db - 1, 300))
+                a = (small * ((1 << shift) + 1)) % M
+                assert ratrec(a, M, N, D) == dixon.rational_reconstruct(a, M, N, D)
+
+
 # ------------------------------------------------------------------ reconstruction stage
 
 def digits_to_words(digits):
