@@ -117,6 +117,7 @@ struct Layout {
     size_t off_pend;      // u8 [2][53][pitch]         scaled pivot rows
     size_t off_GT;        // int8 [53][pitch][32]      old pivot rows of a panel, transposed
     size_t off_flags;     // int32 [53]                singular mod q_j
+    size_t off_wq;        // int32 [n / 32 + 2][8]     blocked elimination: per panel, the update's per-XCD tile queues
     size_t off_rowmax;    // uint64 [n]                max |A_ij| per row
     size_t off_rownorm;   // double [n]                row norms^2 of A
     size_t off_colpart;   // double [ceil(n/64)][n]    column partial sums
@@ -176,6 +177,9 @@ hipError_t launch_gj_step(const Layout& L, uint8_t* ws, int k, hipStream_t st);
 // blocked form of the same elimination: 32 steps per panel launch, then one
 // MFMA update launch (residues must be balanced: launch_residues(..., true))
 constexpr int kPanel = 32;
+// rows of the blocked elimination's queue counters (one per lookahead launch)
+inline int work_queue_rows(int n) { return n / kPanel + 2; }
+int device_cu_count();
 bool blocked_inverse_fits(const Layout& L);
 hipError_t launch_gj_panel(const Layout& L, uint8_t* ws, int K, hipStream_t st);
 hipError_t launch_gj_update(const Layout& L, uint8_t* ws, int K, hipStream_t st);

@@ -73,6 +73,7 @@ Layout make_layout(int n, int c) {
     L.off_pend = take(2 * E * (size_t)L.pitch);
     L.off_GT = take(n <= 4096 ? E * (size_t)L.pitch * kPanel : 0);  // blocked elimination only
     L.off_flags = take(E * sizeof(int32_t));
+    L.off_wq = take((size_t)work_queue_rows(n) * 8 * sizeof(int32_t));
     L.off_rowmax = take((size_t)n * sizeof(uint64_t));
     L.off_rownorm = take((size_t)n * sizeof(double));
     L.off_colpart = take(nrb * n * sizeof(double));

@@ -249,6 +249,20 @@ __global__ __launch_bounds__(256) void pivot0_kernel(const uint8_t* __restrict__
     if (threadIdx.x == 0) piv[(size_t)j * (n + 1)] = smin;
 }
 
+// compute units of the current device (queried once per device)
+int device_cu_count() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int cus = 0;
+        cache[dev] = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0
+                         ? cus
+                         : 256;
+    }
+    return cache[dev];
+}
+
 hipError_t launch_residues(const int64_t* A, const Layout& L, uint8_t* ws, bool make_a32,
                            hipStream_t st, bool balanced_out) {
     // caller guarantees small (< 2^32) entries whenever make_a32 is set
@@ -259,6 +273,10 @@ hipError_t launch_residues(const int64_t* A, const Layout& L, uint8_t* ws, bool 
     else
         es_launch(residue_kernel<false>, grid, dim3(256), 0, st, A, L.n, L.pitch,
                            ws + L.off_S, (int32_t*)(ws + L.off_A32), 0, balanced_out ? 1 : 0);
+    if (balanced_out) {  // the blocked elimination's update queues start empty
+        const hipError_t e = launch_fill_u32((uint32_t*)(ws + L.off_wq), (size_t)work_queue_rows(L.n) * 8, 0u, st);
+        if (e != hipSuccess) return e;
+    }
     if (!balanced_out)  // the step-wise elimination takes its first pivot from here
         es_launch(pivot0_kernel, dim3(kNumPrimes), dim3(256), 0, st,
                            (const uint8_t*)(ws + L.off_S), L.n, L.pitch, (int*)(ws + L.off_piv));
@@ -303,6 +321,17 @@ __device__ __forceinline__ uint32_t mad_i24(uint32_t a, int32_t b, uint32_t c) {
     uint32_t r;
     asm("v_mad_i32_i24 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(b), "v"(c));
     return r;
+}
+
+// Balanced x mod q for odd q < 256 and |x| < 2^19, in full-rate operations:
+// t = x / q rounded to nearest in single precision is the nearest integer to
+// x / q, because the float product (x exact, 1 / q and the product each
+// rounded once) lies within 2^-23 2^19 / q = 2^-4 / q of x / q, while x / q,
+// q odd, lies at least 1 / (2q) from every half-integer; x - t q is then the
+// residue in [-(q - 1) / 2, (q - 1) / 2].  rq = 1 / q rounded, nq = -q.
+__device__ __forceinline__ int bal_mod_19(int x, float rq, int32_t nq) {
+    const int t = (int)__builtin_rintf((float)x * rq);
+    return (int)mad_i24((uint32_t)t, nq, (uint32_t)x);
 }
 
 // 256 (x mod q) from xs = 256 x, x < 2^16 (exact quotient, no correction)
@@ -548,9 +577,9 @@ __device__ __forceinline__ void panel_old_rows(int8_t* __restrict__ Sj, int n, i
                                                const int* clist, const int8_t (*Zt)[64], uint32_t q, int lane,
                                                int wave) {
     const int lr = lane & 15, lg = lane >> 4;
-    // |S Z| < 32 * 125^2 < 2^19: x' = x + q ceil(2^19 / q) lies in (0, 2^20)
-    const uint32_t m28 = (uint32_t)((268435456ull + q - 1) / q);
-    const int off = (int)(q * ((524288u + q - 1) / q));
+    // |S Z| <= 32 * 125^2 < 2^19
+    const float rq = 1.0f / (float)q;
+    const int32_t nq = -(int32_t)q;
     v4i_t za[2];
 #pragma unroll
     for (int a = 0; a < 2; a++) za[a] = lg < 2 ? *(const v4i_t*)(&Zt[16 * a + lr][16 * lg]) : v4i_t{0, 0, 0, 0};
@@ -565,13 +594,7 @@ __device__ __forceinline__ void panel_old_rows(int8_t* __restrict__ Sj, int n, i
             const v4i_t acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(za[a], sb, v4i_t{0, 0, 0, 0}, 0, 0, 0);
             uint32_t outw = 0;
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const uint32_t xp = (uint32_t)(off - acc[e]);
-                const uint32_t tq = __umulhi(xp << 4, m28);  // floor(xp / q)
-                const int rr = (int)(xp - tq * q);
-                const int v = rr > (int)(q >> 1) ? rr - (int)q : rr;
-                outw |= ((uint32_t)v & 0xffu) << (8 * e);
-            }
+            for (int e = 0; e < 4; e++) outw |= ((uint32_t)bal_mod_19(-acc[e], rq, nq) & 0xffu) << (8 * e);
             if (i >= 0) *(uint32_t*)(Sj + (size_t)i * pitch + K + 16 * a + 4 * lg) = outw;
         }
     }
@@ -1139,10 +1162,9 @@ __device__ __forceinline__ void update_tile(int8_t* __restrict__ S, int n, int p
     const int row0 = ty * 128 + (w4 >> 1) * 64; // and 64 rows
     if (col0 >= pitch || row0 >= n || (col0 >= skip0 && col0 + 64 <= skip1)) return;  // wave-uniform
     const uint32_t q = c_pt.q[j];
-    // |x| < 32 * 125^2 + 125 < 2^19: x' = x + q ceil(2^19 / q) lies in (0, 2^20), where
-    // ceil(2^28 / q) is an exact round-up reciprocal (20 + 8 bits of precision)
-    const uint32_t m28 = (uint32_t)((268435456ull + q - 1) / q);
-    const int off = (int)(q * ((524288u + q - 1) / q));
+    // |x| <= 32 * 125^2 + 125 < 2^19
+    const float rq = 1.0f / (float)q;
+    const int32_t nq = -(int32_t)q;
     int8_t* Sj = S + (size_t)j * n * pitch;
     const int* rpj = rowpos + (size_t)j * n;
     const int8_t* GTj = GT + (size_t)j * pitch * kPanel;
@@ -1161,15 +1183,23 @@ __device__ __forceinline__ void update_tile(int8_t* __restrict__ S, int n, int p
     // this lane's 16 columns col0 + 16 lg .. are written unless they lie in the skipped range
     const int mycol = col0 + 16 * lg;
     const bool wr = !(mycol >= skip0 && mycol < skip1);
+    // old S for rows row0 + 16 b + lr, 16 columns per lane, and the rows'
+    // pivot steps: every load of the tile is issued before the first use
+    uint4 old16[4];
+    int rp[4];
 #pragma unroll
     for (int b = 0; b < 4; b++) {
-        // old S for rows row0 + 16 b + lr, 16 columns per lane, through LDS
+        const int i = row0 + 16 * b + lr;
+        old16[b] = i < n ? *(const uint4*)(Sj + (size_t)i * pitch + mycol) : make_uint4(0, 0, 0, 0);
+        rp[b] = i < n ? rpj[i] : 0;
+    }
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+        // through LDS into the accumulator layout
         const int i = row0 + 16 * b + lr;
         const bool rowok = i < n;
-        const uint4 old16 = rowok ? *(const uint4*)(Sj + (size_t)i * pitch + mycol) : make_uint4(0, 0, 0, 0);
-        *(uint4*)(st + lr * kUpdLS + 16 * lg) = old16;
-        const int rp = rowok ? rpj[i] : 0;
-        const bool pivot_row = rp >= K && rp < K + kPanel;
+        *(uint4*)(st + lr * kUpdLS + 16 * lg) = old16[b];
+        const bool pivot_row = rp[b] >= K && rp[b] < K + kPanel;
         wave_lds_sync();
         // accumulator layout: lane holds row lr, columns 16 a + 4 lg + 0..3
 #pragma unroll
@@ -1177,15 +1207,11 @@ __device__ __forceinline__ void update_tile(int8_t* __restrict__ S, int n, int p
             const v4i_t acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(ga[a], pb[b], v4i_t{0, 0, 0, 0}, 0, 0, 0);
             const uint32_t old = *(const uint32_t*)(st + lr * kUpdLS + 16 * a + 4 * lg);
             uint32_t outw = 0;
+            const uint32_t oldw = pivot_row ? 0u : old;
 #pragma unroll
             for (int e = 0; e < 4; e++) {
-                const int so = (int)(int8_t)(old >> (8 * e));
-                const int x = (pivot_row ? 0 : so) + acc[e];
-                const uint32_t xp = (uint32_t)(x + off);
-                const uint32_t tq = __umulhi(xp << 4, m28);  // floor(xp / q)
-                const int r = (int)(xp - tq * q);
-                const int v = r > (int)(q >> 1) ? r - (int)q : r;
-                outw |= ((uint32_t)v & 0xffu) << (8 * e);
+                const int x = (int)(int8_t)(oldw >> (8 * e)) + acc[e];
+                outw |= ((uint32_t)bal_mod_19(x, rq, nq) & 0xffu) << (8 * e);
             }
             *(uint32_t*)(st + lr * kUpdLS + 16 * a + 4 * lg) = outw;
         }
@@ -1266,13 +1292,8 @@ __device__ __forceinline__ void finish_pivot_rows(int8_t* __restrict__ S, int n,
         int acc = 0;
 #pragma unroll
         for (int c = 0; c < kPanel; c++) acc += (int)mul[r][c] * (int)oldb[c][col];
-        const uint32_t q = c_pt.q[j];
-        const uint32_t m28 = (uint32_t)((268435456ull + q - 1) / q);
-        const int off = (int)(q * ((524288u + q - 1) / q));
-        const uint32_t xp = (uint32_t)(acc + off);
-        const uint32_t tq = __umulhi(xp << 4, m28);
-        const int rr = (int)(xp - tq * q);
-        Sj[(size_t)pl[r] * pitch + K + col] = (int8_t)(rr > (int)(q >> 1) ? rr - (int)q : rr);
+        const uint32_t q = c_pt.q[j];  // |acc| <= 32 * 125^2 < 2^19
+        Sj[(size_t)pl[r] * pitch + K + col] = (int8_t)bal_mod_19(acc, 1.0f / (float)q, -(int32_t)q);
     }
     __syncthreads();
 }
@@ -1287,25 +1308,39 @@ template <int RPT, bool UP>
 __global__ __launch_bounds__(1024) void gj_panel_rest_kernel(int8_t* __restrict__ S, int n, int pitch, int K,
                                                              int* __restrict__ piv, int* __restrict__ rowpos,
                                                              int* __restrict__ flags, const int8_t* __restrict__ GT,
-                                                             int ntx, int nty) {
+                                                             int ntx, int nty, int* __restrict__ wq) {
     const int np = K < n ? kNumPrimes : 0;
     if ((int)blockIdx.x < np) {
         if (K >= kPanel && !flags[blockIdx.x]) finish_pivot_rows(S, n, pitch, K, piv, blockIdx.x);
         if (UP) (void)panel_up_body<RPT>(S, n, pitch, K, piv, rowpos, flags, blockIdx.x);
         else (void)panel_packed_body<RPT>(S, n, pitch, K, piv, rowpos, flags, blockIdx.x);
-        return;
+        // then the panel's block joins the update below
     }
+    if (K < kPanel) return;  // no earlier panel to update
+    // The update of panel K - 32: each block takes four units at a time
+    // from its XCD's queue (blocks are dealt to the eight XCDs round-robin by
+    // index, and update_unit gives each XCD whole row tiles) until the queue
+    // is empty, so the CUs that ran a panel take the update's tail too.  The
+    // counters start at zero (set before the elimination); every round takes
+    // four more, so the loop ends.
     __shared__ __attribute__((aligned(16))) uint8_t stage[16][64 * kUpdLS];
+    __shared__ int s_base;
     const int wave = threadIdx.x >> 6;
-    // the k-th update block on XCD x (blocks are dealt round-robin from
-    // index 0, panel blocks included) takes that XCD's units 4k .. 4k + 3
     const int x = (int)blockIdx.x & 7;
-    const int first = np + (((x - np) % 8) + 8) % 8;  // this XCD's first update block
-    const int k = ((int)blockIdx.x - first) >> 3;
-    int j, tx, ty;
-    if (!update_unit(x, 4 * k + (wave >> 2), ntx, nty, &j, &tx, &ty) || flags[j]) return;
+    const int units = ntx * ((nty * kNumPrimes - x + 7) / 8);  // this XCD's units
+    int* qx = wq + (size_t)(K / kPanel) * 8 + x;
     const int Kr = K - kPanel;
-    update_tile(S, n, pitch, Kr, rowpos, GT, j, tx, ty, wave & 3, threadIdx.x & 63, stage[wave], Kr, Kr + 2 * kPanel);
+    for (;;) {
+        __syncthreads();  // everyone has read the previous round's base
+        if (threadIdx.x == 0) s_base = atomicAdd(qx, 4);
+        __syncthreads();
+        const int base = s_base;
+        if (base >= units) break;
+        int j, tx, ty;
+        if (update_unit(x, base + (wave >> 2), ntx, nty, &j, &tx, &ty) && !flags[j])
+            update_tile(S, n, pitch, Kr, rowpos, GT, j, tx, ty, wave & 3, threadIdx.x & 63, stage[wave], Kr,
+                        Kr + 2 * kPanel);
+    }
 }
 
 // After panel K: its pivot rows to GT, 256 columns per block (grid
@@ -1350,9 +1385,9 @@ __device__ __forceinline__ void next_cols_block(int8_t* __restrict__ S, int n, i
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int lr = lane & 15, lg = lane >> 4;
     int8_t* Sj = S + (size_t)j * n * pitch;
-    const uint32_t q = c_pt.q[j];
-    const uint32_t m28 = (uint32_t)((268435456ull + q - 1) / q);
-    const int off = (int)(q * ((524288u + q - 1) / q));
+    const uint32_t q = c_pt.q[j];  // |x| <= 32 * 125^2 + 125 < 2^19 below
+    const float rq = 1.0f / (float)q;
+    const int32_t nq = -(int32_t)q;
     const int* rpj = rowpos + (size_t)j * n;
     const int c0 = K + kPanel;
     __shared__ __attribute__((aligned(16))) int8_t prs[kPanel][kPanel];  // prs[c][col] = S[piv[K + c]][c0 + col]
@@ -1383,15 +1418,11 @@ __device__ __forceinline__ void next_cols_block(int8_t* __restrict__ S, int n, i
         const int col = c0 + 16 * a + 4 * lg;
         const uint32_t old = rowok ? *(const uint32_t*)(Sj + (size_t)i * pitch + col) : 0u;
         uint32_t outw = 0;
+        const uint32_t oldw = pivot_row ? 0u : old;
 #pragma unroll
         for (int e = 0; e < 4; e++) {
-            const int so = (int)(int8_t)(old >> (8 * e));
-            const int x = (pivot_row ? 0 : so) + acc[e];
-            const uint32_t xp = (uint32_t)(x + off);
-            const uint32_t tq = __umulhi(xp << 4, m28);
-            const int r = (int)(xp - tq * q);
-            const int v = r > (int)(q >> 1) ? r - (int)q : r;
-            outw |= ((uint32_t)v & 0xffu) << (8 * e);
+            const int x = (int)(int8_t)(oldw >> (8 * e)) + acc[e];
+            outw |= ((uint32_t)bal_mod_19(x, rq, nq) & 0xffu) << (8 * e);
         }
         // the panel's own pivot rows are read by every block of this launch
         // (prs): the next panel's block updates them (finish_pivot_rows)
@@ -1457,17 +1488,21 @@ hipError_t launch_gj_panel_rest(const Layout& L, uint8_t* ws, int K, hipStream_t
     int* flags = (int*)(ws + L.off_flags);
     const int8_t* GT = (const int8_t*)(ws + L.off_GT);
     const int ntx = (L.pitch + 127) / 128, nty = (L.n + 127) / 128;
-    // four units a block, dealt per XCD (update_unit): 8 ceil(units per XCD / 4) blocks
-    const int nupd = K > 0 ? 8 * ((ntx * ((nty * kNumPrimes + 7) / 8) + 3) / 4) : 0;
+    int* wq = (int*)(ws + L.off_wq);
+    if (K / kPanel >= work_queue_rows(L.n)) return hipErrorInvalidValue;
+    // one 1024-thread block per CU: the update blocks fill the CUs the panel
+    // blocks leave (a multiple of 8, so every XCD gets its share); they and
+    // the panel blocks drain the per-XCD queues
     const int np = K < L.n ? kNumPrimes : 0;
+    const int nupd = K >= kPanel ? std::max(8, (device_cu_count() - np + 7) / 8 * 8) : 0;
     const dim3 g(np + nupd), b(1024);
     if (np + nupd == 0) return hipSuccess;
     switch (K < L.n ? panel_kind(L, K) : 1) {
-        case 0: es_launch((gj_panel_rest_kernel<1, true>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT, ntx, nty); break;
-        case 1: es_launch((gj_panel_rest_kernel<1, false>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT, ntx, nty); break;
-        case 2: es_launch((gj_panel_rest_kernel<2, false>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT, ntx, nty); break;
-        case 5: es_launch((gj_panel_rest_kernel<2, true>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT, ntx, nty); break;
-        default: es_launch((gj_panel_rest_kernel<4, false>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT, ntx, nty); break;
+        case 0: es_launch((gj_panel_rest_kernel<1, true>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT, ntx, nty, wq); break;
+        case 1: es_launch((gj_panel_rest_kernel<1, false>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT, ntx, nty, wq); break;
+        case 2: es_launch((gj_panel_rest_kernel<2, false>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT, ntx, nty, wq); break;
+        case 5: es_launch((gj_panel_rest_kernel<2, true>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT, ntx, nty, wq); break;
+        default: es_launch((gj_panel_rest_kernel<4, false>), g, b, 0, st, S, L.n, L.pitch, K, piv, rowpos, flags, GT, ntx, nty, wq); break;
     }
     return hipGetLastError();
 }

@@ -100,6 +100,22 @@ def test_round_up_reciprocal_gives_exact_quotients():
         assert int(x[-1] << np.uint64(8)) < (1 << 24)
 
 
+def test_single_precision_rounding_gives_balanced_residues():
+    """The rank-32 updates reduce |x| < 2^19 (32 products of balanced
+    residues plus one) as x - t q with t = rint(float(x) * float(1 / q)):
+    the float product is within 2^-4 / q of x / q and x / q (q odd) is at
+    least 1 / (2q) from every half-integer, so t is the nearest integer and
+    x - t q the balanced residue.  Checked exhaustively in IEEE single
+    precision (one rounding for 1 / q, one for the product)."""
+    x = np.arange(-(1 << 19) + 1, 1 << 19, dtype=np.int64)
+    xf = x.astype(np.float32)
+    for q in es.primes():
+        rq = np.float32(1.0) / np.float32(q)
+        t = np.rint((xf * rq).astype(np.float32)).astype(np.int64)
+        assert np.abs(t).max() < (1 << 23)  # a signed 24-bit operand
+        assert np.array_equal(x - t * q, ((x + q // 2) % q) - q // 2), q
+
+
 # ------------------------------------------------------------------ bignum
 
 def to_limbs(v):
