@@ -810,10 +810,13 @@ static size_t gcd_lds_pad(const void* kernel, int blocks) {
 }
 
 // Components per gcd block: the components spread evenly over the compute
-// units, at most gmax per block (gmax + 1 waves must fit one CU).
+// units, at most gmax per block (gmax + 1 waves must fit one CU).  Three or
+// four components per CU go as two blocks of two (each Euclid wave then
+// waits for two components' runs, not four: 0.13 ms less at n = 1024).
 static int gcd_group(int rows, int gmax) {
     const int cus = device_cus();
     int G = cus > 0 ? (rows + cus - 1) / cus : 4;
+    if (G > 2 && G <= 4) G = 2;
     return G < 1 ? 1 : (G > gmax ? gmax : G);
 }
 
