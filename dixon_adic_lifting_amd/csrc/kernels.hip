@@ -1994,6 +1994,11 @@ typedef unsigned v4u __attribute__((ext_vector_type(4)));
 // and the cache-policy operand of a non-temporal load
 constexpr int kBufferWord3 = 0x00020000;
 constexpr int kCacheNT = 2;
+// L2 bytes per XCD that the fused lift's cached row batches may take: at
+// n = 1024 that is 8 of a block's 26 batches (2 MB of an XCD's 6.7 MB
+// share; 6 to 9 batches measured alike, 2.41 -> 2.35 ms for the lift; 15
+// or more thrash the 4 MB L2)
+constexpr size_t kLiftCachedBytes = (size_t)2 << 20;
 constexpr int kFusedMinThreads = kNumPrimes * (kDigitWords + 1);
 
 // The step's share of the CRT for a block's kFusedComps components (one wave:
@@ -2062,7 +2067,7 @@ __global__ __launch_bounds__(1024) void lift_gemv_crt_kernel(const int8_t* __res
                                                             int E, const int8_t* __restrict__ rho,
                                                             const LiftParams* __restrict__ prm,
                                                             uint8_t* __restrict__ urec,
-                                                            uint64_t* __restrict__ xlow) {
+                                                            uint64_t* __restrict__ xlow, int cached) {
     constexpr int C = kFusedComps, KB = kFusedBatches;
     constexpr int kTabD = kNumPrimes * (kDigitWords + 1), kTabU = kNumPrimes * 4;
     constexpr int NP = 8 / C;  // primes per batch
@@ -2121,10 +2126,14 @@ __global__ __launch_bounds__(1024) void lift_gemv_crt_kernel(const int8_t* __res
         for (int kb = 0; kb < KB; kb++) {
 #pragma unroll
             for (int p = 0; p < NP; p++) rvs[kb][p] = *(const uint4*)(rvp[kb][p] + colc);
+            // the block's first `cached` batches with plain loads, the rest
+            // non-temporal: each XCD's blocks read the same rows every step,
+            // and those then stay in its L2 from step to step
+            const bool keep = wave + nw * kb < cached;
 #pragma unroll
             for (int r = 0; r < 8; r++) {
-                // each row is read once per step: a non-temporal (streaming) load
-                const v4u t = __builtin_amdgcn_raw_buffer_load_b128(srs, colc, rowo[kb][r], kCacheNT);
+                const v4u t = keep ? __builtin_amdgcn_raw_buffer_load_b128(srs, colc, rowo[kb][r], 0)
+                                   : __builtin_amdgcn_raw_buffer_load_b128(srs, colc, rowo[kb][r], kCacheNT);
                 sv[kb][r] = make_uint4(t.x, t.y, t.z, t.w);
             }
         }
@@ -2669,10 +2678,14 @@ hipError_t launch_lift_contract_crt(const Layout& L, uint8_t* ws, int E, int slo
     const int nb = (E * kFusedComps + 7) / 8;
     const int waves = max((nb + kFusedBatches - 1) / kFusedBatches, (kFusedMinThreads + 63) / 64);
     if (slot < 0 || slot >= L.krec) return hipErrorInvalidValue;
-    es_launch(lift_gemv_crt_kernel, dim3((L.n + kFusedComps - 1) / kFusedComps), dim3(waves * 64), 0, st,
+    const int blocks = (L.n + kFusedComps - 1) / kFusedComps;
+    // cached batches a block: kLiftCachedBytes over the XCD's blocks (dealt
+    // round-robin to the eight XCDs) at 8 rows of `pitch` bytes a batch
+    const int cached = (int)std::min<size_t>((size_t)nb, kLiftCachedBytes / ((size_t)((blocks + 7) / 8) * 8 * L.pitch));
+    es_launch(lift_gemv_crt_kernel, dim3(blocks), dim3(waves * 64), 0, st,
                        (const int8_t*)(ws + L.off_Sperm), L.n, L.pitch, E, (const int8_t*)(ws + L.off_rho),
                        (const LiftParams*)(ws + L.off_params), ws + L.off_urec + (size_t)slot * L.n * 64,
-                       (uint64_t*)(ws + L.off_xlow));
+                       (uint64_t*)(ws + L.off_xlow), cached);
     return hipGetLastError();
 }
 
