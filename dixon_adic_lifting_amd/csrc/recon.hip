@@ -388,11 +388,14 @@ __device__ __forceinline__ double row_max(double C1, double D1, double C2, doubl
 // waves 0, 4, 8 and 12 share a SIMD: they run the Euclidean steps (wave 0,
 // and wave 4 when the block has more than eight components) or stay idle,
 // so that the latency-bound Euclid chains never wait behind limb work; every
-// other wave holds one component's limbs.  Up to twelve components in a
+// other wave holds one component's limbs.  A thirteenth component's limbs
+// go to wave 8, on the Euclid waves' SIMD: with that many components a
+// launch is bound by the limb waves on the other three SIMDs (four each),
+// and the Euclid waves have room.  Up to thirteen components in a
 // 1024-thread block.
-constexpr int kGcdMaxGroup = 12;
-__host__ __device__ constexpr int gcd_limb_wave(int g) { return g + 1 + g / 3; }
-__host__ __device__ constexpr int gcd_block_waves(int G) { return gcd_limb_wave(G - 1) + 1; }
+constexpr int kGcdMaxGroup = 13;
+__host__ __device__ constexpr int gcd_limb_wave(int g) { return g < 12 ? g + 1 + g / 3 : 8; }
+__host__ __device__ constexpr int gcd_block_waves(int G) { return G <= 12 ? gcd_limb_wave(G - 1) + 1 : 16; }
 static_assert(gcd_block_waves(kGcdMaxGroup) == 16, "gcd block layout");
 
 // A block serves G components.  Eight lanes of a Euclid wave serve one
@@ -422,7 +425,8 @@ __global__ __launch_bounds__(64 * gcd_block_waves(GMAX)) void gcd_kernel(const u
     if (threadIdx.x == 0 && G <= 8) sDone[0][1] = sDone[1][1] = 1;  // no second Euclid wave
 
     const bool euclid = wave == 0 || (wave == 4 && G > 8);
-    if ((wave & 3) == 0 && !euclid) {
+    const bool limb12 = wave == gcd_limb_wave(12) && G > 12;  // the thirteenth component's limb wave
+    if ((wave & 3) == 0 && !euclid && !limb12) {
         // ---- idle wave: keeps the Euclid waves' SIMD free; joins the barriers
         __syncthreads();
         for (int r = 1;; r++) {
@@ -436,7 +440,7 @@ __global__ __launch_bounds__(64 * gcd_block_waves(GMAX)) void gcd_kernel(const u
         // the two's-complement words (y's sign extended through every
         // limb), then one split pass makes them signed limbs; the carry
         // dropped off the top limb removes the extension
-        const int g = wave - 1 - wave / 4;
+        const int g = limb12 ? 12 : wave - 1 - wave / 4;
         const int j = j0 + g;
         const bool valid = g < G && j < valid_rows && status[j] < 2;
         const uint32_t ext = valid && status[j] == 1 ? 0xffffffffu : 0u;

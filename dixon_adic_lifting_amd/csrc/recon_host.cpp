@@ -152,11 +152,14 @@ GpuReconPlan plan_gpu_recon(int n, int c, int m, size_t mbits, int nbits) {
     pl.off_W = take((size_t)pl.Kpad * pl.Ncolsp);
     pl.off_WT = take((size_t)pl.Kpad * pl.Ncolsp);
     pl.off_VT = take((size_t)pl.Ncolsp * pl.NCcp * sizeof(int));
-    pl.off_Y = take((size_t)pl.NCcp * pl.nw * sizeof(uint32_t));
-    pl.off_status = take((size_t)pl.NCcp * sizeof(int));
+    // numerators, their status and the gcds for every component: the GEMM
+    // runs chunk by chunk, the gcd kernel once over all of them
+    const size_t NCp = round_up(pl.NC, 128);
+    pl.off_Y = take(NCp * pl.nw * sizeof(uint32_t));
+    pl.off_status = take(NCp * sizeof(int));
     pl.off_Dw = take((size_t)pl.NW * sizeof(uint32_t));
-    pl.off_G = take((size_t)pl.NCcp * sizeof(uint64_t));
-    pl.off_gstat = take((size_t)pl.NCcp * sizeof(int));
+    pl.off_G = take(NCp * sizeof(uint64_t));
+    pl.off_gstat = take(NCp * sizeof(int));
     pl.total = o;
     pl.ok = pl.total <= ((size_t)16 << 30);
     return pl;
@@ -342,21 +345,23 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
             HIPOK(launch_recon_gemm(S, WT, pl.Kpad, pl.NCcp, pl.Ncolsp, VT, st));
             kt->stop(ev);
             ev = kt->start(KC_RECON_OTHER);
-            HIPOK(launch_numer(VT, pl.Ncolsp, rowsum, rows, Mwd, TM, Mtop, nbits, Yd, std_, st));
+            HIPOK(launch_numer(VT, pl.Ncolsp, rowsum, rows, Mwd, TM, Mtop, nbits, Yd + j0 * nw, std_ + j0, st));
             kt->stop(ev);
             // the numerator words leave before the gcds, so the host converts
             // them while the gcd kernel runs
-            HIPOK(hipMemcpyAsync(Yh + j0 * nw, Yd, (size_t)rows * nw * sizeof(uint32_t), hipMemcpyDeviceToHost,
-                                 st));
-            HIPOK(hipMemcpyAsync(sth + j0, std_, (size_t)rows * sizeof(int), hipMemcpyDeviceToHost, st));
-            HIPOK(hipEventRecord(words_ready, st));
-            if (gpu_gcd) {
-                ev = kt->start_one(KC_RECON_GCD);
-                HIPOK(launch_gcd(Yd, nw, std_, rows, Dwd, nwd, Gd, gstd, st));
-                kt->stop(ev);
-                HIPOK(hipMemcpyAsync(Gh + j0, Gd, (size_t)rows * sizeof(uint64_t), hipMemcpyDeviceToHost, st));
-                HIPOK(hipMemcpyAsync(gsth + j0, gstd, (size_t)rows * sizeof(int), hipMemcpyDeviceToHost, st));
-            }
+            HIPOK(hipMemcpyAsync(Yh + j0 * nw, Yd + j0 * nw, (size_t)rows * nw * sizeof(uint32_t),
+                                 hipMemcpyDeviceToHost, st));
+            HIPOK(hipMemcpyAsync(sth + j0, std_ + j0, (size_t)rows * sizeof(int), hipMemcpyDeviceToHost, st));
+        }
+        HIPOK(hipEventRecord(words_ready, st));
+        if (gpu_gcd) {
+            // one launch over every component (the blocks fill the CUs in
+            // fewer rounds than chunk by chunk)
+            long ev = kt->start_one(KC_RECON_GCD);
+            HIPOK(launch_gcd(Yd, nw, std_, (int)NC, Dwd, nwd, Gd, gstd, st));
+            kt->stop(ev);
+            HIPOK(hipMemcpyAsync(Gh, Gd, NC * sizeof(uint64_t), hipMemcpyDeviceToHost, st));
+            HIPOK(hipMemcpyAsync(gsth, gstd, NC * sizeof(int), hipMemcpyDeviceToHost, st));
         }
         return ES_OK;
     };
