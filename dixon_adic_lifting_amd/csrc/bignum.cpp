@@ -451,21 +451,6 @@ BigInt pow_u(const BigInt& a, unsigned e) {
 
 // ------------------------------------------------------------------ Lehmer
 
-// Leading 62 bits of x and the bits of y at the same position.
-static void leading_pair(const BigInt& x, const BigInt& y, int64_t* xh, int64_t* yh) {
-    size_t bl = x.bit_length();
-    size_t sh = bl > 62 ? bl - 62 : 0;
-    auto extract = [&](const BigInt& v) -> uint64_t {
-        size_t w = sh / 64, s = sh % 64;
-        if (w >= v.size()) return 0;
-        uint64_t lo = v.d[w] >> s;
-        uint64_t hi = (s && w + 1 < v.size()) ? v.d[w + 1] << (64 - s) : 0;
-        return (lo | hi) & ((1ULL << 62) - 1 + (1ULL << 62));  // at most 63 bits
-    };
-    *xh = (int64_t)extract(x);
-    *yh = (int64_t)extract(y);
-}
-
 // Algorithm L inner loop: the cofactor matrix [[A, B], [C, D]] of as many
 // Euclidean steps as the leading words determine.  Returns false when not
 // even one step is certain (B == 0).
@@ -576,41 +561,6 @@ static bool lehmer_matrix2(u128 xh, u128 yh, int64_t* A, int64_t* B, int64_t* C,
     *C = c;
     *D = d;
     return b != 0;
-}
-
-// (x, y) <- (A x + B y, C x + D y) in place, for nonnegative x, y whose
-// images are nonnegative (guaranteed by Algorithm L).
-static void apply_matrix(BigInt& x, BigInt& y, int64_t A, int64_t B, int64_t C, int64_t D) {
-    const size_t n = std::max(x.size(), y.size());
-    x.d.resize(n, 0);
-    y.d.resize(n, 0);
-    lincomb_rem(x.d.data(), y.d.data(), n, A, B, C, D);
-    x.trim();
-    y.trim();
-}
-
-BigInt gcd(const BigInt& a0, const BigInt& b0) {
-    BigInt x = a0, y = b0;
-    x.neg = y.neg = false;
-    if (cmp_abs(x, y) < 0) std::swap(x, y);
-    while (!y.is_zero()) {
-        if (x.size() <= 1) {
-            uint64_t u = x.is_zero() ? 0 : x.d[0], v = y.d[0];
-            while (v) { uint64_t t = u % v; u = v; v = t; }
-            return BigInt::from_u64(u);
-        }
-        int64_t xh, yh, A, B, C, D;
-        leading_pair(x, y, &xh, &yh);
-        if (yh != 0 && lehmer_matrix(xh, yh, &A, &B, &C, &D)) {
-            apply_matrix(x, y, A, B, C, D);
-        } else {
-            BigInt r;
-            divmod_trunc(x, y, nullptr, &r);
-            x = std::move(y);
-            y = std::move(r);
-        }
-    }
-    return x;
 }
 
 BigInt lcm(const BigInt& a, const BigInt& b) {
@@ -747,6 +697,67 @@ static bool small_division_step(limb_t* x, size_t* nx, const limb_t* y, size_t n
     }
     *qo = q;
     return true;
+}
+
+// gcd by Lehmer's method on raw limbs: matrices from two-word leading parts
+// (about 62 bits a pass over the limbs), one-word quotients in place, a
+// full division only for a quotient of 2^62 or more, and the last two limbs
+// in 128-bit arithmetic.
+BigInt gcd(const BigInt& a0, const BigInt& b0) {
+    const size_t L = std::max(a0.size(), b0.size()) + 1;
+    std::vector<limb_t> r0(L, 0), r1(L, 0);
+    std::copy(a0.d.begin(), a0.d.end(), r0.begin());
+    std::copy(b0.d.begin(), b0.d.end(), r1.begin());
+    size_t n0 = a0.size(), n1 = b0.size();
+    if (cmp_limbs(r0.data(), n0, r1.data(), n1) < 0) {
+        std::swap(r0, r1);
+        std::swap(n0, n1);
+    }
+    while (n1 > 0) {
+        if (n0 <= 2) {
+            u128 u = ((u128)(n0 > 1 ? r0[1] : 0) << 64) | (n0 > 0 ? r0[0] : 0);
+            u128 v = ((u128)(n1 > 1 ? r1[1] : 0) << 64) | r1[0];
+            while (v) {
+                const u128 t = u % v;
+                u = v;
+                v = t;
+            }
+            BigInt g;
+            g.d = {(limb_t)u, (limb_t)(u >> 64)};
+            g.trim();
+            return g;
+        }
+        // the top 124 bits of r0 (n0 >= 3: at least 129 bits) and r1's at the same position
+        const size_t sh = bits_of(r0.data(), n0) - 124;
+        const u128 xh = bits124_at(r0.data(), n0, sh), yh = bits124_at(r1.data(), n1, sh);
+        int64_t A, B, C, D;
+        if (yh != 0 && lehmer_matrix2(xh, yh, &A, &B, &C, &D)) {
+            lincomb_rem(r0.data(), r1.data(), n0, A, B, C, D);  // images below the old r0
+            n1 = trimmed(r1.data(), n0);
+            n0 = trimmed(r0.data(), n0);
+            continue;
+        }
+        uint64_t q;
+        if (small_division_step(r0.data(), &n0, r1.data(), n1, &q)) {
+            std::swap(r0, r1);
+            std::swap(n0, n1);
+            continue;
+        }
+        BigInt x, y, r;
+        x.d.assign(r0.begin(), r0.begin() + n0);
+        y.d.assign(r1.begin(), r1.begin() + n1);
+        divmod_trunc(x, y, nullptr, &r);
+        std::fill(r0.begin(), r0.end(), 0);
+        std::copy(r1.begin(), r1.begin() + n1, r0.begin());
+        n0 = n1;
+        std::fill(r1.begin(), r1.end(), 0);
+        std::copy(r.d.begin(), r.d.end(), r1.begin());
+        n1 = r.size();
+    }
+    BigInt g;
+    g.d.assign(r0.begin(), r0.begin() + n0);
+    g.trim();
+    return g;
 }
 
 // The cofactor magnitudes |t0|, |t1| of the extended Euclid below: Lehmer

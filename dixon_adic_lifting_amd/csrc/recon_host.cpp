@@ -379,12 +379,16 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
         });
     };
     auto reduce = [&](const std::vector<size_t>& which) {
+        // the components whose gcd the host computes (long) are listed
+        // first, so that the pool's threads share them before the divisions
         std::vector<size_t> need;
         std::vector<uint64_t> gs;  // the distinct one-word gcds other than 1
+        for (size_t j : which)
+            if ((sth[j] == 0 || sth[j] == 1) && gsth[j] != 0) need.push_back(j);
         for (size_t j : which) {
-            if ((sth[j] != 0 && sth[j] != 1) || (gsth[j] == 0 && Gh[j] == 1)) continue;
+            if ((sth[j] != 0 && sth[j] != 1) || gsth[j] != 0 || Gh[j] == 1) continue;
             need.push_back(j);
-            if (gsth[j] == 0) gs.push_back(Gh[j]);
+            gs.push_back(Gh[j]);
         }
         std::sort(gs.begin(), gs.end());
         gs.erase(std::unique(gs.begin(), gs.end()), gs.end());

@@ -202,6 +202,16 @@ def test_bignum_gcd():
     while len(fib) < 3000:
         fib.append(fib[-1] + fib[-2])
     assert dbg(2, fib[-1], fib[-2])[0] == 1   # worst case for Euclid
+    # lengths far apart, quotients of 2^100 (a full division) and of 2^61
+    # (one in-place step), equal values, powers of two, a large shared factor
+    big = rand_int(rng, 300, signed=False) | 1
+    cases = [(rand_int(rng, 900, signed=False), rand_int(rng, 3, signed=False) | 1),
+             (big * ((1 << 100) + 7) + 3, big), (big * ((1 << 61) + 5) + 11, big),
+             (big, big), (1 << 5000, 1 << 3001), ((1 << 4000) * 3, (1 << 4100) * 9),
+             (big * rand_int(rng, 600, signed=False), big * rand_int(rng, 580, signed=False))]
+    for a, b in cases:
+        assert dbg(2, a, b)[0] == math.gcd(a, b)
+        assert dbg(2, b, a)[0] == math.gcd(a, b)
 
 
 def test_bignum_add_sub():
