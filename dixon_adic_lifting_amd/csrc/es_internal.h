@@ -227,8 +227,16 @@ hipError_t launch_transpose_offset(const uint8_t* W, int Kpad, int Ncolsp, int8_
 hipError_t launch_recon_gemm(const int8_t* S, const int8_t* WT, int Kpad, int NCcp, int Ncolsp, int* VT,
                              hipStream_t st);
 int gcd_words_per_lane(int words);  // 0 when the numbers do not fit one wave
+// group: components per block, 0 to choose it from valid_rows
 hipError_t launch_gcd(const uint32_t* Y, int nw, const int* status, int valid_rows, const uint32_t* Dw, int nwd,
-                      uint64_t* G, int* gstat, hipStream_t st);
+                      uint64_t* G, int* gstat, int group, hipStream_t st);
+// Components of the first of two gcd launches over valid_rows components
+// (valid_rows when one launch should serve them all) and, in *group, the
+// components per block both launches use.  The split falls on a whole round
+// of the CUs' resident blocks and leaves about a fifth of the rounds to the
+// second launch, so that the host can finish the first launch's components
+// while the second runs; only launches of four rounds or more are split.
+int gcd_split(int valid_rows, int nw, int nwd, int* group);
 int numer_words_per_lane(int NW);  // 0 when a numerator pass does not fit one wave
 hipError_t launch_numer(const int* V, int Ncolsp, const int* rowsum, int valid_rows, const uint32_t* Mw, int TM,
                         double Mtop, int nbits, uint32_t* Y, int* status, hipStream_t st);

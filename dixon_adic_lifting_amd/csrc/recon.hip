@@ -826,8 +826,8 @@ static int gcd_group(int rows, int gmax) {
 
 template <int CW, int GMAX>
 static void launch_gcd_as(const uint32_t* Y, int nw, const int* status, int valid_rows, const uint32_t* Dw,
-                          int nwd, uint64_t* G, int* gstat, hipStream_t st) {
-    const int grp = gcd_group(valid_rows, GMAX);
+                          int nwd, uint64_t* G, int* gstat, int group, hipStream_t st) {
+    const int grp = group > 0 ? group : gcd_group(valid_rows, GMAX);
     const int blocks = (valid_rows + grp - 1) / grp;
     const int waves = gcd_block_waves(grp);
     const size_t pad = gcd_lds_pad((const void*)gcd_kernel<CW, GMAX>, blocks);
@@ -843,18 +843,50 @@ static void launch_gcd_as(const uint32_t* Y, int nw, const int* status, int vali
 }
 
 hipError_t launch_gcd(const uint32_t* Y, int nw, const int* status, int valid_rows, const uint32_t* Dw, int nwd,
-                      uint64_t* G, int* gstat, hipStream_t st) {
+                      uint64_t* G, int* gstat, int group, hipStream_t st) {
     const int cw = gcd_words_per_lane(nw > nwd ? nw : nwd);
     if (valid_rows <= 0) return hipSuccess;
+    if (group > kGcdMaxGroup) return hipErrorInvalidValue;
     if (cw == 8)
-        launch_gcd_as<8, kGcdMaxGroup>(Y, nw, status, valid_rows, Dw, nwd, G, gstat, st);
+        launch_gcd_as<8, kGcdMaxGroup>(Y, nw, status, valid_rows, Dw, nwd, G, gstat, group, st);
     else if (cw == 16)
-        launch_gcd_as<16, kGcdMaxGroup>(Y, nw, status, valid_rows, Dw, nwd, G, gstat, st);
+        launch_gcd_as<16, kGcdMaxGroup>(Y, nw, status, valid_rows, Dw, nwd, G, gstat, group, st);
     else if (cw == 32)
-        launch_gcd_as<32, kGcdMaxGroup>(Y, nw, status, valid_rows, Dw, nwd, G, gstat, st);
+        launch_gcd_as<32, kGcdMaxGroup>(Y, nw, status, valid_rows, Dw, nwd, G, gstat, group, st);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
+}
+
+// Blocks of the gcd kernel one CU holds at once (waves and registers; the
+// LDS padding only lowers it further); 0 when the device does not say.
+template <int CW, int GMAX>
+static int gcd_blocks_per_cu(int grp) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, (const void*)gcd_kernel<CW, GMAX>,
+                                                     64 * gcd_block_waves(grp), 0) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    return nb;
+}
+
+int gcd_split(int valid_rows, int nw, int nwd, int* group) {
+    const int cw = gcd_words_per_lane(nw > nwd ? nw : nwd);
+    const int grp = gcd_group(valid_rows, kGcdMaxGroup);
+    *group = grp;
+    const int per_cu = cw == 8    ? gcd_blocks_per_cu<8, kGcdMaxGroup>(grp)
+                       : cw == 16 ? gcd_blocks_per_cu<16, kGcdMaxGroup>(grp)
+                       : cw == 32 ? gcd_blocks_per_cu<32, kGcdMaxGroup>(grp)
+                                  : 0;
+    const int cus = device_cus();
+    if (valid_rows <= 0 || per_cu <= 0 || cus <= 0) return valid_rows;
+    const long per_round = (long)cus * per_cu;  // blocks resident at once
+    const long blocks = (valid_rows + grp - 1) / grp;
+    const long rounds = (blocks + per_round - 1) / per_round;
+    if (rounds < 4) return valid_rows;
+    const long second = rounds >= 10 ? rounds / 5 : 1;
+    return (int)((rounds - second) * per_round * grp);
 }
 
 int numer_words_per_lane(int NW) {

@@ -64,6 +64,8 @@ struct ReadyEvent {
     }
 };
 thread_local ReadyEvent g_words_ready;
+// Marks the arrival on the host of the first gcd launch's results.
+thread_local ReadyEvent g_first_gcds;
 
 // little-endian 32-bit words of a nonnegative BigInt, zero-padded to nw
 void to_words(const BigInt& v, uint32_t* w, int nw) {
@@ -311,8 +313,9 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
     // weight seeds T_i = P^i d mod M (host), weight rows, GEMM, numerators
     // and gcds (GPU), results to the pinned arrays.
     bool gpu_gcd = false;
-    hipEvent_t words_ready = g_words_ready.get();
-    if (!words_ready) return ES_EHIP;
+    size_t gcd_first = NC;  // components of the first gcd launch
+    hipEvent_t words_ready = g_words_ready.get(), first_gcds = g_first_gcds.get();
+    if (!words_ready || !first_gcds) return ES_EHIP;
     auto gpu_pass = [&]() -> int {
         // the chain T_{i+1} = T_i P mod M, cut into segments that each start
         // from P^{i0} d mod M = (d mod P^{m - i0}) P^{i0} (M = P^m: the
@@ -354,14 +357,26 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
             HIPOK(hipMemcpyAsync(sth + j0, std_ + j0, (size_t)rows * sizeof(int), hipMemcpyDeviceToHost, st));
         }
         HIPOK(hipEventRecord(words_ready, st));
+        gcd_first = NC;
         if (gpu_gcd) {
-            // one launch over every component (the blocks fill the CUs in
-            // fewer rounds than chunk by chunk)
-            long ev = kt->start_one(KC_RECON_GCD);
-            HIPOK(launch_gcd(Yd, nw, std_, (int)NC, Dwd, nwd, Gd, gstd, st));
-            kt->stop(ev);
-            HIPOK(hipMemcpyAsync(Gh, Gd, NC * sizeof(uint64_t), hipMemcpyDeviceToHost, st));
-            HIPOK(hipMemcpyAsync(gsth, gstd, NC * sizeof(int), hipMemcpyDeviceToHost, st));
+            // over every component at once (the blocks fill the CUs in fewer
+            // rounds than chunk by chunk), as two launches when the blocks
+            // take many rounds: the host brings the first launch's
+            // components to lowest terms while the second runs
+            int grp = 0;
+            gcd_first = (size_t)gcd_split((int)NC, nw, nwd, &grp);
+            if (gcd_first > NC) gcd_first = NC;
+            const size_t bounds[3] = {0, gcd_first, NC};
+            for (int part = 0; part < 2; part++) {
+                const size_t j0 = bounds[part], rows = bounds[part + 1] - j0;
+                if (rows == 0) continue;
+                long ev = kt->start_one(KC_RECON_GCD);
+                HIPOK(launch_gcd(Yd + j0 * nw, nw, std_ + j0, (int)rows, Dwd, nwd, Gd + j0, gstd + j0, grp, st));
+                kt->stop(ev);
+                HIPOK(hipMemcpyAsync(Gh + j0, Gd + j0, rows * sizeof(uint64_t), hipMemcpyDeviceToHost, st));
+                HIPOK(hipMemcpyAsync(gsth + j0, gstd + j0, rows * sizeof(int), hipMemcpyDeviceToHost, st));
+                if (part == 0) HIPOK(hipEventRecord(first_gcds, st));
+            }
         }
         return ES_OK;
     };
@@ -453,11 +468,20 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
         }
         HIPOK(hipEventSynchronize(words_ready));
         convert(todo);
+        std::vector<size_t> later;  // components of the second gcd launch
+        if (gpu_gcd && gcd_first < NC) {
+            std::vector<size_t> early;
+            for (size_t j : todo) (j < gcd_first ? early : later).push_back(j);
+            HIPOK(hipEventSynchronize(first_gcds));
+            reduce(early);
+        } else {
+            later = todo;
+        }
         HIPOK(hipStreamSynchronize(st));
         if (!gpu_gcd)
             for (size_t j = 0; j < NC; j++) gsth[j] = 1;
         lap(tm ? &tm->gpu_ms : nullptr, "gpu");
-        reduce(todo);
+        reduce(later);
         std::vector<size_t> failed;
         for (size_t j : todo)
             if (sth[j] != 0 && sth[j] != 1) failed.push_back(j);

@@ -105,3 +105,31 @@ def test_gcd_groups_and_partial_blocks(n, c, seed):
         _lib.set_gpu_reconstruction(True)
     assert Xg == Xh
     assert any(q != max(qq for row in Xg for (_, qq) in row) for row in Xg for (_, q) in row) or n * c < 300
+
+
+@pytest.mark.gpu
+def test_gcds_in_two_launches():
+    """With many components the gcd blocks take several rounds of the
+    compute units, and the gcds go as two launches (the host finishes the
+    first launch's components while the second runs).  n = 48 and c = 640
+    give 30720 short components: 2364 blocks of thirteen, five rounds of two
+    blocks per compute unit, split four rounds to one.  The result must
+    match the host path, with no component reconstructed alone."""
+    n, c = 48, 640
+    A, b = W.uniform_system(n, c, 24, 41)
+    dA, db = torch.as_tensor(A).cuda(), torch.as_tensor(b).cuda()
+    try:
+        _lib.set_profiling(True)
+        Xg = es.solve_pairs(dA, db)
+        prof = _lib.kernel_profile()
+    finally:
+        _lib.set_profiling(False)
+    alone, host_gcds = _lib.last_recon_counts()
+    assert alone == 0 and 0 <= host_gcds <= 3, (alone, host_gcds)
+    assert prof["recon_gcd"][1] == 2, prof["recon_gcd"]
+    try:
+        _lib.set_gpu_reconstruction(False)
+        Xh = es.solve_pairs(dA, db)
+    finally:
+        _lib.set_gpu_reconstruction(True)
+    assert Xg == Xh
