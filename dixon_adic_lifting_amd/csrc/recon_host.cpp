@@ -286,9 +286,31 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
     }
     if (!rest_now) start_rest();
     if (bad) return ES_EINTERNAL;
-    BigInt d = sden[0];
-    for (size_t k = 1; k < nfirst; k++) d = lcm(d, sden[k]);
+    // dbase: the lcm of the denominators known so far; d, the pass's
+    // common denominator, is a multiple of it
+    BigInt dbase = sden[0];
+    for (size_t k = 1; k < nfirst; k++) dbase = lcm(dbase, sden[k]);
+    BigInt d = dbase;
     bool sample_checked = rest.empty();
+    // When the pass starts from part of the sample, d also takes the small
+    // factors the rest most often adds (2^6, and 3^2, 5^2 and 7 when they
+    // are not among the lift's primes, so that they may divide det A): a
+    // pass with a d that the whole sample's denominators divide is kept,
+    // and a component's y = d x in the bound is exact whatever multiple of
+    // its denominator d is, as long as d stays within the denominator bound
+    // (both are below the bounds that M separates).  The gcd takes the
+    // extra factors out again.
+    const BigInt Dcap = shl(BigInt::from_u64(1), (size_t)dbits);
+    auto widen = [&](const BigInt& base) {
+        if (sample_checked) return base;
+        uint64_t s = 64;
+        const uint64_t qs[3] = {3, 5, 7}, pe[3] = {9, 25, 7};
+        for (int i = 0; i < 3; i++)
+            if (!mod_floor(P, BigInt::from_u64(qs[i])).is_zero()) s *= pe[i];
+        BigInt ds = mul_small(base, (int64_t)s);
+        return cmp(ds, Dcap) <= 0 ? ds : base;
+    };
+    d = widen(dbase);
     lap(tm ? &tm->sample_ms : nullptr, "sample");
 
     uint32_t* Td = (uint32_t*)(scr + pl.off_T);
@@ -454,14 +476,19 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
             rest_join.join();
             sample_checked = true;
             if (bad) return ES_EINTERNAL;
-            BigInt dall = d;
-            for (size_t k = nfirst; k < sden.size(); k++) dall = lcm(dall, sden[k]);
+            for (size_t k = nfirst; k < sden.size(); k++) dbase = lcm(dbase, sden[k]);
+            const BigInt dall = lcm(d, dbase);
             if (cmp(dall, d) != 0) {
-                // the first samples missed part of the denominator: this
-                // pass is dropped and run again with the whole sample's lcm
-                if (verbose()) fprintf(stderr, "[es] gpu reconstruct: the sample widened d, pass again\n");
+                // d missed part of the sample's denominators: this pass is
+                // dropped and run again with their lcm (with d's extra
+                // factors while that stays within the bound)
+                if (verbose()) {
+                    const BigInt f = divexact(dall, d);
+                    fprintf(stderr, "[es] gpu reconstruct: the sample widened d by a %zu-bit factor (%llu if one word), pass again\n",
+                            f.bit_length(), f.size() == 1 ? (unsigned long long)f.d[0] : 0ULL);
+                }
                 HIPOK(hipStreamSynchronize(st));
-                d = dall;
+                d = cmp(dall, Dcap) <= 0 ? dall : dbase;
                 pass--;
                 continue;
             }
@@ -504,12 +531,15 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
             if (bad) return ES_EINTERNAL;
             break;
         }
-        // many left: widen d by the first one's denominator and run them again
+        // many left: d becomes the lcm of the known denominators and the
+        // first one's (any extra factors dropped: they may have pushed the
+        // numerators past the bound), and they run again
         rc = fetch(std::vector<size_t>{failed[0]}, &digs);
         if (rc != ES_OK) return rc;
         BigInt nu, de;
         if (!alone(digs.data(), &nu, &de, true)) return ES_EINTERNAL;
-        d = lcm(d, de);
+        dbase = lcm(dbase, de);
+        d = dbase;
         todo.swap(failed);
     }
     if (verbose())
