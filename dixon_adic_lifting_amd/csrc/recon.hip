@@ -198,6 +198,7 @@ __global__ __launch_bounds__(256) void transpose_offset_kernel(const uint8_t* __
 // column counts are multiples of 128 and Kpad of 64 (the caller pads), so
 // nothing is bounds-checked.
 typedef int v4i __attribute__((ext_vector_type(4)));
+static int device_cus();
 
 constexpr int kGemmLds = 64 + 16;  // LDS row stride, bytes
 
@@ -760,9 +761,135 @@ hipError_t launch_transpose_offset(const uint8_t* W, int Kpad, int Ncolsp, int8_
     return hipGetLastError();
 }
 
+// Large products: block tile 256 x 256, four waves in a 2 x 2 arrangement,
+// each owning 128 x 128 as 8 x 8 MFMA tiles (256 accumulators a lane, one
+// wave a SIMD), so a block reads half the operand bytes per product of the
+// 128 x 128 kernel, whose operand traffic from L2 bounds it.  The chunks of
+// 64 bytes of k go through two LDS buffers.  While chunk k's products run
+// (row by row), each fragment register is refilled with chunk k + 1's
+// fragment from the other buffer right after its last product (the A
+// fragment of row i after that row, the B fragments during the last row),
+// so the LDS reads hide behind the products without a second register set;
+// chunk k + 2 goes from registers into chunk k's buffer (free since the
+// previous barrier) and chunk k + 3 is loaded from memory.  One barrier a
+// chunk.  Same operand and output lane layouts as above; rows and columns
+// are multiples of 256.
+constexpr int kBigTile = 256;
+constexpr size_t kBigLds = (size_t)2 * 2 * kBigTile * kGemmLds;
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void recon_gemm_big_kernel(
+    const int8_t* __restrict__ S, const int8_t* __restrict__ WT, int Kpad, int Ncolsp, int* __restrict__ V) {
+    extern __shared__ __attribute__((aligned(16))) int8_t lds[];
+    int8_t* As = lds;                               // [2][256][kGemmLds]
+    int8_t* Bs = lds + 2 * kBigTile * kGemmLds;     // [2][256][kGemmLds]
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int wr = wave >> 1, wc = wave & 1;
+    const int j0 = blockIdx.x * kBigTile, c0 = blockIdx.y * kBigTile;
+    const int lr = lane & 15, lg = lane >> 4;
+    // global -> registers -> LDS: thread t moves rows t / 4 + 64 q (q < 4),
+    // 16-byte piece t % 4, of both operands
+    const int gr = t >> 2, gc = (t & 3) * 16;
+    const int8_t* Ag = S + (size_t)(j0 + gr) * Kpad + gc;
+    const int8_t* Bg = WT + (size_t)(c0 + gr) * Kpad + gc;
+    const size_t q64 = (size_t)64 * Kpad;
+    const int nk = Kpad / 64;
+    v4i ra[4], rb[4];
+    // past the last chunk a load repeats the last chunk (never used)
+    auto gload = [&](int kc) {
+        kc = min(kc, nk - 1);
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            ra[q] = *(const v4i*)(Ag + q * q64 + 64 * kc);
+            rb[q] = *(const v4i*)(Bg + q * q64 + 64 * kc);
+        }
+    };
+    auto lstore = [&](int buf) {
+        int8_t* a = As + buf * kBigTile * kGemmLds;
+        int8_t* b = Bs + buf * kBigTile * kGemmLds;
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            *(v4i*)(a + (gr + 64 * q) * kGemmLds + gc) = ra[q];
+            *(v4i*)(b + (gr + 64 * q) * kGemmLds + gc) = rb[q];
+        }
+    };
+    // this wave's fragment rows in buffer `buf`
+    auto afrag = [&](int buf, int i) {
+        return *(const v4i*)(As + buf * kBigTile * kGemmLds + (128 * wr + 16 * i + lr) * kGemmLds + 16 * lg);
+    };
+    auto bfrag = [&](int buf, int i) {
+        return *(const v4i*)(Bs + buf * kBigTile * kGemmLds + (128 * wc + 16 * i + lr) * kGemmLds + 16 * lg);
+    };
+    v4i acc[8][8];
+#pragma unroll
+    for (int a = 0; a < 8; a++)
+#pragma unroll
+        for (int b = 0; b < 8; b++) acc[a][b] = v4i{0, 0, 0, 0};
+    v4i fa[8], fb[8];
+    gload(0);
+    lstore(0);
+    gload(1);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 8; i++) fa[i] = afrag(0, i);
+#pragma unroll
+    for (int i = 0; i < 8; i++) fb[i] = bfrag(0, i);
+    lstore(1);
+    gload(2);
+    __syncthreads();
+    // entering chunk kc: its fragments in fa / fb, chunk kc + 1 in buffer
+    // (kc + 1) & 1, chunk kc + 2 in ra / rb
+    for (int kc = 0; kc < nk; kc++) {
+        const int cur = kc & 1, nxt = cur ^ 1;
+        if (kc + 2 < nk) lstore(cur);
+        gload(kc + 3);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 7; i++) {
+#pragma unroll
+            for (int jj = 0; jj < 8; jj++)
+                acc[i][jj] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fb[jj], acc[i][jj], 0, 0, 0);
+            fa[i] = afrag(nxt, i);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int jj = 0; jj < 8; jj++) {
+            acc[7][jj] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[7], fb[jj], acc[7][jj], 0, 0, 0);
+            fb[jj] = bfrag(nxt, jj);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        fa[7] = afrag(nxt, 7);
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+#pragma unroll
+        for (int jj = 0; jj < 8; jj++) {
+            const int col = c0 + 128 * wc + 16 * jj + lr;
+            const int j = j0 + 128 * wr + 16 * i + 4 * lg;
+#pragma unroll
+            for (int r = 0; r < 4; r++) V[(size_t)(j + r) * Ncolsp + col] = acc[i][jj][r];
+        }
+}
+
 hipError_t launch_recon_gemm(const int8_t* S, const int8_t* WT, int Kpad, int NCcp, int Ncolsp, int* V,
                              hipStream_t st) {
-    // component tiles vary fastest, so the blocks in flight share weight tiles
+    if (NCcp % 128 != 0 || Ncolsp % 128 != 0 || Kpad % 64 != 0) return hipErrorInvalidValue;
+    // the 256 x 256 tiles once they give every CU two blocks or more
+    static int big_ok = -1;
+    if (big_ok < 0)
+        big_ok = hipFuncSetAttribute((const void*)recon_gemm_big_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)kBigLds) == hipSuccess
+                     ? 1
+                     : 0;
+    (void)hipGetLastError();
+    const int cus = device_cus();
+    if (big_ok && cus > 0 && NCcp % kBigTile == 0 && Ncolsp % kBigTile == 0 &&
+        (long)(NCcp / kBigTile) * (Ncolsp / kBigTile) >= 2L * cus) {
+        // component tiles vary fastest, so the blocks in flight share weight tiles
+        es_launch(recon_gemm_big_kernel, dim3(NCcp / kBigTile, Ncolsp / kBigTile), dim3(256), kBigLds, st, S, WT,
+                  Kpad, Ncolsp, V);
+        return hipGetLastError();
+    }
     es_launch(recon_gemm_kernel, dim3(NCcp / 128, Ncolsp / 128), dim3(256), 0, st, S, WT, Kpad, Ncolsp, V);
     return hipGetLastError();
 }

@@ -136,7 +136,7 @@ GpuReconPlan plan_gpu_recon(int n, int c, int m, size_t mbits, int nbits) {
     if (pl.TM < 2 || wchain_words_per_lane(pl.NW) == 0 || numer_words_per_lane(pl.NW) == 0 || 48 * (size_t)m > 65536 ||
         pl.nw > pl.NW)
         return pl;
-    pl.Ncolsp = (int)round_up((size_t)4 * pl.NW, 128);
+    pl.Ncolsp = (int)round_up((size_t)4 * pl.NW, 256);
     pl.Kpad = (int)round_up((size_t)48 * m, 192);
     pl.NCc = (int)std::min<size_t>(pl.NC, 8192);
     pl.NCcp = (int)round_up((size_t)pl.NCc, 128);

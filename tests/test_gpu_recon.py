@@ -133,3 +133,23 @@ def test_gcds_in_two_launches():
     finally:
         _lib.set_gpu_reconstruction(True)
     assert Xg == Xh
+
+
+@pytest.mark.gpu
+def test_large_numerator_product_tiles():
+    """n = 1024, c = 8: 8192 components against weight rows of about 6900
+    bytes, enough 256 x 256 tiles to give every compute unit two blocks, so
+    the numerators come from the large-tile product kernel.  Every component
+    must be accepted on the GPU (a wrong product sends components outside
+    the bound) and match the host path."""
+    A, b = W.uniform_system(1024, 8, 24, 43)
+    dA, db = torch.as_tensor(A).cuda(), torch.as_tensor(b).cuda()
+    Xg = es.solve_pairs(dA, db)
+    alone, host_gcds = _lib.last_recon_counts()
+    assert alone == 0 and 0 <= host_gcds <= 3, (alone, host_gcds)
+    try:
+        _lib.set_gpu_reconstruction(False)
+        Xh = es.solve_pairs(dA, db)
+    finally:
+        _lib.set_gpu_reconstruction(True)
+    assert Xg == Xh

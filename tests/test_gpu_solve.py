@@ -115,6 +115,10 @@ def test_solve_c5():
     assert torch.cuda.memory_allocated() == alloc0
     assert free0 - free1 < (2 << 20), (free0, free1)
     assert len(X) == 2048 and len(X[0]) == 16
+    # every numerator came out of the GPU pass (a wrong product would push
+    # components outside the bound and onto the host)
+    alone, _ = _lib.last_recon_counts()
+    assert alone == 0, alone
     assert_normal_form(X)
     assert exact_limb_check(A, b, X)
 
