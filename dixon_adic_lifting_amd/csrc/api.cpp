@@ -530,7 +530,7 @@ int es_solution_get(const es_solution* s, int32_t i, int32_t k, int* num_sign, c
     if (i < 0 || i >= s->data.n || k < 0 || k >= s->data.c) return ES_EINVAL;
     const size_t idx = (size_t)i * s->data.c + k;
     const BigInt& nu = s->data.num[idx];
-    const BigInt& de = s->data.den[idx];
+    const BigInt& de = s->data.den(idx);
     *num_sign = nu.is_zero() ? 0 : (nu.neg ? -1 : 1);
     *num = nu.d.data();
     *num_len = (int32_t)nu.size();

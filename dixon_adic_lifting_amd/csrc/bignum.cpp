@@ -418,6 +418,13 @@ BigInt divexact_u64(const BigInt& a, uint64_t b) {
     if (b == 0) throw std::domain_error("division by zero");
     const int t = __builtin_ctzll(b);
     const uint64_t bo = b >> t;
+    if (bo == 1) {
+        // a power of two: a shift
+        if (!a.is_zero() && (a.d[0] & (b - 1))) throw std::logic_error("inexact division");
+        BigInt q = shr_abs(a, (size_t)t);
+        q.neg = a.neg && !q.is_zero();
+        return q;
+    }
     uint64_t inv = bo;
     for (int i = 0; i < 5; i++) inv *= 2 - bo * inv;
     const size_t n = a.size();

@@ -321,75 +321,92 @@ int default_threads() {
 // A pool of worker threads started on first use and kept for the life of
 // the process (thread start-up costs far more than the short host phases of
 // a solve).  One job at a time: a caller that finds the pool busy, or that
-// is itself a pool worker, runs its loop alone.  The first exception thrown
-// by the loop body is rethrown in the caller.
+// is itself a pool worker, runs its loop alone.  The caller works on its
+// own job and returns once every item is done, without waiting for workers
+// that have not woken yet (a wake-up can take tens of microseconds): items
+// are claimed through a ticket that carries the job's generation, so a late
+// worker finds the ticket moved on and claims nothing.  The first exception
+// thrown by the loop body is rethrown in the caller (the items after it are
+// skipped).
 namespace {
 thread_local bool t_pool_worker = false;
 
 struct ThreadPool {
     std::mutex mu, serial;
     std::condition_variable cv_work, cv_done;
-    uint64_t generation = 0;
+    uint32_t gen = 0;  // current job (under mu)
     const std::function<void(size_t)>* job = nullptr;
     size_t count = 0;
-    std::atomic<size_t> next{0};
-    int busy = 0;
-    int nworkers;
+    std::atomic<uint64_t> ticket{0};  // gen << 32 | next item
+    std::atomic<size_t> done{0};      // items of the current job finished or skipped
+    std::atomic<bool> stop{false};
     std::exception_ptr error;
 
-    explicit ThreadPool(int n) : nworkers(n) {
+    explicit ThreadPool(int n) {
         for (int i = 0; i < n; i++) std::thread([this] { run(); }).detach();
     }
-    void drain(const std::function<void(size_t)>& f, size_t cnt) {
+    // claims and runs items of job g until none is left
+    void drain(uint32_t g, const std::function<void(size_t)>* f, size_t cnt) {
         for (;;) {
-            const size_t i = next.fetch_add(1);
-            if (i >= cnt) break;
-            try {
-                f(i);
-            } catch (...) {
+            uint64_t t = ticket.load(std::memory_order_acquire);
+            if ((uint32_t)(t >> 32) != g || (size_t)(uint32_t)t >= cnt) return;
+            if (!ticket.compare_exchange_weak(t, t + 1, std::memory_order_acq_rel)) continue;
+            if (!stop.load(std::memory_order_relaxed)) {
+                try {
+                    (*f)((size_t)(uint32_t)t);
+                } catch (...) {
+                    std::lock_guard<std::mutex> lk(mu);
+                    if (!error) error = std::current_exception();
+                    stop = true;
+                }
+            }
+            if (done.fetch_add(1, std::memory_order_acq_rel) + 1 == cnt) {
                 std::lock_guard<std::mutex> lk(mu);
-                if (!error) error = std::current_exception();
-                next = cnt;  // stop handing out work
+                cv_done.notify_all();
             }
         }
     }
     void run() {
         t_pool_worker = true;
-        uint64_t seen = 0;
+        uint32_t seen = 0;
         for (;;) {
             const std::function<void(size_t)>* f;
             size_t cnt;
+            uint32_t g;
             {
                 std::unique_lock<std::mutex> lk(mu);
-                cv_work.wait(lk, [&] { return generation != seen; });
-                seen = generation;
+                cv_work.wait(lk, [&] { return gen != seen; });
+                seen = g = gen;
                 f = job;
                 cnt = count;
             }
-            drain(*f, cnt);
-            std::lock_guard<std::mutex> lk(mu);
-            if (--busy == 0) cv_done.notify_all();
+            // *f is only used for an item claimed under generation g, and
+            // the caller waits for every such item: it is still alive then
+            drain(g, f, cnt);
         }
     }
     // false when the pool is busy with another caller's job
     bool parallel(size_t cnt, const std::function<void(size_t)>& f) {
+        if (cnt >= ((size_t)1 << 32)) return false;
         std::unique_lock<std::mutex> one(serial, std::try_to_lock);
         if (!one.owns_lock()) return false;
+        uint32_t g;
         {
             std::lock_guard<std::mutex> lk(mu);
             job = &f;
             count = cnt;
-            next = 0;
-            busy = nworkers;
+            done = 0;
+            stop = false;
             error = nullptr;
-            generation++;
+            g = ++gen;
+            ticket.store((uint64_t)g << 32, std::memory_order_release);
         }
         cv_work.notify_all();
-        drain(f, cnt);
+        drain(g, &f, cnt);
         std::exception_ptr e;
         {
             std::unique_lock<std::mutex> lk(mu);
-            cv_done.wait(lk, [&] { return busy == 0; });
+            cv_done.wait(lk, [&] { return done.load(std::memory_order_acquire) >= cnt; });
             e = error;
             error = nullptr;
         }
@@ -530,7 +547,9 @@ int reconstruct(const int64_t* digits, size_t stride_m, int n, int c, int m, con
     out->n = n;
     out->c = c;
     out->num.assign(NC, BigInt());
-    out->den.assign(NC, BigInt());
+    out->dens.assign(1, d);  // entry 0: d itself
+    out->den_of.assign(NC, 0);
+    std::vector<BigInt> own(NC);  // a component's own denominator (when not d)
     std::vector<char> failed(NC, 0);
     parallel_for(NC, nthreads, [&](size_t j) {
         BigInt y = mod_floor(mul(d, X[j]), M);
@@ -540,16 +559,23 @@ int reconstruct(const int64_t* digits, size_t stride_m, int n, int c, int m, con
             return;
         }
         BigInt g = gcd(y, d);
+        if (g.size() == 1 && g.d[0] == 1) {
+            out->num[j] = y;
+            return;
+        }
         out->num[j] = divexact(y, g);
-        out->den[j] = divexact(d, g);
+        own[j] = divexact(d, g);
     });
     lap("numerators");
     for (size_t j = 0; j < NC; j++) {
-        if (!failed[j]) continue;
-        BigInt a = mod_floor(X[j], M), nu, de;
-        if (!rational_reconstruct(a, M, Nb, Db, &nu, &de)) return ES_EINTERNAL;
-        out->num[j] = nu;
-        out->den[j] = de;
+        if (failed[j]) {
+            BigInt a = mod_floor(X[j], M), nu;
+            if (!rational_reconstruct(a, M, Nb, Db, &nu, &own[j])) return ES_EINTERNAL;
+            out->num[j] = nu;
+        }
+        if (own[j].is_zero()) continue;
+        out->den_of[j] = (uint32_t)out->dens.size();
+        out->dens.push_back(std::move(own[j]));
     }
     return ES_OK;
 }

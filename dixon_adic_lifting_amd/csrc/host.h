@@ -13,7 +13,12 @@ namespace es {
 
 struct SolutionData {
     int n = 0, c = 0;
-    std::vector<BigInt> num, den;  // [n*c], lowest terms, den > 0
+    std::vector<BigInt> num;  // [n*c], lowest terms
+    // the denominators (> 0): component j's is dens[den_of[j]], so that the
+    // components sharing one (most of them, as a rule) share its limbs
+    std::vector<BigInt> dens;
+    std::vector<uint32_t> den_of;  // [n*c]
+    const BigInt& den(size_t j) const { return dens[den_of[j]]; }
     int live = 0, m = 0, nbits = 0, dbits = 0;
     int mbits = 0;  // bit length of M = P^m
 };

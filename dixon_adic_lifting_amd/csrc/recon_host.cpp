@@ -408,11 +408,13 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
     // where the gcd is not 1.
     std::atomic<size_t> host_gcds{0};
     auto convert = [&](const std::vector<size_t>& which) {
+        const uint32_t di = (uint32_t)out->dens.size();  // this pass's d
+        out->dens.push_back(d);
         parallel_for_each(which.size(), nthreads, [&](size_t k) {
             const size_t j = which[k];
             if (sth[j] != 0 && sth[j] != 1) return;
             out->num[j] = from_words(Yh + j * nw, nw, sth[j] == 1);
-            out->den[j] = d;
+            out->den_of[j] = di;
         });
     };
     auto reduce = [&](const std::vector<size_t>& which) {
@@ -429,27 +431,38 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
         }
         std::sort(gs.begin(), gs.end());
         gs.erase(std::unique(gs.begin(), gs.end()), gs.end());
-        std::vector<BigInt> dg(gs.size());  // d / g for each of them
-        parallel_for_each(gs.size(), nthreads, [&](size_t k) { dg[k] = divexact_u64(d, gs[k]); });
+        // d / g for each of them (a few: on this thread), as new entries of
+        // the denominator table
+        const size_t base = out->dens.size();
+        out->dens.resize(base + gs.size());
+        parallel_for_each(gs.size(), gs.size() <= 8 ? 1 : nthreads,
+                          [&](size_t k) { out->dens[base + k] = divexact_u64(d, gs[k]); });
+        std::vector<BigInt> own(need.size());  // denominators of the host gcds
         parallel_for_each(need.size(), nthreads, [&](size_t k) {
             const size_t j = need[k];
             if (gsth[j] == 0) {
                 out->num[j] = divexact_u64(out->num[j], Gh[j]);
-                out->den[j] = dg[(size_t)(std::lower_bound(gs.begin(), gs.end(), Gh[j]) - gs.begin())];
+                out->den_of[j] = (uint32_t)(base + (size_t)(std::lower_bound(gs.begin(), gs.end(), Gh[j]) - gs.begin()));
                 return;
             }
             const BigInt g = gcd(out->num[j], d);
             host_gcds++;
             if (g.size() == 1 && g.d[0] == 1) return;
             out->num[j] = divexact(out->num[j], g);
-            out->den[j] = divexact(d, g);
+            own[k] = divexact(d, g);
         });
+        for (size_t k = 0; k < need.size(); k++) {
+            if (own[k].is_zero()) continue;
+            out->den_of[need[k]] = (uint32_t)out->dens.size();
+            out->dens.push_back(std::move(own[k]));
+        }
     };
 
     out->n = pl.n;
     out->c = pl.c;
     out->num.assign(NC, BigInt());
-    out->den.assign(NC, BigInt());
+    out->dens.clear();
+    out->den_of.assign(NC, 0);
     std::vector<size_t> todo(NC);
     for (size_t j = 0; j < NC; j++) todo[j] = j;
     // Digits of the listed components, copied to the host on the solve's stream.
@@ -522,13 +535,17 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
             rc = fetch(failed, &digs);
             if (rc != ES_OK) return rc;
             std::atomic<int> bad{0};
+            std::vector<BigInt> own(failed.size());
             parallel_for_each(failed.size(), nthreads, [&](size_t k) {
-                BigInt nu, de;
-                if (!alone(digs.data() + k * dig_comp, &nu, &de, 4 * failed.size() <= (size_t)nthreads)) bad = 1;
+                BigInt nu;
+                if (!alone(digs.data() + k * dig_comp, &nu, &own[k], 4 * failed.size() <= (size_t)nthreads)) bad = 1;
                 out->num[failed[k]] = nu;
-                out->den[failed[k]] = de;
             });
             if (bad) return ES_EINTERNAL;
+            for (size_t k = 0; k < failed.size(); k++) {
+                out->den_of[failed[k]] = (uint32_t)out->dens.size();
+                out->dens.push_back(std::move(own[k]));
+            }
             break;
         }
         // many left: d becomes the lcm of the known denominators and the

@@ -231,9 +231,15 @@ def test_divexact_one_word():
             if rng.random() < 0.3:
                 b = (b << rng.randrange(8)) % (1 << 64) or 2
             assert dbg(5, a * b, b)[0] == a
+    # powers of two (a shift), signed quotients, and limb-boundary shifts
+    for la in [0, 1, 2, 7, 300]:
+        for t in [0, 1, 6, 31, 63]:
+            a = rand_int(rng, la)
+            for sgn in (1, -1):
+                assert dbg(5, sgn * a << t, 1 << t)[0] == sgn * a
     # not exact, or b wider than one limb: refused
     L = ctypes.CDLL(_lib.LIB_PATH)
-    for a, b in [(7, 2), (3 << 70, 1 << 65), (10, 0)]:
+    for a, b in [(7, 2), (3 << 70, 1 << 65), (10, 0), ((1 << 200) + 32, 64), ((1 << 100) + 1, 2)]:
         pa, la_ = arr(to_limbs(a))
         pb, lb_ = arr(to_limbs(b))
         r = (ctypes.c_uint64 * 64)()
