@@ -292,25 +292,30 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
     for (size_t k = 1; k < nfirst; k++) dbase = lcm(dbase, sden[k]);
     BigInt d = dbase;
     bool sample_checked = rest.empty();
-    // When the pass starts from part of the sample, d also takes the small
-    // factors the rest most often adds (2^6, and 3^2, 5^2 and 7 when they
-    // are not among the lift's primes, so that they may divide det A): a
-    // pass with a d that the whole sample's denominators divide is kept,
-    // and a component's y = d x in the bound is exact whatever multiple of
-    // its denominator d is, as long as d stays within the denominator bound
-    // (both are below the bounds that M separates).  The gcd takes the
-    // extra factors out again.
+    // d also takes the small factors a sample most often misses: a
+    // component's y = d x in the bound is exact whatever multiple of its
+    // denominator d is, as long as d stays within the denominator bound
+    // (both are below the bounds that M separates), and the gcd takes the
+    // extra factors out again.  When the pass starts from part of the
+    // sample, 2^6, and 3^2, 5^2 and 7 when they are not among the lift's
+    // primes (so that they may divide det A): a pass whose d the whole
+    // sample's denominators divide is kept.  Otherwise (the whole sample
+    // comes first) 2^2: on random systems with sixteen right-hand sides the
+    // sample's lcm lacked a factor 2 of other components' denominators in
+    // about one system in twenty, and 2^2 keeps the one-word gcds
+    // d / (denominator) well inside 64 bits.
     const BigInt Dcap = shl(BigInt::from_u64(1), (size_t)dbits);
-    auto widen = [&](const BigInt& base) {
-        if (sample_checked) return base;
-        uint64_t s = 64;
-        const uint64_t qs[3] = {3, 5, 7}, pe[3] = {9, 25, 7};
-        for (int i = 0; i < 3; i++)
-            if (!mod_floor(P, BigInt::from_u64(qs[i])).is_zero()) s *= pe[i];
-        BigInt ds = mul_small(base, (int64_t)s);
-        return cmp(ds, Dcap) <= 0 ? ds : base;
-    };
-    d = widen(dbase);
+    {
+        uint64_t s = 4;
+        if (!sample_checked) {
+            s = 64;
+            const uint64_t qs[3] = {3, 5, 7}, pe[3] = {9, 25, 7};
+            for (int i = 0; i < 3; i++)
+                if (!mod_floor(P, BigInt::from_u64(qs[i])).is_zero()) s *= pe[i];
+        }
+        const BigInt ds = mul_small(dbase, (int64_t)s);
+        if (cmp(ds, Dcap) <= 0) d = ds;
+    }
     lap(tm ? &tm->sample_ms : nullptr, "sample");
 
     uint32_t* Td = (uint32_t*)(scr + pl.off_T);

@@ -153,3 +153,36 @@ def test_large_numerator_product_tiles():
     finally:
         _lib.set_gpu_reconstruction(True)
     assert Xg == Xh
+
+
+def _sample_rule(NC, c):
+    # the reconstruction's sample: the first row, then the k-th of seven
+    # more components at k NC / 8 + (k mod c)
+    s = list(range(min(c, NC)))
+    for k in range(1, 8):
+        j = k * NC // 8 + k % c
+        if c <= j < NC and j not in s:
+            s.append(j)
+    return s
+
+
+@pytest.mark.gpu
+def test_several_rhs_sample_missing_a_factor_two():
+    """n = 40, c = 16, seed 5029: the sample's denominators have an lcm that
+    lacks a factor 2 which 128 of the 640 components' denominators carry (a
+    pattern that random systems with sixteen right-hand sides show about
+    one time in twenty).  The pass's d carries 2^2 beyond the sample's lcm,
+    so every component is accepted in the one pass (none outside the bound)
+    and the result is the oracle's."""
+    n, c = 40, 16
+    A, b = W.uniform_system(n, c, 24, 5029)
+    ref = exact.solve(A, b)
+    dens = [d for row in ref for (_, d) in row]
+    ds = 1
+    for j in _sample_rule(n * c, c):
+        ds = ds * dens[j] // math.gcd(ds, dens[j])
+    assert sum(1 for d in dens if ds % d) == 128     # the case: the sample misses a factor
+    X = es.solve_pairs(torch.as_tensor(A).cuda(), torch.as_tensor(b).cuda())
+    alone, _ = _lib.last_recon_counts()
+    assert alone == 0, alone
+    assert X == ref
