@@ -203,12 +203,21 @@ static int device_cus();
 constexpr int kGemmLds = 64 + 16;  // LDS row stride, bytes
 
 __global__ __launch_bounds__(256) void recon_gemm_kernel(const int8_t* __restrict__ S, const int8_t* __restrict__ WT,
-                                                         int Kpad, int Ncolsp, int* __restrict__ V) {
+                                                         int Kpad, int Ncolsp, int* __restrict__ V, int nx,
+                                                         int tiles) {
     __shared__ __attribute__((aligned(16))) int8_t As[128 * kGemmLds];
     __shared__ __attribute__((aligned(16))) int8_t Bs[128 * kGemmLds];
+    // Blocks go to the eight XCDs round-robin by index; tile number
+    // (b mod 8) (grid / 8) + b / 8 gives each XCD a run of consecutive
+    // tiles (row tiles fastest), so the row tiles that share a weight tile
+    // share an L2 instead of each XCD reading every weight tile.  The grid
+    // is a multiple of 8; tiles past the last do nothing.
+    const int b = blockIdx.x;
+    const int tile = (b & 7) * (int)(gridDim.x >> 3) + (b >> 3);
+    if (tile >= tiles) return;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int wr = wave >> 1, wc = wave & 1;
-    const int j0 = blockIdx.x * 128, c0 = blockIdx.y * 128;
+    const int j0 = (tile % nx) * 128, c0 = (tile / nx) * 128;
     const int lr = lane & 15, lg = lane >> 4;
     v4i acc[4][4];
 #pragma unroll
@@ -890,7 +899,8 @@ hipError_t launch_recon_gemm(const int8_t* S, const int8_t* WT, int Kpad, int NC
                   Kpad, Ncolsp, V);
         return hipGetLastError();
     }
-    es_launch(recon_gemm_kernel, dim3(NCcp / 128, Ncolsp / 128), dim3(256), 0, st, S, WT, Kpad, Ncolsp, V);
+    const int nx = NCcp / 128, tiles = nx * (Ncolsp / 128);
+    es_launch(recon_gemm_kernel, dim3((tiles + 7) / 8 * 8), dim3(256), 0, st, S, WT, Kpad, Ncolsp, V, nx, tiles);
     return hipGetLastError();
 }
 
