@@ -1139,7 +1139,7 @@ __device__ __forceinline__ bool panel_up_body(int8_t* __restrict__ S, int n, int
 // holds four consecutive columns of one row:
 // C[i][col] = sum_c S'[i][K + c] S[p_c][col]; then
 // S'[i][col] = [i not pivot] S[i][col] + C, reduced balanced.  The columns
-// in [skip0, skip1) (a multiple of 16 wide, holding the panel) are neither
+// in [skip0, skip1) (both ends multiples of 32, holding the panel) are neither
 // changed nor written.
 
 // Orders this wave's LDS writes before its later LDS reads (no cross-wave sync).
@@ -1149,18 +1149,24 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-constexpr int kUpdLS = 80;  // LDS row stride of the update staging, bytes (16-byte aligned,
-                            // conflict-free for 4-byte access)
+constexpr int kUpdLS = 144;  // LDS row stride of the update staging: a 128-byte row plus 16
+                             // (16-byte aligned, at most 2-way conflicts for 4-byte access)
 
-// One wave's 64 x 64 part (w4 = 0..3 within the four waves of the tile).
+// One wave's 32 x 128 part (w4 = 0..3 within the four waves of the tile):
+// rows row0 .. row0 + 31 across all of the tile's 128 columns, so that each
+// row's 128-byte line is read and written whole, 32 bytes by each of four
+// lanes (a line written in halves by two waves cost a line read each).
+// The row pitch is a multiple of 64, so the tile's upper 64 columns may lie
+// past it: their operands are zero and their lanes write nothing.
 __device__ __forceinline__ void update_tile(int8_t* __restrict__ S, int n, int pitch, int K,
                                             const int* __restrict__ rowpos, const int8_t* __restrict__ GT,
                                             int j, int tx, int ty, int w4, int lane, uint8_t* st, int skip0,
                                             int skip1) {
     const int lr = lane & 15, lg = lane >> 4;
-    const int col0 = tx * 128 + (w4 & 1) * 64;  // this wave's 64 columns
-    const int row0 = ty * 128 + (w4 >> 1) * 64; // and 64 rows
-    if (col0 >= pitch || row0 >= n || (col0 >= skip0 && col0 + 64 <= skip1)) return;  // wave-uniform
+    const int col0 = tx * 128;                // the tile's 128 columns
+    const int row0 = ty * 128 + 32 * w4;      // this wave's 32 rows
+    const int colend = min(col0 + 128, pitch);
+    if (col0 >= pitch || row0 >= n || (col0 >= skip0 && colend <= skip1)) return;  // wave-uniform
     const uint32_t q = c_pt.q[j];
     // |x| <= 32 * 125^2 + 125 < 2^19
     const float rq = 1.0f / (float)q;
@@ -1169,41 +1175,45 @@ __device__ __forceinline__ void update_tile(int8_t* __restrict__ S, int n, int p
     const int* rpj = rowpos + (size_t)j * n;
     const int8_t* GTj = GT + (size_t)j * pitch * kPanel;
     // operands: lanes of group lg supply k in [16 lg, 16 lg + 16); only k < 32 is nonzero
-    v4i_t ga[4], pb[4];
+    v4i_t ga[8], pb[2];
 #pragma unroll
-    for (int a = 0; a < 4; a++) {
+    for (int a = 0; a < 8; a++) {
         const int col = col0 + 16 * a + lr;
-        ga[a] = lg < 2 ? *(const v4i_t*)(GTj + (size_t)col * kPanel + 16 * lg) : v4i_t{0, 0, 0, 0};
+        ga[a] = (lg < 2 && col < pitch) ? *(const v4i_t*)(GTj + (size_t)col * kPanel + 16 * lg) : v4i_t{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int b = 0; b < 4; b++) {
+    for (int b = 0; b < 2; b++) {
         const int i = row0 + 16 * b + lr;
         pb[b] = (lg < 2 && i < n) ? *(const v4i_t*)(Sj + (size_t)i * pitch + K + 16 * lg) : v4i_t{0, 0, 0, 0};
     }
-    // this lane's 16 columns col0 + 16 lg .. are written unless they lie in the skipped range
-    const int mycol = col0 + 16 * lg;
-    const bool wr = !(mycol >= skip0 && mycol < skip1);
-    // old S for rows row0 + 16 b + lr, 16 columns per lane, and the rows'
+    // this lane's 32 columns col0 + 32 lg .. are written when they lie below
+    // the pitch and outside the skipped range (both ends multiples of 32)
+    const int mycol = col0 + 32 * lg;
+    const bool wr = mycol < pitch && !(mycol >= skip0 && mycol < skip1);
+    // old S for rows row0 + 16 b + lr, 32 columns per lane, and the rows'
     // pivot steps: every load of the tile is issued before the first use
-    uint4 old16[4];
-    int rp[4];
+    uint4 old32[2][2];
+    int rp[2];
 #pragma unroll
-    for (int b = 0; b < 4; b++) {
+    for (int b = 0; b < 2; b++) {
         const int i = row0 + 16 * b + lr;
-        old16[b] = i < n ? *(const uint4*)(Sj + (size_t)i * pitch + mycol) : make_uint4(0, 0, 0, 0);
+        const bool in = i < n && mycol < pitch;
+        old32[b][0] = in ? *(const uint4*)(Sj + (size_t)i * pitch + mycol) : make_uint4(0, 0, 0, 0);
+        old32[b][1] = in ? *(const uint4*)(Sj + (size_t)i * pitch + mycol + 16) : make_uint4(0, 0, 0, 0);
         rp[b] = i < n ? rpj[i] : 0;
     }
 #pragma unroll
-    for (int b = 0; b < 4; b++) {
+    for (int b = 0; b < 2; b++) {
         // through LDS into the accumulator layout
         const int i = row0 + 16 * b + lr;
         const bool rowok = i < n;
-        *(uint4*)(st + lr * kUpdLS + 16 * lg) = old16[b];
+        *(uint4*)(st + lr * kUpdLS + 32 * lg) = old32[b][0];
+        *(uint4*)(st + lr * kUpdLS + 32 * lg + 16) = old32[b][1];
         const bool pivot_row = rp[b] >= K && rp[b] < K + kPanel;
         wave_lds_sync();
         // accumulator layout: lane holds row lr, columns 16 a + 4 lg + 0..3
 #pragma unroll
-        for (int a = 0; a < 4; a++) {
+        for (int a = 0; a < 8; a++) {
             const v4i_t acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(ga[a], pb[b], v4i_t{0, 0, 0, 0}, 0, 0, 0);
             const uint32_t old = *(const uint32_t*)(st + lr * kUpdLS + 16 * a + 4 * lg);
             uint32_t outw = 0;
@@ -1216,7 +1226,10 @@ __device__ __forceinline__ void update_tile(int8_t* __restrict__ S, int n, int p
             *(uint32_t*)(st + lr * kUpdLS + 16 * a + 4 * lg) = outw;
         }
         wave_lds_sync();
-        if (rowok && wr) *(uint4*)(Sj + (size_t)i * pitch + mycol) = *(const uint4*)(st + lr * kUpdLS + 16 * lg);
+        if (rowok && wr) {
+            *(uint4*)(Sj + (size_t)i * pitch + mycol) = *(const uint4*)(st + lr * kUpdLS + 32 * lg);
+            *(uint4*)(Sj + (size_t)i * pitch + mycol + 16) = *(const uint4*)(st + lr * kUpdLS + 32 * lg + 16);
+        }
         wave_lds_sync();
     }
 }
@@ -1245,7 +1258,7 @@ __global__ __launch_bounds__(256) void gj_update_kernel(int8_t* __restrict__ S, 
                                                         const int* __restrict__ flags,
                                                         const int8_t* __restrict__ GT, int skip1, int ntx,
                                                         int nty) {
-    __shared__ __attribute__((aligned(16))) uint8_t stage[4][64 * kUpdLS];
+    __shared__ __attribute__((aligned(16))) uint8_t stage[4][16 * kUpdLS];
     int j, tx, ty;
     if (!update_unit(blockIdx.x & 7, blockIdx.x >> 3, ntx, nty, &j, &tx, &ty) || flags[j]) return;
     const int wave = threadIdx.x >> 6;
@@ -1323,7 +1336,7 @@ __global__ __launch_bounds__(1024) void gj_panel_rest_kernel(int8_t* __restrict_
     // is empty, so the CUs that ran a panel take the update's tail too.  The
     // counters start at zero (set before the elimination); every round takes
     // four more, so the loop ends.
-    __shared__ __attribute__((aligned(16))) uint8_t stage[16][64 * kUpdLS];
+    __shared__ __attribute__((aligned(16))) uint8_t stage[16][16 * kUpdLS];
     __shared__ int s_base;
     const int wave = threadIdx.x >> 6;
     const int x = (int)blockIdx.x & 7;
