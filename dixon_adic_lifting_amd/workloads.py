@@ -7,9 +7,9 @@ here without sharing any of the method.
 
 Workloads follow the exact-solve card (phanerozoic/exact-solve, sections
 "Usage", "Measured" and "Correctness"): integer ``A`` of shape ``[n, n]`` and
-``b`` of shape ``[n, c]``; the timed cases use 24-bit integer entries; the
-correctness families include the order-30 Pascal system, a planted integer
-solution and a scaled Hilbert system.
+``b`` of shape ``[n, c]``; the timed cases draw entries of 24 bits; the
+correctness systems are the order-30 symmetric Pascal matrix, systems built
+around a chosen integer solution, and Hilbert matrices scaled to integers.
 
 Generator: ``numpy.random.default_rng(seed)`` (PCG64); ``integers(lo, hi)``
 with ``hi`` exclusive; ``A`` is drawn row-major first, then ``b`` as ``[n][c]``.

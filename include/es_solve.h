@@ -183,8 +183,8 @@ int es_kernel_profile(double *total_ms, int32_t *counts, int32_t cap);
  * ------------------------------------------------------------------------ */
 
 /*
- * Batched modular inverse (card, "Method": A^-1 mod q_j for every prime by
- * Gauss-Jordan elimination of [A | I], each elimination step one launch
+ * Batched modular inverse (card, "Method": the inverse of A modulo each
+ * prime q_j by Gauss-Jordan elimination of [A | I], each elimination step one launch
  * over every prime, reductions by precomputed reciprocals rather than the
  * hardware remainder).
  * dA: device int64 [n][n]; d_ws: workspace as for es_solve_device with c = 1.

@@ -1,5 +1,5 @@
 /*
- * Exact rational solution of A x = b by fraction-free Bareiss elimination,
+ * The solution of A x = b as exact fractions, by fraction-free Bareiss elimination,
  * in plain C with its own arbitrary-precision integers and POSIX threads.
  *
  * TEST INFRASTRUCTURE ONLY: this is the CPU oracle for the exact solver.  Only

@@ -1,10 +1,10 @@
-"""Exact rational solution of A x = b by fraction-free Bareiss elimination.
+"""The solution of A x = b as exact fractions, by fraction-free Bareiss elimination.
 
 Test infrastructure (see ``oracle/__init__``).  Follows the exact-solve card
-(phanerozoic/exact-solve): "API" -- the solution is ``[n][c]`` exact fractions,
-``None`` when A is singular over the rationals; "Correctness" -- an exact
-Gaussian-elimination oracle and the integer identity A @ N == d * b with
-numerators N and common denominator d.
+(phanerozoic/exact-solve): "API" -- an ``[n][c]`` result of exact fractions,
+``None`` for a matrix with determinant zero; "Correctness" -- an exact
+elimination oracle, and the check that A N = d b holds in integers for the
+numerators N over a common denominator d.
 
 The result has a plain definition (x = A^-1 b in lowest terms with a positive
 denominator), so this module computes that definition directly and does not
@@ -121,7 +121,7 @@ def reduce_fraction(num: int, den: int):
 
 
 def check_identity(A, b, N, d) -> bool:
-    """The card's integer identity A @ N == d * b (exact)."""
+    """A N == d b in exact integer arithmetic (card, "Correctness")."""
     n = len(A)
     c = len(N[0]) if n else 0
     for i in range(n):
