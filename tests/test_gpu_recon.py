@@ -186,3 +186,20 @@ def test_several_rhs_sample_missing_a_factor_two():
     alone, _ = _lib.last_recon_counts()
     assert alone == 0, alone
     assert X == ref
+
+
+@pytest.mark.parametrize("diag,c", [((8388593, 8388587), 1), ((8388593, 8388587, 8388581, 8388571, 8388547), 1),
+                                    ((8388593, 8388587, 8388581), 3)])
+def test_tight_denominator_bound(diag, c):
+    """Diagonal systems whose entries are distinct primes near 2^23: the
+    common denominator is the whole determinant, which equals the Hadamard
+    bound, so the small factors the pass's d takes beyond the sample's lcm
+    do not fit under the denominator bound (d stays the lcm) and the
+    numerators d x reach the numerator bound.  The result must still be
+    the oracle's, in lowest terms."""
+    n = len(diag)
+    A = np.diag(np.array(diag, dtype=np.int64))
+    rng = np.random.default_rng(n + c)
+    b = rng.integers(-(1 << 22), 1 << 22, size=(n, c), dtype=np.int64)
+    X = es.solve_pairs(torch.as_tensor(A).cuda(), torch.as_tensor(b).cuda())
+    assert X == exact.solve(A, b)
