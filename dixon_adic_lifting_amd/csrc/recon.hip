@@ -367,32 +367,22 @@ constexpr int kGcdSeg = 6;  // limbs handed from the limb wave to the Euclid wav
 // so floor(xs / y estimate) never exceeds the true quotient, and falls short
 // of it only for quotients near 2^21 or above, or when x / y is that close
 // above an integer (a short quotient leaves a remainder of at least y, which
-// the next steps take up).  The quotient is at least 1 whenever x >= y (the
-// high word of +0.0 raised to that of 1.0), so x = y cannot repeat.  Every
-// value stays in vector registers: no step waits on the scalar unit.
+// the next steps take up).  The quotient is at least 1 whenever x >= y, so
+// x = y cannot repeat.  The chain from one divisor to the next is the
+// reciprocal, a product, a floor, a maximum and a fused multiply-add.
 __device__ __forceinline__ void euclid_step(double x, double xs, double y, double A, double B, double C, double D,
                                             double& ys, double& ny, double& nC, double& nD) {
     const double r = __builtin_amdgcn_rcp(y);
     ys = y * (1.0 - 0x1p-22);
-    const uint32_t g = x >= y ? 0x3ff00000u : 0u;
-    const uint64_t f = __double_as_longlong(floor(xs * r));
-    const uint32_t fh = (uint32_t)(f >> 32);
-    const double q = __longlong_as_double((long long)(((uint64_t)(fh > g ? fh : g) << 32) | (uint32_t)f));
+    const double q = fmax(floor(xs * r), x >= y ? 1.0 : 0.0);
     ny = fma(-q, y, x);
     nC = fma(-q, C, A);
     nD = fma(-q, D, B);
 }
 
-// Largest |entry| of two cofactor rows.  With q >= 0 throughout and the
-// signs of each column alternating down the sequence of rows, every new row
-// dominates the row two before it (|A - q C| = |A| + q |C|), so the two
-// latest rows bound every earlier one; likewise each divisor is at most the
-// one two steps before it.  A run of steps is acceptable when its last two
-// divisors are at least 2^26 and its last two rows stay below 2^26 (which
-// also keeps every quotient below 2^26).
-__device__ __forceinline__ double row_max(double C1, double D1, double C2, double D2) {
-    return fmax(fmax(fabs(C1), fabs(D1)), fmax(fabs(C2), fabs(D2)));
-}
+// Steps of one run on the leading parts: a fixed count, enough for the
+// 26 bits of cofactor growth a run takes on average (about fifteen steps).
+constexpr int kEuclidRun = 16;
 
 // Waves of a gcd block.  Waves are dealt round-robin to the four SIMDs, so
 // waves 0, 4, 8 and 12 share a SIMD: they run the Euclidean steps (wave 0,
@@ -430,7 +420,8 @@ __global__ __launch_bounds__(64 * gcd_block_waves(GMAX)) void gcd_kernel(const u
     __shared__ int32_t sSeg[2][GMAX][2][8];      // limbs h - 4 .. h + 1 of a and b
     __shared__ int sTop[2][GMAX];                // h
     __shared__ int sDone[2][2];                  // per Euclid wave: all its components are done
-    const int max_rounds = (32 * (nw > nwd ? nw : nwd)) / 12 + 64;
+    __shared__ double2 sRows[2][kEuclidRun + 2][8];  // per Euclid wave: each component's cofactor rows of a run
+    const int max_rounds = (32 * (nw > nwd ? nw : nwd)) / 8 + 64;
     const int j0 = blockIdx.x * G;
     if (threadIdx.x == 0 && G <= 8) sDone[0][1] = sDone[1][1] = 1;  // no second Euclid wave
 
@@ -608,33 +599,39 @@ __global__ __launch_bounds__(64 * gcd_block_waves(GMAX)) void gcd_kernel(const u
                 (void)frexp(fmax(fabs(fa), fabs(fb)), &ex);
                 double x = floor(ldexp(fabs(fa), 52 - ex)), y = floor(ldexp(fabs(fb), 52 - ex));
                 double xs = x * (1.0 - 0x1p-22);
+                // The run: rows R_0 = (A, B) and R_1 = (C, D) start it, step
+                // k divides by y_{k-1} and makes R_{k+1} = R_{k-1} - q_k R_k,
+                // and k steps give the matrix (R_k; R_{k+1}).  k steps are
+                // acceptable when the divisors of steps k - 1 and k are at
+                // least 2^26 and rows k and k + 1 stay below 2^26.  The rows
+                // need no test of their own: with q >= 0 throughout the
+                // signs of each column alternate down the rows, so that
+                // |R_{k+1}| y_{k-1} + |R_k| y_k keeps its starting value x or
+                // y (below 2^52) and a divisor of at least 2^26 bounds the
+                // rows next to it by 2^26.  Every divisor is at most the one
+                // two steps before it, so the acceptable runs are those whose
+                // divisors so far are all at least 2^26; J counts them while
+                // the steps run, in vector registers, and the steps' rows go
+                // to LDS, the accepted pair read back at the end.
                 double A = fa < 0.0 ? -1.0 : 1.0, B = 0.0, C = 0.0, D = fb < 0.0 ? -1.0 : 1.0;
-                int steps = 0;
-                for (int it = 0; it < 16; it++) {
-                    // four steps; divisors y, y1, y2, y3; new rows (C1, D1) .. (C4, D4)
-                    double s1, y1, C1, D1, s2, y2, C2, D2, s3, y3, C3, D3, s4, y4, C4, D4;
-                    euclid_step(x, xs, y, A, B, C, D, s1, y1, C1, D1);
-                    euclid_step(y, s1, y1, C, D, C1, D1, s2, y2, C2, D2);
-                    euclid_step(y1, s2, y2, C1, D1, C2, D2, s3, y3, C3, D3);
-                    euclid_step(y2, s3, y3, C2, D2, C3, D3, s4, y4, C4, D4);
-                    if ((fmin(y2, y3) >= 0x1p26) & (row_max(C3, D3, C4, D4) < 0x1p26)) {
-                        x = y3, xs = s4, y = y4;
-                        A = C3, B = D3, C = C4, D = D4;
-                        steps += 4;
-                        continue;
-                    }
-                    // the last block: keep its longest acceptable prefix
-                    if ((fmin(y1, y2) >= 0x1p26) & (row_max(C2, D2, C3, D3) < 0x1p26)) {
-                        A = C2, B = D2, C = C3, D = D3;
-                        steps += 3;
-                    } else if ((fmin(y, y1) >= 0x1p26) & (row_max(C1, D1, C2, D2) < 0x1p26)) {
-                        A = C1, B = D1, C = C2, D = D2;
-                        steps += 2;
-                    } else if ((y >= 0x1p26) & (row_max(C1, D1, C1, D1) < 0x1p26)) {
-                        A = C, B = D, C = C1, D = D1;
-                        steps += 1;
-                    }
-                    break;
+                sRows[ew][0][q] = make_double2(A, B);
+                sRows[ew][1][q] = make_double2(C, D);
+                int J = 0;
+                double ymin = y;
+#pragma unroll
+                for (int k = 1; k <= kEuclidRun; k++) {
+                    ymin = fmin(ymin, y);
+                    J += ymin >= 0x1p26 ? 1 : 0;
+                    double ys, ny, nC, nD;
+                    euclid_step(x, xs, y, A, B, C, D, ys, ny, nC, nD);
+                    sRows[ew][k + 1][q] = make_double2(nC, nD);
+                    x = y, xs = ys, y = ny;
+                    A = C, B = D, C = nC, D = nD;
+                }
+                const int steps = J;
+                if (J > 0) {
+                    const double2 r0 = sRows[ew][J][q], r1 = sRows[ew][J + 1][q];
+                    A = r0.x, B = r0.y, C = r1.x, D = r1.y;
                 }
                 if (steps == 0) {
                     stop = true;  // no certain progress: the host finishes
@@ -940,9 +937,16 @@ static size_t gcd_lds_pad(const void* kernel, int blocks) {
     }
     const int cus = device_cus();
     if (cus <= 0 || lds_cu <= 0 || blocks <= 0) return 0;
+    hipFuncAttributes fa;
+    if (hipFuncGetAttributes(&fa, kernel) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    // the kernel's own LDS, with a kilobyte of room for allocation granules
+    const int own = (int)((fa.sharedSizeBytes + 1023) / 1024 * 1024) + 1024;
     const int cap = (blocks + cus - 1) / cus;
-    const int pad = lds_cu / cap - 4096;  // room for the kernel's own LDS
-    if (pad <= 0 || pad + 4096 > lds_blk) return 0;
+    const int pad = lds_cu / cap - own;
+    if (pad <= 0 || pad + own > lds_blk) return 0;
     if (pad > 48 * 1024 && hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, pad) != hipSuccess) {
         (void)hipGetLastError();
         return 0;
