@@ -358,7 +358,6 @@ __device__ __forceinline__ int top_limb(const int32_t (&a)[CW], const int32_t (&
     return -1;
 }
 
-constexpr int kGcdSeg = 6;  // limbs handed from the limb wave to the Euclid wave
 
 // One Euclidean step on the leading parts: (x, y) -> (y, x - q y) with the
 // cofactor rows (A, B), (C, D) -> (C, D), (A - q C, B - q D).  xs is x
@@ -398,34 +397,39 @@ __host__ __device__ constexpr int gcd_limb_wave(int g) { return g < 12 ? g + 1 +
 __host__ __device__ constexpr int gcd_block_waves(int G) { return G <= 12 ? gcd_limb_wave(G - 1) + 1 : 16; }
 static_assert(gcd_block_waves(kGcdMaxGroup) == 16, "gcd block layout");
 
-// A block serves G components.  Eight lanes of a Euclid wave serve one
-// component, lane e holding entry e of its window (limbs base + e of a and
-// b; entries 6 and 7 are zero when a window is read): the matrix applied
-// last updates the window lane-parallel, and the leading parts come from
-// three of its entries.  Per round the Euclid waves turn each window into
-// the component's next matrix while the limb waves apply the previous one;
-// one barrier per round for the whole block, and per Euclid wave a flag
-// raised once all its components are done, so that all waves leave the loop
-// at the same barrier.
-template <int CW, int GMAX>
+// A block serves G components.  LPC lanes of a Euclid wave serve one
+// component (eight, or thirty-two when a block has at most four), lane e
+// holding entry e of its window: limbs base + e of a and b, LPC - 2 of them
+// handed over by the limb wave with the top limb at entry LPC - 4 (the
+// entries above are zero when a window is read).  A matrix updates the
+// window lane-parallel, and the leading parts come from three of its
+// entries.  Per round the Euclid waves turn each window into KM matrices of
+// the component while the limb waves apply those of the round before; one
+// barrier per round for the whole block, and per Euclid wave a flag raised
+// once all its components are done, so that all waves leave the loop at
+// the same barrier.
+template <int CW, int GMAX, int LPC, int KM>
 __global__ __launch_bounds__(64 * gcd_block_waves(GMAX)) void gcd_kernel(const uint32_t* __restrict__ Y, int nw,
                                                                           const int* __restrict__ status,
                                                                           int valid_rows,
                                                                           const uint32_t* __restrict__ Dw, int nwd,
                                                                           int G, uint64_t* __restrict__ Gout,
                                                                           int* __restrict__ gstat) {
+    static_assert((LPC == 8 || LPC == 32) && KM >= 1, "gcd window layout");
+    constexpr int kSeg = LPC - 2;       // limbs handed over: h - (kSeg - 2) .. h + 1
+    constexpr int kPerWave = 64 / LPC;  // components per Euclid wave
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const bool lane0 = lane == 0;
-    __shared__ int4 sM[2][GMAX];                 // round matrices [A B; C D]; all zero: that component is done
-    __shared__ int32_t sSeg[2][GMAX][2][8];      // limbs h - 4 .. h + 1 of a and b
+    __shared__ int4 sM[2][GMAX][KM];             // round matrices [A B; C D]; all zero: that component is done
+    __shared__ int32_t sSeg[2][GMAX][2][LPC];    // the windows of a and b
     __shared__ int sTop[2][GMAX];                // h
     __shared__ int sDone[2][2];                  // per Euclid wave: all its components are done
     __shared__ double2 sRows[2][kEuclidRun + 2][8];  // per Euclid wave: each component's cofactor rows of a run
-    const int max_rounds = (32 * (nw > nwd ? nw : nwd)) / 8 + 64;
+    const int max_rounds = ((32 * (nw > nwd ? nw : nwd)) / 8 + 64) / KM + 2;
     const int j0 = blockIdx.x * G;
-    if (threadIdx.x == 0 && G <= 8) sDone[0][1] = sDone[1][1] = 1;  // no second Euclid wave
+    if (threadIdx.x == 0 && G <= kPerWave) sDone[0][1] = sDone[1][1] = 1;  // no second Euclid wave
 
-    const bool euclid = wave == 0 || (wave == 4 && G > 8);
+    const bool euclid = wave == 0 || (wave == 4 && G > kPerWave);
     const bool limb12 = wave == gcd_limb_wave(12) && G > 12;  // the thirteenth component's limb wave
     if ((wave & 3) == 0 && !euclid && !limb12) {
         // ---- idle wave: keeps the Euclid waves' SIMD free; joins the barriers
@@ -455,19 +459,21 @@ __global__ __launch_bounds__(64 * gcd_block_waves(GMAX)) void gcd_kernel(const u
         limb_apply<CW>(a, b, 1, 0, 0, 1, CW, lane0);
         int ns = CW, hprev = 64 * CW - 1;
         // the top h (at most one limb above the last one: a matrix entry is
-        // below 2^26) and the six limbs h - 4 .. h + 1 (zero below limb 0):
-        // the lane holding limb k0 + e writes entry e, from slot k >> 6, which
-        // is one of the two slots the window touches
+        // below 2^26, and the numbers only shrink) and the limbs
+        // h - (kSeg - 2) .. h + 1 (zero below limb 0): the lane holding limb
+        // k0 + e writes entry e, from slot k >> 6, which is one of the two
+        // slots the window touches.  ns covers limb h + 1 for every matrix
+        // until the next hand-over.
         auto hand_over = [&](int buf) {
             const int h = __builtin_amdgcn_readfirstlane(top_limb<CW>(a, b, min(CW - 1, (hprev + 1) >> 6)));
             hprev = h;
             ns = h < 0 ? 1 : min(CW, (h + 1) / 64 + 1);
-            const int k0 = h - 4;
+            const int k0 = h - (kSeg - 2);
             const int e = (lane - k0) & 63;
             const int k = k0 + e;
             const int slo = k0 < 0 ? 0 : k0 >> 6, shi = (h + 1) >> 6;
             const int32_t alo = a[slo], ahi = a[min(shi, CW - 1)], blo = b[slo], bhi = b[min(shi, CW - 1)];
-            if (e < kGcdSeg) {
+            if (e < kSeg) {
                 const bool up = (k >> 6) != slo;
                 sSeg[buf][g][0][e] = k < 0 ? 0 : (up ? ahi : alo);
                 sSeg[buf][g][1][e] = k < 0 ? 0 : (up ? bhi : blo);
@@ -481,186 +487,220 @@ __global__ __launch_bounds__(64 * gcd_block_waves(GMAX)) void gcd_kernel(const u
             __syncthreads();  // matrices r are ready (and the windows after matrices r - 1 were read)
             if (sDone[r & 1][0] & sDone[r & 1][1]) break;
             if (!alive) continue;
-            const int4 m = sM[r & 1][g];
-            const int32_t A = __builtin_amdgcn_readfirstlane(m.x), B = __builtin_amdgcn_readfirstlane(m.y);
-            const int32_t C = __builtin_amdgcn_readfirstlane(m.z), D = __builtin_amdgcn_readfirstlane(m.w);
-            if ((A | B | C | D) == 0) {
-                alive = false;
-                continue;
+            for (int i = 0; i < KM; i++) {
+                const int4 m = sM[r & 1][g][i];
+                const int32_t A = __builtin_amdgcn_readfirstlane(m.x), B = __builtin_amdgcn_readfirstlane(m.y);
+                const int32_t C = __builtin_amdgcn_readfirstlane(m.z), D = __builtin_amdgcn_readfirstlane(m.w);
+                if ((A | B | C | D) == 0) {
+                    alive = false;
+                    break;
+                }
+                if (!(A == 1 && B == 0 && C == 0 && D == 1)) limb_apply<CW>(a, b, A, B, C, D, ns, lane0);
             }
-            if (!(A == 1 && B == 0 && C == 0 && D == 1)) limb_apply<CW>(a, b, A, B, C, D, ns, lane0);
-            hand_over(r & 1);
+            if (alive) hand_over(r & 1);
         }
         return;
     }
 
-    // ---- Euclid wave ew: lane 8 q + e serves component g = 8 ew + q,
-    // entry e of its window.  Every decision below is uniform over a
-    // component's eight lanes.
+    // ---- Euclid wave ew: lane LPC q + e serves component g = kPerWave ew +
+    // q, entry e of its window.  Every value below is uniform over a
+    // component's lanes.
     __builtin_amdgcn_s_setprio(3);
-    const int ew = wave >> 2, q = lane >> 3, e = lane & 7;
-    const int g = 8 * ew + q;
+    const int ew = wave >> 2, q = lane / LPC, e = lane % LPC;
+    const int g = kPerWave * ew + q;
     const int j = j0 + g;
     bool stopped = !(g < G && j < valid_rows);
     if (!stopped && status[j] >= 2) {
         if (e == 0) gstat[j] = 1;  // outside the bound: the host reconstructs it
         stopped = true;
     }
+    // whether this lane's component is reconstructed here (its result is
+    // written when the loop ends)
+    const bool live0 = !stopped;
     __syncthreads();  // the windows after the split are in buffer 0
     int32_t wa = 0, wb = 0;
     int base = 0;
+    int lo = 0;  // low entries of the window made inexact by the matrices applied to it
+    // lanes of no component read those of the last one (and ignore them)
+    const int gl = g < GMAX ? g : GMAX - 1;
     auto read_window = [&](int buf) {
-        const int ee = e < kGcdSeg ? e : kGcdSeg - 1;
-        const int32_t va = sSeg[buf][g][0][ee], vb = sSeg[buf][g][1][ee];
-        wa = e < kGcdSeg ? va : 0;
-        wb = e < kGcdSeg ? vb : 0;
-        base = sTop[buf][g] - 4;
+        const int ee = e < kSeg ? e : kSeg - 1;
+        const int32_t va = sSeg[buf][gl][0][ee], vb = sSeg[buf][gl][1][ee];
+        wa = e < kSeg ? va : 0;
+        wb = e < kSeg ? vb : 0;
+        base = sTop[buf][gl] - (kSeg - 2);
+        lo = 0;
     };
-    // entry x of this component's window (x in 0 .. 7)
-    auto entry = [&](int32_t v, int x) { return __shfl(v, 8 * q + x); };
+    // entry x of this component's window (x in 0 .. LPC - 1)
+    auto entry = [&](int32_t v, int x) { return __shfl(v, LPC * q + x); };
+    // the window after matrix (m0 m1; m2 m3): limb k changes from limbs k
+    // and k - 1 only, so the lowest entry lacks the high part entering from
+    // below and one more entry becomes inexact; an identity or a zero matrix
+    // (a stopped component) leaves it as it is
+    auto window_update = [&](int32_t m0, int32_t m1, int32_t m2, int32_t m3) {
+        const bool moved = !((m0 == 1) & (m1 == 0) & (m2 == 0) & (m3 == 1)) & ((m0 | m1 | m2 | m3) != 0);
+        const int64_t va = (int64_t)m0 * wa + ((int64_t)m1 * wb + (1 << 29));
+        const int64_t vb = (int64_t)m2 * wa + ((int64_t)m3 * wb + (1 << 29));
+        const int32_t ha = (int32_t)(va >> 30), hb = (int32_t)(vb >> 30);
+        int32_t ia, ib;
+        if (LPC <= 16) {
+            ia = __builtin_amdgcn_update_dpp(0, ha, 0x111, 0xf, 0xf, false);  // row_shr:1
+            ib = __builtin_amdgcn_update_dpp(0, hb, 0x111, 0xf, 0xf, false);
+        } else {
+            ia = wave_ror1(ha);
+            ib = wave_ror1(hb);
+        }
+        const int32_t na = e <= kSeg ? (int32_t)((uint32_t)va & 0x3fffffffu) - (1 << 29) + (e == 0 ? 0 : ia) : 0;
+        const int32_t nb = e <= kSeg ? (int32_t)((uint32_t)vb & 0x3fffffffu) - (1 << 29) + (e == 0 ? 0 : ib) : 0;
+        wa = moved ? na : wa;
+        wb = moved ? nb : wb;
+        lo += moved ? 1 : 0;
+    };
+    // The leading parts from limbs h, h - 1, h - 2 (entries top .. top - 2)
+    // and a run of Euclidean steps on them.  The leading parts' signs start
+    // the cofactor matrix, so the steps run on magnitudes.  Rows R_0 =
+    // (A, B) and R_1 = (C, D) start the run, step k divides by y_{k-1} and
+    // makes R_{k+1} = R_{k-1} - q_k R_k, and k steps give the matrix
+    // (R_k; R_{k+1}).  k steps are acceptable when the divisors of steps
+    // k - 1 and k are at least 2^26 and rows k and k + 1 stay below 2^26.
+    // The rows need no test of their own: with q >= 0 throughout the signs
+    // of each column alternate down the rows, so that |R_{k+1}| y_{k-1} +
+    // |R_k| y_k keeps its starting value x or y (below 2^52) and a divisor
+    // of at least 2^26 bounds the rows next to it by 2^26.  Every divisor is
+    // at most the one two steps before it, so the acceptable runs are those
+    // whose divisors so far are all at least 2^26; J counts them while the
+    // steps run, in vector registers, and the steps' rows go to LDS, the
+    // accepted pair read back at the end (rows 0 and 1 when J = 0).
+    auto euclid_run = [&](int top, int& J, int32_t& m0, int32_t& m1, int32_t& m2, int32_t& m3) {
+        const double fa = fma(fma((double)entry(wa, top), 0x1p30, (double)entry(wa, top - 1)), 0x1p30,
+                              (double)entry(wa, top - 2));
+        const double fb = fma(fma((double)entry(wb, top), 0x1p30, (double)entry(wb, top - 1)), 0x1p30,
+                              (double)entry(wb, top - 2));
+        int ex;
+        (void)frexp(fmax(fabs(fa), fabs(fb)), &ex);
+        double x = floor(ldexp(fabs(fa), 52 - ex)), y = floor(ldexp(fabs(fb), 52 - ex));
+        double xs = x * (1.0 - 0x1p-22);
+        double A = fa < 0.0 ? -1.0 : 1.0, B = 0.0, C = 0.0, D = fb < 0.0 ? -1.0 : 1.0;
+        sRows[ew][0][q] = make_double2(A, B);
+        sRows[ew][1][q] = make_double2(C, D);
+        J = 0;
+        double ymin = y;
+#pragma unroll
+        for (int k = 1; k <= kEuclidRun; k++) {
+            ymin = fmin(ymin, y);
+            J += ymin >= 0x1p26 ? 1 : 0;
+            double ys, ny, nC, nD;
+            euclid_step(x, xs, y, A, B, C, D, ys, ny, nC, nD);
+            sRows[ew][k + 1][q] = make_double2(nC, nD);
+            x = y, xs = ys, y = ny;
+            A = C, B = D, C = nC, D = nD;
+        }
+        const double2 r0 = sRows[ew][J][q], r1 = sRows[ew][J + 1][q];
+        m0 = (int32_t)r0.x;
+        m1 = (int32_t)r0.y;
+        m2 = (int32_t)r1.x;
+        m3 = (int32_t)r1.y;
+    };
     if (!stopped) read_window(0);
-    int32_t M0 = 1, M1 = 0, M2 = 0, M3 = 1;  // the matrix issued last (applied by now to the limbs)
+    // the component's result, written when the loop ends: 0 with the gcd in
+    // gv, or 1 (the host finishes it)
+    int result = 1;
+    uint64_t gv = 0;
+    const bool writer = e == 0 && g < G;  // the lane that issues the component's matrices
+    // the matrices issued last round (applied by now to the limbs, and to
+    // the window after the barrier)
+    int32_t Mp[KM][4];
+#pragma unroll
+    for (int i = 0; i < KM; i++) Mp[i][0] = 1, Mp[i][1] = 0, Mp[i][2] = 0, Mp[i][3] = 1;
+    bool idle = __ballot(!stopped) == 0;  // every component of the wave is done (its zero matrices issued)
     for (int r = 1;; r++) {
-        int32_t nM0 = 0, nM1 = 0, nM2 = 0, nM3 = 0;
-        if (!stopped) {
-            // the window after the matrix issued last: limb k changes from
-            // limbs k and k - 1 only, so entries 1 .. 6 become exact (entry 0
-            // lacks the high part entering from below)
-            int lo_lane = 0;
-            if (!(M0 == 1 && M1 == 0 && M2 == 0 && M3 == 1)) {
-                const int64_t va = (int64_t)M0 * wa + ((int64_t)M1 * wb + (1 << 29));
-                const int64_t vb = (int64_t)M2 * wa + ((int64_t)M3 * wb + (1 << 29));
-                const int32_t ha = (int32_t)(va >> 30), hb = (int32_t)(vb >> 30);
-                const int32_t ia = __builtin_amdgcn_update_dpp(0, ha, 0x111, 0xf, 0xf, false);  // row_shr:1
-                const int32_t ib = __builtin_amdgcn_update_dpp(0, hb, 0x111, 0xf, 0xf, false);
-                wa = e <= kGcdSeg ? (int32_t)((uint32_t)va & 0x3fffffffu) - (1 << 29) + (e == 0 ? 0 : ia) : 0;
-                wb = e <= kGcdSeg ? (int32_t)((uint32_t)vb & 0x3fffffffu) - (1 << 29) + (e == 0 ? 0 : ib) : 0;
-                lo_lane = 1;
-            }
-            const uint64_t nzm = __ballot((wa != 0 || wb != 0) && e >= lo_lane && e <= kGcdSeg);
-            const uint32_t gb = (uint32_t)(nzm >> (8 * q)) & 0xffu;
-            const int top = gb ? 31 - __builtin_clz(gb) : -1;  // entry of the top limb
-            const int h = base + top;
-            int result = 1;
-            uint64_t gv = 0;
-            bool stop = false, identity = false;
-            if (r > max_rounds || top < 0 || h >= 64 * CW - 3) {
-                stop = true;  // no progress in sight, no limb in view or no headroom left: the host finishes
-            } else if (h <= 3 && base + lo_lane <= 0) {
-                // exact values from limbs 0..3, then the binary gcd (entries
-                // past 7 are above the top and zero)
-                __int128 xa = 0, xb = 0;
+        bool pend = false;  // the last limbs are in view and exact: the gcd from them, after the matrices
+        if (!idle) {
+            // the window handed over trails by the matrices issued last round
 #pragma unroll
-                for (int k = 3; k >= 0; k--) {
-                    const int x = k - base;
-                    const int32_t la = entry(wa, x < 8 ? x : 7), lb = entry(wb, x < 8 ? x : 7);
-                    xa = xa * (1 << 30) + (x < 8 ? la : 0);
-                    xb = xb * (1 << 30) + (x < 8 ? lb : 0);
-                }
-                unsigned __int128 u = (unsigned __int128)(xa < 0 ? -xa : xa);
-                unsigned __int128 v = (unsigned __int128)(xb < 0 ? -xb : xb);
-                auto ctz = [](unsigned __int128 x) -> int {
-                    const uint64_t lo = (uint64_t)x;
-                    return lo ? __builtin_ctzll(lo) : 64 + __builtin_ctzll((uint64_t)(x >> 64));
-                };
-                if (u == 0) {
-                    u = v;
-                } else if (v != 0) {
-                    const int sh = ctz(u | v);
-                    u >>= ctz(u);
-                    do {
-                        v >>= ctz(v);
-                        if (u > v) {
-                            const unsigned __int128 t = u;
-                            u = v;
-                            v = t;
-                        }
-                        v -= u;
-                    } while (v != 0);
-                    u <<= sh;
-                }
-                if ((uint64_t)(u >> 64) == 0) {
-                    gv = (uint64_t)u;
-                    result = 0;
-                }
-                stop = true;
-            } else if (top - 2 < lo_lane || h <= 3) {
-                // the window lacks the limbs the leading parts (or the last
-                // four limbs) need: issue the identity and read a fresh window
-                identity = true;
-            } else {
-                // leading parts from limbs h, h - 1, h - 2; their signs start
-                // the cofactor matrix, so the steps run on magnitudes
-                const double fa = fma(fma((double)entry(wa, top), 0x1p30, (double)entry(wa, top - 1)), 0x1p30,
-                                      (double)entry(wa, top - 2));
-                const double fb = fma(fma((double)entry(wb, top), 0x1p30, (double)entry(wb, top - 1)), 0x1p30,
-                                      (double)entry(wb, top - 2));
-                int ex;
-                (void)frexp(fmax(fabs(fa), fabs(fb)), &ex);
-                double x = floor(ldexp(fabs(fa), 52 - ex)), y = floor(ldexp(fabs(fb), 52 - ex));
-                double xs = x * (1.0 - 0x1p-22);
-                // The run: rows R_0 = (A, B) and R_1 = (C, D) start it, step
-                // k divides by y_{k-1} and makes R_{k+1} = R_{k-1} - q_k R_k,
-                // and k steps give the matrix (R_k; R_{k+1}).  k steps are
-                // acceptable when the divisors of steps k - 1 and k are at
-                // least 2^26 and rows k and k + 1 stay below 2^26.  The rows
-                // need no test of their own: with q >= 0 throughout the
-                // signs of each column alternate down the rows, so that
-                // |R_{k+1}| y_{k-1} + |R_k| y_k keeps its starting value x or
-                // y (below 2^52) and a divisor of at least 2^26 bounds the
-                // rows next to it by 2^26.  Every divisor is at most the one
-                // two steps before it, so the acceptable runs are those whose
-                // divisors so far are all at least 2^26; J counts them while
-                // the steps run, in vector registers, and the steps' rows go
-                // to LDS, the accepted pair read back at the end.
-                double A = fa < 0.0 ? -1.0 : 1.0, B = 0.0, C = 0.0, D = fb < 0.0 ? -1.0 : 1.0;
-                sRows[ew][0][q] = make_double2(A, B);
-                sRows[ew][1][q] = make_double2(C, D);
-                int J = 0;
-                double ymin = y;
+            for (int i = 0; i < KM; i++) window_update(Mp[i][0], Mp[i][1], Mp[i][2], Mp[i][3]);
 #pragma unroll
-                for (int k = 1; k <= kEuclidRun; k++) {
-                    ymin = fmin(ymin, y);
-                    J += ymin >= 0x1p26 ? 1 : 0;
-                    double ys, ny, nC, nD;
-                    euclid_step(x, xs, y, A, B, C, D, ys, ny, nC, nD);
-                    sRows[ew][k + 1][q] = make_double2(nC, nD);
-                    x = y, xs = ys, y = ny;
-                    A = C, B = D, C = nC, D = nD;
-                }
-                const int steps = J;
-                if (J > 0) {
-                    const double2 r0 = sRows[ew][J][q], r1 = sRows[ew][J + 1][q];
-                    A = r0.x, B = r0.y, C = r1.x, D = r1.y;
-                }
-                if (steps == 0) {
-                    stop = true;  // no certain progress: the host finishes
-                } else {
-                    nM0 = (int32_t)A;
-                    nM1 = (int32_t)B;
-                    nM2 = (int32_t)C;
-                    nM3 = (int32_t)D;
-                }
-            }
-            if (identity) nM0 = 1, nM1 = 0, nM2 = 0, nM3 = 1;
-            if (stop) {
-                if (e == 0) {
-                    gstat[j] = result;
-                    Gout[j] = gv;
-                }
-                stopped = true;
-                nM0 = nM1 = nM2 = nM3 = 0;
+            for (int i = 0; i < KM; i++) {
+                // (bitwise operators: no branch on the lane masks)
+                const uint64_t nzm = __ballot(!stopped & ((wa | wb) != 0) & (e >= lo) & (e <= kSeg));
+                const uint64_t gb = (nzm >> (LPC * q)) & (LPC == 64 ? ~0ull : ((1ull << LPC) - 1));
+                const int top = gb ? 63 - __builtin_clzll(gb) : -1;  // entry of the top limb
+                const int h = base + top;
+                // no progress in sight, no limb in view or no headroom left: the host finishes
+                const bool c_stop = (r > max_rounds) | (top < 0) | (h >= 64 * CW - 3);
+                const bool c_exact = (h <= 3) & (base + lo <= 0);
+                // the window lacks the limbs the leading parts (or the last four
+                // limbs) need: the identity, and a fresh window next round
+                const bool c_ident = (top - 2 < lo) | (h <= 3);
+                // every lane takes the run (lanes of stopped or other cases drop it)
+                int J;
+                int32_t m0, m1, m2, m3;
+                euclid_run(top < 2 ? 2 : (top > LPC - 1 ? LPC - 1 : top), J, m0, m1, m2, m3);
+                const bool live = !stopped & !c_stop;
+                const bool exact = live & c_exact;
+                const bool main = live & !c_exact;
+                const bool go = main & !c_ident & (J > 0);
+                const bool idn = main & c_ident;
+                const int32_t n0 = go ? m0 : (idn ? 1 : 0), n1 = go ? m1 : 0;
+                const int32_t n2 = go ? m2 : 0, n3 = go ? m3 : (idn ? 1 : 0);
+                pend = pend | exact;
+                // stopped: the host finishes (result 1), or the exact gcd below
+                stopped = stopped | c_stop | exact | (main & !c_ident & (J == 0));
+                if (writer) sM[r & 1][g][i] = make_int4(n0, n1, n2, n3);
+                Mp[i][0] = n0, Mp[i][1] = n1, Mp[i][2] = n2, Mp[i][3] = n3;
+                if (i + 1 < KM) window_update(n0, n1, n2, n3);
             }
         }
-        if (e == 0 && g < G) sM[r & 1][g] = make_int4(nM0, nM1, nM2, nM3);
-        const bool all_done = __ballot(!stopped) == 0;
-        if (lane0) sDone[r & 1][ew] = all_done ? 1 : 0;
+        if (__ballot(pend) != 0 && pend) {
+            // exact values from limbs 0..3, then the binary gcd (entries past
+            // LPC - 1 are above the top and zero)
+            __int128 xa = 0, xb = 0;
+#pragma unroll
+            for (int k = 3; k >= 0; k--) {
+                const int x = k - base;
+                const int32_t la = entry(wa, x < LPC ? x : LPC - 1), lb = entry(wb, x < LPC ? x : LPC - 1);
+                xa = xa * (1 << 30) + (x < LPC ? la : 0);
+                xb = xb * (1 << 30) + (x < LPC ? lb : 0);
+            }
+            unsigned __int128 u = (unsigned __int128)(xa < 0 ? -xa : xa);
+            unsigned __int128 v = (unsigned __int128)(xb < 0 ? -xb : xb);
+            auto ctz = [](unsigned __int128 x) -> int {
+                const uint64_t lo64 = (uint64_t)x;
+                return lo64 ? __builtin_ctzll(lo64) : 64 + __builtin_ctzll((uint64_t)(x >> 64));
+            };
+            if (u == 0) {
+                u = v;
+            } else if (v != 0) {
+                const int sh = ctz(u | v);
+                u >>= ctz(u);
+                do {
+                    v >>= ctz(v);
+                    if (u > v) {
+                        const unsigned __int128 t = u;
+                        u = v;
+                        v = t;
+                    }
+                    v -= u;
+                } while (v != 0);
+                u <<= sh;
+            }
+            if ((uint64_t)(u >> 64) == 0) {
+                gv = (uint64_t)u;
+                result = 0;
+            }
+        }
+        idle = __ballot(!stopped) == 0;
+        if (lane0) sDone[r & 1][ew] = idle ? 1 : 0;
         __syncthreads();  // matrices r are ready; the windows after matrices r - 1 are ready
         if (sDone[r & 1][0] & sDone[r & 1][1]) break;
-        // the windows handed over after matrices r - 1; the next iteration
+        // the windows handed over after matrices r - 1 (read by every lane;
+        // those of stopped components are not used); the next iteration
         // applies matrices r to them
-        if (!stopped) read_window((r & 1) ^ 1);
-        M0 = nM0, M1 = nM1, M2 = nM2, M3 = nM3;
+        read_window((r & 1) ^ 1);
+    }
+    if (writer && live0) {
+        gstat[j] = result;
+        Gout[j] = gv;
     }
 }
 
@@ -965,13 +1005,33 @@ static int gcd_group(int rows, int gmax) {
     return G < 1 ? 1 : (G > gmax ? gmax : G);
 }
 
-template <int CW, int GMAX>
+// Blocks of at most kGcdWideGroup components take the wide windows
+// (thirty-two lanes a component, four matrices a round): with few
+// components per CU each Euclid chain's rounds set the time, and a round's
+// barrier and hand-over then serve four matrices.
+constexpr int kGcdWideGroup = 4;
+
+// Waves of a gcd block of grp components: a wide block of more than two
+// components has its second Euclid wave at wave 4.
+static int gcd_waves(int grp) {
+    const int w = gcd_block_waves(grp);
+    return grp <= kGcdWideGroup && grp > 2 && w < 5 ? 5 : w;
+}
+
+// The gcd kernel for CW limb slots and a group of grp components.
+template <int CW>
+static const void* gcd_kernel_for(int grp) {
+    return grp <= kGcdWideGroup ? (const void*)gcd_kernel<CW, kGcdWideGroup, 32, 4>
+                                : (const void*)gcd_kernel<CW, kGcdMaxGroup, 8, 1>;
+}
+
+template <int CW>
 static void launch_gcd_as(const uint32_t* Y, int nw, const int* status, int valid_rows, const uint32_t* Dw,
                           int nwd, uint64_t* G, int* gstat, int group, hipStream_t st) {
-    const int grp = group > 0 ? group : gcd_group(valid_rows, GMAX);
+    const int grp = group > 0 ? group : gcd_group(valid_rows, kGcdMaxGroup);
     const int blocks = (valid_rows + grp - 1) / grp;
-    const int waves = gcd_block_waves(grp);
-    const size_t pad = gcd_lds_pad((const void*)gcd_kernel<CW, GMAX>, blocks);
+    const int waves = gcd_waves(grp);
+    const size_t pad = gcd_lds_pad(gcd_kernel_for<CW>(grp), blocks);
     static const bool verbose = [] {
         const char* e = std::getenv("ES_VERBOSE");
         return e && *e && *e != '0';
@@ -979,8 +1039,12 @@ static void launch_gcd_as(const uint32_t* Y, int nw, const int* status, int vali
     if (verbose)
         fprintf(stderr, "[es] gcd: %d components, %d per block, %d blocks, %zu bytes of LDS padding, %d slots\n",
                 valid_rows, grp, blocks, pad, CW);
-    es_launch(gcd_kernel<CW, GMAX>, dim3(blocks), dim3(64 * waves), pad, st, Y, nw, status, valid_rows, Dw, nwd,
-              grp, G, gstat);
+    if (grp <= kGcdWideGroup)
+        es_launch(gcd_kernel<CW, kGcdWideGroup, 32, 4>, dim3(blocks), dim3(64 * waves), pad, st, Y, nw, status,
+                  valid_rows, Dw, nwd, grp, G, gstat);
+    else
+        es_launch(gcd_kernel<CW, kGcdMaxGroup, 8, 1>, dim3(blocks), dim3(64 * waves), pad, st, Y, nw, status,
+                  valid_rows, Dw, nwd, grp, G, gstat);
 }
 
 hipError_t launch_gcd(const uint32_t* Y, int nw, const int* status, int valid_rows, const uint32_t* Dw, int nwd,
@@ -989,11 +1053,11 @@ hipError_t launch_gcd(const uint32_t* Y, int nw, const int* status, int valid_ro
     if (valid_rows <= 0) return hipSuccess;
     if (group > kGcdMaxGroup) return hipErrorInvalidValue;
     if (cw == 8)
-        launch_gcd_as<8, kGcdMaxGroup>(Y, nw, status, valid_rows, Dw, nwd, G, gstat, group, st);
+        launch_gcd_as<8>(Y, nw, status, valid_rows, Dw, nwd, G, gstat, group, st);
     else if (cw == 16)
-        launch_gcd_as<16, kGcdMaxGroup>(Y, nw, status, valid_rows, Dw, nwd, G, gstat, group, st);
+        launch_gcd_as<16>(Y, nw, status, valid_rows, Dw, nwd, G, gstat, group, st);
     else if (cw == 32)
-        launch_gcd_as<32, kGcdMaxGroup>(Y, nw, status, valid_rows, Dw, nwd, G, gstat, group, st);
+        launch_gcd_as<32>(Y, nw, status, valid_rows, Dw, nwd, G, gstat, group, st);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
@@ -1001,11 +1065,11 @@ hipError_t launch_gcd(const uint32_t* Y, int nw, const int* status, int valid_ro
 
 // Blocks of the gcd kernel one CU holds at once (waves and registers; the
 // LDS padding only lowers it further); 0 when the device does not say.
-template <int CW, int GMAX>
+template <int CW>
 static int gcd_blocks_per_cu(int grp) {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, (const void*)gcd_kernel<CW, GMAX>,
-                                                     64 * gcd_block_waves(grp), 0) != hipSuccess) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, gcd_kernel_for<CW>(grp), 64 * gcd_waves(grp), 0) !=
+        hipSuccess) {
         (void)hipGetLastError();
         return 0;
     }
@@ -1016,9 +1080,9 @@ int gcd_split(int valid_rows, int nw, int nwd, int* group) {
     const int cw = gcd_words_per_lane(nw > nwd ? nw : nwd);
     const int grp = gcd_group(valid_rows, kGcdMaxGroup);
     *group = grp;
-    const int per_cu = cw == 8    ? gcd_blocks_per_cu<8, kGcdMaxGroup>(grp)
-                       : cw == 16 ? gcd_blocks_per_cu<16, kGcdMaxGroup>(grp)
-                       : cw == 32 ? gcd_blocks_per_cu<32, kGcdMaxGroup>(grp)
+    const int per_cu = cw == 8    ? gcd_blocks_per_cu<8>(grp)
+                       : cw == 16 ? gcd_blocks_per_cu<16>(grp)
+                       : cw == 32 ? gcd_blocks_per_cu<32>(grp)
                                   : 0;
     const int cus = device_cus();
     if (valid_rows <= 0 || per_cu <= 0 || cus <= 0) return valid_rows;
