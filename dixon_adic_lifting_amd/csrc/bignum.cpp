@@ -410,39 +410,45 @@ BigInt divexact(const BigInt& a, const BigInt& b) {
     return q;
 }
 
-// Exact division by one word: the factor 2^t of b shifts out, then the odd
-// part's inverse modulo 2^64 (Newton's iteration, each pass doubling the
-// correct low bits from 3) turns the division into a product, limb by limb
-// from the bottom, carrying the high words of q_i b' as a borrow (Hensel).
-BigInt divexact_u64(const BigInt& a, uint64_t b) {
+// Exact division by one word, in place: the factor 2^t of b shifts out,
+// then the odd part's inverse modulo 2^64 (Newton's iteration, each pass
+// doubling the correct low bits from 3) turns the division into a product,
+// limb by limb from the bottom, carrying the high words of q_i b' as a
+// borrow (Hensel).  Limb i of the quotient needs limbs i and i + 1 of a
+// only, so it overwrites limb i.  Throws when b does not divide a (a is
+// then left unspecified, unless the low bits of a already show it).
+void divexact_u64_inplace(BigInt& a, uint64_t b) {
     if (b == 0) throw std::domain_error("division by zero");
+    if (a.is_zero() || b == 1) return;
     const int t = __builtin_ctzll(b);
     const uint64_t bo = b >> t;
-    if (bo == 1) {
-        // a power of two: a shift
-        if (!a.is_zero() && (a.d[0] & (b - 1))) throw std::logic_error("inexact division");
-        BigInt q = shr_abs(a, (size_t)t);
-        q.neg = a.neg && !q.is_zero();
-        return q;
-    }
-    uint64_t inv = bo;
-    for (int i = 0; i < 5; i++) inv *= 2 - bo * inv;
+    if (t && (a.d[0] & ((1ULL << t) - 1))) throw std::logic_error("inexact division");
     const size_t n = a.size();
-    BigInt q;
-    q.d.resize(n);
-    uint64_t borrow = 0;
-    for (size_t i = 0; i < n; i++) {
-        // limb i of a >> t
-        const uint64_t ai = t ? (a.d[i] >> t) | (i + 1 < n ? a.d[i + 1] << (64 - t) : 0) : a.d[i];
-        if (t && (i == 0) && (a.d[0] & ((1ULL << t) - 1))) throw std::logic_error("inexact division");
-        const uint64_t s = ai - borrow;
-        const uint64_t qi = s * inv;
-        borrow = (uint64_t)(((u128)qi * bo) >> 64) + (ai < borrow);
-        q.d[i] = qi;
+    limb_t* v = a.d.data();
+    if (bo != 1) {
+        uint64_t inv = bo;
+        for (int i = 0; i < 5; i++) inv *= 2 - bo * inv;
+        uint64_t borrow = 0;
+        for (size_t i = 0; i < n; i++) {
+            const uint64_t ai = t ? (v[i] >> t) | (i + 1 < n ? v[i + 1] << (64 - t) : 0) : v[i];
+            const uint64_t s = ai - borrow;
+            const uint64_t qi = s * inv;
+            borrow = (uint64_t)(((u128)qi * bo) >> 64) + (ai < borrow);
+            v[i] = qi;
+        }
+        if (borrow != 0) throw std::logic_error("inexact division");
+    } else {
+        // a power of two: a shift
+        for (size_t i = 0; i + 1 < n; i++) v[i] = (v[i] >> t) | (v[i + 1] << (64 - t));
+        v[n - 1] >>= t;
     }
-    if (borrow != 0) throw std::logic_error("inexact division");
-    q.trim();
-    q.neg = a.neg && !q.is_zero();
+    a.trim();
+    if (a.is_zero()) a.neg = false;
+}
+
+BigInt divexact_u64(const BigInt& a, uint64_t b) {
+    BigInt q = a;
+    divexact_u64_inplace(q, b);
     return q;
 }
 

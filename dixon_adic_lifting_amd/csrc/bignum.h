@@ -45,6 +45,7 @@ void divmod_trunc(const BigInt& a, const BigInt& b, BigInt* q, BigInt* r);
 BigInt mod_floor(const BigInt& a, const BigInt& m);
 BigInt divexact(const BigInt& a, const BigInt& b);  // a / b, exact (checked)
 BigInt divexact_u64(const BigInt& a, uint64_t b);  // a / b for 0 < b < 2^64, exact (checked)
+void divexact_u64_inplace(BigInt& a, uint64_t b);  // a <- a / b, exact (checked; a unspecified on a throw)
 BigInt shl(const BigInt& a, size_t bits);
 BigInt shr_abs(const BigInt& a, size_t bits);       // |a| >> bits
 BigInt pow_u(const BigInt& a, unsigned e);

@@ -1,6 +1,8 @@
 // Test hooks into the host bignum code (include/es_debug.h).
 #include "../../include/es_debug.h"
 
+#include <vector>
+
 #include "bignum.h"
 #include "host.h"
 
@@ -48,6 +50,30 @@ extern "C" int es_dbg_bignum(int op, const uint64_t* a, int32_t la, int a_neg, c
         }
         if (!put(x, r1, l1, n1, cap)) return -1;
         if (op == ES_DBG_DIVMOD && !put(y, r2, l2, n2, cap)) return -1;
+        return 0;
+    } catch (...) {
+        return -6;
+    }
+}
+
+extern "C" int es_dbg_assemble(const uint64_t* P, int32_t lP, const int64_t* digits, int32_t m, int32_t count,
+                               int32_t parts, uint64_t* out, int32_t* lens, int* neg, int32_t cap) {
+    if (!P || lP < 1 || !digits || m < 1 || count < 1 || parts < 1 || (parts & (parts - 1)) || !out || !lens ||
+        !neg)
+        return -1;
+    try {
+        const BigInt Pb = make(P, lP, 0);
+        std::vector<BigInt> pw((size_t)m + 1);
+        pw[0] = BigInt::from_u64(1);
+        for (int i = 1; i <= m; i++) pw[i] = es::mul(pw[i - 1], Pb);
+        const size_t stride = (size_t)m * 6;
+        std::vector<BigInt> split((size_t)count);
+        es::assemble_split(digits, stride, (size_t)count, m, pw, parts, es::default_threads(), split.data());
+        for (int32_t k = 0; k < count; k++) {
+            const BigInt whole = es::assemble(digits + (size_t)k * stride, m, pw);
+            if (es::cmp(whole, split[k]) != 0) return -2;
+            if (!put(whole, out + (size_t)k * cap, &lens[k], &neg[k], cap)) return -1;
+        }
         return 0;
     } catch (...) {
         return -6;

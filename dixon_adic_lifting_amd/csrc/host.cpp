@@ -325,42 +325,52 @@ int default_threads() {
 // own job and returns once every item is done, without waiting for workers
 // that have not woken yet (a wake-up can take tens of microseconds): items
 // are claimed through a ticket that carries the job's generation, so a late
-// worker finds the ticket moved on and claims nothing.  The first exception
-// thrown by the loop body is rethrown in the caller (the items after it are
-// skipped).
+// worker finds the ticket moved on and claims nothing.  Items are claimed a
+// chunk at a time (a quarter of an even share), so that short items do not
+// queue on the ticket, and a worker that has finished a job watches for the
+// next one for a short while before it sleeps (the host phases of a solve
+// come in quick succession).  The first exception thrown by the loop body
+// is rethrown in the caller (the items after it are skipped).
 namespace {
 thread_local bool t_pool_worker = false;
 
 struct ThreadPool {
+    static constexpr int64_t kWatchNs = 60000;  // how long an idle worker watches for the next job
     std::mutex mu, serial;
     std::condition_variable cv_work, cv_done;
-    uint32_t gen = 0;  // current job (under mu)
+    uint32_t gen = 0;                  // current job (under mu)
+    std::atomic<uint32_t> pub{0};      // gen, for workers watching without the lock
     const std::function<void(size_t)>* job = nullptr;
-    size_t count = 0;
+    size_t count = 0, chunk = 1;
     std::atomic<uint64_t> ticket{0};  // gen << 32 | next item
     std::atomic<size_t> done{0};      // items of the current job finished or skipped
     std::atomic<bool> stop{false};
     std::exception_ptr error;
+    const int workers;
 
-    explicit ThreadPool(int n) {
+    explicit ThreadPool(int n) : workers(n) {
         for (int i = 0; i < n; i++) std::thread([this] { run(); }).detach();
     }
-    // claims and runs items of job g until none is left
-    void drain(uint32_t g, const std::function<void(size_t)>* f, size_t cnt) {
+    // claims and runs chunks of job g until none is left
+    void drain(uint32_t g, const std::function<void(size_t)>* f, size_t cnt, size_t ch) {
         for (;;) {
             uint64_t t = ticket.load(std::memory_order_acquire);
-            if ((uint32_t)(t >> 32) != g || (size_t)(uint32_t)t >= cnt) return;
-            if (!ticket.compare_exchange_weak(t, t + 1, std::memory_order_acq_rel)) continue;
-            if (!stop.load(std::memory_order_relaxed)) {
+            const size_t i0 = (size_t)(uint32_t)t;
+            if ((uint32_t)(t >> 32) != g || i0 >= cnt) return;
+            const size_t i1 = std::min(cnt, i0 + ch);
+            if (!ticket.compare_exchange_weak(t, ((uint64_t)g << 32) | (uint64_t)i1, std::memory_order_acq_rel))
+                continue;
+            for (size_t i = i0; i < i1; i++) {
+                if (stop.load(std::memory_order_relaxed)) break;
                 try {
-                    (*f)((size_t)(uint32_t)t);
+                    (*f)(i);
                 } catch (...) {
                     std::lock_guard<std::mutex> lk(mu);
                     if (!error) error = std::current_exception();
                     stop = true;
                 }
             }
-            if (done.fetch_add(1, std::memory_order_acq_rel) + 1 == cnt) {
+            if (done.fetch_add(i1 - i0, std::memory_order_acq_rel) + (i1 - i0) == cnt) {
                 std::lock_guard<std::mutex> lk(mu);
                 cv_done.notify_all();
             }
@@ -370,8 +380,17 @@ struct ThreadPool {
         t_pool_worker = true;
         uint32_t seen = 0;
         for (;;) {
+            // watch for the next job a while, then sleep until one comes
+            const auto t0 = std::chrono::steady_clock::now();
+            for (int k = 0; pub.load(std::memory_order_acquire) == seen; k++) {
+                __builtin_ia32_pause();
+                if ((k & 255) == 255 &&
+                    std::chrono::duration_cast<std::chrono::nanoseconds>(std::chrono::steady_clock::now() - t0)
+                            .count() > kWatchNs)
+                    break;
+            }
             const std::function<void(size_t)>* f;
-            size_t cnt;
+            size_t cnt, ch;
             uint32_t g;
             {
                 std::unique_lock<std::mutex> lk(mu);
@@ -379,30 +398,34 @@ struct ThreadPool {
                 seen = g = gen;
                 f = job;
                 cnt = count;
+                ch = chunk;
             }
             // *f is only used for an item claimed under generation g, and
             // the caller waits for every such item: it is still alive then
-            drain(g, f, cnt);
+            drain(g, f, cnt, ch);
         }
     }
     // false when the pool is busy with another caller's job
-    bool parallel(size_t cnt, const std::function<void(size_t)>& f) {
+    bool parallel(size_t cnt, const std::function<void(size_t)>& f, size_t grain) {
         if (cnt >= ((size_t)1 << 32)) return false;
         std::unique_lock<std::mutex> one(serial, std::try_to_lock);
         if (!one.owns_lock()) return false;
         uint32_t g;
+        const size_t ch = grain > 0 ? grain : std::max<size_t>(1, cnt / (4 * (size_t)(workers + 1)));
         {
             std::lock_guard<std::mutex> lk(mu);
             job = &f;
             count = cnt;
+            chunk = ch;
             done = 0;
             stop = false;
             error = nullptr;
             g = ++gen;
             ticket.store((uint64_t)g << 32, std::memory_order_release);
+            pub.store(g, std::memory_order_release);
         }
         cv_work.notify_all();
-        drain(g, &f, cnt);
+        drain(g, &f, cnt, ch);
         std::exception_ptr e;
         {
             std::unique_lock<std::mutex> lk(mu);
@@ -431,11 +454,11 @@ ThreadPool* pool() {
 }  // namespace
 
 template <class F>
-static void parallel_for(size_t count, int nthreads, F&& fn) {
+static void parallel_for(size_t count, int nthreads, F&& fn, size_t grain = 0) {
     if (count == 0) return;
     if (nthreads > 1 && count > 1 && !t_pool_worker) {
         const std::function<void(size_t)> f = fn;
-        if (pool()->parallel(count, f)) return;
+        if (pool()->parallel(count, f, grain)) return;
     }
     for (size_t i = 0; i < count; i++) fn(i);
 }
@@ -468,6 +491,35 @@ BigInt assemble(const int64_t* dig, int m, const std::vector<BigInt>& pw) {
     return assemble_range(dig, 0, m, pw);
 }
 
+void assemble_split(const int64_t* dig, size_t stride, size_t count, int m, const std::vector<BigInt>& pw,
+                    int parts, int nthreads, BigInt* out) {
+    if (m < 1 || count == 0) return;
+    if (parts < 2 || m < 8 * parts || (int)pw.size() <= m) {
+        parallel_for(count, nthreads, [&](size_t k) { out[k] = assemble(dig + k * stride, m, pw); });
+        return;
+    }
+    // ranges [m q / parts, m (q + 1) / parts), then pairs joined level by
+    // level: the left part plus P^(start of right - start of left) times the right
+    std::vector<BigInt> X(count * (size_t)parts);
+    std::vector<int> start(parts + 1);
+    for (int q = 0; q <= parts; q++) start[q] = (int)((long)m * q / parts);
+    parallel_for(X.size(), nthreads, [&](size_t t) {
+        const size_t k = t / parts;
+        const int q = (int)(t % parts);
+        X[t] = assemble_range(dig + k * stride, start[q], start[q + 1], pw);
+    });
+    for (int w = 1; w < parts; w *= 2) {
+        const size_t joins = count * (size_t)(parts / (2 * w));
+        parallel_for(joins, nthreads, [&](size_t t) {
+            const size_t k = t / (parts / (2 * w));
+            const int q = (int)(t % (parts / (2 * w))) * 2 * w;
+            BigInt& left = X[k * parts + q];
+            left = add(left, mul(pw[start[q + w] - start[q]], X[k * parts + q + w]));
+        });
+    }
+    for (size_t k = 0; k < count; k++) out[k] = std::move(X[k * parts]);
+}
+
 static bool verbose() {
     static const bool v = [] {
         const char* e = std::getenv("ES_VERBOSE");
@@ -476,8 +528,8 @@ static bool verbose() {
     return v;
 }
 
-void parallel_for_each(size_t count, int nthreads, const std::function<void(size_t)>& fn) {
-    parallel_for(count, nthreads, fn);
+void parallel_for_each(size_t count, int nthreads, const std::function<void(size_t)>& fn, size_t grain) {
+    parallel_for(count, nthreads, fn, grain);
 }
 
 std::vector<size_t> sample_indices(size_t NC, int c) {

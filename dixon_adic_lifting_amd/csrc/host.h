@@ -59,9 +59,16 @@ int default_threads();
 BigInt assemble(const int64_t* dig, int m, const BigInt& P);
 // the same from the powers pw[k] = P^k, k <= m (halves joined by one product)
 BigInt assemble(const int64_t* dig, int m, const std::vector<BigInt>& pw);
+// The same for `count` components (digits dig + k stride), each cut into
+// `parts` (a power of two) ranges assembled on the pool's threads and joined
+// pairwise: a shorter wait for a few long components.
+void assemble_split(const int64_t* dig, size_t stride, size_t count, int m, const std::vector<BigInt>& pw,
+                    int parts, int nthreads, BigInt* out);
 
-// Runs fn(i) for i in [0, count) on up to nthreads host threads.
-void parallel_for_each(size_t count, int nthreads, const std::function<void(size_t)>& fn);
+// Runs fn(i) for i in [0, count) on up to nthreads host threads, the items
+// claimed `grain` at a time (0: a quarter of an even share; 1 for items of
+// very uneven cost).
+void parallel_for_each(size_t count, int nthreads, const std::function<void(size_t)>& fn, size_t grain = 0);
 
 // The sampled common denominator (card, "Method"): d = lcm of the reduced
 // denominators of the sample components (the first row, i.e. one component

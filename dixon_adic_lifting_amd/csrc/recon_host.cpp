@@ -19,6 +19,7 @@
 #include <memory>
 #include <mutex>
 #include <thread>
+#include <stdexcept>
 #include <vector>
 
 #include "../../include/es_solve.h"
@@ -93,6 +94,57 @@ BigInt from_words(const uint32_t* w, int nw, bool neg) {
     r.trim();
     r.neg = neg && !r.is_zero();
     return r;
+}
+
+// floor(a / b) for a >= 0, b > 0
+BigInt shr_pow(const BigInt& a, const BigInt& b) {
+    BigInt q;
+    divmod_trunc(a, b, &q, nullptr);
+    return q;
+}
+
+// t <- P t - q M, for t of n limbs (zero padded) in [0, M) and the quotient
+// q = floor(P t / M), so that the result lies in [0, M) too (n = M's limbs):
+// one pass over the columns with a signed three-word accumulator, the old
+// limbs of t the column needs kept in a ring.  Throws if the result does
+// not fit (a wrong q).
+void seed_step(uint64_t* t, size_t n, const uint64_t* p, size_t lp, const uint64_t* q, size_t lq,
+               const uint64_t* M) {
+    typedef unsigned __int128 u128;
+    if (lp > 8) throw std::logic_error("seed multiplier too wide");
+    uint64_t old[8] = {0, 0, 0, 0, 0, 0, 0, 0};  // old[k] = t[i - k] before this step
+    uint64_t a0 = 0, a1 = 0;
+    int64_t a2 = 0;
+    const size_t cols = n + std::max(lp, lq) + 1;
+    for (size_t i = 0; i < cols; i++) {
+        for (size_t k = lp - 1; k > 0; k--) old[k] = old[k - 1];
+        old[0] = i < n ? t[i] : 0;
+        for (size_t k = 0; k < lp && k <= i; k++) {
+            const u128 pr = (u128)p[k] * old[k];
+            const u128 s0 = (u128)a0 + (uint64_t)pr;
+            a0 = (uint64_t)s0;
+            const u128 s1 = (u128)a1 + (uint64_t)(pr >> 64) + (uint64_t)(s0 >> 64);
+            a1 = (uint64_t)s1;
+            a2 += (int64_t)(uint64_t)(s1 >> 64);
+        }
+        for (size_t k = 0; k < lq && k <= i; k++) {
+            if (i - k >= n) continue;
+            const u128 pr = (u128)q[k] * M[i - k];
+            const uint64_t lo = (uint64_t)pr, hi = (uint64_t)(pr >> 64);
+            const uint64_t b0 = a0 < lo;
+            a0 -= lo;
+            const u128 sub = (u128)hi + b0;
+            const uint64_t b1 = (u128)a1 < sub;
+            a1 = (uint64_t)((u128)a1 - sub);
+            a2 -= (int64_t)b1;
+        }
+        if (i < n) t[i] = a0;
+        else if (a0 != 0) throw std::logic_error("seed step out of range");
+        a0 = a1;
+        a1 = (uint64_t)a2;
+        a2 = a2 < 0 ? -1 : 0;
+    }
+    if (a0 != 0 || a1 != 0 || a2 != 0) throw std::logic_error("seed step out of range");
 }
 
 bool verbose() {
@@ -236,8 +288,6 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
         HIPOK(hipMemcpyAsync(sd + k * dig_comp, dig + sidx[k] * dig_comp, dig_comp * sizeof(int64_t),
                              hipMemcpyDeviceToHost, st));
     HIPOK(hipStreamSynchronize(st));
-    std::vector<BigInt> xs(sidx.size());
-    parallel_for_each(sidx.size(), nthreads, [&](size_t k) { xs[k] = assemble(sd + k * dig_comp, m, pw); });
     // The sample's denominators (Wang reconstruction of each X mod M; their
     // lcm is d).  With one right-hand side the first two run first, with a
     // second thread each for the cofactors, and the GPU pass starts from
@@ -245,21 +295,28 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
     // the whole sample's lcm differs the pass is run again with it before any
     // of its results are used.  With several right-hand sides (whose
     // denominators differ, so a part of the sample misses factors far more
-    // often) the whole sample runs first.
+    // often) the whole sample runs first.  The first ones' X are assembled
+    // each in parts on the pool's threads, the others' on their own threads.
+    const size_t nfirst = pl.c == 1 ? std::min<size_t>(2, sidx.size()) : sidx.size();
+    std::vector<BigInt> xs(sidx.size());
+    {
+        int parts = 1;
+        while (parts < 8 && (size_t)parts * 2 * nfirst <= (size_t)nthreads) parts *= 2;
+        assemble_split(sd, dig_comp, nfirst, m, pw, parts, nthreads, xs.data());
+    }
     const BigInt Nb = shl(BigInt::from_u64(1), (size_t)nbits);
     const BigInt Db = shl(BigInt::from_u64(1), (size_t)dbits);
     std::vector<BigInt> sden(xs.size());
     std::atomic<int> bad{0};
     auto sample_rr = [&](size_t k, bool split) {
         try {
-            BigInt a = mod_floor(xs[k], M), nu, de;
+            BigInt a = mod_floor(k < nfirst ? xs[k] : assemble(sd + k * dig_comp, m, pw), M), nu, de;
             if (!rational_reconstruct(a, M, Nb, Db, &nu, &de, false, split)) bad = 1;
             else sden[k] = de;
         } catch (...) {
             bad = 1;
         }
     };
-    const size_t nfirst = pl.c == 1 ? std::min<size_t>(2, xs.size()) : xs.size();
     const bool split_first = 4 * nfirst <= (size_t)nthreads;
     std::vector<std::thread> rest;
     struct Joiner {
@@ -344,16 +401,37 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
     hipEvent_t words_ready = g_words_ready.get(), first_gcds = g_first_gcds.get();
     if (!words_ready || !first_gcds) return ES_EHIP;
     auto gpu_pass = [&]() -> int {
-        // the chain T_{i+1} = T_i P mod M, cut into segments that each start
+        // The chain T_{i+1} = T_i P mod M, cut into segments that each start
         // from P^{i0} d mod M = (d mod P^{m - i0}) P^{i0} (M = P^m: the
-        // product is below M, no division by M) and run in parallel
+        // product is below M, no division by M) and run in parallel.  With
+        // T_i = P^i D_i, D_i = d mod P^{m - i}, the step's quotient
+        // floor(P T_i / M) is D_i's base-P digit m - i - 1, so each step is
+        // T_{i+1} = P T_i - delta M with no division: a segment takes its
+        // digits from one division of D_{i0} by a power of P.
         const int nseg = std::max(1, std::min(nthreads, m / 8));
         parallel_for_each((size_t)nseg, nthreads, [&](size_t sg) {
             const int i0 = (int)(sg * (size_t)m / nseg), i1 = (int)((sg + 1) * (size_t)m / nseg);
-            BigInt Ti = i0 == 0 ? mod_floor(d, M) : mul(mod_floor(d, pw[m - i0]), pw[i0]);
+            const BigInt D = mod_floor(d, pw[m - i0]);
+            // digits m - i1 + 1 .. m - i0 - 1 of D, lowest first
+            std::vector<BigInt> delta;
+            if (i1 - i0 >= 2) {
+                BigInt Q = shr_pow(D, pw[m - i1 + 1]);
+                for (int k = 0; k < i1 - i0 - 1; k++) {
+                    BigInt qq, r;
+                    divmod_trunc(Q, P, &qq, &r);
+                    delta.push_back(std::move(r));
+                    Q = std::move(qq);
+                }
+                if (!Q.is_zero()) throw std::logic_error("seed digits left over");
+            }
+            BigInt Ti = mul(D, pw[i0]);
+            Ti.d.resize(M.size(), 0);
             for (int i = i0; i < i1; i++) {
                 to_words(Ti, &T[(size_t)i * NW], NW);
-                if (i + 1 < i1) Ti = mod_floor(mul(Ti, P), M);
+                if (i + 1 < i1) {
+                    const BigInt& q = delta[(size_t)(i1 - 2 - i)];
+                    seed_step(Ti.d.data(), M.size(), P.d.data(), P.size(), q.d.data(), q.size(), M.d.data());
+                }
             }
         });
         lap(tm ? &tm->seeds_ms : nullptr, "seeds");
@@ -424,11 +502,13 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
     };
     auto reduce = [&](const std::vector<size_t>& which) {
         // the components whose gcd the host computes (long) are listed
-        // first, so that the pool's threads share them before the divisions
+        // first, one item each, so that the pool's threads share them; the
+        // one-word divisions follow in batches
         std::vector<size_t> need;
         std::vector<uint64_t> gs;  // the distinct one-word gcds other than 1
         for (size_t j : which)
             if ((sth[j] == 0 || sth[j] == 1) && gsth[j] != 0) need.push_back(j);
+        const size_t nlong = need.size();
         for (size_t j : which) {
             if ((sth[j] != 0 && sth[j] != 1) || gsth[j] != 0 || Gh[j] == 1) continue;
             need.push_back(j);
@@ -442,21 +522,27 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
         out->dens.resize(base + gs.size());
         parallel_for_each(gs.size(), gs.size() <= 8 ? 1 : nthreads,
                           [&](size_t k) { out->dens[base + k] = divexact_u64(d, gs[k]); });
-        std::vector<BigInt> own(need.size());  // denominators of the host gcds
-        parallel_for_each(need.size(), nthreads, [&](size_t k) {
-            const size_t j = need[k];
-            if (gsth[j] == 0) {
-                out->num[j] = divexact_u64(out->num[j], Gh[j]);
-                out->den_of[j] = (uint32_t)(base + (size_t)(std::lower_bound(gs.begin(), gs.end(), Gh[j]) - gs.begin()));
+        std::vector<BigInt> own(nlong);  // denominators of the host gcds
+        const size_t kBatch = 32, nbatch = (need.size() - nlong + kBatch - 1) / kBatch;
+        parallel_for_each(nlong + nbatch, nthreads, [&](size_t it) {
+            if (it >= nlong) {
+                const size_t k0 = nlong + (it - nlong) * kBatch, k1 = std::min(need.size(), k0 + kBatch);
+                for (size_t k = k0; k < k1; k++) {
+                    const size_t j = need[k];
+                    divexact_u64_inplace(out->num[j], Gh[j]);
+                    out->den_of[j] =
+                        (uint32_t)(base + (size_t)(std::lower_bound(gs.begin(), gs.end(), Gh[j]) - gs.begin()));
+                }
                 return;
             }
+            const size_t j = need[it];
             const BigInt g = gcd(out->num[j], d);
             host_gcds++;
             if (g.size() == 1 && g.d[0] == 1) return;
             out->num[j] = divexact(out->num[j], g);
-            own[k] = divexact(d, g);
-        });
-        for (size_t k = 0; k < need.size(); k++) {
+            own[it] = divexact(d, g);
+        }, 1);
+        for (size_t k = 0; k < nlong; k++) {
             if (own[k].is_zero()) continue;
             out->den_of[need[k]] = (uint32_t)out->dens.size();
             out->dens.push_back(std::move(own[k]));

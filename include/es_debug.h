@@ -42,6 +42,15 @@ int es_dbg_ratrec(const uint64_t *a, int32_t la, const uint64_t *M, int32_t lM, 
 int es_dbg_step_count(uint64_t mask, int32_t nbits, int32_t dbits, int32_t *m_exact, int64_t *bits_exact,
                       int32_t *m_fast, int64_t *bits_fast);
 
+/* X_k = sum_{i<m} x_{k,i} P^i for `count` components of m digits each
+ * (int64 [count][m][6]: balanced 384-bit two's-complement digits), the way
+ * the sample is assembled: each whole, and cut into `parts` ranges (a power
+ * of two) assembled on the pool's threads and joined pairwise.  X_k goes to
+ * out + k cap (lens[k] limbs, neg[k] its sign).  Returns 0, -1 on bad input
+ * or a result wider than cap, -2 if the two ways disagree. */
+int es_dbg_assemble(const uint64_t *P, int32_t lP, const int64_t *digits, int32_t m, int32_t count,
+                    int32_t parts, uint64_t *out, int32_t *lens, int *neg, int32_t cap);
+
 /* For the last solve on the calling thread that took the GPU
  * reconstruction: `alone` = components whose GPU numerator fell outside the
  * bound and were reconstructed alone on the host; `host_gcds` = components

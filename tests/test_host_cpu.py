@@ -239,7 +239,8 @@ def test_divexact_one_word():
                 assert dbg(5, sgn * a << t, 1 << t)[0] == sgn * a
     # not exact, or b wider than one limb: refused
     L = ctypes.CDLL(_lib.LIB_PATH)
-    for a, b in [(7, 2), (3 << 70, 1 << 65), (10, 0), ((1 << 200) + 32, 64), ((1 << 100) + 1, 2)]:
+    for a, b in [(7, 2), (3 << 70, 1 << 65), (10, 0), ((1 << 200) + 32, 64), ((1 << 100) + 1, 2), (10, 3),
+                 ((1 << 300) + 5, 7), (3 * ((1 << 200) + 1) + 1, 3 << 5)]:
         pa, la_ = arr(to_limbs(a))
         pb, lb_ = arr(to_limbs(b))
         r = (ctypes.c_uint64 * 64)()
@@ -247,6 +248,41 @@ def test_divexact_one_word():
         st = L.es_dbg_bignum(5, pa, la_, 0, pb, lb_, 0, r, ctypes.byref(l1), ctypes.byref(n1), r,
                              ctypes.byref(l1), ctypes.byref(n1), 64)
         assert st != 0
+
+
+@pytest.mark.parametrize("m,count,parts", [(1, 1, 1), (7, 2, 1), (40, 3, 4), (172, 2, 4), (172, 1, 8), (61, 2, 2)])
+def test_assemble_in_parts(m, count, parts):
+    """The sample's X = sum_i x_i P^i from balanced digits (384-bit two's
+    complement, |x_i| <= P / 2), assembled whole and in `parts` ranges on
+    the pool's threads joined pairwise (ranges too short for the split fall
+    back to whole components): both against Python's own sum."""
+    rng = random.Random(m * 31 + count * 7 + parts)
+    P = 1
+    for q in modular.odd_primes_below(256):
+        P *= q
+    digits = np.zeros((count, m, 6), dtype=np.int64)
+    want = []
+    for k in range(count):
+        X = 0
+        for i in range(m):
+            x = rng.randrange(-(P // 2), P // 2 + 1)
+            if rng.random() < 0.1:
+                x = rng.choice([0, P // 2, -(P // 2)])
+            X += x * P ** i
+            u = x % (1 << 384)
+            digits[k, i] = np.array([(u >> (64 * t)) & ((1 << 64) - 1) for t in range(6)], dtype=np.uint64).view(np.int64)
+        want.append(X)
+    L = ctypes.CDLL(_lib.LIB_PATH)
+    pP, lP = arr(to_limbs(P))
+    cap = 6 * m + 8
+    out = (ctypes.c_uint64 * (cap * count))()
+    lens = (ctypes.c_int32 * count)()
+    neg = (ctypes.c_int * count)()
+    st = L.es_dbg_assemble(pP, lP, digits.ctypes.data_as(ctypes.c_void_p), m, count, parts, out, lens, neg, cap)
+    assert st == 0, st
+    for k in range(count):
+        got = from_limbs(out[k * cap:(k + 1) * cap], lens[k], neg[k])
+        assert got == want[k], k
 
 
 def ratrec(a, M, N, D, cap=4096):
