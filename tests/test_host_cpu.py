@@ -324,6 +324,32 @@ def test_ratrec_matches_oracle():
         assert ratrec(a, M, 1 << half, 1 << half) == dixon.rational_reconstruct(a, M, 1 << half, 1 << half)
 
 
+@pytest.mark.parametrize("k", [100, 172])
+def test_ratrec_long_remainders(k):
+    """Moduli of 550 and 860 limbs (the size of the sample's reconstructions
+    at n = 1024): the two-word Lehmer matrices over long remainders, with the
+    cofactors on a second thread in the hook's second run; both runs must
+    agree with the oracle, for balanced and unbalanced bounds (Wang's
+    stopping point in the middle, low and high)."""
+    rng = random.Random(k)
+    P = math.prod(modular.odd_primes_below(256))
+    M = P ** k
+    bits = M.bit_length() - 2
+    for nb in (bits // 2, bits // 6, (5 * bits) // 6):
+        db = bits - nb
+        N, D = 1 << nb, 1 << db
+        for _ in range(2):
+            den = rng.randrange(1, D)
+            num = rng.randrange(-N + 1, N)
+            if math.gcd(den, M) != 1:
+                continue
+            a = num * pow(den, -1, M) % M
+            assert ratrec(a, M, N, D) == dixon.rational_reconstruct(a, M, N, D)
+    a = rng.randrange(M)
+    half = bits // 2
+    assert ratrec(a, M, 1 << half, 1 << half) == dixon.rational_reconstruct(a, M, 1 << half, 1 << half)
+
+
 def test_ratrec_unbalanced_bounds_and_large_quotients():
     """Wang's stopping point away from the middle (N and D of different
     sizes), and remainder sequences with quotients of 2^62 and more (a full
