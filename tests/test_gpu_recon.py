@@ -84,12 +84,14 @@ def test_signs_and_zero_numerators():
 
 @pytest.mark.parametrize("n,c,seed", [(257, 1, 31), (267, 3, 34), (301, 4, 32), (521, 8, 33)])
 def test_gcd_groups_and_partial_blocks(n, c, seed):
-    """The gcd kernel runs several components per block (one Euclid wave for
-    eight of them, one limb wave each), as many as the component count
-    spread over the compute units asks for, up to thirteen, and three or
-    four per compute unit as two blocks of two.  n c = 257, 801, 1204 and
-    4168 components give groups of 2, 2, 5 and 13 (256 compute units), each
-    with a partial last block; the GPU path must match the host path and
+    """The gcd kernel runs several components per block (one limb wave each;
+    a Euclid wave for two of them on wide windows, four matrices a round,
+    in blocks of up to four, else for eight of them on narrow windows), as
+    many as the component count spread over the compute units asks for, up
+    to thirteen, and three or four per compute unit as two blocks of two.
+    n c = 257, 801, 1204 and 4168 components give groups of 2, 2, 5 and 13
+    (256 compute units): both window forms, each with a partial last block
+    (a lone component in the first case); the GPU path must match the host path and
     reconstruct no component alone.  A gcd goes back to the host only when a Euclidean quotient
     reaches 2^26 (about 2e-8 per step by the Gauss-Kuzmin law, so about once
     in the 3e7 steps of the largest case) or the gcd exceeds 64 bits."""
