@@ -55,6 +55,18 @@ struct PinnedStage {
 };
 thread_local PinnedStage g_pinned_stage;
 
+// A second stream for the numerator words' copies to the host, per thread
+// (kept until the process ends; default priority): the gcd kernel reads the
+// same words on the solve's stream meanwhile.
+struct CopyStream {
+    hipStream_t s = nullptr;
+    hipStream_t get() {
+        if (!s && hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) s = nullptr;
+        return s;
+    }
+};
+thread_local CopyStream g_copy_stream;
+
 // Marks the arrival of the numerator words on the host, per thread (kept
 // until the process ends).
 struct ReadyEvent {
@@ -67,6 +79,8 @@ struct ReadyEvent {
 thread_local ReadyEvent g_words_ready;
 // Marks the arrival on the host of the first gcd launch's results.
 thread_local ReadyEvent g_first_gcds;
+// Marks a chunk's numerators on the device, for the copy stream to wait on.
+thread_local ReadyEvent g_numer_done;
 
 // little-endian 32-bit words of a nonnegative BigInt, zero-padded to nw
 void to_words(const BigInt& v, uint32_t* w, int nw) {
@@ -277,6 +291,14 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
     const size_t y_bytes = round_up(NC * nw * sizeof(uint32_t), 256), st_bytes = round_up(NC * sizeof(int), 256);
     const size_t g_bytes = round_up(NC * sizeof(uint64_t), 256);
     const size_t sd_bytes = sidx.size() * dig_comp * sizeof(int64_t);
+    // the copy stream is idle whenever this returns (every exit waits for
+    // it), so the pinned stage and the caller's workspace are free to reuse
+    hipStream_t cst = g_copy_stream.get();
+    if (!cst) return ES_EHIP;
+    struct SyncOnExit {
+        hipStream_t s;
+        ~SyncOnExit() { (void)hipStreamSynchronize(s); }
+    } sync_copies{cst};
     uint8_t* pin = (uint8_t*)g_pinned_stage.get(y_bytes + 2 * st_bytes + g_bytes + sd_bytes);
     if (!pin) return ES_ENOMEM;
     uint32_t* Yh = (uint32_t*)pin;
@@ -399,7 +421,8 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
     bool gpu_gcd = false;
     size_t gcd_first = NC;  // components of the first gcd launch
     hipEvent_t words_ready = g_words_ready.get(), first_gcds = g_first_gcds.get();
-    if (!words_ready || !first_gcds) return ES_EHIP;
+    hipEvent_t numer_done = g_numer_done.get();
+    if (!words_ready || !first_gcds || !numer_done || !cst) return ES_EHIP;
     auto gpu_pass = [&]() -> int {
         // The chain T_{i+1} = T_i P mod M, cut into segments that each start
         // from P^{i0} d mod M = (d mod P^{m - i0}) P^{i0} (M = P^m: the
@@ -455,13 +478,15 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
             ev = kt->start(KC_RECON_OTHER);
             HIPOK(launch_numer(VT, pl.Ncolsp, rowsum, rows, Mwd, TM, Mtop, nbits, Yd + j0 * nw, std_ + j0, st));
             kt->stop(ev);
-            // the numerator words leave before the gcds, so the host converts
-            // them while the gcd kernel runs
+            // the numerator words leave on the copy stream while the gcds
+            // run, and the host converts them meanwhile
+            HIPOK(hipEventRecord(numer_done, st));
+            HIPOK(hipStreamWaitEvent(cst, numer_done, 0));
             HIPOK(hipMemcpyAsync(Yh + j0 * nw, Yd + j0 * nw, (size_t)rows * nw * sizeof(uint32_t),
-                                 hipMemcpyDeviceToHost, st));
-            HIPOK(hipMemcpyAsync(sth + j0, std_ + j0, (size_t)rows * sizeof(int), hipMemcpyDeviceToHost, st));
+                                 hipMemcpyDeviceToHost, cst));
+            HIPOK(hipMemcpyAsync(sth + j0, std_ + j0, (size_t)rows * sizeof(int), hipMemcpyDeviceToHost, cst));
         }
-        HIPOK(hipEventRecord(words_ready, st));
+        HIPOK(hipEventRecord(words_ready, cst));
         gcd_first = NC;
         if (gpu_gcd) {
             // over every component at once (the blocks fill the CUs in fewer
