@@ -134,29 +134,65 @@ struct Prep {
     bool a32 = false;
 };
 
-// Initialise the workspace, compute the norms, check the range.
-int prepare(const int64_t* dA, const int64_t* db, int32_t n, int32_t c, uint8_t* ws, hipStream_t st,
-            Prep* pr) {
+// Pinned host memory, kept per thread and grown on demand
+// (device-to-host copies into pageable memory go through an extra staging
+// copy, and pinned memory is allocated with hipHostMalloc, never registered).
+struct PinnedBuffer {
+    void* p = nullptr;
+    size_t bytes = 0;
+    ~PinnedBuffer() {
+        if (p) (void)hipHostFree(p);
+    }
+    void* get(size_t need) {
+        if (need <= bytes) return p;
+        if (p) (void)hipHostFree(p);
+        p = nullptr;
+        bytes = 0;
+        if (hipHostMalloc(&p, need, hipHostMallocDefault) != hipSuccess) {
+            p = nullptr;
+            return nullptr;
+        }
+        bytes = need;
+        return p;
+    }
+};
+thread_local PinnedBuffer g_pinned;  // the digits
+thread_local PinnedBuffer g_stats;   // the range statistics of A and b
+
+// Initialise the workspace and enqueue the norms and their copy to the host;
+// the elimination can be enqueued behind them before the host reads them.
+int prepare_launch(const int64_t* dA, const int64_t* db, int32_t n, int32_t c, uint8_t* ws, hipStream_t st,
+                   Prep* pr) {
     Layout& L = pr->L;
     HIP_CHECK(launch_fill_u32((uint32_t*)(ws + L.off_piv), (size_t)kNumPrimes * (n + 1), (uint32_t)INT_MAX, st));
     HIP_CHECK(launch_fill_u32((uint32_t*)(ws + L.off_rowpos), (size_t)kNumPrimes * n, 0xffffffffu, st));
     HIP_CHECK(launch_fill_u32((uint32_t*)(ws + L.off_flags), kNumPrimes, 0u, st));
     HIP_CHECK(launch_fill_u32((uint32_t*)(ws + L.off_rho), (size_t)kNumPrimes * c * L.pitch / 4, 0u, st));
     HIP_CHECK(launch_stats(dA, db, L, ws, st));
-    std::vector<uint64_t> rowmax(n);
-    std::vector<double> rn(n), cn(n), bn(c);
-    HIP_CHECK(hipMemcpyAsync(rowmax.data(), ws + L.off_rowmax, n * sizeof(uint64_t), hipMemcpyDeviceToHost, st));
-    HIP_CHECK(hipMemcpyAsync(rn.data(), ws + L.off_rownorm, n * sizeof(double), hipMemcpyDeviceToHost, st));
-    HIP_CHECK(hipMemcpyAsync(cn.data(), ws + L.off_colnorm, n * sizeof(double), hipMemcpyDeviceToHost, st));
-    HIP_CHECK(hipMemcpyAsync(bn.data(), ws + L.off_bnorm, c * sizeof(double), hipMemcpyDeviceToHost, st));
-    HIP_CHECK(hipStreamSynchronize(st));
+    uint8_t* h = (uint8_t*)g_stats.get(((size_t)3 * n + c) * 8);
+    if (!h) return ES_ENOMEM;
+    HIP_CHECK(hipMemcpyAsync(h, ws + L.off_rowmax, n * sizeof(uint64_t), hipMemcpyDeviceToHost, st));
+    HIP_CHECK(hipMemcpyAsync(h + (size_t)8 * n, ws + L.off_rownorm, n * sizeof(double), hipMemcpyDeviceToHost, st));
+    HIP_CHECK(hipMemcpyAsync(h + (size_t)16 * n, ws + L.off_colnorm, n * sizeof(double), hipMemcpyDeviceToHost, st));
+    HIP_CHECK(hipMemcpyAsync(h + (size_t)24 * n, ws + L.off_bnorm, c * sizeof(double), hipMemcpyDeviceToHost, st));
+    return ES_OK;
+}
+
+// After the stream has passed prepare_launch's copies: check the range and
+// bound the solution's size.
+int prepare_finish(int32_t n, int32_t c, Prep* pr) {
+    const uint8_t* h = (const uint8_t*)g_stats.p;
+    const uint64_t* rowmax = (const uint64_t*)h;
+    const double* rn = (const double*)(h + (size_t)8 * n);
+    const double* cn = (const double*)(h + (size_t)16 * n);
+    const double* bn = (const double*)(h + (size_t)24 * n);
     uint64_t mx = 0;
     for (int i = 0; i < n; i++) mx = rowmax[i] > mx ? rowmax[i] : mx;
     pr->maxabs = mx;
     if ((unsigned __int128)mx * (unsigned)n >= ((unsigned __int128)1 << 63)) return ES_ERANGE;
     for (int i = 0; i < n; i++)
         if (rn[i] == 0.0 || cn[i] == 0.0) return ES_SINGULAR;  // a zero row or column
-    hadamard_bits(rn.data(), cn.data(), bn.data(), n, c, &pr->nbits, &pr->dbits);
+    hadamard_bits(rn, cn, bn, n, c, &pr->nbits, &pr->dbits);
     pr->a32 = mx < (1ULL << 31);
     return ES_OK;
 }
@@ -188,7 +224,7 @@ int run_inverse(const int64_t* dA, uint8_t* ws, hipStream_t st, Prep* pr, int* f
     const Layout& L = pr->L;
     const bool blocked = use_blocked(L);
     long ev = prof->start(KC_RESIDUES);
-    HIP_CHECK(launch_residues(dA, L, ws, pr->a32, st, blocked));
+    HIP_CHECK(launch_residues(dA, L, ws, st, blocked));
     prof->stop(ev);
     if (blocked && !prof->on && use_lookahead()) {
         // panel K runs together with the update of panel K - 32 (the columns
@@ -234,29 +270,6 @@ int no_prime_decision(const int64_t* dA, int32_t n, const Prep& pr, hipStream_t 
     return ES_SINGULAR;  // singular modulo two 62-bit primes as well
 }
 
-// Pinned host memory for the digits, kept per thread and grown on demand
-// (device-to-host copies into pageable memory go through an extra staging
-// copy, and pinned memory is allocated with hipHostMalloc, never registered).
-struct PinnedBuffer {
-    void* p = nullptr;
-    size_t bytes = 0;
-    ~PinnedBuffer() {
-        if (p) (void)hipHostFree(p);
-    }
-    void* get(size_t need) {
-        if (need <= bytes) return p;
-        if (p) (void)hipHostFree(p);
-        p = nullptr;
-        bytes = 0;
-        if (hipHostMalloc(&p, need, hipHostMallocDefault) != hipSuccess) {
-            p = nullptr;
-            return nullptr;
-        }
-        bytes = need;
-        return p;
-    }
-};
-thread_local PinnedBuffer g_pinned;
 
 // Lift m steps; digits land in host [n*c][m][6].
 // With dig_dev set, the digits stay on the device ([n*c][m][6] at dig_dev)
@@ -412,13 +425,17 @@ int es_solve_device(const int64_t* dA, const int64_t* db, int32_t n, int32_t c, 
     Profiler prof(st);
     try {
         auto t0 = clk::now();
-        int rc = prepare(dA, db, n, c, ws, st, &pr);
+        int rc = prepare_launch(dA, db, n, c, ws, st, &pr);
         g_timings[0] = ms_since(t0);
         if (rc != ES_OK) return rc;
         t0 = clk::now();
         int flags[kNumPrimes];
         rc = run_inverse(dA, ws, st, &pr, flags, &prof);
         g_timings[1] = ms_since(t0);
+        if (rc != ES_OK) return rc;
+        t0 = clk::now();
+        rc = prepare_finish(n, c, &pr);
+        g_timings[0] += ms_since(t0);
         if (rc != ES_OK) return rc;
         LiveSet ls = make_live_set(flags);
         if (ls.E == 0) return no_prime_decision(dA, n, pr, st);
@@ -563,12 +580,14 @@ int batched_inverse_in(const int64_t* dA, const Layout& L, uint8_t* ws, hipStrea
     Prep pr;
     pr.L = L;
     // the norms of b are not needed here; A stands in for it
-    int rc = prepare(dA, dA, L.n, 1, ws, st, &pr);
-    if (rc == ES_SINGULAR) rc = ES_OK;  // a zero row/column just makes every prime singular
+    int rc = prepare_launch(dA, dA, L.n, 1, ws, st, &pr);
     if (rc != ES_OK) return rc;
     int flags[kNumPrimes];
     Profiler prof(st);
     rc = run_inverse(dA, ws, st, &pr, flags, &prof);
+    if (rc != ES_OK) return rc;
+    rc = prepare_finish(L.n, 1, &pr);
+    if (rc == ES_SINGULAR) rc = ES_OK;  // a zero row/column just makes every prime singular
     if (rc != ES_OK) return rc;
     HIP_CHECK(launch_export_inverse(pr.L, ws, dB_out, st));
     HIP_CHECK(hipStreamSynchronize(st));
@@ -626,11 +645,13 @@ int es_lift_digits(const int64_t* dA, const int64_t* db, int32_t n, int32_t c, v
     hipStream_t st = (hipStream_t)stream;
     uint8_t* ws = (uint8_t*)d_ws;
     try {
-        int rc = prepare(dA, db, n, c, ws, st, &pr);
+        int rc = prepare_launch(dA, db, n, c, ws, st, &pr);
         if (rc != ES_OK) return rc;
         int flags[kNumPrimes];
         Profiler prof(st);
         rc = run_inverse(dA, ws, st, &pr, flags, &prof);
+        if (rc != ES_OK) return rc;
+        rc = prepare_finish(n, c, &pr);
         if (rc != ES_OK) return rc;
         LiveSet ls = make_live_set(flags);
         if (ls.E == 0) return no_prime_decision(dA, n, pr, st);

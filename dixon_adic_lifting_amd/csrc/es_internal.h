@@ -171,8 +171,9 @@ int lift_record_steps(const Layout& L);
 hipError_t launch_fill_u32(uint32_t* p, size_t count, uint32_t value, hipStream_t st);
 hipError_t launch_stats(const int64_t* A, const int64_t* b, const Layout& L, uint8_t* ws,
                         hipStream_t st);
-hipError_t launch_residues(const int64_t* A, const Layout& L, uint8_t* ws, bool make_a32,
-                           hipStream_t st, bool balanced_out = false);
+// also writes the int32 copy of A (meaningful only when every |A_ij| < 2^31)
+hipError_t launch_residues(const int64_t* A, const Layout& L, uint8_t* ws, hipStream_t st,
+                           bool balanced_out = false);
 hipError_t launch_gj_step(const Layout& L, uint8_t* ws, int k, hipStream_t st);
 // blocked form of the same elimination: 32 steps per panel launch, then one
 // MFMA update launch (residues must be balanced: launch_residues(..., true))

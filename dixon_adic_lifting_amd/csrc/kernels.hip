@@ -199,36 +199,50 @@ hipError_t launch_stats(const int64_t* A, const int64_t* b, const Layout& L, uin
 }
 
 // ---------------------------------------------------------------- residues of A
-// S[j][i][col] = A[i][col] mod q_j for all 53 primes (zero in the pitch
-// padding); optionally an int32 copy of A for the residual update.
-template <bool SMALL>  // SMALL: every |A_ij| < 2^32
-__global__ __launch_bounds__(256) void residue_kernel(const int64_t* __restrict__ A, int n, int pitch,
-                                                      uint8_t* __restrict__ S,
-                                                      int32_t* __restrict__ A32, int make_a32, int bal) {
-    const int i = blockIdx.x;
-    const int col = (blockIdx.y * 256 + threadIdx.x) * 4;
-    if (col >= pitch) return;
-    uint64_t mag[4];
-    bool neg[4];
-#pragma unroll
-    for (int u = 0; u < 4; u++) {
-        int64_t a = (col + u < n) ? A[(size_t)i * n + col + u] : 0;
-        if (make_a32 && col + u < n) A32[(size_t)i * n + col + u] = (int32_t)a;
-        neg[u] = a < 0;
-        mag[u] = a < 0 ? (uint64_t)0 - (uint64_t)a : (uint64_t)a;
-    }
+// The 53 residue bytes of four entries (magnitudes mag, signs neg) of row i
+// from column col: BIG reduces 64-bit magnitudes, else 32-bit ones.
+template <bool BIG>
+__device__ __forceinline__ void residue_bytes(const uint64_t* mag, const bool* neg, int n, int pitch, int i,
+                                              int col, uint8_t* __restrict__ S, int bal) {
     for (int j = 0; j < kNumPrimes; j++) {
         const uint32_t q = c_pt.q[j], mu16 = c_pt.mu16[j], mu32 = c_pt.mu32[j], r32 = c_pt.r32[j];
         uint32_t w = 0;
 #pragma unroll
         for (int u = 0; u < 4; u++) {
-            uint32_t r = SMALL ? red32((uint32_t)mag[u], q, mu32) : red64(mag[u], q, mu16, mu32, r32);
+            uint32_t r = BIG ? red64(mag[u], q, mu16, mu32, r32) : red32((uint32_t)mag[u], q, mu32);
             if (neg[u] && r) r = q - r;
             if (bal && r > (q >> 1)) r = (r - q) & 0xffu;  // balanced residue as a two's-complement byte
             w |= r << (8 * u);
         }
         *(uint32_t*)(S + ((size_t)j * n + i) * pitch + col) = w;
     }
+}
+
+// S[j][i][col] = A[i][col] mod q_j for all 53 primes (zero in the pitch
+// padding), reduced from 32 bits where a thread's four magnitudes fit them;
+// and an int32 copy of A for the residual update (used only when every
+// entry fits, which the host learns from the range statistics meanwhile).
+__global__ __launch_bounds__(256) void residue_kernel(const int64_t* __restrict__ A, int n, int pitch,
+                                                      uint8_t* __restrict__ S,
+                                                      int32_t* __restrict__ A32, int bal) {
+    const int i = blockIdx.x;
+    const int col = (blockIdx.y * 256 + threadIdx.x) * 4;
+    if (col >= pitch) return;
+    uint64_t mag[4];
+    bool neg[4];
+    uint64_t any = 0;
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+        int64_t a = (col + u < n) ? A[(size_t)i * n + col + u] : 0;
+        if (col + u < n) A32[(size_t)i * n + col + u] = (int32_t)a;
+        neg[u] = a < 0;
+        mag[u] = a < 0 ? (uint64_t)0 - (uint64_t)a : (uint64_t)a;
+        any |= mag[u];
+    }
+    if (any >> 32)
+        residue_bytes<true>(mag, neg, n, pitch, i, col, S, bal);
+    else
+        residue_bytes<false>(mag, neg, n, pitch, i, col, S, bal);
 }
 
 // first pivot (step 0) per prime: the lowest row with a nonzero residue in column 0
@@ -263,16 +277,10 @@ int device_cu_count() {
     return cache[dev];
 }
 
-hipError_t launch_residues(const int64_t* A, const Layout& L, uint8_t* ws, bool make_a32,
-                           hipStream_t st, bool balanced_out) {
-    // caller guarantees small (< 2^32) entries whenever make_a32 is set
+hipError_t launch_residues(const int64_t* A, const Layout& L, uint8_t* ws, hipStream_t st, bool balanced_out) {
     dim3 grid(L.n, (L.pitch / 4 + 255) / 256);
-    if (make_a32)
-        es_launch(residue_kernel<true>, grid, dim3(256), 0, st, A, L.n, L.pitch,
-                           ws + L.off_S, (int32_t*)(ws + L.off_A32), 1, balanced_out ? 1 : 0);
-    else
-        es_launch(residue_kernel<false>, grid, dim3(256), 0, st, A, L.n, L.pitch,
-                           ws + L.off_S, (int32_t*)(ws + L.off_A32), 0, balanced_out ? 1 : 0);
+    es_launch(residue_kernel, grid, dim3(256), 0, st, A, L.n, L.pitch, ws + L.off_S, (int32_t*)(ws + L.off_A32),
+              balanced_out ? 1 : 0);
     if (balanced_out) {  // the blocked elimination's update queues start empty
         const hipError_t e = launch_fill_u32((uint32_t*)(ws + L.off_wq), (size_t)work_queue_rows(L.n) * 8, 0u, st);
         if (e != hipSuccess) return e;

@@ -54,6 +54,29 @@ def test_inverse_elementwise(n, bits, seed, primes):
     check_identity_gpu(A, B, flags, primes)
 
 
+@pytest.mark.parametrize("n,seed", [(70, 11), (261, 12)])
+def test_inverse_mixed_width_entries(n, seed, primes):
+    """Entries below 2^24 mixed with entries of 33 to 54 bits in the same rows
+    (and the same groups of four columns): each group is reduced from 64 bits
+    when any of its entries needs them, from 32 bits otherwise."""
+    A, _ = W.uniform_system(n, 1, 24, seed)
+    rng = np.random.default_rng(seed)
+    wide = rng.random((n, n)) < 0.1
+    mags = rng.integers(1 << 32, 1 << 54, size=(n, n), dtype=np.int64)
+    signs = rng.choice(np.array([-1, 1], dtype=np.int64), size=(n, n))
+    A = np.where(wide, signs * mags, A)
+    assert n * int(np.abs(A).max()) < (1 << 63)
+    B, flags = es.batched_inverse(torch.as_tensor(A).cuda())
+    Bh = B.cpu().numpy()
+    for q in (primes[:3] + primes[-3:]):
+        j = primes.index(q)
+        ref = modular.inverse_mod(A, q)
+        assert flags[j] == (1 if ref is None else 0), q
+        if ref is not None:
+            assert np.array_equal(Bh[j], balanced_np(ref, q)), q
+    check_identity_gpu(A, B, flags, primes)
+
+
 def test_inverse_pascal(primes):
     A, _ = W.generate("c2_pascal30")
     B, flags = es.batched_inverse(torch.as_tensor(A).cuda())
