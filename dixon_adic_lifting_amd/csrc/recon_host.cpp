@@ -281,6 +281,15 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
         if (verbose()) fprintf(stderr, "[es] gpu reconstruct %-12s %8.3f ms\n", what, ms);
         t0 = t1;
     };
+    // parts of a stage, printed only (the stage's lap keeps its total)
+    auto ts = clk::now();
+    auto sublap = [&](const char* what) {
+        const auto t1 = clk::now();
+        if (verbose())
+            fprintf(stderr, "[es] gpu reconstruct   %-10s %8.3f ms\n", what,
+                    std::chrono::duration<double, std::milli>(t1 - ts).count());
+        ts = t1;
+    };
     const int m = pl.m, NW = pl.NW, TM = pl.TM, nw = pl.nw;
     const size_t NC = pl.NC;
     const uint64_t* dig = (const uint64_t*)(scr + pl.off_digits);
@@ -310,6 +319,7 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
         HIPOK(hipMemcpyAsync(sd + k * dig_comp, dig + sidx[k] * dig_comp, dig_comp * sizeof(int64_t),
                              hipMemcpyDeviceToHost, st));
     HIPOK(hipStreamSynchronize(st));
+    sublap("digits");
     // The sample's denominators (Wang reconstruction of each X mod M; their
     // lcm is d).  With one right-hand side the first two run first, with a
     // second thread each for the cofactors, and the GPU pass starts from
@@ -326,6 +336,7 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
         while (parts < 8 && (size_t)parts * 2 * nfirst <= (size_t)nthreads) parts *= 2;
         assemble_split(sd, dig_comp, nfirst, m, pw, parts, nthreads, xs.data());
     }
+    sublap("assemble");
     const BigInt Nb = shl(BigInt::from_u64(1), (size_t)nbits);
     const BigInt Db = shl(BigInt::from_u64(1), (size_t)dbits);
     std::vector<BigInt> sden(xs.size());
@@ -363,6 +374,7 @@ int reconstruct_gpu(const GpuReconPlan& pl, uint8_t* scr, const BigInt& P, const
     } else {
         parallel_for_each(nfirst, nthreads, [&](size_t k) { sample_rr(k, split_first); });
     }
+    sublap("wang");
     if (!rest_now) start_rest();
     if (bad) return ES_EINTERNAL;
     // dbase: the lcm of the denominators known so far; d, the pass's
