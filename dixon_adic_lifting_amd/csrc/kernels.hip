@@ -608,34 +608,36 @@ __device__ __forceinline__ void panel_old_rows(int8_t* __restrict__ Sj, int n, i
     }
 }
 
-// The panel's pivot rows (all columns) to GT transposed, [col][c] with 32
-// bytes per column (their panel columns are never read): 1024 columns at a
-// time, words read along the rows, bytes regrouped in LDS by column (gts,
-// 32 KB), then one 32-byte row of GT per column.  Every thread of the block
-// takes part (barriers inside).
-__device__ __forceinline__ void panel_gather_gt(const int8_t* __restrict__ Sj, int pitch, int bw,
-                                                const int* __restrict__ plist, uint8_t* gts,
-                                                int8_t* __restrict__ GTj, int t) {
-    for (int c0 = 0; c0 < pitch; c0 += 1024) {
-        const int ncol = min(1024, pitch - c0);
+// Columns col .. col + 3 of pivot rows r0 .. r0 + 7 (of the panel's bw,
+// rows plist[c]) into GT transposed ([col][c], 32 bytes a column): eight
+// word loads, the 8 x 4 bytes regrouped in registers, and one 8-byte slice
+// of each of the four columns' GT rows.  col + 3 < pitch.
+__device__ __forceinline__ void gt_slice(const int8_t* __restrict__ Sj, int pitch, int bw,
+                                         const int* __restrict__ plist, int8_t* __restrict__ GTj, int col, int r0) {
+    uint32_t w[8];
 #pragma unroll
-        for (int u = 0; u < 8; u++) {
-            const int w = t + 1024 * u;  // word w: row c = w / 256, columns 4 (w % 256) .. + 3
-            const int c = w >> 8, cw = w & 255;
-            if (4 * cw >= ncol) continue;
-            const uint32_t v = c < bw ? *(const uint32_t*)(Sj + (size_t)plist[c] * pitch + c0 + 4 * cw) : 0u;
+    for (int r = 0; r < 8; r++)
+        w[r] = r0 + r < bw ? *(const uint32_t*)(Sj + (size_t)plist[r0 + r] * pitch + col) : 0u;
 #pragma unroll
-            for (int bb = 0; bb < 4; bb++) gts[(4 * cw + bb) * kPanel + c] = (uint8_t)(v >> (8 * bb));
+    for (int b = 0; b < 4; b++) {
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            lo |= ((w[r] >> (8 * b)) & 0xffu) << (8 * r);
+            hi |= ((w[r + 4] >> (8 * b)) & 0xffu) << (8 * r);
         }
-        __syncthreads();
-        if (t < ncol) {
-            const uint4* src = (const uint4*)(gts + t * kPanel);
-            uint4* dst = (uint4*)(GTj + (size_t)(c0 + t) * kPanel);
-            dst[0] = src[0];
-            dst[1] = src[1];
-        }
-        __syncthreads();
+        *(uint2*)(GTj + (size_t)(col + b) * kPanel + r0) = make_uint2(lo, hi);
     }
+}
+
+// The panel's pivot rows (all columns) to GT, by a 1024-thread block:
+// thread t takes columns 4 (t mod 256) + 1024 i .. + 3 of the pivot rows
+// 8 (t / 256) .. + 7 (each wave's loads cover 256 contiguous bytes of a
+// row; the pitch is a multiple of 64).
+__device__ __forceinline__ void panel_gather_gt(const int8_t* __restrict__ Sj, int pitch, int bw,
+                                                const int* __restrict__ plist, int8_t* __restrict__ GTj, int t) {
+    const int r0 = 8 * (t >> 8);
+    for (int col = 4 * (t & 255); col < pitch; col += 1024) gt_slice(Sj, pitch, bw, plist, GTj, col, r0);
 }
 
 // The candidate rows (no pivot step yet, rowpos < 0) in row order at
@@ -1282,9 +1284,8 @@ __global__ __launch_bounds__(1024) void gj_panel_kernel(int8_t* __restrict__ S, 
     const bool ok = UP ? panel_up_body<RPT>(S, n, pitch, K, piv, rowpos, flags, j)
                        : panel_packed_body<RPT>(S, n, pitch, K, piv, rowpos, flags, j);
     if (!ok) return;  // the whole block
-    __syncthreads();
-    __shared__ __attribute__((aligned(16))) uint8_t gts[1024 * kPanel];
-    panel_gather_gt(S + (size_t)j * n * pitch, pitch, min(kPanel, n - K), piv + (size_t)j * (n + 1) + K, gts,
+    __syncthreads();  // the pivot rows the panel wrote are visible to the block
+    panel_gather_gt(S + (size_t)j * n * pitch, pitch, min(kPanel, n - K), piv + (size_t)j * (n + 1) + K,
                     GT + (size_t)j * pitch * kPanel, threadIdx.x);
 }
 
@@ -1365,34 +1366,18 @@ __global__ __launch_bounds__(1024) void gj_panel_rest_kernel(int8_t* __restrict_
 }
 
 // After panel K: its pivot rows to GT, 256 columns per block (grid
-// (column chunks, primes)), words read along the rows and regrouped by
-// column in LDS, one 32-byte row of GT per column.
+// (column chunks, primes)), with no LDS: thread t takes columns
+// c0 + 4 (t mod 64) .. + 3 of the pivot rows 8 (t / 64) .. + 7 (each wave's
+// loads cover 256 contiguous bytes of a row); the block's four waves fill
+// the 32-byte GT rows of its columns.
 __device__ __forceinline__ void gather_gt_block(const int8_t* __restrict__ S, int n, int pitch, int K,
                                                 const int* __restrict__ piv, int8_t* __restrict__ GT, int j,
                                                 int bx) {
     const int t = threadIdx.x;
-    const int c0 = bx * 256;
-    const int ncol = min(256, pitch - c0);
-    const int bw = min(kPanel, n - K);
-    const int8_t* Sj = S + (size_t)j * n * pitch;
-    const int* plist = piv + (size_t)j * (n + 1) + K;
-    __shared__ __attribute__((aligned(16))) uint8_t gts[256 * kPanel];
-#pragma unroll
-    for (int u = 0; u < 8; u++) {
-        const int w = t + 256 * u;  // word w: row c = w / 64, columns 4 (w % 64) .. + 3
-        const int c = w >> 6, cw = w & 63;
-        if (4 * cw >= ncol) continue;
-        const uint32_t v = c < bw ? *(const uint32_t*)(Sj + (size_t)plist[c] * pitch + c0 + 4 * cw) : 0u;
-#pragma unroll
-        for (int bb = 0; bb < 4; bb++) gts[(4 * cw + bb) * kPanel + c] = (uint8_t)(v >> (8 * bb));
-    }
-    __syncthreads();
-    if (t < ncol) {
-        const uint4* src = (const uint4*)(gts + t * kPanel);
-        uint4* dst = (uint4*)(GT + ((size_t)j * pitch + c0 + t) * kPanel);
-        dst[0] = src[0];
-        dst[1] = src[1];
-    }
+    const int col = bx * 256 + 4 * (t & 63);
+    if (col >= pitch) return;  // the pitch is a multiple of 64: col + 3 < pitch otherwise
+    gt_slice(S + (size_t)j * n * pitch, pitch, min(kPanel, n - K), piv + (size_t)j * (n + 1) + K,
+             GT + (size_t)j * pitch * kPanel, col, 8 * (t >> 6));
 }
 
 // Then, when K + 32 < n, the update of the next panel's columns
